@@ -1,0 +1,8 @@
+"""Gated DeltaNet chunked-prefill forward for AMD MI355X (gfx950).
+
+The forward runs in hand-written HIP kernels behind a C ABI (include/gdn.h,
+built into _build/libgdn.so); this package is the thin Python binding over it
+plus a seeded synthetic-input generator.
+"""
+from .binding import (GDNError, chunk_gated_delta_rule, chunk_prep, fwd, load_library,  # noqa: F401
+                      plan, LIB_PATH)

@@ -1,0 +1,350 @@
+// C ABI of the Gated DeltaNet chunked-prefill forward: validation, the AutoCP
+// planner and kernel launches. Host code only; see include/gdn.h.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+constexpr float kDefaultLambda = 1.0f;
+constexpr int kDefaultWarmup = 6;
+constexpr int kMaxWarmup = 8;
+constexpr float kDefaultNoiseFloor = 1e-4f;
+constexpr size_t kStateElems = (size_t)gdn::kDim * gdn::kDim;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+    int n_seqs = 0;
+    std::vector<int> len;       // tokens per sequence
+    int n_chunks_total = 0, n_chunks_max = 0;
+    int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0;
+    float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
+    size_t off_state = 0, off_M = 0, off_H = 0, off_warm = 0, ws_bytes = 0;
+};
+
+int n_chunks_of(int len) { return (len + gdn::kChunk - 1) / gdn::kChunk; }
+int n_segs_of(int N, int L) { return N == 0 ? 1 : (N + L - 1) / L; }
+
+gdn_status validate_desc(const gdn_desc* d) {
+    if (!d) return fail(GDN_ERR_NULL_ARG, "desc is NULL");
+    if (d->B < 1 || d->T < 0 || d->h_qk < 1 || d->h_v < 1)
+        return fail(GDN_ERR_BAD_SHAPE, "need B >= 1, T >= 0, h_qk >= 1, h_v >= 1 (got B=%d T=%d h_qk=%d h_v=%d)",
+                    d->B, d->T, d->h_qk, d->h_v);
+    if (d->h_v % d->h_qk != 0)
+        return fail(GDN_ERR_BAD_SHAPE, "h_v (%d) must be a multiple of h_qk (%d)", d->h_v, d->h_qk);
+    if (d->h_v > 65535) return fail(GDN_ERR_BAD_SHAPE, "h_v (%d) exceeds 65535", d->h_v);
+    if (d->d_k != gdn::kDim || d->d_v != gdn::kDim)
+        return fail(GDN_ERR_UNSUPPORTED_DIM, "only d_k = d_v = 128 is supported (got %d, %d)", d->d_k, d->d_v);
+    if (d->io_dtype != GDN_BF16 && d->io_dtype != GDN_F32)
+        return fail(GDN_ERR_BAD_DTYPE, "io_dtype %d is not GDN_BF16 or GDN_F32", d->io_dtype);
+    if (d->cp_mode < GDN_CP_AUTO || d->cp_mode > GDN_CP_WARMUP)
+        return fail(GDN_ERR_BAD_OPTION, "cp_mode %d out of range", d->cp_mode);
+    if (!(d->lambda >= 0.f) || !std::isfinite(d->lambda))
+        return fail(GDN_ERR_BAD_OPTION, "lambda must be finite and >= 0");
+    if (d->warmup_chunks < 0 || d->warmup_chunks > kMaxWarmup)
+        return fail(GDN_ERR_BAD_OPTION, "warmup_chunks must be in 0..%d (got %d)", kMaxWarmup, d->warmup_chunks);
+    if (!(d->noise_floor >= 0.f && d->noise_floor < 1.f))
+        return fail(GDN_ERR_BAD_OPTION, "noise_floor must be in [0, 1)");
+    if (d->n_cu < 0) return fail(GDN_ERR_BAD_OPTION, "n_cu must be >= 0");
+    if ((long long)d->B * d->T > 0x7fffffffLL)
+        return fail(GDN_ERR_BAD_SHAPE, "B * T exceeds 2^31 - 1 tokens");
+    if (d->host_cu_seqlens) {
+        if (d->B != 1) return fail(GDN_ERR_BAD_SHAPE, "cu_seqlens requires B == 1 (got B=%d)", d->B);
+        if (d->n_seqs < 1) return fail(GDN_ERR_BAD_SHAPE, "n_seqs must be >= 1 with cu_seqlens");
+        const int32_t* cu = d->host_cu_seqlens;
+        if (cu[0] != 0) return fail(GDN_ERR_BAD_SHAPE, "cu_seqlens[0] must be 0");
+        for (int n = 0; n < d->n_seqs; ++n)
+            if (cu[n + 1] < cu[n]) return fail(GDN_ERR_BAD_SHAPE, "cu_seqlens must be non-decreasing (at %d)", n);
+        if (cu[d->n_seqs] != d->T)
+            return fail(GDN_ERR_BAD_SHAPE, "cu_seqlens[n_seqs] (%d) must equal T (%d)", cu[d->n_seqs], d->T);
+    } else if (d->n_seqs != d->B) {
+        return fail(GDN_ERR_BAD_SHAPE, "n_seqs (%d) must equal B (%d) without cu_seqlens", d->n_seqs, d->B);
+    }
+    return GDN_OK;
+}
+
+gdn_status query_cu_count(int* n_cu) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "querying the CU count failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+// The AutoCP planner (section "Gate-Driven Automatic Intra-Card Context
+// Parallelism (AutoCP)": L = lambda sqrt(N) chunks per segment). Readings:
+// N is the chunk count of the longest sequence; L is rounded half-up and
+// capped at the largest L that still gives every CU a workgroup; AUTO keeps
+// a sequence whole when (sequences x heads) already cover the CUs or when the
+// sequence is shorter than two warm-up windows.
+gdn_status make_plan(const gdn_desc* d, Plan* pl) {
+    gdn_status st = validate_desc(d);
+    if (st != GDN_OK) return st;
+    Plan P;
+    P.n_seqs = d->host_cu_seqlens ? d->n_seqs : d->B;
+    P.len.resize(P.n_seqs);
+    for (int n = 0; n < P.n_seqs; ++n)
+        P.len[n] = d->host_cu_seqlens ? d->host_cu_seqlens[n + 1] - d->host_cu_seqlens[n] : d->T;
+    long long nct = 0;
+    for (int n = 0; n < P.n_seqs; ++n) {
+        const int N = n_chunks_of(P.len[n]);
+        nct += N;
+        P.n_chunks_max = std::max(P.n_chunks_max, N);
+    }
+    if (nct > 0x7fffffffLL) return fail(GDN_ERR_BAD_SHAPE, "too many chunks");
+    P.n_chunks_total = (int)nct;
+    P.w = d->warmup_chunks ? d->warmup_chunks : kDefaultWarmup;
+    P.lambda = d->lambda > 0.f ? d->lambda : kDefaultLambda;
+    P.eps = d->noise_floor > 0.f ? d->noise_floor : kDefaultNoiseFloor;
+    if (d->n_cu > 0) P.n_cu = d->n_cu;
+    else if ((st = query_cu_count(&P.n_cu)) != GDN_OK) return st;
+
+    const int Nm = P.n_chunks_max;
+    auto total_segs = [&](int L) {
+        long long s = 0;
+        for (int n = 0; n < P.n_seqs; ++n) s += n_segs_of(n_chunks_of(P.len[n]), L);
+        return s;
+    };
+    bool split = d->cp_mode != GDN_CP_OFF && Nm > 1;
+    if (split && d->cp_mode == GDN_CP_AUTO &&
+        ((long long)P.n_seqs * d->h_v >= P.n_cu || Nm < 2 * (P.w + 1)))
+        split = false;
+    if (!split) {
+        P.L = std::max(Nm, 1);
+    } else {
+        const int L_lam = std::max(1, (int)std::floor(P.lambda * std::sqrt((double)Nm) + 0.5));
+        int L = std::min(L_lam, Nm);
+        while (L > 1 && total_segs(L) * d->h_v < P.n_cu) --L;  // fill every CU
+        P.L = L;
+    }
+    long long ns = 0;
+    for (int n = 0; n < P.n_seqs; ++n) {
+        const int s = n_segs_of(n_chunks_of(P.len[n]), P.L);
+        ns += s;
+        P.P_max = std::max(P.P_max, s);
+    }
+    if (ns > 0x7fffffffLL / 2) return fail(GDN_ERR_BAD_SHAPE, "too many segments");
+    P.n_segments = (int)ns;
+    P.cp_on = P.P_max > 1;
+    size_t off = 0;
+    if (P.cp_on) {
+        const size_t st_bytes = (size_t)P.n_segments * d->h_v * kStateElems * sizeof(float);
+        P.off_state = off; off = align_up(off + st_bytes, 256);
+        P.off_M = off;     off = align_up(off + st_bytes, 256);
+        P.off_H = off;     off = align_up(off + st_bytes, 256);
+        P.off_warm = off;  off = align_up(off + (size_t)P.n_segments * d->h_v * sizeof(int32_t), 256);
+    }
+    P.ws_bytes = off;
+    *pl = std::move(P);
+    return GDN_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+gdn_status check_ptr(const void* p, const char* name, bool required, size_t align = 16) {
+    if (!p) {
+        if (required) return fail(GDN_ERR_NULL_ARG, "%s is NULL", name);
+        return GDN_OK;
+    }
+    if (!aligned(p, align)) return fail(GDN_ERR_MISALIGNED, "%s is not %zu-byte aligned", name, align);
+    return GDN_OK;
+}
+
+gdn::Params base_params(const gdn_desc* d, const Plan& P) {
+    gdn::Params p{};
+    p.n_seqs = P.n_seqs;
+    p.seq_len = d->T;
+    p.h_qk = d->h_qk;
+    p.h_v = d->h_v;
+    p.group = d->h_v / d->h_qk;
+    p.L = P.L;
+    p.w = P.w;
+    p.cp_mode = d->cp_mode;
+    p.n_segments = P.n_segments;
+    p.n_chunks = P.n_chunks_total;
+    p.log_eps = std::log(P.eps);
+    return p;
+}
+
+gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, float scale, const float* s_init, const int32_t* cu, void* out,
+                   float* s_final, void* ws, size_t ws_bytes, void* stream, float* seg_out,
+                   int32_t* path_out) {
+    Plan P;
+    gdn_status st = make_plan(d, &P);
+    if (st != GDN_OK) return st;
+    const bool varlen = d->host_cu_seqlens != nullptr;
+    if (varlen && !cu) return fail(GDN_ERR_NULL_ARG, "cu_seqlens is NULL but desc->host_cu_seqlens is set");
+    if (!varlen && cu) return fail(GDN_ERR_NULL_ARG, "desc->host_cu_seqlens is required with cu_seqlens");
+    const bool any = (long long)d->B * d->T > 0;
+    if ((st = check_ptr(q, "q", any)) || (st = check_ptr(k, "k", any)) || (st = check_ptr(v, "v", any)) ||
+        (st = check_ptr(g, "g", any)) || (st = check_ptr(beta, "beta", any)) ||
+        (st = check_ptr(out, "out", any)) || (st = check_ptr(s_init, "initial_state", false)) ||
+        (st = check_ptr(s_final, "final_state", false)) || (st = check_ptr(cu, "cu_seqlens", false, 4)) ||
+        (st = check_ptr(seg_out, "seg_state_out", false)) || (st = check_ptr(path_out, "path_out", false, 4)))
+        return st;
+    if (!std::isfinite(scale)) return fail(GDN_ERR_BAD_SCALE, "scale is not finite");
+    if (ws_bytes < P.ws_bytes)
+        return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, P.ws_bytes);
+    if (P.ws_bytes > 0 && (st = check_ptr(ws, "workspace", true, 256))) return st;
+
+    gdn::Params p = base_params(d, P);
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.s_init = s_init; p.cu = cu;
+    p.out = out; p.s_final = s_final; p.scale = scale;
+    char* w8 = static_cast<char*>(ws);
+    if (P.cp_on) {
+        p.seg_state = reinterpret_cast<float*>(w8 + P.off_state);
+        p.seg_M = reinterpret_cast<float*>(w8 + P.off_M);
+        p.seg_H = reinterpret_cast<float*>(w8 + P.off_H);
+        p.warm = reinterpret_cast<int32_t*>(w8 + P.off_warm);
+    }
+    const int io = d->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
+    int e;
+    if (P.cp_on) {
+        if ((e = gdn::launch_cp_prep(p, io, stream)))
+            return fail(GDN_ERR_HIP, "cp_prep launch: %s", hipGetErrorString((hipError_t)e));
+        if ((e = gdn::launch_cp_combine(p, stream)))
+            return fail(GDN_ERR_HIP, "cp_combine launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    if ((e = gdn::launch_fwd(p, io, stream)))
+        return fail(GDN_ERR_HIP, "fwd launch: %s", hipGetErrorString((hipError_t)e));
+
+    if (seg_out || path_out) {
+        hipStream_t s = (hipStream_t)stream;
+        const size_t per_seg = (size_t)d->h_v * kStateElems;
+        hipError_t he = hipSuccess;
+        if (seg_out) {
+            if (P.cp_on)
+                he = hipMemcpyAsync(seg_out, p.seg_state, P.n_segments * per_seg * sizeof(float),
+                                    hipMemcpyDeviceToDevice, s);
+            int base = 0;
+            for (int n = 0; n < P.n_seqs && he == hipSuccess; ++n) {
+                float* dst = seg_out + (size_t)base * per_seg;
+                if (s_init)
+                    he = hipMemcpyAsync(dst, s_init + (size_t)n * per_seg, per_seg * sizeof(float),
+                                        hipMemcpyDeviceToDevice, s);
+                else
+                    he = hipMemsetAsync(dst, 0, per_seg * sizeof(float), s);
+                base += n_segs_of(n_chunks_of(P.len[n]), P.L);
+            }
+        }
+        if (he != hipSuccess) return fail(GDN_ERR_HIP, "debug copy: %s", hipGetErrorString(he));
+        if (path_out && (e = gdn::launch_debug_path(p, path_out, stream)))
+            return fail(GDN_ERR_HIP, "debug path launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
+    if (!out) return fail(GDN_ERR_NULL_ARG, "out is NULL");
+    Plan P;
+    gdn_status st = make_plan(desc, &P);
+    if (st != GDN_OK) return st;
+    out->chunk = gdn::kChunk;
+    out->n_chunks_total = P.n_chunks_total;
+    out->n_chunks_max = P.n_chunks_max;
+    out->cp_on = P.cp_on;
+    out->L = P.L;
+    out->n_segments = P.n_segments;
+    out->P_max = P.P_max;
+    out->warmup_chunks = P.w;
+    out->n_cu = P.n_cu;
+    out->lambda = P.lambda;
+    out->noise_floor = P.eps;
+    out->workspace_bytes = P.ws_bytes;
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+size_t gdn_fwd_workspace_bytes(const gdn_desc* desc) {
+    Plan P;
+    if (make_plan(desc, &P) != GDN_OK) return 0;
+    return P.ws_bytes;
+}
+
+gdn_status gdn_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, float scale, const float* initial_state, const int32_t* cu_seqlens,
+                   void* out, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_fwd(desc, q, k, v, g, beta, scale, initial_state, cu_seqlens, out, final_state, workspace,
+                   workspace_bytes, stream, nullptr, nullptr);
+}
+
+gdn_status gdn_fwd_debug(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, const float* initial_state,
+                         const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                         size_t workspace_bytes, void* stream, float* seg_state_out, int32_t* path_out) {
+    return run_fwd(desc, q, k, v, g, beta, scale, initial_state, cu_seqlens, out, final_state, workspace,
+                   workspace_bytes, stream, seg_state_out, path_out);
+}
+
+gdn_status gdn_chunk_prep(const gdn_desc* desc, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* cu_seqlens, float* gamma_out, float* W_out,
+                          float* U_out, void* stream) {
+    Plan P;
+    gdn_status st = make_plan(desc, &P);
+    if (st != GDN_OK) return st;
+    const bool varlen = desc->host_cu_seqlens != nullptr;
+    if (varlen && !cu_seqlens) return fail(GDN_ERR_NULL_ARG, "cu_seqlens is NULL but desc->host_cu_seqlens is set");
+    if (!varlen && cu_seqlens) return fail(GDN_ERR_NULL_ARG, "desc->host_cu_seqlens is required with cu_seqlens");
+    const bool any = P.n_chunks_total > 0;
+    if ((st = check_ptr(k, "k", any)) || (st = check_ptr(v, "v", any)) || (st = check_ptr(g, "g", any)) ||
+        (st = check_ptr(beta, "beta", any)) || (st = check_ptr(gamma_out, "gamma_out", any)) ||
+        (st = check_ptr(W_out, "W_out", any)) || (st = check_ptr(U_out, "U_out", any)) ||
+        (st = check_ptr(cu_seqlens, "cu_seqlens", false, 4)))
+        return st;
+    gdn::Params p = base_params(desc, P);
+    p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu = cu_seqlens;
+    p.prep_gamma = gamma_out; p.prep_W = W_out; p.prep_U = U_out;
+    const int io = desc->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
+    const int e = gdn::launch_chunk_prep(p, io, stream);
+    if (e) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString((hipError_t)e));
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL_ARG: return "GDN_ERR_NULL_ARG: a required pointer is NULL";
+        case GDN_ERR_BAD_SHAPE: return "GDN_ERR_BAD_SHAPE: inconsistent sizes";
+        case GDN_ERR_UNSUPPORTED_DIM: return "GDN_ERR_UNSUPPORTED_DIM: only d_k = d_v = 128";
+        case GDN_ERR_BAD_DTYPE: return "GDN_ERR_BAD_DTYPE: unknown io dtype";
+        case GDN_ERR_MISALIGNED: return "GDN_ERR_MISALIGNED: pointer alignment";
+        case GDN_ERR_BAD_SCALE: return "GDN_ERR_BAD_SCALE: scale is not finite";
+        case GDN_ERR_WORKSPACE_TOO_SMALL: return "GDN_ERR_WORKSPACE_TOO_SMALL";
+        case GDN_ERR_BAD_OPTION: return "GDN_ERR_BAD_OPTION: option out of range";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP runtime error";
+    }
+    return "unknown gdn_status";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal launch parameters shared by the host code (gdn_api.cpp) and the
+// kernels (gdn_kernels.hip). Not part of the public ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kDim = 128;    // d_k == d_v
+
+struct Params {
+    // inputs
+    const void* q;            // [tokens][h_qk][128]
+    const void* k;
+    const void* v;            // [tokens][h_v][128]
+    const float* g;           // [tokens][h_v]
+    const float* beta;        // [tokens][h_v]
+    const float* s_init;      // [n_seqs][h_v][128][128] or null (zeros)
+    const int32_t* cu;        // [n_seqs + 1] or null (uniform sequences of seq_len)
+    // outputs
+    void* out;                // [tokens][h_v][128]
+    float* s_final;           // [n_seqs][h_v][128][128] or null
+    // workspace (segments numbered sequence by sequence)
+    float* seg_state;         // [n_segments][h_v][128][128] initial state of segment s >= 1
+    float* seg_M;             // [n_segments][h_v][128][128] state map of segment s: S -> M S + H
+    float* seg_H;
+    int32_t* warm;            // [n_segments][h_v] 1 if the boundary before segment s warms up
+    // low-level chunk-prep outputs
+    float* prep_gamma;        // [n_chunks][h_v][64]
+    float* prep_W;            // [n_chunks][h_v][64][128]
+    float* prep_U;
+    // sizes and options
+    int32_t n_seqs;
+    int32_t seq_len;          // tokens per sequence when cu == null
+    int32_t h_qk, h_v, group; // group = h_v / h_qk
+    int32_t L;                // chunks per segment
+    int32_t w;                // warm-up chunks
+    int32_t cp_mode;          // gdn_cp_mode
+    int32_t n_segments;
+    int32_t n_chunks;
+    float log_eps;            // log(noise floor)
+    float scale;
+};
+
+enum IoType { kIoBf16 = 0, kIoF32 = 1 };
+
+// Kernel launchers (gdn_kernels.hip). Return 0 or a hipError_t value.
+int launch_chunk_prep(const Params& p, int io, void* stream);
+int launch_cp_prep(const Params& p, int io, void* stream);
+int launch_cp_combine(const Params& p, void* stream);
+int launch_fwd(const Params& p, int io, void* stream);
+int launch_debug_path(const Params& p, int32_t* path_out, void* stream);
+
+}  // namespace gdn

@@ -1,0 +1,174 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet chunked-prefill forward for AMD MI355X
+ * (gfx950), with gate-driven intra-card context parallelism.
+ *
+ * Sources (the FlashQLA pages, "FlashQLA: CP-/Bwd-friendly fused linear
+ * attention kernels for GDN"):
+ *   - section on optimising GDN chunked prefill: the prefill evaluates the
+ *     Gated DeltaNet recurrence chunk by chunk; the intermediates W, U and S
+ *     should not round-trip through HBM, and the per-(batch, head) recurrence
+ *     alone cannot fill the GPU at small batch or under tensor parallelism;
+ *   - section "Gate-Driven Automatic Intra-Card Context Parallelism (AutoCP)":
+ *     each sequence is cut into segments ("CP ranks") of L = lambda * sqrt(N)
+ *     chunks (N = chunks in the sequence); a segment's initial state comes from
+ *     the exact correction matrix M or, for heads whose gate decay drives the
+ *     old state below a noise floor, from a 6-8 chunk warm-up;
+ *   - section "Implementation & requirements": a high-level API with FLA's
+ *     argument order plus low-level entry points.
+ * The recurrence (gated delta rule, state stored d_k x d_v):
+ *     S_t = exp(g_t) S_{t-1} + beta_t k_t (v_t - exp(g_t) S_{t-1}^T k_t)^T
+ *     o_t = scale * S_t^T q_t
+ * Value head h reads query/key head h / (h_v / h_qk).
+ *
+ * Every entry point returns a gdn_status; none throws or aborts. A failed call
+ * leaves a message readable with gdn_last_error() (per thread). Calls that
+ * launch work do so asynchronously on the caller's HIP stream and never
+ * synchronise the host; faults inside kernels surface at the caller's next
+ * synchronisation. The library keeps no pointer after a call returns and
+ * allocates no device memory: all scratch lives in the caller's workspace.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_ARG = 1,        /* a required pointer is NULL */
+    GDN_ERR_BAD_SHAPE = 2,       /* sizes negative/inconsistent, h_v % h_qk != 0, bad seqlens */
+    GDN_ERR_UNSUPPORTED_DIM = 3, /* d_k or d_v other than 128 */
+    GDN_ERR_BAD_DTYPE = 4,       /* io_dtype not a gdn_dtype */
+    GDN_ERR_MISALIGNED = 5,      /* a tensor pointer not 16-byte aligned */
+    GDN_ERR_BAD_SCALE = 6,       /* scale not finite */
+    GDN_ERR_WORKSPACE_TOO_SMALL = 7,
+    GDN_ERR_BAD_OPTION = 8,      /* cp_mode, lambda, warmup_chunks or noise_floor out of range */
+    GDN_ERR_HIP = 9              /* a HIP runtime call or kernel launch failed */
+} gdn_status;
+
+/* Element type of q, k, v and out. g, beta and every state are always fp32. */
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* How segment initial states are obtained when a sequence is split. */
+typedef enum {
+    GDN_CP_AUTO = 0,    /* split only if (sequences x heads) leave CUs idle; path per head from the gates */
+    GDN_CP_OFF = 1,     /* one segment per sequence */
+    GDN_CP_EXACT = 2,   /* split; every head uses the exact (M, H) composition */
+    GDN_CP_WARMUP = 3   /* split; every head uses the warm-up (approximate for slow-decay heads) */
+} gdn_cp_mode;
+
+/* Problem descriptor.
+ * Layouts (row-major, contiguous):
+ *   q, k          [B, T, h_qk, d_k]      io_dtype
+ *   v, out        [B, T, h_v, d_v]       io_dtype
+ *   g, beta       [B, T, h_v]            fp32; g = log(alpha) must be finite and <= 0
+ *   states        [n_seqs, h_v, d_k, d_v] fp32 (initial_state, final_state)
+ *   cu_seqlens    [n_seqs + 1] int32 token offsets, 0 = c_0 <= c_1 <= ... = T;
+ *                 only with B == 1 (packed variable-length sequences).
+ * Without cu_seqlens the B rows are the sequences (n_seqs == B). */
+typedef struct {
+    int32_t B, T, h_qk, h_v, d_k, d_v;
+    int32_t n_seqs;                    /* B, or len(cu_seqlens) - 1 */
+    const int32_t* host_cu_seqlens;    /* host copy of cu_seqlens; set = packed sequences */
+    int32_t io_dtype;                  /* gdn_dtype */
+    int32_t cp_mode;                   /* gdn_cp_mode */
+    float lambda;                      /* L = lambda * sqrt(N); 0 = library default */
+    int32_t warmup_chunks;             /* warm-up window in chunks, 1..8; 0 = default (6) */
+    float noise_floor;                 /* warm-up accepted if window decay <= this; 0 = default 1e-4 */
+    int32_t n_cu;                      /* compute units to plan for; 0 = query the current device */
+} gdn_desc;
+
+/* Result of planning (host-only arithmetic on the descriptor). */
+typedef struct {
+    int32_t chunk;           /* chunk length in tokens (64) */
+    int32_t n_chunks_total;  /* chunks over all sequences */
+    int32_t n_chunks_max;    /* chunks of the longest sequence (N in L = lambda sqrt(N)) */
+    int32_t cp_on;           /* 1 if any sequence is split into more than one segment */
+    int32_t L;               /* chunks per segment */
+    int32_t n_segments;      /* segments over all sequences (workgroups per head in the forward) */
+    int32_t P_max;           /* most segments of one sequence */
+    int32_t warmup_chunks;
+    int32_t n_cu;
+    float lambda;
+    float noise_floor;
+    size_t workspace_bytes;  /* what gdn_fwd needs for this descriptor */
+} gdn_plan_info;
+
+/* Plan a forward: chunk counts, segment length L and workspace size.
+ * Host arithmetic only, except that n_cu == 0 queries the current device's
+ * compute-unit count. */
+gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out);
+
+/* Workspace bytes gdn_fwd needs for desc (0 and a message on an invalid desc). */
+size_t gdn_fwd_workspace_bytes(const gdn_desc* desc);
+
+/* The forward pass (the chunked-prefill forward of the FlashQLA pages, section on
+ * optimising GDN chunked prefill, with the AutoCP split of the AutoCP section).
+ *   q, k, v, g, beta   device inputs (layouts above), 16-byte aligned
+ *   scale              read-out scale (callers usually pass d_k^-1/2)
+ *   initial_state      device [n_seqs, h_v, d_k, d_v] fp32, or NULL for zeros
+ *   cu_seqlens         device int32 [n_seqs + 1]; required exactly when
+ *                      desc->host_cu_seqlens is set (the same values on the host)
+ *   out                device output, same layout and dtype as v
+ *   final_state        device [n_seqs, h_v, d_k, d_v] fp32, or NULL to skip
+ *   workspace          device scratch of at least gdn_fwd_workspace_bytes(desc) bytes,
+ *                      256-byte aligned; its contents on entry are ignored
+ *   stream             the hipStream_t to launch on (NULL = default stream)
+ * All buffers stay owned by the caller and must stay valid until the stream
+ * has run the launched kernels. Arguments are validated before any launch. */
+gdn_status gdn_fwd(const gdn_desc* desc,
+                   const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, float scale,
+                   const float* initial_state, const int32_t* cu_seqlens,
+                   void* out, float* final_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* gdn_fwd, then copies of what the context-parallel step decided (section
+ * "Gate-Driven Automatic Intra-Card Context Parallelism (AutoCP)"):
+ *   seg_state_out  device fp32 [n_segments, h_v, d_k, d_v]: the initial state of
+ *                  every segment (segments numbered sequence by sequence) as the
+ *                  forward used it; NULL to skip
+ *   path_out       device int32 [n_seqs, h_v], over the boundaries whose
+ *                  warm-up window does not reach the sequence start (those
+ *                  warm up from the initial state, which is exact):
+ *                  1 = all warmed up, 0 = all exact, 2 = mixed, 3 = no such
+ *                  boundary, -1 = the sequence was not split; NULL to skip
+ * Same ownership and error behaviour as gdn_fwd. */
+gdn_status gdn_fwd_debug(const gdn_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float scale,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         void* out, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         float* seg_state_out, int32_t* path_out);
+
+/* Low-level entry: the chunk-preparation step alone (gate cumsum, masked
+ * beta K K^T, triangular inverse, WY factors; the "fused kernel 1" role of the
+ * section on optimising GDN chunked prefill), written out for inspection:
+ *   gamma_out  device fp32 [n_chunks_total, h_v, 64]: chunk-local cumulative sum of g
+ *   W_out      device fp32 [n_chunks_total, h_v, 64, d_k]: T diag(beta exp(gamma)) K
+ *   U_out      device fp32 [n_chunks_total, h_v, 64, d_v]: T diag(beta) V
+ * with T = (I + A)^-1, A[i][j] = beta_i exp(gamma_i - gamma_j) k_i.k_j for i > j.
+ * Chunks are numbered sequence by sequence; rows past the end of a short final
+ * chunk are what zero padding (g = beta = 0, k = v = 0) gives. The forward
+ * itself never writes these to memory. */
+gdn_status gdn_chunk_prep(const gdn_desc* desc,
+                          const void* k, const void* v,
+                          const float* g, const float* beta, const int32_t* cu_seqlens,
+                          float* gamma_out, float* W_out, float* U_out, void* stream);
+
+/* Static text for a status code. */
+const char* gdn_status_string(gdn_status status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */
