@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark: Gated DeltaNet chunked-prefill forward on one MI355X.
+
+One step = one call of the library's forward (cp_prep, cp_combine and the fused
+forward kernel) over one batch of seeded synthetic input already resident in
+HBM. Before every step a 1 GiB fill evicts the L2 caches and the 256 MB
+Infinity Cache (outside the measured interval); each step's GPU time comes
+from HIP events the library records on the call's stream around its own
+kernels. The default workload is the TP8-shaped prompt (B=1, T=32768, h_qk=2,
+h_v=8, d=128, chunk 64, bf16 inputs, 70 % fast-decay heads).
+
+Prints one JSON line. Besides the contract fields it carries:
+  roofline      the forward kernel's algorithmic HBM bytes / its measured time
+  cpu_baseline  the fp64 CPU oracle timed on the host cores on a token prefix
+  parity        GPU output vs that oracle on the same prefix
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN fwd ms & tokens/s at B=1,T=32768 per head config; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def algorithmic_bytes(B, T, h_qk, h_v, d=128, e_io=2, initial=False, final=True, n_seqs=None):
+    """What the forward must move: q, k (per query/key head), v, out (per value
+    head), g and beta, plus the states it reads and writes."""
+    n_seqs = B if n_seqs is None else n_seqs
+    per_token = 2 * h_qk * d * e_io + 2 * h_v * d * e_io + 8 * h_v
+    return B * T * per_token + (int(initial) + int(final)) * n_seqs * h_v * d * d * 4
+
+
+def algorithmic_flops(B, T, h_qk, h_v, d=128, C=64):
+    """Per token and value head: 6 d^2 (W S, Q S, K^T V'), C (d + 2 d) (triangular
+    T X for W and U, causal P V'), 2 C d h_qk/h_v (K K^T and Q K^T lower halves,
+    shared by the head group), 2 C^2 / 3 (64 x 64 triangular inverse)."""
+    per = 6 * d * d + C * (d + 2 * d) + 2 * C * d * h_qk / h_v + 2 * C * C / 3
+    return B * T * h_v * per
+
+
+def cores_available():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="tp8",
+                    choices=["tiny", "tp8", "tp2", "tp1", "tp1_b4", "long"])
+    ap.add_argument("--cp-mode", default="auto", choices=["auto", "off", "exact", "warmup"])
+    ap.add_argument("--lam", type=float, default=0.0)
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
+                    help="tokens of sequence 0 the CPU oracle runs (0 = skip)")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_chunked_03_amd as gdn
+    from gated_deltanet_chunked_03_amd.synth import CONFIGS, config_inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_gen = time.time()
+    inp = config_inputs(args.config)
+    print(f"[bench] generated {args.config} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    dt = torch.bfloat16 if inp.io_dtype == "bf16" else torch.float32
+    dv = lambda a, d=torch.float32: torch.from_numpy(a).to(device=dev, dtype=d)  # noqa: E731
+    q, k, v = dv(inp.q, dt), dv(inp.k, dt), dv(inp.v, dt)
+    g, beta = dv(inp.g), dv(inp.beta)
+    s0 = None if inp.initial_state is None else dv(inp.initial_state)
+    B, T, h_qk, h_v = inp.B, inp.T, inp.h_qk, inp.h_v
+    n_seqs = inp.n_seqs
+    out = torch.empty_like(v)
+    fs = torch.empty((n_seqs, h_v, 128, 128), dtype=torch.float32, device=dev)
+    pl = gdn.plan(B, T, h_qk, h_v, io_dtype=0 if inp.io_dtype == "bf16" else 1,
+                  cp_mode=args.cp_mode, lam=args.lam)
+    ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step():
+        gdn.fwd(q, k, v, g, beta, scale=inp.scale, initial_state=s0, cp_mode=args.cp_mode,
+                lam=args.lam, workspace=ws, out=out, final_state=fs)
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.zero_()
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, plan L={pl['L']} segments={pl['n_segments']}",
+          file=sys.stderr, flush=True)
+
+    gdn.profile_enable(True)
+    per = {"cp_prep": [], "cp_combine": [], "fwd": [], "total": []}
+    torch.cuda.synchronize()
+    t0 = time.time()
+    for _ in range(args.steps):
+        if not args.no_flush:
+            flush.zero_()
+        step()
+        for key, val in gdn.profile_read().items():
+            per[key].append(val)
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    # warm-cache figure (no flush), for reference
+    warm = []
+    for _ in range(max(3, args.steps // 2)):
+        step()
+        warm.append(gdn.profile_read()["total"])
+    gdn.profile_enable(False)
+    print(f"[bench] timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
+
+    mean = {key: float(np.mean(vals)) for key, vals in per.items()}
+    ms = mean["total"]
+    tokens = B * T
+    value = tokens / (ms * 1e-3)
+    nbytes = algorithmic_bytes(B, T, h_qk, h_v, e_io=2 if inp.io_dtype == "bf16" else 4,
+                               initial=s0 is not None, final=True, n_seqs=n_seqs)
+    flops = algorithmic_flops(B, T, h_qk, h_v)
+    fwd_s = mean["fwd"] * 1e-3
+    achieved = nbytes / fwd_s / 1e9
+    roofline = {"bound": "hbm", "kernel": "k_fwd", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_bytes": nbytes}
+    mfma = {"algorithmic_tflops_fwd_kernel": round(flops / fwd_s / 1e12, 2),
+            "peak_tflops_bf16": MFMA_BF16_PEAK_TFLOPS,
+            "frac_algorithmic": round(flops / fwd_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_gflop": round(flops / 1e9, 2)}
+
+    cpu = None
+    parity = None
+    if args.cpu_tokens > 0:
+        from oracle import gdn_sequential
+        n_tok = min(args.cpu_tokens, T if inp.cu_seqlens is None else int(inp.cu_seqlens[1]))
+        threads = max(1, min(cores_available(), 16, h_v))
+        qf, kf, vf, gf, bf = (a[:n_tok] for a in inp.flat())
+        s0_np = None if inp.initial_state is None else inp.initial_state[:1]
+        t1 = time.time()
+        o_ref, _, _ = gdn_sequential(qf, kf, vf, gf, bf, inp.scale, s0_np, None, n_threads=threads)
+        cpu_s = time.time() - t1
+        cpu = {"value": round(n_tok / cpu_s, 1), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"first {n_tok} tokens of sequence 0, all {h_v} value heads, fp64 "
+                         f"token-by-token recurrence, one thread per head ({cpu_s:.1f}s wall)"}
+        o_gpu = out[0, :n_tok].float().cpu().numpy().astype(np.float64)
+        d = np.abs(o_gpu - o_ref)
+        parity = {"tokens": n_tok, "max_rel": float(d.max() / np.abs(o_ref).max()),
+                  "mean_rel_l1": float(d.sum() / np.abs(o_ref).sum()),
+                  "tol_max_rel": 1e-2, "tol_mean_rel": 2e-3}
+
+    cfg = CONFIGS[args.config]
+    workload = (f"{args.config}: B={B} T={T} h_qk={h_qk} h_v={h_v} d_k=d_v=128 chunk=64 "
+                f"{inp.io_dtype} inputs, fp32 state, heads {','.join(inp.head_class)}")
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": workload, "B": B, "T": T, "h_qk": h_qk, "h_v": h_v, "d": 128,
+                   "chunk": 64, "cp_mode": args.cp_mode, "seed": cfg["seed"]},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "kernels_ms": {key: round(val, 4) for key, val in mean.items()},
+        "warm_cache_ms_per_step": round(float(np.mean(warm)), 4),
+        "mfma": mfma, "parity": parity,
+        "plan": {key: pl[key] for key in ("L", "n_segments", "P_max", "cp_on", "warmup_chunks",
+                                          "n_cu", "lambda")},
+        "precision": "bf16 MFMA operands, fp32 accumulation; non-input operands split hi+lo",
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

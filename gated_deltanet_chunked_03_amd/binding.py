@@ -23,7 +23,7 @@ CP_MODES = {"auto": 0, "off": 1, "exact": 2, "warmup": 3}
 GDN_BF16, GDN_F32 = 0, 1
 
 EXPORTED = ["gdn_plan", "gdn_fwd_workspace_bytes", "gdn_fwd", "gdn_fwd_debug", "gdn_chunk_prep",
-            "gdn_status_string", "gdn_last_error"]
+            "gdn_profile_enable", "gdn_profile_read", "gdn_status_string", "gdn_last_error"]
 
 
 class GdnDesc(ctypes.Structure):
@@ -85,6 +85,10 @@ def load_library(path: Optional[str] = None):
         lib.gdn_fwd_debug.restype = S
         lib.gdn_chunk_prep.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, P, P, P, P]
         lib.gdn_chunk_prep.restype = S
+        lib.gdn_profile_enable.argtypes = [ctypes.c_int]
+        lib.gdn_profile_enable.restype = S
+        lib.gdn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float)]
+        lib.gdn_profile_read.restype = S
         lib.gdn_status_string.argtypes = [S]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_last_error.argtypes = []
@@ -237,6 +241,20 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=Tru
     _check(lib, lib.gdn_fwd_debug(*args, _ptr(seg), _ptr(path)))
     del keep
     return out, fs, {"plan": info, "seg_state": seg, "path": path}
+
+
+def profile_enable(on=True):
+    """Record HIP events around each kernel of later fwd calls (measurement only)."""
+    lib = load_library()
+    _check(lib, lib.gdn_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """Milliseconds of the last profiled fwd call: dict cp_prep, cp_combine, fwd, total."""
+    lib = load_library()
+    ms = (ctypes.c_float * 4)()
+    _check(lib, lib.gdn_profile_read(ms))
+    return {"cp_prep": ms[0], "cp_combine": ms[1], "fwd": ms[2], "total": ms[3]}
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,

@@ -161,6 +161,17 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
     return GDN_OK;
 }
 
+// Profiling events (gdn_profile_enable / gdn_profile_read).
+struct Profiler {
+    bool on = false, created = false, recorded = false, ran[3] = {false, false, false};
+    hipEvent_t ev[4];
+};
+Profiler g_prof;
+
+void prof_mark(int i, hipStream_t s) {
+    if (g_prof.on) (void)hipEventRecord(g_prof.ev[i], s);
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 gdn_status check_ptr(const void* p, const char* name, bool required, size_t align = 16) {
@@ -221,15 +232,25 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
         p.warm = reinterpret_cast<int32_t*>(w8 + P.off_warm);
     }
     const int io = d->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
+    const hipStream_t hs = (hipStream_t)stream;
     int e;
+    prof_mark(0, hs);
     if (P.cp_on) {
         if ((e = gdn::launch_cp_prep(p, io, stream)))
             return fail(GDN_ERR_HIP, "cp_prep launch: %s", hipGetErrorString((hipError_t)e));
+        prof_mark(1, hs);
         if ((e = gdn::launch_cp_combine(p, stream)))
             return fail(GDN_ERR_HIP, "cp_combine launch: %s", hipGetErrorString((hipError_t)e));
+        prof_mark(2, hs);
     }
     if ((e = gdn::launch_fwd(p, io, stream)))
         return fail(GDN_ERR_HIP, "fwd launch: %s", hipGetErrorString((hipError_t)e));
+    prof_mark(3, hs);
+    if (g_prof.on) {
+        g_prof.recorded = true;
+        g_prof.ran[0] = g_prof.ran[1] = P.cp_on != 0;
+        g_prof.ran[2] = true;
+    }
 
     if (seg_out || path_out) {
         hipStream_t s = (hipStream_t)stream;
@@ -325,6 +346,37 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc, const void* k, const void* v, co
     const int io = desc->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
     const int e = gdn::launch_chunk_prep(p, io, stream);
     if (e) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString((hipError_t)e));
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+gdn_status gdn_profile_enable(int on) {
+    if (on && !g_prof.created) {
+        for (int i = 0; i < 4; ++i) {
+            const hipError_t e = hipEventCreate(&g_prof.ev[i]);
+            if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+        }
+        g_prof.created = true;
+    }
+    g_prof.on = on != 0;
+    g_prof.recorded = false;
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+gdn_status gdn_profile_read(float ms[4]) {
+    if (!ms) return fail(GDN_ERR_NULL_ARG, "ms is NULL");
+    if (!g_prof.recorded) return fail(GDN_ERR_BAD_OPTION, "no profiled call since gdn_profile_enable");
+    hipError_t e = hipEventSynchronize(g_prof.ev[3]);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    const int from[4] = {0, 1, 2, 0}, to[4] = {1, 2, 3, 3};
+    for (int i = 0; i < 4; ++i) {
+        ms[i] = 0.f;
+        if (i < 3 && !g_prof.ran[i]) continue;
+        const int a = (i == 2 && !g_prof.ran[0]) ? 0 : from[i];
+        e = hipEventElapsedTime(&ms[i], g_prof.ev[a], g_prof.ev[to[i]]);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+    }
     g_last_error.clear();
     return GDN_OK;
 }

@@ -49,15 +49,21 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int CH = kChunk;
 constexpr int DK = kDim;
 constexpr int NTHR = 256;
-constexpr int LDQ = 132;   // row stride (elements) of [64][128] bf16 tiles
-constexpr int LDKT = 68;   // row stride of [128][64] bf16 tiles
+constexpr int LDQ = 136;   // row stride (elements) of [64][128] bf16 tiles
+constexpr int LDKT = 72;   // row stride of [128][64] bf16 tiles
 constexpr int LDF = 68;    // row stride of [64][64] fp32 tiles
-constexpr int LDP = 68;    // row stride of [64][64] bf16 tiles
+constexpr int LDP = 72;    // row stride of [64][64] bf16 tiles
 constexpr int LDC = 132;   // row stride of the combine kernel's [32][128] fp32 tile
+constexpr int LDO = 136;   // row stride of the staged [64][128] bf16 output tile
+constexpr int kMaxFlags = 2048;  // boundary flags the combine kernel keeps in LDS
 
 enum { kCpAuto = 0, kCpOff = 1, kCpExact = 2, kCpWarmup = 3 };
 
@@ -76,31 +82,56 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ f32x4 mma16k32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The lane index passes through an empty asm, so that the LDS addresses
+// derived from it are formed in the function that uses them: otherwise the
+// compiler hoists hundreds of loop-invariant addresses out of the chunk loop
+// and spills them to scratch. The wave index is wave-uniform (a scalar).
+__device__ __forceinline__ int lane_id() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+}
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Row of accumulator element i for lane half h (32x32 tiles).
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
+// hi/lo splits. hi is x with its low 16 bits cleared (a bf16 value), lo is
+// x - hi (exact in fp32) rounded to nearest bf16, so hi + lo = x to within
+// 2^-16 |x|.
+__device__ __forceinline__ unsigned pack_rne(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+    const unsigned u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+    hi = (u0 >> 16) | (u1 & 0xffff0000u);
+    lo = pack_rne(x0 - __uint_as_float(u0 & 0xffff0000u), x1 - __uint_as_float(u1 & 0xffff0000u));
+}
+__device__ __forceinline__ void split1(float x, bf16& hi, bf16& lo) {
+    const unsigned u = __float_as_uint(x);
+    hi = __builtin_bit_cast(bf16, (unsigned short)(u >> 16));
+    lo = (bf16)(x - __uint_as_float(u & 0xffff0000u));
+}
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16 t = (bf16)x[e];
-        hi[e] = t;
-        lo[e] = (bf16)(x[e] - (float)t);
-    }
+    unsigned h0, h1, l0, l1;
+    split_pair(x[0], x[1], h0, l0);
+    split_pair(x[2], x[3], h1, l1);
+    hi = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
+    lo = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
 }
 
 // Elements [B, B + 8) of an accumulator tile as a hi/lo B operand.
 template <int B>
 __device__ __forceinline__ void split_acc(const f32x16& a, bf16x8& hi, bf16x8& lo) {
+    unsigned h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = a[B + e];
-        const bf16 t = (bf16)x;
-        hi[e] = t;
-        lo[e] = (bf16)(x - (float)t);
-    }
+    for (int e = 0; e < 4; ++e) split_pair(a[B + 2 * e], a[B + 2 * e + 1], h[e], l[e]);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
 __device__ __forceinline__ void split_half(const f32x16& a, int half, bf16x8& hi, bf16x8& lo) {
@@ -108,11 +139,16 @@ __device__ __forceinline__ void split_half(const f32x16& a, int half, bf16x8& hi
     else split_acc<0>(a, hi, lo);
 }
 
-// Operand from a bf16 row: p = row start + kb + 4h; elements p[0..3], p[8..11].
-__device__ __forceinline__ bf16x8 lds_op(const bf16* p) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 8);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+// bf16 operand tiles in LDS keep their contraction (k) axis in a permuted
+// order: within every group of 16, the 4-element blocks 1 and 2 trade places.
+// Then the 8 values lane half h needs for one k step (k = kb + kperm(h, e))
+// sit contiguously at kb + 8 h and come in one 16-byte read.
+__device__ __forceinline__ int pk(int k) {
+    const int b = (k >> 2) & 3;
+    return (k & ~12) | ((b == 1 ? 2 : (b == 2 ? 1 : b)) << 2);
+}
+__device__ __forceinline__ bf16x8 lds_op16(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
 }
 
 // Operand from an fp32 row (same element placement), optionally times a
@@ -132,28 +168,6 @@ __device__ __forceinline__ void f32_op(const float* p, const float* sc, bf16x8& 
     lo = __builtin_shufflevector(al, bl, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Operand from a global row of 128 io elements (row read as zero if !valid).
-__device__ __forceinline__ void g_row_op(const bf16* rowp, bool valid, int kb, int h,
-                                         bf16x8& hi, bf16x8& lo) {
-    if (valid) {
-        hi = lds_op(rowp + kb + 4 * h);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) hi[e] = (bf16)0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lo[e] = (bf16)0.f;
-}
-__device__ __forceinline__ void g_row_op(const float* rowp, bool valid, int kb, int h,
-                                         bf16x8& hi, bf16x8& lo) {
-    if (valid) {
-        f32_op<false>(rowp + kb + 4 * h, nullptr, hi, lo);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { hi[e] = (bf16)0.f; lo[e] = (bf16)0.f; }
-    }
-}
-
 // B operand from one column of a token-major global tile: element e is token
 // kb + kperm(h, e); tokens >= nvalid read as zero.
 template <typename IO>
@@ -163,9 +177,15 @@ __device__ __forceinline__ void g_col_op(const IO* col0, size_t ts, int kb, int 
     for (int e = 0; e < 8; ++e) {
         const int t = kb + ((e < 4) ? (4 * h + e) : (4 + 4 * h + e));
         const float x = (t < nvalid) ? (float)col0[(size_t)t * ts] : 0.f;
-        const bf16 th = (bf16)x;
-        hi[e] = th;
-        lo[e] = Io<IO>::kExact ? (bf16)0.f : (bf16)(x - (float)th);
+        if (Io<IO>::kExact) {
+            hi[e] = (bf16)x;
+            lo[e] = (bf16)0.f;
+        } else {
+            bf16 th, tl;
+            split1(x, th, tl);
+            hi[e] = th;
+            lo[e] = tl;
+        }
     }
 }
 
@@ -178,9 +198,15 @@ struct __attribute__((aligned(16))) Smem {
     bf16 q_lo[EX ? 8 : CH * LDQ];
     bf16 kt_hi[DK * LDKT];                // K chunk transposed: [d_k][token]
     bf16 kt_lo[EX ? 8 : DK * LDKT];
+    bf16 vt[EX ? DK * LDKT : 8];          // V chunk transposed (bf16 inputs; fp32 V is read from HBM)
     bf16 p_hi[CH * LDP];                  // P = (Q K^T) o D, causal, split
     bf16 p_lo[CH * LDP];
-    float t[CH * LDF];                    // T = (I + A)^-1
+    bf16 tw[EX ? 2 * CH * LDP : 8];       // T diag(beta e^gamma), hi rows then lo rows
+    bf16 tu[EX ? 2 * CH * LDP : 8];       // T diag(beta), hi rows then lo rows
+    union {
+        float t[CH * LDF];                // T = (I + A)^-1
+        bf16 k_rm[EX ? CH * LDQ : 8];     // K chunk token-major, until the gram products are done
+    } u;
     union {
         float a[CH * LDF];                // A (strictly lower), until T is built
         bf16 w[2 * CH * LDQ];             // -W split: hi rows then lo rows
@@ -264,143 +290,260 @@ __device__ bool locate_chunk(const Params& p, int slot, int& seq, int& c, int& l
 // ----------------------------------------------------------------------------
 // Chunk preparation: load, gamma, gram products, inverse, W and U
 
-// Loads K (transposed into kt), optionally Q, and the gates of one chunk.
-// Token rows >= nvalid are zero padding (and g = beta = 0 there).
+// One chunk's inputs in registers between the global load and the LDS store
+// (so the next chunk's loads overlap the current chunk's work). Thread t
+// holds pieces t + 256 j (j < 4): token row (piece / 16), columns
+// 8 (piece % 16) .. + 8 of K, Q and V, so sixteen lanes cover one 256-byte row.
+template <typename IO> struct Chunk;
+template <> struct Chunk<bf16> { u32x4 k[4], q[4], v[4]; float g, b; };
+template <> struct Chunk<float> { f32x4 k[8], q[8]; float g, b; };
+
 template <typename IO, bool WANT_Q>
-__device__ void load_chunk(Smem<Io<IO>::kExact>& sm, const Params& p, size_t tok0, int nvalid,
-                           int h, int hq) {
+__device__ __forceinline__ void fetch_chunk(Chunk<IO>& r, const Params& p, size_t tok0, int nvalid,
+                                            int h, int hq) {
     constexpr bool EX = Io<IO>::kExact;
-    const int tid = threadIdx.x;
-    const size_t ts = (size_t)p.h_qk * DK;
+    const int t = threadIdx.x;
+    const size_t ts = (size_t)p.h_qk * DK, tsv = (size_t)p.h_v * DK;
     const IO* kb = static_cast<const IO*>(p.k) + tok0 * ts + (size_t)hq * DK;
     const IO* qb = static_cast<const IO*>(p.q) + tok0 * ts + (size_t)hq * DK;
+    const IO* vb = static_cast<const IO*>(p.v) + tok0 * tsv + (size_t)h * DK;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int pc = tid + NTHR * it;
-        const int row = pc >> 4, c8 = (pc & 15) * 8;
-        float kv[8], qv[8];
-        if (row < nvalid) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kv[e] = (float)kb[(size_t)row * ts + c8 + e];
+    for (int j = 0; j < 4; ++j) {
+        const int pc = t + NTHR * j, row = pc >> 4, c8 = (pc & 15) * 8;
+        const bool ok = row < nvalid;
+        if constexpr (EX) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            r.k[j] = ok ? *reinterpret_cast<const u32x4*>(kb + row * ts + c8) : z;
+            if (WANT_Q) r.q[j] = ok ? *reinterpret_cast<const u32x4*>(qb + row * ts + c8) : z;
+            r.v[j] = ok ? *reinterpret_cast<const u32x4*>(vb + row * tsv + c8) : z;
+        } else {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            r.k[2 * j] = ok ? *reinterpret_cast<const f32x4*>(kb + row * ts + c8) : z;
+            r.k[2 * j + 1] = ok ? *reinterpret_cast<const f32x4*>(kb + row * ts + c8 + 4) : z;
             if (WANT_Q) {
+                r.q[2 * j] = ok ? *reinterpret_cast<const f32x4*>(qb + row * ts + c8) : z;
+                r.q[2 * j + 1] = ok ? *reinterpret_cast<const f32x4*>(qb + row * ts + c8 + 4) : z;
+            }
+        }
+    }
+    r.g = 0.f;
+    r.b = 0.f;
+    if (wave_id() == 0 && lane_id() < nvalid) {
+        const size_t idx = (tok0 + lane_id()) * (size_t)p.h_v + h;
+        r.g = p.g[idx];
+        r.b = p.beta[idx];
+    }
+}
+
+// Two bf16 of the same column from two rows packed into one 32-bit word.
+__device__ __forceinline__ unsigned int pack_col(const u32x4& a, const u32x4& b, int e) {
+    const unsigned int wa = a[e >> 1], wb = b[e >> 1];
+    return (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+}
+
+// Writes a fetched chunk to LDS and derives the gate quantities. bf16
+// inputs: K, Q and V token-major (K in the T area and V in the T'' area,
+// both free until the inverse; the gram phase transposes them); fp32 inputs: Q and K^T as hi/lo pairs. Rows
+// past the end of the sequence were fetched as zeros (g = beta = 0 there).
+template <typename IO, bool WANT_Q>
+__device__ __forceinline__ void stage_chunk(Smem<Io<IO>::kExact>& sm, const Chunk<IO>& r) {
+    constexpr bool EX = Io<IO>::kExact;
+    const int t = threadIdx.x;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] = (float)qb[(size_t)row * ts + c8 + e];
+    for (int j = 0; j < 4; ++j) {
+        const int pc = t + NTHR * j, row = pc >> 4, c8 = (pc & 15) * 8;
+        if constexpr (EX) {
+            const int o0 = row * LDQ + pk(c8), o1 = row * LDQ + pk(c8 + 4);
+            *reinterpret_cast<u32x2*>(sm.u.k_rm + o0) = u32x2{r.k[j][0], r.k[j][1]};
+            *reinterpret_cast<u32x2*>(sm.u.k_rm + o1) = u32x2{r.k[j][2], r.k[j][3]};
+            *reinterpret_cast<u32x2*>(sm.tu + o0) = u32x2{r.v[j][0], r.v[j][1]};
+            *reinterpret_cast<u32x2*>(sm.tu + o1) = u32x2{r.v[j][2], r.v[j][3]};
+            if (WANT_Q) {
+                *reinterpret_cast<u32x2*>(sm.q_hi + o0) = u32x2{r.q[j][0], r.q[j][1]};
+                *reinterpret_cast<u32x2*>(sm.q_hi + o1) = u32x2{r.q[j][2], r.q[j][3]};
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { kv[e] = 0.f; qv[e] = 0.f; }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bf16 th = (bf16)kv[e];
-            sm.kt_hi[(c8 + e) * LDKT + row] = th;
-            if (!EX) sm.kt_lo[(c8 + e) * LDKT + row] = (bf16)(kv[e] - (float)th);
-        }
-        if (WANT_Q) {
-            bf16x4 h0, h1, l0, l1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h0[e] = (bf16)qv[e];
-                h1[e] = (bf16)qv[4 + e];
-                l0[e] = (bf16)(qv[e] - (float)h0[e]);
-                l1[e] = (bf16)(qv[4 + e] - (float)h1[e]);
-            }
-            *reinterpret_cast<bf16x4*>(sm.q_hi + row * LDQ + c8) = h0;
-            *reinterpret_cast<bf16x4*>(sm.q_hi + row * LDQ + c8 + 4) = h1;
-            if (!EX) {
-                *reinterpret_cast<bf16x4*>(sm.q_lo + row * LDQ + c8) = l0;
-                *reinterpret_cast<bf16x4*>(sm.q_lo + row * LDQ + c8 + 4) = l1;
+            for (int e = 0; e < 8; ++e) {
+                bf16 th, tl;
+                split1(r.k[2 * j + (e >> 2)][e & 3], th, tl);
+                sm.kt_hi[(c8 + e) * LDKT + pk(row)] = th;
+                sm.kt_lo[(c8 + e) * LDKT + pk(row)] = tl;
+                if (WANT_Q) {
+                    split1(r.q[2 * j + (e >> 2)][e & 3], th, tl);
+                    sm.q_hi[row * LDQ + pk(c8 + e)] = th;
+                    sm.q_lo[row * LDQ + pk(c8 + e)] = tl;
+                }
             }
         }
     }
     if (wave_id() == 0) {
-        const int t = lane_id();
-        float gv = 0.f, bv = 0.f;
-        if (t < nvalid) {
-            const size_t idx = (tok0 + t) * (size_t)p.h_v + h;
-            gv = p.g[idx];
-            bv = p.beta[idx];
-        }
-        float s = gv;  // inclusive scan over the 64 lanes
+        const int lane = lane_id();
+        float s = r.g;  // inclusive scan over the 64 lanes
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const float o = __shfl_up(s, d, 64);
-            if (t >= d) s += o;
+            if (lane >= d) s += o;
         }
         const float gc = __shfl(s, 63, 64);
         const float es = __expf(s);
-        sm.gam[t] = s;
-        sm.eg[t] = es;
-        sm.egc[t] = __expf(gc - s);
-        sm.beta[t] = bv;
-        sm.bw[t] = bv * es;
-        if (t == 0) sm.red[0] = __expf(gc);
+        sm.gam[lane] = s;
+        sm.eg[lane] = es;
+        sm.egc[lane] = __expf(gc - s);
+        sm.beta[lane] = r.b;
+        sm.bw[lane] = r.b * es;
+        if (lane == 0) sm.red[0] = __expf(gc);
     }
 }
 
-// One 32x32 tile (ti, tj) of X K^T, X = K (global rows) or Q (LDS rows).
-template <typename IO, bool FROM_Q>
-__device__ f32x16 gram_tile(const Smem<Io<IO>::kExact>& sm, const IO* krow0, size_t ts, int nvalid,
-                            int ti, int tj) {
-    constexpr bool EX = Io<IO>::kExact;
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
-    const int ra = 32 * ti + col, rb = 32 * tj + col;
-    f32x16 acc = {};
+// Two bf16 of the same column from two rows packed into one 32-bit word.
+__device__ __forceinline__ unsigned pack_col(u32x2 a, u32x2 b, int e) {
+    const unsigned wa = a[e >> 1], wb = b[e >> 1];
+    return (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+}
+
+// K^T and V^T from the token-major LDS tiles (bf16 inputs; after a barrier):
+// thread t packs rows 2 (t % 32), 2 (t % 32) + 1 of column blocks t / 32 and
+// t / 32 + 8 into 32-bit words of the transposed tiles.
+__device__ __forceinline__ void transpose_kv(Smem<true>& sm) {
+    const int t = threadIdx.x, rp = t & 31, cbk = t >> 5;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 ah, al, bh, bl;
-        if (FROM_Q) {
-            ah = lds_op(sm.q_hi + ra * LDQ + 16 * ks + 4 * h);
-            if (!EX) al = lds_op(sm.q_lo + ra * LDQ + 16 * ks + 4 * h);
-        } else {
-            g_row_op(krow0 + (size_t)ra * ts, ra < nvalid, 16 * ks, h, ah, al);
-        }
-        g_row_op(krow0 + (size_t)rb * ts, rb < nvalid, 16 * ks, h, bh, bl);
-        acc = mma32(ah, bh, acc);
-        if (!EX) {
-            acc = mma32(ah, bl, acc);
-            acc = mma32(al, bh, acc);
-        }
-    }
-    return acc;
-}
-
-// A[i][j] = beta_i exp(gamma_i - gamma_j) (k_i . k_j) for i > j, else 0.
-template <bool EX>
-__device__ void store_A(Smem<EX>& sm, const f32x16& acc, int ti, int tj) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
-    const int c = 32 * tj + col;
-    const float gc = sm.gam[c];
+    for (int jb = 0; jb < 2; ++jb) {
+        const int c8 = 8 * (cbk + 8 * jb);
+        const int tp = pk(2 * rp);  // the token pair stays adjacent under the permutation
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = 32 * ti + acc_row(i, h);
-        const float d = __expf(sm.gam[r] - gc);
-        sm.x.a[r * LDF + c] = (r > c) ? sm.beta[r] * d * acc[i] : 0.f;
+        for (int half = 0; half < 2; ++half) {
+            const int o = (2 * rp) * LDQ + pk(c8 + 4 * half);
+            const u32x2 ka = *reinterpret_cast<const u32x2*>(sm.u.k_rm + o);
+            const u32x2 kb = *reinterpret_cast<const u32x2*>(sm.u.k_rm + o + LDQ);
+            const u32x2 va = *reinterpret_cast<const u32x2*>(sm.tu + o);
+            const u32x2 vb = *reinterpret_cast<const u32x2*>(sm.tu + o + LDQ);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = c8 + 4 * half + e;
+                *reinterpret_cast<unsigned*>(sm.kt_hi + c * LDKT + tp) = pack_col(ka, kb, e);
+                *reinterpret_cast<unsigned*>(sm.vt + c * LDKT + tp) = pack_col(va, vb, e);
+            }
+        }
     }
 }
 
+// Gram products on 16x16 tiles (16x16x32 MFMA; lane l: A row l % 16 and
+// B column l % 16, each with the 8 consecutive k values 8 (l / 16)..; C rows
+// 4 (l / 16).. of column l % 16). The ten lower tiles (bi >= bj) of K K^T and
+// of Q K^T are twenty jobs, run as interleaved chains. Each is computed
+// transposed (K rows of block bj against K or Q rows of block bi), so a lane
+// ends up with four consecutive columns j of one row i and stores them at once.
+__device__ __forceinline__ void lower_tile(int job, int& bi, int& bj) {
+    bi = (job >= 6) ? 3 : (job >= 3) ? 2 : (job >= 1) ? 1 : 0;
+    bj = job - (bi * (bi + 1)) / 2;
+}
+
+// The operand a gram lane group reads from a permuted LDS row (8 physical
+// elements at 8 g4 within a 32-wide k step), taken from a global fp32 row
+// instead: logical elements p[0..3] and p[8..11] with p = row + 32 ks +
+// 16 (g4 / 2) + 4 (g4 % 2). Zero if !valid.
+__device__ __forceinline__ void g_row8(const float* p, bool valid, bf16x8& hi, bf16x8& lo) {
+    if (valid) {
+        bf16x4 h0, l0, h1, l1;
+        split4(*reinterpret_cast<const f32x4*>(p), h0, l0);
+        split4(*reinterpret_cast<const f32x4*>(p + 8), h1, l1);
+        hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+        lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        hi = bf16x8{};
+        lo = bf16x8{};
+    }
+}
+__device__ __forceinline__ bf16x8 lds_row8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// A[i][j] = beta_i exp(gamma_i - gamma_j) (k_i . k_j) for i > j, else 0 (fp32), and
 // P[i][j] = exp(gamma_i - gamma_j) (q_i . k_j) for i >= j, else 0 (hi/lo bf16).
-template <bool EX>
-__device__ void store_P(Smem<EX>& sm, const f32x16& acc, int ti, int tj) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
-    const int c = 32 * tj + col;
-    const float gc = sm.gam[c];
+// Jobs first, first + stride, ... (job >= 10: the P tile job - 10).
+template <typename IO, int NJOB>
+__device__ void gram_jobs(Smem<Io<IO>::kExact>& sm, const IO* krow0, size_t ts, int nvalid, int first,
+                          int stride) {
+    constexpr bool EX = Io<IO>::kExact;
+    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
+    f32x4 acc[NJOB];
+    int bi[NJOB], bj[NJOB];
+    bool isq[NJOB];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = 32 * ti + acc_row(i, h);
-        const float d = __expf(sm.gam[r] - gc);
-        const float v = (r >= c) ? d * acc[i] : 0.f;
-        const bf16 th = (bf16)v;
-        sm.p_hi[r * LDP + c] = th;
-        sm.p_lo[r * LDP + c] = (bf16)(v - (float)th);
+    for (int t = 0; t < NJOB; ++t) {
+        const int job = first + stride * t;
+        isq[t] = job >= 10;
+        lower_tile(isq[t] ? job - 10 : job, bi[t], bj[t]);
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int kb = 32 * ks + 8 * g4;                                 // physical (LDS)
+        const int kg = 32 * ks + 16 * (g4 >> 1) + 4 * (g4 & 1);          // logical start (HBM rows)
+#pragma unroll
+        for (int t = 0; t < NJOB; ++t) {
+            const int ra = 16 * bj[t] + n, rb = 16 * bi[t] + n;   // A: K rows of bj; B: rows of bi
+            if constexpr (EX) {
+                const bf16x8 a = lds_row8(sm.u.k_rm + ra * LDQ + kb);
+                const bf16x8 b = lds_row8((isq[t] ? sm.q_hi : sm.u.k_rm) + rb * LDQ + kb);
+                acc[t] = mma16k32(a, b, acc[t]);
+            } else {
+                bf16x8 ah, al, bh, bl;
+                g_row8(krow0 + (size_t)ra * ts + kg, ra < nvalid, ah, al);
+                if (isq[t]) {
+                    bh = lds_row8(sm.q_hi + rb * LDQ + kb);
+                    bl = lds_row8(sm.q_lo + rb * LDQ + kb);
+                } else {
+                    g_row8(krow0 + (size_t)rb * ts + kg, rb < nvalid, bh, bl);
+                }
+                acc[t] = mma16k32(ah, bh, acc[t]);
+                acc[t] = mma16k32(ah, bl, acc[t]);
+                acc[t] = mma16k32(al, bh, acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NJOB; ++t) {
+        const int i = 16 * bi[t] + n, j0 = 16 * bj[t] + 4 * g4;   // row i, columns j0 .. j0 + 3
+        const float gi = sm.gam[i];
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(sm.gam + j0);
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float d = __expf(gi - gj[r]);
+            v[r] = isq[t] ? ((i >= j0 + r) ? d * acc[t][r] : 0.f) : ((i > j0 + r) ? d * acc[t][r] : 0.f);
+        }
+        if (!isq[t]) {
+            *reinterpret_cast<f32x4*>(sm.x.a + i * LDF + j0) = v * sm.beta[i];
+        } else {
+            unsigned h0, h1, l0, l1;
+            split_pair(v[0], v[1], h0, l0);
+            split_pair(v[2], v[3], h1, l1);
+            *reinterpret_cast<u32x2*>(sm.p_hi + i * LDP + pk(j0)) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(sm.p_lo + i * LDP + pk(j0)) = u32x2{l0, l1};
+        }
     }
 }
 
-// Diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution, one block
-// per wave; lane j < 16 solves column j.
+// Zero P on the upper 16x16 tile of a diagonal 32x32 block (read by the P V' product).
+template <bool EX>
+__device__ void zero_p_tile(Smem<EX>& sm, int bi, int bj) {
+    const int lane = lane_id();
+    const bf16 z = (bf16)0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = lane + 64 * e, r = 16 * bi + (idx >> 4), c = 16 * bj + (idx & 15);
+        sm.p_hi[r * LDP + pk(c)] = z;
+        sm.p_lo[r * LDP + pk(c)] = z;
+    }
+}
+
+// Diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution. Every
+// wave solves all four blocks (lane 16 b + j: block b, column j) and writes
+// them; the values are identical across waves, so each wave can read the
+// blocks back without waiting for the others.
 template <bool EX>
 __device__ void inv_diag(Smem<EX>& sm) {
-    const int lane = lane_id(), b = 16 * wave_id(), j = lane & 15;
+    const int lane = lane_id(), b = 16 * (lane >> 4), j = lane & 15;
     const float* A = sm.x.a + b * LDF + b;
     float x[16];
 #pragma unroll
@@ -410,10 +553,8 @@ __device__ void inv_diag(Smem<EX>& sm) {
         for (int m = 0; m < i; ++m) s = fmaf(-A[i * LDF + m], x[m], s);
         x[i] = s;
     }
-    if (lane < 16) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.t[(b + i) * LDF + b + j] = x[i];
-    }
+    for (int i = 0; i < 16; ++i) sm.u.t[(b + i) * LDF + b + j] = x[i];
 }
 
 // Block column J of T below the diagonal: T_iJ = -X_i sum_{m=J}^{i-1} A_im T_mJ,
@@ -424,7 +565,7 @@ __device__ void inv_col(Smem<EX>& sm) {
     const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
     f32x4 Tc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Tc[J][r] = sm.t[(16 * J + 4 * g4 + r) * LDF + 16 * J + n];
+    for (int r = 0; r < 4; ++r) Tc[J][r] = sm.u.t[(16 * J + 4 * g4 + r) * LDF + 16 * J + n];
 #pragma unroll
     for (int i = J + 1; i < 4; ++i) {
         f32x4 R = {0.f, 0.f, 0.f, 0.f};
@@ -438,7 +579,7 @@ __device__ void inv_col(Smem<EX>& sm) {
             R = mma16(ah, bl, R);
             R = mma16(al, bh, R);
         }
-        const f32x4 xi = *reinterpret_cast<const f32x4*>(sm.t + (16 * i + n) * LDF + 16 * i + 4 * g4);
+        const f32x4 xi = *reinterpret_cast<const f32x4*>(sm.u.t + (16 * i + n) * LDF + 16 * i + 4 * g4);
         bf16x4 xh, xl, rh, rl;
         split4(xi, xh, xl);
         split4(R, rh, rl);
@@ -448,73 +589,118 @@ __device__ void inv_col(Smem<EX>& sm) {
         P = mma16(xl, rh, P);
         Tc[i] = -P;
     }
+    if constexpr (EX) {
+        // T's block column J scaled by beta e^gamma (tw) and by beta (tu), split
+        const int c = 16 * J + n;
+        const float sw = sm.bw[c], su = sm.beta[c];
+        const bf16 z = (bf16)0.f;
 #pragma unroll
-    for (int i = 0; i < J; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i + 4 * g4 + r;
+                bf16 wh = z, wl = z, uh = z, ul = z;
+                if (i >= J) {
+                    split1(Tc[i][r] * sw, wh, wl);
+                    split1(Tc[i][r] * su, uh, ul);
+                }
+                const int o = row * LDP + pk(c);
+                sm.tw[o] = wh;
+                sm.tw[CH * LDP + o] = wl;
+                sm.tu[o] = uh;
+                sm.tu[CH * LDP + o] = ul;
+            }
+    } else {
 #pragma unroll
-    for (int i = J + 1; i < 4; ++i)
+        for (int i = 0; i < J; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = Tc[i][r];
+            for (int r = 0; r < 4; ++r) sm.u.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = 0.f;
+#pragma unroll
+        for (int i = J + 1; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.u.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = Tc[i][r];
+    }
 }
 
-// out = T diag(sc) X[:, 32w:32w+32] for X a token-major global tile (V or K).
+// U = T diag(beta) V[:, 32w:32w+32] and W = T diag(beta e^gamma) K[:, 32w:32w+32]
+// (T is lower triangular, so row tile 0 needs k steps 0..1 only). The B
+// operands come from the transposed LDS tiles (fp32 V from HBM); hi and lo
+// products accumulate into separate tiles so that four or more independent
+// MFMA chains are in flight.
 template <typename IO>
-__device__ void wy_tiles(const Smem<Io<IO>::kExact>& sm, const float* sc, const IO* col0, size_t ts,
-                         int nvalid, f32x16 out[2]) {
+__device__ void wy_tiles(const Smem<Io<IO>::kExact>& sm, const IO* vcol, size_t ts, int nvalid,
+                         bool want_U, f32x16 U[2], f32x16 W[2]) {
     constexpr bool EX = Io<IO>::kExact;
     const int lane = lane_id(), col = lane & 31, h = lane >> 5;
-    out[0] = f32x16{};
-    out[1] = f32x16{};
+    const int n = 32 * wave_id() + col;
+    U[0] = U[1] = W[0] = W[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 bh, bl;
-        g_col_op<IO>(col0, ts, 16 * ks, h, nvalid, bh, bl);
+        bf16x8 kh, kl, vh, vl;
+        kh = lds_op16(sm.kt_hi + n * LDKT + 16 * ks + 8 * h);
+        if (!EX) kl = lds_op16(sm.kt_lo + n * LDKT + 16 * ks + 8 * h);
+        if (want_U) {
+            if constexpr (EX) vh = lds_op16(sm.vt + n * LDKT + 16 * ks + 8 * h);
+            else g_col_op<IO>(vcol, ts, 16 * ks, h, nvalid, vh, vl);
+        }
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
-            if (ti == 0 && ks >= 2) continue;  // T is lower triangular
-            bf16x8 ah, al;
-            f32_op<true>(sm.t + (32 * ti + col) * LDF + 16 * ks + 4 * h, sc + 16 * ks + 4 * h, ah, al);
-            out[ti] = mma32(ah, bh, out[ti]);
-            out[ti] = mma32(al, bh, out[ti]);
-            if (!EX) out[ti] = mma32(ah, bl, out[ti]);
+            if (ti == 0 && ks >= 2) continue;
+            const int r = 32 * ti + col;
+            bf16x8 wah, wal, uah, ual;
+            if constexpr (EX) {
+                wah = lds_op16(sm.tw + r * LDP + 16 * ks + 8 * h);
+                wal = lds_op16(sm.tw + CH * LDP + r * LDP + 16 * ks + 8 * h);
+                uah = lds_op16(sm.tu + r * LDP + 16 * ks + 8 * h);
+                ual = lds_op16(sm.tu + CH * LDP + r * LDP + 16 * ks + 8 * h);
+            } else {
+                f32_op<true>(sm.u.t + r * LDF + 16 * ks + 4 * h, sm.bw + 16 * ks + 4 * h, wah, wal);
+                f32_op<true>(sm.u.t + r * LDF + 16 * ks + 4 * h, sm.beta + 16 * ks + 4 * h, uah, ual);
+            }
+            W[ti] = mma32(wah, kh, W[ti]);
+            if (want_U) U[ti] = mma32(uah, vh, U[ti]);
+            W[ti] = mma32(wal, kh, W[ti]);
+            if (want_U) U[ti] = mma32(ual, vh, U[ti]);
+            if (!EX) {
+                W[ti] = mma32(wah, kl, W[ti]);
+                if (want_U) U[ti] = mma32(uah, vl, U[ti]);
+            }
         }
     }
 }
 
-// Full chunk preparation after load_chunk and a barrier. On return (before
-// the caller's barrier) -W is being written to LDS; U (this wave's columns)
-// and, if requested, W's tile for this wave's d_k columns are in registers.
+// Chunk preparation, part 1 (after stage_chunk and a barrier): the gram
+// products. A = masked beta K K^T goes to LDS, and P = masked Q K^T when the
+// output is wanted. The caller then synchronises.
 template <typename IO, bool WANT_P>
-__device__ void prep_chunk(Smem<Io<IO>::kExact>& sm, const Params& p, size_t tok0, int nvalid,
-                           int h, int hq, bool want_U, f32x16 U[2], f32x16 Wt[2]) {
-    constexpr bool EX = Io<IO>::kExact;
-    const int wave = wave_id(), lane = lane_id(), col = lane & 31, hh = lane >> 5;
+__device__ void prep_gram(Smem<Io<IO>::kExact>& sm, const Params& p, size_t tok0, int nvalid, int hq) {
+    const int wave = wave_id();
     const size_t ts_qk = (size_t)p.h_qk * DK;
     const IO* krow0 = static_cast<const IO*>(p.k) + tok0 * ts_qk + (size_t)hq * DK;
-
-    // gram tiles: A from K K^T, P from Q K^T (lower 32x32 tiles only)
+    if constexpr (Io<IO>::kExact) transpose_kv(sm);
     if (WANT_P) {
-        if (wave == 0) {
-            store_A<EX>(sm, gram_tile<IO, false>(sm, krow0, ts_qk, nvalid, 0, 0), 0, 0);
-            store_A<EX>(sm, gram_tile<IO, false>(sm, krow0, ts_qk, nvalid, 1, 1), 1, 1);
-        } else if (wave == 1) {
-            store_A<EX>(sm, gram_tile<IO, false>(sm, krow0, ts_qk, nvalid, 1, 0), 1, 0);
-        } else if (wave == 2) {
-            store_P<EX>(sm, gram_tile<IO, true>(sm, krow0, ts_qk, nvalid, 0, 0), 0, 0);
-            store_P<EX>(sm, gram_tile<IO, true>(sm, krow0, ts_qk, nvalid, 1, 1), 1, 1);
-        } else {
-            store_P<EX>(sm, gram_tile<IO, true>(sm, krow0, ts_qk, nvalid, 1, 0), 1, 0);
-        }
+        gram_jobs<IO, 5>(sm, krow0, ts_qk, nvalid, wave, 4);   // jobs w, w+4, ..., w+16
+        if (wave == 0) zero_p_tile(sm, 0, 1);
+        if (wave == 1) zero_p_tile(sm, 2, 3);
     } else {
-        if (wave < 3) {
-            const int ti = (wave == 0) ? 0 : 1, tj = (wave == 2) ? 1 : 0;
-            store_A<EX>(sm, gram_tile<IO, false>(sm, krow0, ts_qk, nvalid, ti, tj), ti, tj);
-        }
+        // the ten K K^T tiles: three per wave, the last wave takes one
+        if (wave < 3) gram_jobs<IO, 3>(sm, krow0, ts_qk, nvalid, wave, 3);
+        else gram_jobs<IO, 1>(sm, krow0, ts_qk, nvalid, 9, 1);
     }
-    __syncthreads();
+}
+
+// Chunk preparation, part 2 (after prep_gram and a barrier): T = (I + A)^-1,
+// U = T diag(beta) V for this wave's columns and W = T diag(beta e^gamma) K.
+// On return (before the caller's barrier) -W is being written to LDS; U and
+// this wave's W tile are in registers.
+template <typename IO>
+__device__ void prep_wy(Smem<Io<IO>::kExact>& sm, const Params& p, size_t tok0, int nvalid, int h,
+                        bool want_U, f32x16 U[2], f32x16 Wt[2]) {
+    constexpr bool EX = Io<IO>::kExact;
+    const int wave = wave_id(), lane = lane_id(), col = lane & 31, hh = lane >> 5;
     inv_diag<EX>(sm);
-    __syncthreads();
+    // the diagonal blocks this wave reads next are the ones it just wrote
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     switch (wave) {
         case 0: inv_col<0, EX>(sm); break;
         case 1: inv_col<1, EX>(sm); break;
@@ -522,26 +708,19 @@ __device__ void prep_chunk(Smem<Io<IO>::kExact>& sm, const Params& p, size_t tok
         default: inv_col<3, EX>(sm); break;
     }
     __syncthreads();
-    if (want_U) {
-        const size_t ts_v = (size_t)p.h_v * DK;
-        const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 32 * wave + col;
-        wy_tiles<IO>(sm, sm.beta, vcol, ts_v, nvalid, U);
-    } else {
-        U[0] = f32x16{};
-        U[1] = f32x16{};
-    }
-    const IO* kcol = krow0 + 32 * wave + col;
-    wy_tiles<IO>(sm, sm.bw, kcol, ts_qk, nvalid, Wt);
+    const size_t ts_v = (size_t)p.h_v * DK;
+    const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 32 * wave + col;
+    wy_tiles<IO>(sm, vcol, ts_v, nvalid, want_U, U, Wt);
     // -W as hi/lo into the region that held A (all reads of A are behind the barrier)
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = 32 * ti + acc_row(i, hh), c = 32 * wave + col;
-            const float x = -Wt[ti][i];
-            const bf16 th = (bf16)x;
-            sm.x.w[r * LDQ + c] = th;
-            sm.x.w[CH * LDQ + r * LDQ + c] = (bf16)(x - (float)th);
+            bf16 th, tl;
+            split1(-Wt[ti][i], th, tl);
+            sm.x.w[r * LDQ + pk(c)] = th;
+            sm.x.w[CH * LDQ + r * LDQ + pk(c)] = tl;
         }
 }
 
@@ -550,53 +729,116 @@ __device__ void prep_chunk(Smem<Io<IO>::kExact>& sm, const Params& p, size_t tok
 //   Vp (holds U on entry): V' = U - W S
 //   O (if OUT):            O = diag(e^gamma) Q S + P V'   (scale applied at the store)
 //   S:                     S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
-template <bool EX, bool OUT>
-__device__ void chain(const Smem<EX>& sm, f32x16 S[4], f32x16 Vp[2], f32x16 O[2]) {
+// The state as hi/lo B operands, one pair per 16-row k step (computed once per
+// chunk, used by both products with S).
+struct SplitS {
+    bf16x8 hi[8], lo[8];
+};
+__device__ __forceinline__ void split_state(const f32x16 S[4], SplitS& ss) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) split_half(S[ks >> 1], ks & 1, ss.hi[ks], ss.lo[ks]);
+}
+
+// V' = U - W S (Vp holds U on entry).
+template <bool EX>
+__device__ void chain_vp(const Smem<EX>& sm, const SplitS& ss, f32x16 Vp[2]) {
     const int lane = lane_id(), col = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 sh, sl;
-        split_half(S[ks >> 1], ks & 1, sh, sl);
+        bf16x8 wh[2], wl[2];
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
             const int r = 32 * ti + col;
-            const bf16x8 wh = lds_op(sm.x.w + r * LDQ + 16 * ks + 4 * h);
-            const bf16x8 wl = lds_op(sm.x.w + CH * LDQ + r * LDQ + 16 * ks + 4 * h);
-            Vp[ti] = mma32(wh, sh, Vp[ti]);
-            Vp[ti] = mma32(wh, sl, Vp[ti]);
-            Vp[ti] = mma32(wl, sh, Vp[ti]);
-            if (OUT) {
-                const bf16x8 qh = lds_op(sm.q_hi + r * LDQ + 16 * ks + 4 * h);
-                O[ti] = mma32(qh, sh, O[ti]);
-                O[ti] = mma32(qh, sl, O[ti]);
-                if (!EX) {
-                    const bf16x8 ql = lds_op(sm.q_lo + r * LDQ + 16 * ks + 4 * h);
-                    O[ti] = mma32(ql, sh, O[ti]);
-                }
-            }
+            wh[ti] = lds_op16(sm.x.w + r * LDQ + 16 * ks + 8 * h);
+            wl[ti] = lds_op16(sm.x.w + CH * LDQ + r * LDQ + 16 * ks + 8 * h);
+        }
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) Vp[ti] = mma32(wh[ti], ss.hi[ks], Vp[ti]);
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) Vp[ti] = mma32(wh[ti], ss.lo[ks], Vp[ti]);
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) Vp[ti] = mma32(wl[ti], ss.hi[ks], Vp[ti]);
+    }
+}
+
+// O = scale (diag(e^gamma) Q S + P V') for this wave's columns (both 32-row
+// tiles, interleaved), stored to the output (rows < nvalid).
+template <typename IO>
+__device__ void chain_out(const Smem<Io<IO>::kExact>& sm, const SplitS& ss, const f32x16 Vp[2],
+                          IO* ocol, size_t ts, int nvalid, float scale) {
+    constexpr bool EX = Io<IO>::kExact;
+    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
+    f32x16 O[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        bf16x8 qh[2], ql[2];
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            qh[ti] = lds_op16(sm.q_hi + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
+            if (!EX) ql[ti] = lds_op16(sm.q_lo + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
+        }
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(qh[ti], ss.hi[ks], O[ti]);
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(qh[ti], ss.lo[ks], O[ti]);
+        if (!EX) {
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(ql[ti], ss.hi[ks], O[ti]);
         }
     }
-    if (OUT) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[ti][i] *= sm.eg[32 * ti + acc_row(i, h)];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {  // P is causal: row tile 0 needs k steps 0..1
+        bf16x8 vh, vl;
+        split_half(Vp[ks >> 1], ks & 1, vh, vl);
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            if (ti == 0 && ks >= 2) continue;
+            const bf16x8 ph = lds_op16(sm.p_hi + (32 * ti + col) * LDP + 16 * ks + 8 * h);
+            const bf16x8 pl = lds_op16(sm.p_lo + (32 * ti + col) * LDP + 16 * ks + 8 * h);
+            O[ti] = mma32(ph, vh, O[ti]);
+            O[ti] = mma32(ph, vl, O[ti]);
+            O[ti] = mma32(pl, vh, O[ti]);
+        }
+    }
+    if constexpr (EX) {
+        // staged in LDS (the T' / T'' area is free until the next chunk's
+        // inverse); written to HBM in 16-byte row pieces by store_out
+        bf16* st = const_cast<bf16*>(sm.tw);
+        const int c = 32 * wave_id() + col;
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) O[ti][i] *= sm.eg[32 * ti + acc_row(i, h)];
+            for (int i = 0; i < 16; ++i) st[(32 * ti + acc_row(i, h)) * LDO + c] = (bf16)(O[ti][i] * scale);
+    } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 vh, vl;
-            split_half(Vp[ks >> 1], ks & 1, vh, vl);
+        for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                if (ti == 0 && ks >= 2) continue;  // P is causal
-                const int r = 32 * ti + col;
-                const bf16x8 ph = lds_op(sm.p_hi + r * LDP + 16 * ks + 4 * h);
-                const bf16x8 pl = lds_op(sm.p_lo + r * LDP + 16 * ks + 4 * h);
-                O[ti] = mma32(ph, vh, O[ti]);
-                O[ti] = mma32(ph, vl, O[ti]);
-                O[ti] = mma32(pl, vh, O[ti]);
+            for (int i = 0; i < 16; ++i) {
+                const int row = 32 * ti + acc_row(i, h);
+                if (row < nvalid) ocol[(size_t)row * ts] = (IO)(O[ti][i] * scale);
             }
-        }
     }
+}
+
+// Copies the staged bf16 output tile of a chunk to HBM (after a barrier).
+__device__ void store_out(const Smem<true>& sm, bf16* orow0, size_t ts, int nvalid) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int pc = threadIdx.x + NTHR * it, row = pc >> 4, c8 = (pc & 15) * 8;
+        if (row < nvalid)
+            *reinterpret_cast<u32x4*>(orow0 + (size_t)row * ts + c8) =
+                *reinterpret_cast<const u32x4*>(sm.tw + row * LDO + c8);
+    }
+}
+
+// S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V' (Vp is scaled in place).
+template <bool EX>
+__device__ void chain_state(const Smem<EX>& sm, f32x16 S[4], f32x16 Vp[2]) {
+    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
@@ -608,16 +850,20 @@ __device__ void chain(const Smem<EX>& sm, f32x16 S[4], f32x16 Vp[2], f32x16 O[2]
     for (int ks = 0; ks < 4; ++ks) {
         bf16x8 vh, vl;
         split_half(Vp[ks >> 1], ks & 1, vh, vl);
+        bf16x8 kh[4], kl[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int r = 32 * t + col;
-            const bf16x8 kh = lds_op(sm.kt_hi + r * LDKT + 16 * ks + 4 * h);
-            S[t] = mma32(kh, vh, S[t]);
-            S[t] = mma32(kh, vl, S[t]);
-            if (!EX) {
-                const bf16x8 kl = lds_op(sm.kt_lo + r * LDKT + 16 * ks + 4 * h);
-                S[t] = mma32(kl, vh, S[t]);
-            }
+            kh[t] = lds_op16(sm.kt_hi + (32 * t + col) * LDKT + 16 * ks + 8 * h);
+            if (!EX) kl[t] = lds_op16(sm.kt_lo + (32 * t + col) * LDKT + 16 * ks + 8 * h);
+        }
+        // four independent chains: each tile is touched once per pass
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[t] = mma32(kh[t], vh, S[t]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[t] = mma32(kh[t], vl, S[t]);
+        if (!EX) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) S[t] = mma32(kl[t], vh, S[t]);
         }
     }
 }
@@ -670,10 +916,16 @@ __global__ __launch_bounds__(NTHR) void k_chunk_prep(Params p) {
     if (!locate_chunk(p, blockIdx.x, seq, c, len, tok_s)) return;
     const size_t tok0 = tok_s + (size_t)c * CH;
     const int nvalid = min(CH, len - c * CH);
-    load_chunk<IO, false>(sm, p, tok0, nvalid, h, hq);
+    {
+        Chunk<IO> r;
+        fetch_chunk<IO, false>(r, p, tok0, nvalid, h, hq);
+        stage_chunk<IO, false>(sm, r);
+    }
     __syncthreads();
     f32x16 U[2], Wt[2];
-    prep_chunk<IO, false>(sm, p, tok0, nvalid, h, hq, true, U, Wt);
+    prep_gram<IO, false>(sm, p, tok0, nvalid, hq);
+    __syncthreads();
+    prep_wy<IO>(sm, p, tok0, nvalid, h, true, U, Wt);
     const int lane = lane_id(), col = lane & 31, hh = lane >> 5, w = wave_id();
     const size_t base = ((size_t)blockIdx.x * p.h_v + h) * CH;
     if (w == 0) p.prep_gamma[base + lane] = sm.gam[lane];
@@ -745,15 +997,27 @@ __global__ __launch_bounds__(NTHR) void k_cp_prep(Params p) {
             want_U = false;
         }
     }
+    Chunk<IO> nxt;
+    if (c_lo < c_hi)
+        fetch_chunk<IO, false>(nxt, p, loc.tok0 + (size_t)c_lo * CH, min(CH, loc.len - c_lo * CH), h, hq);
     for (int c = c_lo; c < c_hi; ++c) {
         const size_t tok0 = loc.tok0 + (size_t)c * CH;
         const int nvalid = min(CH, loc.len - c * CH);
-        load_chunk<IO, false>(sm, p, tok0, nvalid, h, hq);
+        stage_chunk<IO, false>(sm, nxt);
         __syncthreads();
-        f32x16 U[2], Wt[2], O[2];
-        prep_chunk<IO, false>(sm, p, tok0, nvalid, h, hq, want_U, U, Wt);
+        prep_gram<IO, false>(sm, p, tok0, nvalid, hq);
         __syncthreads();
-        chain<EX, false>(sm, S, U, O);
+        if (c + 1 < c_hi)
+            fetch_chunk<IO, false>(nxt, p, tok0 + CH, min(CH, loc.len - (c + 1) * CH), h, hq);
+        f32x16 U[2], Wt[2];
+        prep_wy<IO>(sm, p, tok0, nvalid, h, want_U, U, Wt);
+        __syncthreads();
+        {
+            SplitS ss;
+            split_state(S, ss);
+            chain_vp<EX>(sm, ss, U);
+        }
+        chain_state<EX>(sm, S, U);
         __syncthreads();
     }
     float* dst;
@@ -780,9 +1044,18 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
         P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
     }
     if (P <= 1) return;
-    bool any_exact = false;
-    for (int s = 1; s < P; ++s) any_exact |= (p.warm[(size_t)(seg_base + s) * p.h_v + h] == 0);
-    if (!any_exact) return;
+    // boundary choices, staged in LDS so that a step never waits on a global load to branch
+    __shared__ int wflag[kMaxFlags];
+    int n_exact = 0;
+    for (int s = 1 + (int)threadIdx.x; s < P; s += NTHR) {
+        const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h];
+        if (s < kMaxFlags) wflag[s] = f;
+        n_exact += (f == 0);
+    }
+    if (!__syncthreads_or(n_exact)) return;
+    auto warm_of = [&](int s) {
+        return s < kMaxFlags ? wflag[s] : p.warm[(size_t)(seg_base + s) * p.h_v + h];
+    };
 
     const int lane = lane_id(), col = lane & 31, hh = lane >> 5, w = wave_id();
     const int cglob = 32 * cb + col;
@@ -796,31 +1069,54 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sT[0][col * LDC + 32 * w + acc_row(i, hh)] = acc[i];
+
+    // Operands of step s (boundary s) are fetched one step ahead: the warm-up
+    // state, or H_{s-1} and this wave's rows of M_{s-1}.
+    int warm_n = 0;
+    f32x16 tile_n;
+    f32x4 m_n[16];
+    auto fetch = [&](int s) {
+        warm_n = warm_of(s);
+        const float* src = warm_n ? p.seg_state + state_off(seg_base + s, p.h_v, h)
+                                  : p.seg_H + state_off(seg_base + s - 1, p.h_v, h);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tile_n[i] = src[(32 * w + acc_row(i, hh)) * DK + cglob];
+        if (!warm_n && (s > 1 || p.s_init)) {
+            const float* mrow = p.seg_M + state_off(seg_base + s - 1, p.h_v, h) + (size_t)(32 * w + col) * DK;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                m_n[2 * ks] = *reinterpret_cast<const f32x4*>(mrow + 16 * ks + 4 * hh);
+                m_n[2 * ks + 1] = *reinterpret_cast<const f32x4*>(mrow + 16 * ks + 8 + 4 * hh);
+            }
+        }
+    };
+    fetch(1);
     __syncthreads();
     int buf = 0;
     for (int s = 1; s < P; ++s) {
-        float* dst = p.seg_state + state_off(seg_base + s, p.h_v, h);
-        const int warm = p.warm[(size_t)(seg_base + s) * p.h_v + h];
-        if (warm) {
+        const int warm = warm_n;
+        acc = tile_n;
+        f32x4 m[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = dst[(32 * w + acc_row(i, hh)) * DK + cglob];
-        } else {
-            const float* Hs = p.seg_H + state_off(seg_base + s - 1, p.h_v, h);
-            const float* Ms = p.seg_M + state_off(seg_base + s - 1, p.h_v, h);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = Hs[(32 * w + acc_row(i, hh)) * DK + cglob];
+        for (int r = 0; r < 16; ++r) m[r] = m_n[r];
+        if (s + 1 < P) fetch(s + 1);
+        if (!warm) {
             if (s > 1 || p.s_init) {
-                const float* mrow = Ms + (size_t)(32 * w + col) * DK;
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
-                    bf16x8 ah, al, bh, bl;
-                    f32_op<false>(mrow + 16 * ks + 4 * hh, nullptr, ah, al);
+                    bf16x4 a0h, a0l, a1h, a1l;
+                    split4(m[2 * ks], a0h, a0l);
+                    split4(m[2 * ks + 1], a1h, a1l);
+                    const bf16x8 ah = __builtin_shufflevector(a0h, a1h, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const bf16x8 al = __builtin_shufflevector(a0l, a1l, 0, 1, 2, 3, 4, 5, 6, 7);
+                    bf16x8 bh, bl;
                     f32_op<false>(&sT[buf][col * LDC + 16 * ks + 4 * hh], nullptr, bh, bl);
                     acc = mma32(ah, bh, acc);
                     acc = mma32(ah, bl, acc);
                     acc = mma32(al, bh, acc);
                 }
             }
+            float* dst = p.seg_state + state_off(seg_base + s, p.h_v, h);
 #pragma unroll
             for (int i = 0; i < 16; ++i) dst[(32 * w + acc_row(i, hh)) * DK + cglob] = acc[i];
         }
@@ -847,27 +1143,31 @@ __global__ __launch_bounds__(NTHR) void k_fwd(Params p) {
         load_state(p.seg_state + state_off(loc.seg_base + loc.s, p.h_v, h), S);
     }
     const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
-    const int lane = lane_id(), col = lane & 31, hh = lane >> 5, w = wave_id();
     const size_t ts_v = (size_t)p.h_v * DK;
+    Chunk<IO> nxt;
+    if (c0 < c1) fetch_chunk<IO, true>(nxt, p, loc.tok0 + (size_t)c0 * CH, min(CH, loc.len - c0 * CH), h, hq);
     for (int c = c0; c < c1; ++c) {
         const size_t tok0 = loc.tok0 + (size_t)c * CH;
         const int nvalid = min(CH, loc.len - c * CH);
-        load_chunk<IO, true>(sm, p, tok0, nvalid, h, hq);
+        stage_chunk<IO, true>(sm, nxt);
         __syncthreads();
+        prep_gram<IO, true>(sm, p, tok0, nvalid, hq);
+        __syncthreads();
+        if (c + 1 < c1)
+            fetch_chunk<IO, true>(nxt, p, tok0 + CH, min(CH, loc.len - (c + 1) * CH), h, hq);
         f32x16 U[2], Wt[2];
-        prep_chunk<IO, true>(sm, p, tok0, nvalid, h, hq, true, U, Wt);
+        prep_wy<IO>(sm, p, tok0, nvalid, h, true, U, Wt);
         __syncthreads();
-        f32x16 O[2] = {f32x16{}, f32x16{}};
-        chain<EX, true>(sm, S, U, O);
-        IO* ocol = static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK + 32 * w + col;
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 32 * ti + acc_row(i, hh);
-                if (r < nvalid) ocol[(size_t)r * ts_v] = (IO)(O[ti][i] * p.scale);
-            }
+        {
+            SplitS ss;
+            split_state(S, ss);
+            chain_vp<EX>(sm, ss, U);
+            IO* ocol = static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK + 32 * wave_id() + (lane_id() & 31);
+            chain_out<IO>(sm, ss, U, ocol, ts_v, nvalid, p.scale);
+        }
+        chain_state<EX>(sm, S, U);
         __syncthreads();
+        if constexpr (EX) store_out(sm, static_cast<bf16*>(p.out) + tok0 * ts_v + (size_t)h * DK, ts_v, nvalid);
     }
     if (loc.s == loc.P - 1 && p.s_final) store_state(p.s_final + state_off(loc.seq, p.h_v, h), S);
 }

@@ -161,6 +161,16 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc,
                           const float* g, const float* beta, const int32_t* cu_seqlens,
                           float* gamma_out, float* W_out, float* U_out, void* stream);
 
+/* Measurement support. While enabled (on != 0), every gdn_fwd / gdn_fwd_debug
+ * call records HIP events on its stream before its first launch and after
+ * each of its kernels; gdn_profile_read then waits for the last call's events
+ * and returns elapsed milliseconds:
+ *   ms[0] cp_prep, ms[1] cp_combine, ms[2] forward kernel, ms[3] whole call
+ * (phases that did not run read 0). Process-wide state, not thread-safe; the
+ * events are created on the first enable, on the current device. */
+gdn_status gdn_profile_enable(int on);
+gdn_status gdn_profile_read(float ms[4]);
+
 /* Static text for a status code. */
 const char* gdn_status_string(gdn_status status);
 

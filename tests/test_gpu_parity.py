@@ -47,10 +47,13 @@ def test_chunk_prep_matches_model(io):
     G0, W0, U0 = chunk_model.prep_all(k, v, g, b, h_v=inp.h_v)
     print(f"[chunk_prep {io}] shapes {tuple(W.shape)}", flush=True)
     assert errors(gam.cpu().numpy(), G0)[0] < 1e-5
+    # Each MFMA operand that is not an exact bf16 input is a hi + lo bf16 pair
+    # (relative representation error <= 2^-16); a product of two such operands
+    # with fp32 accumulation is good to about 3 * 2^-16 = 4.6e-5 per term.
     for name, x, ref in (("W", W, W0), ("U", U, U0)):
         mx, mean = errors(x.cpu().numpy(), ref)
         print(f"  {name}: max-rel {mx:.2e} mean-rel {mean:.2e}")
-        assert mx < 1e-4 and mean < 1e-5, name
+        assert mx < 1e-4 and mean < 3e-5, name
 
 
 @pytest.mark.parametrize("io,T,h_qk,h_v", [("bf16", 64 * 5 + 13, 2, 4), ("f32", 512, 1, 1),
