@@ -1,0 +1,225 @@
+"""C ABI on the CPU: the library loads, exports what include/gdn.h declares,
+plans, sizes its workspace and rejects bad arguments before any launch.
+
+No call here reaches a kernel launch: every gdn_fwd / gdn_chunk_prep call is
+made with an argument that validation rejects, and planning is given an
+explicit CU count so that it never queries a device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from gated_deltanet_chunked_03_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libgdn.so not built (run __graft_entry__.build())")
+
+
+def lib():
+    return B.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(B.EXPORTED), (names, B.EXPORTED)
+    l = lib()
+    for n in names:
+        assert hasattr(l, n), n
+
+
+def test_status_strings():
+    l = lib()
+    for code, name in enumerate(B.STATUS_NAMES):
+        assert l.gdn_status_string(code).decode().startswith(name)
+
+
+def desc(**kw):
+    args = dict(B=1, T=32768, h_qk=2, h_v=8, n_cu=256)
+    args.update(kw)
+    d, keep = B.make_desc(**args)
+    return d, keep
+
+
+def plan(**kw):
+    d, keep = desc(**kw)
+    return B.plan_desc(d)
+
+
+# ---------------------------------------------------------------- planner
+
+def n_chunks(t):
+    return (t + 63) // 64
+
+
+def expected_L(lens, h_v, n_cu, lam=1.0, w=6, mode="auto"):
+    """The planner rule stated in gdn_api.cpp: L = round-half-up(lam sqrt(N_max)),
+    lowered until (segments over all sequences) x h_v covers the CUs; AUTO keeps
+    sequences whole when sequences x heads already cover the CUs or N_max < 2 (w + 1)."""
+    Nm = max(n_chunks(t) for t in lens)
+    if mode == "off" or Nm <= 1:
+        return max(Nm, 1)
+    if mode == "auto" and (len(lens) * h_v >= n_cu or Nm < 2 * (w + 1)):
+        return max(Nm, 1)
+    L = min(max(1, int(math.floor(lam * math.sqrt(Nm) + 0.5))), Nm)
+    segs = lambda L: sum(1 if n_chunks(t) == 0 else -(-n_chunks(t) // L) for t in lens)  # noqa
+    while L > 1 and segs(L) * h_v < n_cu:
+        L -= 1
+    return L
+
+
+@pytest.mark.parametrize("name,B_,T,h_qk,h_v,L", [
+    ("tp8", 1, 32768, 2, 8, 16),      # sqrt(512) = 22.6 -> 23, lowered to 16 so 8 x 32 segments fill 256 CUs
+    ("tp2", 1, 32768, 8, 24, 23),
+    ("tp1", 1, 32768, 16, 16, 23),
+    ("tp1_b4", 4, 32768, 16, 16, 23),
+    ("long", 1, 262144, 2, 8, 64),
+    ("tiny", 1, 512, 1, 1, 8),        # 8 chunks < 2 (6 + 1): kept whole
+])
+def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
+    p = plan(B=B_, T=T, h_qk=h_qk, h_v=h_v)
+    assert p["L"] == L == expected_L([T] * B_, h_v, 256)
+    N = n_chunks(T)
+    assert p["n_chunks_max"] == N and p["n_chunks_total"] == N * B_
+    assert p["P_max"] == -(-N // L) and p["n_segments"] == B_ * p["P_max"]
+    assert p["cp_on"] == int(p["P_max"] > 1)
+    per_seg = h_v * 128 * 128 * 4
+    if p["cp_on"]:
+        flags = -(-(p["n_segments"] * h_v * 4) // 256) * 256
+        assert p["workspace_bytes"] == 3 * p["n_segments"] * per_seg + flags
+    else:
+        assert p["workspace_bytes"] == 0
+
+
+def test_plan_options_and_modes():
+    assert plan(cp_mode="off")["cp_on"] == 0
+    p = plan(lam=0.5)
+    assert p["L"] == expected_L([32768], 8, 256, lam=0.5) and p["lambda"] == pytest.approx(0.5)
+    # forced modes split even when the heads already cover the CUs
+    assert plan(B=4, h_qk=16, h_v=64, cp_mode="auto")["cp_on"] == 0
+    assert plan(B=4, h_qk=16, h_v=64, cp_mode="exact")["cp_on"] == 1
+    assert plan(warmup_chunks=8)["warmup_chunks"] == 8
+    assert plan()["warmup_chunks"] == 6 and plan()["noise_floor"] == pytest.approx(1e-4)
+
+
+def test_plan_varlen():
+    cu = [0, 700, 700, 701, 64 * 20 + 3, 64 * 20 + 3 + 130]
+    p = plan(T=cu[-1], h_qk=1, h_v=4, cu_seqlens=cu, n_cu=64, warmup_chunks=2, cp_mode="exact")
+    lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    L = expected_L(lens, 4, 64, w=2, mode="exact")
+    assert p["L"] == L
+    assert p["n_chunks_total"] == sum(n_chunks(t) for t in lens)
+    assert p["n_segments"] == sum(1 if n_chunks(t) == 0 else -(-n_chunks(t) // L) for t in lens)
+
+
+@pytest.mark.parametrize("B_,T,h_v,n_cu", [(1, 32768, 8, 256), (1, 4096, 3, 100), (2, 100000, 5, 304),
+                                           (1, 262144, 8, 256), (1, 1000, 2, 8)])
+def test_plan_fill_property(B_, T, h_v, n_cu):
+    """L never exceeds N, and either the segments cover the CUs or L is 1."""
+    p = plan(B=B_, T=T, h_qk=1, h_v=h_v, n_cu=n_cu, cp_mode="exact")
+    assert 1 <= p["L"] <= max(p["n_chunks_max"], 1)
+    assert p["n_segments"] * h_v >= n_cu or p["L"] == 1
+
+
+# ---------------------------------------------------------------- validation
+
+def call_fwd(d, q=0x1000, k=0x1000, v=0x1000, g=0x1000, beta=0x1000, scale=0.1, s0=None, cu=None,
+             out=0x1000, fs=None, ws=None, ws_bytes=0):
+    l = lib()
+    P = ctypes.c_void_p
+    st = l.gdn_fwd(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), scale, P(s0) if s0 else None,
+                   P(cu) if cu else None, P(out), P(fs) if fs else None, P(ws) if ws else None,
+                   ws_bytes, None)
+    return st, l.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), "GDN_ERR_BAD_SHAPE"),
+    (dict(T=-1), "GDN_ERR_BAD_SHAPE"),
+    (dict(h_qk=3, h_v=8), "GDN_ERR_BAD_SHAPE"),
+    (dict(d_k=64, d_v=64), "GDN_ERR_UNSUPPORTED_DIM"),
+    (dict(io_dtype=7), "GDN_ERR_BAD_DTYPE"),
+    (dict(cp_mode=9), "GDN_ERR_BAD_OPTION"),
+    (dict(lam=-1.0), "GDN_ERR_BAD_OPTION"),
+    (dict(warmup_chunks=9), "GDN_ERR_BAD_OPTION"),
+    (dict(noise_floor=1.5), "GDN_ERR_BAD_OPTION"),
+    (dict(B=2, cu_seqlens=[0, 10, 20], T=20), "GDN_ERR_BAD_SHAPE"),
+    (dict(T=20, cu_seqlens=[0, 15, 10, 20]), "GDN_ERR_BAD_SHAPE"),
+    (dict(T=20, cu_seqlens=[0, 10, 19]), "GDN_ERR_BAD_SHAPE"),
+])
+def test_bad_descriptor(kw, status):
+    d, keep = desc(**kw)
+    st, msg = call_fwd(d)
+    assert B.STATUS_NAMES[st] == status, msg
+    assert msg
+    info = B.GdnPlanInfo()
+    assert lib().gdn_plan(ctypes.byref(d), ctypes.byref(info)) == st
+    assert lib().gdn_fwd_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_null_and_misaligned_pointers():
+    d, keep = desc(cp_mode="off")
+    assert B.STATUS_NAMES[call_fwd(d, q=0)[0]] == "GDN_ERR_NULL_ARG"
+    assert B.STATUS_NAMES[call_fwd(d, out=0)[0]] == "GDN_ERR_NULL_ARG"
+    assert B.STATUS_NAMES[call_fwd(d, beta=0)[0]] == "GDN_ERR_NULL_ARG"
+    st, msg = call_fwd(d, k=0x1002)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_MISALIGNED" and "k" in msg
+    assert B.STATUS_NAMES[call_fwd(d, s0=0x1004)[0]] == "GDN_ERR_MISALIGNED"
+    # cu_seqlens on the device without the host copy in the descriptor (and vice versa)
+    assert B.STATUS_NAMES[call_fwd(d, cu=0x1000)[0]] == "GDN_ERR_NULL_ARG"
+    d2, keep2 = desc(T=20, cu_seqlens=[0, 10, 20], cp_mode="off")
+    assert B.STATUS_NAMES[call_fwd(d2)[0]] == "GDN_ERR_NULL_ARG"
+
+
+def test_scale_and_workspace():
+    d, keep = desc(cp_mode="off")
+    assert B.STATUS_NAMES[call_fwd(d, scale=float("nan"))[0]] == "GDN_ERR_BAD_SCALE"
+    assert B.STATUS_NAMES[call_fwd(d, scale=float("inf"))[0]] == "GDN_ERR_BAD_SCALE"
+    d, keep = desc()  # CP on: needs a workspace
+    need = lib().gdn_fwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    st, msg = call_fwd(d, ws=0x1000, ws_bytes=need - 1)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_WORKSPACE_TOO_SMALL" and str(need) in msg
+    st, msg = call_fwd(d, ws=0x1010, ws_bytes=need)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_MISALIGNED"
+
+
+def test_chunk_prep_validation():
+    l = lib()
+    d, keep = desc(d_k=64)
+    P = ctypes.c_void_p
+    st = l.gdn_chunk_prep(ctypes.byref(d), P(0x1000), P(0x1000), P(0x1000), P(0x1000), None,
+                          P(0x1000), P(0x1000), P(0x1000), None)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_UNSUPPORTED_DIM"
+    d, keep = desc()
+    st = l.gdn_chunk_prep(ctypes.byref(d), P(0x1000), P(0x1000), P(0x1000), P(0x1000), None,
+                          None, P(0x1000), P(0x1000), None)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_NULL_ARG"
+
+
+def test_profile_read_without_profiled_call():
+    l = lib()
+    ms = (ctypes.c_float * 4)()
+    assert B.STATUS_NAMES[l.gdn_profile_read(ms)] == "GDN_ERR_BAD_OPTION"
+    assert B.STATUS_NAMES[l.gdn_profile_read(None)] == "GDN_ERR_NULL_ARG"
+
+
+def test_python_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 64, 1, 128)
+    g = torch.zeros(1, 64, 1)
+    with pytest.raises(ValueError):
+        B.fwd(x, x, x, g, g)
