@@ -130,7 +130,7 @@ def main():
           file=sys.stderr, flush=True)
 
     gdn.profile_enable(True)
-    per = {"cp_prep": [], "cp_combine": [], "fwd": [], "total": []}
+    per = {"prep": [], "cp_prep": [], "cp_combine": [], "fwd": [], "total": []}
     torch.cuda.synchronize()
     t0 = time.time()
     for _ in range(args.steps):

@@ -250,11 +250,11 @@ def profile_enable(on=True):
 
 
 def profile_read():
-    """Milliseconds of the last profiled fwd call: dict cp_prep, cp_combine, fwd, total."""
+    """Milliseconds of the last profiled fwd call: dict prep, cp_prep, cp_combine, fwd, total."""
     lib = load_library()
-    ms = (ctypes.c_float * 4)()
+    ms = (ctypes.c_float * 5)()
     _check(lib, lib.gdn_profile_read(ms))
-    return {"cp_prep": ms[0], "cp_combine": ms[1], "fwd": ms[2], "total": ms[3]}
+    return {"prep": ms[0], "cp_prep": ms[1], "cp_combine": ms[2], "fwd": ms[3], "total": ms[4]}
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,

@@ -41,7 +41,7 @@ struct Plan {
     int n_chunks_total = 0, n_chunks_max = 0;
     int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0;
     float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
-    size_t off_state = 0, off_M = 0, off_H = 0, off_warm = 0, ws_bytes = 0;
+    size_t off_T = 0, off_GB = 0, off_state = 0, off_M = 0, off_H = 0, off_warm = 0, ws_bytes = 0;
 };
 
 int n_chunks_of(int len) { return (len + gdn::kChunk - 1) / gdn::kChunk; }
@@ -98,7 +98,12 @@ gdn_status query_cu_count(int* n_cu) {
 // N is the chunk count of the longest sequence; L is rounded half-up and
 // capped at the largest L that still gives every CU a workgroup; AUTO keeps
 // a sequence whole when (sequences x heads) already cover the CUs or when the
-// sequence is shorter than two warm-up windows.
+// sequence is shorter than two warm-up windows. L is raised where needed so
+// that no sequence has more than kMaxSegsPerSeq segments.
+//
+// Workspace: T (split hi/lo, 16 KiB) and gamma, beta (512 bytes) per (chunk,
+// value head); with a split, the segment states, the maps M and H, and the
+// boundary flags.
 gdn_status make_plan(const gdn_desc* d, Plan* pl) {
     gdn_status st = validate_desc(d);
     if (st != GDN_OK) return st;
@@ -137,6 +142,7 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
         const int L_lam = std::max(1, (int)std::floor(P.lambda * std::sqrt((double)Nm) + 0.5));
         int L = std::min(L_lam, Nm);
         while (L > 1 && total_segs(L) * d->h_v < P.n_cu) --L;  // fill every CU
+        while (n_segs_of(Nm, L) > gdn::kMaxSegsPerSeq) ++L;
         P.L = L;
     }
     long long ns = 0;
@@ -149,6 +155,9 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
     P.n_segments = (int)ns;
     P.cp_on = P.P_max > 1;
     size_t off = 0;
+    const size_t blk = (size_t)gdn::kChunk * gdn::kChunk * sizeof(float);
+    P.off_T = off;   off = align_up(off + (size_t)P.n_chunks_total * d->h_v * blk, 256);
+    P.off_GB = off;  off = align_up(off + (size_t)P.n_chunks_total * d->h_v * 2 * gdn::kChunk * sizeof(float), 256);
     if (P.cp_on) {
         const size_t st_bytes = (size_t)P.n_segments * d->h_v * kStateElems * sizeof(float);
         P.off_state = off; off = align_up(off + st_bytes, 256);
@@ -162,9 +171,10 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
 }
 
 // Profiling events (gdn_profile_enable / gdn_profile_read).
+constexpr int kProfEvents = 5;   // before prep, after prep, cp_prep, cp_combine, forward
 struct Profiler {
-    bool on = false, created = false, recorded = false, ran[3] = {false, false, false};
-    hipEvent_t ev[4];
+    bool on = false, created = false, recorded = false, ran[4] = {false, false, false, false};
+    hipEvent_t ev[kProfEvents];
 };
 Profiler g_prof;
 
@@ -196,6 +206,11 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
     p.n_segments = P.n_segments;
     p.n_chunks = P.n_chunks_total;
     p.log_eps = std::log(P.eps);
+    p.t_stride = (int64_t)gdn::kChunk * gdn::kChunk;
+    p.gb_stride = 2 * gdn::kChunk;
+    // chunks per k_prep workgroup: about two workgroups per CU in one round
+    const long long items = (long long)P.n_chunks_total * d->h_v, slots = 2LL * std::max(P.n_cu, 1);
+    p.prep_cpw = (int)std::min<long long>(std::max<long long>((items + slots - 1) / slots, 1), 32);
     return p;
 }
 
@@ -225,6 +240,10 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.s_init = s_init; p.cu = cu;
     p.out = out; p.s_final = s_final; p.scale = scale;
     char* w8 = static_cast<char*>(ws);
+    if (P.n_chunks_total > 0) {
+        p.prep_T = reinterpret_cast<float*>(w8 + P.off_T);
+        p.prep_GB = reinterpret_cast<float*>(w8 + P.off_GB);
+    }
     if (P.cp_on) {
         p.seg_state = reinterpret_cast<float*>(w8 + P.off_state);
         p.seg_M = reinterpret_cast<float*>(w8 + P.off_M);
@@ -235,21 +254,25 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
     const hipStream_t hs = (hipStream_t)stream;
     int e;
     prof_mark(0, hs);
+    if ((e = gdn::launch_prep(p, io, stream)))
+        return fail(GDN_ERR_HIP, "prep launch: %s", hipGetErrorString((hipError_t)e));
+    prof_mark(1, hs);
     if (P.cp_on) {
         if ((e = gdn::launch_cp_prep(p, io, stream)))
             return fail(GDN_ERR_HIP, "cp_prep launch: %s", hipGetErrorString((hipError_t)e));
-        prof_mark(1, hs);
+        prof_mark(2, hs);
         if ((e = gdn::launch_cp_combine(p, stream)))
             return fail(GDN_ERR_HIP, "cp_combine launch: %s", hipGetErrorString((hipError_t)e));
-        prof_mark(2, hs);
+        prof_mark(3, hs);
     }
     if ((e = gdn::launch_fwd(p, io, stream)))
         return fail(GDN_ERR_HIP, "fwd launch: %s", hipGetErrorString((hipError_t)e));
-    prof_mark(3, hs);
+    prof_mark(4, hs);
     if (g_prof.on) {
         g_prof.recorded = true;
-        g_prof.ran[0] = g_prof.ran[1] = P.cp_on != 0;
-        g_prof.ran[2] = true;
+        g_prof.ran[0] = true;
+        g_prof.ran[1] = g_prof.ran[2] = P.cp_on != 0;
+        g_prof.ran[3] = true;
     }
 
     if (seg_out || path_out) {
@@ -343,8 +366,16 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc, const void* k, const void* v, co
     gdn::Params p = base_params(desc, P);
     p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu = cu_seqlens;
     p.prep_gamma = gamma_out; p.prep_W = W_out; p.prep_U = U_out;
+    // T (split) goes to the start of each chunk's W_out block and gamma, beta to the
+    // start of its U_out block; the second kernel reads them and then
+    // overwrites the blocks with W and U
+    p.prep_T = W_out;
+    p.prep_GB = U_out;
+    p.t_stride = (int64_t)gdn::kChunk * gdn::kDim;
+    p.gb_stride = (int64_t)gdn::kChunk * gdn::kDim;
     const int io = desc->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
-    const int e = gdn::launch_chunk_prep(p, io, stream);
+    int e = gdn::launch_prep(p, io, stream);
+    if (!e) e = gdn::launch_wu(p, io, stream);
     if (e) return fail(GDN_ERR_HIP, "chunk_prep launch: %s", hipGetErrorString((hipError_t)e));
     g_last_error.clear();
     return GDN_OK;
@@ -352,7 +383,7 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc, const void* k, const void* v, co
 
 gdn_status gdn_profile_enable(int on) {
     if (on && !g_prof.created) {
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kProfEvents; ++i) {
             const hipError_t e = hipEventCreate(&g_prof.ev[i]);
             if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
         }
@@ -364,16 +395,18 @@ gdn_status gdn_profile_enable(int on) {
     return GDN_OK;
 }
 
-gdn_status gdn_profile_read(float ms[4]) {
+gdn_status gdn_profile_read(float ms[5]) {
     if (!ms) return fail(GDN_ERR_NULL_ARG, "ms is NULL");
     if (!g_prof.recorded) return fail(GDN_ERR_BAD_OPTION, "no profiled call since gdn_profile_enable");
-    hipError_t e = hipEventSynchronize(g_prof.ev[3]);
+    hipError_t e = hipEventSynchronize(g_prof.ev[4]);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
-    const int from[4] = {0, 1, 2, 0}, to[4] = {1, 2, 3, 3};
-    for (int i = 0; i < 4; ++i) {
+    // phase i runs from event from[i] to event to[i]; without a split the
+    // forward follows the prep directly
+    const int from[5] = {0, 1, 2, 3, 0}, to[5] = {1, 2, 3, 4, 4};
+    for (int i = 0; i < 5; ++i) {
         ms[i] = 0.f;
-        if (i < 3 && !g_prof.ran[i]) continue;
-        const int a = (i == 2 && !g_prof.ran[0]) ? 0 : from[i];
+        if (i < 4 && !g_prof.ran[i]) continue;
+        const int a = (i == 3 && !g_prof.ran[1]) ? 1 : from[i];
         e = hipEventElapsedTime(&ms[i], g_prof.ev[a], g_prof.ev[to[i]]);
         if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
     }

@@ -8,6 +8,7 @@ namespace gdn {
 
 constexpr int kChunk = 64;   // tokens per chunk
 constexpr int kDim = 128;    // d_k == d_v
+constexpr int kMaxSegsPerSeq = 2048;  // the combine kernel keeps one flag per segment in LDS
 
 struct Params {
     // inputs
@@ -26,6 +27,11 @@ struct Params {
     float* seg_M;             // [n_segments][h_v][128][128] state map of segment s: S -> M S + H
     float* seg_H;
     int32_t* warm;            // [n_segments][h_v] 1 if the boundary before segment s warms up
+    float* prep_T;            // [n_chunks][h_v] blocks of t_stride floats: T split hi/lo (16 KiB) first
+    int64_t t_stride;         // floats between consecutive T blocks (>= 64 * 64)
+    float* prep_GB;           // [n_chunks][h_v] blocks of gb_stride floats: gamma (64), beta (64)
+    int64_t gb_stride;        // floats between consecutive gamma/beta blocks (>= 128)
+    int32_t prep_cpw;         // chunks per k_prep workgroup
     // low-level chunk-prep outputs
     float* prep_gamma;        // [n_chunks][h_v][64]
     float* prep_W;            // [n_chunks][h_v][64][128]
@@ -46,7 +52,8 @@ struct Params {
 enum IoType { kIoBf16 = 0, kIoF32 = 1 };
 
 // Kernel launchers (gdn_kernels.hip). Return 0 or a hipError_t value.
-int launch_chunk_prep(const Params& p, int io, void* stream);
+int launch_prep(const Params& p, int io, void* stream);
+int launch_wu(const Params& p, int io, void* stream);
 int launch_cp_prep(const Params& p, int io, void* stream);
 int launch_cp_combine(const Params& p, void* stream);
 int launch_fwd(const Params& p, int io, void* stream);

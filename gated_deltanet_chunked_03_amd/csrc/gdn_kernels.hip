@@ -10,24 +10,29 @@
 //   V' = U - W S                           (pseudo-values)
 //   O = scale (diag(e^gamma) Q S + (Q K^T o D) V'),  D[r][i] = e^(gamma_r - gamma_i), i <= r
 //   S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
-// Section on optimising GDN chunked prefill: W, U and S are never written to
-// HBM here; the preparation (gamma, A, T, W, U) is recomputed on chip by every
-// kernel that needs it. Section "Gate-Driven Automatic Intra-Card Context
-// Parallelism (AutoCP)": each sequence is cut into segments of L chunks that
-// run as independent workgroups; cp_prep computes the state at each segment
-// boundary by a short warm-up (gates decayed below the noise floor) or the
-// exact state map S -> M S + H of the previous segment, and cp_combine chains
-// the exact maps.
 //
-// Work layout. A workgroup is 4 waves (256 lanes). Wave w owns d_v columns
-// [32w, 32w + 32): its 128 x 32 slice of S, its slice of U / V' and of the
-// output all stay in its registers, so the sequential state chain never
-// crosses waves. Operands that every wave needs (Q, K^T, -W, P = QK^T o D,
-// T) are staged in LDS. Products use 32x32x16 bf16 MFMAs with fp32
-// accumulation. Values that are not exact bf16 inputs (S, V', T, W, P) enter
-// the MFMA as a hi + lo pair of bf16 (x = hi + lo to about 16 bits), giving
-// 2 or 3 MFMAs per product; diagonal gate factors are applied in fp32 on the
-// accumulators instead of being rounded into operands.
+// Kernels. k_prep solves for T and the chunk-local gate sums of every chunk
+// in one wide launch (chunks are independent; this is the state-free half of
+// the preparation step). The chain kernels then walk their chunks in order;
+// with T at hand they need neither W nor U: V' = U - W S = T Y with
+// Y = diag(beta) (V - diag(e^gamma) K S), so the intermediates W, U and S
+// never reach HBM (section on optimising GDN chunked prefill). Section
+// "Gate-Driven Automatic Intra-Card Context Parallelism (AutoCP)": each
+// sequence is cut into segments of L chunks that run as independent
+// workgroups; k_cp_prep computes the state at each segment boundary by a
+// short warm-up (gates decayed below the noise floor) or the exact state map
+// S -> M S + H of the previous segment, k_cp_combine chains the exact maps,
+// and k_fwd runs every segment.
+//
+// Work layout of the chain kernels. A workgroup is 4 waves (256 lanes). Wave
+// w owns d_v columns [32w, 32w + 32): its 128 x 32 slice of S, its slice of
+// Y / V' and of the output all stay in its registers, so the sequential state
+// chain never crosses waves. Operands that every wave needs (Q, K, K^T, V^T,
+// T, P = QK^T o D) are staged in LDS. Products use 32x32x16 bf16 MFMAs with
+// fp32 accumulation. Values that are not exact bf16 inputs (S, Y, V', T, P)
+// enter the MFMA as a hi + lo pair of bf16 (x = hi + lo to about 16 bits),
+// giving 2 or 3 MFMAs per product; diagonal gate factors are applied in fp32
+// on the accumulators instead of being rounded into operands.
 //
 // Register layouts (verified on gfx950): 32x32x16 bf16 MFMA, lane l,
 //   A operand: row l % 32, 8 k values; B operand: column l % 32, 8 k values
@@ -35,7 +40,9 @@
 // Element e of an operand is placed at k = kb + kperm(h, e), h = l / 32, with
 // kperm(h, e) = 4h + e (e < 4) or 8 + 4h + (e - 4); that is exactly where the
 // accumulator layout holds rows, so a 32-row accumulator tile serves directly
-// as the B operand of two consecutive k steps (elements 0..7 and 8..15).
+// as the B operand of two consecutive k steps (elements 0..7 and 8..15), and,
+// as the A and B layouts mirror each other, as the A operand of the
+// transposed product.
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -61,9 +68,7 @@ constexpr int LDQ = 136;   // row stride (elements) of [64][128] bf16 tiles
 constexpr int LDKT = 72;   // row stride of [128][64] bf16 tiles
 constexpr int LDF = 68;    // row stride of [64][64] fp32 tiles
 constexpr int LDP = 72;    // row stride of [64][64] bf16 tiles
-constexpr int LDC = 132;   // row stride of the combine kernel's [32][128] fp32 tile
-constexpr int LDO = 136;   // row stride of the staged [64][128] bf16 output tile
-constexpr int kMaxFlags = 2048;  // boundary flags the combine kernel keeps in LDS
+constexpr int kMaxFlags = kMaxSegsPerSeq;  // boundary flags the combine kernel keeps in LDS
 
 enum { kCpAuto = 0, kCpOff = 1, kCpExact = 2, kCpWarmup = 3 };
 
@@ -151,22 +156,11 @@ __device__ __forceinline__ bf16x8 lds_op16(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Operand from an fp32 row (same element placement), optionally times a
-// per-column scale read at the same offsets, split into hi/lo.
-template <bool SCALE>
-__device__ __forceinline__ void f32_op(const float* p, const float* sc, bf16x8& hi, bf16x8& lo) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    f32x4 b = *reinterpret_cast<const f32x4*>(p + 8);
-    if (SCALE) {
-        a *= *reinterpret_cast<const f32x4*>(sc);
-        b *= *reinterpret_cast<const f32x4*>(sc + 8);
-    }
-    bf16x4 ah, al, bh, bl;
-    split4(a, ah, al);
-    split4(b, bh, bl);
-    hi = __builtin_shufflevector(ah, bh, 0, 1, 2, 3, 4, 5, 6, 7);
-    lo = __builtin_shufflevector(al, bl, 0, 1, 2, 3, 4, 5, 6, 7);
-}
+// Row of the transposed [128][64] LDS tiles (K^T, V^T) that holds column c:
+// the low three bits are XORed with bits 3..5 and 6, so that the staging
+// stores (sixteen lanes eight columns apart, four consecutive tokens each)
+// fall on distinct banks; a bijection on 0..127.
+__device__ __forceinline__ int trow(int c) { return (c & ~7) | ((c ^ (c >> 3) ^ (c >> 6)) & 7); }
 
 // B operand from one column of a token-major global tile: element e is token
 // kb + kperm(h, e); tokens >= nvalid read as zero.
@@ -190,46 +184,17 @@ __device__ __forceinline__ void g_col_op(const IO* col0, size_t ts, int kb, int 
 }
 
 // ----------------------------------------------------------------------------
-// Shared memory of the chunk workgroups
-
-template <bool EX>
-struct __attribute__((aligned(16))) Smem {
-    bf16 q_hi[CH * LDQ];                  // Q chunk, token-major
-    bf16 q_lo[EX ? 8 : CH * LDQ];
-    bf16 kt_hi[DK * LDKT];                // K chunk transposed: [d_k][token]
-    bf16 kt_lo[EX ? 8 : DK * LDKT];
-    bf16 vt[EX ? DK * LDKT : 8];          // V chunk transposed (bf16 inputs; fp32 V is read from HBM)
-    bf16 p_hi[CH * LDP];                  // P = (Q K^T) o D, causal, split
-    bf16 p_lo[CH * LDP];
-    bf16 tw[EX ? 2 * CH * LDP : 8];       // T diag(beta e^gamma), hi rows then lo rows
-    bf16 tu[EX ? 2 * CH * LDP : 8];       // T diag(beta), hi rows then lo rows
-    union {
-        float t[CH * LDF];                // T = (I + A)^-1
-        bf16 k_rm[EX ? CH * LDQ : 8];     // K chunk token-major, until the gram products are done
-    } u;
-    union {
-        float a[CH * LDF];                // A (strictly lower), until T is built
-        bf16 w[2 * CH * LDQ];             // -W split: hi rows then lo rows
-    } x;
-    float gam[CH];                        // gamma
-    float eg[CH];                         // exp(gamma)
-    float egc[CH];                        // exp(gamma_C - gamma)
-    float bw[CH];                         // beta exp(gamma)
-    float beta[CH];
-    float red[64];                        // red[0] = exp(gamma_C); reductions
-};
-
-// ----------------------------------------------------------------------------
-// Locating work items
+// Work items: segments and chunks
 
 struct SegLoc {
-    int seq;      // -1 if the slot is past the last segment
-    int s;        // segment index within the sequence
-    int P;        // segments of the sequence
-    int N;        // chunks of the sequence
-    int len;      // tokens of the sequence
-    int seg_base; // global index of the sequence's segment 0
-    size_t tok0;  // global token index of the sequence start
+    int seq;          // -1 if the slot is past the last segment
+    int s;            // segment index within the sequence
+    int P;            // segments of the sequence
+    int N;            // chunks of the sequence
+    int len;          // tokens of the sequence
+    int seg_base;     // global index of the sequence's segment 0
+    int chunk_base;   // global index of the sequence's chunk 0
+    size_t tok0;      // global token index of the sequence start
 };
 
 __device__ __forceinline__ int n_chunks_of(int len) { return (len + CH - 1) / CH; }
@@ -238,7 +203,7 @@ __device__ __forceinline__ int n_segs_of(int N, int L) { return N == 0 ? 1 : (N 
 __device__ SegLoc locate_segment(const Params& p, int slot) {
     SegLoc o;
     o.seq = -1;
-    o.s = o.P = o.N = o.len = o.seg_base = 0;
+    o.s = o.P = o.N = o.len = o.seg_base = o.chunk_base = 0;
     o.tok0 = 0;
     if (!p.cu) {
         const int N = n_chunks_of(p.seq_len);
@@ -246,20 +211,21 @@ __device__ SegLoc locate_segment(const Params& p, int slot) {
         const int seq = slot / P;
         if (seq < p.n_seqs) {
             o.seq = seq; o.s = slot - seq * P; o.P = P; o.N = N; o.len = p.seq_len;
-            o.seg_base = seq * P; o.tok0 = (size_t)seq * p.seq_len;
+            o.seg_base = seq * P; o.chunk_base = seq * N; o.tok0 = (size_t)seq * p.seq_len;
         }
         return o;
     }
-    int base = 0;
+    int base = 0, cbase = 0;
     for (int n = 0; n < p.n_seqs; ++n) {
         const int a = p.cu[n], len = p.cu[n + 1] - a;
         const int N = n_chunks_of(len), P = n_segs_of(N, p.L);
         if (slot < base + P) {
             o.seq = n; o.s = slot - base; o.P = P; o.N = N; o.len = len;
-            o.seg_base = base; o.tok0 = (size_t)a;
+            o.seg_base = base; o.chunk_base = cbase; o.tok0 = (size_t)a;
             return o;
         }
         base += P;
+        cbase += N;
     }
     return o;
 }
@@ -287,153 +253,34 @@ __device__ bool locate_chunk(const Params& p, int slot, int& seq, int& c, int& l
     return false;
 }
 
+// Inclusive scan of g over the 64 lanes of a wave (lane = token of the chunk).
+__device__ __forceinline__ float wave_scan(float s) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(s, d, 64);
+        if (lane >= d) s += o;
+    }
+    return s;
+}
+
+
 // ----------------------------------------------------------------------------
-// Chunk preparation: load, gamma, gram products, inverse, W and U
+// Chunk preparation kernel: gamma, beta and T = (I + A)^-1 of every (chunk,
+// value head). Chunks are independent, so this runs as a wide grid at two
+// workgroups per CU; the chain kernels then read T instead of solving the
+// triangular system inside their sequential loops.
 
-// One chunk's inputs in registers between the global load and the LDS store
-// (so the next chunk's loads overlap the current chunk's work). Thread t
-// holds pieces t + 256 j (j < 4): token row (piece / 16), columns
-// 8 (piece % 16) .. + 8 of K, Q and V, so sixteen lanes cover one 256-byte row.
-template <typename IO> struct Chunk;
-template <> struct Chunk<bf16> { u32x4 k[4], q[4], v[4]; float g, b; };
-template <> struct Chunk<float> { f32x4 k[8], q[8]; float g, b; };
+template <bool EX>
+struct __attribute__((aligned(16))) PrepSmem {
+    bf16 k_rm[EX ? CH * LDQ : 8];   // K chunk token-major, d_k permuted (bf16 inputs)
+    float a[CH * LDF];              // A (strictly lower)
+    float t[CH * LDF];              // T = (I + A)^-1
+    float gam[CH];
+    float beta[CH];
+};
 
-template <typename IO, bool WANT_Q>
-__device__ __forceinline__ void fetch_chunk(Chunk<IO>& r, const Params& p, size_t tok0, int nvalid,
-                                            int h, int hq) {
-    constexpr bool EX = Io<IO>::kExact;
-    const int t = threadIdx.x;
-    const size_t ts = (size_t)p.h_qk * DK, tsv = (size_t)p.h_v * DK;
-    const IO* kb = static_cast<const IO*>(p.k) + tok0 * ts + (size_t)hq * DK;
-    const IO* qb = static_cast<const IO*>(p.q) + tok0 * ts + (size_t)hq * DK;
-    const IO* vb = static_cast<const IO*>(p.v) + tok0 * tsv + (size_t)h * DK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int pc = t + NTHR * j, row = pc >> 4, c8 = (pc & 15) * 8;
-        const bool ok = row < nvalid;
-        if constexpr (EX) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            r.k[j] = ok ? *reinterpret_cast<const u32x4*>(kb + row * ts + c8) : z;
-            if (WANT_Q) r.q[j] = ok ? *reinterpret_cast<const u32x4*>(qb + row * ts + c8) : z;
-            r.v[j] = ok ? *reinterpret_cast<const u32x4*>(vb + row * tsv + c8) : z;
-        } else {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            r.k[2 * j] = ok ? *reinterpret_cast<const f32x4*>(kb + row * ts + c8) : z;
-            r.k[2 * j + 1] = ok ? *reinterpret_cast<const f32x4*>(kb + row * ts + c8 + 4) : z;
-            if (WANT_Q) {
-                r.q[2 * j] = ok ? *reinterpret_cast<const f32x4*>(qb + row * ts + c8) : z;
-                r.q[2 * j + 1] = ok ? *reinterpret_cast<const f32x4*>(qb + row * ts + c8 + 4) : z;
-            }
-        }
-    }
-    r.g = 0.f;
-    r.b = 0.f;
-    if (wave_id() == 0 && lane_id() < nvalid) {
-        const size_t idx = (tok0 + lane_id()) * (size_t)p.h_v + h;
-        r.g = p.g[idx];
-        r.b = p.beta[idx];
-    }
-}
-
-// Two bf16 of the same column from two rows packed into one 32-bit word.
-__device__ __forceinline__ unsigned int pack_col(const u32x4& a, const u32x4& b, int e) {
-    const unsigned int wa = a[e >> 1], wb = b[e >> 1];
-    return (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
-}
-
-// Writes a fetched chunk to LDS and derives the gate quantities. bf16
-// inputs: K, Q and V token-major (K in the T area and V in the T'' area,
-// both free until the inverse; the gram phase transposes them); fp32 inputs: Q and K^T as hi/lo pairs. Rows
-// past the end of the sequence were fetched as zeros (g = beta = 0 there).
-template <typename IO, bool WANT_Q>
-__device__ __forceinline__ void stage_chunk(Smem<Io<IO>::kExact>& sm, const Chunk<IO>& r) {
-    constexpr bool EX = Io<IO>::kExact;
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int pc = t + NTHR * j, row = pc >> 4, c8 = (pc & 15) * 8;
-        if constexpr (EX) {
-            const int o0 = row * LDQ + pk(c8), o1 = row * LDQ + pk(c8 + 4);
-            *reinterpret_cast<u32x2*>(sm.u.k_rm + o0) = u32x2{r.k[j][0], r.k[j][1]};
-            *reinterpret_cast<u32x2*>(sm.u.k_rm + o1) = u32x2{r.k[j][2], r.k[j][3]};
-            *reinterpret_cast<u32x2*>(sm.tu + o0) = u32x2{r.v[j][0], r.v[j][1]};
-            *reinterpret_cast<u32x2*>(sm.tu + o1) = u32x2{r.v[j][2], r.v[j][3]};
-            if (WANT_Q) {
-                *reinterpret_cast<u32x2*>(sm.q_hi + o0) = u32x2{r.q[j][0], r.q[j][1]};
-                *reinterpret_cast<u32x2*>(sm.q_hi + o1) = u32x2{r.q[j][2], r.q[j][3]};
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16 th, tl;
-                split1(r.k[2 * j + (e >> 2)][e & 3], th, tl);
-                sm.kt_hi[(c8 + e) * LDKT + pk(row)] = th;
-                sm.kt_lo[(c8 + e) * LDKT + pk(row)] = tl;
-                if (WANT_Q) {
-                    split1(r.q[2 * j + (e >> 2)][e & 3], th, tl);
-                    sm.q_hi[row * LDQ + pk(c8 + e)] = th;
-                    sm.q_lo[row * LDQ + pk(c8 + e)] = tl;
-                }
-            }
-        }
-    }
-    if (wave_id() == 0) {
-        const int lane = lane_id();
-        float s = r.g;  // inclusive scan over the 64 lanes
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float o = __shfl_up(s, d, 64);
-            if (lane >= d) s += o;
-        }
-        const float gc = __shfl(s, 63, 64);
-        const float es = __expf(s);
-        sm.gam[lane] = s;
-        sm.eg[lane] = es;
-        sm.egc[lane] = __expf(gc - s);
-        sm.beta[lane] = r.b;
-        sm.bw[lane] = r.b * es;
-        if (lane == 0) sm.red[0] = __expf(gc);
-    }
-}
-
-// Two bf16 of the same column from two rows packed into one 32-bit word.
-__device__ __forceinline__ unsigned pack_col(u32x2 a, u32x2 b, int e) {
-    const unsigned wa = a[e >> 1], wb = b[e >> 1];
-    return (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
-}
-
-// K^T and V^T from the token-major LDS tiles (bf16 inputs; after a barrier):
-// thread t packs rows 2 (t % 32), 2 (t % 32) + 1 of column blocks t / 32 and
-// t / 32 + 8 into 32-bit words of the transposed tiles.
-__device__ __forceinline__ void transpose_kv(Smem<true>& sm) {
-    const int t = threadIdx.x, rp = t & 31, cbk = t >> 5;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-        const int c8 = 8 * (cbk + 8 * jb);
-        const int tp = pk(2 * rp);  // the token pair stays adjacent under the permutation
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int o = (2 * rp) * LDQ + pk(c8 + 4 * half);
-            const u32x2 ka = *reinterpret_cast<const u32x2*>(sm.u.k_rm + o);
-            const u32x2 kb = *reinterpret_cast<const u32x2*>(sm.u.k_rm + o + LDQ);
-            const u32x2 va = *reinterpret_cast<const u32x2*>(sm.tu + o);
-            const u32x2 vb = *reinterpret_cast<const u32x2*>(sm.tu + o + LDQ);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = c8 + 4 * half + e;
-                *reinterpret_cast<unsigned*>(sm.kt_hi + c * LDKT + tp) = pack_col(ka, kb, e);
-                *reinterpret_cast<unsigned*>(sm.vt + c * LDKT + tp) = pack_col(va, vb, e);
-            }
-        }
-    }
-}
-
-// Gram products on 16x16 tiles (16x16x32 MFMA; lane l: A row l % 16 and
-// B column l % 16, each with the 8 consecutive k values 8 (l / 16)..; C rows
-// 4 (l / 16).. of column l % 16). The ten lower tiles (bi >= bj) of K K^T and
-// of Q K^T are twenty jobs, run as interleaved chains. Each is computed
-// transposed (K rows of block bj against K or Q rows of block bi), so a lane
-// ends up with four consecutive columns j of one row i and stores them at once.
+// Lower 16x16 tile number job (0..9) -> block row bi >= block column bj.
 __device__ __forceinline__ void lower_tile(int job, int& bi, int& bj) {
     bi = (job >= 6) ? 3 : (job >= 3) ? 2 : (job >= 1) ? 1 : 0;
     bj = job - (bi * (bi + 1)) / 2;
@@ -457,22 +304,23 @@ __device__ __forceinline__ void g_row8(const float* p, bool valid, bf16x8& hi, b
 }
 __device__ __forceinline__ bf16x8 lds_row8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// A[i][j] = beta_i exp(gamma_i - gamma_j) (k_i . k_j) for i > j, else 0 (fp32), and
-// P[i][j] = exp(gamma_i - gamma_j) (q_i . k_j) for i >= j, else 0 (hi/lo bf16).
-// Jobs first, first + stride, ... (job >= 10: the P tile job - 10).
+// A[i][j] = beta_i exp(gamma_i - gamma_j) (k_i . k_j) for i > j, else 0, on
+// 16x16 tiles (16x16x32 MFMA; lane l: A row l % 16 and B column l % 16, each
+// with the 8 consecutive k values 8 (l / 16)..; C rows 4 (l / 16).. of column
+// l % 16). The ten lower tiles are jobs first, first + stride, ..., run as
+// interleaved chains; each is computed transposed (K rows of block bj against
+// K rows of block bi), so a lane ends up with four consecutive columns j of
+// one row i and stores them at once.
 template <typename IO, int NJOB>
-__device__ void gram_jobs(Smem<Io<IO>::kExact>& sm, const IO* krow0, size_t ts, int nvalid, int first,
-                          int stride) {
+__device__ void gram_a(PrepSmem<Io<IO>::kExact>& sm, const IO* krow0, size_t ts, int nvalid, int first,
+                       int stride) {
     constexpr bool EX = Io<IO>::kExact;
     const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
     f32x4 acc[NJOB];
     int bi[NJOB], bj[NJOB];
-    bool isq[NJOB];
 #pragma unroll
     for (int t = 0; t < NJOB; ++t) {
-        const int job = first + stride * t;
-        isq[t] = job >= 10;
-        lower_tile(isq[t] ? job - 10 : job, bi[t], bj[t]);
+        lower_tile(first + stride * t, bi[t], bj[t]);
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
@@ -481,23 +329,425 @@ __device__ void gram_jobs(Smem<Io<IO>::kExact>& sm, const IO* krow0, size_t ts, 
         const int kg = 32 * ks + 16 * (g4 >> 1) + 4 * (g4 & 1);          // logical start (HBM rows)
 #pragma unroll
         for (int t = 0; t < NJOB; ++t) {
-            const int ra = 16 * bj[t] + n, rb = 16 * bi[t] + n;   // A: K rows of bj; B: rows of bi
+            const int ra = 16 * bj[t] + n, rb = 16 * bi[t] + n;
             if constexpr (EX) {
-                const bf16x8 a = lds_row8(sm.u.k_rm + ra * LDQ + kb);
-                const bf16x8 b = lds_row8((isq[t] ? sm.q_hi : sm.u.k_rm) + rb * LDQ + kb);
-                acc[t] = mma16k32(a, b, acc[t]);
+                acc[t] = mma16k32(lds_row8(sm.k_rm + ra * LDQ + kb), lds_row8(sm.k_rm + rb * LDQ + kb), acc[t]);
             } else {
                 bf16x8 ah, al, bh, bl;
                 g_row8(krow0 + (size_t)ra * ts + kg, ra < nvalid, ah, al);
-                if (isq[t]) {
-                    bh = lds_row8(sm.q_hi + rb * LDQ + kb);
-                    bl = lds_row8(sm.q_lo + rb * LDQ + kb);
-                } else {
-                    g_row8(krow0 + (size_t)rb * ts + kg, rb < nvalid, bh, bl);
-                }
+                g_row8(krow0 + (size_t)rb * ts + kg, rb < nvalid, bh, bl);
                 acc[t] = mma16k32(ah, bh, acc[t]);
                 acc[t] = mma16k32(ah, bl, acc[t]);
                 acc[t] = mma16k32(al, bh, acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NJOB; ++t) {
+        const int i = 16 * bi[t] + n, j0 = 16 * bj[t] + 4 * g4;   // row i, columns j0 .. j0 + 3
+        const float gi = sm.gam[i], bt = sm.beta[i];
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(sm.gam + j0);
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (i > j0 + r) ? bt * __expf(gi - gj[r]) * acc[t][r] : 0.f;
+        *reinterpret_cast<f32x4*>(sm.a + i * LDF + j0) = v;
+    }
+}
+
+// Diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution. Every
+// wave solves all four blocks (lane 16 b + j: block b, column j) and writes
+// them; the values are identical across waves, so each wave can read the
+// blocks back without waiting for the others.
+template <bool EX>
+__device__ void inv_diag(PrepSmem<EX>& sm) {
+    const int lane = lane_id(), b = 16 * (lane >> 4), j = lane & 15;
+    const float* A = sm.a + b * LDF + b;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float s = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) s = fmaf(-A[i * LDF + m], x[m], s);
+        x[i] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.t[(b + i) * LDF + b + j] = x[i];
+}
+
+// Block column J of T below the diagonal: T_iJ = -X_i sum_{m=J}^{i-1} A_im T_mJ,
+// with 16x16x16 bf16 MFMAs on hi/lo operands (lane l: A row l % 16, k 4 (l/16)..;
+// B / C column l % 16, rows 4 (l/16)..). Zeros above the diagonal block.
+template <int J, bool EX>
+__device__ void inv_col(PrepSmem<EX>& sm) {
+    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
+    f32x4 Tc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Tc[J][r] = sm.t[(16 * J + 4 * g4 + r) * LDF + 16 * J + n];
+#pragma unroll
+    for (int i = J + 1; i < 4; ++i) {
+        f32x4 R = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = J; m < i; ++m) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(sm.a + (16 * i + n) * LDF + 16 * m + 4 * g4);
+            bf16x4 ah, al, bh, bl;
+            split4(a, ah, al);
+            split4(Tc[m], bh, bl);
+            R = mma16(ah, bh, R);
+            R = mma16(ah, bl, R);
+            R = mma16(al, bh, R);
+        }
+        const f32x4 xi = *reinterpret_cast<const f32x4*>(sm.t + (16 * i + n) * LDF + 16 * i + 4 * g4);
+        bf16x4 xh, xl, rh, rl;
+        split4(xi, xh, xl);
+        split4(R, rh, rl);
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+        P = mma16(xh, rh, P);
+        P = mma16(xh, rl, P);
+        P = mma16(xl, rh, P);
+        Tc[i] = -P;
+    }
+#pragma unroll
+    for (int i = 0; i < J; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = 0.f;
+#pragma unroll
+    for (int i = J + 1; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = Tc[i][r];
+}
+
+// Inputs of one chunk for k_prep, prefetched into registers: K rows (bf16;
+// thread t: row (t + 256 j) / 16, columns 8 ((t + 256 j) % 16) .. + 8; fp32 K
+// is read from HBM by the gram itself) and g, beta of token lane.
+template <typename IO> struct PrepIn;
+template <> struct PrepIn<bf16> { u32x4 k[4]; float g, b; };
+template <> struct PrepIn<float> { float g, b; };
+
+// Loads are unconditional (rows past the end of the sequence read its last
+// row) and the values of those rows are replaced by zeros afterwards.
+template <typename IO>
+__device__ __forceinline__ void prep_fetch(PrepIn<IO>& r, const Params& p, size_t tok0, int nvalid, int h, int hq) {
+    const size_t ts = (size_t)p.h_qk * DK;
+    if constexpr (Io<IO>::kExact) {
+        const IO* kb = static_cast<const IO*>(p.k) + tok0 * ts + (size_t)hq * DK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pc = threadIdx.x + NTHR * j, row = pc >> 4, c8 = (pc & 15) * 8;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + (size_t)min(row, nvalid - 1) * ts + c8);
+            r.k[j] = row < nvalid ? kv : z;
+        }
+    }
+    const int lane = lane_id();
+    const size_t idx = (tok0 + min(lane, nvalid - 1)) * (size_t)p.h_v + h;
+    const float g = p.g[idx], b = p.beta[idx];
+    r.g = lane < nvalid ? g : 0.f;
+    r.b = lane < nvalid ? b : 0.f;
+}
+
+// Grid (groups of p.prep_cpw consecutive chunk slots, value heads); each
+// workgroup walks its chunks, fetching the next chunk's inputs while it works
+// on the current one. Per (chunk slot, value head), block b = slot h_v + h:
+//   prep_T + b t_stride: T diag(beta) split into bf16 hi and lo, [part][row][k]
+//     (2 x 64 x 64), the k (column) axis permuted within each group of 16 as
+//     the chain kernels' LDS operands are (zeros above the diagonal);
+//   prep_GB + b gb_stride: gamma (64 fp32), then beta (64 fp32).
+template <typename IO>
+__global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
+    constexpr bool EX = Io<IO>::kExact;
+    __shared__ PrepSmem<EX> sm;
+    const int h = blockIdx.y, hq = h / p.group, wave = wave_id(), lane = lane_id();
+    const int s0 = blockIdx.x * p.prep_cpw, s1 = min(s0 + p.prep_cpw, p.n_chunks);
+    const size_t ts = (size_t)p.h_qk * DK;
+    int seq, c, len;
+    size_t tok_s;
+    if (s0 >= s1 || !locate_chunk(p, s0, seq, c, len, tok_s)) return;
+    size_t tok0 = tok_s + (size_t)c * CH;
+    int nvalid = min(CH, len - c * CH);
+    PrepIn<IO> nxt;
+    prep_fetch<IO>(nxt, p, tok0, nvalid, h, hq);
+    for (int slot = s0; slot < s1; ++slot) {
+        const size_t tok_cur = tok0;
+        const int nv_cur = nvalid;
+        const IO* krow0 = static_cast<const IO*>(p.k) + tok_cur * ts + (size_t)hq * DK;
+        if constexpr (EX) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int pc = threadIdx.x + NTHR * j, row = pc >> 4, c8 = (pc & 15) * 8;
+                *reinterpret_cast<u32x2*>(sm.k_rm + row * LDQ + pk(c8)) = u32x2{nxt.k[j][0], nxt.k[j][1]};
+                *reinterpret_cast<u32x2*>(sm.k_rm + row * LDQ + pk(c8 + 4)) = u32x2{nxt.k[j][2], nxt.k[j][3]};
+            }
+        }
+        if (wave == 0) {
+            const float gam = wave_scan(nxt.g);
+            sm.gam[lane] = gam;
+            sm.beta[lane] = nxt.b;
+            float* gb = p.prep_GB + ((size_t)slot * p.h_v + h) * (size_t)p.gb_stride;
+            gb[lane] = gam;
+            gb[CH + lane] = nxt.b;
+        }
+        __syncthreads();
+        if (slot + 1 < s1 && locate_chunk(p, slot + 1, seq, c, len, tok_s)) {
+            tok0 = tok_s + (size_t)c * CH;
+            nvalid = min(CH, len - c * CH);
+            prep_fetch<IO>(nxt, p, tok0, nvalid, h, hq);
+        }
+        // the ten tiles: three per wave, the last wave takes one
+        if (wave < 3) gram_a<IO, 3>(sm, krow0, ts, nv_cur, wave, 3);
+        else gram_a<IO, 1>(sm, krow0, ts, nv_cur, 9, 1);
+        __syncthreads();
+        inv_diag<EX>(sm);
+        // the diagonal blocks this wave reads next are the ones it just wrote
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        switch (wave) {
+            case 0: inv_col<0, EX>(sm); break;
+            case 1: inv_col<1, EX>(sm); break;
+            case 2: inv_col<2, EX>(sm); break;
+            default: inv_col<3, EX>(sm); break;
+        }
+        __syncthreads();
+        // (the next chunk's LDS writes touch k_rm and the gate arrays only, all
+        // read before the previous barrier; T is rewritten after two more).
+        // T diag(beta): thread t takes row t / 4 and the 16 physical k
+        // positions 16 (t % 4) ..; physical 4-blocks 0..3 of a 16-group hold
+        // logical blocks 0, 2, 1, 3.
+        bf16* Tg = reinterpret_cast<bf16*>(p.prep_T + ((size_t)slot * p.h_v + h) * (size_t)p.t_stride);
+        {
+            const int row = threadIdx.x >> 2, g16 = 16 * (threadIdx.x & 3);
+            const float* tr = sm.t + row * LDF + g16;
+            const float* br = sm.beta + g16;
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(tr) * *reinterpret_cast<const f32x4*>(br);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(tr + 8) * *reinterpret_cast<const f32x4*>(br + 8);
+            const f32x4 b2 = *reinterpret_cast<const f32x4*>(tr + 4) * *reinterpret_cast<const f32x4*>(br + 4);
+            const f32x4 b3 = *reinterpret_cast<const f32x4*>(tr + 12) * *reinterpret_cast<const f32x4*>(br + 12);
+            bf16x4 h0, l0, h1, l1, h2, l2, h3, l3;
+            split4(b0, h0, l0);
+            split4(b1, h1, l1);
+            split4(b2, h2, l2);
+            split4(b3, h3, l3);
+            const bf16x8 hA = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 hB = __builtin_shufflevector(h2, h3, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 lA = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 lB = __builtin_shufflevector(l2, l3, 0, 1, 2, 3, 4, 5, 6, 7);
+            *reinterpret_cast<bf16x8*>(Tg + row * CH + g16) = hA;
+            *reinterpret_cast<bf16x8*>(Tg + row * CH + g16 + 8) = hB;
+            *reinterpret_cast<bf16x8*>(Tg + (CH + row) * CH + g16) = lA;
+            *reinterpret_cast<bf16x8*>(Tg + (CH + row) * CH + g16 + 8) = lB;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// The chain kernels. For a chunk with incoming state S, the same quantities as
+// the WY form, evaluated without W and U:
+//   Y  = V - diag(e^gamma) K S                    (the prediction error)
+//   V' = T diag(beta) Y                           (= U - W S)
+//   O  = diag(e^gamma) Q S + P V',  P = (Q K^T) o D  (both times the scale)
+//   S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
+// so each wave needs, besides its own state columns, only K, K^T, V^T, Q, P
+// and T from LDS, and the products of different waves never meet.
+
+template <bool EX>
+struct __attribute__((aligned(16))) ChainSmem {
+    bf16 q_hi[CH * LDQ];                  // Q token-major, d_k permuted
+    bf16 q_lo[EX ? 8 : CH * LDQ];
+    bf16 k_hi[CH * LDQ];                  // K token-major, d_k permuted
+    bf16 k_lo[EX ? 8 : CH * LDQ];
+    bf16 kt_hi[DK * LDKT];                // K^T: [d_k][token permuted]
+    bf16 kt_lo[EX ? 8 : DK * LDKT];
+    bf16 vt[EX ? DK * LDKT : 8];          // V^T (bf16 inputs; fp32 V is read from HBM)
+    bf16 p[2 * CH * LDP];                 // P = (Q K^T) o D, causal: hi rows, then lo rows
+    bf16 t[2 * CH * LDP];                 // T diag(beta): hi rows, then lo rows (token axis permuted)
+    float gam[CH];                        // gamma
+    float eg[CH];                         // exp(gamma)
+    float egs[CH];                        // scale exp(gamma)
+    float egc[CH];                        // exp(gamma_C - gamma)
+    float red[8];                         // red[0] = exp(gamma_C); per-chunk gate sums
+};
+
+// One chunk's inputs in registers between the global loads and the LDS
+// stores, so that the next chunk's loads overlap the current chunk's work.
+// K, V: thread t holds token rows 4 (t / 16) + j (j < 4), columns
+// 8 (t % 16) .. + 8 (sixteen lanes cover one 256-byte row, and a lane holds
+// four consecutive tokens of each of its columns, written to K^T / V^T as
+// 8-byte stores). Q: rows t / 16 + 16 j, same columns. T: four 16-byte pieces
+// (t + 256 j) of its [part][row][64] image. Gates: gamma, beta of token lane.
+template <typename IO> struct Chunk;
+template <> struct Chunk<bf16> { u32x4 k[4], v[4], q[4], t[4]; float gl, bl; };
+template <> struct Chunk<float> { f32x4 k[8], q[8]; u32x4 t[4]; float gl, bl; };
+
+// Full chunks load rows directly; the last chunk of a sequence loads its rows
+// with the index clamped to the last token and replaces the rows past the end
+// by zeros. Addresses are a wave-uniform base plus 32-bit lane offsets.
+template <typename IO, bool WANT_Q, bool WANT_V>
+__device__ __forceinline__ void fetch_chunk(Chunk<IO>& r, const Params& p, size_t tok0, int nvalid, int h,
+                                            int hq, int slot) {
+    constexpr bool EX = Io<IO>::kExact;
+    const int t = threadIdx.x, m = t >> 4, c8 = (t & 15) * 8;
+    const int ts = p.h_qk * DK, tsv = p.h_v * DK;
+    const IO* kb = static_cast<const IO*>(p.k) + tok0 * (size_t)ts + (size_t)hq * DK;
+    const IO* qb = static_cast<const IO*>(p.q) + tok0 * (size_t)ts + (size_t)hq * DK;
+    const IO* vb = static_cast<const IO*>(p.v) + tok0 * (size_t)tsv + (size_t)h * DK;
+    const bool full = nvalid == CH;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rk = 4 * m + j, rq = m + 16 * j;
+        const unsigned ok_k = (unsigned)((full ? rk : min(rk, nvalid - 1)) * ts + c8);
+        const unsigned ok_v = (unsigned)((full ? rk : min(rk, nvalid - 1)) * tsv + c8);
+        const unsigned ok_q = (unsigned)((full ? rq : min(rq, nvalid - 1)) * ts + c8);
+        const bool vk = full || rk < nvalid, vq = full || rq < nvalid;
+        if constexpr (EX) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + ok_k);
+            r.k[j] = vk ? kv : z;
+            if (WANT_V) {
+                const u32x4 vv = *reinterpret_cast<const u32x4*>(vb + ok_v);
+                r.v[j] = vk ? vv : z;
+            }
+            if (WANT_Q) {
+                const u32x4 qv = *reinterpret_cast<const u32x4*>(qb + ok_q);
+                r.q[j] = vq ? qv : z;
+            }
+        } else {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 ka = *reinterpret_cast<const f32x4*>(kb + ok_k);
+            const f32x4 kc = *reinterpret_cast<const f32x4*>(kb + ok_k + 4);
+            r.k[2 * j] = vk ? ka : z;
+            r.k[2 * j + 1] = vk ? kc : z;
+            if (WANT_Q) {
+                const f32x4 qa = *reinterpret_cast<const f32x4*>(qb + ok_q);
+                const f32x4 qc = *reinterpret_cast<const f32x4*>(qb + ok_q + 4);
+                r.q[2 * j] = vq ? qa : z;
+                r.q[2 * j + 1] = vq ? qc : z;
+            }
+        }
+    }
+    const size_t blk = (size_t)slot * p.h_v + h;
+    const u32x4* Tg = reinterpret_cast<const u32x4*>(p.prep_T + blk * (size_t)p.t_stride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.t[j] = Tg[t + NTHR * j];
+    const float* gb = p.prep_GB + blk * (size_t)p.gb_stride;
+    r.gl = gb[lane_id()];
+    r.bl = gb[CH + lane_id()];
+}
+
+// Two bf16 of the same column from two rows packed into one 32-bit word.
+__device__ __forceinline__ unsigned int pack_col(const u32x4& a, const u32x4& b, int e) {
+    const unsigned int wa = a[e >> 1], wb = b[e >> 1];
+    return (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+}
+
+// Writes a fetched chunk to LDS: K token-major and transposed (four
+// consecutive tokens of a column per 8-byte store), V^T, Q, T and the gate
+// factors (wave 0). Rows past the end of the sequence were fetched as zeros
+// (g = beta = 0 there).
+template <typename IO, bool WANT_Q, bool WANT_V>
+__device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const Chunk<IO>& r, float scale) {
+    constexpr bool EX = Io<IO>::kExact;
+    const int t = threadIdx.x, lane = lane_id(), m = t >> 4, c8 = (t & 15) * 8;
+    if (wave_id() == 0) {
+        const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.gl), 63));
+        const float es = __expf(r.gl);
+        sm.gam[lane] = r.gl;
+        sm.eg[lane] = es;
+        sm.egs[lane] = es * scale;
+        sm.egc[lane] = __expf(gc - r.gl);
+        if (lane == 0) sm.red[0] = __expf(gc);
+    }
+    const int tp = pk(4 * m);   // the four tokens stay contiguous under the permutation
+    if constexpr (EX) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 4 * m + j;
+            *reinterpret_cast<u32x2*>(sm.k_hi + row * LDQ + pk(c8)) = u32x2{r.k[j][0], r.k[j][1]};
+            *reinterpret_cast<u32x2*>(sm.k_hi + row * LDQ + pk(c8 + 4)) = u32x2{r.k[j][2], r.k[j][3]};
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = c8 + e;
+            *reinterpret_cast<u32x2*>(sm.kt_hi + trow(c) * LDKT + tp) =
+                u32x2{pack_col(r.k[0], r.k[1], e), pack_col(r.k[2], r.k[3], e)};
+            if (WANT_V)
+                *reinterpret_cast<u32x2*>(sm.vt + trow(c) * LDKT + tp) =
+                    u32x2{pack_col(r.v[0], r.v[1], e), pack_col(r.v[2], r.v[3], e)};
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 4 * m + j;
+            bf16x4 ah, al, bh, bl;
+            split4(r.k[2 * j], ah, al);
+            split4(r.k[2 * j + 1], bh, bl);
+            *reinterpret_cast<bf16x4*>(sm.k_hi + row * LDQ + pk(c8)) = ah;
+            *reinterpret_cast<bf16x4*>(sm.k_lo + row * LDQ + pk(c8)) = al;
+            *reinterpret_cast<bf16x4*>(sm.k_hi + row * LDQ + pk(c8 + 4)) = bh;
+            *reinterpret_cast<bf16x4*>(sm.k_lo + row * LDQ + pk(c8 + 4)) = bl;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = c8 + e;
+            f32x4 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = r.k[2 * j + (e >> 2)][e & 3];
+            bf16x4 xh, xl;
+            split4(x, xh, xl);
+            *reinterpret_cast<bf16x4*>(sm.kt_hi + trow(c) * LDKT + tp) = xh;
+            *reinterpret_cast<bf16x4*>(sm.kt_lo + trow(c) * LDKT + tp) = xl;
+        }
+    }
+    if (WANT_Q) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = m + 16 * j;
+            const int o0 = row * LDQ + pk(c8), o1 = row * LDQ + pk(c8 + 4);
+            if constexpr (EX) {
+                *reinterpret_cast<u32x2*>(sm.q_hi + o0) = u32x2{r.q[j][0], r.q[j][1]};
+                *reinterpret_cast<u32x2*>(sm.q_hi + o1) = u32x2{r.q[j][2], r.q[j][3]};
+            } else {
+                bf16x4 ah, al, bh, bl;
+                split4(r.q[2 * j], ah, al);
+                split4(r.q[2 * j + 1], bh, bl);
+                *reinterpret_cast<bf16x4*>(sm.q_hi + o0) = ah;
+                *reinterpret_cast<bf16x4*>(sm.q_lo + o0) = al;
+                *reinterpret_cast<bf16x4*>(sm.q_hi + o1) = bh;
+                *reinterpret_cast<bf16x4*>(sm.q_lo + o1) = bl;
+            }
+        }
+    }
+    // T: piece t + 256 j of the [part][row][64] image -> row part * 64 + row of sm.t
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int pc = t + NTHR * j, prow = pc >> 3, k8 = (pc & 7) * 8;
+        *reinterpret_cast<u32x4*>(sm.t + prow * LDP + k8) = r.t[j];
+    }
+}
+
+// scale P, P = (Q K^T) o D, on the ten lower 16x16 tiles (16x16x32 MFMA, each tile
+// computed transposed so that a lane holds four consecutive columns of one
+// row), split into hi/lo; the two upper tiles inside the diagonal 32-blocks,
+// which the P V' product reads, are zeroed. Jobs first, first + stride, ...
+template <bool EX, int NJOB>
+__device__ void gram_p(ChainSmem<EX>& sm, int first, int stride, float scale) {
+    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
+    f32x4 acc[NJOB];
+    int bi[NJOB], bj[NJOB];
+#pragma unroll
+    for (int t = 0; t < NJOB; ++t) {
+        lower_tile(first + stride * t, bi[t], bj[t]);
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int kb = 32 * ks + 8 * g4;
+#pragma unroll
+        for (int t = 0; t < NJOB; ++t) {
+            const int ra = 16 * bj[t] + n, rb = 16 * bi[t] + n;   // A: K rows of bj; B: Q rows of bi
+            const bf16x8 a = lds_row8(sm.k_hi + ra * LDQ + kb);
+            const bf16x8 b = lds_row8(sm.q_hi + rb * LDQ + kb);
+            acc[t] = mma16k32(a, b, acc[t]);
+            if (!EX) {
+                acc[t] = mma16k32(a, lds_row8(sm.q_lo + rb * LDQ + kb), acc[t]);
+                acc[t] = mma16k32(lds_row8(sm.k_lo + ra * LDQ + kb), b, acc[t]);
             }
         }
     }
@@ -508,229 +758,22 @@ __device__ void gram_jobs(Smem<Io<IO>::kExact>& sm, const IO* krow0, size_t ts, 
         const f32x4 gj = *reinterpret_cast<const f32x4*>(sm.gam + j0);
         f32x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float d = __expf(gi - gj[r]);
-            v[r] = isq[t] ? ((i >= j0 + r) ? d * acc[t][r] : 0.f) : ((i > j0 + r) ? d * acc[t][r] : 0.f);
-        }
-        if (!isq[t]) {
-            *reinterpret_cast<f32x4*>(sm.x.a + i * LDF + j0) = v * sm.beta[i];
-        } else {
-            unsigned h0, h1, l0, l1;
-            split_pair(v[0], v[1], h0, l0);
-            split_pair(v[2], v[3], h1, l1);
-            *reinterpret_cast<u32x2*>(sm.p_hi + i * LDP + pk(j0)) = u32x2{h0, h1};
-            *reinterpret_cast<u32x2*>(sm.p_lo + i * LDP + pk(j0)) = u32x2{l0, l1};
-        }
+        for (int r = 0; r < 4; ++r) v[r] = (i >= j0 + r) ? scale * __expf(gi - gj[r]) * acc[t][r] : 0.f;
+        bf16x4 hi, lo;
+        split4(v, hi, lo);
+        *reinterpret_cast<bf16x4*>(sm.p + i * LDP + pk(j0)) = hi;
+        *reinterpret_cast<bf16x4*>(sm.p + (CH + i) * LDP + pk(j0)) = lo;
     }
 }
 
-// Zero P on the upper 16x16 tile of a diagonal 32x32 block (read by the P V' product).
-template <bool EX>
-__device__ void zero_p_tile(Smem<EX>& sm, int bi, int bj) {
-    const int lane = lane_id();
-    const bf16 z = (bf16)0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = lane + 64 * e, r = 16 * bi + (idx >> 4), c = 16 * bj + (idx & 15);
-        sm.p_hi[r * LDP + pk(c)] = z;
-        sm.p_lo[r * LDP + pk(c)] = z;
-    }
+__device__ __forceinline__ void zero_p_tile(bf16* p, int bi, int bj) {
+    // lane: row 16 bi + lane / 4, columns 16 bj + 4 (lane % 4) .. + 4, hi and lo
+    const int lane = lane_id(), i = 16 * bi + (lane >> 2), j0 = 16 * bj + 4 * (lane & 3);
+    *reinterpret_cast<u32x2*>(p + i * LDP + pk(j0)) = u32x2{0u, 0u};
+    *reinterpret_cast<u32x2*>(p + (CH + i) * LDP + pk(j0)) = u32x2{0u, 0u};
 }
 
-// Diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution. Every
-// wave solves all four blocks (lane 16 b + j: block b, column j) and writes
-// them; the values are identical across waves, so each wave can read the
-// blocks back without waiting for the others.
-template <bool EX>
-__device__ void inv_diag(Smem<EX>& sm) {
-    const int lane = lane_id(), b = 16 * (lane >> 4), j = lane & 15;
-    const float* A = sm.x.a + b * LDF + b;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float s = (i == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < i; ++m) s = fmaf(-A[i * LDF + m], x[m], s);
-        x[i] = s;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.u.t[(b + i) * LDF + b + j] = x[i];
-}
-
-// Block column J of T below the diagonal: T_iJ = -X_i sum_{m=J}^{i-1} A_im T_mJ,
-// with 16x16x16 bf16 MFMAs on hi/lo operands (lane l: A row l % 16, k 4 (l/16)..;
-// B / C column l % 16, rows 4 (l/16)..). Zeros above the diagonal block.
-template <int J, bool EX>
-__device__ void inv_col(Smem<EX>& sm) {
-    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
-    f32x4 Tc[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Tc[J][r] = sm.u.t[(16 * J + 4 * g4 + r) * LDF + 16 * J + n];
-#pragma unroll
-    for (int i = J + 1; i < 4; ++i) {
-        f32x4 R = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = J; m < i; ++m) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(sm.x.a + (16 * i + n) * LDF + 16 * m + 4 * g4);
-            bf16x4 ah, al, bh, bl;
-            split4(a, ah, al);
-            split4(Tc[m], bh, bl);
-            R = mma16(ah, bh, R);
-            R = mma16(ah, bl, R);
-            R = mma16(al, bh, R);
-        }
-        const f32x4 xi = *reinterpret_cast<const f32x4*>(sm.u.t + (16 * i + n) * LDF + 16 * i + 4 * g4);
-        bf16x4 xh, xl, rh, rl;
-        split4(xi, xh, xl);
-        split4(R, rh, rl);
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
-        P = mma16(xh, rh, P);
-        P = mma16(xh, rl, P);
-        P = mma16(xl, rh, P);
-        Tc[i] = -P;
-    }
-    if constexpr (EX) {
-        // T's block column J scaled by beta e^gamma (tw) and by beta (tu), split
-        const int c = 16 * J + n;
-        const float sw = sm.bw[c], su = sm.beta[c];
-        const bf16 z = (bf16)0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * i + 4 * g4 + r;
-                bf16 wh = z, wl = z, uh = z, ul = z;
-                if (i >= J) {
-                    split1(Tc[i][r] * sw, wh, wl);
-                    split1(Tc[i][r] * su, uh, ul);
-                }
-                const int o = row * LDP + pk(c);
-                sm.tw[o] = wh;
-                sm.tw[CH * LDP + o] = wl;
-                sm.tu[o] = uh;
-                sm.tu[CH * LDP + o] = ul;
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < J; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.u.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = 0.f;
-#pragma unroll
-        for (int i = J + 1; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.u.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = Tc[i][r];
-    }
-}
-
-// U = T diag(beta) V[:, 32w:32w+32] and W = T diag(beta e^gamma) K[:, 32w:32w+32]
-// (T is lower triangular, so row tile 0 needs k steps 0..1 only). The B
-// operands come from the transposed LDS tiles (fp32 V from HBM); hi and lo
-// products accumulate into separate tiles so that four or more independent
-// MFMA chains are in flight.
-template <typename IO>
-__device__ void wy_tiles(const Smem<Io<IO>::kExact>& sm, const IO* vcol, size_t ts, int nvalid,
-                         bool want_U, f32x16 U[2], f32x16 W[2]) {
-    constexpr bool EX = Io<IO>::kExact;
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
-    const int n = 32 * wave_id() + col;
-    U[0] = U[1] = W[0] = W[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 kh, kl, vh, vl;
-        kh = lds_op16(sm.kt_hi + n * LDKT + 16 * ks + 8 * h);
-        if (!EX) kl = lds_op16(sm.kt_lo + n * LDKT + 16 * ks + 8 * h);
-        if (want_U) {
-            if constexpr (EX) vh = lds_op16(sm.vt + n * LDKT + 16 * ks + 8 * h);
-            else g_col_op<IO>(vcol, ts, 16 * ks, h, nvalid, vh, vl);
-        }
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            if (ti == 0 && ks >= 2) continue;
-            const int r = 32 * ti + col;
-            bf16x8 wah, wal, uah, ual;
-            if constexpr (EX) {
-                wah = lds_op16(sm.tw + r * LDP + 16 * ks + 8 * h);
-                wal = lds_op16(sm.tw + CH * LDP + r * LDP + 16 * ks + 8 * h);
-                uah = lds_op16(sm.tu + r * LDP + 16 * ks + 8 * h);
-                ual = lds_op16(sm.tu + CH * LDP + r * LDP + 16 * ks + 8 * h);
-            } else {
-                f32_op<true>(sm.u.t + r * LDF + 16 * ks + 4 * h, sm.bw + 16 * ks + 4 * h, wah, wal);
-                f32_op<true>(sm.u.t + r * LDF + 16 * ks + 4 * h, sm.beta + 16 * ks + 4 * h, uah, ual);
-            }
-            W[ti] = mma32(wah, kh, W[ti]);
-            if (want_U) U[ti] = mma32(uah, vh, U[ti]);
-            W[ti] = mma32(wal, kh, W[ti]);
-            if (want_U) U[ti] = mma32(ual, vh, U[ti]);
-            if (!EX) {
-                W[ti] = mma32(wah, kl, W[ti]);
-                if (want_U) U[ti] = mma32(uah, vl, U[ti]);
-            }
-        }
-    }
-}
-
-// Chunk preparation, part 1 (after stage_chunk and a barrier): the gram
-// products. A = masked beta K K^T goes to LDS, and P = masked Q K^T when the
-// output is wanted. The caller then synchronises.
-template <typename IO, bool WANT_P>
-__device__ void prep_gram(Smem<Io<IO>::kExact>& sm, const Params& p, size_t tok0, int nvalid, int hq) {
-    const int wave = wave_id();
-    const size_t ts_qk = (size_t)p.h_qk * DK;
-    const IO* krow0 = static_cast<const IO*>(p.k) + tok0 * ts_qk + (size_t)hq * DK;
-    if constexpr (Io<IO>::kExact) transpose_kv(sm);
-    if (WANT_P) {
-        gram_jobs<IO, 5>(sm, krow0, ts_qk, nvalid, wave, 4);   // jobs w, w+4, ..., w+16
-        if (wave == 0) zero_p_tile(sm, 0, 1);
-        if (wave == 1) zero_p_tile(sm, 2, 3);
-    } else {
-        // the ten K K^T tiles: three per wave, the last wave takes one
-        if (wave < 3) gram_jobs<IO, 3>(sm, krow0, ts_qk, nvalid, wave, 3);
-        else gram_jobs<IO, 1>(sm, krow0, ts_qk, nvalid, 9, 1);
-    }
-}
-
-// Chunk preparation, part 2 (after prep_gram and a barrier): T = (I + A)^-1,
-// U = T diag(beta) V for this wave's columns and W = T diag(beta e^gamma) K.
-// On return (before the caller's barrier) -W is being written to LDS; U and
-// this wave's W tile are in registers.
-template <typename IO>
-__device__ void prep_wy(Smem<Io<IO>::kExact>& sm, const Params& p, size_t tok0, int nvalid, int h,
-                        bool want_U, f32x16 U[2], f32x16 Wt[2]) {
-    constexpr bool EX = Io<IO>::kExact;
-    const int wave = wave_id(), lane = lane_id(), col = lane & 31, hh = lane >> 5;
-    inv_diag<EX>(sm);
-    // the diagonal blocks this wave reads next are the ones it just wrote
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    switch (wave) {
-        case 0: inv_col<0, EX>(sm); break;
-        case 1: inv_col<1, EX>(sm); break;
-        case 2: inv_col<2, EX>(sm); break;
-        default: inv_col<3, EX>(sm); break;
-    }
-    __syncthreads();
-    const size_t ts_v = (size_t)p.h_v * DK;
-    const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 32 * wave + col;
-    wy_tiles<IO>(sm, vcol, ts_v, nvalid, want_U, U, Wt);
-    // -W as hi/lo into the region that held A (all reads of A are behind the barrier)
-#pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 32 * ti + acc_row(i, hh), c = 32 * wave + col;
-            bf16 th, tl;
-            split1(-Wt[ti][i], th, tl);
-            sm.x.w[r * LDQ + pk(c)] = th;
-            sm.x.w[CH * LDQ + r * LDQ + pk(c)] = tl;
-        }
-}
-
-// ----------------------------------------------------------------------------
-// The state chain of one chunk (after prep_chunk and a barrier).
-//   Vp (holds U on entry): V' = U - W S
-//   O (if OUT):            O = diag(e^gamma) Q S + P V'   (scale applied at the store)
-//   S:                     S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
-// The state as hi/lo B operands, one pair per 16-row k step (computed once per
-// chunk, used by both products with S).
+// The state as hi/lo B operands, one pair per 16-row k step.
 struct SplitS {
     bf16x8 hi[8], lo[8];
 };
@@ -739,36 +782,83 @@ __device__ __forceinline__ void split_state(const f32x16 S[4], SplitS& ss) {
     for (int ks = 0; ks < 8; ++ks) split_half(S[ks >> 1], ks & 1, ss.hi[ks], ss.lo[ks]);
 }
 
-// V' = U - W S (Vp holds U on entry).
-template <bool EX>
-__device__ void chain_vp(const Smem<EX>& sm, const SplitS& ss, f32x16 Vp[2]) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
+// V' = T diag(beta) (V - diag(e^gamma) K S) for this wave's columns.
+// KS: A = K rows (token-major LDS), B = S; Y in fp32 on the accumulators
+// (V from V^T in LDS, four consecutive tokens per 8-byte read, or from HBM
+// for fp32 inputs); then (T diag(beta)) Y with both split hi/lo (T is lower
+// triangular: token tile 0 needs k steps 0..1).
+template <typename IO, bool WANT_V>
+__device__ void chain_vp(const ChainSmem<Io<IO>::kExact>& sm, const SplitS& ss, const IO* vcol, size_t ts,
+                         int nvalid, f32x16 Vp[2]) {
+    constexpr bool EX = Io<IO>::kExact;
+    const int lane = lane_id(), col = lane & 31, h = lane >> 5, n = 32 * wave_id() + col;
+    f32x16 KS[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 wh[2], wl[2];
+        bf16x8 kh[2], kl[2];
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
-            const int r = 32 * ti + col;
-            wh[ti] = lds_op16(sm.x.w + r * LDQ + 16 * ks + 8 * h);
-            wl[ti] = lds_op16(sm.x.w + CH * LDQ + r * LDQ + 16 * ks + 8 * h);
+            kh[ti] = lds_op16(sm.k_hi + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
+            if (!EX) kl[ti] = lds_op16(sm.k_lo + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
         }
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) Vp[ti] = mma32(wh[ti], ss.hi[ks], Vp[ti]);
+        for (int ti = 0; ti < 2; ++ti) KS[ti] = mma32(kh[ti], ss.hi[ks], KS[ti]);
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) Vp[ti] = mma32(wh[ti], ss.lo[ks], Vp[ti]);
+        for (int ti = 0; ti < 2; ++ti) KS[ti] = mma32(kh[ti], ss.lo[ks], KS[ti]);
+        if (!EX) {
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) Vp[ti] = mma32(wl[ti], ss.hi[ks], Vp[ti]);
+            for (int ti = 0; ti < 2; ++ti) KS[ti] = mma32(kl[ti], ss.hi[ks], KS[ti]);
+        }
+    }
+    // Y = V - e^gamma KS on rows 32 ti + 8 q + 4 h + (0..3)
+    const int vrow = trow(n) * LDKT;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r0 = 32 * ti + 8 * q + 4 * h;
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(sm.eg + r0);
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (WANT_V) {
+                if constexpr (EX) {
+                    const u32x2 vv = *reinterpret_cast<const u32x2*>(sm.vt + vrow + pk(r0));
+                    v = f32x4{__uint_as_float(vv[0] << 16), __uint_as_float(vv[0] & 0xffff0000u),
+                              __uint_as_float(vv[1] << 16), __uint_as_float(vv[1] & 0xffff0000u)};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (r0 + e < nvalid) ? (float)vcol[(size_t)(r0 + e) * ts] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) KS[ti][4 * q + e] = fmaf(-eg[e], KS[ti][4 * q + e], v[e]);
+        }
+    Vp[0] = Vp[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 yh, yl;
+        split_half(KS[ks >> 1], ks & 1, yh, yl);
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            if (ti == 0 && ks >= 2) continue;
+            const bf16x8 th = lds_op16(sm.t + (32 * ti + col) * LDP + 16 * ks + 8 * h);
+            const bf16x8 tl = lds_op16(sm.t + (CH + 32 * ti + col) * LDP + 16 * ks + 8 * h);
+            Vp[ti] = mma32(th, yh, Vp[ti]);
+            Vp[ti] = mma32(th, yl, Vp[ti]);
+            Vp[ti] = mma32(tl, yh, Vp[ti]);
+        }
     }
 }
 
-// O = scale (diag(e^gamma) Q S + P V') for this wave's columns (both 32-row
-// tiles, interleaved), stored to the output (rows < nvalid).
-template <typename IO>
-__device__ void chain_out(const Smem<Io<IO>::kExact>& sm, const SplitS& ss, const f32x16 Vp[2],
-                          IO* ocol, size_t ts, int nvalid, float scale) {
-    constexpr bool EX = Io<IO>::kExact;
+// O^T = scale S^T (diag(e^gamma) Q)^T for this wave's d_v rows (token columns): the
+// split state serves as the A operand unchanged (the MFMA's A and B register
+// layouts mirror each other). Then (chain_pv_out, after P is in LDS) the
+// causal part V'^T P^T and the store: a lane holds four consecutive d_v of
+// one token per accumulator group, written as one 8- (bf16) or 16-byte
+// (fp32) store; rows >= nvalid are not written.
+template <bool EX>
+__device__ void chain_qs(const ChainSmem<EX>& sm, const SplitS& ss, f32x16 O[2]) {
     const int lane = lane_id(), col = lane & 31, h = lane >> 5;
-    f32x16 O[2] = {f32x16{}, f32x16{}};
+    O[0] = O[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
         bf16x8 qh[2], ql[2];
@@ -778,71 +868,66 @@ __device__ void chain_out(const Smem<Io<IO>::kExact>& sm, const SplitS& ss, cons
             if (!EX) ql[ti] = lds_op16(sm.q_lo + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
         }
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(qh[ti], ss.hi[ks], O[ti]);
+        for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(ss.hi[ks], qh[ti], O[ti]);
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(qh[ti], ss.lo[ks], O[ti]);
+        for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(ss.lo[ks], qh[ti], O[ti]);
         if (!EX) {
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(ql[ti], ss.hi[ks], O[ti]);
+            for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(ss.hi[ks], ql[ti], O[ti]);
         }
     }
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int ti = 0; ti < 2; ++ti) O[ti] *= sm.egs[32 * ti + col];
+}
+
+template <typename IO>
+__device__ void chain_pv_out(const ChainSmem<Io<IO>::kExact>& sm, const f32x16 Vp[2], f32x16 O[2], IO* orow0,
+                             size_t ts, int nvalid) {
+    constexpr bool EX = Io<IO>::kExact;
+    const int lane = lane_id(), col = lane & 31, h = lane >> 5, w = wave_id();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) O[ti][i] *= sm.eg[32 * ti + acc_row(i, h)];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {  // P is causal: row tile 0 needs k steps 0..1
+    for (int ks = 0; ks < 4; ++ks) {  // P is causal: token tile 0 needs k steps 0..1
         bf16x8 vh, vl;
         split_half(Vp[ks >> 1], ks & 1, vh, vl);
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
             if (ti == 0 && ks >= 2) continue;
-            const bf16x8 ph = lds_op16(sm.p_hi + (32 * ti + col) * LDP + 16 * ks + 8 * h);
-            const bf16x8 pl = lds_op16(sm.p_lo + (32 * ti + col) * LDP + 16 * ks + 8 * h);
-            O[ti] = mma32(ph, vh, O[ti]);
-            O[ti] = mma32(ph, vl, O[ti]);
-            O[ti] = mma32(pl, vh, O[ti]);
+            const bf16x8 ph = lds_op16(sm.p + (32 * ti + col) * LDP + 16 * ks + 8 * h);
+            const bf16x8 pl = lds_op16(sm.p + (CH + 32 * ti + col) * LDP + 16 * ks + 8 * h);
+            O[ti] = mma32(vh, ph, O[ti]);
+            O[ti] = mma32(vl, ph, O[ti]);
+            O[ti] = mma32(vh, pl, O[ti]);
         }
     }
-    if constexpr (EX) {
-        // staged in LDS (the T' / T'' area is free until the next chunk's
-        // inverse); written to HBM in 16-byte row pieces by store_out
-        bf16* st = const_cast<bf16*>(sm.tw);
-        const int c = 32 * wave_id() + col;
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
+    for (int ti = 0; ti < 2; ++ti) {
+        const int r = 32 * ti + col;
+        if (r >= nvalid) continue;
+        IO* dst = orow0 + (size_t)r * ts + 32 * w + 4 * h;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) st[(32 * ti + acc_row(i, h)) * LDO + c] = (bf16)(O[ti][i] * scale);
-    } else {
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = 32 * ti + acc_row(i, h);
-                if (row < nvalid) ocol[(size_t)row * ts] = (IO)(O[ti][i] * scale);
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 x = f32x4{O[ti][4 * q], O[ti][4 * q + 1], O[ti][4 * q + 2], O[ti][4 * q + 3]};
+            if constexpr (EX) {
+                *reinterpret_cast<u32x2*>(dst + 8 * q) = u32x2{pack_rne(x[0], x[1]), pack_rne(x[2], x[3])};
+            } else {
+                *reinterpret_cast<f32x4*>(dst + 8 * q) = x;
             }
-    }
-}
-
-// Copies the staged bf16 output tile of a chunk to HBM (after a barrier).
-__device__ void store_out(const Smem<true>& sm, bf16* orow0, size_t ts, int nvalid) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int pc = threadIdx.x + NTHR * it, row = pc >> 4, c8 = (pc & 15) * 8;
-        if (row < nvalid)
-            *reinterpret_cast<u32x4*>(orow0 + (size_t)row * ts + c8) =
-                *reinterpret_cast<const u32x4*>(sm.tw + row * LDO + c8);
+        }
     }
 }
 
 // S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V' (Vp is scaled in place).
 template <bool EX>
-__device__ void chain_state(const Smem<EX>& sm, f32x16 S[4], f32x16 Vp[2]) {
+__device__ void chain_state(const ChainSmem<EX>& sm, f32x16 S[4], f32x16 Vp[2]) {
     const int lane = lane_id(), col = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Vp[ti][i] *= sm.egc[32 * ti + acc_row(i, h)];
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 e = *reinterpret_cast<const f32x4*>(sm.egc + 32 * ti + 8 * q + 4 * h);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Vp[ti][4 * q + r] *= e[r];
+        }
     const float ec = sm.red[0];
 #pragma unroll
     for (int t = 0; t < 4; ++t) S[t] *= ec;
@@ -853,8 +938,8 @@ __device__ void chain_state(const Smem<EX>& sm, f32x16 S[4], f32x16 Vp[2]) {
         bf16x8 kh[4], kl[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            kh[t] = lds_op16(sm.kt_hi + (32 * t + col) * LDKT + 16 * ks + 8 * h);
-            if (!EX) kl[t] = lds_op16(sm.kt_lo + (32 * t + col) * LDKT + 16 * ks + 8 * h);
+            kh[t] = lds_op16(sm.kt_hi + trow(32 * t + col) * LDKT + 16 * ks + 8 * h);
+            if (!EX) kl[t] = lds_op16(sm.kt_lo + trow(32 * t + col) * LDKT + 16 * ks + 8 * h);
         }
         // four independent chains: each tile is touched once per pass
 #pragma unroll
@@ -902,49 +987,166 @@ __device__ __forceinline__ size_t state_off(int idx, int h_v, int h) {
     return ((size_t)idx * h_v + h) * (size_t)DK * DK;
 }
 
+// Runs chunks [c_lo, c_hi) of sequence loc from the state S (no outputs):
+// the warm-up scan, the H chain (WANT_V) or the M chain (V = 0, S starts at I).
+template <typename IO, bool WANT_V>
+__device__ void scan_chunks(ChainSmem<Io<IO>::kExact>& sm, const Params& p, const SegLoc& loc, int h, int hq,
+                            int c_lo, int c_hi, f32x16 S[4]) {
+    constexpr bool EX = Io<IO>::kExact;
+    const size_t ts_v = (size_t)p.h_v * DK;
+    Chunk<IO> nxt;
+    if (c_lo < c_hi)
+        fetch_chunk<IO, false, WANT_V>(nxt, p, loc.tok0 + (size_t)c_lo * CH, min(CH, loc.len - c_lo * CH), h, hq,
+                                       loc.chunk_base + c_lo);
+    for (int c = c_lo; c < c_hi; ++c) {
+        const size_t tok0 = loc.tok0 + (size_t)c * CH;
+        const int nvalid = min(CH, loc.len - c * CH);
+        stage_chunk<IO, false, WANT_V>(sm, nxt, 1.f);
+        __syncthreads();
+        if (c + 1 < c_hi)
+            fetch_chunk<IO, false, WANT_V>(nxt, p, tok0 + CH, min(CH, loc.len - (c + 1) * CH), h, hq,
+                                           loc.chunk_base + c + 1);
+        f32x16 Vp[2];
+        {
+            SplitS ss;
+            split_state(S, ss);
+            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 32 * wave_id() + (lane_id() & 31);
+            chain_vp<IO, WANT_V>(sm, ss, vcol, ts_v, nvalid, Vp);
+        }
+        chain_state<EX>(sm, S, Vp);
+        __syncthreads();
+    }
+}
+
 // ----------------------------------------------------------------------------
 // Kernels
 
-// Low-level chunk preparation: gamma, W, U of every (chunk, value head).
+// Low-level chunk preparation, second half: W = (T diag(beta)) diag(e^gamma) K
+// and U = (T diag(beta)) V of every (chunk, value head), from T diag(beta)
+// (split) and gamma, beta, which k_prep left in the chunk's W_out and U_out
+// blocks. Wave w produces columns [32w, 32w + 32) of both.
 template <typename IO>
-__global__ __launch_bounds__(NTHR) void k_chunk_prep(Params p) {
+__global__ __launch_bounds__(NTHR) void k_wu(Params p) {
     constexpr bool EX = Io<IO>::kExact;
-    __shared__ Smem<EX> sm;
+    __shared__ ChainSmem<EX> sm;
     const int h = blockIdx.y, hq = h / p.group;
     int seq, c, len;
     size_t tok_s;
     if (!locate_chunk(p, blockIdx.x, seq, c, len, tok_s)) return;
     const size_t tok0 = tok_s + (size_t)c * CH;
     const int nvalid = min(CH, len - c * CH);
+    float gl;
     {
         Chunk<IO> r;
-        fetch_chunk<IO, false>(r, p, tok0, nvalid, h, hq);
-        stage_chunk<IO, false>(sm, r);
+        fetch_chunk<IO, false, true>(r, p, tok0, nvalid, h, hq, blockIdx.x);
+        stage_chunk<IO, false, true>(sm, r, 1.f);
+        gl = r.gl;
     }
-    __syncthreads();
-    f32x16 U[2], Wt[2];
-    prep_gram<IO, false>(sm, p, tok0, nvalid, hq);
-    __syncthreads();
-    prep_wy<IO>(sm, p, tok0, nvalid, h, true, U, Wt);
-    const int lane = lane_id(), col = lane & 31, hh = lane >> 5, w = wave_id();
+    __syncthreads();   // every read of T, gamma and beta is done before W and U overwrite them
+    const int lane = lane_id(), col = lane & 31, hh = lane >> 5, w = wave_id(), n = 32 * w + col;
+    const size_t ts_v = (size_t)p.h_v * DK, ts_k = (size_t)p.h_qk * DK;
+    const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + n;
+    const IO* kcol = static_cast<const IO*>(p.k) + tok0 * ts_k + (size_t)hq * DK + n;
+    f32x16 W[2] = {f32x16{}, f32x16{}}, U[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        // B operands: column n, tokens 16 ks + kperm(hh, e) (K scaled by e^gamma of the token)
+        const f32x4 eg0 = *reinterpret_cast<const f32x4*>(sm.eg + 16 * ks + 4 * hh);
+        const f32x4 eg1 = *reinterpret_cast<const f32x4*>(sm.eg + 16 * ks + 8 + 4 * hh);
+        // K and V at those tokens: exact bf16 from LDS, or fp32 from HBM
+        f32x4 k0, k1, v0, v1;
+        if constexpr (EX) {
+            const bf16x8 kh = lds_op16(sm.kt_hi + trow(n) * LDKT + 16 * ks + 8 * hh);
+            const bf16x8 vh = lds_op16(sm.vt + trow(n) * LDKT + 16 * ks + 8 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                k0[e] = (float)kh[e];
+                k1[e] = (float)kh[4 + e];
+                v0[e] = (float)vh[e];
+                v1[e] = (float)vh[4 + e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t0 = 16 * ks + 4 * hh + e, t1 = t0 + 8;
+                k0[e] = t0 < nvalid ? (float)kcol[(size_t)t0 * ts_k] : 0.f;
+                k1[e] = t1 < nvalid ? (float)kcol[(size_t)t1 * ts_k] : 0.f;
+                v0[e] = t0 < nvalid ? (float)vcol[(size_t)t0 * ts_v] : 0.f;
+                v1[e] = t1 < nvalid ? (float)vcol[(size_t)t1 * ts_v] : 0.f;
+            }
+        }
+        k0 *= eg0;
+        k1 *= eg1;
+        bf16x4 a0, a1, b0, b1;
+        bf16x8 kbh, kbl, vbh, vbl;
+        split4(k0, a0, b0);
+        split4(k1, a1, b1);
+        kbh = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        kbl = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        split4(v0, a0, b0);
+        split4(v1, a1, b1);
+        vbh = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        vbl = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            if (ti == 0 && ks >= 2) continue;
+            const bf16x8 th = lds_op16(sm.t + (32 * ti + col) * LDP + 16 * ks + 8 * hh);
+            const bf16x8 tl = lds_op16(sm.t + (CH + 32 * ti + col) * LDP + 16 * ks + 8 * hh);
+            W[ti] = mma32(th, kbh, W[ti]);
+            W[ti] = mma32(th, kbl, W[ti]);
+            W[ti] = mma32(tl, kbh, W[ti]);
+            U[ti] = mma32(th, vbh, U[ti]);
+            U[ti] = mma32(th, vbl, U[ti]);
+            U[ti] = mma32(tl, vbh, U[ti]);
+        }
+    }
     const size_t base = ((size_t)blockIdx.x * p.h_v + h) * CH;
-    if (w == 0) p.prep_gamma[base + lane] = sm.gam[lane];
+    if (w == 0) p.prep_gamma[base + lane] = gl;
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const size_t r = base + 32 * ti + acc_row(i, hh);
-            p.prep_W[r * DK + 32 * w + col] = Wt[ti][i];
-            p.prep_U[r * DK + 32 * w + col] = U[ti][i];
+            p.prep_W[r * DK + n] = W[ti][i];
+            p.prep_U[r * DK + n] = U[ti][i];
         }
+}
+
+// The map M of a segment, written for the combine kernel: split into hi/lo
+// bf16 and laid out as that kernel's MFMA A operands, so that its loads are
+// contiguous and it does no splitting on its sequential path. Element
+// M[r][k] goes to ((((r / 32) * 8 + k / 16) * 2 + part) * 64 + lane) * 8 + e
+// with lane = r % 32 + 32 h, k % 16 = kperm(h, e), part 0 = hi, 1 = lo
+// (64 KiB per map). The chunk loop's LDS serves as the staging buffer; the
+// caller's chain is finished (behind a barrier) when this starts.
+__device__ void store_m_operand(bf16* buf, const f32x16 S[4], bf16* dst) {
+    const int lane = lane_id(), col = lane & 31, h = lane >> 5, w = wave_id();
+    const int kk = col & 15, ks = 2 * w + (col >> 4);
+    const int hh = (kk >> 2) & 1, e = (kk & 3) | ((kk & 8) >> 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r2 = acc_row(i, h);   // row within the 32-row block t
+            const int idx = (((t * 8 + ks) * 2) * 64 + r2 + 32 * hh) * 8 + e;
+            bf16 hi, lo;
+            split1(S[t][i], hi, lo);
+            buf[idx] = hi;
+            buf[idx + 64 * 8] = lo;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int off = (threadIdx.x + NTHR * it) * 8;
+        *reinterpret_cast<u32x4*>(dst + off) = *reinterpret_cast<const u32x4*>(buf + off);
+    }
 }
 
 // Warm-up or exact segment map for the boundary before segment s >= 1.
 // blockIdx.x = 2 * segment slot + part; part 0: warm-up state or H, part 1: M.
 template <typename IO>
 __global__ __launch_bounds__(NTHR) void k_cp_prep(Params p) {
-    constexpr bool EX = Io<IO>::kExact;
-    __shared__ Smem<EX> sm;
+    __shared__ ChainSmem<Io<IO>::kExact> sm;
     const int slot = blockIdx.x >> 1, part = blockIdx.x & 1, h = blockIdx.y, hq = h / p.group;
     const SegLoc loc = locate_segment(p, slot);
     if (loc.seq < 0 || loc.s == 0) return;
@@ -952,26 +1154,40 @@ __global__ __launch_bounds__(NTHR) void k_cp_prep(Params p) {
 
     // Gate-driven choice: warm up iff the log-decay over the window of w chunks
     // before the boundary is at most log(noise floor) (or the window reaches
-    // the sequence start, where the warm-up is exact).
+    // the sequence start, where the warm-up is exact). The warm-up then scans
+    // the shortest run of chunks before the boundary (wq <= w) whose log-decay
+    // is already at most log(noise floor); the state it misses is bounded by
+    // that decay times the state at the run's start.
     // warm: 0 exact map, 1 warm-up (decayed below the floor, or forced), 2 warm-up
     // from the sequence start (exact)
-    int warm;
+    int warm, wq = p.w;
     if (p.cp_mode == kCpExact) {
         warm = 0;
     } else if (a - p.w <= 0) {
         warm = 2;
-    } else if (p.cp_mode == kCpWarmup) {
-        warm = 1;
+        wq = a;
     } else {
-        const size_t t0 = loc.tok0 + (size_t)(a - p.w) * CH;
-        float s = 0.f;
-        for (int t = threadIdx.x; t < p.w * CH; t += NTHR) s += p.g[(t0 + t) * (size_t)p.h_v + h];
+        // chunk a - 1 - j (a full chunk: only a sequence's last chunk is short) -> red[j]
+        const int wave = wave_id(), lane = lane_id();
+        for (int j = wave; j < p.w; j += 4) {
+            float s = p.g[(loc.tok0 + (size_t)(a - 1 - j) * CH + lane) * (size_t)p.h_v + h];
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
-        if (lane_id() == 0) sm.red[8 + wave_id()] = s;
+            for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+            if (lane == 0) sm.red[j] = s;
+        }
         __syncthreads();
-        const float tot = sm.red[8] + sm.red[9] + sm.red[10] + sm.red[11];
-        warm = (tot <= p.log_eps) ? 1 : 0;
+        float cum = 0.f;
+        int found = 0;
+        for (int j = 0; j < p.w && !found; ++j) {
+            cum += sm.red[j];
+            if (cum <= p.log_eps) found = j + 1;
+        }
+        if (found) {
+            warm = 1;
+            wq = found;
+        } else {
+            warm = (p.cp_mode == kCpWarmup) ? 1 : 0;
+        }
         __syncthreads();
     }
     if (part == 0 && threadIdx.x == 0) p.warm[(size_t)(loc.seg_base + loc.s) * p.h_v + h] = warm;
@@ -980,58 +1196,58 @@ __global__ __launch_bounds__(NTHR) void k_cp_prep(Params p) {
     if (!warm && part == 1 && loc.s == 1 && !p.s_init) return;
 
     f32x16 S[4];
-    int c_lo, c_hi;
-    bool want_U = true;
+    float* dst;
     if (warm) {
-        c_lo = max(a - p.w, 0);
-        c_hi = a;
+        const int c_lo = a - wq;
         if (c_lo == 0 && p.s_init) load_state(p.s_init + state_off(loc.seq, p.h_v, h), S);
         else zero_state(S);
+        scan_chunks<IO, true>(sm, p, loc, h, hq, c_lo, a, S);
+        dst = p.seg_state + state_off(loc.seg_base + loc.s, p.h_v, h);
+    } else if (part == 0) {
+        zero_state(S);
+        scan_chunks<IO, true>(sm, p, loc, h, hq, a - p.L, a, S);
+        dst = p.seg_H + state_off(loc.seg_base + loc.s - 1, p.h_v, h);
     } else {
-        c_lo = a - p.L;
-        c_hi = a;
-        if (part == 0) {
-            zero_state(S);
-        } else {
-            identity_state(S);
-            want_U = false;
-        }
+        identity_state(S);
+        scan_chunks<IO, false>(sm, p, loc, h, hq, a - p.L, a, S);
+        store_m_operand(reinterpret_cast<bf16*>(&sm), S,
+                        reinterpret_cast<bf16*>(p.seg_M + state_off(loc.seg_base + loc.s - 1, p.h_v, h)));
+        return;
     }
-    Chunk<IO> nxt;
-    if (c_lo < c_hi)
-        fetch_chunk<IO, false>(nxt, p, loc.tok0 + (size_t)c_lo * CH, min(CH, loc.len - c_lo * CH), h, hq);
-    for (int c = c_lo; c < c_hi; ++c) {
-        const size_t tok0 = loc.tok0 + (size_t)c * CH;
-        const int nvalid = min(CH, loc.len - c * CH);
-        stage_chunk<IO, false>(sm, nxt);
-        __syncthreads();
-        prep_gram<IO, false>(sm, p, tok0, nvalid, hq);
-        __syncthreads();
-        if (c + 1 < c_hi)
-            fetch_chunk<IO, false>(nxt, p, tok0 + CH, min(CH, loc.len - (c + 1) * CH), h, hq);
-        f32x16 U[2], Wt[2];
-        prep_wy<IO>(sm, p, tok0, nvalid, h, want_U, U, Wt);
-        __syncthreads();
-        {
-            SplitS ss;
-            split_state(S, ss);
-            chain_vp<EX>(sm, ss, U);
-        }
-        chain_state<EX>(sm, S, U);
-        __syncthreads();
-    }
-    float* dst;
-    if (warm) dst = p.seg_state + state_off(loc.seg_base + loc.s, p.h_v, h);
-    else if (part == 0) dst = p.seg_H + state_off(loc.seg_base + loc.s - 1, p.h_v, h);
-    else dst = p.seg_M + state_off(loc.seg_base + loc.s - 1, p.h_v, h);
     store_state(dst, S);
 }
 
 // Sequential composition of the exact segment maps for one (sequence, head,
 // 32-column block): S0(s) = M_{s-1} S0(s-1) + H_{s-1}, or the warm-up state
 // where the boundary warmed up. Wave w computes rows [32w, 32w + 32).
+// Each step is one 128 x 32 x 128 product on hi/lo operands. M arrives split
+// and in A-operand order (contiguous loads, requested one step ahead); each
+// lane writes the split of its rows of the new S0 straight into the B-operand
+// slots of the next step (its accumulator rows are exactly that operand's k
+// values), so the sequential path has no operand shuffling; the three partial
+// products (hi hi, hi lo, lo hi) run as independent MFMA chains. The boundary
+// flags come from LDS (the planner keeps segments per sequence within
+// kMaxFlags), so no step waits on a global load to branch.
+struct CombineIn {
+    f32x16 tile;      // H_{s-1} or the warm-up state, this wave's rows
+    bf16x8 ah[8], al[8];   // this lane's A operands of M_{s-1}
+};
+
+__device__ __forceinline__ void combine_split_out(bf16* sB, const f32x16& acc, int w, int lane) {
+    // sB: [ks][part][lane][8]; rows 32w + acc_row(i, h) are k = 16 (2w + i / 8) + kperm(h, i % 8)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        bf16x8 hi, lo;
+        split_half(acc, half, hi, lo);
+        const int ks = 2 * w + half;
+        *reinterpret_cast<bf16x8*>(sB + ((ks * 2 + 0) * 64 + lane) * 8) = hi;
+        *reinterpret_cast<bf16x8*>(sB + ((ks * 2 + 1) * 64 + lane) * 8) = lo;
+    }
+}
+
 __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
-    __shared__ __attribute__((aligned(16))) float sT[2][32 * LDC];  // S0 block, [column][d_k]
+    __shared__ __attribute__((aligned(16))) bf16 sB[2][8 * 2 * 64 * 8];  // S0 block as split B operands
+    __shared__ int wflag[kMaxFlags];
     const int seq = blockIdx.x >> 2, cb = blockIdx.x & 3, h = blockIdx.y;
     if (seq >= p.n_seqs) return;
     int P, seg_base;
@@ -1043,96 +1259,89 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
         for (int n = 0; n < seq; ++n) seg_base += n_segs_of(n_chunks_of(p.cu[n + 1] - p.cu[n]), p.L);
         P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
     }
-    if (P <= 1) return;
-    // boundary choices, staged in LDS so that a step never waits on a global load to branch
-    __shared__ int wflag[kMaxFlags];
+    if (P <= 1 || P > kMaxFlags) return;
     int n_exact = 0;
     for (int s = 1 + (int)threadIdx.x; s < P; s += NTHR) {
         const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h];
-        if (s < kMaxFlags) wflag[s] = f;
+        wflag[s] = f;
         n_exact += (f == 0);
     }
     if (!__syncthreads_or(n_exact)) return;
-    auto warm_of = [&](int s) {
-        return s < kMaxFlags ? wflag[s] : p.warm[(size_t)(seg_base + s) * p.h_v + h];
-    };
 
     const int lane = lane_id(), col = lane & 31, hh = lane >> 5, w = wave_id();
     const int cglob = 32 * cb + col;
-    f32x16 acc;
-    if (p.s_init) {
-        const float* S0 = p.s_init + state_off(seq, p.h_v, h);
+    {
+        f32x16 acc;
+        if (p.s_init) {
+            const float* S0 = p.s_init + state_off(seq, p.h_v, h);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = S0[(32 * w + acc_row(i, hh)) * DK + cglob];
-    } else {
-        acc = f32x16{};
+            for (int i = 0; i < 16; ++i) acc[i] = S0[(32 * w + acc_row(i, hh)) * DK + cglob];
+        } else {
+            acc = f32x16{};
+        }
+        combine_split_out(sB[0], acc, w, lane);
     }
+    auto fetch = [&](int s1, CombineIn& in) {
+        const int warm1 = wflag[s1];
+        const float* src = warm1 ? p.seg_state + state_off(seg_base + s1, p.h_v, h)
+                                 : p.seg_H + state_off(seg_base + s1 - 1, p.h_v, h);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sT[0][col * LDC + 32 * w + acc_row(i, hh)] = acc[i];
-
-    // Operands of step s (boundary s) are fetched one step ahead: the warm-up
-    // state, or H_{s-1} and this wave's rows of M_{s-1}.
-    int warm_n = 0;
-    f32x16 tile_n;
-    f32x4 m_n[16];
-    auto fetch = [&](int s) {
-        warm_n = warm_of(s);
-        const float* src = warm_n ? p.seg_state + state_off(seg_base + s, p.h_v, h)
-                                  : p.seg_H + state_off(seg_base + s - 1, p.h_v, h);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tile_n[i] = src[(32 * w + acc_row(i, hh)) * DK + cglob];
-        if (!warm_n && (s > 1 || p.s_init)) {
-            const float* mrow = p.seg_M + state_off(seg_base + s - 1, p.h_v, h) + (size_t)(32 * w + col) * DK;
+        for (int i = 0; i < 16; ++i) in.tile[i] = src[(32 * w + acc_row(i, hh)) * DK + cglob];
+        if (!warm1 && (s1 > 1 || p.s_init)) {
+            const bf16* mop = reinterpret_cast<const bf16*>(p.seg_M + state_off(seg_base + s1 - 1, p.h_v, h));
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
-                m_n[2 * ks] = *reinterpret_cast<const f32x4*>(mrow + 16 * ks + 4 * hh);
-                m_n[2 * ks + 1] = *reinterpret_cast<const f32x4*>(mrow + 16 * ks + 8 + 4 * hh);
+                in.ah[ks] = *reinterpret_cast<const bf16x8*>(mop + (((w * 8 + ks) * 2 + 0) * 64 + lane) * 8);
+                in.al[ks] = *reinterpret_cast<const bf16x8*>(mop + (((w * 8 + ks) * 2 + 1) * 64 + lane) * 8);
             }
         }
     };
-    fetch(1);
+    CombineIn nxt;
+    fetch(1, nxt);
     __syncthreads();
     int buf = 0;
     for (int s = 1; s < P; ++s) {
-        const int warm = warm_n;
-        acc = tile_n;
-        f32x4 m[16];
+        const int warm = wflag[s];
+        const bool mm = !warm && (s > 1 || p.s_init);
+        f32x16 acc = nxt.tile;
+        bf16x8 ah[8], al[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m[r] = m_n[r];
-        if (s + 1 < P) fetch(s + 1);
-        if (!warm) {
-            if (s > 1 || p.s_init) {
+        for (int ks = 0; ks < 8; ++ks) {
+            ah[ks] = nxt.ah[ks];
+            al[ks] = nxt.al[ks];
+        }
+        if (s + 1 < P) fetch(s + 1, nxt);
+        if (mm) {
+            f32x16 hl = f32x16{}, lh = f32x16{};
+            const bf16* B = sB[buf];
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    bf16x4 a0h, a0l, a1h, a1l;
-                    split4(m[2 * ks], a0h, a0l);
-                    split4(m[2 * ks + 1], a1h, a1l);
-                    const bf16x8 ah = __builtin_shufflevector(a0h, a1h, 0, 1, 2, 3, 4, 5, 6, 7);
-                    const bf16x8 al = __builtin_shufflevector(a0l, a1l, 0, 1, 2, 3, 4, 5, 6, 7);
-                    bf16x8 bh, bl;
-                    f32_op<false>(&sT[buf][col * LDC + 16 * ks + 4 * hh], nullptr, bh, bl);
-                    acc = mma32(ah, bh, acc);
-                    acc = mma32(ah, bl, acc);
-                    acc = mma32(al, bh, acc);
-                }
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(B + ((ks * 2 + 0) * 64 + lane) * 8);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(B + ((ks * 2 + 1) * 64 + lane) * 8);
+                acc = mma32(ah[ks], bh, acc);
+                hl = mma32(ah[ks], bl, hl);
+                lh = mma32(al[ks], bh, lh);
             }
+            acc += hl + lh;
+        }
+        if (!warm) {
             float* dst = p.seg_state + state_off(seg_base + s, p.h_v, h);
 #pragma unroll
             for (int i = 0; i < 16; ++i) dst[(32 * w + acc_row(i, hh)) * DK + cglob] = acc[i];
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sT[buf ^ 1][col * LDC + 32 * w + acc_row(i, hh)] = acc[i];
+        combine_split_out(sB[buf ^ 1], acc, w, lane);
         __syncthreads();
         buf ^= 1;
     }
 }
 
-// The fused forward of one segment: prep, state chain and output per chunk.
+// The fused forward of one segment: per chunk the P tiles, the state chain and
+// the output.
 template <typename IO>
 __global__ __launch_bounds__(NTHR) void k_fwd(Params p) {
     constexpr bool EX = Io<IO>::kExact;
-    __shared__ Smem<EX> sm;
-    const int h = blockIdx.y, hq = h / p.group;
+    __shared__ ChainSmem<EX> sm;
+    const int h = blockIdx.y, hq = h / p.group, wave = wave_id();
     const SegLoc loc = locate_segment(p, blockIdx.x);
     if (loc.seq < 0) return;
     f32x16 S[4];
@@ -1145,29 +1354,38 @@ __global__ __launch_bounds__(NTHR) void k_fwd(Params p) {
     const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
     const size_t ts_v = (size_t)p.h_v * DK;
     Chunk<IO> nxt;
-    if (c0 < c1) fetch_chunk<IO, true>(nxt, p, loc.tok0 + (size_t)c0 * CH, min(CH, loc.len - c0 * CH), h, hq);
+    if (c0 < c1)
+        fetch_chunk<IO, true, true>(nxt, p, loc.tok0 + (size_t)c0 * CH, min(CH, loc.len - c0 * CH), h, hq,
+                                    loc.chunk_base + c0);
     for (int c = c0; c < c1; ++c) {
         const size_t tok0 = loc.tok0 + (size_t)c * CH;
         const int nvalid = min(CH, loc.len - c * CH);
-        stage_chunk<IO, true>(sm, nxt);
-        __syncthreads();
-        prep_gram<IO, true>(sm, p, tok0, nvalid, hq);
+        stage_chunk<IO, true, true>(sm, nxt, p.scale);
         __syncthreads();
         if (c + 1 < c1)
-            fetch_chunk<IO, true>(nxt, p, tok0 + CH, min(CH, loc.len - (c + 1) * CH), h, hq);
-        f32x16 U[2], Wt[2];
-        prep_wy<IO>(sm, p, tok0, nvalid, h, true, U, Wt);
-        __syncthreads();
+            fetch_chunk<IO, true, true>(nxt, p, tok0 + CH, min(CH, loc.len - (c + 1) * CH), h, hq,
+                                        loc.chunk_base + c + 1);
+        // P tiles: three per wave, the last wave takes one and zeroes the two
+        // upper tiles inside the diagonal 32-blocks
+        if (wave < 3) {
+            gram_p<EX, 3>(sm, wave, 3, p.scale);
+        } else {
+            gram_p<EX, 1>(sm, 9, 1, p.scale);
+            zero_p_tile(sm.p, 0, 1);
+            zero_p_tile(sm.p, 2, 3);
+        }
+        f32x16 Vp[2], O[2];
         {
             SplitS ss;
             split_state(S, ss);
-            chain_vp<EX>(sm, ss, U);
-            IO* ocol = static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK + 32 * wave_id() + (lane_id() & 31);
-            chain_out<IO>(sm, ss, U, ocol, ts_v, nvalid, p.scale);
+            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 32 * wave + (lane_id() & 31);
+            chain_vp<IO, true>(sm, ss, vcol, ts_v, nvalid, Vp);
+            chain_qs<EX>(sm, ss, O);
         }
-        chain_state<EX>(sm, S, U);
         __syncthreads();
-        if constexpr (EX) store_out(sm, static_cast<bf16*>(p.out) + tok0 * ts_v + (size_t)h * DK, ts_v, nvalid);
+        chain_pv_out<IO>(sm, Vp, O, static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK, ts_v, nvalid);
+        chain_state<EX>(sm, S, Vp);
+        __syncthreads();
     }
     if (loc.s == loc.P - 1 && p.s_final) store_state(p.s_final + state_off(loc.seq, p.h_v, h), S);
 }
@@ -1208,11 +1426,19 @@ __global__ void k_debug_path(Params p, int32_t* path) {
 
 static int launched() { return (int)hipGetLastError(); }
 
-int launch_chunk_prep(const Params& p, int io, void* stream) {
+int launch_prep(const Params& p, int io, void* stream) {
+    if (p.n_chunks <= 0) return 0;
+    const dim3 grid((p.n_chunks + p.prep_cpw - 1) / p.prep_cpw, p.h_v), block(NTHR);
+    if (io == kIoBf16) hipLaunchKernelGGL(k_prep<bf16>, grid, block, 0, (hipStream_t)stream, p);
+    else hipLaunchKernelGGL(k_prep<float>, grid, block, 0, (hipStream_t)stream, p);
+    return launched();
+}
+
+int launch_wu(const Params& p, int io, void* stream) {
     if (p.n_chunks <= 0) return 0;
     const dim3 grid(p.n_chunks, p.h_v), block(NTHR);
-    if (io == kIoBf16) hipLaunchKernelGGL(k_chunk_prep<bf16>, grid, block, 0, (hipStream_t)stream, p);
-    else hipLaunchKernelGGL(k_chunk_prep<float>, grid, block, 0, (hipStream_t)stream, p);
+    if (io == kIoBf16) hipLaunchKernelGGL(k_wu<bf16>, grid, block, 0, (hipStream_t)stream, p);
+    else hipLaunchKernelGGL(k_wu<float>, grid, block, 0, (hipStream_t)stream, p);
     return launched();
 }
 

@@ -116,7 +116,11 @@ size_t gdn_fwd_workspace_bytes(const gdn_desc* desc);
  *   out                device output, same layout and dtype as v
  *   final_state        device [n_seqs, h_v, d_k, d_v] fp32, or NULL to skip
  *   workspace          device scratch of at least gdn_fwd_workspace_bytes(desc) bytes,
- *                      256-byte aligned; its contents on entry are ignored
+ *                      256-byte aligned; its contents on entry are ignored. It holds
+ *                      T = (I + A)^-1 (16 KiB) and the chunk's gate sums and beta
+ *                      (512 bytes) per (chunk, value head), and with a split the
+ *                      segment states, the maps M and H (64 KiB per segment and
+ *                      value head each) and the boundary flags
  *   stream             the hipStream_t to launch on (NULL = default stream)
  * All buffers stay owned by the caller and must stay valid until the stream
  * has run the launched kernels. Arguments are validated before any launch. */
@@ -165,11 +169,12 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc,
  * call records HIP events on its stream before its first launch and after
  * each of its kernels; gdn_profile_read then waits for the last call's events
  * and returns elapsed milliseconds:
- *   ms[0] cp_prep, ms[1] cp_combine, ms[2] forward kernel, ms[3] whole call
+ *   ms[0] chunk preparation (T of every chunk), ms[1] cp_prep,
+ *   ms[2] cp_combine, ms[3] forward kernel, ms[4] whole call
  * (phases that did not run read 0). Process-wide state, not thread-safe; the
  * events are created on the first enable, on the current device. */
 gdn_status gdn_profile_enable(int on);
-gdn_status gdn_profile_read(float ms[4]);
+gdn_status gdn_profile_read(float ms[5]);
 
 /* Static text for a status code. */
 const char* gdn_status_string(gdn_status status);

@@ -95,11 +95,26 @@ def segments(N, L):
     return [(s * L, min((s + 1) * L, N)) for s in range(P)]
 
 
-def warmup_window(a, w):
-    """Chunk window [max(a - w, 0), a) scanned to approximate the state at chunk a.
-    The window reaching chunk 0 makes the warm-up exact (it starts from the
-    sequence's initial state)."""
-    return max(a - w, 0), a
+def warmup_window(a, w, g_seq=None, eps=None):
+    """Chunk window [lo, a) scanned to approximate the state at chunk a.
+
+    Without gates: the w chunks before a. A window reaching chunk 0 makes the
+    warm-up exact (it starts from the sequence's initial state), so when
+    a <= w the window is [0, a). With gates (g_seq, eps): the shortest run of
+    whole chunks before a, at most w, whose total log-decay sum(g) is at most
+    ln(eps) -- the gate has then already damped the state the scan misses to
+    below the noise floor; if no run of up to w chunks qualifies, the w chunks
+    before a (the AutoCP section's warm-up of a fixed number of chunks, read
+    as an upper bound on the window)."""
+    if a - w <= 0:
+        return 0, a
+    if g_seq is not None:
+        cum = 0.0
+        for j in range(1, w + 1):
+            cum += float(np.sum(g_seq[(a - j) * CHUNK:(a - j + 1) * CHUNK]))
+            if cum <= math.log(eps):
+                return a - j, a
+    return a - w, a
 
 
 def choose_path(g_seq, N, L, w, eps):
@@ -176,7 +191,7 @@ def chunked_forward(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None
                     S0.append(M @ S0[-1] + Hm)
             elif path == "warmup":
                 for (a, _) in segs[1:]:
-                    lo, hi = warmup_window(a, w)
+                    lo, hi = warmup_window(a, w, gs, eps)
                     S = S_init.copy() if lo == 0 else np.zeros((d_k, d_v))
                     for c in range(lo, hi):
                         sl, gam, _, _, W, U = prep[c]

@@ -97,11 +97,13 @@ def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
     assert p["P_max"] == -(-N // L) and p["n_segments"] == B_ * p["P_max"]
     assert p["cp_on"] == int(p["P_max"] > 1)
     per_seg = h_v * 128 * 128 * 4
+    # T (64 x 64, split into two bf16 halves) and gamma, beta per (chunk, value head)
+    prep = p["n_chunks_total"] * h_v * (64 * 64 * 4 + 2 * 64 * 4)
     if p["cp_on"]:
         flags = -(-(p["n_segments"] * h_v * 4) // 256) * 256
-        assert p["workspace_bytes"] == 3 * p["n_segments"] * per_seg + flags
+        assert p["workspace_bytes"] == prep + 3 * p["n_segments"] * per_seg + flags
     else:
-        assert p["workspace_bytes"] == 0
+        assert p["workspace_bytes"] == prep
 
 
 def test_plan_options_and_modes():
@@ -212,7 +214,7 @@ def test_chunk_prep_validation():
 
 def test_profile_read_without_profiled_call():
     l = lib()
-    ms = (ctypes.c_float * 4)()
+    ms = (ctypes.c_float * 5)()
     assert B.STATUS_NAMES[l.gdn_profile_read(ms)] == "GDN_ERR_BAD_OPTION"
     assert B.STATUS_NAMES[l.gdn_profile_read(None)] == "GDN_ERR_NULL_ARG"
 

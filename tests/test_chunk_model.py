@@ -111,6 +111,47 @@ def test_warmup_error_within_contraction_bound():
     assert checked >= 2
 
 
+def test_adaptive_warmup_window():
+    """The warm-up window is the shortest run of whole chunks before the
+    boundary (at most w) whose log-decay reaches ln(eps); the w chunks if none
+    does; [0, a) when the w-chunk window would reach the sequence start."""
+    eps, w = 1e-4, 6
+    g = np.zeros(64 * 16)
+    g[64 * 9:64 * 10] = -83.0 / 64          # chunk 9 alone decays far below eps
+    assert cm.warmup_window(10, w, g, eps) == (9, 10)
+    g[:] = 0.0
+    g[64 * 7:64 * 10] = -4.0 / 64           # -4 per chunk: three chunks needed (-12 <= ln 1e-4)
+    assert cm.warmup_window(10, w, g, eps) == (7, 10)
+    g[:] = -1e-4                            # slow decay: no run of <= w chunks qualifies
+    assert cm.warmup_window(10, w, g, eps) == (4, 10)
+    assert cm.warmup_window(10, w) == (4, 10)
+    assert cm.warmup_window(5, w, g, eps) == (0, 5)
+    assert cm.warmup_window(6, w, g, eps) == (0, 6)
+
+
+def test_adaptive_warmup_error_within_bound():
+    """With fast-decay gates the adaptive window is one chunk, and the state it
+    misses is bounded by exp(sum g over that chunk) |S at the window start|."""
+    T, L, w, eps = 64 * 12, 3, 6, 1e-4
+    inp, q, k, v, g, b = _case(T, h_qk=1, h_v=1, seed=7, gate="fast", init_std=0.5)
+    _, _, snaps = gdn_sequential(q, k, v, g, b, inp.scale, inp.initial_state, snap_stride=64, n_snap=13)
+    _, _, info = cm.chunked_forward(q, k, v, g, b, inp.scale, inp.initial_state, L=L, mode="warmup",
+                                    w=w, eps=eps)
+    S0s = info["S0"][0][0]
+    for s in range(1, len(S0s)):
+        a = s * L
+        lo, hi = cm.warmup_window(a, w, g[:, 0], eps)
+        assert hi == a and (lo == 0 or lo == a - 1)
+        err = np.linalg.norm(S0s[s] - snaps[0, 0, a])
+        if lo == 0:
+            assert err < 1e-12
+            continue
+        bound = math.exp(float(np.sum(g[lo * 64:a * 64, 0], dtype=np.float64))) * np.linalg.norm(snaps[0, 0, lo])
+        # fp64 rounding of the two evaluation orders on top of the bound
+        assert err <= bound * (1 + 1e-9) + 1e-12 * np.linalg.norm(snaps[0, 0, a])
+        assert bound <= eps * np.linalg.norm(snaps[0, 0, lo])
+
+
 def test_warmup_exact_when_window_reaches_start():
     T = 64 * 5
     inp, q, k, v, g, b = _case(T, h_qk=1, h_v=2, seed=6, gate="slow")
