@@ -41,7 +41,7 @@ struct Plan {
     int n_chunks_total = 0, n_chunks_max = 0;
     int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0;
     float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
-    size_t off_T = 0, off_GB = 0, off_state = 0, off_M = 0, off_H = 0, off_warm = 0, ws_bytes = 0;
+    size_t off_sink = 0, off_T = 0, off_GB = 0, off_state = 0, off_M = 0, off_H = 0, off_warm = 0, ws_bytes = 0;
 };
 
 int n_chunks_of(int len) { return (len + gdn::kChunk - 1) / gdn::kChunk; }
@@ -101,7 +101,8 @@ gdn_status query_cu_count(int* n_cu) {
 // sequence is shorter than two warm-up windows. L is raised where needed so
 // that no sequence has more than kMaxSegsPerSeq segments.
 //
-// Workspace: T (split hi/lo, 16 KiB) and gamma, beta (512 bytes) per (chunk,
+// Workspace: an 8 KiB scratch line (stores of rows past a sequence's end land
+// there), T (split hi/lo, 16 KiB) and gamma, beta (512 bytes) per (chunk,
 // value head); with a split, the segment states, the maps M and H, and the
 // boundary flags.
 gdn_status make_plan(const gdn_desc* d, Plan* pl) {
@@ -156,6 +157,7 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
     P.cp_on = P.P_max > 1;
     size_t off = 0;
     const size_t blk = (size_t)gdn::kChunk * gdn::kChunk * sizeof(float);
+    if (P.n_chunks_total > 0) { P.off_sink = off; off += 8192; }
     P.off_T = off;   off = align_up(off + (size_t)P.n_chunks_total * d->h_v * blk, 256);
     P.off_GB = off;  off = align_up(off + (size_t)P.n_chunks_total * d->h_v * 2 * gdn::kChunk * sizeof(float), 256);
     if (P.cp_on) {
@@ -241,6 +243,7 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
     p.out = out; p.s_final = s_final; p.scale = scale;
     char* w8 = static_cast<char*>(ws);
     if (P.n_chunks_total > 0) {
+        p.sink = reinterpret_cast<float*>(w8 + P.off_sink);
         p.prep_T = reinterpret_cast<float*>(w8 + P.off_T);
         p.prep_GB = reinterpret_cast<float*>(w8 + P.off_GB);
     }

@@ -32,6 +32,7 @@ struct Params {
     float* prep_GB;           // [n_chunks][h_v] blocks of gb_stride floats: gamma (64), beta (64)
     int64_t gb_stride;        // floats between consecutive gamma/beta blocks (>= 128)
     int32_t prep_cpw;         // chunks per k_prep workgroup
+    float* sink;              // 8 KiB scratch line for stores of rows past a sequence's end
     // low-level chunk-prep outputs
     float* prep_gamma;        // [n_chunks][h_v][64]
     float* prep_W;            // [n_chunks][h_v][64][128]

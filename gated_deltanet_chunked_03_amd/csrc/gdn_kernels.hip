@@ -466,6 +466,16 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
     int nvalid = min(CH, len - c * CH);
     PrepIn<IO> nxt;
     prep_fetch<IO>(nxt, p, tok0, nvalid, h, hq);
+    if (p.sink) {   // (null for the low-level entry, which has no workspace)
+        // the loop body's stores (gamma, beta; T) come after its loads; the same
+        // stores to the scratch line here make the loop's entry look alike, so
+        // that the wait at its head covers the loads only
+        float* sk = p.sink + 32 * lane;
+        sk[0] = 0.f;
+        sk[1] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sk + 4 * i) = u32x4{0u, 0u, 0u, 0u};
+    }
     for (int slot = s0; slot < s1; ++slot) {
         const size_t tok_cur = tok0;
         const int nv_cur = nvalid;
@@ -478,7 +488,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
                 *reinterpret_cast<u32x2*>(sm.k_rm + row * LDQ + pk(c8 + 4)) = u32x2{nxt.k[j][2], nxt.k[j][3]};
             }
         }
-        if (wave == 0) {
+        {   // every wave scans and writes the same values (no branch in the loop)
             const float gam = wave_scan(nxt.g);
             sm.gam[lane] = gam;
             sm.beta[lane] = nxt.b;
@@ -487,11 +497,14 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
             gb[CH + lane] = nxt.b;
         }
         __syncthreads();
-        if (slot + 1 < s1 && locate_chunk(p, slot + 1, seq, c, len, tok_s)) {
+        // always a prefetch (the last slot fetches itself again), so that every
+        // iteration has the same memory operations and the compiler's waits on
+        // them stay exact across the loop
+        if (locate_chunk(p, min(slot + 1, s1 - 1), seq, c, len, tok_s)) {
             tok0 = tok_s + (size_t)c * CH;
             nvalid = min(CH, len - c * CH);
-            prep_fetch<IO>(nxt, p, tok0, nvalid, h, hq);
         }
+        prep_fetch<IO>(nxt, p, tok0, nvalid, h, hq);
         // the ten tiles: three per wave, the last wave takes one
         if (wave < 3) gram_a<IO, 3>(sm, krow0, ts, nv_cur, wave, 3);
         else gram_a<IO, 1>(sm, krow0, ts, nv_cur, 9, 1);
@@ -576,9 +589,14 @@ template <typename IO> struct Chunk;
 template <> struct Chunk<bf16> { u32x4 k[4], v[4], q[4], t[4]; float gl, bl; };
 template <> struct Chunk<float> { f32x4 k[8], q[8]; u32x4 t[4]; float gl, bl; };
 
-// Full chunks load rows directly; the last chunk of a sequence loads its rows
-// with the index clamped to the last token and replaces the rows past the end
-// by zeros. Addresses are a wave-uniform base plus 32-bit lane offsets.
+// Rows past the end of the sequence (last chunk only) read its last row
+// again: their values never matter, since such tokens carry beta = 0, which
+// zeroes their columns of T diag(beta), so their K, V and Q rows reach
+// neither a valid output nor the state. Addresses are a wave-uniform base plus
+// 32-bit lane offsets. The chunk loops issue the same loads and stores in
+// every iteration (no conditional memory operations), so that the compiler's
+// waits on them stay exact across the loop instead of draining every
+// outstanding operation.
 template <typename IO, bool WANT_Q, bool WANT_V>
 __device__ __forceinline__ void fetch_chunk(Chunk<IO>& r, const Params& p, size_t tok0, int nvalid, int h,
                                             int hq, int slot) {
@@ -588,37 +606,21 @@ __device__ __forceinline__ void fetch_chunk(Chunk<IO>& r, const Params& p, size_
     const IO* kb = static_cast<const IO*>(p.k) + tok0 * (size_t)ts + (size_t)hq * DK;
     const IO* qb = static_cast<const IO*>(p.q) + tok0 * (size_t)ts + (size_t)hq * DK;
     const IO* vb = static_cast<const IO*>(p.v) + tok0 * (size_t)tsv + (size_t)h * DK;
-    const bool full = nvalid == CH;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int rk = 4 * m + j, rq = m + 16 * j;
-        const unsigned ok_k = (unsigned)((full ? rk : min(rk, nvalid - 1)) * ts + c8);
-        const unsigned ok_v = (unsigned)((full ? rk : min(rk, nvalid - 1)) * tsv + c8);
-        const unsigned ok_q = (unsigned)((full ? rq : min(rq, nvalid - 1)) * ts + c8);
-        const bool vk = full || rk < nvalid, vq = full || rq < nvalid;
+        const int rk = min(4 * m + j, nvalid - 1), rq = min(m + 16 * j, nvalid - 1);
+        const unsigned ok_k = (unsigned)(rk * ts + c8), ok_v = (unsigned)(rk * tsv + c8);
+        const unsigned ok_q = (unsigned)(rq * ts + c8);
         if constexpr (EX) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + ok_k);
-            r.k[j] = vk ? kv : z;
-            if (WANT_V) {
-                const u32x4 vv = *reinterpret_cast<const u32x4*>(vb + ok_v);
-                r.v[j] = vk ? vv : z;
-            }
-            if (WANT_Q) {
-                const u32x4 qv = *reinterpret_cast<const u32x4*>(qb + ok_q);
-                r.q[j] = vq ? qv : z;
-            }
+            r.k[j] = *reinterpret_cast<const u32x4*>(kb + ok_k);
+            if (WANT_V) r.v[j] = *reinterpret_cast<const u32x4*>(vb + ok_v);
+            if (WANT_Q) r.q[j] = *reinterpret_cast<const u32x4*>(qb + ok_q);
         } else {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 ka = *reinterpret_cast<const f32x4*>(kb + ok_k);
-            const f32x4 kc = *reinterpret_cast<const f32x4*>(kb + ok_k + 4);
-            r.k[2 * j] = vk ? ka : z;
-            r.k[2 * j + 1] = vk ? kc : z;
+            r.k[2 * j] = *reinterpret_cast<const f32x4*>(kb + ok_k);
+            r.k[2 * j + 1] = *reinterpret_cast<const f32x4*>(kb + ok_k + 4);
             if (WANT_Q) {
-                const f32x4 qa = *reinterpret_cast<const f32x4*>(qb + ok_q);
-                const f32x4 qc = *reinterpret_cast<const f32x4*>(qb + ok_q + 4);
-                r.q[2 * j] = vq ? qa : z;
-                r.q[2 * j + 1] = vq ? qc : z;
+                r.q[2 * j] = *reinterpret_cast<const f32x4*>(qb + ok_q);
+                r.q[2 * j + 1] = *reinterpret_cast<const f32x4*>(qb + ok_q + 4);
             }
         }
     }
@@ -639,20 +641,19 @@ __device__ __forceinline__ unsigned int pack_col(const u32x4& a, const u32x4& b,
 
 // Writes a fetched chunk to LDS: K token-major and transposed (four
 // consecutive tokens of a column per 8-byte store), V^T, Q, T and the gate
-// factors (wave 0). Rows past the end of the sequence were fetched as zeros
-// (g = beta = 0 there).
+// factors (tokens past the end of the sequence have g = beta = 0).
 template <typename IO, bool WANT_Q, bool WANT_V>
 __device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const Chunk<IO>& r, float scale) {
     constexpr bool EX = Io<IO>::kExact;
     const int t = threadIdx.x, lane = lane_id(), m = t >> 4, c8 = (t & 15) * 8;
-    if (wave_id() == 0) {
+    {   // every wave writes the same values (no branch in the chunk loop)
         const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.gl), 63));
         const float es = __expf(r.gl);
         sm.gam[lane] = r.gl;
         sm.eg[lane] = es;
         sm.egs[lane] = es * scale;
         sm.egc[lane] = __expf(gc - r.gl);
-        if (lane == 0) sm.red[0] = __expf(gc);
+        sm.red[0] = __expf(gc);
     }
     const int tp = pk(4 * m);   // the four tokens stay contiguous under the permutation
     if constexpr (EX) {
@@ -882,7 +883,7 @@ __device__ void chain_qs(const ChainSmem<EX>& sm, const SplitS& ss, f32x16 O[2])
 
 template <typename IO>
 __device__ void chain_pv_out(const ChainSmem<Io<IO>::kExact>& sm, const f32x16 Vp[2], f32x16 O[2], IO* orow0,
-                             size_t ts, int nvalid) {
+                             size_t ts, int nvalid, float* sink) {
     constexpr bool EX = Io<IO>::kExact;
     const int lane = lane_id(), col = lane & 31, h = lane >> 5, w = wave_id();
 #pragma unroll
@@ -899,11 +900,13 @@ __device__ void chain_pv_out(const ChainSmem<Io<IO>::kExact>& sm, const f32x16 V
             O[ti] = mma32(vh, pl, O[ti]);
         }
     }
+    // rows past the end of the sequence are written to a scratch line (every
+    // chunk issues the same stores; see fetch_chunk)
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
         const int r = 32 * ti + col;
-        if (r >= nvalid) continue;
-        IO* dst = orow0 + (size_t)r * ts + 32 * w + 4 * h;
+        IO* dst = (r < nvalid) ? orow0 + (size_t)r * ts + 32 * w + 4 * h
+                               : reinterpret_cast<IO*>(sink + 32 * lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const f32x4 x = f32x4{O[ti][4 * q], O[ti][4 * q + 1], O[ti][4 * q + 2], O[ti][4 * q + 3]};
@@ -1003,9 +1006,11 @@ __device__ void scan_chunks(ChainSmem<Io<IO>::kExact>& sm, const Params& p, cons
         const int nvalid = min(CH, loc.len - c * CH);
         stage_chunk<IO, false, WANT_V>(sm, nxt, 1.f);
         __syncthreads();
-        if (c + 1 < c_hi)
-            fetch_chunk<IO, false, WANT_V>(nxt, p, tok0 + CH, min(CH, loc.len - (c + 1) * CH), h, hq,
-                                           loc.chunk_base + c + 1);
+        {   // always a prefetch (the last chunk fetches itself again): see fetch_chunk
+            const int cn = min(c + 1, c_hi - 1);
+            fetch_chunk<IO, false, WANT_V>(nxt, p, loc.tok0 + (size_t)cn * CH, min(CH, loc.len - cn * CH), h, hq,
+                                           loc.chunk_base + cn);
+        }
         f32x16 Vp[2];
         {
             SplitS ss;
@@ -1281,57 +1286,64 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
         }
         combine_split_out(sB[0], acc, w, lane);
     }
+    // Operands of step s1 (boundary s1): the warm-up state or H_{s1-1}, and
+    // this lane's A operands of M_{s1-1}.
+    // (every step issues the same loads and stores: a step past the end loads
+    // the last one again, M is loaded whether or not the step applies it, and
+    // the state is stored back also where it is a warm-up state; then the
+    // compiler's waits stay exact across the loop and the prefetch works)
     auto fetch = [&](int s1, CombineIn& in) {
+        s1 = min(s1, P - 1);
         const int warm1 = wflag[s1];
         const float* src = warm1 ? p.seg_state + state_off(seg_base + s1, p.h_v, h)
                                  : p.seg_H + state_off(seg_base + s1 - 1, p.h_v, h);
 #pragma unroll
         for (int i = 0; i < 16; ++i) in.tile[i] = src[(32 * w + acc_row(i, hh)) * DK + cglob];
-        if (!warm1 && (s1 > 1 || p.s_init)) {
-            const bf16* mop = reinterpret_cast<const bf16*>(p.seg_M + state_off(seg_base + s1 - 1, p.h_v, h));
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                in.ah[ks] = *reinterpret_cast<const bf16x8*>(mop + (((w * 8 + ks) * 2 + 0) * 64 + lane) * 8);
-                in.al[ks] = *reinterpret_cast<const bf16x8*>(mop + (((w * 8 + ks) * 2 + 1) * 64 + lane) * 8);
-            }
-        }
-    };
-    CombineIn nxt;
-    fetch(1, nxt);
-    __syncthreads();
-    int buf = 0;
-    for (int s = 1; s < P; ++s) {
-        const int warm = wflag[s];
-        const bool mm = !warm && (s > 1 || p.s_init);
-        f32x16 acc = nxt.tile;
-        bf16x8 ah[8], al[8];
+        const bf16* mop = reinterpret_cast<const bf16*>(p.seg_M + state_off(seg_base + s1 - 1, p.h_v, h));
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            ah[ks] = nxt.ah[ks];
-            al[ks] = nxt.al[ks];
+            in.ah[ks] = *reinterpret_cast<const bf16x8*>(mop + (((w * 8 + ks) * 2 + 0) * 64 + lane) * 8);
+            in.al[ks] = *reinterpret_cast<const bf16x8*>(mop + (((w * 8 + ks) * 2 + 1) * 64 + lane) * 8);
         }
-        if (s + 1 < P) fetch(s + 1, nxt);
+    };
+    // One step from the operands in `in`, then `in` is refilled with those of
+    // step s + 2: two register sets alternate, so each step's loads have two
+    // steps to arrive. The three partial products run as independent chains.
+    int buf = 0;
+    auto step = [&](int s, CombineIn& in) {
+        const int warm = wflag[s];
+        const bool mm = !warm && (s > 1 || p.s_init);
+        f32x16 acc = in.tile;
         if (mm) {
             f32x16 hl = f32x16{}, lh = f32x16{};
-            const bf16* B = sB[buf];
+            const bf16* Bp = sB[buf];
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(B + ((ks * 2 + 0) * 64 + lane) * 8);
-                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(B + ((ks * 2 + 1) * 64 + lane) * 8);
-                acc = mma32(ah[ks], bh, acc);
-                hl = mma32(ah[ks], bl, hl);
-                lh = mma32(al[ks], bh, lh);
+                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 0) * 64 + lane) * 8);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 1) * 64 + lane) * 8);
+                acc = mma32(in.ah[ks], bh, acc);
+                hl = mma32(in.ah[ks], bl, hl);
+                lh = mma32(in.al[ks], bh, lh);
             }
             acc += hl + lh;
         }
-        if (!warm) {
+        fetch(s + 2, in);
+        combine_split_out(sB[buf ^ 1], acc, w, lane);
+        {
             float* dst = p.seg_state + state_off(seg_base + s, p.h_v, h);
 #pragma unroll
             for (int i = 0; i < 16; ++i) dst[(32 * w + acc_row(i, hh)) * DK + cglob] = acc[i];
         }
-        combine_split_out(sB[buf ^ 1], acc, w, lane);
         __syncthreads();
         buf ^= 1;
+    };
+    CombineIn in0, in1;
+    fetch(1, in0);
+    fetch(2, in1);
+    __syncthreads();
+    for (int s = 1; s < P; s += 2) {
+        step(s, in0);
+        if (s + 1 < P) step(s + 1, in1);
     }
 }
 
@@ -1357,14 +1369,27 @@ __global__ __launch_bounds__(NTHR) void k_fwd(Params p) {
     if (c0 < c1)
         fetch_chunk<IO, true, true>(nxt, p, loc.tok0 + (size_t)c0 * CH, min(CH, loc.len - c0 * CH), h, hq,
                                     loc.chunk_base + c0);
+    if (c0 < c1) {   // (the scratch line exists whenever there is a chunk)
+        // the loop body ends with the output's eight stores after its loads; the
+        // same stores (to the scratch line) here make the loop's entry look
+        // alike, so that the wait at its head covers the loads only
+        IO* dst = reinterpret_cast<IO*>(p.sink + 32 * lane_id());
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (EX) *reinterpret_cast<u32x2*>(dst + 8 * (i & 3)) = u32x2{0u, 0u};
+            else *reinterpret_cast<f32x4*>(dst + 8 * (i & 3)) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     for (int c = c0; c < c1; ++c) {
         const size_t tok0 = loc.tok0 + (size_t)c * CH;
         const int nvalid = min(CH, loc.len - c * CH);
         stage_chunk<IO, true, true>(sm, nxt, p.scale);
         __syncthreads();
-        if (c + 1 < c1)
-            fetch_chunk<IO, true, true>(nxt, p, tok0 + CH, min(CH, loc.len - (c + 1) * CH), h, hq,
-                                        loc.chunk_base + c + 1);
+        {   // always a prefetch (the last chunk fetches itself again): see fetch_chunk
+            const int cn = min(c + 1, c1 - 1);
+            fetch_chunk<IO, true, true>(nxt, p, loc.tok0 + (size_t)cn * CH, min(CH, loc.len - cn * CH), h, hq,
+                                        loc.chunk_base + cn);
+        }
         // P tiles: three per wave, the last wave takes one and zeroes the two
         // upper tiles inside the diagonal 32-blocks
         if (wave < 3) {
@@ -1383,7 +1408,7 @@ __global__ __launch_bounds__(NTHR) void k_fwd(Params p) {
             chain_qs<EX>(sm, ss, O);
         }
         __syncthreads();
-        chain_pv_out<IO>(sm, Vp, O, static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK, ts_v, nvalid);
+        chain_pv_out<IO>(sm, Vp, O, static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK, ts_v, nvalid, p.sink);
         chain_state<EX>(sm, S, Vp);
         __syncthreads();
     }

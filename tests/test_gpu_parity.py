@@ -144,3 +144,22 @@ def test_gate_closed_and_no_write_special_cases():
     ref = 0.5 * np.einsum("tk,hkv->thv", q[:, 0].astype(np.float64), inp.initial_state[0])
     assert_within_tolerance(o.float().cpu().numpy().reshape(ref.shape), ref)
     np.testing.assert_array_equal(S.cpu().numpy(), inp.initial_state)
+
+
+def test_empty_inputs_pass_the_state_through():
+    """No tokens (T = 0, and packed sequences that are all empty): nothing to
+    write, and the final state is the initial state (zeros without one)."""
+    import torch
+    gdn = _gdn()
+    dev = torch.device("cuda")
+    S0 = torch.randn(2, 3, 128, 128, device=dev)
+    for cu in (None, [0, 0, 0]):
+        B = 2 if cu is None else 1
+        q = torch.zeros(B, 0, 1, 128, dtype=torch.bfloat16, device=dev)
+        v = torch.zeros(B, 0, 3, 128, dtype=torch.bfloat16, device=dev)
+        g = torch.zeros(B, 0, 3, device=dev)
+        for mode in ("off", "auto"):
+            o, S = gdn.fwd(q, q, v, g, g, scale=0.1, initial_state=S0, cu_seqlens=cu, cp_mode=mode)
+            o2, S2 = gdn.fwd(q, q, v, g, g, scale=0.1, cu_seqlens=cu, cp_mode=mode)
+            torch.cuda.synchronize()
+            assert o.numel() == 0 and torch.equal(S, S0) and torch.count_nonzero(S2) == 0
