@@ -95,11 +95,13 @@ gdn_status query_cu_count(int* n_cu) {
 
 // The AutoCP planner (section "Gate-Driven Automatic Intra-Card Context
 // Parallelism (AutoCP)": L = lambda sqrt(N) chunks per segment). Readings:
-// N is the chunk count of the longest sequence; L is rounded half-up and
-// capped at the largest L that still gives every CU a workgroup; AUTO keeps
-// a sequence whole when (sequences x heads) already cover the CUs or when the
-// sequence is shorter than two warm-up windows. L is raised where needed so
-// that no sequence has more than kMaxSegsPerSeq segments.
+// N is the chunk count of the longest sequence; lambda sqrt(N), rounded
+// half-up, is the largest L considered; below it L is chosen for the hardware
+// (every CU gets a workgroup, and whole rounds of workgroups: see the cost
+// model below); AUTO keeps a sequence whole when (sequences x heads) already
+// cover the CUs or when the sequence is shorter than two warm-up windows. L is
+// raised where needed so that no sequence has more than kMaxSegsPerSeq
+// segments.
 //
 // Workspace: an 8 KiB scratch line (stores of rows past a sequence's end land
 // there), T (split hi/lo, 16 KiB) and gamma, beta (512 bytes) per (chunk,
@@ -140,9 +142,27 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
     if (!split) {
         P.L = std::max(Nm, 1);
     } else {
-        const int L_lam = std::max(1, (int)std::floor(P.lambda * std::sqrt((double)Nm) + 0.5));
-        int L = std::min(L_lam, Nm);
-        while (L > 1 && total_segs(L) * d->h_v < P.n_cu) --L;  // fill every CU
+        const int L_lam = std::min(std::max(1, (int)std::floor(P.lambda * std::sqrt((double)Nm) + 0.5)), Nm);
+        // Among L <= L_lam whose segments fill every CU (or L = 1), the one with
+        // the least estimated time in chunk steps: the forward runs
+        // ceil(workgroups / CUs) rounds of L chunks, the exact maps L more, and
+        // the combine one short step (about a quarter chunk) per boundary.
+        int best_L = 1;
+        double best = 0.0;
+        bool found = false;
+        for (int L = L_lam; L >= 1; --L) {
+            const long long segs = total_segs(L), wg = segs * d->h_v;
+            if (wg < P.n_cu && L > 1) continue;
+            if (n_segs_of(Nm, L) > gdn::kMaxSegsPerSeq) break;
+            const long long rounds = (wg + P.n_cu - 1) / P.n_cu;
+            const double cost = (double)rounds * L + 0.5 * L + 0.25 * (n_segs_of(Nm, L) - 1);
+            if (!found || cost < best) {   // ties keep the longer segments
+                found = true;
+                best = cost;
+                best_L = L;
+            }
+        }
+        int L = best_L;
         while (n_segs_of(Nm, L) > gdn::kMaxSegsPerSeq) ++L;
         P.L = L;
     }

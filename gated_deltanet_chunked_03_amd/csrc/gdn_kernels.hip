@@ -1292,42 +1292,70 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
     // the last one again, M is loaded whether or not the step applies it, and
     // the state is stored back also where it is a warm-up state; then the
     // compiler's waits stay exact across the loop and the prefetch works)
-    auto fetch = [&](int s1, CombineIn& in) {
+    auto tile_src = [&](int s1) {
         s1 = min(s1, P - 1);
-        const int warm1 = wflag[s1];
-        const float* src = warm1 ? p.seg_state + state_off(seg_base + s1, p.h_v, h)
-                                 : p.seg_H + state_off(seg_base + s1 - 1, p.h_v, h);
+        return __builtin_amdgcn_readfirstlane(wflag[s1]) ? p.seg_state + state_off(seg_base + s1, p.h_v, h)
+                                                          : p.seg_H + state_off(seg_base + s1 - 1, p.h_v, h);
+    };
+    auto m_src = [&](int s1) {
+        s1 = min(s1, P - 1);
+        return reinterpret_cast<const bf16*>(p.seg_M + state_off(seg_base + s1 - 1, p.h_v, h)) +
+               (size_t)(w * 8 * 2 * 64 + lane) * 8;
+    };
+    auto fetch = [&](int s1, CombineIn& in) {
+        const float* src = tile_src(s1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) in.tile[i] = src[(32 * w + acc_row(i, hh)) * DK + cglob];
-        const bf16* mop = reinterpret_cast<const bf16*>(p.seg_M + state_off(seg_base + s1 - 1, p.h_v, h));
+        const bf16* mop = m_src(s1);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            in.ah[ks] = *reinterpret_cast<const bf16x8*>(mop + (((w * 8 + ks) * 2 + 0) * 64 + lane) * 8);
-            in.al[ks] = *reinterpret_cast<const bf16x8*>(mop + (((w * 8 + ks) * 2 + 1) * 64 + lane) * 8);
+            in.ah[ks] = *reinterpret_cast<const bf16x8*>(mop + (ks * 2 + 0) * 64 * 8);
+            in.al[ks] = *reinterpret_cast<const bf16x8*>(mop + (ks * 2 + 1) * 64 * 8);
         }
     };
-    // One step from the operands in `in`, then `in` is refilled with those of
-    // step s + 2: two register sets alternate, so each step's loads have two
-    // steps to arrive. The three partial products run as independent chains.
+    // One step from the operands in `in`, which are refilled with those of
+    // step s + 2 as they are consumed (each operand's load is issued right
+    // after the MFMAs that read it, so the loads overlap the products): two
+    // register sets alternate, and each step's loads have two steps to
+    // arrive. The three partial products run as independent chains.
     int buf = 0;
     auto step = [&](int s, CombineIn& in) {
-        const int warm = wflag[s];
+        const int warm = __builtin_amdgcn_readfirstlane(wflag[s]);   // uniform: a scalar branch
         const bool mm = !warm && (s > 1 || p.s_init);
         f32x16 acc = in.tile;
-        if (mm) {
-            f32x16 hl = f32x16{}, lh = f32x16{};
-            const bf16* Bp = sB[buf];
+        {
+            const float* src = tile_src(s + 2);
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 0) * 64 + lane) * 8);
-                const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 1) * 64 + lane) * 8);
-                acc = mma32(in.ah[ks], bh, acc);
-                hl = mma32(in.ah[ks], bl, hl);
-                lh = mma32(in.al[ks], bh, lh);
-            }
-            acc += hl + lh;
+            for (int i = 0; i < 16; ++i) in.tile[i] = src[(32 * w + acc_row(i, hh)) * DK + cglob];
         }
-        fetch(s + 2, in);
+        const bf16* mop = m_src(s + 2);
+        // (the products run also where they are not applied -- a warm-up
+        // boundary, or M_0 without an initial state -- and are then dropped:
+        // no branch separates the loads from the products)
+        const f32x16 base = acc;
+        f32x16 hl = f32x16{}, lh = f32x16{};
+        const bf16* Bp = sB[buf];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 0) * 64 + lane) * 8);
+            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 1) * 64 + lane) * 8);
+            acc = mma32(in.ah[ks], bh, acc);
+            hl = mma32(in.ah[ks], bl, hl);
+            lh = mma32(in.al[ks], bh, lh);
+            in.ah[ks] = *reinterpret_cast<const bf16x8*>(mop + (ks * 2 + 0) * 64 * 8);
+            in.al[ks] = *reinterpret_cast<const bf16x8*>(mop + (ks * 2 + 1) * 64 * 8);
+        }
+        // instruction order for the scheduler: the tile loads, then per k step
+        // two LDS reads, three MFMAs and the two loads that refill their operands
+        __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        }
+        acc += hl + lh;
+        if (!mm) acc = base;
         combine_split_out(sB[buf ^ 1], acc, w, lane);
         {
             float* dst = p.seg_state + state_off(seg_base + s, p.h_v, h);

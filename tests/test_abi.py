@@ -66,27 +66,34 @@ def n_chunks(t):
 
 
 def expected_L(lens, h_v, n_cu, lam=1.0, w=6, mode="auto"):
-    """The planner rule stated in gdn_api.cpp: L = round-half-up(lam sqrt(N_max)),
-    lowered until (segments over all sequences) x h_v covers the CUs; AUTO keeps
-    sequences whole when sequences x heads already cover the CUs or N_max < 2 (w + 1)."""
+    """The planner rule stated in gdn_api.cpp: among L <= round-half-up(lam sqrt(N_max))
+    whose segments times heads cover the CUs (or L = 1), the least
+    ceil(segments h_v / CUs) L + L / 2 + (P - 1) / 4, ties to the larger L; AUTO
+    keeps sequences whole when sequences x heads already cover the CUs or N_max < 2 (w + 1)."""
     Nm = max(n_chunks(t) for t in lens)
     if mode == "off" or Nm <= 1:
         return max(Nm, 1)
     if mode == "auto" and (len(lens) * h_v >= n_cu or Nm < 2 * (w + 1)):
         return max(Nm, 1)
-    L = min(max(1, int(math.floor(lam * math.sqrt(Nm) + 0.5))), Nm)
+    L_lam = min(max(1, int(math.floor(lam * math.sqrt(Nm) + 0.5))), Nm)
     segs = lambda L: sum(1 if n_chunks(t) == 0 else -(-n_chunks(t) // L) for t in lens)  # noqa
-    while L > 1 and segs(L) * h_v < n_cu:
-        L -= 1
-    return L
+    best = None
+    for L in range(L_lam, 0, -1):
+        wg = segs(L) * h_v
+        if wg < n_cu and L > 1:
+            continue
+        cost = -(-wg // n_cu) * L + 0.5 * L + 0.25 * (-(-Nm // L) - 1)
+        if best is None or cost < best[0]:
+            best = (cost, L)
+    return best[1]
 
 
 @pytest.mark.parametrize("name,B_,T,h_qk,h_v,L", [
-    ("tp8", 1, 32768, 2, 8, 16),      # sqrt(512) = 22.6 -> 23, lowered to 16 so 8 x 32 segments fill 256 CUs
-    ("tp2", 1, 32768, 8, 24, 23),
-    ("tp1", 1, 32768, 16, 16, 23),
-    ("tp1_b4", 4, 32768, 16, 16, 23),
-    ("long", 1, 262144, 2, 8, 64),
+    ("tp8", 1, 32768, 2, 8, 16),      # sqrt(512) = 22.6 -> 23; 16 is the largest that fills 256 CUs
+    ("tp2", 1, 32768, 8, 24, 16),     # 16 x 24 x 32 segments = three whole rounds (23: 552 workgroups)
+    ("tp1", 1, 32768, 16, 16, 16),    # two whole rounds
+    ("tp1_b4", 4, 32768, 16, 16, 16),
+    ("long", 1, 262144, 2, 8, 43),   # 96 segments x 8 heads = three whole rounds
     ("tiny", 1, 512, 1, 1, 8),        # 8 chunks < 2 (6 + 1): kept whole
 ])
 def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
