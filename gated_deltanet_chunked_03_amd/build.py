@@ -18,8 +18,6 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-    # the iterative ILP scheduler interleaves the long MFMA and VALU runs better
-    "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
     # packed fp32 ops are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,

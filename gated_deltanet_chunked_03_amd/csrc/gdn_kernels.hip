@@ -63,7 +63,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int CH = kChunk;
 constexpr int DK = kDim;
-constexpr int NTHR = 256;
+constexpr int NTHR = 256;      // k_prep, k_cp_combine: 4 waves
+constexpr int NTHR_CH = 512;   // chain kernels: 8 waves
+constexpr int NW_CH = NTHR_CH / 64;
 constexpr int LDQ = 136;   // row stride (elements) of [64][128] bf16 tiles
 constexpr int LDKT = 72;   // row stride of [128][64] bf16 tiles
 constexpr int LDF = 68;    // row stride of [64][64] fp32 tiles
@@ -129,6 +131,17 @@ __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
     lo = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
 }
 
+// hi/lo operand of eight accumulator values: elements 0..3 from a, 4..7 from b.
+__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+    unsigned h[4], l[4];
+    split_pair(a[0], a[1], h[0], l[0]);
+    split_pair(a[2], a[3], h[1], l[1]);
+    split_pair(b[0], b[1], h[2], l[2]);
+    split_pair(b[2], b[3], h[3], l[3]);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
 // Elements [B, B + 8) of an accumulator tile as a hi/lo B operand.
 template <int B>
 __device__ __forceinline__ void split_acc(const f32x16& a, bf16x8& hi, bf16x8& lo) {
@@ -156,32 +169,17 @@ __device__ __forceinline__ bf16x8 lds_op16(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Row of the transposed [128][64] LDS tiles (K^T, V^T) that holds column c:
-// the low three bits are XORed with bits 3..5 and 6, so that the staging
-// stores (sixteen lanes eight columns apart, four consecutive tokens each)
-// fall on distinct banks; a bijection on 0..127.
-__device__ __forceinline__ int trow(int c) { return (c & ~7) | ((c ^ (c >> 3) ^ (c >> 6)) & 7); }
-
-// B operand from one column of a token-major global tile: element e is token
-// kb + kperm(h, e); tokens >= nvalid read as zero.
-template <typename IO>
-__device__ __forceinline__ void g_col_op(const IO* col0, size_t ts, int kb, int h, int nvalid,
-                                         bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int t = kb + ((e < 4) ? (4 * h + e) : (4 + 4 * h + e));
-        const float x = (t < nvalid) ? (float)col0[(size_t)t * ts] : 0.f;
-        if (Io<IO>::kExact) {
-            hi[e] = (bf16)x;
-            lo[e] = (bf16)0.f;
-        } else {
-            bf16 th, tl;
-            split1(x, th, tl);
-            hi[e] = th;
-            lo[e] = tl;
-        }
-    }
+// Position of contraction index x in an LDS operand row: within each block of
+// 32, x = 16 b4 + 4 a + e (a < 4, e < 4) sits at 8 a + 4 b4 + e.
+__device__ __forceinline__ int kp(int x) {
+    return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
 }
+
+// Transposed tiles (K^T, V^T: row = d_k or d_v index d, 64 tokens) XOR their
+// 8-element chunks with (d / 16) mod 8: the staging stores (32 lanes on rows
+// four apart) then meet at most two to a bank, and the operand reads (16
+// consecutive rows) not at all.
+__device__ __forceinline__ int tswz(int d) { return 8 * ((d >> 4) & 7); }
 
 // ----------------------------------------------------------------------------
 // Work items: segments and chunks
@@ -449,8 +447,8 @@ __device__ __forceinline__ void prep_fetch(PrepIn<IO>& r, const Params& p, size_
 // workgroup walks its chunks, fetching the next chunk's inputs while it works
 // on the current one. Per (chunk slot, value head), block b = slot h_v + h:
 //   prep_T + b t_stride: T diag(beta) split into bf16 hi and lo, [part][row][k]
-//     (2 x 64 x 64), the k (column) axis permuted within each group of 16 as
-//     the chain kernels' LDS operands are (zeros above the diagonal);
+//     (2 x 64 x 64), the k (column) axis in the kp order of the chain
+//     kernels' LDS operands (zeros above the diagonal);
 //   prep_GB + b gb_stride: gamma (64 fp32), then beta (64 fp32).
 template <typename IO>
 __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
@@ -509,6 +507,19 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
         if (wave < 3) gram_a<IO, 3>(sm, krow0, ts, nv_cur, wave, 3);
         else gram_a<IO, 1>(sm, krow0, ts, nv_cur, 9, 1);
         __syncthreads();
+        // beta of the columns this thread scales T by below, read now: the next
+        // chunk's staging rewrites the gate arrays as soon as a wave has passed
+        // the barrier that ends this chunk's inversion
+        f32x4 bcol[4];
+        {
+            const int q = (threadIdx.x >> 1) & 1;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int l0 = 32 * q + 4 * (2 * (threadIdx.x & 1) + u);
+                bcol[2 * u] = *reinterpret_cast<const f32x4*>(sm.beta + l0);
+                bcol[2 * u + 1] = *reinterpret_cast<const f32x4*>(sm.beta + l0 + 16);
+            }
+        }
         inv_diag<EX>(sm);
         // the diagonal blocks this wave reads next are the ones it just wrote
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -519,33 +530,26 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
             default: inv_col<3, EX>(sm); break;
         }
         __syncthreads();
-        // (the next chunk's LDS writes touch k_rm and the gate arrays only, all
-        // read before the previous barrier; T is rewritten after two more).
-        // T diag(beta): thread t takes row t / 4 and the 16 physical k
-        // positions 16 (t % 4) ..; physical 4-blocks 0..3 of a 16-group hold
-        // logical blocks 0, 2, 1, 3.
+        // (the next chunk's LDS writes touch k_rm and the gate arrays, whose
+        // last reads come before the previous barrier; T is rewritten after two
+        // more).
+        // T diag(beta) with its column (token) axis in kp order: thread t takes
+        // row t / 4 and the physical 8-element pieces 32 q + 8 a, q = (t / 2) % 2,
+        // a = 2 (t % 2) + (0, 1); piece 32 q + 8 a holds logical columns
+        // 32 q + 4 a + (0..3) and 32 q + 16 + 4 a + (0..3).
         bf16* Tg = reinterpret_cast<bf16*>(p.prep_T + ((size_t)slot * p.h_v + h) * (size_t)p.t_stride);
         {
-            const int row = threadIdx.x >> 2, g16 = 16 * (threadIdx.x & 3);
-            const float* tr = sm.t + row * LDF + g16;
-            const float* br = sm.beta + g16;
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(tr) * *reinterpret_cast<const f32x4*>(br);
-            const f32x4 b1 = *reinterpret_cast<const f32x4*>(tr + 8) * *reinterpret_cast<const f32x4*>(br + 8);
-            const f32x4 b2 = *reinterpret_cast<const f32x4*>(tr + 4) * *reinterpret_cast<const f32x4*>(br + 4);
-            const f32x4 b3 = *reinterpret_cast<const f32x4*>(tr + 12) * *reinterpret_cast<const f32x4*>(br + 12);
-            bf16x4 h0, l0, h1, l1, h2, l2, h3, l3;
-            split4(b0, h0, l0);
-            split4(b1, h1, l1);
-            split4(b2, h2, l2);
-            split4(b3, h3, l3);
-            const bf16x8 hA = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 hB = __builtin_shufflevector(h2, h3, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 lA = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 lB = __builtin_shufflevector(l2, l3, 0, 1, 2, 3, 4, 5, 6, 7);
-            *reinterpret_cast<bf16x8*>(Tg + row * CH + g16) = hA;
-            *reinterpret_cast<bf16x8*>(Tg + row * CH + g16 + 8) = hB;
-            *reinterpret_cast<bf16x8*>(Tg + (CH + row) * CH + g16) = lA;
-            *reinterpret_cast<bf16x8*>(Tg + (CH + row) * CH + g16 + 8) = lB;
+            const int row = threadIdx.x >> 2, q = (threadIdx.x >> 1) & 1;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int a = 2 * (threadIdx.x & 1) + u, l0 = 32 * q + 4 * a, l1 = l0 + 16;
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l0) * bcol[2 * u];
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l1) * bcol[2 * u + 1];
+                bf16x8 hi, lo;
+                split8(x0, x1, hi, lo);
+                *reinterpret_cast<bf16x8*>(Tg + row * CH + 32 * q + 8 * a) = hi;
+                *reinterpret_cast<bf16x8*>(Tg + (CH + row) * CH + 32 * q + 8 * a) = lo;
+            }
         }
     }
 }
@@ -557,20 +561,33 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
 //   V' = T diag(beta) Y                           (= U - W S)
 //   O  = diag(e^gamma) Q S + P V',  P = (Q K^T) o D  (both times the scale)
 //   S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
-// so each wave needs, besides its own state columns, only K, K^T, V^T, Q, P
-// and T from LDS, and the products of different waves never meet.
+// Every product keeps the d_v columns apart, so a workgroup of 8 waves gives
+// wave w the columns [16w, 16w + 16): its 128 x 16 slice of S, its slices of
+// Y, V' and the output stay in its registers, and the state chain never
+// crosses waves. Two waves share each SIMD, so one wave's splits and scalings
+// run while the other's MFMAs do. Operands that every wave needs (K, K^T, V^T,
+// Q, T, P) are staged in LDS.
+//
+// 16x16x32 bf16 MFMA, lane l = 16 g + c: A row c, B column c, each with the
+// eight k values 8g .. 8g + 7; C/D rows 4g .. 4g + 3 of column c. Two C tiles
+// stacked (rows 0..15 and 16..31) therefore hand lane group g the rows
+// 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3: that is the k order of a B (or,
+// mirrored, an A) operand once the contraction axis of every LDS operand is
+// stored in the order kp below, and accumulator tiles feed the next product
+// without any shuffle.
+
 
 template <bool EX>
 struct __attribute__((aligned(16))) ChainSmem {
-    bf16 q_hi[CH * LDQ];                  // Q token-major, d_k permuted
-    bf16 q_lo[EX ? 8 : CH * LDQ];
-    bf16 k_hi[CH * LDQ];                  // K token-major, d_k permuted
+    bf16 k_hi[CH * LDQ];                  // K token-major, d_k in kp order
     bf16 k_lo[EX ? 8 : CH * LDQ];
-    bf16 kt_hi[DK * LDKT];                // K^T: [d_k][token permuted]
+    bf16 q_hi[CH * LDQ];                  // Q token-major, d_k in kp order
+    bf16 q_lo[EX ? 8 : CH * LDQ];
+    bf16 kt_hi[DK * LDKT];                // K^T: row d_k, tokens in kp order (chunks swizzled)
     bf16 kt_lo[EX ? 8 : DK * LDKT];
-    bf16 vt[EX ? DK * LDKT : 8];          // V^T (bf16 inputs; fp32 V is read from HBM)
-    bf16 p[2 * CH * LDP];                 // P = (Q K^T) o D, causal: hi rows, then lo rows
-    bf16 t[2 * CH * LDP];                 // T diag(beta): hi rows, then lo rows (token axis permuted)
+    bf16 vt[EX ? DK * LDKT : 8];          // V^T: row d_v, tokens in order (chunks swizzled)
+    bf16 t[2 * CH * LDP];                 // T diag(beta): hi rows, then lo rows; tokens in kp order
+    bf16 p[2 * CH * LDP];                 // P: hi rows, then lo rows; columns in kp order
     float gam[CH];                        // gamma
     float eg[CH];                         // exp(gamma)
     float egs[CH];                        // scale exp(gamma)
@@ -580,14 +597,14 @@ struct __attribute__((aligned(16))) ChainSmem {
 
 // One chunk's inputs in registers between the global loads and the LDS
 // stores, so that the next chunk's loads overlap the current chunk's work.
-// K, V: thread t holds token rows 4 (t / 16) + j (j < 4), columns
-// 8 (t % 16) .. + 8 (sixteen lanes cover one 256-byte row, and a lane holds
-// four consecutive tokens of each of its columns, written to K^T / V^T as
-// 8-byte stores). Q: rows t / 16 + 16 j, same columns. T: four 16-byte pieces
-// (t + 256 j) of its [part][row][64] image. Gates: gamma, beta of token lane.
+// K, V, Q: thread t holds tokens 4 (t / 32) + j (j < 4), columns
+// 4 (t % 32) .. + 4 (32 lanes cover one 256-byte row, and a lane holds four
+// consecutive tokens of each of its columns, written to K^T / V^T as 8-byte
+// stores). T: pieces t and t + 512 of its [part][row][64] image (16 bytes
+// each). Gates: gamma, beta of token lane.
 template <typename IO> struct Chunk;
-template <> struct Chunk<bf16> { u32x4 k[4], v[4], q[4], t[4]; float gl, bl; };
-template <> struct Chunk<float> { f32x4 k[8], q[8]; u32x4 t[4]; float gl, bl; };
+template <> struct Chunk<bf16> { u32x2 k[4], v[4], q[4]; u32x4 t[2]; float gl, bl; };
+template <> struct Chunk<float> { f32x4 k[4], q[4]; u32x4 t[2]; float gl, bl; };
 
 // Rows past the end of the sequence (last chunk only) read its last row
 // again: their values never matter, since such tokens carry beta = 0, which
@@ -601,42 +618,39 @@ template <typename IO, bool WANT_Q, bool WANT_V>
 __device__ __forceinline__ void fetch_chunk(Chunk<IO>& r, const Params& p, size_t tok0, int nvalid, int h,
                                             int hq, int slot) {
     constexpr bool EX = Io<IO>::kExact;
-    const int t = threadIdx.x, m = t >> 4, c8 = (t & 15) * 8;
+    const int t = threadIdx.x, m = t >> 5, c4 = (t & 31) * 4;
     const int ts = p.h_qk * DK, tsv = p.h_v * DK;
     const IO* kb = static_cast<const IO*>(p.k) + tok0 * (size_t)ts + (size_t)hq * DK;
     const IO* qb = static_cast<const IO*>(p.q) + tok0 * (size_t)ts + (size_t)hq * DK;
     const IO* vb = static_cast<const IO*>(p.v) + tok0 * (size_t)tsv + (size_t)h * DK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int rk = min(4 * m + j, nvalid - 1), rq = min(m + 16 * j, nvalid - 1);
-        const unsigned ok_k = (unsigned)(rk * ts + c8), ok_v = (unsigned)(rk * tsv + c8);
-        const unsigned ok_q = (unsigned)(rq * ts + c8);
+        const int row = min(4 * m + j, nvalid - 1);
+        const unsigned ok = (unsigned)(row * ts + c4), ov = (unsigned)(row * tsv + c4);
         if constexpr (EX) {
-            r.k[j] = *reinterpret_cast<const u32x4*>(kb + ok_k);
-            if (WANT_V) r.v[j] = *reinterpret_cast<const u32x4*>(vb + ok_v);
-            if (WANT_Q) r.q[j] = *reinterpret_cast<const u32x4*>(qb + ok_q);
+            r.k[j] = *reinterpret_cast<const u32x2*>(kb + ok);
+            if (WANT_V) r.v[j] = *reinterpret_cast<const u32x2*>(vb + ov);
+            if (WANT_Q) r.q[j] = *reinterpret_cast<const u32x2*>(qb + ok);
         } else {
-            r.k[2 * j] = *reinterpret_cast<const f32x4*>(kb + ok_k);
-            r.k[2 * j + 1] = *reinterpret_cast<const f32x4*>(kb + ok_k + 4);
-            if (WANT_Q) {
-                r.q[2 * j] = *reinterpret_cast<const f32x4*>(qb + ok_q);
-                r.q[2 * j + 1] = *reinterpret_cast<const f32x4*>(qb + ok_q + 4);
-            }
+            r.k[j] = *reinterpret_cast<const f32x4*>(kb + ok);
+            if (WANT_Q) r.q[j] = *reinterpret_cast<const f32x4*>(qb + ok);
         }
     }
     const size_t blk = (size_t)slot * p.h_v + h;
     const u32x4* Tg = reinterpret_cast<const u32x4*>(p.prep_T + blk * (size_t)p.t_stride);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.t[j] = Tg[t + NTHR * j];
+    for (int j = 0; j < 2; ++j) r.t[j] = Tg[t + NTHR_CH * j];
     const float* gb = p.prep_GB + blk * (size_t)p.gb_stride;
     r.gl = gb[lane_id()];
     r.bl = gb[CH + lane_id()];
 }
 
-// Two bf16 of the same column from two rows packed into one 32-bit word.
-__device__ __forceinline__ unsigned int pack_col(const u32x4& a, const u32x4& b, int e) {
-    const unsigned int wa = a[e >> 1], wb = b[e >> 1];
-    return (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+// Element e (0..3) of four bf16 rows, packed two tokens to a 32-bit word.
+__device__ __forceinline__ u32x2 pack_col4(const u32x2 (&a)[4], int e) {
+    const int w = e >> 1, sh = 16 * (e & 1);
+    const unsigned x0 = (a[0][w] >> sh) & 0xffffu, x1 = (a[1][w] >> sh) & 0xffffu;
+    const unsigned x2 = (a[2][w] >> sh) & 0xffffu, x3 = (a[3][w] >> sh) & 0xffffu;
+    return u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
 }
 
 // Writes a fetched chunk to LDS: K token-major and transposed (four
@@ -645,7 +659,7 @@ __device__ __forceinline__ unsigned int pack_col(const u32x4& a, const u32x4& b,
 template <typename IO, bool WANT_Q, bool WANT_V>
 __device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const Chunk<IO>& r, float scale) {
     constexpr bool EX = Io<IO>::kExact;
-    const int t = threadIdx.x, lane = lane_id(), m = t >> 4, c8 = (t & 15) * 8;
+    const int t = threadIdx.x, lane = lane_id(), m = t >> 5, c4 = (t & 31) * 4;
     {   // every wave writes the same values (no branch in the chunk loop)
         const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.gl), 63));
         const float es = __expf(r.gl);
@@ -655,335 +669,298 @@ __device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const
         sm.egc[lane] = __expf(gc - r.gl);
         sm.red[0] = __expf(gc);
     }
-    const int tp = pk(4 * m);   // the four tokens stay contiguous under the permutation
+    const int kc = kp(c4), tk = kp(4 * m) ^ tswz(c4), tv = (4 * m) ^ tswz(c4);
     if constexpr (EX) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 4 * m + j;
-            *reinterpret_cast<u32x2*>(sm.k_hi + row * LDQ + pk(c8)) = u32x2{r.k[j][0], r.k[j][1]};
-            *reinterpret_cast<u32x2*>(sm.k_hi + row * LDQ + pk(c8 + 4)) = u32x2{r.k[j][2], r.k[j][3]};
-        }
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(sm.k_hi + (4 * m + j) * LDQ + kc) = r.k[j];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = c8 + e;
-            *reinterpret_cast<u32x2*>(sm.kt_hi + trow(c) * LDKT + tp) =
-                u32x2{pack_col(r.k[0], r.k[1], e), pack_col(r.k[2], r.k[3], e)};
-            if (WANT_V)
-                *reinterpret_cast<u32x2*>(sm.vt + trow(c) * LDKT + tp) =
-                    u32x2{pack_col(r.v[0], r.v[1], e), pack_col(r.v[2], r.v[3], e)};
+        for (int e = 0; e < 4; ++e) {
+            *reinterpret_cast<u32x2*>(sm.kt_hi + (c4 + e) * LDKT + tk) = pack_col4(r.k, e);
+            if (WANT_V) *reinterpret_cast<u32x2*>(sm.vt + (c4 + e) * LDKT + tv) = pack_col4(r.v, e);
+        }
+        if (WANT_Q) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(sm.q_hi + (4 * m + j) * LDQ + kc) = r.q[j];
         }
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int row = 4 * m + j;
-            bf16x4 ah, al, bh, bl;
-            split4(r.k[2 * j], ah, al);
-            split4(r.k[2 * j + 1], bh, bl);
-            *reinterpret_cast<bf16x4*>(sm.k_hi + row * LDQ + pk(c8)) = ah;
-            *reinterpret_cast<bf16x4*>(sm.k_lo + row * LDQ + pk(c8)) = al;
-            *reinterpret_cast<bf16x4*>(sm.k_hi + row * LDQ + pk(c8 + 4)) = bh;
-            *reinterpret_cast<bf16x4*>(sm.k_lo + row * LDQ + pk(c8 + 4)) = bl;
+            bf16x4 hi, lo;
+            split4(r.k[j], hi, lo);
+            *reinterpret_cast<bf16x4*>(sm.k_hi + (4 * m + j) * LDQ + kc) = hi;
+            *reinterpret_cast<bf16x4*>(sm.k_lo + (4 * m + j) * LDQ + kc) = lo;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = c8 + e;
-            f32x4 x;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = r.k[2 * j + (e >> 2)][e & 3];
-            bf16x4 xh, xl;
-            split4(x, xh, xl);
-            *reinterpret_cast<bf16x4*>(sm.kt_hi + trow(c) * LDKT + tp) = xh;
-            *reinterpret_cast<bf16x4*>(sm.kt_lo + trow(c) * LDKT + tp) = xl;
+        for (int e = 0; e < 4; ++e) {
+            const f32x4 x = {r.k[0][e], r.k[1][e], r.k[2][e], r.k[3][e]};
+            bf16x4 hi, lo;
+            split4(x, hi, lo);
+            *reinterpret_cast<bf16x4*>(sm.kt_hi + (c4 + e) * LDKT + tk) = hi;
+            *reinterpret_cast<bf16x4*>(sm.kt_lo + (c4 + e) * LDKT + tk) = lo;
         }
-    }
-    if (WANT_Q) {
+        if (WANT_Q) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = m + 16 * j;
-            const int o0 = row * LDQ + pk(c8), o1 = row * LDQ + pk(c8 + 4);
-            if constexpr (EX) {
-                *reinterpret_cast<u32x2*>(sm.q_hi + o0) = u32x2{r.q[j][0], r.q[j][1]};
-                *reinterpret_cast<u32x2*>(sm.q_hi + o1) = u32x2{r.q[j][2], r.q[j][3]};
-            } else {
-                bf16x4 ah, al, bh, bl;
-                split4(r.q[2 * j], ah, al);
-                split4(r.q[2 * j + 1], bh, bl);
-                *reinterpret_cast<bf16x4*>(sm.q_hi + o0) = ah;
-                *reinterpret_cast<bf16x4*>(sm.q_lo + o0) = al;
-                *reinterpret_cast<bf16x4*>(sm.q_hi + o1) = bh;
-                *reinterpret_cast<bf16x4*>(sm.q_lo + o1) = bl;
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 hi, lo;
+                split4(r.q[j], hi, lo);
+                *reinterpret_cast<bf16x4*>(sm.q_hi + (4 * m + j) * LDQ + kc) = hi;
+                *reinterpret_cast<bf16x4*>(sm.q_lo + (4 * m + j) * LDQ + kc) = lo;
             }
         }
     }
-    // T: piece t + 256 j of the [part][row][64] image -> row part * 64 + row of sm.t
+    // T: piece t + 512 j of the [part][row][64] image -> row part * 64 + row of sm.t
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int pc = t + NTHR * j, prow = pc >> 3, k8 = (pc & 7) * 8;
+    for (int j = 0; j < 2; ++j) {
+        const int pc = t + NTHR_CH * j, prow = pc >> 3, k8 = (pc & 7) * 8;
         *reinterpret_cast<u32x4*>(sm.t + prow * LDP + k8) = r.t[j];
     }
 }
 
-// scale P, P = (Q K^T) o D, on the ten lower 16x16 tiles (16x16x32 MFMA, each tile
-// computed transposed so that a lane holds four consecutive columns of one
-// row), split into hi/lo; the two upper tiles inside the diagonal 32-blocks,
-// which the P V' product reads, are zeroed. Jobs first, first + stride, ...
-template <bool EX, int NJOB>
-__device__ void gram_p(ChainSmem<EX>& sm, int first, int stride, float scale) {
-    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
-    f32x4 acc[NJOB];
-    int bi[NJOB], bj[NJOB];
+// One tile of scale P, P = (Q K^T) o D: the lower 16x16 tile `job` (0..9),
+// computed transposed (K rows against Q rows) so that a lane ends up with four
+// consecutive columns of one row of P, stored split into hi/lo. The two upper
+// tiles inside the diagonal 32-blocks, which the P V' product reads, stay zero
+// (cleared once per kernel).
+template <bool EX>
+__device__ __forceinline__ void gram_tile(ChainSmem<EX>& sm, int job, float scale) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    int ri, ii;
+    lower_tile(job, ri, ii);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < NJOB; ++t) {
-        lower_tile(first + stride * t, bi[t], bj[t]);
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int kb = 32 * ks + 8 * g4;
-#pragma unroll
-        for (int t = 0; t < NJOB; ++t) {
-            const int ra = 16 * bj[t] + n, rb = 16 * bi[t] + n;   // A: K rows of bj; B: Q rows of bi
-            const bf16x8 a = lds_row8(sm.k_hi + ra * LDQ + kb);
-            const bf16x8 b = lds_row8(sm.q_hi + rb * LDQ + kb);
-            acc[t] = mma16k32(a, b, acc[t]);
-            if (!EX) {
-                acc[t] = mma16k32(a, lds_row8(sm.q_lo + rb * LDQ + kb), acc[t]);
-                acc[t] = mma16k32(lds_row8(sm.k_lo + ra * LDQ + kb), b, acc[t]);
-            }
+    for (int s = 0; s < 4; ++s) {
+        const int kb = 32 * s + 8 * g;
+        const bf16x8 a = lds_row8(sm.k_hi + (16 * ii + c) * LDQ + kb);
+        const bf16x8 b = lds_row8(sm.q_hi + (16 * ri + c) * LDQ + kb);
+        acc = mma16k32(a, b, acc);
+        if (!EX) {
+            acc = mma16k32(a, lds_row8(sm.q_lo + (16 * ri + c) * LDQ + kb), acc);
+            acc = mma16k32(lds_row8(sm.k_lo + (16 * ii + c) * LDQ + kb), b, acc);
         }
     }
+    const int r = 16 * ri + c, i0 = 16 * ii + 4 * g;   // row r of P, columns i0 .. i0 + 3
+    const float gr = sm.gam[r];
+    const f32x4 gi = *reinterpret_cast<const f32x4*>(sm.gam + i0);
+    f32x4 v;
 #pragma unroll
-    for (int t = 0; t < NJOB; ++t) {
-        const int i = 16 * bi[t] + n, j0 = 16 * bj[t] + 4 * g4;   // row i, columns j0 .. j0 + 3
-        const float gi = sm.gam[i];
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(sm.gam + j0);
-        f32x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (i >= j0 + r) ? scale * __expf(gi - gj[r]) * acc[t][r] : 0.f;
-        bf16x4 hi, lo;
-        split4(v, hi, lo);
-        *reinterpret_cast<bf16x4*>(sm.p + i * LDP + pk(j0)) = hi;
-        *reinterpret_cast<bf16x4*>(sm.p + (CH + i) * LDP + pk(j0)) = lo;
-    }
+    for (int e = 0; e < 4; ++e) v[e] = (i0 + e <= r) ? scale * __expf(gr - gi[e]) * acc[e] : 0.f;
+    bf16x4 hi, lo;
+    split4(v, hi, lo);
+    *reinterpret_cast<bf16x4*>(sm.p + r * LDP + kp(i0)) = hi;
+    *reinterpret_cast<bf16x4*>(sm.p + (CH + r) * LDP + kp(i0)) = lo;
 }
 
-__device__ __forceinline__ void zero_p_tile(bf16* p, int bi, int bj) {
-    // lane: row 16 bi + lane / 4, columns 16 bj + 4 (lane % 4) .. + 4, hi and lo
-    const int lane = lane_id(), i = 16 * bi + (lane >> 2), j0 = 16 * bj + 4 * (lane & 3);
-    *reinterpret_cast<u32x2*>(p + i * LDP + pk(j0)) = u32x2{0u, 0u};
-    *reinterpret_cast<u32x2*>(p + (CH + i) * LDP + pk(j0)) = u32x2{0u, 0u};
+// The P tiles of a chunk: one per wave, waves 0 and 1 take a second.
+template <bool EX>
+__device__ __forceinline__ void gram_p(ChainSmem<EX>& sm, float scale) {
+    const int w = wave_id();
+    gram_tile<EX>(sm, w, scale);
+    if (w < 2) gram_tile<EX>(sm, NW_CH + w, scale);
 }
 
-// The state as hi/lo B operands, one pair per 16-row k step.
+// The state as hi/lo B operands, one pair per 32-row k step.
 struct SplitS {
-    bf16x8 hi[8], lo[8];
+    bf16x8 hi[4], lo[4];
 };
-__device__ __forceinline__ void split_state(const f32x16 S[4], SplitS& ss) {
+__device__ __forceinline__ void split_state(const f32x4 S[8], SplitS& ss) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) split_half(S[ks >> 1], ks & 1, ss.hi[ks], ss.lo[ks]);
+    for (int s = 0; s < 4; ++s) split8(S[2 * s], S[2 * s + 1], ss.hi[s], ss.lo[s]);
 }
 
 // V' = T diag(beta) (V - diag(e^gamma) K S) for this wave's columns.
 // KS: A = K rows (token-major LDS), B = S; Y in fp32 on the accumulators
 // (V from V^T in LDS, four consecutive tokens per 8-byte read, or from HBM
 // for fp32 inputs); then (T diag(beta)) Y with both split hi/lo (T is lower
-// triangular: token tile 0 needs k steps 0..1).
+// triangular: token tiles 0 and 1 need k step 0 only).
 template <typename IO, bool WANT_V>
 __device__ void chain_vp(const ChainSmem<Io<IO>::kExact>& sm, const SplitS& ss, const IO* vcol, size_t ts,
-                         int nvalid, f32x16 Vp[2]) {
+                         int nvalid, f32x4 Vp[4]) {
     constexpr bool EX = Io<IO>::kExact;
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5, n = 32 * wave_id() + col;
-    f32x16 KS[2] = {f32x16{}, f32x16{}};
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, n = 16 * wave_id() + c;
+    f32x4 KS[4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 kh[2], kl[2];
+    for (int rt = 0; rt < 4; ++rt) KS[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            kh[ti] = lds_op16(sm.k_hi + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
-            if (!EX) kl[ti] = lds_op16(sm.k_lo + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
+    for (int s = 0; s < 4; ++s) {
+        bf16x8 kh[4], kl[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            kh[rt] = lds_op16(sm.k_hi + (16 * rt + c) * LDQ + 32 * s + 8 * g);
+            if (!EX) kl[rt] = lds_op16(sm.k_lo + (16 * rt + c) * LDQ + 32 * s + 8 * g);
         }
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) KS[ti] = mma32(kh[ti], ss.hi[ks], KS[ti]);
+        for (int rt = 0; rt < 4; ++rt) KS[rt] = mma16k32(kh[rt], ss.hi[s], KS[rt]);
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) KS[ti] = mma32(kh[ti], ss.lo[ks], KS[ti]);
+        for (int rt = 0; rt < 4; ++rt) KS[rt] = mma16k32(kh[rt], ss.lo[s], KS[rt]);
         if (!EX) {
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) KS[ti] = mma32(kl[ti], ss.hi[ks], KS[ti]);
+            for (int rt = 0; rt < 4; ++rt) KS[rt] = mma16k32(kl[rt], ss.hi[s], KS[rt]);
         }
     }
-    // Y = V - e^gamma KS on rows 32 ti + 8 q + 4 h + (0..3)
-    const int vrow = trow(n) * LDKT;
+    // Y = V - e^gamma KS on rows 16 rt + 4 g + (0..3)
+    const int vrow = n * LDKT, sw = tswz(n);
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int rt = 0; rt < 4; ++rt) {
+        const int r0 = 16 * rt + 4 * g;
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(sm.eg + r0);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (WANT_V) {
+            if constexpr (EX) {
+                const u32x2 vv = *reinterpret_cast<const u32x2*>(sm.vt + vrow + (r0 ^ sw));
+                v = f32x4{__uint_as_float(vv[0] << 16), __uint_as_float(vv[0] & 0xffff0000u),
+                          __uint_as_float(vv[1] << 16), __uint_as_float(vv[1] & 0xffff0000u)};
+            } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r0 = 32 * ti + 8 * q + 4 * h;
-            const f32x4 eg = *reinterpret_cast<const f32x4*>(sm.eg + r0);
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (WANT_V) {
-                if constexpr (EX) {
-                    const u32x2 vv = *reinterpret_cast<const u32x2*>(sm.vt + vrow + pk(r0));
-                    v = f32x4{__uint_as_float(vv[0] << 16), __uint_as_float(vv[0] & 0xffff0000u),
-                              __uint_as_float(vv[1] << 16), __uint_as_float(vv[1] & 0xffff0000u)};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = (r0 + e < nvalid) ? (float)vcol[(size_t)(r0 + e) * ts] : 0.f;
-                }
+                for (int e = 0; e < 4; ++e) v[e] = (r0 + e < nvalid) ? (float)vcol[(size_t)(r0 + e) * ts] : 0.f;
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) KS[ti][4 * q + e] = fmaf(-eg[e], KS[ti][4 * q + e], v[e]);
         }
-    Vp[0] = Vp[1] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+        for (int e = 0; e < 4; ++e) KS[rt][e] = fmaf(-eg[e], KS[rt][e], v[e]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) Vp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
         bf16x8 yh, yl;
-        split_half(KS[ks >> 1], ks & 1, yh, yl);
+        split8(KS[2 * s], KS[2 * s + 1], yh, yl);
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            if (ti == 0 && ks >= 2) continue;
-            const bf16x8 th = lds_op16(sm.t + (32 * ti + col) * LDP + 16 * ks + 8 * h);
-            const bf16x8 tl = lds_op16(sm.t + (CH + 32 * ti + col) * LDP + 16 * ks + 8 * h);
-            Vp[ti] = mma32(th, yh, Vp[ti]);
-            Vp[ti] = mma32(th, yl, Vp[ti]);
-            Vp[ti] = mma32(tl, yh, Vp[ti]);
+        for (int rt = 0; rt < 4; ++rt) {
+            if (s == 1 && rt < 2) continue;
+            const bf16x8 th = lds_op16(sm.t + (16 * rt + c) * LDP + 32 * s + 8 * g);
+            const bf16x8 tl = lds_op16(sm.t + (CH + 16 * rt + c) * LDP + 32 * s + 8 * g);
+            Vp[rt] = mma16k32(th, yh, Vp[rt]);
+            Vp[rt] = mma16k32(th, yl, Vp[rt]);
+            Vp[rt] = mma16k32(tl, yh, Vp[rt]);
         }
     }
 }
 
-// O^T = scale S^T (diag(e^gamma) Q)^T for this wave's d_v rows (token columns): the
-// split state serves as the A operand unchanged (the MFMA's A and B register
-// layouts mirror each other). Then (chain_pv_out, after P is in LDS) the
-// causal part V'^T P^T and the store: a lane holds four consecutive d_v of
-// one token per accumulator group, written as one 8- (bf16) or 16-byte
-// (fp32) store; rows >= nvalid are not written.
+// O^T = scale S^T (diag(e^gamma) Q)^T for this wave's d_v rows (token columns):
+// the split state serves as the A operand unchanged (the MFMA's A and B
+// register layouts mirror each other). Then (chain_pv_out, after P is in
+// LDS) the causal part V'^T P^T and the store: a lane holds four consecutive
+// d_v of one token per tile, written as one 8- (bf16) or 16-byte (fp32)
+// store.
 template <bool EX>
-__device__ void chain_qs(const ChainSmem<EX>& sm, const SplitS& ss, f32x16 O[2]) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
-    O[0] = O[1] = f32x16{};
+__device__ void chain_qs(const ChainSmem<EX>& sm, const SplitS& ss, f32x4 O[4]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 qh[2], ql[2];
+    for (int ct = 0; ct < 4; ++ct) O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            qh[ti] = lds_op16(sm.q_hi + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
-            if (!EX) ql[ti] = lds_op16(sm.q_lo + (32 * ti + col) * LDQ + 16 * ks + 8 * h);
+    for (int s = 0; s < 4; ++s) {
+        bf16x8 qh[4], ql[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            qh[ct] = lds_op16(sm.q_hi + (16 * ct + c) * LDQ + 32 * s + 8 * g);
+            if (!EX) ql[ct] = lds_op16(sm.q_lo + (16 * ct + c) * LDQ + 32 * s + 8 * g);
         }
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(ss.hi[ks], qh[ti], O[ti]);
+        for (int ct = 0; ct < 4; ++ct) O[ct] = mma16k32(ss.hi[s], qh[ct], O[ct]);
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(ss.lo[ks], qh[ti], O[ti]);
+        for (int ct = 0; ct < 4; ++ct) O[ct] = mma16k32(ss.lo[s], qh[ct], O[ct]);
         if (!EX) {
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) O[ti] = mma32(ss.hi[ks], ql[ti], O[ti]);
+            for (int ct = 0; ct < 4; ++ct) O[ct] = mma16k32(ss.hi[s], ql[ct], O[ct]);
         }
     }
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) O[ti] *= sm.egs[32 * ti + col];
+    for (int ct = 0; ct < 4; ++ct) O[ct] *= sm.egs[16 * ct + c];
 }
 
 template <typename IO>
-__device__ void chain_pv_out(const ChainSmem<Io<IO>::kExact>& sm, const f32x16 Vp[2], f32x16 O[2], IO* orow0,
+__device__ void chain_pv_out(const ChainSmem<Io<IO>::kExact>& sm, const f32x4 Vp[4], f32x4 O[4], IO* orow0,
                              size_t ts, int nvalid, float* sink) {
     constexpr bool EX = Io<IO>::kExact;
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5, w = wave_id();
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {  // P is causal: token tile 0 needs k steps 0..1
+    for (int s = 0; s < 2; ++s) {  // P is causal: token tiles 0 and 1 need k step 0 only
         bf16x8 vh, vl;
-        split_half(Vp[ks >> 1], ks & 1, vh, vl);
+        split8(Vp[2 * s], Vp[2 * s + 1], vh, vl);
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            if (ti == 0 && ks >= 2) continue;
-            const bf16x8 ph = lds_op16(sm.p + (32 * ti + col) * LDP + 16 * ks + 8 * h);
-            const bf16x8 pl = lds_op16(sm.p + (CH + 32 * ti + col) * LDP + 16 * ks + 8 * h);
-            O[ti] = mma32(vh, ph, O[ti]);
-            O[ti] = mma32(vl, ph, O[ti]);
-            O[ti] = mma32(vh, pl, O[ti]);
+        for (int ct = 0; ct < 4; ++ct) {
+            if (s == 1 && ct < 2) continue;
+            const bf16x8 ph = lds_op16(sm.p + (16 * ct + c) * LDP + 32 * s + 8 * g);
+            const bf16x8 pl = lds_op16(sm.p + (CH + 16 * ct + c) * LDP + 32 * s + 8 * g);
+            O[ct] = mma16k32(vh, ph, O[ct]);
+            O[ct] = mma16k32(vl, ph, O[ct]);
+            O[ct] = mma16k32(vh, pl, O[ct]);
         }
     }
     // rows past the end of the sequence are written to a scratch line (every
     // chunk issues the same stores; see fetch_chunk)
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-        const int r = 32 * ti + col;
-        IO* dst = (r < nvalid) ? orow0 + (size_t)r * ts + 32 * w + 4 * h
-                               : reinterpret_cast<IO*>(sink + 32 * lane);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 x = f32x4{O[ti][4 * q], O[ti][4 * q + 1], O[ti][4 * q + 2], O[ti][4 * q + 3]};
-            if constexpr (EX) {
-                *reinterpret_cast<u32x2*>(dst + 8 * q) = u32x2{pack_rne(x[0], x[1]), pack_rne(x[2], x[3])};
-            } else {
-                *reinterpret_cast<f32x4*>(dst + 8 * q) = x;
-            }
+    for (int ct = 0; ct < 4; ++ct) {
+        const int r = 16 * ct + c;
+        IO* dst = (r < nvalid) ? orow0 + (size_t)r * ts + 16 * w + 4 * g : reinterpret_cast<IO*>(sink + 32 * lane);
+        if constexpr (EX) {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_rne(O[ct][0], O[ct][1]), pack_rne(O[ct][2], O[ct][3])};
+        } else {
+            *reinterpret_cast<f32x4*>(dst) = O[ct];
         }
     }
 }
 
 // S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V' (Vp is scaled in place).
 template <bool EX>
-__device__ void chain_state(const ChainSmem<EX>& sm, f32x16 S[4], f32x16 Vp[2]) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5;
+__device__ void chain_state(const ChainSmem<EX>& sm, f32x4 S[8], f32x4 Vp[4]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 e = *reinterpret_cast<const f32x4*>(sm.egc + 32 * ti + 8 * q + 4 * h);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Vp[ti][4 * q + r] *= e[r];
-        }
+    for (int rt = 0; rt < 4; ++rt) Vp[rt] *= *reinterpret_cast<const f32x4*>(sm.egc + 16 * rt + 4 * g);
     const float ec = sm.red[0];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) S[t] *= ec;
+    for (int i = 0; i < 8; ++i) S[i] *= ec;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int s = 0; s < 2; ++s) {
         bf16x8 vh, vl;
-        split_half(Vp[ks >> 1], ks & 1, vh, vl);
-        bf16x8 kh[4], kl[4];
+        split8(Vp[2 * s], Vp[2 * s + 1], vh, vl);
+        bf16x8 kh[8], kl[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            kh[t] = lds_op16(sm.kt_hi + trow(32 * t + col) * LDKT + 16 * ks + 8 * h);
-            if (!EX) kl[t] = lds_op16(sm.kt_lo + trow(32 * t + col) * LDKT + 16 * ks + 8 * h);
+        for (int i = 0; i < 8; ++i) {
+            const int off = (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i));
+            kh[i] = lds_op16(sm.kt_hi + off);
+            if (!EX) kl[i] = lds_op16(sm.kt_lo + off);
         }
-        // four independent chains: each tile is touched once per pass
+        // eight independent chains: each tile is touched once per pass
 #pragma unroll
-        for (int t = 0; t < 4; ++t) S[t] = mma32(kh[t], vh, S[t]);
+        for (int i = 0; i < 8; ++i) S[i] = mma16k32(kh[i], vh, S[i]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) S[t] = mma32(kh[t], vl, S[t]);
+        for (int i = 0; i < 8; ++i) S[i] = mma16k32(kh[i], vl, S[i]);
         if (!EX) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) S[t] = mma32(kl[t], vh, S[t]);
+            for (int i = 0; i < 8; ++i) S[i] = mma16k32(kl[i], vh, S[i]);
         }
     }
 }
 
 // ----------------------------------------------------------------------------
-// State tiles in registers: wave w holds columns [32w, 32w + 32) of a
-// [128][128] row-major fp32 matrix, as four 32-row accumulator tiles.
+// State tiles in registers: wave w holds columns [16w, 16w + 16) of a
+// [128][128] row-major fp32 matrix as eight 16-row accumulator tiles (tile i,
+// lane 16 g + c: rows 16 i + 4 g + (0..3), column 16 w + c).
 
-__device__ void load_state(const float* Sg, f32x16 S[4]) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5, c = 32 * wave_id() + col;
+__device__ void load_state(const float* Sg, f32x4 S[8]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, col = 16 * wave_id() + c;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[t][i] = Sg[(32 * t + acc_row(i, h)) * DK + c];
+        for (int e = 0; e < 4; ++e) S[i][e] = Sg[(16 * i + 4 * g + e) * DK + col];
 }
-__device__ void store_state(float* Sg, const f32x16 S[4]) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5, c = 32 * wave_id() + col;
+__device__ void store_state(float* Sg, const f32x4 S[8]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, col = 16 * wave_id() + c;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Sg[(32 * t + acc_row(i, h)) * DK + c] = S[t][i];
+        for (int e = 0; e < 4; ++e) Sg[(16 * i + 4 * g + e) * DK + col] = S[i][e];
 }
-__device__ void zero_state(f32x16 S[4]) {
+__device__ void zero_state(f32x4 S[8]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) S[t] = f32x16{};
+    for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
-__device__ void identity_state(f32x16 S[4]) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5, c = 32 * wave_id() + col;
+__device__ void identity_state(f32x4 S[8]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, col = 16 * wave_id() + c;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[t][i] = (32 * t + acc_row(i, h) == c) ? 1.f : 0.f;
+        for (int e = 0; e < 4; ++e) S[i][e] = (16 * i + 4 * g + e == col) ? 1.f : 0.f;
 }
 
 __device__ __forceinline__ size_t state_off(int idx, int h_v, int h) {
@@ -994,7 +971,7 @@ __device__ __forceinline__ size_t state_off(int idx, int h_v, int h) {
 // the warm-up scan, the H chain (WANT_V) or the M chain (V = 0, S starts at I).
 template <typename IO, bool WANT_V>
 __device__ void scan_chunks(ChainSmem<Io<IO>::kExact>& sm, const Params& p, const SegLoc& loc, int h, int hq,
-                            int c_lo, int c_hi, f32x16 S[4]) {
+                            int c_lo, int c_hi, f32x4 S[8]) {
     constexpr bool EX = Io<IO>::kExact;
     const size_t ts_v = (size_t)p.h_v * DK;
     Chunk<IO> nxt;
@@ -1011,11 +988,11 @@ __device__ void scan_chunks(ChainSmem<Io<IO>::kExact>& sm, const Params& p, cons
             fetch_chunk<IO, false, WANT_V>(nxt, p, loc.tok0 + (size_t)cn * CH, min(CH, loc.len - cn * CH), h, hq,
                                            loc.chunk_base + cn);
         }
-        f32x16 Vp[2];
+        f32x4 Vp[4];
         {
             SplitS ss;
             split_state(S, ss);
-            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 32 * wave_id() + (lane_id() & 31);
+            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 16 * wave_id() + (lane_id() & 15);
             chain_vp<IO, WANT_V>(sm, ss, vcol, ts_v, nvalid, Vp);
         }
         chain_state<EX>(sm, S, Vp);
@@ -1029,9 +1006,9 @@ __device__ void scan_chunks(ChainSmem<Io<IO>::kExact>& sm, const Params& p, cons
 // Low-level chunk preparation, second half: W = (T diag(beta)) diag(e^gamma) K
 // and U = (T diag(beta)) V of every (chunk, value head), from T diag(beta)
 // (split) and gamma, beta, which k_prep left in the chunk's W_out and U_out
-// blocks. Wave w produces columns [32w, 32w + 32) of both.
+// blocks. Wave w produces columns [16w, 16w + 16) of both.
 template <typename IO>
-__global__ __launch_bounds__(NTHR) void k_wu(Params p) {
+__global__ __launch_bounds__(NTHR_CH) void k_wu(Params p) {
     constexpr bool EX = Io<IO>::kExact;
     __shared__ ChainSmem<EX> sm;
     const int h = blockIdx.y, hq = h / p.group;
@@ -1048,101 +1025,96 @@ __global__ __launch_bounds__(NTHR) void k_wu(Params p) {
         gl = r.gl;
     }
     __syncthreads();   // every read of T, gamma and beta is done before W and U overwrite them
-    const int lane = lane_id(), col = lane & 31, hh = lane >> 5, w = wave_id(), n = 32 * w + col;
+    const int lane = lane_id(), cc = lane & 15, g = lane >> 4, w = wave_id(), n = 16 * w + cc;
     const size_t ts_v = (size_t)p.h_v * DK, ts_k = (size_t)p.h_qk * DK;
     const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + n;
     const IO* kcol = static_cast<const IO*>(p.k) + tok0 * ts_k + (size_t)hq * DK + n;
-    f32x16 W[2] = {f32x16{}, f32x16{}}, U[2] = {f32x16{}, f32x16{}};
+    f32x4 W[4], U[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        // B operands: column n, tokens 16 ks + kperm(hh, e) (K scaled by e^gamma of the token)
-        const f32x4 eg0 = *reinterpret_cast<const f32x4*>(sm.eg + 16 * ks + 4 * hh);
-        const f32x4 eg1 = *reinterpret_cast<const f32x4*>(sm.eg + 16 * ks + 8 + 4 * hh);
-        // K and V at those tokens: exact bf16 from LDS, or fp32 from HBM
+    for (int rt = 0; rt < 4; ++rt) W[rt] = U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        // B operands: column n, tokens t0 + (0..3) and t1 + (0..3) (K scaled by e^gamma of the token)
+        const int t0 = 32 * s + 4 * g, t1 = t0 + 16;
         f32x4 k0, k1, v0, v1;
         if constexpr (EX) {
-            const bf16x8 kh = lds_op16(sm.kt_hi + trow(n) * LDKT + 16 * ks + 8 * hh);
-            const bf16x8 vh = lds_op16(sm.vt + trow(n) * LDKT + 16 * ks + 8 * hh);
+            const bf16x8 kh = lds_op16(sm.kt_hi + n * LDKT + ((32 * s + 8 * g) ^ tswz(n)));
+            const u32x2 va = *reinterpret_cast<const u32x2*>(sm.vt + n * LDKT + (t0 ^ tswz(n)));
+            const u32x2 vb = *reinterpret_cast<const u32x2*>(sm.vt + n * LDKT + (t1 ^ tswz(n)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 k0[e] = (float)kh[e];
                 k1[e] = (float)kh[4 + e];
-                v0[e] = (float)vh[e];
-                v1[e] = (float)vh[4 + e];
             }
+            v0 = f32x4{__uint_as_float(va[0] << 16), __uint_as_float(va[0] & 0xffff0000u),
+                       __uint_as_float(va[1] << 16), __uint_as_float(va[1] & 0xffff0000u)};
+            v1 = f32x4{__uint_as_float(vb[0] << 16), __uint_as_float(vb[0] & 0xffff0000u),
+                       __uint_as_float(vb[1] << 16), __uint_as_float(vb[1] & 0xffff0000u)};
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t0 = 16 * ks + 4 * hh + e, t1 = t0 + 8;
-                k0[e] = t0 < nvalid ? (float)kcol[(size_t)t0 * ts_k] : 0.f;
-                k1[e] = t1 < nvalid ? (float)kcol[(size_t)t1 * ts_k] : 0.f;
-                v0[e] = t0 < nvalid ? (float)vcol[(size_t)t0 * ts_v] : 0.f;
-                v1[e] = t1 < nvalid ? (float)vcol[(size_t)t1 * ts_v] : 0.f;
+                k0[e] = t0 + e < nvalid ? (float)kcol[(size_t)(t0 + e) * ts_k] : 0.f;
+                k1[e] = t1 + e < nvalid ? (float)kcol[(size_t)(t1 + e) * ts_k] : 0.f;
+                v0[e] = t0 + e < nvalid ? (float)vcol[(size_t)(t0 + e) * ts_v] : 0.f;
+                v1[e] = t1 + e < nvalid ? (float)vcol[(size_t)(t1 + e) * ts_v] : 0.f;
             }
         }
-        k0 *= eg0;
-        k1 *= eg1;
-        bf16x4 a0, a1, b0, b1;
+        k0 *= *reinterpret_cast<const f32x4*>(sm.eg + t0);
+        k1 *= *reinterpret_cast<const f32x4*>(sm.eg + t1);
         bf16x8 kbh, kbl, vbh, vbl;
-        split4(k0, a0, b0);
-        split4(k1, a1, b1);
-        kbh = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        kbl = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-        split4(v0, a0, b0);
-        split4(v1, a1, b1);
-        vbh = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        vbl = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        split8(k0, k1, kbh, kbl);
+        split8(v0, v1, vbh, vbl);
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            if (ti == 0 && ks >= 2) continue;
-            const bf16x8 th = lds_op16(sm.t + (32 * ti + col) * LDP + 16 * ks + 8 * hh);
-            const bf16x8 tl = lds_op16(sm.t + (CH + 32 * ti + col) * LDP + 16 * ks + 8 * hh);
-            W[ti] = mma32(th, kbh, W[ti]);
-            W[ti] = mma32(th, kbl, W[ti]);
-            W[ti] = mma32(tl, kbh, W[ti]);
-            U[ti] = mma32(th, vbh, U[ti]);
-            U[ti] = mma32(th, vbl, U[ti]);
-            U[ti] = mma32(tl, vbh, U[ti]);
+        for (int rt = 0; rt < 4; ++rt) {
+            if (s == 1 && rt < 2) continue;
+            const bf16x8 th = lds_op16(sm.t + (16 * rt + cc) * LDP + 32 * s + 8 * g);
+            const bf16x8 tl = lds_op16(sm.t + (CH + 16 * rt + cc) * LDP + 32 * s + 8 * g);
+            W[rt] = mma16k32(th, kbh, W[rt]);
+            W[rt] = mma16k32(th, kbl, W[rt]);
+            W[rt] = mma16k32(tl, kbh, W[rt]);
+            U[rt] = mma16k32(th, vbh, U[rt]);
+            U[rt] = mma16k32(th, vbl, U[rt]);
+            U[rt] = mma16k32(tl, vbh, U[rt]);
         }
     }
     const size_t base = ((size_t)blockIdx.x * p.h_v + h) * CH;
     if (w == 0) p.prep_gamma[base + lane] = gl;
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const size_t r = base + 32 * ti + acc_row(i, hh);
-            p.prep_W[r * DK + n] = W[ti][i];
-            p.prep_U[r * DK + n] = U[ti][i];
+        for (int e = 0; e < 4; ++e) {
+            const size_t r = base + 16 * rt + 4 * g + e;
+            p.prep_W[r * DK + n] = W[rt][e];
+            p.prep_U[r * DK + n] = U[rt][e];
         }
 }
 
 // The map M of a segment, written for the combine kernel: split into hi/lo
-// bf16 and laid out as that kernel's MFMA A operands, so that its loads are
-// contiguous and it does no splitting on its sequential path. Element
-// M[r][k] goes to ((((r / 32) * 8 + k / 16) * 2 + part) * 64 + lane) * 8 + e
+// bf16 and laid out as that kernel's MFMA A operands (32x32x16), so that its
+// loads are contiguous and it does no splitting on its sequential path.
+// Element M[r][k] goes to ((((r / 32) * 8 + k / 16) * 2 + part) * 64 + lane) * 8 + e
 // with lane = r % 32 + 32 h, k % 16 = kperm(h, e), part 0 = hi, 1 = lo
 // (64 KiB per map). The chunk loop's LDS serves as the staging buffer; the
 // caller's chain is finished (behind a barrier) when this starts.
-__device__ void store_m_operand(bf16* buf, const f32x16 S[4], bf16* dst) {
-    const int lane = lane_id(), col = lane & 31, h = lane >> 5, w = wave_id();
-    const int kk = col & 15, ks = 2 * w + (col >> 4);
-    const int hh = (kk >> 2) & 1, e = (kk & 3) | ((kk & 8) >> 1);
+__device__ void store_m_operand(bf16* buf, const f32x4 S[8], bf16* dst) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
+    // column k = 16 w + c: k step w, k % 16 = c
+    const int hh = (c >> 2) & 1, e = (c & 3) | ((c & 8) >> 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r2 = acc_row(i, h);   // row within the 32-row block t
-            const int idx = (((t * 8 + ks) * 2) * 64 + r2 + 32 * hh) * 8 + e;
+        for (int q = 0; q < 4; ++q) {
+            const int r = 16 * i + 4 * g + q;
+            const int idx = ((((r >> 5) * 8 + w) * 2) * 64 + (r & 31) + 32 * hh) * 8 + e;
             bf16 hi, lo;
-            split1(S[t][i], hi, lo);
+            split1(S[i][q], hi, lo);
             buf[idx] = hi;
             buf[idx + 64 * 8] = lo;
         }
     __syncthreads();
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int off = (threadIdx.x + NTHR * it) * 8;
+    for (int it = 0; it < 8; ++it) {
+        const int off = (threadIdx.x + NTHR_CH * it) * 8;
         *reinterpret_cast<u32x4*>(dst + off) = *reinterpret_cast<const u32x4*>(buf + off);
     }
 }
@@ -1150,7 +1122,7 @@ __device__ void store_m_operand(bf16* buf, const f32x16 S[4], bf16* dst) {
 // Warm-up or exact segment map for the boundary before segment s >= 1.
 // blockIdx.x = 2 * segment slot + part; part 0: warm-up state or H, part 1: M.
 template <typename IO>
-__global__ __launch_bounds__(NTHR) void k_cp_prep(Params p) {
+__global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
     __shared__ ChainSmem<Io<IO>::kExact> sm;
     const int slot = blockIdx.x >> 1, part = blockIdx.x & 1, h = blockIdx.y, hq = h / p.group;
     const SegLoc loc = locate_segment(p, slot);
@@ -1174,7 +1146,7 @@ __global__ __launch_bounds__(NTHR) void k_cp_prep(Params p) {
     } else {
         // chunk a - 1 - j (a full chunk: only a sequence's last chunk is short) -> red[j]
         const int wave = wave_id(), lane = lane_id();
-        for (int j = wave; j < p.w; j += 4) {
+        for (int j = wave; j < p.w; j += NW_CH) {
             float s = p.g[(loc.tok0 + (size_t)(a - 1 - j) * CH + lane) * (size_t)p.h_v + h];
 #pragma unroll
             for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
@@ -1200,7 +1172,7 @@ __global__ __launch_bounds__(NTHR) void k_cp_prep(Params p) {
     // the map of segment 0 is only applied to a nonzero initial state
     if (!warm && part == 1 && loc.s == 1 && !p.s_init) return;
 
-    f32x16 S[4];
+    f32x4 S[8];
     float* dst;
     if (warm) {
         const int c_lo = a - wq;
@@ -1378,13 +1350,18 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
 // The fused forward of one segment: per chunk the P tiles, the state chain and
 // the output.
 template <typename IO>
-__global__ __launch_bounds__(NTHR) void k_fwd(Params p) {
+__global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
     constexpr bool EX = Io<IO>::kExact;
     __shared__ ChainSmem<EX> sm;
-    const int h = blockIdx.y, hq = h / p.group, wave = wave_id();
+    const int h = blockIdx.y, hq = h / p.group;
     const SegLoc loc = locate_segment(p, blockIdx.x);
     if (loc.seq < 0) return;
-    f32x16 S[4];
+    // P's upper tiles inside the diagonal 32-blocks stay zero (the chunk loop
+    // writes the ten lower tiles only); the first barrier of the loop orders
+    // this before every read
+    for (int i = threadIdx.x; i < 2 * CH * LDP / 8; i += NTHR_CH)
+        *reinterpret_cast<u32x4*>(sm.p + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+    f32x4 S[8];
     if (loc.s == 0) {
         if (p.s_init) load_state(p.s_init + state_off(loc.seq, p.h_v, h), S);
         else zero_state(S);
@@ -1398,14 +1375,14 @@ __global__ __launch_bounds__(NTHR) void k_fwd(Params p) {
         fetch_chunk<IO, true, true>(nxt, p, loc.tok0 + (size_t)c0 * CH, min(CH, loc.len - c0 * CH), h, hq,
                                     loc.chunk_base + c0);
     if (c0 < c1) {   // (the scratch line exists whenever there is a chunk)
-        // the loop body ends with the output's eight stores after its loads; the
+        // the loop body ends with the output's four stores after its loads; the
         // same stores (to the scratch line) here make the loop's entry look
         // alike, so that the wait at its head covers the loads only
         IO* dst = reinterpret_cast<IO*>(p.sink + 32 * lane_id());
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if constexpr (EX) *reinterpret_cast<u32x2*>(dst + 8 * (i & 3)) = u32x2{0u, 0u};
-            else *reinterpret_cast<f32x4*>(dst + 8 * (i & 3)) = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (EX) *reinterpret_cast<u32x2*>(dst + 4 * i) = u32x2{0u, 0u};
+            else *reinterpret_cast<f32x4*>(dst + 4 * i) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     for (int c = c0; c < c1; ++c) {
@@ -1418,20 +1395,12 @@ __global__ __launch_bounds__(NTHR) void k_fwd(Params p) {
             fetch_chunk<IO, true, true>(nxt, p, loc.tok0 + (size_t)cn * CH, min(CH, loc.len - cn * CH), h, hq,
                                         loc.chunk_base + cn);
         }
-        // P tiles: three per wave, the last wave takes one and zeroes the two
-        // upper tiles inside the diagonal 32-blocks
-        if (wave < 3) {
-            gram_p<EX, 3>(sm, wave, 3, p.scale);
-        } else {
-            gram_p<EX, 1>(sm, 9, 1, p.scale);
-            zero_p_tile(sm.p, 0, 1);
-            zero_p_tile(sm.p, 2, 3);
-        }
-        f32x16 Vp[2], O[2];
+        gram_p<EX>(sm, p.scale);
+        f32x4 Vp[4], O[4];
         {
             SplitS ss;
             split_state(S, ss);
-            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 32 * wave + (lane_id() & 31);
+            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 16 * wave_id() + (lane_id() & 15);
             chain_vp<IO, true>(sm, ss, vcol, ts_v, nvalid, Vp);
             chain_qs<EX>(sm, ss, O);
         }
@@ -1489,14 +1458,14 @@ int launch_prep(const Params& p, int io, void* stream) {
 
 int launch_wu(const Params& p, int io, void* stream) {
     if (p.n_chunks <= 0) return 0;
-    const dim3 grid(p.n_chunks, p.h_v), block(NTHR);
+    const dim3 grid(p.n_chunks, p.h_v), block(NTHR_CH);
     if (io == kIoBf16) hipLaunchKernelGGL(k_wu<bf16>, grid, block, 0, (hipStream_t)stream, p);
     else hipLaunchKernelGGL(k_wu<float>, grid, block, 0, (hipStream_t)stream, p);
     return launched();
 }
 
 int launch_cp_prep(const Params& p, int io, void* stream) {
-    const dim3 grid(2 * p.n_segments, p.h_v), block(NTHR);
+    const dim3 grid(2 * p.n_segments, p.h_v), block(NTHR_CH);
     if (io == kIoBf16) hipLaunchKernelGGL(k_cp_prep<bf16>, grid, block, 0, (hipStream_t)stream, p);
     else hipLaunchKernelGGL(k_cp_prep<float>, grid, block, 0, (hipStream_t)stream, p);
     return launched();
@@ -1516,7 +1485,7 @@ int launch_debug_path(const Params& p, int32_t* path_out, void* stream) {
 }
 
 int launch_fwd(const Params& p, int io, void* stream) {
-    const dim3 grid(p.n_segments, p.h_v), block(NTHR);
+    const dim3 grid(p.n_segments, p.h_v), block(NTHR_CH);
     if (io == kIoBf16) hipLaunchKernelGGL(k_fwd<bf16>, grid, block, 0, (hipStream_t)stream, p);
     else hipLaunchKernelGGL(k_fwd<float>, grid, block, 0, (hipStream_t)stream, p);
     return launched();
