@@ -66,10 +66,14 @@ constexpr int DK = kDim;
 constexpr int NTHR = 256;      // k_prep, k_cp_combine: 4 waves
 constexpr int NTHR_CH = 512;   // chain kernels: 8 waves
 constexpr int NW_CH = NTHR_CH / 64;
-constexpr int LDQ = 136;   // row stride (elements) of [64][128] bf16 tiles
-constexpr int LDKT = 72;   // row stride of [128][64] bf16 tiles
-constexpr int LDF = 68;    // row stride of [64][64] fp32 tiles
-constexpr int LDP = 72;    // row stride of [64][64] bf16 tiles
+// Row strides of the LDS tiles. A 16x16x32 operand read has sixteen lanes on
+// sixteen rows at one 16-byte column (and four such column groups); on gfx950
+// such reads run without bank conflicts when the row stride is 32 bytes past
+// a multiple of 64 (measured), hence 288- and 160-byte rows.
+constexpr int LDQ = 144;   // row stride (elements) of [64][128] bf16 tiles
+constexpr int LDKT = 80;   // row stride of [128][64] bf16 tiles
+constexpr int LDF = 72;    // row stride of [64][64] fp32 tiles
+constexpr int LDP = 80;    // row stride of [64][64] bf16 tiles
 constexpr int kMaxFlags = kMaxSegsPerSeq;  // boundary flags the combine kernel keeps in LDS
 
 enum { kCpAuto = 0, kCpOff = 1, kCpExact = 2, kCpWarmup = 3 };
@@ -252,13 +256,21 @@ __device__ bool locate_chunk(const Params& p, int slot, int& seq, int& c, int& l
 }
 
 // Inclusive scan of g over the 64 lanes of a wave (lane = token of the chunk).
+// DPP steps: shifts by 1, 2, 4, 8 lanes within each row of 16 (lanes without a
+// source add 0), then lane 15 of a row added to the next row (rows 1 and 3),
+// then lane 31 added to rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float s) {
+    return s + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), CTRL, ROW_MASK,
+                                                                      0xf, true));
+}
 __device__ __forceinline__ float wave_scan(float s) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float o = __shfl_up(s, d, 64);
-        if (lane >= d) s += o;
-    }
+    s = dpp_add<0x111, 0xf>(s);   // row_shr:1
+    s = dpp_add<0x112, 0xf>(s);   // row_shr:2
+    s = dpp_add<0x114, 0xf>(s);   // row_shr:4
+    s = dpp_add<0x118, 0xf>(s);   // row_shr:8
+    s = dpp_add<0x142, 0xa>(s);   // row_bcast:15
+    s = dpp_add<0x143, 0xc>(s);   // row_bcast:31
     return s;
 }
 
@@ -340,78 +352,117 @@ __device__ void gram_a(PrepSmem<Io<IO>::kExact>& sm, const IO* krow0, size_t ts,
             }
         }
     }
+    // acc[t][r] = k_(j0 + r) . k_i. Off the diagonal the lane stores A[i][j0 .. j0 + 3]
+    // in row i; a diagonal tile is stored transposed (A[j0 + r][i] in row i, the
+    // column the substitution in inv_diag reads).
 #pragma unroll
     for (int t = 0; t < NJOB; ++t) {
-        const int i = 16 * bi[t] + n, j0 = 16 * bj[t] + 4 * g4;   // row i, columns j0 .. j0 + 3
+        const int i = 16 * bi[t] + n, j0 = 16 * bj[t] + 4 * g4;
         const float gi = sm.gam[i], bt = sm.beta[i];
         const f32x4 gj = *reinterpret_cast<const f32x4*>(sm.gam + j0);
         f32x4 v;
+        if (bi[t] == bj[t]) {
+            const f32x4 bj4 = *reinterpret_cast<const f32x4*>(sm.beta + j0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (i > j0 + r) ? bt * __expf(gi - gj[r]) * acc[t][r] : 0.f;
+            for (int r = 0; r < 4; ++r) v[r] = (j0 + r > i) ? bj4[r] * __expf(gj[r] - gi) * acc[t][r] : 0.f;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = bt * __expf(gi - gj[r]) * acc[t][r];
+        }
         *reinterpret_cast<f32x4*>(sm.a + i * LDF + j0) = v;
     }
 }
 
-// Diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution. Every
-// wave solves all four blocks (lane 16 b + j: block b, column j) and writes
-// them; the values are identical across waves, so each wave can read the
-// blocks back without waiting for the others.
+// Diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution, column
+// by column: lane 16 b + j solves column j of block b in registers; step m
+// fixes x_m and removes its share from the rows below, reading column m of
+// the block (gram_a stores the diagonal tiles transposed, so that column is
+// one LDS row, read as a broadcast). Every wave solves all four blocks and
+// writes them (identical values), so each can read the blocks back without
+// waiting for the others.
 template <bool EX>
 __device__ void inv_diag(PrepSmem<EX>& sm) {
     const int lane = lane_id(), b = 16 * (lane >> 4), j = lane & 15;
-    const float* A = sm.a + b * LDF + b;
-    float x[16];
+    float s[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float s = (i == j) ? 1.f : 0.f;
+    for (int i = 0; i < 16; ++i) s[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int m = 0; m < i; ++m) s = fmaf(-A[i * LDF + m], x[m], s);
-        x[i] = s;
+    for (int m = 0; m < 15; ++m) {
+        const float* col = sm.a + (b + m) * LDF + b;   // A[b + i][b + m] at col[i], i > m
+        f32x4 c4[4];
+#pragma unroll
+        for (int q = (m + 1) / 4; q < 4; ++q) c4[q] = *reinterpret_cast<const f32x4*>(col + 4 * q);
+#pragma unroll
+        for (int i = m + 1; i < 16; ++i) s[i] = fmaf(-c4[i / 4][i % 4], s[m], s[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.t[(b + i) * LDF + b + j] = x[i];
+    for (int i = 0; i < 16; ++i) sm.t[(b + i) * LDF + b + j] = s[i];
 }
 
-// Block column J of T below the diagonal: T_iJ = -X_i sum_{m=J}^{i-1} A_im T_mJ,
-// with 16x16x16 bf16 MFMAs on hi/lo operands (lane l: A row l % 16, k 4 (l/16)..;
-// B / C column l % 16, rows 4 (l/16)..). Zeros above the diagonal block.
-template <int J, bool EX>
-__device__ void inv_col(PrepSmem<EX>& sm) {
+// 16x16 block products on hi/lo bf16 operands (16x16x16 MFMA; lane l: A row
+// l % 16 with k 4 (l / 16) .. + 4; B and C column l % 16 with rows 4 (l / 16) .. + 4).
+// The A operand is the LDS block at (r0, c0) of an fp32 [64][LDF] matrix.
+__device__ __forceinline__ f32x4 mm_lds(const float* m, int r0, int c0, const f32x4& bv, f32x4 acc) {
     const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
-    f32x4 Tc[4];
+    const f32x4 av = *reinterpret_cast<const f32x4*>(m + (r0 + n) * LDF + c0 + 4 * g4);
+    bf16x4 ah, al, bh, bl;
+    split4(av, ah, al);
+    split4(bv, bh, bl);
+    acc = mma16(ah, bh, acc);
+    acc = mma16(ah, bl, acc);
+    return mma16(al, bh, acc);
+}
+// The LDS block at (r0, c0) in the C (B operand) layout.
+__device__ __forceinline__ f32x4 blk_c(const float* m, int r0, int c0) {
+    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
+    f32x4 v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Tc[J][r] = sm.t[(16 * J + 4 * g4 + r) * LDF + 16 * J + n];
+    for (int r = 0; r < 4; ++r) v[r] = m[(r0 + 4 * g4 + r) * LDF + c0 + n];
+    return v;
+}
+__device__ __forceinline__ void blk_store(float* m, int r0, int c0, const f32x4& v) {
+    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
 #pragma unroll
-    for (int i = J + 1; i < 4; ++i) {
-        f32x4 R = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = J; m < i; ++m) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(sm.a + (16 * i + n) * LDF + 16 * m + 4 * g4);
-            bf16x4 ah, al, bh, bl;
-            split4(a, ah, al);
-            split4(Tc[m], bh, bl);
-            R = mma16(ah, bh, R);
-            R = mma16(ah, bl, R);
-            R = mma16(al, bh, R);
-        }
-        const f32x4 xi = *reinterpret_cast<const f32x4*>(sm.t + (16 * i + n) * LDF + 16 * i + 4 * g4);
-        bf16x4 xh, xl, rh, rl;
-        split4(xi, xh, xl);
-        split4(R, rh, rl);
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
-        P = mma16(xh, rh, P);
-        P = mma16(xh, rl, P);
-        P = mma16(xl, rh, P);
-        Tc[i] = -P;
+    for (int r = 0; r < 4; ++r) m[(r0 + 4 * g4 + r) * LDF + c0 + n] = v[r];
+}
+
+// Blocks below the diagonal, from T_iJ = -T_ii sum_{m=J}^{i-1} A_im T_mJ, four
+// waves with one block of the lower-left quadrant each (block row i = 2 + w / 2,
+// column j = w % 2):
+//   T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (the waves that need them
+//   compute them, and write them),
+//   X_aj = sum_{m=j}^{1} A_am T_mj (a = 2, 3),  T_ij = -sum_{a=2}^{i} T_ia X_aj.
+// T_32 enters as an A operand, so its waves write it to LDS and read it back
+// (after a wave-local fence; both write identical values).
+template <bool EX>
+__device__ void inv_off(PrepSmem<EX>& sm) {
+    const int w = wave_id(), bi = 2 + (w >> 1), bj = w & 1;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 t10 = z;
+    if (bj == 0) {
+        t10 = -mm_lds(sm.t, 16, 16, mm_lds(sm.a, 16, 0, blk_c(sm.t, 0, 0), z), z);
+        if (w == 0) blk_store(sm.t, 16, 0, t10);
     }
-#pragma unroll
-    for (int i = 0; i < J; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = 0.f;
-#pragma unroll
-    for (int i = J + 1; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.t[(16 * i + 4 * g4 + r) * LDF + 16 * J + n] = Tc[i][r];
+    if (bi == 3) {
+        const f32x4 t32 = -mm_lds(sm.t, 48, 48, mm_lds(sm.a, 48, 32, blk_c(sm.t, 32, 32), z), z);
+        blk_store(sm.t, 48, 32, t32);
+    }
+    // X_2j and (for block row 3) X_3j
+    f32x4 x2, x3 = z;
+    if (bj == 0) {
+        const f32x4 t00 = blk_c(sm.t, 0, 0);
+        x2 = mm_lds(sm.a, 32, 16, t10, mm_lds(sm.a, 32, 0, t00, z));
+        if (bi == 3) x3 = mm_lds(sm.a, 48, 16, t10, mm_lds(sm.a, 48, 0, t00, z));
+    } else {
+        const f32x4 t11 = blk_c(sm.t, 16, 16);
+        x2 = mm_lds(sm.a, 32, 16, t11, z);
+        if (bi == 3) x3 = mm_lds(sm.a, 48, 16, t11, z);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    f32x4 r;
+    if (bi == 2) r = -mm_lds(sm.t, 32, 32, x2, z);
+    else r = -mm_lds(sm.t, 48, 48, x3, mm_lds(sm.t, 48, 32, x2, z));
+    blk_store(sm.t, 16 * bi, 16 * bj, r);
 }
 
 // Inputs of one chunk for k_prep, prefetched into registers: K rows (bf16;
@@ -443,9 +494,10 @@ __device__ __forceinline__ void prep_fetch(PrepIn<IO>& r, const Params& p, size_
     r.b = lane < nvalid ? b : 0.f;
 }
 
-// Grid (groups of p.prep_cpw consecutive chunk slots, value heads); each
-// workgroup walks its chunks, fetching the next chunk's inputs while it works
-// on the current one. Per (chunk slot, value head), block b = slot h_v + h:
+// Work items are (value head, chunk slot) pairs, item f = h n_chunks + slot;
+// workgroup b walks items [b prep_cpw, (b + 1) prep_cpw), fetching the next
+// item's inputs while it works on the current one (one round of about two
+// workgroups per CU, however the chunks and heads factor). Per (chunk slot, value head), block b = slot h_v + h:
 //   prep_T + b t_stride: T diag(beta) split into bf16 hi and lo, [part][row][k]
 //     (2 x 64 x 64), the k (column) axis in the kp order of the chain
 //     kernels' LDS operands (zeros above the diagonal);
@@ -454,16 +506,30 @@ template <typename IO>
 __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
     constexpr bool EX = Io<IO>::kExact;
     __shared__ PrepSmem<EX> sm;
-    const int h = blockIdx.y, hq = h / p.group, wave = wave_id(), lane = lane_id();
-    const int s0 = blockIdx.x * p.prep_cpw, s1 = min(s0 + p.prep_cpw, p.n_chunks);
+    const int wave = wave_id(), lane = lane_id();
+    const long long n_items = (long long)p.n_chunks * p.h_v;
+    const long long f0 = (long long)blockIdx.x * p.prep_cpw, f1 = min(f0 + (long long)p.prep_cpw, n_items);
     const size_t ts = (size_t)p.h_qk * DK;
-    int seq, c, len;
-    size_t tok_s;
-    if (s0 >= s1 || !locate_chunk(p, s0, seq, c, len, tok_s)) return;
-    size_t tok0 = tok_s + (size_t)c * CH;
-    int nvalid = min(CH, len - c * CH);
+    if (f0 >= f1) return;
+    // item f -> head, chunk slot and the slot's tokens
+    int h, slot, nvalid;
+    size_t tok0;
+    auto locate = [&](long long f) {
+        h = (int)(f / p.n_chunks);
+        slot = (int)(f - (long long)h * p.n_chunks);
+        int seq, c, len;
+        size_t tok_s;
+        locate_chunk(p, slot, seq, c, len, tok_s);   // slot < n_chunks: always found
+        tok0 = tok_s + (size_t)c * CH;
+        nvalid = min(CH, len - c * CH);
+    };
+    locate(f0);
+    // the blocks of T above the diagonal stay zero (the chunk loop writes the
+    // diagonal and lower blocks only); the loop's first barrier orders this
+    for (int i = threadIdx.x; i < CH * LDF / 4; i += NTHR)
+        reinterpret_cast<f32x4*>(sm.t)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     PrepIn<IO> nxt;
-    prep_fetch<IO>(nxt, p, tok0, nvalid, h, hq);
+    prep_fetch<IO>(nxt, p, tok0, nvalid, h, h / p.group);
     if (p.sink) {   // (null for the low-level entry, which has no workspace)
         // the loop body's stores (gamma, beta; T) come after its loads; the same
         // stores to the scratch line here make the loop's entry look alike, so
@@ -474,10 +540,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sk + 4 * i) = u32x4{0u, 0u, 0u, 0u};
     }
-    for (int slot = s0; slot < s1; ++slot) {
+    for (long long f = f0; f < f1; ++f) {
         const size_t tok_cur = tok0;
-        const int nv_cur = nvalid;
-        const IO* krow0 = static_cast<const IO*>(p.k) + tok_cur * ts + (size_t)hq * DK;
+        const int nv_cur = nvalid, h_cur = h, slot_cur = slot;
+        const IO* krow0 = static_cast<const IO*>(p.k) + tok_cur * ts + (size_t)(h_cur / p.group) * DK;
         if constexpr (EX) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -490,7 +556,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
             const float gam = wave_scan(nxt.g);
             sm.gam[lane] = gam;
             sm.beta[lane] = nxt.b;
-            float* gb = p.prep_GB + ((size_t)slot * p.h_v + h) * (size_t)p.gb_stride;
+            float* gb = p.prep_GB + ((size_t)slot_cur * p.h_v + h_cur) * (size_t)p.gb_stride;
             gb[lane] = gam;
             gb[CH + lane] = nxt.b;
         }
@@ -498,11 +564,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
         // always a prefetch (the last slot fetches itself again), so that every
         // iteration has the same memory operations and the compiler's waits on
         // them stay exact across the loop
-        if (locate_chunk(p, min(slot + 1, s1 - 1), seq, c, len, tok_s)) {
-            tok0 = tok_s + (size_t)c * CH;
-            nvalid = min(CH, len - c * CH);
-        }
-        prep_fetch<IO>(nxt, p, tok0, nvalid, h, hq);
+        locate(min(f + 1, f1 - 1));
+        prep_fetch<IO>(nxt, p, tok0, nvalid, h, h / p.group);
         // the ten tiles: three per wave, the last wave takes one
         if (wave < 3) gram_a<IO, 3>(sm, krow0, ts, nv_cur, wave, 3);
         else gram_a<IO, 1>(sm, krow0, ts, nv_cur, 9, 1);
@@ -523,12 +586,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
         inv_diag<EX>(sm);
         // the diagonal blocks this wave reads next are the ones it just wrote
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        switch (wave) {
-            case 0: inv_col<0, EX>(sm); break;
-            case 1: inv_col<1, EX>(sm); break;
-            case 2: inv_col<2, EX>(sm); break;
-            default: inv_col<3, EX>(sm); break;
-        }
+        inv_off<EX>(sm);
         __syncthreads();
         // (the next chunk's LDS writes touch k_rm and the gate arrays, whose
         // last reads come before the previous barrier; T is rewritten after two
@@ -537,7 +595,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
         // row t / 4 and the physical 8-element pieces 32 q + 8 a, q = (t / 2) % 2,
         // a = 2 (t % 2) + (0, 1); piece 32 q + 8 a holds logical columns
         // 32 q + 4 a + (0..3) and 32 q + 16 + 4 a + (0..3).
-        bf16* Tg = reinterpret_cast<bf16*>(p.prep_T + ((size_t)slot * p.h_v + h) * (size_t)p.t_stride);
+        bf16* Tg = reinterpret_cast<bf16*>(p.prep_T + ((size_t)slot_cur * p.h_v + h_cur) * (size_t)p.t_stride);
         {
             const int row = threadIdx.x >> 2, q = (threadIdx.x >> 1) & 1;
 #pragma unroll
@@ -579,11 +637,16 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
 
 template <bool EX>
 struct __attribute__((aligned(16))) ChainSmem {
+    // What the state update reads (K^T and its gate factors) comes in NB
+    // buffers: with two (bf16 inputs), the next chunk is staged while the
+    // current one finishes its state update, and a chunk takes two barriers
+    // instead of three. fp32 inputs need the LDS for the lo halves instead.
+    static constexpr int NB = EX ? 2 : 1;
     bf16 k_hi[CH * LDQ];                  // K token-major, d_k in kp order
     bf16 k_lo[EX ? 8 : CH * LDQ];
     bf16 q_hi[CH * LDQ];                  // Q token-major, d_k in kp order
     bf16 q_lo[EX ? 8 : CH * LDQ];
-    bf16 kt_hi[DK * LDKT];                // K^T: row d_k, tokens in kp order (chunks swizzled)
+    bf16 kt_hi[NB][DK * LDKT];            // K^T: row d_k, tokens in kp order (chunks swizzled)
     bf16 kt_lo[EX ? 8 : DK * LDKT];
     bf16 vt[EX ? DK * LDKT : 8];          // V^T: row d_v, tokens in order (chunks swizzled)
     bf16 t[2 * CH * LDP];                 // T diag(beta): hi rows, then lo rows; tokens in kp order
@@ -591,8 +654,9 @@ struct __attribute__((aligned(16))) ChainSmem {
     float gam[CH];                        // gamma
     float eg[CH];                         // exp(gamma)
     float egs[CH];                        // scale exp(gamma)
-    float egc[CH];                        // exp(gamma_C - gamma)
-    float red[8];                         // red[0] = exp(gamma_C); per-chunk gate sums
+    float egc[NB][CH];                    // exp(gamma_C - gamma)
+    float ec[NB];                         // exp(gamma_C)
+    float red[8];                         // per-chunk gate sums (boundary choice)
 };
 
 // One chunk's inputs in registers between the global loads and the LDS
@@ -657,7 +721,8 @@ __device__ __forceinline__ u32x2 pack_col4(const u32x2 (&a)[4], int e) {
 // consecutive tokens of a column per 8-byte store), V^T, Q, T and the gate
 // factors (tokens past the end of the sequence have g = beta = 0).
 template <typename IO, bool WANT_Q, bool WANT_V>
-__device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const Chunk<IO>& r, float scale) {
+__device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const Chunk<IO>& r, float scale,
+                                            int b) {
     constexpr bool EX = Io<IO>::kExact;
     const int t = threadIdx.x, lane = lane_id(), m = t >> 5, c4 = (t & 31) * 4;
     {   // every wave writes the same values (no branch in the chunk loop)
@@ -666,8 +731,8 @@ __device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const
         sm.gam[lane] = r.gl;
         sm.eg[lane] = es;
         sm.egs[lane] = es * scale;
-        sm.egc[lane] = __expf(gc - r.gl);
-        sm.red[0] = __expf(gc);
+        sm.egc[b][lane] = __expf(gc - r.gl);
+        sm.ec[b] = __expf(gc);
     }
     const int kc = kp(c4), tk = kp(4 * m) ^ tswz(c4), tv = (4 * m) ^ tswz(c4);
     if constexpr (EX) {
@@ -675,7 +740,7 @@ __device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const
         for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(sm.k_hi + (4 * m + j) * LDQ + kc) = r.k[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            *reinterpret_cast<u32x2*>(sm.kt_hi + (c4 + e) * LDKT + tk) = pack_col4(r.k, e);
+            *reinterpret_cast<u32x2*>(sm.kt_hi[b] + (c4 + e) * LDKT + tk) = pack_col4(r.k, e);
             if (WANT_V) *reinterpret_cast<u32x2*>(sm.vt + (c4 + e) * LDKT + tv) = pack_col4(r.v, e);
         }
         if (WANT_Q) {
@@ -695,7 +760,7 @@ __device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const
             const f32x4 x = {r.k[0][e], r.k[1][e], r.k[2][e], r.k[3][e]};
             bf16x4 hi, lo;
             split4(x, hi, lo);
-            *reinterpret_cast<bf16x4*>(sm.kt_hi + (c4 + e) * LDKT + tk) = hi;
+            *reinterpret_cast<bf16x4*>(sm.kt_hi[b] + (c4 + e) * LDKT + tk) = hi;
             *reinterpret_cast<bf16x4*>(sm.kt_lo + (c4 + e) * LDKT + tk) = lo;
         }
         if (WANT_Q) {
@@ -902,11 +967,11 @@ __device__ void chain_pv_out(const ChainSmem<Io<IO>::kExact>& sm, const f32x4 Vp
 
 // S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V' (Vp is scaled in place).
 template <bool EX>
-__device__ void chain_state(const ChainSmem<EX>& sm, f32x4 S[8], f32x4 Vp[4]) {
+__device__ void chain_state(const ChainSmem<EX>& sm, f32x4 S[8], f32x4 Vp[4], int b) {
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) Vp[rt] *= *reinterpret_cast<const f32x4*>(sm.egc + 16 * rt + 4 * g);
-    const float ec = sm.red[0];
+    for (int rt = 0; rt < 4; ++rt) Vp[rt] *= *reinterpret_cast<const f32x4*>(sm.egc[b] + 16 * rt + 4 * g);
+    const float ec = sm.ec[b];
 #pragma unroll
     for (int i = 0; i < 8; ++i) S[i] *= ec;
 #pragma unroll
@@ -917,7 +982,7 @@ __device__ void chain_state(const ChainSmem<EX>& sm, f32x4 S[8], f32x4 Vp[4]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int off = (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i));
-            kh[i] = lds_op16(sm.kt_hi + off);
+            kh[i] = lds_op16(sm.kt_hi[b] + off);
             if (!EX) kl[i] = lds_op16(sm.kt_lo + off);
         }
         // eight independent chains: each tile is touched once per pass
@@ -969,34 +1034,55 @@ __device__ __forceinline__ size_t state_off(int idx, int h_v, int h) {
 
 // Runs chunks [c_lo, c_hi) of sequence loc from the state S (no outputs):
 // the warm-up scan, the H chain (WANT_V) or the M chain (V = 0, S starts at I).
+// With two K^T buffers a chunk is: V' from the staged chunk | barrier | stage
+// the next chunk (other K^T buffer), fetch the one after, state update |
+// barrier. Every iteration issues the same loads (the last ones fetch the
+// last chunk again): see fetch_chunk.
 template <typename IO, bool WANT_V>
 __device__ void scan_chunks(ChainSmem<Io<IO>::kExact>& sm, const Params& p, const SegLoc& loc, int h, int hq,
                             int c_lo, int c_hi, f32x4 S[8]) {
     constexpr bool EX = Io<IO>::kExact;
+    constexpr bool DB = ChainSmem<EX>::NB == 2;
+    if (c_lo >= c_hi) return;
     const size_t ts_v = (size_t)p.h_v * DK;
     Chunk<IO> nxt;
-    if (c_lo < c_hi)
-        fetch_chunk<IO, false, WANT_V>(nxt, p, loc.tok0 + (size_t)c_lo * CH, min(CH, loc.len - c_lo * CH), h, hq,
-                                       loc.chunk_base + c_lo);
-    for (int c = c_lo; c < c_hi; ++c) {
+    auto fetch = [&](int c) {
+        c = min(c, c_hi - 1);
+        fetch_chunk<IO, false, WANT_V>(nxt, p, loc.tok0 + (size_t)c * CH, min(CH, loc.len - c * CH), h, hq,
+                                       loc.chunk_base + c);
+    };
+    auto chunk_vp = [&](int c, f32x4 Vp[4]) {
         const size_t tok0 = loc.tok0 + (size_t)c * CH;
-        const int nvalid = min(CH, loc.len - c * CH);
-        stage_chunk<IO, false, WANT_V>(sm, nxt, 1.f);
+        SplitS ss;
+        split_state(S, ss);
+        const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 16 * wave_id() + (lane_id() & 15);
+        chain_vp<IO, WANT_V>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp);
+    };
+    fetch(c_lo);
+    if constexpr (DB) {
+        stage_chunk<IO, false, WANT_V>(sm, nxt, 1.f, 0);
+        fetch(c_lo + 1);
         __syncthreads();
-        {   // always a prefetch (the last chunk fetches itself again): see fetch_chunk
-            const int cn = min(c + 1, c_hi - 1);
-            fetch_chunk<IO, false, WANT_V>(nxt, p, loc.tok0 + (size_t)cn * CH, min(CH, loc.len - cn * CH), h, hq,
-                                           loc.chunk_base + cn);
+        for (int c = c_lo; c < c_hi; ++c) {
+            const int b = (c - c_lo) & 1;
+            f32x4 Vp[4];
+            chunk_vp(c, Vp);
+            __syncthreads();
+            stage_chunk<IO, false, WANT_V>(sm, nxt, 1.f, b ^ 1);
+            fetch(c + 2);
+            chain_state<EX>(sm, S, Vp, b);
+            __syncthreads();
         }
-        f32x4 Vp[4];
-        {
-            SplitS ss;
-            split_state(S, ss);
-            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 16 * wave_id() + (lane_id() & 15);
-            chain_vp<IO, WANT_V>(sm, ss, vcol, ts_v, nvalid, Vp);
+    } else {
+        for (int c = c_lo; c < c_hi; ++c) {
+            stage_chunk<IO, false, WANT_V>(sm, nxt, 1.f, 0);
+            __syncthreads();
+            fetch(c + 1);
+            f32x4 Vp[4];
+            chunk_vp(c, Vp);
+            chain_state<EX>(sm, S, Vp, 0);
+            __syncthreads();
         }
-        chain_state<EX>(sm, S, Vp);
-        __syncthreads();
     }
 }
 
@@ -1021,7 +1107,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_wu(Params p) {
     {
         Chunk<IO> r;
         fetch_chunk<IO, false, true>(r, p, tok0, nvalid, h, hq, blockIdx.x);
-        stage_chunk<IO, false, true>(sm, r, 1.f);
+        stage_chunk<IO, false, true>(sm, r, 1.f, 0);
         gl = r.gl;
     }
     __syncthreads();   // every read of T, gamma and beta is done before W and U overwrite them
@@ -1038,7 +1124,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_wu(Params p) {
         const int t0 = 32 * s + 4 * g, t1 = t0 + 16;
         f32x4 k0, k1, v0, v1;
         if constexpr (EX) {
-            const bf16x8 kh = lds_op16(sm.kt_hi + n * LDKT + ((32 * s + 8 * g) ^ tswz(n)));
+            const bf16x8 kh = lds_op16(sm.kt_hi[0] + n * LDKT + ((32 * s + 8 * g) ^ tswz(n)));
             const u32x2 va = *reinterpret_cast<const u32x2*>(sm.vt + n * LDKT + (t0 ^ tswz(n)));
             const u32x2 vb = *reinterpret_cast<const u32x2*>(sm.vt + n * LDKT + (t1 ^ tswz(n)));
 #pragma unroll
@@ -1173,25 +1259,21 @@ __global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
     if (!warm && part == 1 && loc.s == 1 && !p.s_init) return;
 
     f32x4 S[8];
-    float* dst;
-    if (warm) {
-        const int c_lo = a - wq;
-        if (c_lo == 0 && p.s_init) load_state(p.s_init + state_off(loc.seq, p.h_v, h), S);
+    if (warm || part == 0) {
+        // the warm-up state (from the sequence's initial state where the window
+        // starts there), or H: the previous segment run from zero
+        const int c_lo = warm ? a - wq : a - p.L;
+        if (warm && c_lo == 0 && p.s_init) load_state(p.s_init + state_off(loc.seq, p.h_v, h), S);
         else zero_state(S);
         scan_chunks<IO, true>(sm, p, loc, h, hq, c_lo, a, S);
-        dst = p.seg_state + state_off(loc.seg_base + loc.s, p.h_v, h);
-    } else if (part == 0) {
-        zero_state(S);
-        scan_chunks<IO, true>(sm, p, loc, h, hq, a - p.L, a, S);
-        dst = p.seg_H + state_off(loc.seg_base + loc.s - 1, p.h_v, h);
+        store_state(warm ? p.seg_state + state_off(loc.seg_base + loc.s, p.h_v, h)
+                         : p.seg_H + state_off(loc.seg_base + loc.s - 1, p.h_v, h), S);
     } else {
         identity_state(S);
         scan_chunks<IO, false>(sm, p, loc, h, hq, a - p.L, a, S);
         store_m_operand(reinterpret_cast<bf16*>(&sm), S,
                         reinterpret_cast<bf16*>(p.seg_M + state_off(loc.seg_base + loc.s - 1, p.h_v, h)));
-        return;
     }
-    store_state(dst, S);
 }
 
 // Sequential composition of the exact segment maps for one (sequence, head,
@@ -1348,17 +1430,22 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
 }
 
 // The fused forward of one segment: per chunk the P tiles, the state chain and
-// the output.
+// the output. With two K^T buffers (bf16 inputs) a chunk is: P, V' and Q S
+// from the staged chunk | barrier | stage the next chunk, fetch the one
+// after, P V' and the output, state update | barrier. The two waves that share
+// a SIMD (w and w + 4) take the steps of each half in different orders, so
+// that one's MFMA runs tend to meet the other's VALU work.
 template <typename IO>
 __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
     constexpr bool EX = Io<IO>::kExact;
+    constexpr bool DB = ChainSmem<EX>::NB == 2;
     __shared__ ChainSmem<EX> sm;
-    const int h = blockIdx.y, hq = h / p.group;
+    const int h = blockIdx.y, hq = h / p.group, wave = wave_id();
     const SegLoc loc = locate_segment(p, blockIdx.x);
     if (loc.seq < 0) return;
     // P's upper tiles inside the diagonal 32-blocks stay zero (the chunk loop
-    // writes the ten lower tiles only); the first barrier of the loop orders
-    // this before every read
+    // writes the ten lower tiles only); the first barrier below orders this
+    // before every read
     for (int i = threadIdx.x; i < 2 * CH * LDP / 8; i += NTHR_CH)
         *reinterpret_cast<u32x4*>(sm.p + 8 * i) = u32x4{0u, 0u, 0u, 0u};
     f32x4 S[8];
@@ -1370,44 +1457,87 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
     }
     const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
     const size_t ts_v = (size_t)p.h_v * DK;
-    Chunk<IO> nxt;
-    if (c0 < c1)
-        fetch_chunk<IO, true, true>(nxt, p, loc.tok0 + (size_t)c0 * CH, min(CH, loc.len - c0 * CH), h, hq,
-                                    loc.chunk_base + c0);
-    if (c0 < c1) {   // (the scratch line exists whenever there is a chunk)
-        // the loop body ends with the output's four stores after its loads; the
-        // same stores (to the scratch line) here make the loop's entry look
-        // alike, so that the wait at its head covers the loads only
-        IO* dst = reinterpret_cast<IO*>(p.sink + 32 * lane_id());
+    if (c0 < c1) {
+        Chunk<IO> nxt;
+        auto fetch = [&](int c) {
+            c = min(c, c1 - 1);
+            fetch_chunk<IO, true, true>(nxt, p, loc.tok0 + (size_t)c * CH, min(CH, loc.len - c * CH), h, hq,
+                                        loc.chunk_base + c);
+        };
+        // the loop body's loads are followed by the output's four stores; the
+        // same stores (to the scratch line) after the loads before the loop
+        // make its entry look alike, so that the waits stay exact
+        auto sink_stores = [&]() {
+            IO* dst = reinterpret_cast<IO*>(p.sink + 32 * lane_id());
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (EX) *reinterpret_cast<u32x2*>(dst + 4 * i) = u32x2{0u, 0u};
-            else *reinterpret_cast<f32x4*>(dst + 4 * i) = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    for (int c = c0; c < c1; ++c) {
-        const size_t tok0 = loc.tok0 + (size_t)c * CH;
-        const int nvalid = min(CH, loc.len - c * CH);
-        stage_chunk<IO, true, true>(sm, nxt, p.scale);
-        __syncthreads();
-        {   // always a prefetch (the last chunk fetches itself again): see fetch_chunk
-            const int cn = min(c + 1, c1 - 1);
-            fetch_chunk<IO, true, true>(nxt, p, loc.tok0 + (size_t)cn * CH, min(CH, loc.len - cn * CH), h, hq,
-                                        loc.chunk_base + cn);
-        }
-        gram_p<EX>(sm, p.scale);
-        f32x4 Vp[4], O[4];
-        {
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (EX) *reinterpret_cast<u32x2*>(dst + 4 * i) = u32x2{0u, 0u};
+                else *reinterpret_cast<f32x4*>(dst + 4 * i) = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        };
+        // first half of chunk c: V' and the Q S part of the output (and P)
+        auto half1 = [&](int c, f32x4 Vp[4], f32x4 O[4], bool gram_first) {
+            const size_t tok0 = loc.tok0 + (size_t)c * CH;
+            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 16 * wave + (lane_id() & 15);
+            const int nvalid = min(CH, loc.len - c * CH);
             SplitS ss;
-            split_state(S, ss);
-            const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 16 * wave_id() + (lane_id() & 15);
-            chain_vp<IO, true>(sm, ss, vcol, ts_v, nvalid, Vp);
-            chain_qs<EX>(sm, ss, O);
+            if (gram_first) {
+                gram_p<EX>(sm, p.scale);
+                split_state(S, ss);
+                chain_qs<EX>(sm, ss, O);
+                chain_vp<IO, true>(sm, ss, vcol, ts_v, nvalid, Vp);
+            } else {
+                split_state(S, ss);
+                chain_vp<IO, true>(sm, ss, vcol, ts_v, nvalid, Vp);
+                chain_qs<EX>(sm, ss, O);
+                gram_p<EX>(sm, p.scale);
+            }
+        };
+        auto out_part = [&](int c, const f32x4 Vp[4], f32x4 O[4]) {
+            const size_t tok0 = loc.tok0 + (size_t)c * CH;
+            chain_pv_out<IO>(sm, Vp, O, static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK, ts_v,
+                             min(CH, loc.len - c * CH), p.sink);
+        };
+        fetch(c0);
+        if constexpr (DB) {
+            stage_chunk<IO, true, true>(sm, nxt, p.scale, 0);
+            fetch(c0 + 1);
+            sink_stores();
+            __syncthreads();
+            for (int c = c0; c < c1; ++c) {
+                const int b = (c - c0) & 1;
+                f32x4 Vp[4], O[4];
+                if (wave < 4) {
+                    half1(c, Vp, O, false);
+                    __syncthreads();
+                    stage_chunk<IO, true, true>(sm, nxt, p.scale, b ^ 1);
+                    fetch(c + 2);
+                    out_part(c, Vp, O);
+                    chain_state<EX>(sm, S, Vp, b);
+                } else {
+                    half1(c, Vp, O, true);
+                    __syncthreads();
+                    stage_chunk<IO, true, true>(sm, nxt, p.scale, b ^ 1);
+                    fetch(c + 2);
+                    out_part(c, Vp, O);
+                    chain_state<EX>(sm, S, Vp, b);
+                }
+                __syncthreads();
+            }
+        } else {
+            sink_stores();
+            for (int c = c0; c < c1; ++c) {
+                stage_chunk<IO, true, true>(sm, nxt, p.scale, 0);
+                __syncthreads();
+                fetch(c + 1);
+                f32x4 Vp[4], O[4];
+                half1(c, Vp, O, false);
+                __syncthreads();
+                out_part(c, Vp, O);
+                chain_state<EX>(sm, S, Vp, 0);
+                __syncthreads();
+            }
         }
-        __syncthreads();
-        chain_pv_out<IO>(sm, Vp, O, static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK, ts_v, nvalid, p.sink);
-        chain_state<EX>(sm, S, Vp);
-        __syncthreads();
     }
     if (loc.s == loc.P - 1 && p.s_final) store_state(p.s_final + state_off(loc.seq, p.h_v, h), S);
 }
@@ -1450,7 +1580,8 @@ static int launched() { return (int)hipGetLastError(); }
 
 int launch_prep(const Params& p, int io, void* stream) {
     if (p.n_chunks <= 0) return 0;
-    const dim3 grid((p.n_chunks + p.prep_cpw - 1) / p.prep_cpw, p.h_v), block(NTHR);
+    const long long items = (long long)p.n_chunks * p.h_v;
+    const dim3 grid((unsigned)((items + p.prep_cpw - 1) / p.prep_cpw)), block(NTHR);
     if (io == kIoBf16) hipLaunchKernelGGL(k_prep<bf16>, grid, block, 0, (hipStream_t)stream, p);
     else hipLaunchKernelGGL(k_prep<float>, grid, block, 0, (hipStream_t)stream, p);
     return launched();
