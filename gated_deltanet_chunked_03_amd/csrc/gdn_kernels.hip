@@ -1377,11 +1377,6 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
         const int warm = __builtin_amdgcn_readfirstlane(wflag[s]);   // uniform: a scalar branch
         const bool mm = !warm && (s > 1 || p.s_init);
         f32x16 acc = in.tile;
-        {
-            const float* src = tile_src(s + 2);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) in.tile[i] = src[(32 * w + acc_row(i, hh)) * DK + cglob];
-        }
         const bf16* mop = m_src(s + 2);
         // (the products run also where they are not applied -- a warm-up
         // boundary, or M_0 without an initial state -- and are then dropped:
@@ -1389,25 +1384,36 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
         const f32x16 base = acc;
         f32x16 hl = f32x16{}, lh = f32x16{};
         const bf16* Bp = sB[buf];
+        bf16x8 bh[8], bl[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 0) * 64 + lane) * 8);
-            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 1) * 64 + lane) * 8);
-            acc = mma32(in.ah[ks], bh, acc);
-            hl = mma32(in.ah[ks], bl, hl);
-            lh = mma32(in.al[ks], bh, lh);
+            bh[ks] = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 0) * 64 + lane) * 8);
+            bl[ks] = *reinterpret_cast<const bf16x8*>(Bp + ((ks * 2 + 1) * 64 + lane) * 8);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            acc = mma32(in.ah[ks], bh[ks], acc);
+            hl = mma32(in.ah[ks], bl[ks], hl);
+            lh = mma32(in.al[ks], bh[ks], lh);
             in.ah[ks] = *reinterpret_cast<const bf16x8*>(mop + (ks * 2 + 0) * 64 * 8);
             in.al[ks] = *reinterpret_cast<const bf16x8*>(mop + (ks * 2 + 1) * 64 * 8);
         }
-        // instruction order for the scheduler: the tile loads, then per k step
-        // two LDS reads, three MFMAs and the two loads that refill their operands
-        __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+        {
+            const float* src = tile_src(s + 2);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) in.tile[i] = src[(32 * w + acc_row(i, hh)) * DK + cglob];
+        }
+        // instruction order for the scheduler: all sixteen LDS reads of the B
+        // operands first (they arrive while the first products run), then per k
+        // step three MFMAs and the two loads that refill their operands, then
+        // the tile loads
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
         acc += hl + lh;
         if (!mm) acc = base;
         combine_split_out(sB[buf ^ 1], acc, w, lane);
@@ -1432,9 +1438,10 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
 // The fused forward of one segment: per chunk the P tiles, the state chain and
 // the output. With two K^T buffers (bf16 inputs) a chunk is: P, V' and Q S
 // from the staged chunk | barrier | stage the next chunk, fetch the one
-// after, P V' and the output, state update | barrier. The two waves that share
-// a SIMD (w and w + 4) take the steps of each half in different orders, so
-// that one's MFMA runs tend to meet the other's VALU work.
+// after, P V' and the output, state update | barrier. All waves take the
+// steps in the same order: the two waves of a SIMD then tend to reach their
+// VALU and their MFMA runs together, which issues faster than interleaving
+// (a 16x16x32 MFMA leaves little room for VALU work beside it).
 template <typename IO>
 __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
     constexpr bool EX = Io<IO>::kExact;
@@ -1476,22 +1483,14 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
             }
         };
         // first half of chunk c: V' and the Q S part of the output (and P)
-        auto half1 = [&](int c, f32x4 Vp[4], f32x4 O[4], bool gram_first) {
+        auto half1 = [&](int c, f32x4 Vp[4], f32x4 O[4]) {
             const size_t tok0 = loc.tok0 + (size_t)c * CH;
             const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 16 * wave + (lane_id() & 15);
-            const int nvalid = min(CH, loc.len - c * CH);
             SplitS ss;
-            if (gram_first) {
-                gram_p<EX>(sm, p.scale);
-                split_state(S, ss);
-                chain_qs<EX>(sm, ss, O);
-                chain_vp<IO, true>(sm, ss, vcol, ts_v, nvalid, Vp);
-            } else {
-                split_state(S, ss);
-                chain_vp<IO, true>(sm, ss, vcol, ts_v, nvalid, Vp);
-                chain_qs<EX>(sm, ss, O);
-                gram_p<EX>(sm, p.scale);
-            }
+            split_state(S, ss);
+            chain_vp<IO, true>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp);
+            chain_qs<EX>(sm, ss, O);
+            gram_p<EX>(sm, p.scale);
         };
         auto out_part = [&](int c, const f32x4 Vp[4], f32x4 O[4]) {
             const size_t tok0 = loc.tok0 + (size_t)c * CH;
@@ -1507,21 +1506,12 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
             for (int c = c0; c < c1; ++c) {
                 const int b = (c - c0) & 1;
                 f32x4 Vp[4], O[4];
-                if (wave < 4) {
-                    half1(c, Vp, O, false);
-                    __syncthreads();
-                    stage_chunk<IO, true, true>(sm, nxt, p.scale, b ^ 1);
-                    fetch(c + 2);
-                    out_part(c, Vp, O);
-                    chain_state<EX>(sm, S, Vp, b);
-                } else {
-                    half1(c, Vp, O, true);
-                    __syncthreads();
-                    stage_chunk<IO, true, true>(sm, nxt, p.scale, b ^ 1);
-                    fetch(c + 2);
-                    out_part(c, Vp, O);
-                    chain_state<EX>(sm, S, Vp, b);
-                }
+                half1(c, Vp, O);
+                __syncthreads();
+                stage_chunk<IO, true, true>(sm, nxt, p.scale, b ^ 1);
+                fetch(c + 2);
+                out_part(c, Vp, O);
+                chain_state<EX>(sm, S, Vp, b);
                 __syncthreads();
             }
         } else {
@@ -1531,7 +1521,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
                 __syncthreads();
                 fetch(c + 1);
                 f32x4 Vp[4], O[4];
-                half1(c, Vp, O, false);
+                half1(c, Vp, O);
                 __syncthreads();
                 out_part(c, Vp, O);
                 chain_state<EX>(sm, S, Vp, 0);
