@@ -1,13 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark: Gated DeltaNet chunked-prefill forward on one MI355X.
 
-One step = one call of the library's forward (cp_prep, cp_combine and the fused
-forward kernel) over one batch of seeded synthetic input already resident in
-HBM. Before every step a 1 GiB fill evicts the L2 caches and the 256 MB
-Infinity Cache (outside the measured interval); each step's GPU time comes
-from HIP events the library records on the call's stream around its own
-kernels. The default workload is the TP8-shaped prompt (B=1, T=32768, h_qk=2,
-h_v=8, d=128, chunk 64, bf16 inputs, 70 % fast-decay heads).
+One step = one call of the library's forward (k_prep, k_cp_prep, k_cp_combine
+and the fused forward kernel) over one batch of seeded synthetic input already
+resident in HBM. Before every step a 1 GiB fill evicts the L2 caches and the
+256 MB Infinity Cache (outside the measured interval); each step's GPU time
+comes from HIP events on the stream around the step's four eager launches.
+A second pass with events between the kernels gives the per-kernel split;
+with --graph the step is also replayed from a HIP graph of the same launches
+(each replay first checked bit for bit against the eager result) and timed.
+The default workload is the TP8-shaped prompt (B=1, T=32768, h_qk=2, h_v=8,
+d=128, chunk 64, bf16 inputs).
 
 Prints one JSON line. Besides the contract fields it carries:
   roofline      the forward kernel's algorithmic HBM bytes / its measured time
@@ -77,6 +80,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of sequence 0 the CPU oracle runs (0 = skip)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a HIP graph (reported, not the headline: "
+                         "on this stack the replay measured slower than eager launches)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (a kernel of known "
                          "traffic that scales the HBM byte counters of a profiled run)")
@@ -131,18 +137,65 @@ def main():
     print(f"[bench] warmup done, plan L={pl['L']} segments={pl['n_segments']}",
           file=sys.stderr, flush=True)
 
-    gdn.profile_enable(True)
-    per = {"prep": [], "cp_prep": [], "cp_combine": [], "fwd": [], "total": []}
+    def timed(run, n):
+        """GPU ms of n steps: HIP events on the stream around each step (the
+        cache flush before it stays outside the interval); one sync at the end,
+        so the host enqueues ahead of the GPU."""
+        marks = []
+        for _ in range(n):
+            if not args.no_flush:
+                flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            marks.append((a, b))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in marks]
+
+    # eager launches: the four kernels back to back on the stream
     torch.cuda.synchronize()
     t0 = time.time()
+    eager_ms = timed(step, args.steps)
+    wall = time.time() - t0
+
+    # the same four launches replayed from a HIP graph (no host launch gaps);
+    # every replay is checked against the eager result before it is timed
+    graph_ms, graph_ok = None, False
+    if args.graph:
+        step()
+        torch.cuda.synchronize()
+        o_ref, s_ref = out.clone(), fs.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph_ok = True
+        for _ in range(3):
+            out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            graph_ok &= bool(torch.equal(out, o_ref)) and bool(torch.equal(fs, s_ref))
+            step()   # eager work between replays
+            torch.cuda.synchronize()
+        if graph_ok:
+            graph_ms = timed(graph.replay, args.steps)
+        print(f"[bench] graph replays {'match' if graph_ok else 'DIFFER from'} the eager result",
+              file=sys.stderr, flush=True)
+
+    # per-kernel times (events between the kernels; eager, cold caches)
+    gdn.profile_enable(True)
+    per = {"prep": [], "cp_prep": [], "cp_combine": [], "fwd": [], "total": []}
     for _ in range(args.steps):
         if not args.no_flush:
             flush.zero_()
         step()
         for key, val in gdn.profile_read().items():
             per[key].append(val)
-    torch.cuda.synchronize()
-    wall = time.time() - t0
     # warm-cache figure (no flush), for reference
     warm = []
     for _ in range(max(3, args.steps // 2)):
@@ -152,7 +205,8 @@ def main():
     print(f"[bench] timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
 
     mean = {key: float(np.mean(vals)) for key, vals in per.items()}
-    ms = mean["total"]
+    eager = float(np.mean(eager_ms))
+    ms = eager
     tokens = B * T
     value = tokens / (ms * 1e-3)
     nbytes = algorithmic_bytes(B, T, h_qk, h_v, e_io=2 if inp.io_dtype == "bf16" else 4,
@@ -215,6 +269,9 @@ def main():
         "config": {"workload": workload, "B": B, "T": T, "h_qk": h_qk, "h_v": h_v, "d": 128,
                    "chunk": 64, "cp_mode": args.cp_mode, "seed": cfg["seed"]},
         "roofline": roofline, "cpu_baseline": cpu,
+        "launch": "eager",
+        "eager_ms_per_step": round(eager, 4),
+        "graph_ms_per_step": round(float(np.mean(graph_ms)), 4) if graph_ok else None,
         "kernels_ms": {key: round(val, 4) for key, val in mean.items()},
         "warm_cache_ms_per_step": round(float(np.mean(warm)), 4),
         "mfma": mfma, "parity": parity,
