@@ -34,10 +34,10 @@ METRIC = "GDN fwd ms & tokens/s at B=1,T=32768 per head config; % MFMA/HBM roofl
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc", "gdn_kernels.hip")
 # HBM bytes per k_fwd launch on the tp8 workload from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
-# scaled by a 512 MiB copy's counts (FETCH x 1.99979, WRITE x 1.0). Valid only for the kernel
+# scaled by a 512 MiB copy's counts (FETCH x 1.99987, WRITE x 1.0). Valid only for the kernel
 # source with this hash; any other source reports null.
-MEASURED_TRAFFIC = {"tp8": {"sha256": "6601b6ae7ed31c034c490bb89a59d6ac977de2b22ca0d82be09e2bdbcc451a2c",
-                            "read": 119585286, "write": 67633152}}
+MEASURED_TRAFFIC = {"tp8": {"sha256": "8b64767993696f3ed576791edb754f10195cbbb18e290f3de10731783e6d0c3b",
+                            "read": 185291631, "write": 67649536}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
