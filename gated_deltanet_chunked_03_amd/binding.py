@@ -41,7 +41,8 @@ class GdnPlanInfo(ctypes.Structure):
                 ("n_segments", ctypes.c_int32), ("P_max", ctypes.c_int32),
                 ("warmup_chunks", ctypes.c_int32), ("n_cu", ctypes.c_int32),
                 ("lambda_", ctypes.c_float), ("noise_floor", ctypes.c_float),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("combine_group", ctypes.c_int32),
+                ("combine_groups", ctypes.c_int32)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}

@@ -41,7 +41,9 @@ struct Plan {
     int n_chunks_total = 0, n_chunks_max = 0;
     int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0;
     float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
-    size_t off_sink = 0, off_T = 0, off_GB = 0, off_state = 0, off_M = 0, off_H = 0, off_warm = 0, ws_bytes = 0;
+    int comb_G = 0, comb_J = 0;   // grouped combine (0: one chain)
+    size_t off_sink = 0, off_T = 0, off_GB = 0, off_state = 0, off_M = 0, off_H = 0, off_warm = 0;
+    size_t off_GM = 0, off_GH = 0, ws_bytes = 0;
 };
 
 int n_chunks_of(int len) { return (len + gdn::kChunk - 1) / gdn::kChunk; }
@@ -186,6 +188,37 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
         P.off_M = off;     off = align_up(off + st_bytes, 256);
         P.off_H = off;     off = align_up(off + st_bytes, 256);
         P.off_warm = off;  off = align_up(off + (size_t)P.n_segments * d->h_v * sizeof(int32_t), 256);
+        // The combine chains the boundaries of a sequence, P - 1 steps in a row.
+        // Grouped (groups of G boundaries composed in parallel, then linked, then
+        // replayed in parallel) it takes about G + (J - 2) + (G - 1) steps, J =
+        // ceil((P - 1) / G), in three launches. Its composing steps read every
+        // map once per 32-column block (8 workgroups per group and exact head):
+        // with more of them than half the CUs those steps ran ~2.5x slower
+        // (measured), and a whole round more past the CUs. Only exact heads
+        // compose; which heads are exact is decided on the device from the gates,
+        // so the plan assumes the share the pages report (most heads forget fast:
+        // 30 % exact, at least one). Grouped when that estimate beats the single
+        // chain by more than the two extra launches (~4 steps).
+        const int nb = P.P_max - 1;
+        const long long heads = std::max(1LL, ((long long)P.n_seqs * d->h_v * 3 + 9) / 10);
+        double best = nb;
+        for (int G = 2; G < nb; ++G) {
+            const int J = (nb + G - 1) / G;
+            if (J < 2) break;
+            const long long wgs = 8LL * (J - 1) * heads, rounds = (wgs + P.n_cu - 1) / P.n_cu;
+            const double slow = 2 * wgs <= P.n_cu ? 1.0 : 2.5;
+            const double steps = slow * (G * rounds + G - 1) + std::max(J - 2, 0) + 4;
+            if (steps < best) {
+                best = steps;
+                P.comb_G = G;
+                P.comb_J = J;
+            }
+        }
+        if (P.comb_G) {
+            const size_t grp = (size_t)P.n_seqs * P.comb_J * d->h_v * kStateElems * sizeof(float);
+            P.off_GM = off; off = align_up(off + grp, 256);
+            P.off_GH = off; off = align_up(off + 2 * grp, 256);
+        }
     }
     P.ws_bytes = off;
     *pl = std::move(P);
@@ -223,6 +256,8 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
     p.h_v = d->h_v;
     p.group = d->h_v / d->h_qk;
     p.L = P.L;
+    p.comb_G = P.comb_G;
+    p.comb_J = P.comb_J;
     p.w = P.w;
     p.cp_mode = d->cp_mode;
     p.n_segments = P.n_segments;
@@ -273,6 +308,10 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
         p.seg_M = reinterpret_cast<float*>(w8 + P.off_M);
         p.seg_H = reinterpret_cast<float*>(w8 + P.off_H);
         p.warm = reinterpret_cast<int32_t*>(w8 + P.off_warm);
+        if (P.comb_G) {
+            p.seg_GM = reinterpret_cast<float*>(w8 + P.off_GM);
+            p.seg_GH = reinterpret_cast<float*>(w8 + P.off_GH);
+        }
     }
     const int io = d->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
     const hipStream_t hs = (hipStream_t)stream;
@@ -347,6 +386,8 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->lambda = P.lambda;
     out->noise_floor = P.eps;
     out->workspace_bytes = P.ws_bytes;
+    out->combine_group = P.comb_G;
+    out->combine_groups = P.comb_J;
     g_last_error.clear();
     return GDN_OK;
 }

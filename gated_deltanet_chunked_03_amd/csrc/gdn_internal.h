@@ -27,6 +27,10 @@ struct Params {
     float* seg_M;             // [n_segments][h_v][128][128] state map of segment s: S -> M S + H
     float* seg_H;
     int32_t* warm;            // [n_segments][h_v] 1 if the boundary before segment s warms up
+    float* seg_GM;            // [n_seqs][comb_J][h_v] a group's composed map CM (combine operands, 64 KiB)
+    float* seg_GH;            // [n_seqs][comb_J][h_v] its CH (128 x 128 fp32) and a scratch block of the same size
+    int32_t comb_G;           // boundaries per combine group; 0: one chain over all boundaries
+    int32_t comb_J;           // combine groups of the longest sequence
     float* prep_T;            // [n_chunks][h_v] blocks of t_stride floats: T split hi/lo (16 KiB) first
     int64_t t_stride;         // floats between consecutive T blocks (>= 64 * 64)
     float* prep_GB;           // [n_chunks][h_v] blocks of gb_stride floats: gamma (64), beta (64)

@@ -1276,17 +1276,31 @@ __global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
     }
 }
 
-// Sequential composition of the exact segment maps for one (sequence, head,
-// 32-column block): S0(s) = M_{s-1} S0(s-1) + H_{s-1}, or the warm-up state
-// where the boundary warmed up. Wave w computes rows [32w, 32w + 32).
-// Each step is one 128 x 32 x 128 product on hi/lo operands. M arrives split
-// and in A-operand order (contiguous loads, requested one step ahead); each
-// lane writes the split of its rows of the new S0 straight into the B-operand
-// slots of the next step (its accumulator rows are exactly that operand's k
-// values), so the sequential path has no operand shuffling; the three partial
-// products (hi hi, hi lo, lo hi) run as independent MFMA chains. The boundary
-// flags come from LDS (the planner keeps segments per sequence within
-// kMaxFlags), so no step waits on a global load to branch.
+// Chains over the segment boundaries of one (sequence, head, 32-column
+// block). Boundary s (1 <= s < P) maps S0(s - 1) to S0(s): an exact boundary
+// applies the previous segment's map, S0(s) = M_{s-1} S0(s-1) + H_{s-1} (M_0
+// only to a nonzero initial state); a warm-up boundary takes its warm-up
+// state. Wave w computes rows [32w, 32w + 32). Each step is one
+// 128 x 32 x 128 product on hi/lo operands. M arrives split and in A-operand
+// order (contiguous loads, requested two steps ahead); each lane writes the
+// split of its rows of the new state straight into the B-operand slots of the
+// next step (its accumulator rows are exactly that operand's k values), so the
+// sequential path has no operand shuffling. The boundary flags come from LDS
+// (the planner keeps segments per sequence within kMaxFlags), so no step
+// waits on a global load to branch.
+//
+// With many boundaries the chain runs in three launches over groups of G
+// consecutive boundaries (group j: boundaries [1 + jG, min(1 + (j+1) G, P))):
+//   kCombHead   group 0 as a chain from S0(0), writing its states; every later
+//               group composes its boundary maps, X <- F_s(X) from X = [I | 0]
+//               over 256 columns (eight 32-column blocks), into the affine map
+//               (CM_j, CH_j) of the whole group;
+//   kCombGroups the state at the end of each group from the end of the one
+//               before, S0 <- CM_j S0 + CH_j, j = 1 .. J - 2;
+//   kCombApply  every group j >= 1 as a chain from the state at the end of
+//               group j - 1, writing its states;
+// about 2G + P/G steps in sequence instead of P - 1. kCombAll is the single
+// chain (few boundaries).
 struct CombineIn {
     f32x16 tile;      // H_{s-1} or the warm-up state, this wave's rows
     bf16x8 ah[8], al[8];   // this lane's A operands of M_{s-1}
@@ -1304,10 +1318,28 @@ __device__ __forceinline__ void combine_split_out(bf16* sB, const f32x16& acc, i
     }
 }
 
+enum { kCombAll = 0, kCombHead = 1, kCombGroups = 2, kCombApply = 3 };
+
+template <int MODE>
 __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
-    __shared__ __attribute__((aligned(16))) bf16 sB[2][8 * 2 * 64 * 8];  // S0 block as split B operands
+    __shared__ __attribute__((aligned(16))) bf16 sB[2][8 * 2 * 64 * 8];  // the state block as split B operands
     __shared__ int wflag[kMaxFlags];
-    const int seq = blockIdx.x >> 2, cb = blockIdx.x & 3, h = blockIdx.y;
+    const int h = blockIdx.y;
+    int seq, j = 0, cb;   // cb: 32-column block (0..7 when composing: 0..3 the M part, 4..7 the H part)
+    if (MODE == kCombAll || MODE == kCombGroups) {
+        seq = blockIdx.x >> 2;
+        cb = blockIdx.x & 3;
+    } else if (MODE == kCombHead) {
+        seq = blockIdx.x / (8 * p.comb_J);
+        const int r = blockIdx.x - seq * 8 * p.comb_J;
+        j = r >> 3;
+        cb = r & 7;
+    } else {
+        seq = blockIdx.x / (4 * (p.comb_J - 1));
+        const int r = blockIdx.x - seq * 4 * (p.comb_J - 1);
+        j = 1 + (r >> 2);
+        cb = r & 3;
+    }
     if (seq >= p.n_seqs) return;
     int P, seg_base;
     if (!p.cu) {
@@ -1319,43 +1351,77 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
         P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
     }
     if (P <= 1 || P > kMaxFlags) return;
+    const int G = p.comb_G, J = (MODE == kCombAll) ? 1 : (P - 1 + G - 1) / G;
+    const bool compose = MODE == kCombHead && j > 0;
+    if ((MODE == kCombHead || MODE == kCombApply) && j >= J) return;
+    if (MODE == kCombHead && j == 0 && cb >= 4) return;
+    if (MODE == kCombGroups && J < 3) return;
     int n_exact = 0;
     for (int s = 1 + (int)threadIdx.x; s < P; s += NTHR) {
         const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h];
         wflag[s] = f;
         n_exact += (f == 0);
     }
-    if (!__syncthreads_or(n_exact)) return;
+    if (!__syncthreads_or(n_exact)) return;   // every boundary warmed up: nothing to chain
+    // the steps: boundaries [s_lo, s_hi), or groups [1, J - 1) for kCombGroups
+    int s_lo = 1, s_hi = P;
+    if (MODE == kCombHead || MODE == kCombApply) {
+        s_lo = 1 + j * G;
+        s_hi = min(1 + (j + 1) * G, P);
+        // a group's last state (but the last group's) comes from kCombGroups,
+        // and the next group's kCombApply reads it: kCombApply leaves it alone
+        if (MODE == kCombApply && j < J - 1) s_hi -= 1;
+    } else if (MODE == kCombGroups) {
+        s_hi = J - 1;
+    }
 
     const int lane = lane_id(), col = lane & 31, hh = lane >> 5, w = wave_id();
-    const int cglob = 32 * cb + col;
+    const int cglob = 32 * (cb & 3) + col;
+    const size_t grp_base = ((size_t)seq * p.comb_J) * p.h_v + h;   // + j * h_v: group j's block
     {
         f32x16 acc;
-        if (p.s_init) {
-            const float* S0 = p.s_init + state_off(seq, p.h_v, h);
+        const float* S0 = nullptr;
+        if (MODE == kCombAll || (MODE == kCombHead && j == 0)) {
+            if (p.s_init) S0 = p.s_init + state_off(seq, p.h_v, h);
+        } else if (MODE == kCombGroups) {
+            S0 = p.seg_state + state_off(seg_base + G, p.h_v, h);          // end of group 0
+        } else if (MODE == kCombApply) {
+            S0 = p.seg_state + state_off(seg_base + j * G, p.h_v, h);      // end of group j - 1
+        }
+        if (S0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = S0[(32 * w + acc_row(i, hh)) * DK + cglob];
         } else {
-            acc = f32x16{};
+#pragma unroll
+            for (int i = 0; i < 16; ++i)   // composing: [I | 0]; else a zero initial state
+                acc[i] = (compose && cb < 4 && 32 * w + acc_row(i, hh) == cglob) ? 1.f : 0.f;
         }
         combine_split_out(sB[0], acc, w, lane);
     }
-    // Operands of step s1 (boundary s1): the warm-up state or H_{s1-1}, and
-    // this lane's A operands of M_{s1-1}.
+    // Operands of step s1: the tile added (H_{s1-1}, the warm-up state, or CH_j)
+    // and this lane's A operands of the map (M_{s1-1} or CM_j).
     // (every step issues the same loads and stores: a step past the end loads
-    // the last one again, M is loaded whether or not the step applies it, and
-    // the state is stored back also where it is a warm-up state; then the
+    // the last one again, the map is loaded whether or not the step applies it,
+    // and the state is stored back also where it is a warm-up state; then the
     // compiler's waits stay exact across the loop and the prefetch works)
-    auto tile_src = [&](int s1) {
-        s1 = min(s1, P - 1);
-        return __builtin_amdgcn_readfirstlane(wflag[s1]) ? p.seg_state + state_off(seg_base + s1, p.h_v, h)
-                                                          : p.seg_H + state_off(seg_base + s1 - 1, p.h_v, h);
+    auto warm_of = [&](int s1) {
+        return MODE == kCombGroups ? 0 : __builtin_amdgcn_readfirstlane(wflag[s1]);
+    };
+    auto tile_src = [&](int s1) -> const float* {
+        s1 = min(s1, s_hi - 1);
+        if (MODE == kCombGroups) return p.seg_GH + (grp_base + (size_t)s1 * p.h_v) * (2 * DK * DK);
+        return warm_of(s1) ? p.seg_state + state_off(seg_base + s1, p.h_v, h)
+                           : p.seg_H + state_off(seg_base + s1 - 1, p.h_v, h);
     };
     auto m_src = [&](int s1) {
-        s1 = min(s1, P - 1);
-        return reinterpret_cast<const bf16*>(p.seg_M + state_off(seg_base + s1 - 1, p.h_v, h)) +
-               (size_t)(w * 8 * 2 * 64 + lane) * 8;
+        s1 = min(s1, s_hi - 1);
+        const bf16* base = (MODE == kCombGroups)
+            ? reinterpret_cast<const bf16*>(p.seg_GM + (grp_base + (size_t)s1 * p.h_v) * (DK * DK))
+            : reinterpret_cast<const bf16*>(p.seg_M + state_off(seg_base + s1 - 1, p.h_v, h));
+        return base + (size_t)(w * 8 * 2 * 64 + lane) * 8;
     };
+    // the M part of a composition adds no tile
+    const float tscale = (compose && cb < 4) ? 0.f : 1.f;
     auto fetch = [&](int s1, CombineIn& in) {
         const float* src = tile_src(s1);
 #pragma unroll
@@ -1367,16 +1433,24 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
             in.al[ks] = *reinterpret_cast<const bf16x8*>(mop + (ks * 2 + 1) * 64 * 8);
         }
     };
+    // where step s1's state goes; composing, the group's CH block (its H part:
+    // the last step leaves CH there) or the scratch half beside it (M part)
+    auto dst_of = [&](int s1) -> float* {
+        if (MODE == kCombGroups) return p.seg_state + state_off(seg_base + (s1 + 1) * G, p.h_v, h);
+        if (compose) return p.seg_GH + (grp_base + (size_t)j * p.h_v) * (2 * DK * DK) + (cb < 4 ? DK * DK : 0);
+        return p.seg_state + state_off(seg_base + s1, p.h_v, h);
+    };
     // One step from the operands in `in`, which are refilled with those of
     // step s + 2 as they are consumed (each operand's load is issued right
     // after the MFMAs that read it, so the loads overlap the products): two
     // register sets alternate, and each step's loads have two steps to
     // arrive. The three partial products run as independent chains.
     int buf = 0;
+    f32x16 last;
     auto step = [&](int s, CombineIn& in) {
-        const int warm = __builtin_amdgcn_readfirstlane(wflag[s]);   // uniform: a scalar branch
-        const bool mm = !warm && (s > 1 || p.s_init);
-        f32x16 acc = in.tile;
+        const int warm = warm_of(s);   // uniform: a scalar branch
+        const bool mm = !warm && (s > 1 || p.s_init || MODE == kCombGroups);
+        f32x16 acc = in.tile * tscale;
         const bf16* mop = m_src(s + 2);
         // (the products run also where they are not applied -- a warm-up
         // boundary, or M_0 without an initial state -- and are then dropped:
@@ -1418,20 +1492,36 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
         if (!mm) acc = base;
         combine_split_out(sB[buf ^ 1], acc, w, lane);
         {
-            float* dst = p.seg_state + state_off(seg_base + s, p.h_v, h);
+            float* dst = dst_of(s);
 #pragma unroll
             for (int i = 0; i < 16; ++i) dst[(32 * w + acc_row(i, hh)) * DK + cglob] = acc[i];
         }
+        last = acc;
         __syncthreads();
         buf ^= 1;
     };
     CombineIn in0, in1;
-    fetch(1, in0);
-    fetch(2, in1);
+    fetch(s_lo, in0);
+    fetch(s_lo + 1, in1);
     __syncthreads();
-    for (int s = 1; s < P; s += 2) {
+    for (int s = s_lo; s < s_hi; s += 2) {
         step(s, in0);
-        if (s + 1 < P) step(s + 1, in1);
+        if (s + 1 < s_hi) step(s + 1, in1);
+    }
+    if (compose && cb < 4) {
+        // the group's CM: split and laid out as the A operands of kCombGroups
+        // (as k_cp_prep lays out M); columns 32 cb + col are k steps 2 cb, 2 cb + 1
+        bf16* dstm = reinterpret_cast<bf16*>(p.seg_GM + (grp_base + (size_t)j * p.h_v) * (DK * DK));
+        const int kk = col & 15, h2 = (kk >> 2) & 1, e = (kk & 3) | ((kk & 8) >> 1);
+        const int ks = 2 * cb + (col >> 4);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int idx = (((w * 8 + ks) * 2) * 64 + acc_row(i, hh) + 32 * h2) * 8 + e;
+            bf16 hi, lo;
+            split1(last[i], hi, lo);
+            dstm[idx] = hi;
+            dstm[idx + 64 * 8] = lo;
+        }
     }
 }
 
@@ -1593,9 +1683,24 @@ int launch_cp_prep(const Params& p, int io, void* stream) {
 }
 
 int launch_cp_combine(const Params& p, void* stream) {
-    const dim3 grid(4 * p.n_seqs, p.h_v), block(NTHR);
-    hipLaunchKernelGGL(k_cp_combine, grid, block, 0, (hipStream_t)stream, p);
-    return launched();
+    const dim3 block(NTHR);
+    const hipStream_t s = (hipStream_t)stream;
+    if (p.comb_G <= 0) {
+        hipLaunchKernelGGL(k_cp_combine<kCombAll>, dim3(4 * p.n_seqs, p.h_v), block, 0, s, p);
+        return launched();
+    }
+    hipLaunchKernelGGL(k_cp_combine<kCombHead>, dim3(8 * p.comb_J * p.n_seqs, p.h_v), block, 0, s, p);
+    int e = launched();
+    if (e) return e;
+    if (p.comb_J >= 3) {
+        hipLaunchKernelGGL(k_cp_combine<kCombGroups>, dim3(4 * p.n_seqs, p.h_v), block, 0, s, p);
+        if ((e = launched())) return e;
+    }
+    if (p.comb_J >= 2) {
+        hipLaunchKernelGGL(k_cp_combine<kCombApply>, dim3(4 * (p.comb_J - 1) * p.n_seqs, p.h_v), block, 0, s, p);
+        e = launched();
+    }
+    return e;
 }
 
 int launch_debug_path(const Params& p, int32_t* path_out, void* stream) {

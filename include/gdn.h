@@ -96,6 +96,8 @@ typedef struct {
     float lambda;
     float noise_floor;
     size_t workspace_bytes;  /* what gdn_fwd needs for this descriptor */
+    int32_t combine_group;   /* boundaries per group of the grouped combine (0: one chain) */
+    int32_t combine_groups;  /* groups of the longest sequence (0: one chain) */
 } gdn_plan_info;
 
 /* Plan a forward: chunk counts, segment length L and workspace size.
@@ -120,7 +122,9 @@ size_t gdn_fwd_workspace_bytes(const gdn_desc* desc);
  *                      T = (I + A)^-1 (16 KiB) and the chunk's gate sums and beta
  *                      (512 bytes) per (chunk, value head), and with a split the
  *                      segment states, the maps M and H (64 KiB per segment and
- *                      value head each) and the boundary flags
+ *                      value head each), the boundary flags and, with a grouped
+ *                      combine, each group's composed map (192 KiB per group and
+ *                      value head)
  *   stream             the hipStream_t to launch on (NULL = default stream)
  * All buffers stay owned by the caller and must stay valid until the stream
  * has run the launched kernels. Arguments are validated before any launch. */

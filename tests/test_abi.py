@@ -108,9 +108,30 @@ def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
     prep = p["n_chunks_total"] * h_v * (64 * 64 * 4 + 2 * 64 * 4) + 8192   # + the scratch line
     if p["cp_on"]:
         flags = -(-(p["n_segments"] * h_v * 4) // 256) * 256
-        assert p["workspace_bytes"] == prep + 3 * p["n_segments"] * per_seg + flags
+        # the grouped combine (the rule stated in gdn_api.cpp): G boundaries per group
+        # when slow (G rounds + G - 1) + (J - 2) + 4 steps beat the single chain of
+        # P - 1, J = ceil((P - 1) / G), assuming 30 % of the (sequence, head) pairs
+        # exact, 8 composing workgroups per group and exact head, slow = 2.5 past
+        # half the CUs
+        nb, best, G_exp = p["P_max"] - 1, float(p["P_max"] - 1), 0
+        heads = max(1, (B_ * h_v * 3 + 9) // 10)
+        for G in range(2, nb):
+            J = -(-nb // G)
+            if J < 2:
+                break
+            wgs = 8 * (J - 1) * heads
+            rounds = -(-wgs // 256)
+            slow = 1.0 if 2 * wgs <= 256 else 2.5
+            steps = slow * (G * rounds + G - 1) + max(J - 2, 0) + 4
+            if steps < best:
+                best, G_exp = steps, G
+        assert p["combine_group"] == G_exp
+        J_exp = -(-nb // G_exp) if G_exp else 0
+        assert p["combine_groups"] == J_exp
+        grp = 3 * B_ * J_exp * per_seg   # CM, CH and a scratch block per (sequence, group, head)
+        assert p["workspace_bytes"] == prep + 3 * p["n_segments"] * per_seg + flags + grp
     else:
-        assert p["workspace_bytes"] == prep
+        assert p["workspace_bytes"] == prep and p["combine_group"] == 0
 
 
 def test_plan_options_and_modes():

@@ -163,3 +163,38 @@ def test_empty_inputs_pass_the_state_through():
             o2, S2 = gdn.fwd(q, q, v, g, g, scale=0.1, cu_seqlens=cu, cp_mode=mode)
             torch.cuda.synchronize()
             assert o.numel() == 0 and torch.equal(S, S0) and torch.count_nonzero(S2) == 0
+
+
+@pytest.mark.parametrize("mode", ["exact", "auto"])
+def test_grouped_combine(mode):
+    """Enough segments that the planner composes the boundary maps in groups
+    (three launches: group maps, links between groups, replay inside groups):
+    two packed sequences of different lengths (so different group counts), an
+    initial state, a ragged tail, exact and warm-up boundaries. Every boundary
+    state against the oracle's state there; outputs at the stated tolerance."""
+    cu = [0, 64 * 129 + 37, 64 * 129 + 37 + 64 * 70 + 5]
+    inp = make_inputs(1, cu[-1], 2, 4, seed=61, gate="mixed", cu_seqlens=cu, init_std=0.05)
+    o, S, info = _run(inp, cp_mode=mode, n_cu=256, debug=True)
+    plan = info["plan"]
+    print(f"\n[grouped {mode}] plan L={plan['L']} P={plan['P_max']} G={plan['combine_group']} "
+          f"J={plan['combine_groups']}", flush=True)
+    assert plan["cp_on"] == 1 and plan["combine_group"] > 0 and plan["combine_groups"] >= 3
+    L = plan["L"]
+    o_ref, S_ref, snaps = oracle_run(inp, snap_stride=64 * L, n_snap=plan["P_max"])
+    assert_within_tolerance(_o_np(o, inp), o_ref)
+    assert_within_tolerance(S.cpu().numpy(), S_ref, "final_state", 1e-3, 1e-4)
+    seg = info["seg_state"].cpu().numpy()
+    path = info["path"].cpu().numpy()
+    base = 0
+    for n in range(inp.n_seqs):
+        n_ch = -(-(cu[n + 1] - cu[n]) // 64)
+        P = -(-n_ch // L)
+        for h, cls in enumerate(inp.head_class):
+            rel = [np.linalg.norm(seg[base + s, h] - snaps[n, h, s]) / np.linalg.norm(snaps[n, h, s])
+                   for s in range(1, P)]
+            print(f"  seq {n} head {h} ({cls}, path {path[n, h]}) boundary state rel err max {max(rel):.2e}")
+            if mode == "exact" or cls != "fast":
+                assert max(rel) < 1e-4, (n, h)
+            else:
+                assert max(rel) < 1e-3, (n, h)
+        base += P
