@@ -16,6 +16,8 @@ Prints one JSON line. Besides the contract fields it carries:
   roofline      the forward kernel's algorithmic HBM bytes / its measured time
   cpu_baseline  the fp64 CPU oracle timed on the host cores on a token prefix
   parity        GPU output vs that oracle on the same prefix
+  decode        the one-token recurrent decode (gdn_decode) over 256 rows at the TP8 head
+                counts: time per call, HBM roofline, outputs and states vs the oracle
 """
 from __future__ import annotations
 
@@ -33,11 +35,15 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN fwd ms & tokens/s at B=1,T=32768 per head config; % MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc", "gdn_kernels.hip")
-# HBM bytes per k_fwd launch on the tp8 workload from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
-# scaled by a 512 MiB copy's counts (FETCH x 1.99987, WRITE x 1.0). Valid only for the kernel
+# HBM bytes per k_fwd launch on the tp8 workload (and per k_decode launch on the 256-row decode)
+# from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
+# scaled by a 512 MiB copy's counts (FETCH x 1.99986, WRITE x 1.0). Valid only for the kernel
 # source with this hash; any other source reports null.
-MEASURED_TRAFFIC = {"tp8": {"sha256": "8b64767993696f3ed576791edb754f10195cbbb18e290f3de10731783e6d0c3b",
-                            "read": 185291631, "write": 67649536}}
+MEASURED_TRAFFIC = {"tp8": {"sha256": "8d8c7a0aa75c72d1e70f9e5f4ad0213d6cb32b28fa821aaf8c9dd9d9da178aec",
+                            "read": 185300817, "write": 67649536},
+                    # k_decode on the 256-row one-token decode, same passes and scale
+                    "decode256": {"sha256": "8d8c7a0aa75c72d1e70f9e5f4ad0213d6cb32b28fa821aaf8c9dd9d9da178aec",
+                                  "read": 135136290, "write": 134952064}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -57,6 +63,58 @@ def algorithmic_flops(B, T, h_qk, h_v, d=128, C=64):
     shared by the head group), 2 C^2 / 3 (64 x 64 triangular inverse)."""
     per = 6 * d * d + C * (d + 2 * d) + 2 * C * d * h_qk / h_v + 2 * C * C / 3
     return B * T * h_v * per
+
+
+def decode_bytes(rows, h_qk, h_v, d=128, e_io=2):
+    """What one decode call must move per row: its state read and written
+    (fp32 d x d per value head) plus one token's q, k, v, out, g and beta."""
+    return rows * (2 * h_v * d * d * 4 + 2 * h_qk * d * e_io + 2 * h_v * d * e_io + 8 * h_v)
+
+
+def measure_decode(args, gdn, torch, np, dev, flush, timed):
+    """One-token decode over args.decode_rows rows at the TP8 head counts
+    (h_qk = 2, h_v = 8, bf16 inputs, states drawn N(0, 0.1)): GPU time per
+    call (caches flushed before each), HBM roofline, and the outputs of one
+    call against the fp64 oracle."""
+    from gated_deltanet_chunked_03_amd.synth import make_inputs
+    rows, h_qk, h_v = args.decode_rows, 2, 8
+    di = make_inputs(name="decode", B=rows, T=1, h_qk=h_qk, h_v=h_v, seed=26, gate="mixed", init_std=0.1)
+    dv = lambda a, d=torch.float32: torch.from_numpy(a).to(device=dev, dtype=d)  # noqa: E731
+    dq, dk, dvv = dv(di.q, torch.bfloat16), dv(di.k, torch.bfloat16), dv(di.v, torch.bfloat16)
+    dg, db, ds = dv(di.g), dv(di.beta), dv(di.initial_state)
+    do = torch.empty_like(dvv)
+    dso = torch.empty_like(ds)
+
+    def call():
+        gdn.decode(dq, dk, dvv, dg, db, ds, scale=di.scale, out=do, state_out=dso)
+
+    for _ in range(20):
+        call()
+    times = timed(call, max(args.steps, 20))
+    us = float(np.mean(times)) * 1e3
+    nbytes = decode_bytes(rows, h_qk, h_v)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    from oracle import gdn_sequential
+    qf, kf, vf, gf, bf = di.flat()
+    o_ref, s_ref, _ = gdn_sequential(qf, kf, vf, gf, bf, di.scale, di.initial_state, di.flat_cu())
+    o_gpu = do.float().cpu().numpy().reshape(o_ref.shape).astype(np.float64)
+    s_gpu = dso.cpu().numpy().astype(np.float64)
+    err = lambda x, r: (float(np.abs(x - r).max() / np.abs(r).max()),  # noqa: E731
+                        float(np.abs(x - r).sum() / np.abs(r).sum()))
+    (omx, omean), (smx, smean) = err(o_gpu, o_ref), err(s_gpu, s_ref)
+    print(f"[bench] decode {rows} rows: {us:.2f} us/call, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    traffic = None
+    mt = MEASURED_TRAFFIC.get(f"decode{rows}")
+    if mt and hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest() == mt["sha256"]:
+        traffic = mt["read"] + mt["write"]
+    return {"workload": f"one-token decode: {rows} rows, h_qk={h_qk} h_v={h_v} d_k=d_v=128, bf16 "
+                        f"inputs, fp32 states N(0, 0.1), state read and written once per call",
+            "kernel": "k_decode", "us_per_call": round(us, 3),
+            "tokens_per_s": round(rows / (us * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "algorithmic_bytes": nbytes},
+            "parity": {"o_max_rel": omx, "o_mean_rel_l1": omean, "state_max_rel": smx,
+                       "state_mean_rel_l1": smean}}
 
 
 def cores_available():
@@ -83,6 +141,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a HIP graph (reported, not the headline: "
                          "on this stack the replay measured slower than eager launches)")
+    ap.add_argument("--decode-rows", type=int, default=256,
+                    help="rows (sequences) of the one-token decode measurement at the TP8 head "
+                         "counts (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (a kernel of known "
                          "traffic that scales the HBM byte counters of a profiled run)")
@@ -204,6 +265,10 @@ def main():
     gdn.profile_enable(False)
     print(f"[bench] timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
 
+    decode = None
+    if args.decode_rows > 0:
+        decode = measure_decode(args, gdn, torch, np, dev, flush, timed)
+
     mean = {key: float(np.mean(vals)) for key, vals in per.items()}
     eager = float(np.mean(eager_ms))
     ms = eager
@@ -274,7 +339,7 @@ def main():
         "graph_ms_per_step": round(float(np.mean(graph_ms)), 4) if graph_ok else None,
         "kernels_ms": {key: round(val, 4) for key, val in mean.items()},
         "warm_cache_ms_per_step": round(float(np.mean(warm)), 4),
-        "mfma": mfma, "parity": parity,
+        "mfma": mfma, "parity": parity, "decode": decode,
         "plan": {key: pl[key] for key in ("L", "n_segments", "P_max", "cp_on", "warmup_chunks",
                                           "n_cu", "lambda")},
         "precision": "bf16 MFMA operands, fp32 accumulation; non-input operands split hi+lo",

@@ -23,7 +23,7 @@ CP_MODES = {"auto": 0, "off": 1, "exact": 2, "warmup": 3}
 GDN_BF16, GDN_F32 = 0, 1
 
 EXPORTED = ["gdn_plan", "gdn_fwd_workspace_bytes", "gdn_fwd", "gdn_fwd_debug", "gdn_chunk_prep",
-            "gdn_profile_enable", "gdn_profile_read", "gdn_status_string", "gdn_last_error"]
+            "gdn_decode", "gdn_profile_enable", "gdn_profile_read", "gdn_status_string", "gdn_last_error"]
 
 
 class GdnDesc(ctypes.Structure):
@@ -86,6 +86,8 @@ def load_library(path: Optional[str] = None):
         lib.gdn_fwd_debug.restype = S
         lib.gdn_chunk_prep.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, P, P, P, P]
         lib.gdn_chunk_prep.restype = S
+        lib.gdn_decode.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, ctypes.c_float, P, P, P, P]
+        lib.gdn_decode.restype = S
         lib.gdn_profile_enable.argtypes = [ctypes.c_int]
         lib.gdn_profile_enable.restype = S
         lib.gdn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -264,6 +266,39 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     output_final_state, cu_seqlens) -> (o, final_state or None)."""
     return fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state,
                output_final_state=output_final_state, cu_seqlens=cu_seqlens)
+
+
+def decode(q, k, v, g, beta, state, scale=None, out=None, state_out=None, inplace=False):
+    """Recurrent decode continuing from ``state``: B rows of T tokens (T = 1
+    for one generated token each), same layouts as ``fwd``; state is
+    [B, h_v, 128, 128] fp32 or None (zeros). Returns (o, new_state); with
+    inplace=True the new state overwrites ``state``."""
+    torch = _torch()
+    B, T, h_qk, h_v, d_k, d_v, io, _, _ = _prepare(q, k, v, g, beta, None)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if state is not None:
+        _req(state, "state", torch.float32, dev, (B, h_v, d_k, d_v))
+    if inplace:
+        if state is None:
+            raise ValueError("inplace=True needs a state")
+        state_out = state
+    elif state_out is None:
+        state_out = torch.empty((B, h_v, d_k, d_v), dtype=torch.float32, device=dev)
+    else:
+        _req(state_out, "state_out", torch.float32, dev, (B, h_v, d_k, d_v))
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _req(out, "out", v.dtype, dev, tuple(v.shape))
+    desc, keep = make_desc(B, T, h_qk, h_v, d_k, d_v, io)
+    lib = load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    _check(lib, lib.gdn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               float(scale), _ptr(state), _ptr(state_out), _ptr(out), stream))
+    del keep
+    return out, state_out
 
 
 def chunk_prep(k, v, g, beta, cu_seqlens=None):

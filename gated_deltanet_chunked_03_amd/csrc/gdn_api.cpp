@@ -413,6 +413,43 @@ gdn_status gdn_fwd_debug(const gdn_desc* desc, const void* q, const void* k, con
                    workspace_bytes, stream, seg_state_out, path_out);
 }
 
+gdn_status gdn_decode(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, float scale, const float* state_in, float* state_out, void* out,
+                      void* stream) {
+    gdn_status st = validate_desc(desc);
+    if (st != GDN_OK) return st;
+    if (desc->host_cu_seqlens)
+        return fail(GDN_ERR_BAD_SHAPE, "decode takes B rows of T tokens; host_cu_seqlens must be NULL");
+    const bool any = (long long)desc->B * desc->T > 0;
+    if ((st = check_ptr(q, "q", any)) || (st = check_ptr(k, "k", any)) || (st = check_ptr(v, "v", any)) ||
+        (st = check_ptr(g, "g", any)) || (st = check_ptr(beta, "beta", any)) ||
+        (st = check_ptr(out, "out", any)) || (st = check_ptr(state_in, "state_in", false)) ||
+        (st = check_ptr(state_out, "state_out", false)))
+        return st;
+    if (!std::isfinite(scale)) return fail(GDN_ERR_BAD_SCALE, "scale is not finite");
+    if (state_in && state_out && state_in != state_out) {
+        // each workgroup reads its whole (sequence, head) block before writing
+        // it, so only the same pointer or disjoint buffers are safe
+        const size_t bytes = (size_t)desc->B * desc->h_v * gdn::kDim * gdn::kDim * sizeof(float);
+        const uintptr_t a = (uintptr_t)state_in, b = (uintptr_t)state_out;
+        if (a < b + bytes && b < a + bytes)
+            return fail(GDN_ERR_BAD_SHAPE, "state_in and state_out overlap without being the same buffer");
+    }
+    gdn::Params p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.s_init = state_in; p.s_final = state_out; p.out = out; p.scale = scale;
+    p.n_seqs = desc->B;
+    p.seq_len = desc->T;
+    p.h_qk = desc->h_qk;
+    p.h_v = desc->h_v;
+    p.group = desc->h_v / desc->h_qk;
+    const int io = desc->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
+    if (const int e = gdn::launch_decode(p, io, stream))
+        return fail(GDN_ERR_HIP, "decode launch: %s", hipGetErrorString((hipError_t)e));
+    g_last_error.clear();
+    return GDN_OK;
+}
+
 gdn_status gdn_chunk_prep(const gdn_desc* desc, const void* k, const void* v, const float* g,
                           const float* beta, const int32_t* cu_seqlens, float* gamma_out, float* W_out,
                           float* U_out, void* stream) {

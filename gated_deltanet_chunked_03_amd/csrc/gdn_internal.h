@@ -43,7 +43,7 @@ struct Params {
     float* prep_U;
     // sizes and options
     int32_t n_seqs;
-    int32_t seq_len;          // tokens per sequence when cu == null
+    int32_t seq_len;          // tokens per sequence when cu == null (decode: tokens per row)
     int32_t h_qk, h_v, group; // group = h_v / h_qk
     int32_t L;                // chunks per segment
     int32_t w;                // warm-up chunks
@@ -63,5 +63,6 @@ int launch_cp_prep(const Params& p, int io, void* stream);
 int launch_cp_combine(const Params& p, void* stream);
 int launch_fwd(const Params& p, int io, void* stream);
 int launch_debug_path(const Params& p, int32_t* path_out, void* stream);
+int launch_decode(const Params& p, int io, void* stream);
 
 }  // namespace gdn

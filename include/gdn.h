@@ -169,6 +169,32 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc,
                           const float* g, const float* beta, const int32_t* cu_seqlens,
                           float* gamma_out, float* W_out, float* U_out, void* stream);
 
+/* Recurrent decode: the gated delta rule of the section on optimising GDN
+ * chunked prefill applied token by token, continuing from a state a prefill
+ * (gdn_fwd's final_state) or an earlier decode call left, as generation does
+ * after the prompt (the pages' opening: edge-side agent inference, where a
+ * long prefill is followed by token-by-token output). Per token and value
+ * head: S <- exp(g) S + beta k (v - exp(g) S^T k)^T, o = scale S^T q, with the
+ * updated S. desc gives B rows (sequences) of T tokens each (T = 1 for one
+ * token; T = 0 only copies the state); desc->host_cu_seqlens must be NULL and
+ * the context-parallel options are ignored.
+ *   q, k, v, g, beta  device inputs in the gdn_fwd layouts with B rows of T tokens
+ *   scale             read-out scale
+ *   state_in          device [B, h_v, d_k, d_v] fp32 state before the first token,
+ *                     or NULL for zeros
+ *   state_out         device [B, h_v, d_k, d_v] fp32 state after the last token, or
+ *                     NULL to skip; may be the same pointer as state_in (updated in
+ *                     place) but must not overlap it otherwise
+ *   out               device output, layout and dtype of v
+ *   stream            the hipStream_t to launch on (NULL = default stream)
+ * One kernel launch, no workspace. Reads and writes each state once per call
+ * (the state stays in registers across the T tokens). Same ownership and
+ * error behaviour as gdn_fwd. */
+gdn_status gdn_decode(const gdn_desc* desc,
+                      const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, float scale,
+                      const float* state_in, float* state_out, void* out, void* stream);
+
 /* Measurement support. While enabled (on != 0), every gdn_fwd / gdn_fwd_debug
  * call records HIP events on its stream before its first launch and after
  * each of its kernels; gdn_profile_read then waits for the last call's events

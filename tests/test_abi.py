@@ -240,6 +240,33 @@ def test_chunk_prep_validation():
     assert B.STATUS_NAMES[st] == "GDN_ERR_NULL_ARG"
 
 
+def call_decode(d, q=0x1000, k=0x1000, v=0x1000, g=0x1000, beta=0x1000, scale=0.1, s_in=None, s_out=None,
+                out=0x1000):
+    l = lib()
+    P = ctypes.c_void_p
+    st = l.gdn_decode(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), scale, P(s_in) if s_in else None,
+                      P(s_out) if s_out else None, P(out), None)
+    return st, l.gdn_last_error().decode()
+
+
+def test_decode_validation():
+    """gdn_decode rejects bad descriptors and pointers before any launch."""
+    d, keep = desc(B=4, T=1, d_k=64, d_v=64)
+    assert B.STATUS_NAMES[call_decode(d)[0]] == "GDN_ERR_UNSUPPORTED_DIM"
+    d, keep = desc(T=20, cu_seqlens=[0, 10, 20])
+    st, msg = call_decode(d)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_BAD_SHAPE" and "cu_seqlens" in msg
+    d, keep = desc(B=4, T=1)
+    assert B.STATUS_NAMES[call_decode(d, q=0)[0]] == "GDN_ERR_NULL_ARG"
+    assert B.STATUS_NAMES[call_decode(d, out=0)[0]] == "GDN_ERR_NULL_ARG"
+    assert B.STATUS_NAMES[call_decode(d, v=0x1008)[0]] == "GDN_ERR_MISALIGNED"
+    assert B.STATUS_NAMES[call_decode(d, s_in=0x1004)[0]] == "GDN_ERR_MISALIGNED"
+    assert B.STATUS_NAMES[call_decode(d, scale=float("nan"))[0]] == "GDN_ERR_BAD_SCALE"
+    # states: the same buffer is allowed, a partial overlap is not
+    st, msg = call_decode(d, s_in=0x100000, s_out=0x100000 + 65536)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_BAD_SHAPE" and "overlap" in msg
+
+
 def test_profile_read_without_profiled_call():
     l = lib()
     ms = (ctypes.c_float * 5)()

@@ -1,0 +1,120 @@
+"""Recurrent decode (gdn_decode) against the fp64 sequential oracle.
+
+The decode step applies the same gated delta rule token by token to a state
+held in HBM, so the oracle is the sequential recurrence itself: the rows of a
+decode call are sequences of T tokens whose initial state is the given one.
+Cases: one token per row over a batch with random states (bf16 and fp32
+inputs), several tokens per row, a prefill by gdn_fwd continued by decode
+calls (compared with the oracle over the whole sequence), the in-place update,
+the zero state, T = 0, and the batch of 256 rows at the TP8 head counts that
+the benchmark times.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gated_deltanet_chunked_03_amd.synth import make_inputs
+from gpu_util import assert_within_tolerance, oracle_run, to_device
+
+pytestmark = pytest.mark.gpu
+
+STATE_TOL = 1e-5   # fp32 state arithmetic: max-rel and mean-rel bound on the new state
+
+
+def _decode(d, inp, **kw):
+    import gated_deltanet_chunked_03_amd as gdn
+    return gdn.decode(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], scale=inp.scale, **kw)
+
+
+def _check(inp, o, s, what):
+    import torch
+    torch.cuda.synchronize()
+    o_ref, s_ref, _ = oracle_run(inp)
+    o_ref = o_ref.reshape(inp.B, inp.T, inp.h_v, -1)
+    assert_within_tolerance(o.float().cpu().numpy(), o_ref, f"{what}: o")
+    assert_within_tolerance(s.cpu().numpy(), s_ref, f"{what}: state", STATE_TOL, STATE_TOL)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_one_token_batch(io):
+    inp = make_inputs(name="dec1", B=7, T=1, h_qk=2, h_v=8, io_dtype=io, seed=21, gate="mixed", init_std=0.1)
+    print(f"\n[decode/one/{io}] B={inp.B} h_v={inp.h_v}", flush=True)
+    o, s = _decode(to_device(inp), inp)
+    _check(inp, o, s, f"one token {io}")
+
+
+@pytest.mark.parametrize("gate", ["plain", "mixed"])
+def test_decode_several_tokens(gate):
+    inp = make_inputs(name="decT", B=3, T=9, h_qk=1, h_v=3, seed=22, gate=gate, init_std=0.1)
+    print(f"\n[decode/T9/{gate}]", flush=True)
+    o, s = _decode(to_device(inp), inp)
+    _check(inp, o, s, f"9 tokens {gate}")
+
+
+def test_prefill_then_decode_continues_the_recurrence():
+    """gdn_fwd over a prompt, then three decode calls of one token each: the
+    decode outputs and the last state equal the oracle over the whole sequence."""
+    import torch
+    import gated_deltanet_chunked_03_amd as gdn
+    T0, n_dec = 64 * 5 + 23, 3
+    inp = make_inputs(name="cont", B=1, T=T0 + n_dec, h_qk=2, h_v=4, seed=23, gate="mixed")
+    d = to_device(inp)
+    print(f"\n[decode/continue] prefill T={T0}, then {n_dec} tokens", flush=True)
+    pre = {k: d[k][:, :T0].contiguous() for k in ("q", "k", "v", "g", "beta")}
+    _, state = gdn.fwd(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], scale=inp.scale, cp_mode="off")
+    outs = []
+    for t in range(T0, T0 + n_dec):
+        tok = {k: d[k][:, t:t + 1].contiguous() for k in ("q", "k", "v", "g", "beta")}
+        o, state = gdn.decode(tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"], state, scale=inp.scale,
+                              inplace=True)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_ref, s_ref, _ = oracle_run(inp)
+    o_dec = torch.cat(outs, dim=1).float().cpu().numpy()[0]
+    assert_within_tolerance(o_dec, o_ref[T0:], "decoded outputs")
+    # the state went through the bf16-input chunked prefill first: its tolerance
+    # is the forward's final-state bound, not the fp32 decode's
+    assert_within_tolerance(state.cpu().numpy(), s_ref, "state after decode", 1e-3, 1e-4)
+
+
+def test_decode_in_place_equals_out_of_place():
+    import torch
+    inp = make_inputs(name="inpl", B=4, T=2, h_qk=2, h_v=4, seed=24, gate="mixed", init_std=0.1)
+    d = to_device(inp)
+    print("\n[decode/inplace]", flush=True)
+    o1, s1 = _decode(d, inp)
+    st = d["initial_state"].clone()
+    o2, s2 = _decode(dict(d, initial_state=st), inp, inplace=True)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == st.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_decode_zero_state_and_empty():
+    import torch
+    import gated_deltanet_chunked_03_amd as gdn
+    inp = make_inputs(name="zero", B=2, T=1, h_qk=1, h_v=2, seed=25)
+    d = to_device(inp)
+    print("\n[decode/zero+empty]", flush=True)
+    o, s = _decode(d, inp)      # initial_state is None: zeros
+    _check(inp, o, s, "zero state")
+    # T = 0: no token; the state is copied through
+    s0 = torch.randn((2, 2, 128, 128), dtype=torch.float32, device="cuda")
+    e = torch.empty((2, 0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty((2, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    eg = torch.empty((2, 0, 2), dtype=torch.float32, device="cuda")
+    o0, s1 = gdn.decode(e, e, ev, eg, eg, s0)
+    torch.cuda.synchronize()
+    assert o0.shape == ev.shape and torch.equal(s1, s0)
+
+
+def test_decode_benchmark_batch():
+    """The benchmark's decode workload: 256 rows of one token at the TP8 head
+    counts (h_qk = 2, h_v = 8), states drawn N(0, 0.1); every output and
+    state element against the oracle."""
+    inp = make_inputs(name="decbench", B=256, T=1, h_qk=2, h_v=8, seed=26, gate="mixed", init_std=0.1)
+    print("\n[decode/bench batch] B=256 h_v=8", flush=True)
+    o, s = _decode(to_device(inp), inp)
+    _check(inp, o, s, "bench batch")
+    assert np.isfinite(s.cpu().numpy()).all()
