@@ -23,7 +23,7 @@ CP_MODES = {"auto": 0, "off": 1, "exact": 2, "warmup": 3}
 GDN_BF16, GDN_F32 = 0, 1
 
 EXPORTED = ["gdn_plan", "gdn_fwd_workspace_bytes", "gdn_fwd", "gdn_fwd_debug", "gdn_chunk_prep",
-            "gdn_decode", "gdn_profile_enable", "gdn_profile_read", "gdn_status_string", "gdn_last_error"]
+            "gdn_decode", "gdn_bwd_workspace_bytes", "gdn_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_status_string", "gdn_last_error"]
 
 
 class GdnDesc(ctypes.Structure):
@@ -88,6 +88,11 @@ def load_library(path: Optional[str] = None):
         lib.gdn_chunk_prep.restype = S
         lib.gdn_decode.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, ctypes.c_float, P, P, P, P]
         lib.gdn_decode.restype = S
+        lib.gdn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(GdnDesc)]
+        lib.gdn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.gdn_bwd.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, ctypes.c_float, P, P, P, P,
+                                P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.gdn_bwd.restype = S
         lib.gdn_profile_enable.argtypes = [ctypes.c_int]
         lib.gdn_profile_enable.restype = S
         lib.gdn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -266,6 +271,48 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     output_final_state, cu_seqlens) -> (o, final_state or None)."""
     return fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state,
                output_final_state=output_final_state, cu_seqlens=cu_seqlens)
+
+
+def bwd(q, k, v, g, beta, d_out, scale=None, initial_state=None, d_final_state=None, cu_seqlens=None,
+        cp_mode="auto", lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0, workspace=None,
+        want_d_initial=True):
+    """Gradients of ``fwd`` (bf16 q, k, v): given d_out (like v) and optionally
+    d_final_state ([n_seqs, h_v, 128, 128] fp32), returns a dict with dq, dk
+    (like q), dv (like v), dg, dbeta (like g) and d_initial ([n_seqs, h_v, 128, 128]
+    fp32, or None when want_d_initial is False). The forward runs again inside,
+    with the same plan options as ``fwd``."""
+    torch = _torch()
+    B, T, h_qk, h_v, d_k, d_v, io, cu_dev, cu_host = _prepare(q, k, v, g, beta, cu_seqlens)
+    dev = q.device
+    if io != GDN_BF16:
+        raise ValueError("the backward takes bfloat16 q, k, v")
+    n_seqs = B if cu_host is None else len(cu_host) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    _req(d_out, "d_out", v.dtype, dev, tuple(v.shape))
+    sshape = (n_seqs, h_v, d_k, d_v)
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32, dev, sshape)
+    if d_final_state is not None:
+        _req(d_final_state, "d_final_state", torch.float32, dev, sshape)
+    desc, keep = make_desc(B, T, h_qk, h_v, d_k, d_v, io, cu_host, cp_mode, lam, warmup_chunks,
+                           noise_floor, n_cu)
+    lib = load_library()
+    plan_desc(desc)   # raises on an invalid descriptor
+    need = lib.gdn_bwd_workspace_bytes(ctypes.byref(desc))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+               d_initial=torch.empty(sshape, dtype=torch.float32, device=dev) if want_d_initial else None)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    _check(lib, lib.gdn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                            _ptr(initial_state), _ptr(cu_dev), _ptr(d_out), _ptr(d_final_state),
+                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                            _ptr(out["dbeta"]), _ptr(out["d_initial"]), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), stream))
+    del keep
+    return out
 
 
 def decode(q, k, v, g, beta, state, scale=None, out=None, state_out=None, inplace=False):

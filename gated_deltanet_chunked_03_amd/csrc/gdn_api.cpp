@@ -275,7 +275,7 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
 gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, float scale, const float* s_init, const int32_t* cu, void* out,
                    float* s_final, void* ws, size_t ws_bytes, void* stream, float* seg_out,
-                   int32_t* path_out) {
+                   int32_t* path_out, float* chunk_states = nullptr) {
     Plan P;
     gdn_status st = make_plan(d, &P);
     if (st != GDN_OK) return st;
@@ -328,7 +328,8 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
             return fail(GDN_ERR_HIP, "cp_combine launch: %s", hipGetErrorString((hipError_t)e));
         prof_mark(3, hs);
     }
-    if ((e = gdn::launch_fwd(p, io, stream)))
+    p.chunk_states = chunk_states;
+    if ((e = chunk_states ? gdn::launch_fwd_states(p, io, stream) : gdn::launch_fwd(p, io, stream)))
         return fail(GDN_ERR_HIP, "fwd launch: %s", hipGetErrorString((hipError_t)e));
     prof_mark(4, hs);
     if (g_prof.on) {
@@ -365,9 +366,96 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
     return GDN_OK;
 }
 
+// Workspace of the backward: the forward's (for its re-run), then the re-run's
+// output, the state entering every chunk, the gradient of the state leaving
+// every chunk, T / P / gamma per chunk and head, and the per-value-head parts
+// of dq and dk.
+struct BwdLayout {
+    size_t off_o = 0, off_cs = 0, off_ds = 0, off_tpg = 0, off_dq = 0, off_dk = 0, bytes = 0;
+    size_t tokens = 0;
+};
+
+BwdLayout bwd_layout(const gdn_desc* d, const Plan& P) {
+    BwdLayout L;
+    for (int n = 0; n < P.n_seqs; ++n) L.tokens += (size_t)P.len[n];
+    const size_t st = (size_t)P.n_chunks_total * d->h_v * kStateElems * sizeof(float);
+    size_t off = align_up(P.ws_bytes, 256);
+    L.off_o = off;   off = align_up(off + L.tokens * d->h_v * gdn::kDim * 2, 256);
+    L.off_cs = off;  off = align_up(off + st, 256);
+    L.off_ds = off;  off = align_up(off + st, 256);
+    L.off_tpg = off; off = align_up(off + (size_t)P.n_chunks_total * d->h_v * gdn::kBwdTpg * sizeof(float), 256);
+    L.off_dq = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
+    L.off_dk = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
+    L.bytes = off;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t gdn_bwd_workspace_bytes(const gdn_desc* desc) {
+    Plan P;
+    if (make_plan(desc, &P) != GDN_OK) return 0;
+    return bwd_layout(desc, P).bytes;
+}
+
+gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, float scale, const float* initial_state, const int32_t* cu_seqlens,
+                   const void* d_out, const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
+                   float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    Plan P;
+    gdn_status st = make_plan(desc, &P);
+    if (st != GDN_OK) return st;
+    if (desc->io_dtype != GDN_BF16)
+        return fail(GDN_ERR_BAD_DTYPE, "the backward takes bf16 q, k, v (io_dtype GDN_BF16)");
+    const bool varlen = desc->host_cu_seqlens != nullptr;
+    if (varlen && !cu_seqlens) return fail(GDN_ERR_NULL_ARG, "cu_seqlens is NULL but desc->host_cu_seqlens is set");
+    if (!varlen && cu_seqlens) return fail(GDN_ERR_NULL_ARG, "desc->host_cu_seqlens is required with cu_seqlens");
+    const bool any = (long long)desc->B * desc->T > 0;
+    if ((st = check_ptr(q, "q", any)) || (st = check_ptr(k, "k", any)) || (st = check_ptr(v, "v", any)) ||
+        (st = check_ptr(g, "g", any)) || (st = check_ptr(beta, "beta", any)) ||
+        (st = check_ptr(d_out, "d_out", any)) || (st = check_ptr(dq, "dq", any)) ||
+        (st = check_ptr(dk, "dk", any)) || (st = check_ptr(dv, "dv", any)) || (st = check_ptr(dg, "dg", any)) ||
+        (st = check_ptr(dbeta, "dbeta", any)) || (st = check_ptr(initial_state, "initial_state", false)) ||
+        (st = check_ptr(d_final_state, "d_final_state", false)) ||
+        (st = check_ptr(d_initial_state, "d_initial_state", false)) ||
+        (st = check_ptr(cu_seqlens, "cu_seqlens", false, 4)))
+        return st;
+    if (!std::isfinite(scale)) return fail(GDN_ERR_BAD_SCALE, "scale is not finite");
+    const BwdLayout L = bwd_layout(desc, P);
+    if (workspace_bytes < L.bytes)
+        return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", workspace_bytes, L.bytes);
+    if (L.bytes > 0 && (st = check_ptr(workspace, "workspace", true, 256))) return st;
+    char* w8 = static_cast<char*>(workspace);
+    // the forward again, keeping the state entering every chunk
+    if (P.n_chunks_total > 0) {
+        st = run_fwd(desc, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8 + L.off_o, nullptr, workspace,
+                     P.ws_bytes, stream, nullptr, nullptr, reinterpret_cast<float*>(w8 + L.off_cs));
+        if (st != GDN_OK) return st;
+    }
+    gdn::BwdParams b{};
+    b.q = q; b.k = k; b.v = v; b.g = g; b.beta = beta; b.dout = d_out; b.dfinal = d_final_state;
+    b.cu = cu_seqlens; b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dbeta = dbeta; b.dinit = d_initial_state;
+    b.cs = reinterpret_cast<const float*>(w8 + L.off_cs);
+    b.ds = reinterpret_cast<float*>(w8 + L.off_ds);
+    b.tpg = reinterpret_cast<float*>(w8 + L.off_tpg);
+    b.dq_part = reinterpret_cast<float*>(w8 + L.off_dq);
+    b.dk_part = reinterpret_cast<float*>(w8 + L.off_dk);
+    b.n_seqs = P.n_seqs;
+    b.seq_len = desc->T;
+    b.h_qk = desc->h_qk;
+    b.h_v = desc->h_v;
+    b.group = desc->h_v / desc->h_qk;
+    b.n_chunks = P.n_chunks_total;
+    b.scale = scale;
+    int e = gdn::launch_bwd(b, stream);
+    if (!e) e = gdn::launch_bwd_sum(b, (long long)L.tokens, stream);
+    if (e) return fail(GDN_ERR_HIP, "backward launch: %s", hipGetErrorString((hipError_t)e));
+    g_last_error.clear();
+    return GDN_OK;
+}
 
 gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     if (!out) return fail(GDN_ERR_NULL_ARG, "out is NULL");

@@ -37,6 +37,7 @@ struct Params {
     int64_t gb_stride;        // floats between consecutive gamma/beta blocks (>= 128)
     int32_t prep_cpw;         // (head, chunk) items per k_prep workgroup
     float* sink;              // 8 KiB scratch line for stores of rows past a sequence's end
+    float* chunk_states;      // [n_chunks][h_v][128][128] state entering each chunk (backward recompute)
     // low-level chunk-prep outputs
     float* prep_gamma;        // [n_chunks][h_v][64]
     float* prep_W;            // [n_chunks][h_v][64][128]
@@ -56,12 +57,45 @@ struct Params {
 
 enum IoType { kIoBf16 = 0, kIoF32 = 1 };
 
+// Backward pass (gdn_bwd.hip). Chunks are numbered sequence by sequence as in
+// the forward; states are [128][128] fp32 blocks in the API layout.
+constexpr int kBwdTpg = 2 * kChunk * kChunk + kChunk;   // floats per (chunk, head): T, P, gamma
+
+struct BwdParams {
+    const void* q;            // [tokens][h_qk][128] bf16
+    const void* k;
+    const void* v;            // [tokens][h_v][128] bf16
+    const float* g;           // [tokens][h_v]
+    const float* beta;
+    const void* dout;         // [tokens][h_v][128] bf16: loss gradient of the output
+    const float* dfinal;      // [n_seqs][h_v][128][128] loss gradient of the final state, or null
+    const int32_t* cu;        // [n_seqs + 1] or null (uniform sequences of seq_len)
+    void* dq;                 // [tokens][h_qk][128] bf16
+    void* dk;
+    void* dv;                 // [tokens][h_v][128] bf16
+    float* dg;                // [tokens][h_v]
+    float* dbeta;
+    float* dinit;             // [n_seqs][h_v][128][128] or null
+    // workspace
+    const float* cs;          // [n_chunks][h_v] state entering each chunk (from the forward)
+    float* ds;                // [n_chunks][h_v] loss gradient of the state leaving each chunk
+    float* tpg;               // [n_chunks][h_v] blocks of kBwdTpg floats: T, P (row-major 64 x 64), gamma
+    float* dq_part;           // [tokens][h_v][128] per-value-head parts of dq and dk
+    float* dk_part;
+    int32_t n_seqs, seq_len, h_qk, h_v, group, n_chunks;
+    float scale;
+};
+
+int launch_bwd(const BwdParams& p, void* stream);                       // prep, chain, chunk gradients
+int launch_bwd_sum(const BwdParams& p, long long n_tokens, void* stream);  // dq, dk group sums
+
 // Kernel launchers (gdn_kernels.hip). Return 0 or a hipError_t value.
 int launch_prep(const Params& p, int io, void* stream);
 int launch_wu(const Params& p, int io, void* stream);
 int launch_cp_prep(const Params& p, int io, void* stream);
 int launch_cp_combine(const Params& p, void* stream);
 int launch_fwd(const Params& p, int io, void* stream);
+int launch_fwd_states(const Params& p, int io, void* stream);
 int launch_debug_path(const Params& p, int32_t* path_out, void* stream);
 int launch_decode(const Params& p, int io, void* stream);
 

@@ -1532,7 +1532,9 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
 // steps in the same order: the two waves of a SIMD then tend to reach their
 // VALU and their MFMA runs together, which issues faster than interleaving
 // (a 16x16x32 MFMA leaves little room for VALU work beside it).
-template <typename IO>
+// With ST the kernel also writes the state entering every chunk (the
+// backward pass recomputes its chunk gradients from these).
+template <typename IO, bool ST>
 __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
     constexpr bool EX = Io<IO>::kExact;
     constexpr bool DB = ChainSmem<EX>::NB == 2;
@@ -1595,6 +1597,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
             __syncthreads();
             for (int c = c0; c < c1; ++c) {
                 const int b = (c - c0) & 1;
+                if constexpr (ST) store_state(p.chunk_states + state_off(loc.chunk_base + c, p.h_v, h), S);
                 f32x4 Vp[4], O[4];
                 half1(c, Vp, O);
                 __syncthreads();
@@ -1607,6 +1610,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
         } else {
             sink_stores();
             for (int c = c0; c < c1; ++c) {
+                if constexpr (ST) store_state(p.chunk_states + state_off(loc.chunk_base + c, p.h_v, h), S);
                 stage_chunk<IO, true, true>(sm, nxt, p.scale, 0);
                 __syncthreads();
                 fetch(c + 1);
@@ -1829,8 +1833,15 @@ int launch_debug_path(const Params& p, int32_t* path_out, void* stream) {
 
 int launch_fwd(const Params& p, int io, void* stream) {
     const dim3 grid(p.n_segments, p.h_v), block(NTHR_CH);
-    if (io == kIoBf16) hipLaunchKernelGGL(k_fwd<bf16>, grid, block, 0, (hipStream_t)stream, p);
-    else hipLaunchKernelGGL(k_fwd<float>, grid, block, 0, (hipStream_t)stream, p);
+    if (io == kIoBf16) hipLaunchKernelGGL((k_fwd<bf16, false>), grid, block, 0, (hipStream_t)stream, p);
+    else hipLaunchKernelGGL((k_fwd<float, false>), grid, block, 0, (hipStream_t)stream, p);
+    return launched();
+}
+
+int launch_fwd_states(const Params& p, int io, void* stream) {
+    const dim3 grid(p.n_segments, p.h_v), block(NTHR_CH);
+    if (io == kIoBf16) hipLaunchKernelGGL((k_fwd<bf16, true>), grid, block, 0, (hipStream_t)stream, p);
+    else hipLaunchKernelGGL((k_fwd<float, true>), grid, block, 0, (hipStream_t)stream, p);
     return launched();
 }
 

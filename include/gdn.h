@@ -169,6 +169,40 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc,
                           const float* g, const float* beta, const int32_t* cu_seqlens,
                           float* gamma_out, float* W_out, float* U_out, void* stream);
 
+/* Backward pass: the gradients of gdn_fwd's outputs with respect to its
+ * inputs (the FlashQLA pages' title promises a backward-friendly design; they
+ * print no backward formulas, so this is the exact gradient of the gated delta
+ * rule, evaluated on the chunked form). Given the loss gradient of the output
+ * and, optionally, of the final state, returns those of q, k, v, g, beta and,
+ * optionally, of the initial state. Internally the forward runs again (same
+ * plan, so with AutoCP the warm-up boundaries carry the same approximation as
+ * gdn_fwd), writing the state that enters every chunk; the state gradient is
+ * then scanned backwards over the chunks and every chunk's gradients are
+ * formed in parallel.
+ *   desc, q, k, v, g, beta, scale, initial_state, cu_seqlens   as for gdn_fwd;
+ *                      io_dtype must be GDN_BF16
+ *   d_out              device [B, T, h_v, d_v] bf16, loss gradient of the output
+ *   d_final_state      device [n_seqs, h_v, d_k, d_v] fp32, or NULL for zero
+ *   dq, dk             device [B, T, h_qk, d_k] bf16 (summed over the value heads
+ *                      that share a query/key head)
+ *   dv                 device [B, T, h_v, d_v] bf16
+ *   dg, dbeta          device [B, T, h_v] fp32
+ *   d_initial_state    device [n_seqs, h_v, d_k, d_v] fp32, or NULL to skip
+ *   workspace          device scratch of at least gdn_bwd_workspace_bytes(desc)
+ *                      bytes, 256-byte aligned (the forward's workspace, then per
+ *                      (chunk, value head) two 64 KiB states and 32.25 KiB of T, P
+ *                      and gamma, and per token and value head 1.25 KiB)
+ * Same ownership and error behaviour as gdn_fwd. */
+size_t gdn_bwd_workspace_bytes(const gdn_desc* desc);
+gdn_status gdn_bwd(const gdn_desc* desc,
+                   const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, float scale,
+                   const float* initial_state, const int32_t* cu_seqlens,
+                   const void* d_out, const float* d_final_state,
+                   void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                   float* d_initial_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Recurrent decode: the gated delta rule of the section on optimising GDN
  * chunked prefill applied token by token, continuing from a state a prefill
  * (gdn_fwd's final_state) or an earlier decode call left, as generation does

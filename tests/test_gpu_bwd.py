@@ -1,0 +1,90 @@
+"""Backward pass (gdn_bwd) against the fp64 backward oracle.
+
+The oracle is the gradient of the sequential recurrence (oracle/backward.py,
+pinned by finite differences); both sides see the same bf16-rounded inputs and
+the same loss gradients. Tolerances: the bf16 outputs dq, dk, dv take the
+forward's bound (max |x - x_ref| <= 1e-2 max |x_ref|, relative L1 <= 2e-3: bf16
+rounding of the result alone costs about 1.4e-3); the fp32 outputs dg, dbeta
+and the initial-state gradient carry only fp32 arithmetic and the forward
+re-run's state error (about 1e-5 relative), so they are held to max 1e-3 and
+relative L1 1e-4. With AutoCP warm-up boundaries the re-run's states differ
+from the exact ones by at most the noise floor (1e-4 relative), inside both.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gated_deltanet_chunked_03_amd.synth import make_inputs, round_bf16
+from gpu_util import assert_within_tolerance, to_device
+from oracle import gdn_sequential_bwd
+
+pytestmark = pytest.mark.gpu
+
+F32_MAX, F32_MEAN = 1e-3, 1e-4
+
+
+def _grads(seed, shape_o, n_seqs, h_v, with_final=True):
+    r = np.random.default_rng(seed)
+    d_out = round_bf16(r.standard_normal(shape_o)).astype(np.float32)
+    d_fin = (0.1 * r.standard_normal((n_seqs, h_v, 128, 128))).astype(np.float32) if with_final else None
+    return d_out, d_fin
+
+
+def _run(inp, d_out, d_fin, **kw):
+    import torch
+    import gated_deltanet_chunked_03_amd as gdn
+    d = to_device(inp)
+    dd = torch.from_numpy(d_out).to("cuda", torch.bfloat16)
+    df = None if d_fin is None else torch.from_numpy(d_fin).cuda()
+    cu = None if inp.cu_seqlens is None else [int(x) for x in inp.cu_seqlens]
+    res = gdn.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dd, scale=inp.scale,
+                  initial_state=d["initial_state"], d_final_state=df, cu_seqlens=cu, **kw)
+    torch.cuda.synchronize()
+    return {k: (None if x is None else x.float().cpu().numpy()) for k, x in res.items()}
+
+
+def _check(inp, d_out, d_fin, got, what):
+    q, k, v, g, b = inp.flat()
+    BT = inp.B * inp.T
+    ref = gdn_sequential_bwd(q, k, v, g, b, inp.scale, d_out.reshape(BT, inp.h_v, -1), inp.initial_state,
+                             d_fin, inp.flat_cu())
+    shape = lambda x, ref_x: x.reshape(ref_x.shape)  # noqa: E731
+    errs = {}
+    for key in ("dq", "dk", "dv"):
+        errs[key] = assert_within_tolerance(shape(got[key], ref[key]), ref[key], f"{what}: {key}")
+    for key in ("dg", "dbeta"):
+        errs[key] = assert_within_tolerance(shape(got[key], ref[key]), ref[key], f"{what}: {key}", F32_MAX, F32_MEAN)
+    if got["d_initial"] is not None:
+        errs["d_initial"] = assert_within_tolerance(got["d_initial"], ref["d_initial"], f"{what}: d_initial",
+                                                    F32_MAX, F32_MEAN)
+    print(f"[{what}] " + " ".join(f"{k} {m:.2e}/{a:.2e}" for k, (m, a) in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("mode", ["off", "exact"])
+def test_bwd_single_sequence(mode):
+    inp = make_inputs(name="bwd1", B=1, T=64 * 5 + 23, h_qk=2, h_v=4, seed=31, gate="mixed", init_std=0.1)
+    print(f"\n[bwd/single/{mode}] T={inp.T}", flush=True)
+    d_out, d_fin = _grads(131, inp.v.shape, 1, inp.h_v)
+    got = _run(inp, d_out, d_fin, cp_mode=mode, n_cu=8)
+    _check(inp, d_out, d_fin, got, f"single/{mode}")
+
+
+def test_bwd_batch_no_state_gradients():
+    inp = make_inputs(name="bwdB", B=3, T=150, h_qk=1, h_v=2, seed=32, gate="plain")
+    print("\n[bwd/batch] B=3 T=150, no initial state, no final-state gradient", flush=True)
+    d_out, _ = _grads(132, inp.v.shape, 3, inp.h_v, with_final=False)
+    got = _run(inp, d_out, None)
+    _check(inp, d_out, None, got, "batch")
+
+
+def test_bwd_varlen_auto_cp():
+    cu = [0, 64 * 9 + 5, 64 * 9 + 5, 64 * 9 + 5 + 64 * 20 + 40]   # includes an empty sequence
+    inp = make_inputs(name="bwdV", B=1, T=cu[-1], h_qk=2, h_v=4, seed=33, gate="mixed", init_std=0.1,
+                      cu_seqlens=cu)
+    print(f"\n[bwd/varlen] cu={cu}, AutoCP on 32 CUs", flush=True)
+    d_out, d_fin = _grads(133, inp.v.shape, 3, inp.h_v)
+    got = _run(inp, d_out, d_fin, cp_mode="auto", n_cu=32, lam=0.5, warmup_chunks=2)
+    _check(inp, d_out, d_fin, got, "varlen")
+    # the empty sequence passes its state gradient through
+    np.testing.assert_array_equal(got["d_initial"][1], d_fin[1])
