@@ -16,6 +16,8 @@ Prints one JSON line. Besides the contract fields it carries:
   roofline      the forward kernel's algorithmic HBM bytes / its measured time
   cpu_baseline  the fp64 CPU oracle timed on the host cores on a token prefix
   parity        GPU output vs that oracle on the same prefix
+  backward      the backward pass (gdn_bwd) on the same workload: time per call, bytes,
+                fp32 work per kernel, parity on a token prefix vs the fp64 backward oracle
   decode        the one-token recurrent decode (gdn_decode) over 256 rows at the TP8 head
                 counts: time per call, HBM roofline, outputs and states vs the oracle
 """
@@ -47,6 +49,7 @@ MEASURED_TRAFFIC = {"tp8": {"sha256": "8d8c7a0aa75c72d1e70f9e5f4ad0213d6cb32b28f
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector peak
 
 
 def algorithmic_bytes(B, T, h_qk, h_v, d=128, e_io=2, initial=False, final=True, n_seqs=None):
@@ -69,6 +72,81 @@ def decode_bytes(rows, h_qk, h_v, d=128, e_io=2):
     """What one decode call must move per row: its state read and written
     (fp32 d x d per value head) plus one token's q, k, v, out, g and beta."""
     return rows * (2 * h_v * d * d * 4 + 2 * h_qk * d * e_io + 2 * h_v * d * e_io + 8 * h_v)
+
+
+BWD_KERNEL_FLOPS = {
+    # fp32 multiply-adds x 2 that each backward kernel performs per (chunk, value head),
+    # counted from its loops (the implementation's own work, not a minimal count)
+    # chain, per 16-column block: K dSn, the triangular P^T dO and T^T dV', Q^T dO' and K^T dY'
+    "k_bwd_chain": 8 * 2 * (64 * 128 * 16 + 2 * (64 * 64 * 16 // 2) + 2 * 128 * 64 * 16),
+    # chunk: six [64 x 128 x 128] products with S or dSn, eleven [64 x 64 x 128]-sized ones
+    "k_bwd_chunk": 2 * (6 * 64 * 128 * 128 + 11 * 64 * 64 * 128),
+}
+
+
+def measure_backward(args, gdn, torch, np, dev, flush, inp, q, k, v, g, beta, s0):
+    """gdn_bwd on the benchmark workload: GPU time per call (caches flushed
+    before each), the HBM bytes it must move, and its fp32 work; parity of a
+    separate call on a token prefix of sequence 0 against the fp64 backward
+    oracle."""
+    import ctypes
+    B, T, h_qk, h_v = inp.B, inp.T, inp.h_qk, inp.h_v
+    n_seqs = inp.n_seqs
+    r = np.random.default_rng(77)
+    d_out = torch.from_numpy(r.standard_normal(inp.v.shape).astype(np.float32)).to(dev, torch.bfloat16)
+    d_fin = torch.from_numpy((0.1 * r.standard_normal((n_seqs, h_v, 128, 128))).astype(np.float32)).to(dev)
+    cu = None if inp.cu_seqlens is None else [int(x) for x in inp.cu_seqlens]
+    desc, keep = gdn.binding.make_desc(B, T, h_qk, h_v, cu_seqlens=cu)
+    need = gdn.load_library().gdn_bwd_workspace_bytes(ctypes.byref(desc))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def call():
+        return gdn.bwd(q, k, v, g, beta, d_out, scale=inp.scale, initial_state=s0, d_final_state=d_fin,
+                       cu_seqlens=cu, workspace=ws)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    marks = []
+    for _ in range(args.bwd_steps):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        marks.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
+    tokens = B * T
+    n_chunks = gdn.plan(B, T, h_qk, h_v, cu_seqlens=cu)["n_chunks_total"]
+    nbytes = tokens * (4 * h_qk * 128 * 2 + 3 * h_v * 128 * 2 + 16 * h_v) + \
+        ((s0 is not None) + 2) * n_seqs * h_v * 128 * 128 * 4
+    flops = {kname: f * n_chunks * h_v for kname, f in BWD_KERNEL_FLOPS.items()}
+    # parity on a prefix: the first 2048 tokens of sequence 0 as a sequence of their own
+    n_tok = min(2048, T if inp.cu_seqlens is None else int(inp.cu_seqlens[1]))
+    from oracle import gdn_sequential_bwd
+    pq, pk, pv = (x[:1, :n_tok].contiguous() for x in (q, k, v))
+    pg, pb, pdo = g[:1, :n_tok].contiguous(), beta[:1, :n_tok].contiguous(), d_out[:1, :n_tok].contiguous()
+    ps0 = None if s0 is None else s0[:1].contiguous()
+    res = gdn.bwd(pq, pk, pv, pg, pb, pdo, scale=inp.scale, initial_state=ps0, d_final_state=d_fin[:1].contiguous())
+    torch.cuda.synchronize()
+    f64 = lambda x: x[0].float().cpu().numpy().astype(np.float64)  # noqa: E731
+    ref = gdn_sequential_bwd(f64(pq), f64(pk), f64(pv), f64(pg), f64(pb), inp.scale, f64(pdo),
+                             None if ps0 is None else ps0.cpu().numpy(), d_fin[:1].cpu().numpy())
+    par = {}
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial"):
+        x = res[key].float().cpu().numpy().astype(np.float64).reshape(ref[key].shape)
+        d = np.abs(x - ref[key])
+        par[key] = [float(d.max() / np.abs(ref[key]).max()), float(d.sum() / np.abs(ref[key]).sum())]
+    print(f"[bench] backward {ms:.3f} ms", file=sys.stderr, flush=True)
+    del keep
+    return {"ms_per_call": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "algorithmic_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+            "fp32_gflop_per_kernel": {kname: round(f / 1e9, 2) for kname, f in flops.items()},
+            "fp32_peak_tflops": FP32_PEAK_TFLOPS,
+            "precision": "fp32 vector ALU arithmetic on bf16 inputs; forward re-run as in gdn_fwd",
+            "parity_prefix": {"tokens": n_tok, "max_rel_and_mean_rel_l1": par,
+                              "tol": {"dq,dk,dv": [1e-2, 2e-3], "dg,dbeta,d_initial": [1e-3, 1e-4]}}}
 
 
 def measure_decode(args, gdn, torch, np, dev, flush, timed):
@@ -141,6 +219,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a HIP graph (reported, not the headline: "
                          "on this stack the replay measured slower than eager launches)")
+    ap.add_argument("--bwd-steps", type=int, default=5,
+                    help="timed calls of the backward pass on the same workload (0 = skip)")
     ap.add_argument("--decode-rows", type=int, default=256,
                     help="rows (sequences) of the one-token decode measurement at the TP8 head "
                          "counts (0 = skip)")
@@ -265,6 +345,10 @@ def main():
     gdn.profile_enable(False)
     print(f"[bench] timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
 
+    backward = None
+    if args.bwd_steps > 0 and inp.io_dtype == "bf16":
+        backward = measure_backward(args, gdn, torch, np, dev, flush, inp, q, k, v, g, beta, s0)
+
     decode = None
     if args.decode_rows > 0:
         decode = measure_decode(args, gdn, torch, np, dev, flush, timed)
@@ -339,7 +423,7 @@ def main():
         "graph_ms_per_step": round(float(np.mean(graph_ms)), 4) if graph_ok else None,
         "kernels_ms": {key: round(val, 4) for key, val in mean.items()},
         "warm_cache_ms_per_step": round(float(np.mean(warm)), 4),
-        "mfma": mfma, "parity": parity, "decode": decode,
+        "mfma": mfma, "parity": parity, "backward": backward, "decode": decode,
         "plan": {key: pl[key] for key in ("L", "n_segments", "P_max", "cp_on", "warmup_chunks",
                                           "n_cu", "lambda")},
         "precision": "bf16 MFMA operands, fp32 accumulation; non-input operands split hi+lo",

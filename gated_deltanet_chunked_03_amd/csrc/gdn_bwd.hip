@@ -110,11 +110,12 @@ __device__ void bwd_seq(const BwdParams& p, int seq, int& cbase, int& N, int& le
 }
 
 // K and Q rows of a chunk into [64][LKB] bf16 tiles (rows past nv zero).
+template <int NTHR = NT>
 __device__ void load_kq(const BwdParams& p, size_t tok0, int nv, int hq, bf16 (*kb)[LKB], bf16 (*qb)[LKB]) {
     const size_t ts = (size_t)p.h_qk * DK;
     const bf16* k = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK;
     const bf16* q = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK;
-    for (int idx = threadIdx.x; idx < CH * 16; idx += NT) {
+    for (int idx = threadIdx.x; idx < CH * 16; idx += NTHR) {
         const int r = idx >> 4, part = (idx & 15) * 8;
         u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
         if (r < nv) {
@@ -179,9 +180,17 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
     if (t < CH) {   // forward substitution, one column per lane: T[i][c] = d_ic - sum_j A[i][j] T[j][c]
         const int col = t;
         for (int i = 0; i < CH; ++i) {
-            float s = (i == col) ? 1.f : 0.f;
-            for (int j = col; j < i; ++j) s -= am[i][j] * tm[j][col];
-            tm[i][col] = i >= col ? s : 0.f;
+            // four independent partial sums keep the LDS reads ahead of the adds
+            float s0 = (i == col) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+            int j = col;
+            for (; j + 4 <= i; j += 4) {
+                s0 -= am[i][j] * tm[j][col];
+                s1 -= am[i][j + 1] * tm[j + 1][col];
+                s2 -= am[i][j + 2] * tm[j + 2][col];
+                s3 -= am[i][j + 3] * tm[j + 3][col];
+            }
+            for (; j < i; ++j) s0 -= am[i][j] * tm[j][col];
+            tm[i][col] = i >= col ? (s0 + s1) + (s2 + s3) : 0.f;
         }
     }
     __syncthreads();
@@ -191,7 +200,46 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
 // ----------------------------------------------------------------------------
 // Reverse scan of dS over the chunks of one sequence, for one value head and
 // one 16-column block of dS (the columns never mix). Writes the gradient of
-// the state leaving every chunk, and that of the initial state.
+// the state leaving every chunk, and that of the initial state. The inputs of
+// chunk c - 1 (K, Q, T, P, the dO block, gamma, beta) are loaded into
+// registers while chunk c computes.
+struct ChainIn {
+    u32x4 k[4], q[4];
+    f32x4 t[4], pp[4];
+    u32x2 d;
+    float gam, bet;
+};
+
+__device__ void chain_fetch(const BwdParams& p, ChainIn& in, int f, size_t tok0, int nv, int h, int hq, int col0) {
+    const int t = threadIdx.x;
+    const size_t ts = (size_t)p.h_qk * DK, ts_v = (size_t)p.h_v * DK;
+    const bf16* k = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK;
+    const bf16* q = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = t + NT * e, r = idx >> 4, part = (idx & 15) * 8;
+        in.k[e] = in.q[e] = u32x4{0u, 0u, 0u, 0u};
+        if (r < nv) {
+            in.k[e] = *reinterpret_cast<const u32x4*>(k + (size_t)r * ts + part);
+            in.q[e] = *reinterpret_cast<const u32x4*>(q + (size_t)r * ts + part);
+        }
+    }
+    const float* tp = p.tpg + ((size_t)f * p.h_v + h) * kBwdTpg;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = t + NT * e;
+        in.t[e] = *reinterpret_cast<const f32x4*>(tp + 4 * idx);
+        in.pp[e] = *reinterpret_cast<const f32x4*>(tp + CH * CH + 4 * idx);
+    }
+    const int r = t >> 2, j4 = (t & 3) * 4;
+    in.d = u32x2{0u, 0u};
+    if (r < nv)
+        in.d = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.dout) + (tok0 + r) * ts_v + (size_t)h * DK +
+                                               col0 + j4);
+    in.gam = tp[2 * CH * CH + (t & 63)];
+    in.bet = (t & 63) < nv ? p.beta[(tok0 + (t & 63)) * p.h_v + h] : 0.f;
+}
+
 __global__ __launch_bounds__(NT) void k_bwd_chain(BwdParams p) {
     __shared__ bf16 kb[CH][LKB], qb[CH][LKB];
     __shared__ float tm[CH][LM], pm[CH][LM];
@@ -208,39 +256,42 @@ __global__ __launch_bounds__(NT) void k_bwd_chain(BwdParams p) {
         const int i = idx >> 4, j = idx & 15;
         dsm[i][j] = p.dfinal ? p.dfinal[sq + (size_t)i * DK + col0 + j] : 0.f;
     }
-    const size_t ts_v = (size_t)p.h_v * DK;
-    const bf16* dO = static_cast<const bf16*>(p.dout);
     const int r = t >> 2, j4 = (t & 3) * 4;        // [64 x 16] outputs: row r, columns j4 .. j4 + 3
     const int ii = t >> 1, j8 = (t & 1) * 8;       // [128 x 16] outputs: row ii, columns j8 .. j8 + 7
-    __syncthreads();
+    ChainIn in;
+    if (N > 0) chain_fetch(p, in, cbase + N - 1, tok_s + (size_t)(N - 1) * CH, min(CH, len - (N - 1) * CH), h, hq, col0);
     for (int c = N - 1; c >= 0; --c) {
         const int f = cbase + c;
-        const size_t tok0 = tok_s + (size_t)c * CH;
-        const int nv = min(CH, len - c * CH);
-        const size_t sf = state_off(f, p.h_v, h);
-        for (int idx = t; idx < DK * 16; idx += NT) {
-            const int i = idx >> 4, j = idx & 15;
-            p.ds[sf + (size_t)i * DK + col0 + j] = dsm[i][j];
+        // the previous step's last barrier has passed: the tiles may be rewritten
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = t + NT * e, rr = idx >> 4, part = (idx & 15) * 8;
+            *reinterpret_cast<u32x4*>(&kb[rr][part]) = in.k[e];
+            *reinterpret_cast<u32x4*>(&qb[rr][part]) = in.q[e];
+            const int tr = idx >> 4, tc = (idx & 15) * 4;
+            *reinterpret_cast<f32x4*>(&tm[tr][tc]) = in.t[e];
+            *reinterpret_cast<f32x4*>(&pm[tr][tc]) = in.pp[e];
         }
-        load_kq(p, tok0, nv, hq, kb, qb);
-        const float* tp = p.tpg + ((size_t)f * p.h_v + h) * kBwdTpg;
-        for (int idx = t; idx < CH * CH / 4; idx += NT) {
-            const int rr = idx >> 4, cc = (idx & 15) * 4;
-            *reinterpret_cast<f32x4*>(&tm[rr][cc]) = *reinterpret_cast<const f32x4*>(tp + rr * CH + cc);
-            *reinterpret_cast<f32x4*>(&pm[rr][cc]) = *reinterpret_cast<const f32x4*>(tp + CH * CH + rr * CH + cc);
-        }
+        *reinterpret_cast<f32x4*>(&dom[r][j4]) = f32x4{__uint_as_float(in.d[0] << 16), __uint_as_float(in.d[0] & 0xffff0000u),
+                                                      __uint_as_float(in.d[1] << 16), __uint_as_float(in.d[1] & 0xffff0000u)};
         if (t < CH) {
-            gam[t] = tp[2 * CH * CH + t];
-            bet[t] = t < nv ? p.beta[(tok0 + t) * p.h_v + h] : 0.f;
+            gam[t] = in.gam;
+            bet[t] = in.bet;
         }
-        {
-            const f32x4 d = r < nv ? bf4(dO + (tok0 + r) * ts_v + (size_t)h * DK + col0 + j4) : f32x4{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<f32x4*>(&dom[r][j4]) = d;
+        {   // the gradient of the state leaving chunk c
+            const size_t sf = state_off(f, p.h_v, h);
+            for (int idx = t; idx < DK * 16; idx += NT) {
+                const int i = idx >> 4, j = idx & 15;
+                p.ds[sf + (size_t)i * DK + col0 + j] = dsm[i][j];
+            }
         }
         __syncthreads();
+        if (c > 0)
+            chain_fetch(p, in, f - 1, tok_s + (size_t)(c - 1) * CH, min(CH, len - (c - 1) * CH), h, hq, col0);
         // dV' = diag(f) K dSn + scale P^T dO
         {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
             for (int i = 0; i < DK; ++i) a += bf2f(kb[r][i]) * *reinterpret_cast<const f32x4*>(&dsm[i][j4]);
             a *= __expf(gam[CH - 1] - gam[r]);
             f32x4 b = {0.f, 0.f, 0.f, 0.f};
@@ -262,6 +313,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chain(BwdParams p) {
             const float eC = __expf(gam[CH - 1]);
             f32x4 a0 = eC * *reinterpret_cast<const f32x4*>(&dsm[ii][j8]);
             f32x4 a1 = eC * *reinterpret_cast<const f32x4*>(&dsm[ii][j8 + 4]);
+#pragma unroll 8
             for (int m = 0; m < CH; ++m) {
                 const float qv = bf2f(qb[m][ii]), kv = bf2f(kb[m][ii]);
                 a0 += qv * *reinterpret_cast<const f32x4*>(&dom[m][j8]) - kv * *reinterpret_cast<const f32x4*>(&xm[m][j8]);
@@ -283,10 +335,13 @@ __global__ __launch_bounds__(NT) void k_bwd_chain(BwdParams p) {
 
 // ----------------------------------------------------------------------------
 // Every gradient of one (chunk, value head) given the state entering the
-// chunk and the gradient of the state leaving it. Thread t owns rows
-// 8 (t / 32) .. + 7 and columns 4 (t % 32) .. + 3 of every [64 x 128] result
+// chunk and the gradient of the state leaving it; 8 waves. Thread t owns rows
+// 4 (t / 32) .. + 3 and columns 4 (t % 32) .. + 3 of every [64 x 128] result
 // (dq and dk accumulate there across the steps); [64 x 64] results are split
-// as row t / 4, columns 16 (t % 4) .. + 15.
+// as row t / 8, columns 8 (t % 8) .. + 7.
+constexpr int NTC = 512;
+constexpr int RPT = 4;     // rows of a [64 x 128] result per thread
+constexpr int QPT = 8;     // columns of a [64 x 64] result per thread
 struct ChunkSmem {
     bf16 kb[CH][LKB], qb[CH][LKB];
     float x1[CH][LX];           // Y, then dY
@@ -298,7 +353,7 @@ struct ChunkSmem {
     float dgc;
 };
 
-__global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
+__global__ __launch_bounds__(NTC) void k_bwd_chunk(BwdParams p) {
     __shared__ ChunkSmem sm;
     const int f = blockIdx.x, h = blockIdx.y, hq = h / p.group, t = threadIdx.x;
     int seq, c, len;
@@ -314,8 +369,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
     const bf16* dO = static_cast<const bf16*>(p.dout) + tok0 * ts_v + (size_t)h * DK;
     const float scale = p.scale;
 
-    load_kq(p, tok0, nv, hq, sm.kb, sm.qb);
-    for (int idx = t; idx < CH * CH / 4; idx += NT) {
+    load_kq<NTC>(p, tok0, nv, hq, sm.kb, sm.qb);
+    for (int idx = t; idx < CH * CH / 4; idx += NTC) {
         const int rr = idx >> 4, cc = (idx & 15) * 4;
         *reinterpret_cast<f32x4*>(&sm.m1[rr][cc]) = *reinterpret_cast<const f32x4*>(tp + rr * CH + cc);
         *reinterpret_cast<f32x4*>(&sm.m2[rr][cc]) = *reinterpret_cast<const f32x4*>(tp + CH * CH + rr * CH + cc);
@@ -334,29 +389,29 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
     const float eC = __expf(sm.gam[CH - 1]);
     __syncthreads();
 
-    const int r0 = 8 * (t >> 5), j0 = 4 * (t & 31), lane32 = t & 31;
-    const int pr = t >> 2, pi0 = (t & 3) * 16;
+    const int r0 = RPT * (t >> 5), j0 = 4 * (t & 31), lane32 = t & 31;
+    const int pr = t >> 3, pi0 = (t & 7) * QPT;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 dq[8], dk[8];
+    f32x4 dq[RPT], dk[RPT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dq[e] = dk[e] = zero4;
+    for (int e = 0; e < RPT; ++e) dq[e] = dk[e] = zero4;
     auto vrow = [&](const bf16* base, int r) { return r < nv ? bf4(base + (size_t)r * ts_v + j0) : zero4; };
 
     // 1. K S and Q S: Y = V - diag(e) K S; the output's Q S term in dgamma
     {
-        f32x4 ks[8], qs[8];
+        f32x4 ks[RPT], qs[RPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ks[e] = qs[e] = zero4;
+        for (int e = 0; e < RPT; ++e) ks[e] = qs[e] = zero4;
         for (int i = 0; i < DK; ++i) {
             const f32x4 s = *reinterpret_cast<const f32x4*>(S + (size_t)i * DK + j0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < RPT; ++e) {
                 ks[e] += bf2f(sm.kb[r0 + e][i]) * s;
                 qs[e] += bf2f(sm.qb[r0 + e][i]) * s;
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < RPT; ++e) {
             const int r = r0 + e;
             *reinterpret_cast<f32x4*>(&sm.x1[r][j0]) = vrow(V, r) - sm.eg[r] * ks[e];
             const float part = sum32(dot4(qs[e], vrow(dO, r)));
@@ -366,36 +421,36 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
     __syncthreads();
     // 2. V' = T diag(beta) Y
     {
-        f32x4 a[8];
+        f32x4 a[RPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = zero4;
+        for (int e = 0; e < RPT; ++e) a[e] = zero4;
         for (int i = 0; i < CH; ++i) {
             const f32x4 y = sm.bet[i] * *reinterpret_cast<const f32x4*>(&sm.x1[i][j0]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] += sm.m1[r0 + e][i] * y;
+            for (int e = 0; e < RPT; ++e) a[e] += sm.m1[r0 + e][i] * y;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<f32x4*>(&sm.x2[r0 + e][j0]) = a[e];
+        for (int e = 0; e < RPT; ++e) *reinterpret_cast<f32x4*>(&sm.x2[r0 + e][j0]) = a[e];
     }
     __syncthreads();
     // 3. dK~ = V' dSn^T (into dk with diag(f); its dgamma terms), dP = scale dO V'^T -> Psi
     {
-        f32x4 a[8];
+        f32x4 a[RPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = zero4;
+        for (int e = 0; e < RPT; ++e) a[e] = zero4;
         for (int j = 0; j < DK; j += 4) {
             const f32x4 d0 = *reinterpret_cast<const f32x4*>(dSn + (size_t)(j0 + 0) * DK + j);
             const f32x4 d1 = *reinterpret_cast<const f32x4*>(dSn + (size_t)(j0 + 1) * DK + j);
             const f32x4 d2 = *reinterpret_cast<const f32x4*>(dSn + (size_t)(j0 + 2) * DK + j);
             const f32x4 d3 = *reinterpret_cast<const f32x4*>(dSn + (size_t)(j0 + 3) * DK + j);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < RPT; ++e) {
                 const f32x4 vv = *reinterpret_cast<const f32x4*>(&sm.x2[r0 + e][j]);
                 a[e] += f32x4{dot4(vv, d0), dot4(vv, d1), dot4(vv, d2), dot4(vv, d3)};
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < RPT; ++e) {
             const int r = r0 + e;
             dk[e] += sm.fr[r] * a[e];
             const float kap = sum32(sm.fr[r] * dot4(bf4(&sm.kb[r][j0]), a[e]));
@@ -406,17 +461,17 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
         }
     }
     {
-        float a[16];
+        float a[QPT];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) a[q] = 0.f;
+        for (int q = 0; q < QPT; ++q) a[q] = 0.f;
         for (int j = 0; j < DK; j += 4) {
             const f32x4 dov = pr < nv ? bf4(dO + (size_t)pr * ts_v + j) : zero4;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) a[q] += dot4(dov, *reinterpret_cast<const f32x4*>(&sm.x2[pi0 + q][j]));
+            for (int q = 0; q < QPT; ++q) a[q] += dot4(dov, *reinterpret_cast<const f32x4*>(&sm.x2[pi0 + q][j]));
         }
         float erow = 0.f;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < QPT; ++q) {
             const int i = pi0 + q;
             float psi = 0.f, E = 0.f;
             if (i <= pr) {
@@ -433,63 +488,63 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
     __syncthreads();
     // 4. dV' = diag(f) K dSn + scale P^T dO; dq += Psi K + scale diag(e) dO S^T; dk += Psi^T Q
     {
-        f32x4 a[8];
+        f32x4 a[RPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = zero4;
+        for (int e = 0; e < RPT; ++e) a[e] = zero4;
         for (int i = 0; i < DK; ++i) {
             const f32x4 d = *reinterpret_cast<const f32x4*>(dSn + (size_t)i * DK + j0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] += bf2f(sm.kb[r0 + e][i]) * d;
+            for (int e = 0; e < RPT; ++e) a[e] += bf2f(sm.kb[r0 + e][i]) * d;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] *= sm.fr[r0 + e];
+        for (int e = 0; e < RPT; ++e) a[e] *= sm.fr[r0 + e];
         for (int m = 0; m < nv; ++m) {
             const f32x4 dov = scale * bf4(dO + (size_t)m * ts_v + j0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] += sm.m2[m][r0 + e] * dov;
+            for (int e = 0; e < RPT; ++e) a[e] += sm.m2[m][r0 + e] * dov;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<f32x4*>(&sm.x2[r0 + e][j0]) = a[e];
+        for (int e = 0; e < RPT; ++e) *reinterpret_cast<f32x4*>(&sm.x2[r0 + e][j0]) = a[e];
         for (int m = 0; m < CH; ++m) {
             const f32x4 kk = bf4(&sm.kb[m][j0]), qq = bf4(&sm.qb[m][j0]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < RPT; ++e) {
                 dq[e] += sm.m3[r0 + e][m] * kk;
                 dk[e] += sm.m3[m][r0 + e] * qq;
             }
         }
-        f32x4 b[8];
+        f32x4 b[RPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b[e] = zero4;
+        for (int e = 0; e < RPT; ++e) b[e] = zero4;
         for (int j = 0; j < DK; j += 4) {
             const f32x4 s0 = *reinterpret_cast<const f32x4*>(S + (size_t)(j0 + 0) * DK + j);
             const f32x4 s1 = *reinterpret_cast<const f32x4*>(S + (size_t)(j0 + 1) * DK + j);
             const f32x4 s2 = *reinterpret_cast<const f32x4*>(S + (size_t)(j0 + 2) * DK + j);
             const f32x4 s3 = *reinterpret_cast<const f32x4*>(S + (size_t)(j0 + 3) * DK + j);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < RPT; ++e) {
                 const int r = r0 + e;
                 const f32x4 dov = r < nv ? bf4(dO + (size_t)r * ts_v + j) : zero4;
                 b[e] += f32x4{dot4(dov, s0), dot4(dov, s1), dot4(dov, s2), dot4(dov, s3)};
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dq[e] += (scale * sm.eg[r0 + e]) * b[e];
+        for (int e = 0; e < RPT; ++e) dq[e] += (scale * sm.eg[r0 + e]) * b[e];
     }
     __syncthreads();
     // 5. Z = T^T dV', dY = diag(beta) Z (the dv output), dbeta and dgamma terms; dT = dV' (diag(beta) Y)^T
-    f32x4 dy[8];
+    f32x4 dy[RPT];
     {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dy[e] = zero4;
+        for (int e = 0; e < RPT; ++e) dy[e] = zero4;
         for (int m = 0; m < CH; ++m) {
             const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.x2[m][j0]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dy[e] += sm.m1[m][r0 + e] * d;
+            for (int e = 0; e < RPT; ++e) dy[e] += sm.m1[m][r0 + e] * d;
         }
         bf16* dvo = static_cast<bf16*>(p.dv) + tok0 * ts_v + (size_t)h * DK + j0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < RPT; ++e) {
             const int r = r0 + e;
             const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.x1[r][j0]);
             const float zb = sum32(dot4(dy[e], y));
@@ -503,77 +558,77 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
                 *reinterpret_cast<u32x2*>(dvo + (size_t)r * ts_v) = u32x2{pack_rne(dy[e][0], dy[e][1]),
                                                                        pack_rne(dy[e][2], dy[e][3])};
         }
-        float a[16];
+        float a[QPT];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) a[q] = 0.f;
+        for (int q = 0; q < QPT; ++q) a[q] = 0.f;
         for (int j = 0; j < DK; j += 4) {
             const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.x2[pr][j]);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) a[q] += dot4(d, *reinterpret_cast<const f32x4*>(&sm.x1[pi0 + q][j]));
+            for (int q = 0; q < QPT; ++q) a[q] += dot4(d, *reinterpret_cast<const f32x4*>(&sm.x1[pi0 + q][j]));
         }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) sm.m3[pr][pi0 + q] = a[q] * sm.bet[pi0 + q];
+        for (int q = 0; q < QPT; ++q) sm.m3[pr][pi0 + q] = a[q] * sm.bet[pi0 + q];
     }
     __syncthreads();
     // 6. dY into x1 (Y is no longer read); dT T^T into m2
     {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<f32x4*>(&sm.x1[r0 + e][j0]) = dy[e];
-        float a[16];
+        for (int e = 0; e < RPT; ++e) *reinterpret_cast<f32x4*>(&sm.x1[r0 + e][j0]) = dy[e];
+        float a[QPT];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) a[q] = 0.f;
+        for (int q = 0; q < QPT; ++q) a[q] = 0.f;
         for (int m = 0; m < CH; ++m) {
             const float d = sm.m3[pr][m];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) a[q] += d * sm.m1[pi0 + q][m];
+            for (int q = 0; q < QPT; ++q) a[q] += d * sm.m1[pi0 + q][m];
         }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) sm.m2[pr][pi0 + q] = a[q];
+        for (int q = 0; q < QPT; ++q) sm.m2[pr][pi0 + q] = a[q];
     }
     __syncthreads();
     // 7. dA = -T^T (dT T^T), strictly lower, into m3; dk -= diag(e) dY S^T
     {
-        float a[16];
+        float a[QPT];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) a[q] = 0.f;
+        for (int q = 0; q < QPT; ++q) a[q] = 0.f;
         for (int m = 0; m < CH; ++m) {
             const float tv = sm.m1[m][pr];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) a[q] += tv * sm.m2[m][pi0 + q];
+            for (int q = 0; q < QPT; ++q) a[q] += tv * sm.m2[m][pi0 + q];
         }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) sm.m3[pr][pi0 + q] = (pi0 + q < pr) ? -a[q] : 0.f;
-        f32x4 b[8];
+        for (int q = 0; q < QPT; ++q) sm.m3[pr][pi0 + q] = (pi0 + q < pr) ? -a[q] : 0.f;
+        f32x4 b[RPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) b[e] = zero4;
+        for (int e = 0; e < RPT; ++e) b[e] = zero4;
         for (int j = 0; j < DK; j += 4) {
             const f32x4 s0 = *reinterpret_cast<const f32x4*>(S + (size_t)(j0 + 0) * DK + j);
             const f32x4 s1 = *reinterpret_cast<const f32x4*>(S + (size_t)(j0 + 1) * DK + j);
             const f32x4 s2 = *reinterpret_cast<const f32x4*>(S + (size_t)(j0 + 2) * DK + j);
             const f32x4 s3 = *reinterpret_cast<const f32x4*>(S + (size_t)(j0 + 3) * DK + j);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < RPT; ++e) {
                 const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.x1[r0 + e][j]);
                 b[e] += f32x4{dot4(d, s0), dot4(d, s1), dot4(d, s2), dot4(d, s3)};
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dk[e] -= sm.eg[r0 + e] * b[e];
+        for (int e = 0; e < RPT; ++e) dk[e] -= sm.eg[r0 + e] * b[e];
     }
     __syncthreads();
     // 8. through A: dbeta, dgamma and G (into m2)
     {
-        float kk[16];
+        float kk[QPT];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) kk[q] = 0.f;
+        for (int q = 0; q < QPT; ++q) kk[q] = 0.f;
         for (int d = 0; d < DK; d += 4) {
             const f32x4 kr = bf4(&sm.kb[pr][d]);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) kk[q] += dot4(kr, bf4(&sm.kb[pi0 + q][d]));
+            for (int q = 0; q < QPT; ++q) kk[q] += dot4(kr, bf4(&sm.kb[pi0 + q][d]));
         }
         float db = 0.f, dgr = 0.f;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < QPT; ++q) {
             const int i = pi0 + q;
             float G = 0.f;
             if (i < pr) {
@@ -592,7 +647,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
     }
     {   // dgamma_C from the decay of the state: e_C <S, dSn>
         float part = 0.f;
-        for (int idx = t; idx < DK * DK / 4; idx += NT)
+        for (int idx = t; idx < DK * DK / 4; idx += NTC)
             part += dot4(*reinterpret_cast<const f32x4*>(S + 4 * idx), *reinterpret_cast<const f32x4*>(dSn + 4 * idx));
         part = sum32(part);
         if (lane32 == 0) atomicAdd(&sm.dgc, eC * part);
@@ -602,14 +657,14 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdParams p) {
     for (int m = 0; m < CH; ++m) {
         const f32x4 kk = bf4(&sm.kb[m][j0]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dk[e] += (sm.m2[r0 + e][m] + sm.m2[m][r0 + e]) * kk;
+        for (int e = 0; e < RPT; ++e) dk[e] += (sm.m2[r0 + e][m] + sm.m2[m][r0 + e]) * kk;
     }
     // outputs: per-head parts of dq and dk; dg as the reverse cumulative sum of dgamma; dbeta
     {
         float* dqp = p.dq_part + (tok0 * p.h_v + h) * DK + j0;
         float* dkp = p.dk_part + (tok0 * p.h_v + h) * DK + j0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < RPT; ++e) {
             const int r = r0 + e;
             if (r < nv) {
                 *reinterpret_cast<f32x4*>(dqp + (size_t)r * ts_v) = dq[e];
@@ -665,7 +720,7 @@ int launch_bwd(const BwdParams& p, void* stream) {
         if ((e = launched())) return e;
     }
     if (p.n_chunks > 0) {
-        hipLaunchKernelGGL(k_bwd_chunk, dim3(p.n_chunks, p.h_v), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL(k_bwd_chunk, dim3(p.n_chunks, p.h_v), dim3(NTC), 0, s, p);
         if ((e = launched())) return e;
     }
     return 0;
