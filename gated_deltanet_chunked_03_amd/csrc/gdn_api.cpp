@@ -368,10 +368,10 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
 
 // Workspace of the backward: the forward's (for its re-run), then the re-run's
 // output, the state entering every chunk, the gradient of the state leaving
-// every chunk, T / P / gamma per chunk and head, and the per-value-head parts
-// of dq and dk.
+// every chunk, T / P / gamma per chunk and head (fp32, and T^T / scale P^T as
+// bf16 hi/lo images), and the per-value-head parts of dq and dk.
 struct BwdLayout {
-    size_t off_o = 0, off_cs = 0, off_ds = 0, off_tpg = 0, off_dq = 0, off_dk = 0, bytes = 0;
+    size_t off_o = 0, off_cs = 0, off_ds = 0, off_tpg = 0, off_tpt = 0, off_dq = 0, off_dk = 0, bytes = 0;
     size_t tokens = 0;
 };
 
@@ -384,6 +384,7 @@ BwdLayout bwd_layout(const gdn_desc* d, const Plan& P) {
     L.off_cs = off;  off = align_up(off + st, 256);
     L.off_ds = off;  off = align_up(off + st, 256);
     L.off_tpg = off; off = align_up(off + (size_t)P.n_chunks_total * d->h_v * gdn::kBwdTpg * sizeof(float), 256);
+    L.off_tpt = off; off = align_up(off + (size_t)P.n_chunks_total * d->h_v * gdn::kBwdTpt * 2, 256);
     L.off_dq = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
     L.off_dk = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
     L.bytes = off;
@@ -441,6 +442,7 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     b.cs = reinterpret_cast<const float*>(w8 + L.off_cs);
     b.ds = reinterpret_cast<float*>(w8 + L.off_ds);
     b.tpg = reinterpret_cast<float*>(w8 + L.off_tpg);
+    b.tpt = w8 + L.off_tpt;
     b.dq_part = reinterpret_cast<float*>(w8 + L.off_dq);
     b.dk_part = reinterpret_cast<float*>(w8 + L.off_dk);
     b.n_seqs = P.n_seqs;

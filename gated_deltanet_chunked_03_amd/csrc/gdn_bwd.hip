@@ -22,11 +22,12 @@
 //   dgamma from every exponential it enters (P, e, f, A, e_C), dg = reverse
 //   cumulative sum of dgamma over the chunk.
 // Kernels: the forward (re-run with the state entering every chunk written
-// out), k_bwd_prep (T, P, gamma per chunk and head), k_bwd_chain (the reverse
-// scan of dS over the chunks; 16-column blocks of dS are independent),
-// k_bwd_chunk (every other gradient, all chunks in parallel) and k_bwd_sum
-// (query/key gradients summed over the value heads of a group). This first
-// backward computes in fp32 on the vector ALUs; bf16 inputs only.
+// out), k_bwd_prep (T, P, gamma per chunk and head, and T^T / scale P^T as
+// bf16 hi/lo images), the reverse scan of dS over the chunks on the matrix
+// cores (k_bwd_chain_mma, in the forward's kernel file, which shares its
+// operand layouts), k_bwd_chunk (every other gradient, all chunks in
+// parallel, fp32 on the vector ALUs) and k_bwd_sum (query/key gradients
+// summed over the value heads of a group). bf16 inputs only.
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -47,7 +48,6 @@ constexpr int NT = 256;
 constexpr int LKB = 136;   // bf16 row stride of the [64][128] K, Q tiles
 constexpr int LX = 132;    // fp32 row stride of [64][128] tiles
 constexpr int LM = 68;     // fp32 row stride of [64][64] tiles
-constexpr int LB = 20;     // fp32 row stride of 16-column blocks
 
 __device__ __forceinline__ int n_chunks_of(int len) { return (len + CH - 1) / CH; }
 __device__ __forceinline__ size_t state_off(int idx, int h_v, int h) {
@@ -62,6 +62,18 @@ __device__ __forceinline__ f32x4 bf4(const bf16* x) {
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 __device__ __forceinline__ unsigned pack_rne(float a, float b) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// Position of token x in an operand row of the matrix-core chain (within each
+// block of 32, x = 16 b + 4 a + e sits at 8 a + 4 b + e: the order in which a
+// 32-row accumulator pair serves as an MFMA operand).
+__device__ __forceinline__ int kp(int x) {
+    return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
+}
+// hi = x with its low 16 bits cleared, lo = x - hi rounded to bf16
+__device__ __forceinline__ void split1(float x, bf16& hi, bf16& lo) {
+    const unsigned u = __float_as_uint(x);
+    hi = __builtin_bit_cast(bf16, (unsigned short)(u >> 16));
+    lo = (bf16)(x - __uint_as_float(u & 0xffff0000u));
 }
 // sum over the 32 lanes of a half wave
 __device__ __forceinline__ float sum32(float x) {
@@ -93,22 +105,6 @@ __device__ bool bwd_locate(const BwdParams& p, int slot, int& seq, int& c, int& 
     return false;
 }
 
-// Sequence -> its first chunk slot, chunk count, length and first token.
-__device__ void bwd_seq(const BwdParams& p, int seq, int& cbase, int& N, int& len, size_t& tok_s) {
-    if (!p.cu) {
-        len = p.seq_len;
-        N = n_chunks_of(len);
-        cbase = seq * N;
-        tok_s = (size_t)seq * p.seq_len;
-        return;
-    }
-    cbase = 0;
-    for (int n = 0; n < seq; ++n) cbase += n_chunks_of(p.cu[n + 1] - p.cu[n]);
-    len = p.cu[seq + 1] - p.cu[seq];
-    N = n_chunks_of(len);
-    tok_s = (size_t)p.cu[seq];
-}
-
 // K and Q rows of a chunk into [64][LKB] bf16 tiles (rows past nv zero).
 template <int NTHR = NT>
 __device__ void load_kq(const BwdParams& p, size_t tok0, int nv, int hq, bf16 (*kb)[LKB], bf16 (*qb)[LKB]) {
@@ -133,6 +129,9 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
     __shared__ bf16 kb[CH][LKB], qb[CH][LKB];
     __shared__ float am[CH][LM], tm[CH][LM];
     __shared__ float gam[CH], bet[CH];
+    // P takes Q's tile once Q K^T is formed (same size: 64 x 136 bf16 = 64 x 68 fp32)
+    float (*pmat)[LM] = reinterpret_cast<float (*)[LM]>(&qb[0][0]);
+    static_assert(sizeof(qb) == CH * LM * sizeof(float), "P reuses the Q tile");
     const int f = blockIdx.x, h = blockIdx.y, hq = h / p.group, t = threadIdx.x;
     int seq, c, len;
     size_t tok_s;
@@ -153,8 +152,8 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
         out[2 * CH * CH + t] = x;
     }
     __syncthreads();
-    {   // A (strictly lower) and P (lower with the diagonal): row r, columns i0 .. i0 + 15
-        const int r = t >> 2, i0 = (t & 3) * 16;
+    {   // A (strictly lower) and P (lower with the diagonal): row r, columns i0 + 4 ii
+        const int r = t >> 2, i0 = t & 3;
         float kk[16], qk[16];
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) kk[ii] = qk[ii] = 0.f;
@@ -162,18 +161,21 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
             const f32x4 kr = bf4(&kb[r][d]), qr = bf4(&qb[r][d]);
 #pragma unroll
             for (int ii = 0; ii < 16; ++ii) {
-                const f32x4 ki = bf4(&kb[i0 + ii][d]);
+                const f32x4 ki = bf4(&kb[i0 + 4 * ii][d]);
                 kk[ii] += dot4(kr, ki);
                 qk[ii] += dot4(qr, ki);
             }
         }
         float* P = out + CH * CH;
+        __syncthreads();   // every read of Q is done before P overwrites its tile
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-            const int i = i0 + ii;
+            const int i = i0 + 4 * ii;
             const float ex = i <= r ? __expf(gam[r] - gam[i]) : 0.f;
             am[r][i] = i < r ? bet[r] * ex * kk[ii] : 0.f;
-            P[r * CH + i] = i <= r ? ex * qk[ii] : 0.f;
+            const float pv = i <= r ? ex * qk[ii] : 0.f;
+            P[r * CH + i] = pv;
+            pmat[r][i] = pv;
         }
     }
     __syncthreads();
@@ -195,141 +197,27 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
     }
     __syncthreads();
     for (int idx = t; idx < CH * CH; idx += NT) out[idx] = tm[idx >> 6][idx & 63];
-}
-
-// ----------------------------------------------------------------------------
-// Reverse scan of dS over the chunks of one sequence, for one value head and
-// one 16-column block of dS (the columns never mix). Writes the gradient of
-// the state leaving every chunk, and that of the initial state. The inputs of
-// chunk c - 1 (K, Q, T, P, the dO block, gamma, beta) are loaded into
-// registers while chunk c computes.
-struct ChainIn {
-    u32x4 k[4], q[4];
-    f32x4 t[4], pp[4];
-    u32x2 d;
-    float gam, bet;
-};
-
-__device__ void chain_fetch(const BwdParams& p, ChainIn& in, int f, size_t tok0, int nv, int h, int hq, int col0) {
-    const int t = threadIdx.x;
-    const size_t ts = (size_t)p.h_qk * DK, ts_v = (size_t)p.h_v * DK;
-    const bf16* k = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK;
-    const bf16* q = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = t + NT * e, r = idx >> 4, part = (idx & 15) * 8;
-        in.k[e] = in.q[e] = u32x4{0u, 0u, 0u, 0u};
-        if (r < nv) {
-            in.k[e] = *reinterpret_cast<const u32x4*>(k + (size_t)r * ts + part);
-            in.q[e] = *reinterpret_cast<const u32x4*>(q + (size_t)r * ts + part);
-        }
-    }
-    const float* tp = p.tpg + ((size_t)f * p.h_v + h) * kBwdTpg;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = t + NT * e;
-        in.t[e] = *reinterpret_cast<const f32x4*>(tp + 4 * idx);
-        in.pp[e] = *reinterpret_cast<const f32x4*>(tp + CH * CH + 4 * idx);
-    }
-    const int r = t >> 2, j4 = (t & 3) * 4;
-    in.d = u32x2{0u, 0u};
-    if (r < nv)
-        in.d = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.dout) + (tok0 + r) * ts_v + (size_t)h * DK +
-                                               col0 + j4);
-    in.gam = tp[2 * CH * CH + (t & 63)];
-    in.bet = (t & 63) < nv ? p.beta[(tok0 + (t & 63)) * p.h_v + h] : 0.f;
-}
-
-__global__ __launch_bounds__(NT) void k_bwd_chain(BwdParams p) {
-    __shared__ bf16 kb[CH][LKB], qb[CH][LKB];
-    __shared__ float tm[CH][LM], pm[CH][LM];
-    __shared__ float dsm[DK][LB];
-    __shared__ float dom[CH][LB], vm[CH][LB], xm[CH][LB];
-    __shared__ float gam[CH], bet[CH];
-    const int seq = blockIdx.x >> 3, col0 = 16 * (blockIdx.x & 7), h = blockIdx.y, hq = h / p.group;
-    const int t = threadIdx.x;
-    int cbase, N, len;
-    size_t tok_s;
-    bwd_seq(p, seq, cbase, N, len, tok_s);
-    const size_t sq = state_off(seq, p.h_v, h);
-    for (int idx = t; idx < DK * 16; idx += NT) {
-        const int i = idx >> 4, j = idx & 15;
-        dsm[i][j] = p.dfinal ? p.dfinal[sq + (size_t)i * DK + col0 + j] : 0.f;
-    }
-    const int r = t >> 2, j4 = (t & 3) * 4;        // [64 x 16] outputs: row r, columns j4 .. j4 + 3
-    const int ii = t >> 1, j8 = (t & 1) * 8;       // [128 x 16] outputs: row ii, columns j8 .. j8 + 7
-    ChainIn in;
-    if (N > 0) chain_fetch(p, in, cbase + N - 1, tok_s + (size_t)(N - 1) * CH, min(CH, len - (N - 1) * CH), h, hq, col0);
-    for (int c = N - 1; c >= 0; --c) {
-        const int f = cbase + c;
-        // the previous step's last barrier has passed: the tiles may be rewritten
+    // T^T and scale P^T as hi/lo bf16 rows with the contraction token in kp order
+    // (four consecutive tokens stay consecutive in kp order: one 8-byte store each)
+    bf16* img = static_cast<bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt;
+    for (int idx = t; idx < CH * CH / 4; idx += NT) {
+        const int r = idx >> 4, m4 = (idx & 15) * 4, o = r * CH + kp(m4);
+        bf16 th[4], tl[4], ph[4], pl[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int idx = t + NT * e, rr = idx >> 4, part = (idx & 15) * 8;
-            *reinterpret_cast<u32x4*>(&kb[rr][part]) = in.k[e];
-            *reinterpret_cast<u32x4*>(&qb[rr][part]) = in.q[e];
-            const int tr = idx >> 4, tc = (idx & 15) * 4;
-            *reinterpret_cast<f32x4*>(&tm[tr][tc]) = in.t[e];
-            *reinterpret_cast<f32x4*>(&pm[tr][tc]) = in.pp[e];
+            split1(tm[m4 + e][r], th[e], tl[e]);
+            split1(p.scale * pmat[m4 + e][r], ph[e], pl[e]);
         }
-        *reinterpret_cast<f32x4*>(&dom[r][j4]) = f32x4{__uint_as_float(in.d[0] << 16), __uint_as_float(in.d[0] & 0xffff0000u),
-                                                      __uint_as_float(in.d[1] << 16), __uint_as_float(in.d[1] & 0xffff0000u)};
-        if (t < CH) {
-            gam[t] = in.gam;
-            bet[t] = in.bet;
-        }
-        {   // the gradient of the state leaving chunk c
-            const size_t sf = state_off(f, p.h_v, h);
-            for (int idx = t; idx < DK * 16; idx += NT) {
-                const int i = idx >> 4, j = idx & 15;
-                p.ds[sf + (size_t)i * DK + col0 + j] = dsm[i][j];
-            }
-        }
-        __syncthreads();
-        if (c > 0)
-            chain_fetch(p, in, f - 1, tok_s + (size_t)(c - 1) * CH, min(CH, len - (c - 1) * CH), h, hq, col0);
-        // dV' = diag(f) K dSn + scale P^T dO
-        {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int i = 0; i < DK; ++i) a += bf2f(kb[r][i]) * *reinterpret_cast<const f32x4*>(&dsm[i][j4]);
-            a *= __expf(gam[CH - 1] - gam[r]);
-            f32x4 b = {0.f, 0.f, 0.f, 0.f};
-            for (int m = r; m < CH; ++m) b += pm[m][r] * *reinterpret_cast<const f32x4*>(&dom[m][j4]);
-            *reinterpret_cast<f32x4*>(&vm[r][j4]) = a + p.scale * b;
-        }
-        __syncthreads();
-        // e dY = e beta T^T dV' and the scaled dO (own elements)
-        {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            for (int m = r; m < CH; ++m) z += tm[m][r] * *reinterpret_cast<const f32x4*>(&vm[m][j4]);
-            const float er = __expf(gam[r]);
-            *reinterpret_cast<f32x4*>(&xm[r][j4]) = (er * bet[r]) * z;
-            *reinterpret_cast<f32x4*>(&dom[r][j4]) *= p.scale * er;
-        }
-        __syncthreads();
-        // dS <- e_C dS + Q^T (scale e dO) - K^T (e dY)   (own elements)
-        {
-            const float eC = __expf(gam[CH - 1]);
-            f32x4 a0 = eC * *reinterpret_cast<const f32x4*>(&dsm[ii][j8]);
-            f32x4 a1 = eC * *reinterpret_cast<const f32x4*>(&dsm[ii][j8 + 4]);
-#pragma unroll 8
-            for (int m = 0; m < CH; ++m) {
-                const float qv = bf2f(qb[m][ii]), kv = bf2f(kb[m][ii]);
-                a0 += qv * *reinterpret_cast<const f32x4*>(&dom[m][j8]) - kv * *reinterpret_cast<const f32x4*>(&xm[m][j8]);
-                a1 += qv * *reinterpret_cast<const f32x4*>(&dom[m][j8 + 4]) -
-                      kv * *reinterpret_cast<const f32x4*>(&xm[m][j8 + 4]);
-            }
-            *reinterpret_cast<f32x4*>(&dsm[ii][j8]) = a0;
-            *reinterpret_cast<f32x4*>(&dsm[ii][j8 + 4]) = a1;
-        }
-        __syncthreads();
-    }
-    if (p.dinit) {
-        for (int idx = t; idx < DK * 16; idx += NT) {
-            const int i = idx >> 4, j = idx & 15;
-            p.dinit[sq + (size_t)i * DK + col0 + j] = dsm[i][j];
-        }
+        auto pack = [](const bf16 (&x)[4]) {
+            return u32x2{(unsigned)__builtin_bit_cast(unsigned short, x[0]) |
+                             ((unsigned)__builtin_bit_cast(unsigned short, x[1]) << 16),
+                         (unsigned)__builtin_bit_cast(unsigned short, x[2]) |
+                             ((unsigned)__builtin_bit_cast(unsigned short, x[3]) << 16)};
+        };
+        *reinterpret_cast<u32x2*>(img + o) = pack(th);
+        *reinterpret_cast<u32x2*>(img + CH * CH + o) = pack(tl);
+        *reinterpret_cast<u32x2*>(img + 2 * CH * CH + o) = pack(ph);
+        *reinterpret_cast<u32x2*>(img + 3 * CH * CH + o) = pack(pl);
     }
 }
 
@@ -338,7 +226,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chain(BwdParams p) {
 // chunk and the gradient of the state leaving it; 8 waves. Thread t owns rows
 // 4 (t / 32) .. + 3 and columns 4 (t % 32) .. + 3 of every [64 x 128] result
 // (dq and dk accumulate there across the steps); [64 x 64] results are split
-// as row t / 8, columns 8 (t % 8) .. + 7.
+// as row t / 8, columns t % 8 + 8 q (q < 8).
 constexpr int NTC = 512;
 constexpr int RPT = 4;     // rows of a [64 x 128] result per thread
 constexpr int QPT = 8;     // columns of a [64 x 64] result per thread
@@ -390,7 +278,9 @@ __global__ __launch_bounds__(NTC) void k_bwd_chunk(BwdParams p) {
     __syncthreads();
 
     const int r0 = RPT * (t >> 5), j0 = 4 * (t & 31), lane32 = t & 31;
-    const int pr = t >> 3, pi0 = (t & 7) * QPT;
+    // [64 x 64] results: row t / 8, columns t % 8 + 8 q (interleaved, so that the
+    // eight lanes of a row group read rows one apart: no LDS bank conflicts)
+    const int pr = t >> 3, pi0 = t & 7;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     f32x4 dq[RPT], dk[RPT];
 #pragma unroll
@@ -467,12 +357,12 @@ __global__ __launch_bounds__(NTC) void k_bwd_chunk(BwdParams p) {
         for (int j = 0; j < DK; j += 4) {
             const f32x4 dov = pr < nv ? bf4(dO + (size_t)pr * ts_v + j) : zero4;
 #pragma unroll
-            for (int q = 0; q < QPT; ++q) a[q] += dot4(dov, *reinterpret_cast<const f32x4*>(&sm.x2[pi0 + q][j]));
+            for (int q = 0; q < QPT; ++q) a[q] += dot4(dov, *reinterpret_cast<const f32x4*>(&sm.x2[pi0 + 8 * q][j]));
         }
         float erow = 0.f;
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
-            const int i = pi0 + q;
+            const int i = pi0 + 8 * q;
             float psi = 0.f, E = 0.f;
             if (i <= pr) {
                 const float dP = scale * a[q];
@@ -564,10 +454,10 @@ __global__ __launch_bounds__(NTC) void k_bwd_chunk(BwdParams p) {
         for (int j = 0; j < DK; j += 4) {
             const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.x2[pr][j]);
 #pragma unroll
-            for (int q = 0; q < QPT; ++q) a[q] += dot4(d, *reinterpret_cast<const f32x4*>(&sm.x1[pi0 + q][j]));
+            for (int q = 0; q < QPT; ++q) a[q] += dot4(d, *reinterpret_cast<const f32x4*>(&sm.x1[pi0 + 8 * q][j]));
         }
 #pragma unroll
-        for (int q = 0; q < QPT; ++q) sm.m3[pr][pi0 + q] = a[q] * sm.bet[pi0 + q];
+        for (int q = 0; q < QPT; ++q) sm.m3[pr][pi0 + 8 * q] = a[q] * sm.bet[pi0 + 8 * q];
     }
     __syncthreads();
     // 6. dY into x1 (Y is no longer read); dT T^T into m2
@@ -580,10 +470,10 @@ __global__ __launch_bounds__(NTC) void k_bwd_chunk(BwdParams p) {
         for (int m = 0; m < CH; ++m) {
             const float d = sm.m3[pr][m];
 #pragma unroll
-            for (int q = 0; q < QPT; ++q) a[q] += d * sm.m1[pi0 + q][m];
+            for (int q = 0; q < QPT; ++q) a[q] += d * sm.m1[pi0 + 8 * q][m];
         }
 #pragma unroll
-        for (int q = 0; q < QPT; ++q) sm.m2[pr][pi0 + q] = a[q];
+        for (int q = 0; q < QPT; ++q) sm.m2[pr][pi0 + 8 * q] = a[q];
     }
     __syncthreads();
     // 7. dA = -T^T (dT T^T), strictly lower, into m3; dk -= diag(e) dY S^T
@@ -594,10 +484,10 @@ __global__ __launch_bounds__(NTC) void k_bwd_chunk(BwdParams p) {
         for (int m = 0; m < CH; ++m) {
             const float tv = sm.m1[m][pr];
 #pragma unroll
-            for (int q = 0; q < QPT; ++q) a[q] += tv * sm.m2[m][pi0 + q];
+            for (int q = 0; q < QPT; ++q) a[q] += tv * sm.m2[m][pi0 + 8 * q];
         }
 #pragma unroll
-        for (int q = 0; q < QPT; ++q) sm.m3[pr][pi0 + q] = (pi0 + q < pr) ? -a[q] : 0.f;
+        for (int q = 0; q < QPT; ++q) sm.m3[pr][pi0 + 8 * q] = (pi0 + 8 * q < pr) ? -a[q] : 0.f;
         f32x4 b[RPT];
 #pragma unroll
         for (int e = 0; e < RPT; ++e) b[e] = zero4;
@@ -624,12 +514,12 @@ __global__ __launch_bounds__(NTC) void k_bwd_chunk(BwdParams p) {
         for (int d = 0; d < DK; d += 4) {
             const f32x4 kr = bf4(&sm.kb[pr][d]);
 #pragma unroll
-            for (int q = 0; q < QPT; ++q) kk[q] += dot4(kr, bf4(&sm.kb[pi0 + q][d]));
+            for (int q = 0; q < QPT; ++q) kk[q] += dot4(kr, bf4(&sm.kb[pi0 + 8 * q][d]));
         }
         float db = 0.f, dgr = 0.f;
 #pragma unroll
         for (int q = 0; q < QPT; ++q) {
-            const int i = pi0 + q;
+            const int i = pi0 + 8 * q;
             float G = 0.f;
             if (i < pr) {
                 const float ex = __expf(sm.gam[pr] - sm.gam[i]), da = sm.m3[pr][i];
@@ -715,10 +605,7 @@ int launch_bwd(const BwdParams& p, void* stream) {
         hipLaunchKernelGGL(k_bwd_prep, dim3(p.n_chunks, p.h_v), dim3(NT), 0, s, p);
         if ((e = launched())) return e;
     }
-    if (p.n_seqs > 0) {
-        hipLaunchKernelGGL(k_bwd_chain, dim3(8 * p.n_seqs, p.h_v), dim3(NT), 0, s, p);
-        if ((e = launched())) return e;
-    }
+    if ((e = launch_bwd_chain_mma(p, stream))) return e;
     if (p.n_chunks > 0) {
         hipLaunchKernelGGL(k_bwd_chunk, dim3(p.n_chunks, p.h_v), dim3(NTC), 0, s, p);
         if ((e = launched())) return e;

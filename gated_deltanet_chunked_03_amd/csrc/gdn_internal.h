@@ -60,6 +60,7 @@ enum IoType { kIoBf16 = 0, kIoF32 = 1 };
 // Backward pass (gdn_bwd.hip). Chunks are numbered sequence by sequence as in
 // the forward; states are [128][128] fp32 blocks in the API layout.
 constexpr int kBwdTpg = 2 * kChunk * kChunk + kChunk;   // floats per (chunk, head): T, P, gamma
+constexpr int kBwdTpt = 4 * kChunk * kChunk;            // bf16 per (chunk, head) in the T^T / P^T images
 
 struct BwdParams {
     const void* q;            // [tokens][h_qk][128] bf16
@@ -80,6 +81,8 @@ struct BwdParams {
     const float* cs;          // [n_chunks][h_v] state entering each chunk (from the forward)
     float* ds;                // [n_chunks][h_v] loss gradient of the state leaving each chunk
     float* tpg;               // [n_chunks][h_v] blocks of kBwdTpg floats: T, P (row-major 64 x 64), gamma
+    void* tpt;                // [n_chunks][h_v] bf16 images of T^T and scale P^T for the matrix-core
+                              // chain: [T^T hi, T^T lo, P^T hi, P^T lo] rows of 64, tokens in kp order
     float* dq_part;           // [tokens][h_v][128] per-value-head parts of dq and dk
     float* dk_part;
     int32_t n_seqs, seq_len, h_qk, h_v, group, n_chunks;
@@ -88,6 +91,7 @@ struct BwdParams {
 
 int launch_bwd(const BwdParams& p, void* stream);                       // prep, chain, chunk gradients
 int launch_bwd_sum(const BwdParams& p, long long n_tokens, void* stream);  // dq, dk group sums
+int launch_bwd_chain_mma(const BwdParams& p, void* stream);                // dS scan on matrix cores
 
 // Kernel launchers (gdn_kernels.hip). Return 0 or a hipError_t value.
 int launch_prep(const Params& p, int io, void* stream);

@@ -1626,6 +1626,225 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
     if (loc.s == loc.P - 1 && p.s_final) store_state(p.s_final + state_off(loc.seq, p.h_v, h), S);
 }
 
+// ----------------------------------------------------------------------------
+// Backward: the reverse scan of the state gradient dS over the chunks of one
+// sequence and value head on the matrix cores (the formulas are in
+// gdn_bwd.hip). Per chunk, with dS the gradient of the state leaving it:
+//   X   = diag(f) K dS + scale P^T dO          (dV'; K dS as the forward's K S)
+//   Z   = T^T X,  Y' = -diag(e^gamma beta) Z
+//   dS <- e^gamma_C dS + Q^T (scale diag(e^gamma) dO) + K^T Y'
+// Eight waves; wave w keeps columns [16w, 16w + 16) of dS in registers in the
+// forward's state layout, so dS, X, dO and Y' serve as MFMA operands directly
+// (tokens in kp order). T^T and scale P^T come as hi/lo images from the
+// backward prep; K (token-major, d_k in kp order), K^T and Q^T are staged as
+// in the forward. The next chunk's inputs are loaded during the current one.
+struct BwdChainSmem {
+    bf16 k_hi[CH * LDQ];                  // K token-major, d_k in kp order
+    bf16 kt[DK * LDKT];                   // K^T: row d_k, tokens in kp order (chunks swizzled)
+    bf16 qt[DK * LDKT];                   // Q^T, same layout
+    bf16 tt[2 * CH * LDP];                // T^T: hi rows, then lo rows; tokens in kp order
+    bf16 pt[2 * CH * LDP];                // scale P^T, same
+    float fr[CH];                         // exp(gamma_C - gamma)
+    float egb[CH];                        // -exp(gamma) beta
+    float egs[CH];                        // scale exp(gamma)
+    float ec;                             // exp(gamma_C)
+};
+
+struct BwdChainIn {
+    u32x2 k[4], q[4];                     // tokens 4 (t / 32) + j, d_k 4 (t % 32) .. + 3
+    u32x4 img[4];                         // pieces t + 512 j of the T^T / P^T images
+    unsigned d[16];                       // dO, this lane's 16 tokens x 1 column (raw bf16)
+    float gl, bl;                         // gamma, beta of token lane
+    int nv;                               // valid tokens of the chunk
+};
+
+__device__ void bwd_chain_fetch(const BwdParams& p, BwdChainIn& in, int f, size_t tok0, int nv, int h, int hq) {
+    const int t = threadIdx.x, m = t >> 5, c4 = (t & 31) * 4, lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const size_t ts = (size_t)p.h_qk * DK, ts_v = (size_t)p.h_v * DK;
+    const bf16* kb = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK + c4;
+    const bf16* qb = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK + c4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {   // rows past the end read the last row (their values never matter)
+        const int row = min(4 * m + j, nv - 1);
+        in.k[j] = *reinterpret_cast<const u32x2*>(kb + (size_t)row * ts);
+        in.q[j] = *reinterpret_cast<const u32x2*>(qb + (size_t)row * ts);
+    }
+    const u32x4* img = reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) in.img[j] = img[t + NTHR_CH * j];
+    // dO: tokens 16 rt + 4 g + e, column 16 w + c. Every load is issued (rows
+    // past the end read the last row) and zeroed afterwards: a conditional
+    // load would make the compiler drain every outstanding load at its branch.
+    const unsigned short* dob = reinterpret_cast<const unsigned short*>(p.dout) + tok0 * ts_v + (size_t)h * DK +
+                                16 * wave_id() + c;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) in.d[4 * rt + e] = dob[(size_t)min(16 * rt + 4 * g + e, nv - 1) * ts_v];
+    in.gl = p.tpg[((size_t)f * p.h_v + h) * kBwdTpg + 2 * CH * CH + lane];
+    in.bl = p.beta[(tok0 + min(lane, nv - 1)) * p.h_v + h];
+    in.nv = nv;   // (the masking waits for the loads: it happens when the chunk is staged)
+}
+
+__device__ void bwd_chain_stage(BwdChainSmem& sm, const BwdChainIn& in, float scale) {
+    const int t = threadIdx.x, lane = lane_id(), m = t >> 5, c4 = (t & 31) * 4;
+    {   // every wave writes the same values
+        const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, in.gl), 63));
+        const float es = __expf(in.gl);
+        sm.fr[lane] = __expf(gc - in.gl);
+        sm.egb[lane] = lane < in.nv ? -es * in.bl : 0.f;
+        sm.egs[lane] = es * scale;
+        sm.ec = __expf(gc);
+    }
+    const int kc = kp(c4), tk = kp(4 * m) ^ tswz(c4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(sm.k_hi + (4 * m + j) * LDQ + kc) = in.k[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<u32x2*>(sm.kt + (c4 + e) * LDKT + tk) = pack_col4(in.k, e);
+        *reinterpret_cast<u32x2*>(sm.qt + (c4 + e) * LDKT + tk) = pack_col4(in.q, e);
+    }
+    // images: piece idx -> part idx / 512 (T hi, T lo, P hi, P lo), row (idx / 8) % 64, 8 elements at 8 (idx % 8)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int idx = t + NTHR_CH * j, part = idx >> 9, row = (idx >> 3) & 63, k8 = (idx & 7) * 8;
+        bf16* dst = (part < 2 ? sm.tt : sm.pt) + ((part & 1) * CH + row) * LDP + k8;
+        *reinterpret_cast<u32x4*>(dst) = in.img[j];
+    }
+}
+
+__global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
+    __shared__ BwdChainSmem sm;
+    const int seq = blockIdx.x, h = blockIdx.y, hq = h / p.group;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    int cbase, N, len;
+    size_t tok_s;
+    if (!p.cu) {
+        len = p.seq_len;
+        N = n_chunks_of(len);
+        cbase = seq * N;
+        tok_s = (size_t)seq * p.seq_len;
+    } else {
+        cbase = 0;
+        for (int n = 0; n < seq; ++n) cbase += n_chunks_of(p.cu[n + 1] - p.cu[n]);
+        len = p.cu[seq + 1] - p.cu[seq];
+        N = n_chunks_of(len);
+        tok_s = (size_t)p.cu[seq];
+    }
+    f32x4 D[8];
+    if (p.dfinal) load_state(p.dfinal + state_off(seq, p.h_v, h), D);
+    else zero_state(D);
+    BwdChainIn in;
+    if (N > 0) bwd_chain_fetch(p, in, cbase + N - 1, tok_s + (size_t)(N - 1) * CH, min(CH, len - (N - 1) * CH), h, hq);
+    for (int cc = N - 1; cc >= 0; --cc) {
+        // stage first: its wait then covers the prefetched loads only, not the
+        // stores below (loads and stores share one counter)
+        bwd_chain_stage(sm, in, p.scale);
+        store_state(p.ds + state_off(cbase + cc, p.h_v, h), D);   // gradient of the state leaving chunk cc
+        unsigned dO[8];   // this lane's dO tokens as bf16 pairs, rows past the end zero
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r0 = 16 * (i >> 1) + 4 * g + 2 * (i & 1);
+            const unsigned lo = r0 < in.nv ? in.d[2 * i] : 0u, hi = r0 + 1 < in.nv ? in.d[2 * i + 1] : 0u;
+            dO[i] = lo | (hi << 16);
+        }
+        __syncthreads();
+        if (cc > 0)
+            bwd_chain_fetch(p, in, cbase + cc - 1, tok_s + (size_t)(cc - 1) * CH, min(CH, len - (cc - 1) * CH), h, hq);
+        // X = diag(f) K dS + scale P^T dO
+        f32x4 X[4];
+        {
+            SplitS ss;
+            split_state(D, ss);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) X[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 kh[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) kh[rt] = lds_op16(sm.k_hi + (16 * rt + c) * LDQ + 32 * s + 8 * g);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) X[rt] = mma16k32(kh[rt], ss.hi[s], X[rt]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) X[rt] = mma16k32(kh[rt], ss.lo[s], X[rt]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) X[rt] *= *reinterpret_cast<const f32x4*>(sm.fr + 16 * rt + 4 * g);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dO[4 * s], dO[4 * s + 1], dO[4 * s + 2], dO[4 * s + 3]});
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (s == 0 && rt >= 2) continue;   // P^T[r][m] = 0 for m < r
+                const bf16x8 ph = lds_op16(sm.pt + (16 * rt + c) * LDP + 32 * s + 8 * g);
+                const bf16x8 pl = lds_op16(sm.pt + (CH + 16 * rt + c) * LDP + 32 * s + 8 * g);
+                X[rt] = mma16k32(ph, db, X[rt]);
+                X[rt] = mma16k32(pl, db, X[rt]);
+            }
+        }
+        // Z = T^T X, then Y' = -diag(e^gamma beta) Z
+        f32x4 Z[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) Z[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 xh, xl;
+            split8(X[2 * s], X[2 * s + 1], xh, xl);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (s == 0 && rt >= 2) continue;   // T^T[r][m] = 0 for m < r
+                const bf16x8 th = lds_op16(sm.tt + (16 * rt + c) * LDP + 32 * s + 8 * g);
+                const bf16x8 tl = lds_op16(sm.tt + (CH + 16 * rt + c) * LDP + 32 * s + 8 * g);
+                Z[rt] = mma16k32(th, xh, Z[rt]);
+                Z[rt] = mma16k32(th, xl, Z[rt]);
+                Z[rt] = mma16k32(tl, xh, Z[rt]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) Z[rt] *= *reinterpret_cast<const f32x4*>(sm.egb + 16 * rt + 4 * g);
+        // dS <- e^gamma_C dS + Q^T (scale e^gamma dO) + K^T Y'
+        {
+            const float ec = sm.ec;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) D[i] *= ec;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            f32x4 o0, o1;
+            {
+                const f32x4 e0 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 4 * g);
+                const f32x4 e1 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 16 + 4 * g);
+                const unsigned a0 = dO[4 * s], a1 = dO[4 * s + 1], b0 = dO[4 * s + 2], b1 = dO[4 * s + 3];
+                o0 = f32x4{__uint_as_float(a0 << 16), __uint_as_float(a0 & 0xffff0000u),
+                           __uint_as_float(a1 << 16), __uint_as_float(a1 & 0xffff0000u)} * e0;
+                o1 = f32x4{__uint_as_float(b0 << 16), __uint_as_float(b0 & 0xffff0000u),
+                           __uint_as_float(b1 << 16), __uint_as_float(b1 & 0xffff0000u)} * e1;
+            }
+            bf16x8 oh, ol, yh, yl;
+            split8(o0, o1, oh, ol);
+            split8(Z[2 * s], Z[2 * s + 1], yh, yl);
+            bf16x8 qh[8], kh[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int off = (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i));
+                qh[i] = lds_op16(sm.qt + off);
+                kh[i] = lds_op16(sm.kt + off);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) D[i] = mma16k32(qh[i], oh, D[i]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) D[i] = mma16k32(qh[i], ol, D[i]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) D[i] = mma16k32(kh[i], yh, D[i]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) D[i] = mma16k32(kh[i], yl, D[i]);
+        }
+        __syncthreads();
+    }
+    if (p.dinit) store_state(p.dinit + state_off(seq, p.h_v, h), D);
+}
+
 // Per (sequence, head) summary of the boundary choices, over the boundaries
 // whose warm-up window does not reach the sequence start: 1 all warm-up,
 // 0 all exact, 2 mixed, 3 no such boundary; -1 the sequence was not split.
@@ -1850,6 +2069,12 @@ int launch_decode(const Params& p, int io, void* stream) {
     const dim3 grid(p.n_seqs, p.h_v), block(NTHR);
     if (io == kIoBf16) hipLaunchKernelGGL(k_decode<bf16>, grid, block, 0, (hipStream_t)stream, p);
     else hipLaunchKernelGGL(k_decode<float>, grid, block, 0, (hipStream_t)stream, p);
+    return launched();
+}
+
+int launch_bwd_chain_mma(const BwdParams& p, void* stream) {
+    if (p.n_seqs <= 0) return 0;
+    hipLaunchKernelGGL(k_bwd_chain_mma, dim3(p.n_seqs, p.h_v), dim3(NTHR_CH), 0, (hipStream_t)stream, p);
     return launched();
 }
 
