@@ -445,6 +445,15 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     b.tpt = w8 + L.off_tpt;
     b.dq_part = reinterpret_cast<float*>(w8 + L.off_dq);
     b.dk_part = reinterpret_cast<float*>(w8 + L.off_dk);
+    // the state-gradient scan splits the sequences as the forward did; the
+    // forward's segment arrays are free once its re-run has finished
+    b.L = P.cp_on ? P.L : std::max(P.n_chunks_max, 1);
+    b.n_segments = P.cp_on ? P.n_segments : P.n_seqs;
+    if (P.cp_on) {
+        b.seg_state = reinterpret_cast<float*>(w8 + P.off_state);
+        b.seg_M = reinterpret_cast<float*>(w8 + P.off_M);
+        b.seg_H = reinterpret_cast<float*>(w8 + P.off_H);
+    }
     b.n_seqs = P.n_seqs;
     b.seq_len = desc->T;
     b.h_qk = desc->h_qk;

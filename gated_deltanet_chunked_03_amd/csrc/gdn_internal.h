@@ -85,6 +85,11 @@ struct BwdParams {
                               // chain: [T^T hi, T^T lo, P^T hi, P^T lo] rows of 64, tokens in kp order
     float* dq_part;           // [tokens][h_v][128] per-value-head parts of dq and dk
     float* dk_part;
+    // segments of the state-gradient scan (the forward's plan); seg_state null: one per sequence
+    float* seg_state;         // [n_segments][h_v] gradient of the state leaving segment s (s < P - 1)
+    float* seg_M;             // [n_segments][h_v] map of segment s >= 1 (gradient at its end -> at its start)
+    float* seg_H;             // [n_segments][h_v] the scan of segment s >= 1 from zero (last: from dS_final)
+    int32_t L, n_segments;    // chunks per segment, segments over all sequences
     int32_t n_seqs, seq_len, h_qk, h_v, group, n_chunks;
     float scale;
 };

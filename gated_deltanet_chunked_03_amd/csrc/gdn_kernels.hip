@@ -202,7 +202,8 @@ struct SegLoc {
 __device__ __forceinline__ int n_chunks_of(int len) { return (len + CH - 1) / CH; }
 __device__ __forceinline__ int n_segs_of(int N, int L) { return N == 0 ? 1 : (N + L - 1) / L; }
 
-__device__ SegLoc locate_segment(const Params& p, int slot) {
+template <typename PP>
+__device__ SegLoc locate_segment(const PP& p, int slot) {
     SegLoc o;
     o.seq = -1;
     o.s = o.P = o.N = o.len = o.seg_base = o.chunk_base = 0;
@@ -1713,44 +1714,34 @@ __device__ void bwd_chain_stage(BwdChainSmem& sm, const BwdChainIn& in, float sc
     }
 }
 
-__global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
-    __shared__ BwdChainSmem sm;
-    const int seq = blockIdx.x, h = blockIdx.y, hq = h / p.group;
-    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
-    int cbase, N, len;
-    size_t tok_s;
-    if (!p.cu) {
-        len = p.seq_len;
-        N = n_chunks_of(len);
-        cbase = seq * N;
-        tok_s = (size_t)seq * p.seq_len;
-    } else {
-        cbase = 0;
-        for (int n = 0; n < seq; ++n) cbase += n_chunks_of(p.cu[n + 1] - p.cu[n]);
-        len = p.cu[seq + 1] - p.cu[seq];
-        N = n_chunks_of(len);
-        tok_s = (size_t)p.cu[seq];
-    }
-    f32x4 D[8];
-    if (p.dfinal) load_state(p.dfinal + state_off(seq, p.h_v, h), D);
-    else zero_state(D);
+// The scan over chunks [c_lo, c_hi) of one sequence, from D (the gradient of
+// the state leaving chunk c_hi - 1). WANT_DO: the output terms (P^T dO and
+// Q^T dO'); without them the scan applies the homogeneous map only.
+// WRITE_DS: store the gradient of the state leaving every chunk.
+template <bool WANT_DO, bool WRITE_DS>
+__device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc& loc, int c_lo, int c_hi, int h,
+                              f32x4 D[8]) {
+    const int hq = h / p.group, lane = lane_id(), c = lane & 15, g = lane >> 4;
     BwdChainIn in;
-    if (N > 0) bwd_chain_fetch(p, in, cbase + N - 1, tok_s + (size_t)(N - 1) * CH, min(CH, len - (N - 1) * CH), h, hq);
-    for (int cc = N - 1; cc >= 0; --cc) {
+    auto fetch = [&](int cc) {
+        bwd_chain_fetch(p, in, loc.chunk_base + cc, loc.tok0 + (size_t)cc * CH, min(CH, loc.len - cc * CH), h, hq);
+    };
+    if (c_lo < c_hi) fetch(c_hi - 1);
+    for (int cc = c_hi - 1; cc >= c_lo; --cc) {
         // stage first: its wait then covers the prefetched loads only, not the
         // stores below (loads and stores share one counter)
         bwd_chain_stage(sm, in, p.scale);
-        store_state(p.ds + state_off(cbase + cc, p.h_v, h), D);   // gradient of the state leaving chunk cc
+        if (WRITE_DS) store_state(p.ds + state_off(loc.chunk_base + cc, p.h_v, h), D);
         unsigned dO[8];   // this lane's dO tokens as bf16 pairs, rows past the end zero
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r0 = 16 * (i >> 1) + 4 * g + 2 * (i & 1);
-            const unsigned lo = r0 < in.nv ? in.d[2 * i] : 0u, hi = r0 + 1 < in.nv ? in.d[2 * i + 1] : 0u;
+            const unsigned lo = (WANT_DO && r0 < in.nv) ? in.d[2 * i] : 0u;
+            const unsigned hi = (WANT_DO && r0 + 1 < in.nv) ? in.d[2 * i + 1] : 0u;
             dO[i] = lo | (hi << 16);
         }
         __syncthreads();
-        if (cc > 0)
-            bwd_chain_fetch(p, in, cbase + cc - 1, tok_s + (size_t)(cc - 1) * CH, min(CH, len - (cc - 1) * CH), h, hq);
+        if (cc > c_lo) fetch(cc - 1);
         // X = diag(f) K dS + scale P^T dO
         f32x4 X[4];
         {
@@ -1771,16 +1762,18 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) X[rt] *= *reinterpret_cast<const f32x4*>(sm.fr + 16 * rt + 4 * g);
+        if (WANT_DO) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dO[4 * s], dO[4 * s + 1], dO[4 * s + 2], dO[4 * s + 3]});
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dO[4 * s], dO[4 * s + 1], dO[4 * s + 2], dO[4 * s + 3]});
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                if (s == 0 && rt >= 2) continue;   // P^T[r][m] = 0 for m < r
-                const bf16x8 ph = lds_op16(sm.pt + (16 * rt + c) * LDP + 32 * s + 8 * g);
-                const bf16x8 pl = lds_op16(sm.pt + (CH + 16 * rt + c) * LDP + 32 * s + 8 * g);
-                X[rt] = mma16k32(ph, db, X[rt]);
-                X[rt] = mma16k32(pl, db, X[rt]);
+                for (int rt = 0; rt < 4; ++rt) {
+                    if (s == 0 && rt >= 2) continue;   // P^T[r][m] = 0 for m < r
+                    const bf16x8 ph = lds_op16(sm.pt + (16 * rt + c) * LDP + 32 * s + 8 * g);
+                    const bf16x8 pl = lds_op16(sm.pt + (CH + 16 * rt + c) * LDP + 32 * s + 8 * g);
+                    X[rt] = mma16k32(ph, db, X[rt]);
+                    X[rt] = mma16k32(pl, db, X[rt]);
+                }
             }
         }
         // Z = T^T X, then Y' = -diag(e^gamma beta) Z
@@ -1811,30 +1804,34 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            f32x4 o0, o1;
-            {
-                const f32x4 e0 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 4 * g);
-                const f32x4 e1 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 16 + 4 * g);
-                const unsigned a0 = dO[4 * s], a1 = dO[4 * s + 1], b0 = dO[4 * s + 2], b1 = dO[4 * s + 3];
-                o0 = f32x4{__uint_as_float(a0 << 16), __uint_as_float(a0 & 0xffff0000u),
-                           __uint_as_float(a1 << 16), __uint_as_float(a1 & 0xffff0000u)} * e0;
-                o1 = f32x4{__uint_as_float(b0 << 16), __uint_as_float(b0 & 0xffff0000u),
-                           __uint_as_float(b1 << 16), __uint_as_float(b1 & 0xffff0000u)} * e1;
-            }
-            bf16x8 oh, ol, yh, yl;
-            split8(o0, o1, oh, ol);
+            bf16x8 yh, yl;
             split8(Z[2 * s], Z[2 * s + 1], yh, yl);
-            bf16x8 qh[8], kh[8];
+            bf16x8 kh[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int off = (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i));
-                qh[i] = lds_op16(sm.qt + off);
-                kh[i] = lds_op16(sm.kt + off);
+            for (int i = 0; i < 8; ++i)
+                kh[i] = lds_op16(sm.kt + (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i)));
+            if (WANT_DO) {
+                f32x4 o0, o1;
+                {
+                    const f32x4 e0 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 4 * g);
+                    const f32x4 e1 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 16 + 4 * g);
+                    const unsigned a0 = dO[4 * s], a1 = dO[4 * s + 1], b0 = dO[4 * s + 2], b1 = dO[4 * s + 3];
+                    o0 = f32x4{__uint_as_float(a0 << 16), __uint_as_float(a0 & 0xffff0000u),
+                               __uint_as_float(a1 << 16), __uint_as_float(a1 & 0xffff0000u)} * e0;
+                    o1 = f32x4{__uint_as_float(b0 << 16), __uint_as_float(b0 & 0xffff0000u),
+                               __uint_as_float(b1 << 16), __uint_as_float(b1 & 0xffff0000u)} * e1;
+                }
+                bf16x8 oh, ol;
+                split8(o0, o1, oh, ol);
+                bf16x8 qh[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    qh[i] = lds_op16(sm.qt + (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i)));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) D[i] = mma16k32(qh[i], oh, D[i]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) D[i] = mma16k32(qh[i], ol, D[i]);
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) D[i] = mma16k32(qh[i], oh, D[i]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) D[i] = mma16k32(qh[i], ol, D[i]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) D[i] = mma16k32(kh[i], yh, D[i]);
 #pragma unroll
@@ -1842,7 +1839,121 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
         }
         __syncthreads();
     }
-    if (p.dinit) store_state(p.dinit + state_off(seq, p.h_v, h), D);
+}
+
+// MODE kBwdWhole: one workgroup per (sequence, head) over all its chunks.
+// With segments (the forward's plan): kBwdMaps, per (segment s >= 1, part,
+// head): part 0 scans the segment from zero (from dS_final for the last
+// segment) into seg_H[s], part 1 from the identity without output terms into
+// seg_M[s] (the segment's map, not needed for the last); kBwdRerun, per
+// (segment, head): the scan from the gradient at the segment's end (seg_state
+// from the linking pass, dS_final for the last), writing every chunk's.
+enum { kBwdWhole = 0, kBwdMaps = 1, kBwdRerun = 2 };
+
+template <int MODE>
+__global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
+    __shared__ BwdChainSmem sm;
+    const int h = blockIdx.y;
+    f32x4 D[8];
+    if (MODE == kBwdWhole) {
+        const SegLoc loc = locate_segment(p, blockIdx.x);   // (L covers the longest sequence: one segment each)
+        if (loc.seq < 0) return;
+        if (p.dfinal) load_state(p.dfinal + state_off(loc.seq, p.h_v, h), D);
+        else zero_state(D);
+        bwd_chain_run<true, true>(p, sm, loc, 0, loc.N, h, D);
+        if (p.dinit) store_state(p.dinit + state_off(loc.seq, p.h_v, h), D);
+    } else if (MODE == kBwdMaps) {
+        const int part = blockIdx.x & 1;
+        const SegLoc loc = locate_segment(p, blockIdx.x >> 1);
+        if (loc.seq < 0 || loc.s == 0) return;
+        const bool last = loc.s == loc.P - 1;
+        if (part == 1 && last) return;
+        const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
+        if (part == 0) {
+            if (last && p.dfinal) load_state(p.dfinal + state_off(loc.seq, p.h_v, h), D);
+            else zero_state(D);
+            bwd_chain_run<true, false>(p, sm, loc, c0, c1, h, D);
+            store_state(p.seg_H + state_off(loc.seg_base + loc.s, p.h_v, h), D);
+        } else {
+            identity_state(D);
+            bwd_chain_run<false, false>(p, sm, loc, c0, c1, h, D);
+            store_state(p.seg_M + state_off(loc.seg_base + loc.s, p.h_v, h), D);
+        }
+    } else {
+        const SegLoc loc = locate_segment(p, blockIdx.x);
+        if (loc.seq < 0) return;
+        if (loc.s == loc.P - 1) {
+            if (p.dfinal) load_state(p.dfinal + state_off(loc.seq, p.h_v, h), D);
+            else zero_state(D);
+        } else {
+            load_state(p.seg_state + state_off(loc.seg_base + loc.s, p.h_v, h), D);
+        }
+        const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
+        bwd_chain_run<true, true>(p, sm, loc, c0, c1, h, D);
+        if (loc.s == 0 && p.dinit) store_state(p.dinit + state_off(loc.seq, p.h_v, h), D);
+    }
+}
+
+// Links the segment ends of one sequence and head: with G(s) the gradient of
+// the state leaving segment s, G(P - 2) = seg_H[P - 1] and
+// G(s - 1) = seg_M[s] G(s) + seg_H[s] for s = P - 2 .. 1, into seg_state[s - 1].
+// Each map is staged in LDS split hi/lo with its columns in kp order (the
+// MFMA's A operand); the next map and H are loaded while a step computes.
+__global__ __launch_bounds__(NTHR_CH) void k_bwd_link(BwdParams p) {
+    __shared__ bf16 mh[DK * LDQ], ml[DK * LDQ];
+    const int seq = blockIdx.x, h = blockIdx.y, lane = lane_id(), c = lane & 15, g = lane >> 4, t = threadIdx.x;
+    int P, seg_base;
+    if (!p.cu) {
+        P = n_segs_of(n_chunks_of(p.seq_len), p.L);
+        seg_base = seq * P;
+    } else {
+        seg_base = 0;
+        for (int n = 0; n < seq; ++n) seg_base += n_segs_of(n_chunks_of(p.cu[n + 1] - p.cu[n]), p.L);
+        P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
+    }
+    if (P < 2) return;
+    f32x4 D[8], mreg[8], hreg[8];
+    auto fetch = [&](int s) {
+        const float* M = p.seg_M + state_off(seg_base + s, p.h_v, h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mreg[j] = *reinterpret_cast<const f32x4*>(M + 4 * (t + NTHR_CH * j));
+        load_state(p.seg_H + state_off(seg_base + s, p.h_v, h), hreg);
+    };
+    load_state(p.seg_H + state_off(seg_base + P - 1, p.h_v, h), D);
+    store_state(p.seg_state + state_off(seg_base + P - 2, p.h_v, h), D);
+    if (P >= 3) fetch(P - 2);
+    for (int s = P - 2; s >= 1; --s) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {   // piece t + 512 j: row (t + 512 j) / 32, columns 4 ((t + 512 j) % 32) .. + 3
+            const int idx = t + NTHR_CH * j, row = idx >> 5, col = kp((idx & 31) * 4);
+            bf16x4 hi, lo;
+            split4(mreg[j], hi, lo);
+            *reinterpret_cast<bf16x4*>(mh + row * LDQ + col) = hi;
+            *reinterpret_cast<bf16x4*>(ml + row * LDQ + col) = lo;
+        }
+        f32x4 H[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) H[i] = hreg[i];
+        __syncthreads();
+        if (s > 1) fetch(s - 1);
+        SplitS ss;
+        split_state(D, ss);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int off = (16 * i + c) * LDQ + 32 * ks + 8 * g;
+                const bf16x8 ah = lds_op16(mh + off), al = lds_op16(ml + off);
+                H[i] = mma16k32(ah, ss.hi[ks], H[i]);
+                H[i] = mma16k32(ah, ss.lo[ks], H[i]);
+                H[i] = mma16k32(al, ss.hi[ks], H[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) D[i] = H[i];
+        store_state(p.seg_state + state_off(seg_base + s - 1, p.h_v, h), D);
+        __syncthreads();
+    }
 }
 
 // Per (sequence, head) summary of the boundary choices, over the boundaries
@@ -2073,8 +2184,18 @@ int launch_decode(const Params& p, int io, void* stream) {
 }
 
 int launch_bwd_chain_mma(const BwdParams& p, void* stream) {
-    if (p.n_seqs <= 0) return 0;
-    hipLaunchKernelGGL(k_bwd_chain_mma, dim3(p.n_seqs, p.h_v), dim3(NTHR_CH), 0, (hipStream_t)stream, p);
+    const hipStream_t s = (hipStream_t)stream;
+    if (p.n_segments <= 0) return 0;
+    if (!p.seg_state) {   // one segment per sequence
+        hipLaunchKernelGGL(k_bwd_chain_mma<kBwdWhole>, dim3(p.n_segments, p.h_v), dim3(NTHR_CH), 0, s, p);
+        return launched();
+    }
+    hipLaunchKernelGGL(k_bwd_chain_mma<kBwdMaps>, dim3(2 * p.n_segments, p.h_v), dim3(NTHR_CH), 0, s, p);
+    int e = launched();
+    if (e) return e;
+    hipLaunchKernelGGL(k_bwd_link, dim3(p.n_seqs, p.h_v), dim3(NTHR_CH), 0, s, p);
+    if ((e = launched())) return e;
+    hipLaunchKernelGGL(k_bwd_chain_mma<kBwdRerun>, dim3(p.n_segments, p.h_v), dim3(NTHR_CH), 0, s, p);
     return launched();
 }
 
