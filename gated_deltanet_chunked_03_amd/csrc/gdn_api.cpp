@@ -275,7 +275,8 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
 gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, float scale, const float* s_init, const int32_t* cu, void* out,
                    float* s_final, void* ws, size_t ws_bytes, void* stream, float* seg_out,
-                   int32_t* path_out, float* chunk_states = nullptr) {
+                   int32_t* path_out, float* chunk_states = nullptr, float* bwd_y = nullptr,
+                   float* bwd_vp = nullptr, float* bwd_oi = nullptr) {
     Plan P;
     gdn_status st = make_plan(d, &P);
     if (st != GDN_OK) return st;
@@ -329,6 +330,9 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
         prof_mark(3, hs);
     }
     p.chunk_states = chunk_states;
+    p.bwd_y = bwd_y;
+    p.bwd_vp = bwd_vp;
+    p.bwd_oi = bwd_oi;
     if ((e = chunk_states ? gdn::launch_fwd_states(p, io, stream) : gdn::launch_fwd(p, io, stream)))
         return fail(GDN_ERR_HIP, "fwd launch: %s", hipGetErrorString((hipError_t)e));
     prof_mark(4, hs);
@@ -368,10 +372,13 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
 
 // Workspace of the backward: the forward's (for its re-run), then the re-run's
 // output, the state entering every chunk, the gradient of the state leaving
-// every chunk, T / P / gamma per chunk and head (fp32, and T^T / scale P^T as
-// bf16 hi/lo images), and the per-value-head parts of dq and dk.
+// every chunk, T / P / gamma per chunk and head (fp32, and T^T / scale P^T / T
+// as bf16 hi/lo images), per chunk and head Y, V', scale e^gamma Q S (from the
+// re-run) and dV', T^T dV' (from the state-gradient scan), and the
+// per-value-head parts of dq and dk.
 struct BwdLayout {
     size_t off_o = 0, off_cs = 0, off_ds = 0, off_tpg = 0, off_tpt = 0, off_dq = 0, off_dk = 0, bytes = 0;
+    size_t off_y = 0, off_vp = 0, off_oi = 0, off_dvp = 0, off_z = 0;
     size_t tokens = 0;
 };
 
@@ -385,6 +392,12 @@ BwdLayout bwd_layout(const gdn_desc* d, const Plan& P) {
     L.off_ds = off;  off = align_up(off + st, 256);
     L.off_tpg = off; off = align_up(off + (size_t)P.n_chunks_total * d->h_v * gdn::kBwdTpg * sizeof(float), 256);
     L.off_tpt = off; off = align_up(off + (size_t)P.n_chunks_total * d->h_v * gdn::kBwdTpt * 2, 256);
+    const size_t blk = (size_t)P.n_chunks_total * d->h_v * gdn::kChunk * gdn::kDim * sizeof(float);
+    L.off_y = off;   off = align_up(off + blk, 256);
+    L.off_vp = off;  off = align_up(off + blk, 256);
+    L.off_oi = off;  off = align_up(off + blk, 256);
+    L.off_dvp = off; off = align_up(off + blk, 256);
+    L.off_z = off;   off = align_up(off + blk, 256);
     L.off_dq = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
     L.off_dk = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
     L.bytes = off;
@@ -433,7 +446,9 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     // the forward again, keeping the state entering every chunk
     if (P.n_chunks_total > 0) {
         st = run_fwd(desc, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8 + L.off_o, nullptr, workspace,
-                     P.ws_bytes, stream, nullptr, nullptr, reinterpret_cast<float*>(w8 + L.off_cs));
+                     P.ws_bytes, stream, nullptr, nullptr, reinterpret_cast<float*>(w8 + L.off_cs),
+                     reinterpret_cast<float*>(w8 + L.off_y), reinterpret_cast<float*>(w8 + L.off_vp),
+                     reinterpret_cast<float*>(w8 + L.off_oi));
         if (st != GDN_OK) return st;
     }
     gdn::BwdParams b{};
@@ -443,6 +458,11 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     b.ds = reinterpret_cast<float*>(w8 + L.off_ds);
     b.tpg = reinterpret_cast<float*>(w8 + L.off_tpg);
     b.tpt = w8 + L.off_tpt;
+    b.y = reinterpret_cast<const float*>(w8 + L.off_y);
+    b.vp = reinterpret_cast<const float*>(w8 + L.off_vp);
+    b.oi = reinterpret_cast<const float*>(w8 + L.off_oi);
+    b.dvp = reinterpret_cast<float*>(w8 + L.off_dvp);
+    b.z = reinterpret_cast<float*>(w8 + L.off_z);
     b.dq_part = reinterpret_cast<float*>(w8 + L.off_dq);
     b.dk_part = reinterpret_cast<float*>(w8 + L.off_dk);
     // the state-gradient scan splits the sequences as the forward did; the

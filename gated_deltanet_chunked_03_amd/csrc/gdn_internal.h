@@ -38,6 +38,9 @@ struct Params {
     int32_t prep_cpw;         // (head, chunk) items per k_prep workgroup
     float* sink;              // 8 KiB scratch line for stores of rows past a sequence's end
     float* chunk_states;      // [n_chunks][h_v][128][128] state entering each chunk (backward recompute)
+    float* bwd_y;             // with chunk_states: per (chunk, head) [64][128] fp32 Y = V - diag(e^gamma) K S,
+    float* bwd_vp;            //   V', and scale diag(e^gamma) Q S
+    float* bwd_oi;
     // low-level chunk-prep outputs
     float* prep_gamma;        // [n_chunks][h_v][64]
     float* prep_W;            // [n_chunks][h_v][64][128]
@@ -60,7 +63,7 @@ enum IoType { kIoBf16 = 0, kIoF32 = 1 };
 // Backward pass (gdn_bwd.hip). Chunks are numbered sequence by sequence as in
 // the forward; states are [128][128] fp32 blocks in the API layout.
 constexpr int kBwdTpg = 2 * kChunk * kChunk + kChunk;   // floats per (chunk, head): T, P, gamma
-constexpr int kBwdTpt = 4 * kChunk * kChunk;            // bf16 per (chunk, head) in the T^T / P^T images
+constexpr int kBwdTpt = 6 * kChunk * kChunk;            // bf16 per (chunk, head) in the T^T / P^T / T images
 
 struct BwdParams {
     const void* q;            // [tokens][h_qk][128] bf16
@@ -81,8 +84,13 @@ struct BwdParams {
     const float* cs;          // [n_chunks][h_v] state entering each chunk (from the forward)
     float* ds;                // [n_chunks][h_v] loss gradient of the state leaving each chunk
     float* tpg;               // [n_chunks][h_v] blocks of kBwdTpg floats: T, P (row-major 64 x 64), gamma
-    void* tpt;                // [n_chunks][h_v] bf16 images of T^T and scale P^T for the matrix-core
-                              // chain: [T^T hi, T^T lo, P^T hi, P^T lo] rows of 64, tokens in kp order
+    void* tpt;                // [n_chunks][h_v] bf16 images for the matrix cores: [T^T hi, T^T lo,
+                              // scale P^T hi, lo, T hi, lo], rows of 64, contraction token in kp order
+    const float* y;           // [n_chunks][h_v][64][128] fp32 from the forward re-run: Y, V', scale e^gamma Q S
+    const float* vp;
+    const float* oi;
+    float* dvp;               // [n_chunks][h_v][64][128] fp32 from the state-gradient scan: dV', Z = T^T dV'
+    float* z;
     float* dq_part;           // [tokens][h_v][128] per-value-head parts of dq and dk
     float* dk_part;
     // segments of the state-gradient scan (the forward's plan); seg_state null: one per sequence
@@ -97,6 +105,7 @@ struct BwdParams {
 int launch_bwd(const BwdParams& p, void* stream);                       // prep, chain, chunk gradients
 int launch_bwd_sum(const BwdParams& p, long long n_tokens, void* stream);  // dq, dk group sums
 int launch_bwd_chain_mma(const BwdParams& p, void* stream);                // dS scan on matrix cores
+int launch_bwd_chunk_mma(const BwdParams& p, void* stream);                // chunk gradients on matrix cores
 
 // Kernel launchers (gdn_kernels.hip). Return 0 or a hipError_t value.
 int launch_prep(const Params& p, int io, void* stream);

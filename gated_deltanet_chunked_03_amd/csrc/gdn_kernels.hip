@@ -234,7 +234,8 @@ __device__ SegLoc locate_segment(const PP& p, int slot) {
 }
 
 // Chunk slot -> (sequence, chunk within it); returns false past the end.
-__device__ bool locate_chunk(const Params& p, int slot, int& seq, int& c, int& len, size_t& tok0) {
+template <typename PP>
+__device__ bool locate_chunk(const PP& p, int slot, int& seq, int& c, int& len, size_t& tok0) {
     if (!p.cu) {
         const int N = n_chunks_of(p.seq_len);
         if (N == 0) return false;
@@ -840,7 +841,7 @@ __device__ __forceinline__ void split_state(const f32x4 S[8], SplitS& ss) {
 // triangular: token tiles 0 and 1 need k step 0 only).
 template <typename IO, bool WANT_V>
 __device__ void chain_vp(const ChainSmem<Io<IO>::kExact>& sm, const SplitS& ss, const IO* vcol, size_t ts,
-                         int nvalid, f32x4 Vp[4]) {
+                         int nvalid, f32x4 Vp[4], f32x4* Yout = nullptr) {
     constexpr bool EX = Io<IO>::kExact;
     const int lane = lane_id(), c = lane & 15, g = lane >> 4, n = 16 * wave_id() + c;
     f32x4 KS[4];
@@ -882,6 +883,7 @@ __device__ void chain_vp(const ChainSmem<Io<IO>::kExact>& sm, const SplitS& ss, 
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) KS[rt][e] = fmaf(-eg[e], KS[rt][e], v[e]);
+        if (Yout) Yout[rt] = KS[rt];
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) Vp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1581,8 +1583,29 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
             const IO* vcol = static_cast<const IO*>(p.v) + tok0 * ts_v + (size_t)h * DK + 16 * wave + (lane_id() & 15);
             SplitS ss;
             split_state(S, ss);
-            chain_vp<IO, true>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp);
-            chain_qs<EX>(sm, ss, O);
+            if constexpr (ST) {
+                // for the backward: Y, V' (token rows) and scale e^gamma Q S (the
+                // output's state part, O^T tiles) of this chunk, fp32
+                f32x4 Y[4];
+                chain_vp<IO, true>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp, Y);
+                chain_qs<EX>(sm, ss, O);
+                const size_t blk = ((size_t)(loc.chunk_base + c) * p.h_v + h) * CH * DK;
+                const int l = lane_id(), cc = l & 15, g = l >> 4;
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const size_t o = blk + (size_t)(16 * rt + 4 * g + e) * DK + 16 * wave + cc;
+                        p.bwd_y[o] = Y[rt][e];
+                        p.bwd_vp[o] = Vp[rt][e];
+                    }
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    *reinterpret_cast<f32x4*>(p.bwd_oi + blk + (size_t)(16 * ct + cc) * DK + 16 * wave + 4 * g) = O[ct];
+            } else {
+                chain_vp<IO, true>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp);
+                chain_qs<EX>(sm, ss, O);
+            }
             gram_p<EX>(sm, p.scale);
         };
         auto out_part = [&](int c, const f32x4 Vp[4], f32x4 O[4]) {
@@ -1648,6 +1671,7 @@ struct BwdChainSmem {
     float fr[CH];                         // exp(gamma_C - gamma)
     float egb[CH];                        // -exp(gamma) beta
     float egs[CH];                        // scale exp(gamma)
+    float bet[CH];                        // beta (0 past the end)
     float ec;                             // exp(gamma_C)
 };
 
@@ -1694,6 +1718,7 @@ __device__ void bwd_chain_stage(BwdChainSmem& sm, const BwdChainIn& in, float sc
         const float es = __expf(in.gl);
         sm.fr[lane] = __expf(gc - in.gl);
         sm.egb[lane] = lane < in.nv ? -es * in.bl : 0.f;
+        sm.bet[lane] = lane < in.nv ? in.bl : 0.f;
         sm.egs[lane] = es * scale;
         sm.ec = __expf(gc);
     }
@@ -1731,6 +1756,7 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
         // stage first: its wait then covers the prefetched loads only, not the
         // stores below (loads and stores share one counter)
         bwd_chain_stage(sm, in, p.scale);
+        const int in_nv = in.nv;
         if (WRITE_DS) store_state(p.ds + state_off(loc.chunk_base + cc, p.h_v, h), D);
         unsigned dO[8];   // this lane's dO tokens as bf16 pairs, rows past the end zero
 #pragma unroll
@@ -1776,6 +1802,13 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
                 }
             }
         }
+        if (WRITE_DS) {   // dV' for the chunk gradients
+            float* xb = p.dvp + ((size_t)(loc.chunk_base + cc) * p.h_v + h) * CH * DK + 16 * wave_id() + c + 4 * g * DK;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xb[(16 * rt + e) * DK] = X[rt][e];
+        }
         // Z = T^T X, then Y' = -diag(e^gamma beta) Z
         f32x4 Z[4];
 #pragma unroll
@@ -1793,6 +1826,19 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
                 Z[rt] = mma16k32(th, xl, Z[rt]);
                 Z[rt] = mma16k32(tl, xh, Z[rt]);
             }
+        }
+        if (WRITE_DS) {   // for the chunk gradients: Z (fp32) and the output dv = diag(beta) Z
+            float* zb = p.z + ((size_t)(loc.chunk_base + cc) * p.h_v + h) * CH * DK + 16 * wave_id() + c + 4 * g * DK;
+            const unsigned ts_v = (unsigned)(p.h_v * DK);
+            bf16* dv = static_cast<bf16*>(p.dv) + (loc.tok0 + (size_t)cc * CH) * ts_v + (size_t)h * DK + 16 * wave_id() + c;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rt + 4 * g + e;
+                    zb[(16 * rt + e) * DK] = Z[rt][e];
+                    if (r < in_nv) dv[r * ts_v] = (bf16)(sm.bet[r] * Z[rt][e]);
+                }
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) Z[rt] *= *reinterpret_cast<const f32x4*>(sm.egb + 16 * rt + 4 * g);
@@ -1953,6 +1999,416 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_link(BwdParams p) {
         for (int i = 0; i < 8; ++i) D[i] = H[i];
         store_state(p.seg_state + state_off(seg_base + s - 1, p.h_v, h), D);
         __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Backward, every gradient of one (chunk, value head) on the matrix cores.
+// The forward re-run left Y, V' and scale e^gamma Q S of the chunk, the state
+// scan left dV', Z = T^T dV' (and dv); what remains contracts over d_v or
+// over the chunk's tokens (formulas in gdn_bwd.hip):
+//   dq = diag(scale e^gamma) dO S^T + Psi K
+//   dk = diag(f) V' dSn^T - diag(e^gamma) dY S^T + Psi^T Q + (G + G^T) K
+//   dP = scale dO V'^T -> Psi, dT = dV' (diag(beta) Y)^T -> W1 = dT T^T,
+//   dA = -T^T W1 -> G, and the dbeta / dgamma row and column sums.
+// Eight waves; wave w owns d_k columns [16w, 16w + 16) of dq and dk (all 64
+// tokens) and two of the sixteen 16x16 tiles of every 64 x 64 product (row
+// tile w / 2, column tiles 2 (w % 2) + 0, 1). Operands over d_v are read from
+// HBM / L2 straight into the kp order (two 16-byte loads per lane and k step);
+// K^T, Q^T and the 64 x 64 images (T, T^T, Psi, Psi^T, dT, W1^T, G, G^T; hi/lo
+// bf16) go through LDS.
+struct BwdChunkSmem {
+    bf16 kt[DK * LDKT];                   // K^T: row d_k, tokens in kp order (chunks swizzled)
+    bf16 qt[DK * LDKT];                   // Q^T, same layout
+    bf16 tim[2 * CH * LDP];               // T: rows r, tokens in kp order; hi rows, then lo rows
+    bf16 ttim[2 * CH * LDP];              // T^T
+    bf16 sa[2 * CH * LDP];                // Psi, then G
+    bf16 sb[2 * CH * LDP];                // Psi^T, then G^T
+    bf16 sc[2 * CH * LDP];                // dT, then W1^T
+    float gam[CH], eg[CH], fr[CH], bet[CH], dgam[CH], dbe[CH];
+    float dgc;
+};
+
+__device__ __forceinline__ float dot4v(f32x4 a, f32x4 b) { return (a[0] * b[0] + a[1] * b[1]) + (a[2] * b[2] + a[3] * b[3]); }
+// Eight consecutive kp positions 32 ks + 8 g .. of an fp32 row (two 16-byte
+// loads), times s, split hi/lo; and of a bf16 row (two 8-byte loads).
+__device__ __forceinline__ void kp_op_f32(const float* row, int ks, int g, float s, bf16x8& hi, bf16x8& lo) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + 32 * ks + 4 * g);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + 32 * ks + 16 + 4 * g);
+    split8(a * s, b * s, hi, lo);
+}
+__device__ __forceinline__ bf16x8 kp_op_bf16(const bf16* row, int ks, int g, bool keep) {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(row + 32 * ks + 4 * g);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(row + 32 * ks + 16 + 4 * g);
+    const u32x4 v = keep ? u32x4{a[0], a[1], b[0], b[1]} : u32x4{0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(bf16x8, v);
+}
+// Accumulator element (row 16 rt + 4 g + e, column 16 ct + c) of a 64 x 64 tile
+// into an image: at [row][kp(col)] (scalar) or transposed at [col][kp(row)]
+// (the four rows of a lane are consecutive in kp order: one 8-byte store).
+__device__ __forceinline__ void put_img(bf16* img, int rt, int ct, int c, int g, const f32x4& x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16 hi, lo;
+        split1(x[e], hi, lo);
+        const int o = (16 * rt + 4 * g + e) * LDP + kp(16 * ct + c);
+        img[o] = hi;
+        img[CH * LDP + o] = lo;
+    }
+}
+__device__ __forceinline__ void put_img_t(bf16* img, int rt, int ct, int c, int g, const f32x4& x) {
+    bf16x4 hi, lo;
+    split4(x, hi, lo);
+    const int o = (16 * ct + c) * LDP + kp(16 * rt + 4 * g);
+    *reinterpret_cast<bf16x4*>(img + o) = hi;
+    *reinterpret_cast<bf16x4*>(img + CH * LDP + o) = lo;
+}
+// row sums of a 16x16 tile over its 16 columns (lanes c) and column sums over
+// its 16 rows (e, then lane groups g)
+__device__ __forceinline__ float tile_rowsum(float x) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+__device__ __forceinline__ float tile_colsum(const f32x4& x) {
+    float s = (x[0] + x[1]) + (x[2] + x[3]);
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    return s;
+}
+
+__global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
+    __shared__ BwdChunkSmem sm;
+    const int f = blockIdx.x, h = blockIdx.y, hq = h / p.group, t = threadIdx.x;
+    const int w = wave_id(), lane = lane_id(), c = lane & 15, g = lane >> 4;
+    int seq, cidx, len;
+    size_t tok_s;
+    if (!locate_chunk(p, f, seq, cidx, len, tok_s)) return;
+    const size_t tok0 = tok_s + (size_t)cidx * CH;
+    const int nv = min(CH, len - cidx * CH);
+    const size_t ts = (size_t)p.h_qk * DK, ts_v = (size_t)p.h_v * DK;
+    const size_t blk = ((size_t)f * p.h_v + h) * CH * DK;
+    const float* S = p.cs + state_off(f, p.h_v, h);
+    const float* dSn = p.ds + state_off(f, p.h_v, h);
+    const float* Yb = p.y + blk;
+    const float* Vpb = p.vp + blk;
+    const float* Oib = p.oi + blk;
+    const float* dVb = p.dvp + blk;
+    const float* Zb = p.z + blk;
+    const bf16* Kg = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK;
+    const bf16* Qg = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK;
+    const bf16* Vg = static_cast<const bf16*>(p.v) + tok0 * ts_v + (size_t)h * DK;
+    const bf16* dOg = static_cast<const bf16*>(p.dout) + tok0 * ts_v + (size_t)h * DK;
+    const float* tp = p.tpg + ((size_t)f * p.h_v + h) * kBwdTpg;
+    const float scale = p.scale;
+
+    // ---- staging: K^T, Q^T (rows past the end repeat the last; harmless, see the products), images, gates
+    {
+        const int m = t >> 5, c4 = (t & 31) * 4, tk = kp(4 * m) ^ tswz(c4);
+        u32x2 kk[4], qq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = min(4 * m + j, nv - 1);
+            kk[j] = *reinterpret_cast<const u32x2*>(Kg + (size_t)row * ts + c4);
+            qq[j] = *reinterpret_cast<const u32x2*>(Qg + (size_t)row * ts + c4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            *reinterpret_cast<u32x2*>(sm.kt + (c4 + e) * LDKT + tk) = pack_col4(kk, e);
+            *reinterpret_cast<u32x2*>(sm.qt + (c4 + e) * LDKT + tk) = pack_col4(qq, e);
+        }
+        const u32x4* img = reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt);
+        // pieces of the [T^T hi, T^T lo, P^T hi, P^T lo, T hi, T lo] image: parts 0, 1 and 4, 5
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int idx = t + NTHR_CH * j, part = idx >> 9, row = (idx >> 3) & 63, k8 = (idx & 7) * 8;
+            *reinterpret_cast<u32x4*>(sm.ttim + (part * CH + row) * LDP + k8) = img[idx];
+            *reinterpret_cast<u32x4*>(sm.tim + (part * CH + row) * LDP + k8) = img[idx + 2048];
+        }
+        if (t < CH) {
+            const float gm = tp[2 * CH * CH + t];
+            sm.gam[t] = gm;
+            sm.eg[t] = __expf(gm);
+            const float b = p.beta[(tok0 + min(t, nv - 1)) * p.h_v + h];
+            sm.bet[t] = t < nv ? b : 0.f;
+        }
+        if (t == 0) sm.dgc = 0.f;
+    }
+    __syncthreads();
+    if (t < CH) sm.fr[t] = __expf(sm.gam[CH - 1] - sm.gam[t]);
+    // ---- 1. row sums over d_v: thread t takes row t / 8, columns 16 (t % 8) .. + 15
+    {
+        const int r = t >> 3, c0 = (t & 7) * 16, rr = min(r, nv - 1);
+        const bool ok = r < nv;
+        float zb = 0.f, vy = 0.f, qo = 0.f;
+        const float br = sm.bet[r];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int col = c0 + 4 * q4;
+            const f32x4 y = *reinterpret_cast<const f32x4*>(Yb + (size_t)r * DK + col);
+            const f32x4 z = *reinterpret_cast<const f32x4*>(Zb + (size_t)r * DK + col);
+            const f32x4 oi = *reinterpret_cast<const f32x4*>(Oib + (size_t)r * DK + col);
+            const u32x2 vw = *reinterpret_cast<const u32x2*>(Vg + (size_t)rr * ts_v + col);
+            const u32x2 dw = *reinterpret_cast<const u32x2*>(dOg + (size_t)rr * ts_v + col);
+            const f32x4 v = {__uint_as_float(vw[0] << 16), __uint_as_float(vw[0] & 0xffff0000u),
+                             __uint_as_float(vw[1] << 16), __uint_as_float(vw[1] & 0xffff0000u)};
+            const f32x4 d = {__uint_as_float(dw[0] << 16), __uint_as_float(dw[0] & 0xffff0000u),
+                             __uint_as_float(dw[1] << 16), __uint_as_float(dw[1] & 0xffff0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                zb += z[e] * y[e];
+                vy += (v[e] - y[e]) * (br * z[e]);
+                qo += oi[e] * d[e];
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+            zb += __shfl_xor(zb, m, 64);
+            vy += __shfl_xor(vy, m, 64);
+            qo += __shfl_xor(qo, m, 64);
+        }
+        if ((t & 7) == 0) {
+            sm.dbe[r] = ok ? zb : 0.f;       // dbeta: Z . Y (through V' = T diag(beta) Y)
+            sm.dgam[r] = ok ? qo - vy : 0.f; // dgamma: the output's e^gamma Q S term, the e^gamma K S term of Y
+        }
+    }
+    __syncthreads();
+    // ---- 2. d_k-column products: dq = diag(scale e^gamma) dO S^T, dk = diag(f) V' dSn^T - diag(e^gamma) dY S^T
+    f32x4 dq[4], dk[4];
+    {
+        f32x4 aq[4], a1[4], a2[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) aq[rt] = a1[rt] = a2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const float* Srow = S + (size_t)(16 * w + c) * DK;
+        const float* Drow = dSn + (size_t)(16 * w + c) * DK;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 sh, sl, dh, dl;
+            kp_op_f32(Srow, ks, g, 1.f, sh, sl);
+            kp_op_f32(Drow, ks, g, 1.f, dh, dl);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int r = 16 * rt + c;
+                const bf16x8 ao = kp_op_bf16(dOg + (size_t)min(r, nv - 1) * ts_v, ks, g, r < nv);
+                aq[rt] = mma16k32(ao, sh, aq[rt]);
+                aq[rt] = mma16k32(ao, sl, aq[rt]);
+                bf16x8 vh, vl, yh, yl;
+                kp_op_f32(Vpb + (size_t)r * DK, ks, g, 1.f, vh, vl);
+                a1[rt] = mma16k32(vh, dh, a1[rt]);
+                a1[rt] = mma16k32(vh, dl, a1[rt]);
+                a1[rt] = mma16k32(vl, dh, a1[rt]);
+                kp_op_f32(Zb + (size_t)r * DK, ks, g, sm.bet[r], yh, yl);   // dY = diag(beta) Z
+                a2[rt] = mma16k32(yh, sh, a2[rt]);
+                a2[rt] = mma16k32(yh, sl, a2[rt]);
+                a2[rt] = mma16k32(yl, sh, a2[rt]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int r0 = 16 * rt + 4 * g;
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(sm.eg + r0);
+            const f32x4 fr = *reinterpret_cast<const f32x4*>(sm.fr + r0);
+            dq[rt] = (scale * eg) * aq[rt];
+            dk[rt] = fr * a1[rt] - eg * a2[rt];
+            // kappa_r = f_r K_r . dK~_r: through the decay factors of K~
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r0 + e;
+                const float kv = (float)Kg[(size_t)min(r, nv - 1) * ts + 16 * w + c];
+                const float kap = tile_rowsum(fr[e] * kv * a1[rt][e]);
+                if (c == 0 && r < nv) {
+                    atomicAdd(&sm.dgam[r], -kap);
+                    atomicAdd(&sm.dgc, kap);
+                }
+            }
+        }
+    }
+    // ---- 3. 64 x 64 tiles: dP -> Psi (images), dT (image), K K^T (kept)
+    const int prt = w >> 1, pct0 = 2 * (w & 1);
+    f32x4 kkt[2];
+    {
+        f32x4 dp[2], dt[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dp[j] = dt[j] = kkt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int ra = 16 * prt + c;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 ao = kp_op_bf16(dOg + (size_t)min(ra, nv - 1) * ts_v, ks, g, ra < nv);
+            const bf16x8 ak = kp_op_bf16(Kg + (size_t)min(ra, nv - 1) * ts, ks, g, true);
+            bf16x8 adh, adl;
+            kp_op_f32(dVb + (size_t)ra * DK, ks, g, 1.f, adh, adl);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int rb = 16 * (pct0 + j) + c;
+                bf16x8 vh, vl, yh, yl;
+                kp_op_f32(Vpb + (size_t)rb * DK, ks, g, 1.f, vh, vl);
+                dp[j] = mma16k32(ao, vh, dp[j]);
+                dp[j] = mma16k32(ao, vl, dp[j]);
+                kp_op_f32(Yb + (size_t)rb * DK, ks, g, sm.bet[rb], yh, yl);
+                dt[j] = mma16k32(adh, yh, dt[j]);
+                dt[j] = mma16k32(adh, yl, dt[j]);
+                dt[j] = mma16k32(adl, yh, dt[j]);
+                const bf16x8 bk = kp_op_bf16(Kg + (size_t)min(rb, nv - 1) * ts, ks, g, true);
+                kkt[j] = mma16k32(ak, bk, kkt[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ct = pct0 + j, m = 16 * ct + c;
+            f32x4 psi, E;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * prt + 4 * g + e;
+                const float d = scale * dp[j][e];
+                const bool low = m <= r;
+                psi[e] = low ? d * __expf(sm.gam[r] - sm.gam[m]) : 0.f;
+                E[e] = low ? d * tp[CH * CH + r * CH + m] : 0.f;   // dP o P (P is the fp32 copy)
+            }
+            put_img(sm.sa, prt, ct, c, g, psi);
+            put_img_t(sm.sb, prt, ct, c, g, psi);
+            put_img(sm.sc, prt, ct, c, g, dt[j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float rs = tile_rowsum(E[e]);
+                if (c == 0) atomicAdd(&sm.dgam[16 * prt + 4 * g + e], rs);
+            }
+            const float cs = tile_colsum(E);
+            if (g == 0) atomicAdd(&sm.dgam[m], -cs);
+        }
+    }
+    __syncthreads();
+    // ---- 4. W1 = dT T^T (tiles); dq += Psi K; dk += Psi^T Q
+    f32x4 w1[2];
+    {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) w1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int oa = (16 * prt + c) * LDP + 32 * ks + 8 * g;
+            const bf16x8 ah = lds_op16(sm.sc + oa), al = lds_op16(sm.sc + CH * LDP + oa);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int ob = (16 * (pct0 + j) + c) * LDP + 32 * ks + 8 * g;
+                const bf16x8 bh = lds_op16(sm.tim + ob), bl = lds_op16(sm.tim + CH * LDP + ob);
+                w1[j] = mma16k32(ah, bh, w1[j]);
+                w1[j] = mma16k32(ah, bl, w1[j]);
+                w1[j] = mma16k32(al, bh, w1[j]);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int ob = (16 * w + c) * LDKT + ((32 * ks + 8 * g) ^ (8 * w));
+            const bf16x8 kb = lds_op16(sm.kt + ob), qb = lds_op16(sm.qt + ob);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int oa = (16 * rt + c) * LDP + 32 * ks + 8 * g;
+                dq[rt] = mma16k32(lds_op16(sm.sa + oa), kb, dq[rt]);
+                dq[rt] = mma16k32(lds_op16(sm.sa + CH * LDP + oa), kb, dq[rt]);
+                dk[rt] = mma16k32(lds_op16(sm.sb + oa), qb, dk[rt]);
+                dk[rt] = mma16k32(lds_op16(sm.sb + CH * LDP + oa), qb, dk[rt]);
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) put_img_t(sm.sc, prt, pct0 + j, c, g, w1[j]);   // W1^T
+    __syncthreads();
+    // ---- 5. dA = -T^T W1 (strictly lower) -> dbeta, dgamma, G, G^T (images)
+    {
+        f32x4 da[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) da[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int oa = (16 * prt + c) * LDP + 32 * ks + 8 * g;
+            const bf16x8 ah = lds_op16(sm.ttim + oa), al = lds_op16(sm.ttim + CH * LDP + oa);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int ob = (16 * (pct0 + j) + c) * LDP + 32 * ks + 8 * g;
+                const bf16x8 bh = lds_op16(sm.sc + ob), bl = lds_op16(sm.sc + CH * LDP + ob);
+                da[j] = mma16k32(ah, bh, da[j]);
+                da[j] = mma16k32(ah, bl, da[j]);
+                da[j] = mma16k32(al, bh, da[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int ct = pct0 + j, i = 16 * ct + c;
+            f32x4 G, gA;
+            float dbr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * prt + 4 * g + e;
+                const bool low = i < r;
+                const float ex = low ? __expf(sm.gam[r] - sm.gam[i]) : 0.f;
+                const float dA = low ? -da[j][e] : 0.f;
+                const float wv = dA * ex * kkt[j][e];   // dA_ri times dA_ri / dbeta_r
+                dbr[e] = wv;
+                gA[e] = wv * sm.bet[r];                 // dA_ri A_ri
+                G[e] = dA * sm.bet[r] * ex;
+            }
+            put_img(sm.sa, prt, ct, c, g, G);
+            put_img_t(sm.sb, prt, ct, c, g, G);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float rb = tile_rowsum(dbr[e]), rg = tile_rowsum(gA[e]);
+                if (c == 0) {
+                    atomicAdd(&sm.dbe[16 * prt + 4 * g + e], rb);
+                    atomicAdd(&sm.dgam[16 * prt + 4 * g + e], rg);
+                }
+            }
+            const float cs = tile_colsum(gA);
+            if (g == 0) atomicAdd(&sm.dgam[i], -cs);
+        }
+    }
+    {   // dgamma_C from the decay of the state: e^gamma_C <S, dSn>
+        float part = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int idx = t + NTHR_CH * j;
+            part += dot4v(*reinterpret_cast<const f32x4*>(S + 4 * idx), *reinterpret_cast<const f32x4*>(dSn + 4 * idx));
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
+        if (lane == 0) atomicAdd(&sm.dgc, __expf(sm.gam[CH - 1]) * part);
+    }
+    __syncthreads();
+    // ---- 6. dk += (G + G^T) K
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 kb = lds_op16(sm.kt + (16 * w + c) * LDKT + ((32 * ks + 8 * g) ^ (8 * w)));
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int oa = (16 * rt + c) * LDP + 32 * ks + 8 * g;
+            dk[rt] = mma16k32(lds_op16(sm.sa + oa), kb, dk[rt]);
+            dk[rt] = mma16k32(lds_op16(sm.sa + CH * LDP + oa), kb, dk[rt]);
+            dk[rt] = mma16k32(lds_op16(sm.sb + oa), kb, dk[rt]);
+            dk[rt] = mma16k32(lds_op16(sm.sb + CH * LDP + oa), kb, dk[rt]);
+        }
+    }
+    // ---- outputs: per-value-head dq, dk parts; dg (reverse cumulative sum of dgamma), dbeta
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rt + 4 * g + e;
+            if (r < nv) {
+                const size_t o = ((tok0 + r) * p.h_v + h) * DK + 16 * w + c;
+                p.dq_part[o] = dq[rt][e];
+                p.dk_part[o] = dk[rt][e];
+            }
+        }
+    if (t < CH) {
+        float x = sm.dgam[t] + (t == CH - 1 ? sm.dgc : 0.f);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float y = __shfl_down(x, d, 64);
+            if (t + d < 64) x += y;
+        }
+        if (t < nv) {
+            p.dg[(tok0 + t) * p.h_v + h] = x;
+            p.dbeta[(tok0 + t) * p.h_v + h] = sm.dbe[t];
+        }
     }
 }
 
@@ -2196,6 +2652,12 @@ int launch_bwd_chain_mma(const BwdParams& p, void* stream) {
     hipLaunchKernelGGL(k_bwd_link, dim3(p.n_seqs, p.h_v), dim3(NTHR_CH), 0, s, p);
     if ((e = launched())) return e;
     hipLaunchKernelGGL(k_bwd_chain_mma<kBwdRerun>, dim3(p.n_segments, p.h_v), dim3(NTHR_CH), 0, s, p);
+    return launched();
+}
+
+int launch_bwd_chunk_mma(const BwdParams& p, void* stream) {
+    if (p.n_chunks <= 0) return 0;
+    hipLaunchKernelGGL(k_bwd_chunk_mma, dim3(p.n_chunks, p.h_v), dim3(NTHR_CH), 0, (hipStream_t)stream, p);
     return launched();
 }
 

@@ -191,8 +191,8 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc,
  *   workspace          device scratch of at least gdn_bwd_workspace_bytes(desc)
  *                      bytes, 256-byte aligned (the forward's workspace, then per
  *                      (chunk, value head) two 64 KiB states, 32.25 KiB of T, P
- *                      and gamma and 32 KiB of their bf16 images, and per token and
- *                      value head 1.25 KiB)
+ *                      and gamma, 48 KiB of their bf16 images and five 32 KiB
+ *                      intermediates, and per token and value head 1.25 KiB)
  * Same ownership and error behaviour as gdn_fwd. */
 size_t gdn_bwd_workspace_bytes(const gdn_desc* desc);
 gdn_status gdn_bwd(const gdn_desc* desc,
