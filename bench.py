@@ -17,7 +17,8 @@ Prints one JSON line. Besides the contract fields it carries:
   cpu_baseline  the fp64 CPU oracle timed on the host cores on a token prefix
   parity        GPU output vs that oracle on the same prefix
   backward      the backward pass (gdn_bwd) on the same workload: time per call, bytes,
-                fp32 work per kernel, parity on a token prefix vs the fp64 backward oracle
+                matrix work of its chunk-gradient kernel, parity on a token prefix vs the fp64
+                backward oracle
   decode        the one-token recurrent decode (gdn_decode) over 256 rows at the TP8 head
                 counts: time per call, HBM roofline, outputs and states vs the oracle
 """
@@ -49,7 +50,6 @@ MEASURED_TRAFFIC = {"tp8": {"sha256": "8d8c7a0aa75c72d1e70f9e5f4ad0213d6cb32b28f
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector peak
 
 
 def algorithmic_bytes(B, T, h_qk, h_v, d=128, e_io=2, initial=False, final=True, n_seqs=None):
@@ -75,18 +75,16 @@ def decode_bytes(rows, h_qk, h_v, d=128, e_io=2):
 
 
 BWD_KERNEL_FLOPS = {
-    # fp32 multiply-adds x 2 that each backward kernel performs per (chunk, value head),
-    # counted from its loops (the implementation's own work, not a minimal count)
-    # chain, per 16-column block: K dSn, the triangular P^T dO and T^T dV', Q^T dO' and K^T dY'
-    "k_bwd_chain": 8 * 2 * (64 * 128 * 16 + 2 * (64 * 64 * 16 // 2) + 2 * 128 * 64 * 16),
-    # chunk: six [64 x 128 x 128] products with S or dSn, eleven [64 x 64 x 128]-sized ones
-    "k_bwd_chunk": 2 * (6 * 64 * 128 * 128 + 11 * 64 * 64 * 128),
+    # useful multiply-adds x 2 per (chunk, value head) of the chunk-gradient kernel: three
+    # 64x128x128 products (dO S^T, V' dSn^T, dY S^T), seven 64x64x128 (dP, dT, K K^T, Psi K,
+    # Psi^T Q, G K, G^T K) and two 64x64x64 (dT T^T, T^T W1); hi/lo splits not counted
+    "k_bwd_chunk_mma": 2 * (3 * 64 * 128 * 128 + 7 * 64 * 64 * 128 + 2 * 64 * 64 * 64),
 }
 
 
 def measure_backward(args, gdn, torch, np, dev, flush, inp, q, k, v, g, beta, s0):
     """gdn_bwd on the benchmark workload: GPU time per call (caches flushed
-    before each), the HBM bytes it must move, and its fp32 work; parity of a
+    before each), the HBM bytes it must move, and its matrix work; parity of a
     separate call on a token prefix of sequence 0 against the fp64 backward
     oracle."""
     import ctypes
@@ -142,9 +140,10 @@ def measure_backward(args, gdn, torch, np, dev, flush, inp, q, k, v, g, beta, s0
     del keep
     return {"ms_per_call": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
             "algorithmic_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-            "fp32_gflop_per_kernel": {kname: round(f / 1e9, 2) for kname, f in flops.items()},
-            "fp32_peak_tflops": FP32_PEAK_TFLOPS,
-            "precision": "fp32 vector ALU arithmetic on bf16 inputs; forward re-run as in gdn_fwd",
+            "gflop_per_kernel": {kname: round(f / 1e9, 2) for kname, f in flops.items()},
+            "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "precision": "bf16 MFMA with hi/lo splits of fp32 operands, fp32 accumulation; "
+                         "forward re-run as in gdn_fwd",
             "parity_prefix": {"tokens": n_tok, "max_rel_and_mean_rel_l1": par,
                               "tol": {"dq,dk,dv": [1e-2, 2e-3], "dg,dbeta,d_initial": [1e-3, 1e-4]}}}
 
