@@ -42,6 +42,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int CH = kChunk;
 constexpr int DK = kDim;
@@ -144,51 +145,95 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
         out[2 * CH * CH + t] = x;
     }
     __syncthreads();
-    {   // A (strictly lower) and P (lower with the diagonal): row r, columns i0 + 4 ii
-        const int r = t >> 2, i0 = t & 3;
-        float kk[16], qk[16];
+    {   // K K^T and Q K^T on the ten lower 16x16 tiles (16x16x32 MFMA; lane 16 g + c:
+        // A row c and B column c with the k values 8 g .. of each 32-wide step; C rows
+        // 4 g .. 4 g + 3 of column c); wave w takes tiles w, w + 4, w + 8
+        const int w = t >> 6, lane = t & 63, c = lane & 15, g = lane >> 4;
+        f32x4 kk[3], qk[3];
+        int tri[3], tii[3];
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) kk[ii] = qk[ii] = 0.f;
-        for (int d = 0; d < DK; d += 4) {
-            const f32x4 kr = bf4(&kb[r][d]), qr = bf4(&qb[r][d]);
+        for (int j = 0; j < 3; ++j) {
+            const int job = w + 4 * j;
+            tri[j] = job >= 6 ? 3 : job >= 3 ? 2 : job >= 1 ? 1 : 0;
+            tii[j] = job - tri[j] * (tri[j] + 1) / 2;
+            kk[j] = qk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (job >= 10) continue;
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) {
-                const f32x4 ki = bf4(&kb[i0 + 4 * ii][d]);
-                kk[ii] += dot4(kr, ki);
-                qk[ii] += dot4(qr, ki);
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&kb[16 * tri[j] + c][32 * s4 + 8 * g]);
+                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&qb[16 * tri[j] + c][32 * s4 + 8 * g]);
+                const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&kb[16 * tii[j] + c][32 * s4 + 8 * g]);
+                kk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bk, kk[j], 0, 0, 0);
+                qk[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, qk[j], 0, 0, 0);
             }
         }
-        float* P = out + CH * CH;
         __syncthreads();   // every read of Q is done before P overwrites its tile
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-            const int i = i0 + 4 * ii;
-            const float ex = i <= r ? __expf(gam[r] - gam[i]) : 0.f;
-            am[r][i] = i < r ? bet[r] * ex * kk[ii] : 0.f;
-            const float pv = i <= r ? ex * qk[ii] : 0.f;
-            P[r * CH + i] = pv;
-            pmat[r][i] = pv;
-        }
-    }
-    __syncthreads();
-    if (t < CH) {   // forward substitution, one column per lane: T[i][c] = d_ic - sum_j A[i][j] T[j][c]
-        const int col = t;
-        for (int i = 0; i < CH; ++i) {
-            // four independent partial sums keep the LDS reads ahead of the adds
-            float s0 = (i == col) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-            int j = col;
-            for (; j + 4 <= i; j += 4) {
-                s0 -= am[i][j] * tm[j][col];
-                s1 -= am[i][j + 1] * tm[j + 1][col];
-                s2 -= am[i][j + 2] * tm[j + 2][col];
-                s3 -= am[i][j + 3] * tm[j + 3][col];
+        for (int j = 0; j < 3; ++j) {
+            if (w + 4 * j >= 10) continue;
+            const int i = 16 * tii[j] + c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tri[j] + 4 * g + e;
+                const float ex = i <= r ? __expf(gam[r] - gam[i]) : 0.f;
+                am[r][i] = i < r ? bet[r] * ex * kk[j][e] : 0.f;
+                pmat[r][i] = i <= r ? ex * qk[j][e] : 0.f;
             }
-            for (; j < i; ++j) s0 -= am[i][j] * tm[j][col];
-            tm[i][col] = i >= col ? (s0 + s1) + (s2 + s3) : 0.f;
         }
     }
     __syncthreads();
-    for (int idx = t; idx < CH * CH; idx += NT) out[idx] = tm[idx >> 6][idx & 63];
+    // T = (I + A)^-1 by 16x16 blocks: the diagonal blocks by substitution (wave w,
+    // block w, lane c < 16 holds column c in registers), then the blocks below
+    // the diagonal one anti-diagonal at a time:
+    //   X = sum_{k in blocks j .. i-1} A_ik T_kj (kept in the unused upper block
+    //   (j, i) of A), T_ij = -T_ii X.
+    {
+        const int w = t >> 6, c = t & 63;
+        if (c < 16) {
+            float tr[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s0 = (i == c) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+                for (int j = 0; j < i; ++j) {
+                    if (j & 1) s1 -= am[16 * w + i][16 * w + j] * tr[j];
+                    else s0 -= am[16 * w + i][16 * w + j] * tr[j];
+                }
+                tr[i] = i >= c ? s0 + s1 : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tm[16 * w + i][16 * w + c] = tr[i];
+        }
+    }
+    __syncthreads();
+    {
+        const int a = t >> 4, bb = t & 15;
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {
+            for (int j = 0; j + d < 4; ++j) {
+                const int i = j + d;
+                float x = 0.f;
+                for (int k = 16 * j; k < 16 * i; ++k) x += am[16 * i + a][k] * tm[k][16 * j + bb];
+                am[16 * j + a][16 * i + bb] = x;
+            }
+            __syncthreads();
+            for (int j = 0; j + d < 4; ++j) {
+                const int i = j + d;
+                float x = 0.f;
+#pragma unroll
+                for (int m = 0; m < 16; ++m) x += tm[16 * i + a][16 * i + m] * am[16 * j + m][16 * i + bb];
+                tm[16 * i + a][16 * j + bb] = -x;
+            }
+            __syncthreads();
+        }
+    }
+    // fp32 T and P (zero above the diagonal blocks / the diagonal)
+    auto tv = [&](int r, int col) { return (col >> 4) > (r >> 4) ? 0.f : tm[r][col]; };
+    auto pv = [&](int r, int col) { return col > r ? 0.f : pmat[r][col]; };
+    for (int idx = t; idx < CH * CH; idx += NT) {
+        out[idx] = tv(idx >> 6, idx & 63);
+        out[CH * CH + idx] = pv(idx >> 6, idx & 63);
+    }
     // T^T, scale P^T and T as hi/lo bf16 rows with the contraction token in kp order
     // (four consecutive tokens stay consecutive in kp order: one 8-byte store each)
     bf16* img = static_cast<bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt;
@@ -197,8 +242,8 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
         bf16 th[4], tl[4], ph[4], pl[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            split1(tm[m4 + e][r], th[e], tl[e]);
-            split1(p.scale * pmat[m4 + e][r], ph[e], pl[e]);
+            split1(tv(m4 + e, r), th[e], tl[e]);
+            split1(p.scale * pv(m4 + e, r), ph[e], pl[e]);
         }
         auto pack = [](const bf16 (&x)[4]) {
             return u32x2{(unsigned)__builtin_bit_cast(unsigned short, x[0]) |
@@ -212,7 +257,7 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
         *reinterpret_cast<u32x2*>(img + 3 * CH * CH + o) = pack(pl);
         // T itself: row r, tokens m in kp order
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split1(tm[r][m4 + e], th[e], tl[e]);
+        for (int e = 0; e < 4; ++e) split1(tv(r, m4 + e), th[e], tl[e]);
         *reinterpret_cast<u32x2*>(img + 4 * CH * CH + o) = pack(th);
         *reinterpret_cast<u32x2*>(img + 5 * CH * CH + o) = pack(tl);
     }
