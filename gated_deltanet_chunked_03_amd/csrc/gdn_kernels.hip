@@ -1678,7 +1678,6 @@ struct BwdChainSmem {
 struct BwdChainIn {
     u32x2 k[4], q[4];                     // tokens 4 (t / 32) + j, d_k 4 (t % 32) .. + 3
     u32x4 img[4];                         // pieces t + 512 j of the T^T / P^T images
-    unsigned d[16];                       // dO, this lane's 16 tokens x 1 column (raw bf16)
     float gl, bl;                         // gamma, beta of token lane
     int nv;                               // valid tokens of the chunk
 };
@@ -1697,15 +1696,6 @@ __device__ void bwd_chain_fetch(const BwdParams& p, BwdChainIn& in, int f, size_
     const u32x4* img = reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt);
 #pragma unroll
     for (int j = 0; j < 4; ++j) in.img[j] = img[t + NTHR_CH * j];
-    // dO: tokens 16 rt + 4 g + e, column 16 w + c. Every load is issued (rows
-    // past the end read the last row) and zeroed afterwards: a conditional
-    // load would make the compiler drain every outstanding load at its branch.
-    const unsigned short* dob = reinterpret_cast<const unsigned short*>(p.dout) + tok0 * ts_v + (size_t)h * DK +
-                                16 * wave_id() + c;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) in.d[4 * rt + e] = dob[(size_t)min(16 * rt + 4 * g + e, nv - 1) * ts_v];
     in.gl = p.tpg[((size_t)f * p.h_v + h) * kBwdTpg + 2 * CH * CH + lane];
     in.bl = p.beta[(tok0 + min(lane, nv - 1)) * p.h_v + h];
     in.nv = nv;   // (the masking waits for the loads: it happens when the chunk is staged)
@@ -1758,15 +1748,20 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
         bwd_chain_stage(sm, in, p.scale);
         const int in_nv = in.nv;
         if (WRITE_DS) store_state(p.ds + state_off(loc.chunk_base + cc, p.h_v, h), D);
-        unsigned dO[8];   // this lane's dO tokens as bf16 pairs, rows past the end zero
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r0 = 16 * (i >> 1) + 4 * g + 2 * (i & 1);
-            const unsigned lo = (WANT_DO && r0 < in.nv) ? in.d[2 * i] : 0u;
-            const unsigned hi = (WANT_DO && r0 + 1 < in.nv) ? in.d[2 * i + 1] : 0u;
-            dO[i] = lo | (hi << 16);
-        }
         __syncthreads();
+        // this chunk's dO (tokens 16 rt + 4 g + e, column 16 w + c) is loaded here, to
+        // arrive during K dS; every load is issued (rows past the end read the last
+        // row) and masked after the wait: a conditional load would make the
+        // compiler drain every outstanding load at its branch
+        unsigned draw[16];
+        if (WANT_DO) {
+            const unsigned short* dob = reinterpret_cast<const unsigned short*>(p.dout) +
+                                        (loc.tok0 + (size_t)cc * CH) * (size_t)(p.h_v * DK) + (size_t)h * DK +
+                                        16 * wave_id() + c;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                draw[i] = dob[(size_t)min(16 * (i >> 2) + 4 * g + (i & 3), in_nv - 1) * (size_t)(p.h_v * DK)];
+        }
         if (cc > c_lo) fetch(cc - 1);
         // X = diag(f) K dS + scale P^T dO
         f32x4 X[4];
@@ -1788,6 +1783,14 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) X[rt] *= *reinterpret_cast<const f32x4*>(sm.fr + 16 * rt + 4 * g);
+        unsigned dO[8];   // this lane's dO tokens as bf16 pairs, rows past the end zero
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r0 = 16 * (i >> 1) + 4 * g + 2 * (i & 1);
+            const unsigned lo = (WANT_DO && r0 < in_nv) ? draw[2 * i] : 0u;
+            const unsigned hi = (WANT_DO && r0 + 1 < in_nv) ? draw[2 * i + 1] : 0u;
+            dO[i] = lo | (hi << 16);
+        }
         if (WANT_DO) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -1850,38 +1853,36 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            bf16x8 yh, yl;
+            bf16x8 yh, yl, oh, ol;
             split8(Z[2 * s], Z[2 * s + 1], yh, yl);
-            bf16x8 kh[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                kh[i] = lds_op16(sm.kt + (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i)));
             if (WANT_DO) {
-                f32x4 o0, o1;
-                {
-                    const f32x4 e0 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 4 * g);
-                    const f32x4 e1 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 16 + 4 * g);
-                    const unsigned a0 = dO[4 * s], a1 = dO[4 * s + 1], b0 = dO[4 * s + 2], b1 = dO[4 * s + 3];
-                    o0 = f32x4{__uint_as_float(a0 << 16), __uint_as_float(a0 & 0xffff0000u),
-                               __uint_as_float(a1 << 16), __uint_as_float(a1 & 0xffff0000u)} * e0;
-                    o1 = f32x4{__uint_as_float(b0 << 16), __uint_as_float(b0 & 0xffff0000u),
-                               __uint_as_float(b1 << 16), __uint_as_float(b1 & 0xffff0000u)} * e1;
-                }
-                bf16x8 oh, ol;
+                const f32x4 e0 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 4 * g);
+                const f32x4 e1 = *reinterpret_cast<const f32x4*>(sm.egs + 32 * s + 16 + 4 * g);
+                const unsigned a0 = dO[4 * s], a1 = dO[4 * s + 1], b0 = dO[4 * s + 2], b1 = dO[4 * s + 3];
+                const f32x4 o0 = f32x4{__uint_as_float(a0 << 16), __uint_as_float(a0 & 0xffff0000u),
+                                       __uint_as_float(a1 << 16), __uint_as_float(a1 & 0xffff0000u)} * e0;
+                const f32x4 o1 = f32x4{__uint_as_float(b0 << 16), __uint_as_float(b0 & 0xffff0000u),
+                                       __uint_as_float(b1 << 16), __uint_as_float(b1 & 0xffff0000u)} * e1;
                 split8(o0, o1, oh, ol);
-                bf16x8 qh[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    qh[i] = lds_op16(sm.qt + (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i)));
-#pragma unroll
-                for (int i = 0; i < 8; ++i) D[i] = mma16k32(qh[i], oh, D[i]);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) D[i] = mma16k32(qh[i], ol, D[i]);
             }
+            // two row tiles at a time: few operands live, two independent chains
 #pragma unroll
-            for (int i = 0; i < 8; ++i) D[i] = mma16k32(kh[i], yh, D[i]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) D[i] = mma16k32(kh[i], yl, D[i]);
+            for (int i = 0; i < 8; i += 2) {
+                const int o0 = (16 * i + c) * LDKT + ((32 * s + 8 * g) ^ (8 * i));
+                const int o1 = (16 * (i + 1) + c) * LDKT + ((32 * s + 8 * g) ^ (8 * (i + 1)));
+                const bf16x8 k0 = lds_op16(sm.kt + o0), k1 = lds_op16(sm.kt + o1);
+                if (WANT_DO) {
+                    const bf16x8 q0 = lds_op16(sm.qt + o0), q1 = lds_op16(sm.qt + o1);
+                    D[i] = mma16k32(q0, oh, D[i]);
+                    D[i + 1] = mma16k32(q1, oh, D[i + 1]);
+                    D[i] = mma16k32(q0, ol, D[i]);
+                    D[i + 1] = mma16k32(q1, ol, D[i + 1]);
+                }
+                D[i] = mma16k32(k0, yh, D[i]);
+                D[i + 1] = mma16k32(k1, yh, D[i + 1]);
+                D[i] = mma16k32(k0, yl, D[i]);
+                D[i + 1] = mma16k32(k1, yl, D[i + 1]);
+            }
         }
         __syncthreads();
     }
