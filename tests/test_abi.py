@@ -267,6 +267,40 @@ def test_decode_validation():
     assert B.STATUS_NAMES[st] == "GDN_ERR_BAD_SHAPE" and "overlap" in msg
 
 
+def call_bwd(d, q=0x1000, k=0x1000, v=0x1000, g=0x1000, beta=0x1000, scale=0.1, s0=None, cu=None,
+             dout=0x1000, dfin=None, dq=0x1000, dk=0x1000, dv=0x1000, dg=0x1000, dbeta=0x1000, dinit=None,
+             ws=0x1000, ws_bytes=1 << 40):
+    l = lib()
+    P = ctypes.c_void_p
+    opt = lambda x: P(x) if x else None  # noqa: E731
+    st = l.gdn_bwd(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), scale, opt(s0), opt(cu), opt(dout),
+                   opt(dfin), opt(dq), opt(dk), opt(dv), opt(dg), opt(dbeta), opt(dinit), opt(ws), ws_bytes, None)
+    return st, l.gdn_last_error().decode()
+
+
+def test_bwd_validation():
+    """gdn_bwd rejects bad arguments before any launch (only bf16 inputs; every
+    gradient output and d_out required; workspace size and alignment)."""
+    d, keep = desc(io_dtype=B.GDN_F32)
+    st, msg = call_bwd(d)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_BAD_DTYPE" and "bf16" in msg
+    d, keep = desc(d_k=64, d_v=64)
+    assert B.STATUS_NAMES[call_bwd(d)[0]] == "GDN_ERR_UNSUPPORTED_DIM"
+    d, keep = desc()
+    for kw in ("dout", "dq", "dk", "dv", "dg", "dbeta", "q"):
+        st, msg = call_bwd(d, **{kw: 0})
+        assert B.STATUS_NAMES[st] == "GDN_ERR_NULL_ARG", (kw, msg)
+    assert B.STATUS_NAMES[call_bwd(d, dg=0x1002)[0]] == "GDN_ERR_MISALIGNED"
+    assert B.STATUS_NAMES[call_bwd(d, scale=float("inf"))[0]] == "GDN_ERR_BAD_SCALE"
+    need = lib().gdn_bwd_workspace_bytes(ctypes.byref(d))
+    assert need > lib().gdn_fwd_workspace_bytes(ctypes.byref(d))
+    st, msg = call_bwd(d, ws_bytes=need - 1)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_WORKSPACE_TOO_SMALL" and str(need) in msg
+    assert B.STATUS_NAMES[call_bwd(d, ws=0x1010, ws_bytes=need)[0]] == "GDN_ERR_MISALIGNED"
+    d2, keep2 = desc(T=20, cu_seqlens=[0, 10, 20])
+    assert B.STATUS_NAMES[call_bwd(d2)[0]] == "GDN_ERR_NULL_ARG"   # device cu_seqlens missing
+
+
 def test_profile_read_without_profiled_call():
     l = lib()
     ms = (ctypes.c_float * 5)()

@@ -88,3 +88,17 @@ def test_bwd_varlen_auto_cp():
     _check(inp, d_out, d_fin, got, "varlen")
     # the empty sequence passes its state gradient through
     np.testing.assert_array_equal(got["d_initial"][1], d_fin[1])
+
+
+@pytest.mark.parametrize("config", ["tp8"])
+def test_bwd_full_size(config):
+    """The benchmark's workload at full size (B = 1, T = 32768; AutoCP splits it
+    into 32 segments per head, so the segment maps, the linking pass and the
+    re-run all take part): every gradient element against the fp64 backward
+    oracle (about 7 s on 8 host threads)."""
+    from gated_deltanet_chunked_03_amd.synth import config_inputs
+    inp = config_inputs(config)
+    print(f"\n[bwd/full/{config}] T={inp.T} h_qk={inp.h_qk} h_v={inp.h_v}", flush=True)
+    d_out, d_fin = _grads(177, inp.v.shape, inp.n_seqs, inp.h_v)
+    got = _run(inp, d_out, d_fin)
+    _check(inp, d_out, d_fin, got, f"full/{config}")
