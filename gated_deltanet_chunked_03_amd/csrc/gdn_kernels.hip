@@ -2174,34 +2174,70 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
         }
     }
     __syncthreads();
-    // ---- 2. d_k-column products: dq = diag(scale e^gamma) dO S^T, dk = diag(f) V' dSn^T - diag(e^gamma) dY S^T
+    // ---- 2. d_k-column products: dq = diag(scale e^gamma) dO S^T, dk = diag(f) V' dSn^T - diag(e^gamma) dY S^T.
+    // The token-row operands (dO, dY = diag(beta) Z, V'), which every wave needs, are staged once in LDS
+    // (rows with d_v in kp order; the image slots sa .. sc are free until step 3): first dO and dY, then V'.
     f32x4 dq[4], dk[4];
     {
+        bf16* st = sm.sa;                          // 60 KiB: sa, sb, sc
+        bf16* st_do = st;                          // [64][LDQ] dO (kept through step 3's dP)
+        bf16* st_x = st + CH * LDQ;                // [128][LDQ] dY, then V': hi rows, then lo rows
+        static_assert(sizeof(sm.sa) + sizeof(sm.sb) + sizeof(sm.sc) >= 3 * CH * LDQ * sizeof(bf16), "staging fits");
+        auto stage_f32 = [&](bf16* dst, const float* src, bool by_beta) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {   // piece t + 512 j: row / 32, four d_v at 4 (piece % 32)
+                const int idx = t + NTHR_CH * j, r = idx >> 5, c4 = (idx & 31) * 4;
+                f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)r * DK + c4);
+                if (by_beta) x *= sm.bet[r];
+                bf16x4 hi, lo;
+                split4(x, hi, lo);
+                *reinterpret_cast<bf16x4*>(dst + r * LDQ + kp(c4)) = hi;
+                *reinterpret_cast<bf16x4*>(dst + (CH + r) * LDQ + kp(c4)) = lo;
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {   // dO, rows past the end zero (loads issued for every row)
+            const int idx = t + NTHR_CH * j, r = idx >> 5, c4 = (idx & 31) * 4;
+            const u32x2 x = *reinterpret_cast<const u32x2*>(dOg + (size_t)min(r, nv - 1) * ts_v + c4);
+            *reinterpret_cast<u32x2*>(st_do + r * LDQ + kp(c4)) = r < nv ? x : u32x2{0u, 0u};
+        }
+        stage_f32(st_x, Zb, true);
         f32x4 aq[4], a1[4], a2[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) aq[rt] = a1[rt] = a2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const float* Srow = S + (size_t)(16 * w + c) * DK;
         const float* Drow = dSn + (size_t)(16 * w + c) * DK;
+        __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 sh, sl, dh, dl;
+            bf16x8 sh, sl;
             kp_op_f32(Srow, ks, g, 1.f, sh, sl);
-            kp_op_f32(Drow, ks, g, 1.f, dh, dl);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                const int r = 16 * rt + c;
-                const bf16x8 ao = kp_op_bf16(dOg + (size_t)min(r, nv - 1) * ts_v, ks, g, r < nv);
+                const int o = (16 * rt + c) * LDQ + 32 * ks + 8 * g;
+                const bf16x8 ao = lds_op16(st_do + o);
                 aq[rt] = mma16k32(ao, sh, aq[rt]);
                 aq[rt] = mma16k32(ao, sl, aq[rt]);
-                bf16x8 vh, vl, yh, yl;
-                kp_op_f32(Vpb + (size_t)r * DK, ks, g, 1.f, vh, vl);
-                a1[rt] = mma16k32(vh, dh, a1[rt]);
-                a1[rt] = mma16k32(vh, dl, a1[rt]);
-                a1[rt] = mma16k32(vl, dh, a1[rt]);
-                kp_op_f32(Zb + (size_t)r * DK, ks, g, sm.bet[r], yh, yl);   // dY = diag(beta) Z
+                const bf16x8 yh = lds_op16(st_x + o), yl = lds_op16(st_x + CH * LDQ + o);
                 a2[rt] = mma16k32(yh, sh, a2[rt]);
                 a2[rt] = mma16k32(yh, sl, a2[rt]);
                 a2[rt] = mma16k32(yl, sh, a2[rt]);
+            }
+        }
+        __syncthreads();
+        stage_f32(st_x, Vpb, false);
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 dh, dl;
+            kp_op_f32(Drow, ks, g, 1.f, dh, dl);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int o = (16 * rt + c) * LDQ + 32 * ks + 8 * g;
+                const bf16x8 vh = lds_op16(st_x + o), vl = lds_op16(st_x + CH * LDQ + o);
+                a1[rt] = mma16k32(vh, dh, a1[rt]);
+                a1[rt] = mma16k32(vh, dl, a1[rt]);
+                a1[rt] = mma16k32(vl, dh, a1[rt]);
             }
         }
 #pragma unroll
@@ -2232,17 +2268,20 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) dp[j] = dt[j] = kkt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int ra = 16 * prt + c;
+        const bf16* st_do = sm.sa;                       // staged in step 2 (dO, then V' hi / lo rows)
+        const bf16* st_v = sm.sa + CH * LDQ;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 ao = kp_op_bf16(dOg + (size_t)min(ra, nv - 1) * ts_v, ks, g, ra < nv);
+            const bf16x8 ao = lds_op16(st_do + ra * LDQ + 32 * ks + 8 * g);
             const bf16x8 ak = kp_op_bf16(Kg + (size_t)min(ra, nv - 1) * ts, ks, g, true);
             bf16x8 adh, adl;
             kp_op_f32(dVb + (size_t)ra * DK, ks, g, 1.f, adh, adl);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int rb = 16 * (pct0 + j) + c;
-                bf16x8 vh, vl, yh, yl;
-                kp_op_f32(Vpb + (size_t)rb * DK, ks, g, 1.f, vh, vl);
+                bf16x8 yh, yl;
+                const bf16x8 vh = lds_op16(st_v + rb * LDQ + 32 * ks + 8 * g);
+                const bf16x8 vl = lds_op16(st_v + (CH + rb) * LDQ + 32 * ks + 8 * g);
                 dp[j] = mma16k32(ao, vh, dp[j]);
                 dp[j] = mma16k32(ao, vl, dp[j]);
                 kp_op_f32(Yb + (size_t)rb * DK, ks, g, sm.bet[rb], yh, yl);
@@ -2253,6 +2292,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 kkt[j] = mma16k32(ak, bk, kkt[j]);
             }
         }
+        __syncthreads();   // the staging area becomes the image slots again
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int ct = pct0 + j, m = 16 * ct + c;
