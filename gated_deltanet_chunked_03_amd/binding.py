@@ -23,7 +23,7 @@ CP_MODES = {"auto": 0, "off": 1, "exact": 2, "warmup": 3}
 GDN_BF16, GDN_F32 = 0, 1
 
 EXPORTED = ["gdn_plan", "gdn_fwd_workspace_bytes", "gdn_fwd", "gdn_fwd_debug", "gdn_chunk_prep",
-            "gdn_decode", "gdn_bwd_workspace_bytes", "gdn_bwd", "gdn_profile_enable", "gdn_profile_read", "gdn_status_string", "gdn_last_error"]
+            "gdn_decode", "gdn_bwd_workspace_bytes", "gdn_bwd", "gdn_calibrate_lambda", "gdn_profile_enable", "gdn_profile_read", "gdn_status_string", "gdn_last_error"]
 
 
 class GdnDesc(ctypes.Structure):
@@ -93,6 +93,9 @@ def load_library(path: Optional[str] = None):
         lib.gdn_bwd.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, ctypes.c_float, P, P, P, P,
                                 P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.gdn_bwd.restype = S
+        lib.gdn_calibrate_lambda.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, ctypes.c_float, P, P, P,
+                                             ctypes.c_size_t, P, ctypes.c_int32, ctypes.c_int32, P, P, P]
+        lib.gdn_calibrate_lambda.restype = S
         lib.gdn_profile_enable.argtypes = [ctypes.c_int]
         lib.gdn_profile_enable.restype = S
         lib.gdn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -313,6 +316,35 @@ def bwd(q, k, v, g, beta, d_out, scale=None, initial_state=None, d_final_state=N
                             workspace.numel() * workspace.element_size(), stream))
     del keep
     return out
+
+
+def calibrate_lambda(q, k, v, g, beta, lambdas=(0.5, 0.75, 1.0, 1.5, 2.0), reps=3, scale=None, cu_seqlens=None,
+                     cp_mode="auto", warmup_chunks=0, noise_floor=0.0, n_cu=0):
+    """Time the forward on these inputs for each candidate lambda (L = lambda sqrt(N))
+    and return (best_lambda, {lambda: mean ms per forward}). Synchronises the host."""
+    torch = _torch()
+    B, T, h_qk, h_v, d_k, d_v, io, cu_dev, cu_host = _prepare(q, k, v, g, beta, cu_seqlens)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    lib = load_library()
+    need = 256
+    for lam in lambdas:
+        desc, keep = make_desc(B, T, h_qk, h_v, d_k, d_v, io, cu_host, cp_mode, float(lam), warmup_chunks,
+                               noise_floor, n_cu)
+        need = max(need, plan_desc(desc)["workspace_bytes"])
+    desc, keep = make_desc(B, T, h_qk, h_v, d_k, d_v, io, cu_host, cp_mode, 0.0, warmup_chunks, noise_floor, n_cu)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(v)
+    lam_arr = (ctypes.c_float * len(lambdas))(*[float(x) for x in lambdas])
+    ms = (ctypes.c_float * len(lambdas))()
+    best = ctypes.c_float()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    _check(lib, lib.gdn_calibrate_lambda(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         float(scale), _ptr(cu_dev), _ptr(out), _ptr(ws), need, lam_arr,
+                                         len(lambdas), int(reps), stream, ms, ctypes.byref(best)))
+    del keep
+    return best.value, {float(l): ms[i] for i, l in enumerate(lambdas)}
 
 
 def decode(q, k, v, g, beta, state, scale=None, out=None, state_out=None, inplace=False):

@@ -517,6 +517,64 @@ size_t gdn_fwd_workspace_bytes(const gdn_desc* desc) {
     return P.ws_bytes;
 }
 
+gdn_status gdn_calibrate_lambda(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, float scale, const int32_t* cu_seqlens,
+                                void* out, void* workspace, size_t workspace_bytes, const float* lambdas,
+                                int32_t n_lambdas, int32_t reps, void* stream, float* ms_out, float* best_lambda) {
+    if (!desc) return fail(GDN_ERR_NULL_ARG, "desc is NULL");
+    if (!lambdas || !best_lambda) return fail(GDN_ERR_NULL_ARG, "lambdas and best_lambda are required");
+    if (n_lambdas < 1 || n_lambdas > 64) return fail(GDN_ERR_BAD_OPTION, "n_lambdas must be in 1..64");
+    if (reps < 1 || reps > 1000) return fail(GDN_ERR_BAD_OPTION, "reps must be in 1..1000");
+    gdn_desc d = *desc;
+    // every candidate is checked (descriptor, pointers, workspace) before anything runs
+    for (int i = 0; i < n_lambdas; ++i) {
+        if (!(lambdas[i] > 0.f) || !std::isfinite(lambdas[i]))
+            return fail(GDN_ERR_BAD_OPTION, "lambdas[%d] must be finite and > 0", i);
+        d.lambda = lambdas[i];
+        Plan P;
+        gdn_status st = make_plan(&d, &P);
+        if (st != GDN_OK) return st;
+        if (workspace_bytes < P.ws_bytes)
+            return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, lambda %g needs %zu", workspace_bytes,
+                        (double)lambdas[i], P.ws_bytes);
+    }
+    hipEvent_t ev[2];
+    hipError_t e = hipEventCreate(&ev[0]);
+    if (e == hipSuccess && (e = hipEventCreate(&ev[1])) != hipSuccess) (void)hipEventDestroy(ev[0]);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+    const hipStream_t hs = (hipStream_t)stream;
+    float best_ms = 0.f;
+    gdn_status st = GDN_OK;
+    for (int i = 0; i < n_lambdas && st == GDN_OK; ++i) {
+        d.lambda = lambdas[i];
+        // one untimed run, then reps timed ones between two events on the stream
+        st = run_fwd(&d, q, k, v, g, beta, scale, nullptr, cu_seqlens, out, nullptr, workspace, workspace_bytes,
+                     stream, nullptr, nullptr);
+        if (st != GDN_OK) break;
+        if ((e = hipEventRecord(ev[0], hs)) != hipSuccess) { st = fail(GDN_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e)); break; }
+        for (int r = 0; r < reps && st == GDN_OK; ++r)
+            st = run_fwd(&d, q, k, v, g, beta, scale, nullptr, cu_seqlens, out, nullptr, workspace, workspace_bytes,
+                         stream, nullptr, nullptr);
+        if (st != GDN_OK) break;
+        float ms = 0.f;
+        if ((e = hipEventRecord(ev[1], hs)) != hipSuccess || (e = hipEventSynchronize(ev[1])) != hipSuccess ||
+            (e = hipEventElapsedTime(&ms, ev[0], ev[1])) != hipSuccess) {
+            st = fail(GDN_ERR_HIP, "timing: %s", hipGetErrorString(e));
+            break;
+        }
+        ms /= (float)reps;
+        if (ms_out) ms_out[i] = ms;
+        if (i == 0 || ms < best_ms) {
+            best_ms = ms;
+            *best_lambda = lambdas[i];
+        }
+    }
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (st == GDN_OK) g_last_error.clear();
+    return st;
+}
+
 gdn_status gdn_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, float scale, const float* initial_state, const int32_t* cu_seqlens,
                    void* out, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {

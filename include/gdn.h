@@ -169,6 +169,27 @@ gdn_status gdn_chunk_prep(const gdn_desc* desc,
                           const float* g, const float* beta, const int32_t* cu_seqlens,
                           float* gamma_out, float* W_out, float* U_out, void* stream);
 
+/* Calibration of lambda (the AutoCP segment length L = lambda * sqrt(N) of the
+ * section "Gate-Driven Automatic Intra-Card Context Parallelism (AutoCP)";
+ * the pages fix no lambda): times the forward on the caller's inputs for each
+ * candidate and returns the fastest, for the caller to put into later
+ * descriptors. Each candidate runs once untimed, then reps times between two
+ * HIP events on the stream; the call synchronises the host on those events.
+ *   desc, q, k, v, g, beta, scale, cu_seqlens, out   as for gdn_fwd (no states)
+ *   workspace          at least gdn_fwd_workspace_bytes for every candidate
+ *   lambdas            host array of n_lambdas (1..64) finite values > 0
+ *   reps               timed forwards per candidate (1..1000)
+ *   ms_out             host float[n_lambdas]: mean ms per forward, or NULL
+ *   best_lambda        host float: the fastest candidate
+ * Candidates are validated (descriptor, workspace) before anything runs. */
+gdn_status gdn_calibrate_lambda(const gdn_desc* desc,
+                                const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, float scale,
+                                const int32_t* cu_seqlens, void* out,
+                                void* workspace, size_t workspace_bytes,
+                                const float* lambdas, int32_t n_lambdas, int32_t reps,
+                                void* stream, float* ms_out, float* best_lambda);
+
 /* Backward pass: the gradients of gdn_fwd's outputs with respect to its
  * inputs (the FlashQLA pages' title promises a backward-friendly design; they
  * print no backward formulas, so this is the exact gradient of the gated delta

@@ -301,6 +301,30 @@ def test_bwd_validation():
     assert B.STATUS_NAMES[call_bwd(d2)[0]] == "GDN_ERR_NULL_ARG"   # device cu_seqlens missing
 
 
+def test_calibrate_lambda_validation():
+    """gdn_calibrate_lambda checks its candidates and the workspace before running anything."""
+    l = lib()
+    P = ctypes.c_void_p
+    d, keep = desc()
+    best = ctypes.c_float()
+
+    def call(lams, n=None, reps=3, ws_bytes=1 << 40, best_p=True):
+        arr = (ctypes.c_float * max(len(lams), 1))(*lams)
+        st = l.gdn_calibrate_lambda(ctypes.byref(d), P(0x1000), P(0x1000), P(0x1000), P(0x1000), P(0x1000), 0.1,
+                                    None, P(0x1000), P(0x1000), ws_bytes, arr, len(lams) if n is None else n,
+                                    reps, None, None, ctypes.byref(best) if best_p else None)
+        return B.STATUS_NAMES[st], l.gdn_last_error().decode()
+
+    assert call([1.0], n=0)[0] == "GDN_ERR_BAD_OPTION"
+    assert call([1.0], reps=0)[0] == "GDN_ERR_BAD_OPTION"
+    assert call([1.0, -2.0])[0] == "GDN_ERR_BAD_OPTION"
+    assert call([float("nan")])[0] == "GDN_ERR_BAD_OPTION"
+    assert call([1.0], best_p=False)[0] == "GDN_ERR_NULL_ARG"
+    need = max(plan(lam=x)["workspace_bytes"] for x in (0.5, 2.0))
+    st, msg = call([0.5, 2.0], ws_bytes=need - 1)
+    assert st == "GDN_ERR_WORKSPACE_TOO_SMALL" and str(need) in msg
+
+
 def test_profile_read_without_profiled_call():
     l = lib()
     ms = (ctypes.c_float * 5)()

@@ -198,3 +198,23 @@ def test_grouped_combine(mode):
             else:
                 assert max(rel) < 1e-3, (n, h)
         base += P
+
+
+def test_calibrate_lambda_picks_a_candidate():
+    """gdn_calibrate_lambda times every candidate and returns one of them; the
+    forward with it matches the oracle like any other plan."""
+    import torch
+    import gated_deltanet_chunked_03_amd as gdn
+    inp = make_inputs(name="calib", B=1, T=64 * 40, h_qk=2, h_v=4, seed=41, gate="mixed")
+    d = to_device(inp)
+    lams = (0.5, 1.0, 2.0)
+    print("\n[calibrate] T=2560 h_v=4 on 16 CUs", flush=True)
+    best, ms = gdn.calibrate_lambda(d["q"], d["k"], d["v"], d["g"], d["beta"], lambdas=lams, reps=2,
+                                    scale=inp.scale, n_cu=16)
+    print(f"[calibrate] best {best}, ms {ms}", flush=True)
+    assert best in lams and all(x > 0 for x in ms.values())
+    assert ms[best] == min(ms.values())
+    o, _ = gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=inp.scale, lam=best, n_cu=16)
+    torch.cuda.synchronize()
+    o_ref, _, _ = oracle_run(inp)
+    assert_within_tolerance(o.float().cpu().numpy().reshape(o_ref.shape), o_ref, "o")
