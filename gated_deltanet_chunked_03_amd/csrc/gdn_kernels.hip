@@ -63,7 +63,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int CH = kChunk;
 constexpr int DK = kDim;
-constexpr int NTHR = 256;      // k_prep, k_cp_combine: 4 waves
+constexpr int NTHR = 256;      // k_cp_combine, k_decode: 4 waves
 constexpr int NTHR_CH = 512;   // chain kernels: 8 waves
 constexpr int NW_CH = NTHR_CH / 64;
 // Row strides of the LDS tiles. A 16x16x32 operand read has sixteen lanes on
@@ -74,6 +74,7 @@ constexpr int LDQ = 144;   // row stride (elements) of [64][128] bf16 tiles
 constexpr int LDKT = 80;   // row stride of [128][64] bf16 tiles
 constexpr int LDF = 72;    // row stride of [64][64] fp32 tiles
 constexpr int LDP = 80;    // row stride of [64][64] bf16 tiles
+constexpr int LDD = 20;    // row stride of the prep's transposed diagonal blocks (fp32)
 constexpr int kMaxFlags = kMaxSegsPerSeq;  // boundary flags the combine kernel keeps in LDS
 
 enum { kCpAuto = 0, kCpOff = 1, kCpExact = 2, kCpWarmup = 3 };
@@ -279,15 +280,18 @@ __device__ __forceinline__ float wave_scan(float s) {
 
 // ----------------------------------------------------------------------------
 // Chunk preparation kernel: gamma, beta and T = (I + A)^-1 of every (chunk,
-// value head). Chunks are independent, so this runs as a wide grid at two
-// workgroups per CU; the chain kernels then read T instead of solving the
-// triangular system inside their sequential loops.
+// value head). Chunks are independent, so one wave solves one chunk on its
+// own: its K rows come from HBM straight into MFMA operand registers, the
+// gram tiles below the diagonal stay in registers as the operands of the
+// block inversion, and only T (and A's diagonal blocks, for the substitution)
+// pass through the wave's own LDS. No barriers; six one-wave workgroups per
+// CU. The chain kernels then read T instead of solving the triangular system
+// inside their sequential loops.
 
-template <bool EX>
+// LDS of one prep wave.
 struct __attribute__((aligned(16))) PrepSmem {
-    bf16 k_rm[EX ? CH * LDQ : 8];   // K chunk token-major, d_k permuted (bf16 inputs)
-    float a[CH * LDF];              // A (strictly lower)
-    float t[CH * LDF];              // T = (I + A)^-1
+    float t[CH * LDF];      // T = (I + A)^-1 (the blocks above the diagonal stay zero)
+    float ad[CH * LDD];     // A's diagonal 16x16 blocks, transposed: row 16 b + m holds column m of block b
     float gam[CH];
     float beta[CH];
 };
@@ -297,100 +301,100 @@ __device__ __forceinline__ void lower_tile(int job, int& bi, int& bj) {
     bi = (job >= 6) ? 3 : (job >= 3) ? 2 : (job >= 1) ? 1 : 0;
     bj = job - (bi * (bi + 1)) / 2;
 }
-
-// The operand a gram lane group reads from a permuted LDS row (8 physical
-// elements at 8 g4 within a 32-wide k step), taken from a global fp32 row
-// instead: logical elements p[0..3] and p[8..11] with p = row + 32 ks +
-// 16 (g4 / 2) + 4 (g4 % 2). Zero if !valid.
-__device__ __forceinline__ void g_row8(const float* p, bool valid, bf16x8& hi, bf16x8& lo) {
-    if (valid) {
-        bf16x4 h0, l0, h1, l1;
-        split4(*reinterpret_cast<const f32x4*>(p), h0, l0);
-        split4(*reinterpret_cast<const f32x4*>(p + 8), h1, l1);
-        hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-        lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-        hi = bf16x8{};
-        lo = bf16x8{};
-    }
-}
 __device__ __forceinline__ bf16x8 lds_row8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// A[i][j] = beta_i exp(gamma_i - gamma_j) (k_i . k_j) for i > j, else 0, on
-// 16x16 tiles (16x16x32 MFMA; lane l: A row l % 16 and B column l % 16, each
-// with the 8 consecutive k values 8 (l / 16)..; C rows 4 (l / 16).. of column
-// l % 16). The ten lower tiles are jobs first, first + stride, ..., run as
-// interleaved chains; each is computed transposed (K rows of block bj against
-// K rows of block bi), so a lane ends up with four consecutive columns j of
-// one row i and stores them at once.
-template <typename IO, int NJOB>
-__device__ void gram_a(PrepSmem<Io<IO>::kExact>& sm, const IO* krow0, size_t ts, int nvalid, int first,
-                       int stride) {
-    constexpr bool EX = Io<IO>::kExact;
-    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
-    f32x4 acc[NJOB];
-    int bi[NJOB], bj[NJOB];
+// One chunk's K rows as 16x16x32 MFMA operands: lane 16 g + n holds row
+// 16 rb + n, d_k 32 ks + 8 g .. + 7 (the natural k order: both operands of the
+// gram use it). bf16: loaded raw (rows past the end read the last row again,
+// zeroed at use, so that the loads need no wait until then).
+template <typename IO> struct PrepIn;
+template <> struct PrepIn<bf16> { u32x4 k[4][4]; float g, b; int nv; };
+template <> struct PrepIn<float> { float g, b; int nv; };
+
+template <typename IO>
+__device__ __forceinline__ void prep_fetch(PrepIn<IO>& r, const Params& p, size_t tok0, int nvalid, int h, int hq) {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    if constexpr (Io<IO>::kExact) {
+        const size_t ts = (size_t)p.h_qk * DK;
+        const IO* kb = static_cast<const IO*>(p.k) + tok0 * ts + (size_t)hq * DK + 8 * g;
 #pragma unroll
-    for (int t = 0; t < NJOB; ++t) {
-        lower_tile(first + stride * t, bi[t], bj[t]);
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < 4; ++rb) {
+            const unsigned off = (unsigned)(min(16 * rb + n, nvalid - 1) * (int)ts);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) r.k[rb][ks] = *reinterpret_cast<const u32x4*>(kb + off + 32 * ks);
+        }
     }
+    const size_t idx = (tok0 + min(lane, nvalid - 1)) * (size_t)p.h_v + h;
+    r.g = p.g[idx];
+    r.b = p.beta[idx];
+    r.nv = nvalid;
+}
+
+// The ten lower gram tiles of the chunk, each computed transposed (K rows of
+// block bj against K rows of block bi): lane 16 g + n ends up with
+// k_(16 bi + n) . k_(16 bj + 4 g + e), e < 4 -- row i = 16 bi + n of A, four
+// consecutive columns, which is the A-operand layout of a 16x16x16 MFMA.
+template <typename IO>
+__device__ __forceinline__ void prep_gram(const PrepIn<IO>& r, const Params& p, size_t tok0, int hq, f32x4 acc[10]) {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int kb = 32 * ks + 8 * g4;                                 // physical (LDS)
-        const int kg = 32 * ks + 16 * (g4 >> 1) + 4 * (g4 & 1);          // logical start (HBM rows)
+    for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (Io<IO>::kExact) {
+        bf16x8 op[4][4];
 #pragma unroll
-        for (int t = 0; t < NJOB; ++t) {
-            const int ra = 16 * bj[t] + n, rb = 16 * bi[t] + n;
-            if constexpr (EX) {
-                acc[t] = mma16k32(lds_row8(sm.k_rm + ra * LDQ + kb), lds_row8(sm.k_rm + rb * LDQ + kb), acc[t]);
-            } else {
-                bf16x8 ah, al, bh, bl;
-                g_row8(krow0 + (size_t)ra * ts + kg, ra < nvalid, ah, al);
-                g_row8(krow0 + (size_t)rb * ts + kg, rb < nvalid, bh, bl);
-                acc[t] = mma16k32(ah, bh, acc[t]);
-                acc[t] = mma16k32(ah, bl, acc[t]);
-                acc[t] = mma16k32(al, bh, acc[t]);
+        for (int rb = 0; rb < 4; ++rb) {
+            const bool ok = 16 * rb + n < r.nv;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                op[rb][ks] = __builtin_bit_cast(bf16x8, ok ? r.k[rb][ks] : u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int t = 0; t < 10; ++t) {
+                int bi, bj;
+                lower_tile(t, bi, bj);
+                acc[t] = mma16k32(op[bj][ks], op[bi][ks], acc[t]);
+            }
+    } else {
+        // fp32 inputs: rows loaded at use and split hi/lo (three products per k step)
+        const size_t ts = (size_t)p.h_qk * DK;
+        const float* kb = static_cast<const float*>(p.k) + tok0 * ts + (size_t)hq * DK + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 hi[4], lo[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int row = 16 * rb + n;
+                const float* src = kb + (size_t)min(row, r.nv - 1) * ts + 32 * ks;
+                f32x4 x0 = *reinterpret_cast<const f32x4*>(src), x1 = *reinterpret_cast<const f32x4*>(src + 4);
+                if (row >= r.nv) x0 = x1 = f32x4{0.f, 0.f, 0.f, 0.f};
+                split8(x0, x1, hi[rb], lo[rb]);
+            }
+#pragma unroll
+            for (int t = 0; t < 10; ++t) {
+                int bi, bj;
+                lower_tile(t, bi, bj);
+                acc[t] = mma16k32(hi[bj], hi[bi], acc[t]);
+                acc[t] = mma16k32(hi[bj], lo[bi], acc[t]);
+                acc[t] = mma16k32(lo[bj], hi[bi], acc[t]);
             }
         }
     }
-    // acc[t][r] = k_(j0 + r) . k_i. Off the diagonal the lane stores A[i][j0 .. j0 + 3]
-    // in row i; a diagonal tile is stored transposed (A[j0 + r][i] in row i, the
-    // column the substitution in inv_diag reads).
-#pragma unroll
-    for (int t = 0; t < NJOB; ++t) {
-        const int i = 16 * bi[t] + n, j0 = 16 * bj[t] + 4 * g4;
-        const float gi = sm.gam[i], bt = sm.beta[i];
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(sm.gam + j0);
-        f32x4 v;
-        if (bi[t] == bj[t]) {
-            const f32x4 bj4 = *reinterpret_cast<const f32x4*>(sm.beta + j0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (j0 + r > i) ? bj4[r] * __expf(gj[r] - gi) * acc[t][r] : 0.f;
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = bt * __expf(gi - gj[r]) * acc[t][r];
-        }
-        *reinterpret_cast<f32x4*>(sm.a + i * LDF + j0) = v;
-    }
 }
 
-// Diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution, column
-// by column: lane 16 b + j solves column j of block b in registers; step m
-// fixes x_m and removes its share from the rows below, reading column m of
-// the block (gram_a stores the diagonal tiles transposed, so that column is
-// one LDS row, read as a broadcast). Every wave solves all four blocks and
-// writes them (identical values), so each can read the blocks back without
-// waiting for the others.
-template <bool EX>
-__device__ void inv_diag(PrepSmem<EX>& sm) {
+// Diagonal 16x16 blocks of T by forward substitution, column by column: lane
+// 16 b + j solves column j of block b in registers; step m fixes x_m and
+// removes its share from the rows below, reading column m of the block (one
+// LDS row of ad, a broadcast within the lane's block).
+__device__ void prep_inv_diag(PrepSmem& sm) {
     const int lane = lane_id(), b = 16 * (lane >> 4), j = lane & 15;
     float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
     for (int m = 0; m < 15; ++m) {
-        const float* col = sm.a + (b + m) * LDF + b;   // A[b + i][b + m] at col[i], i > m
+        const float* col = sm.ad + (b + m) * LDD;   // A[b + i][b + m] at col[i], i > m
         f32x4 c4[4];
 #pragma unroll
         for (int q = (m + 1) / 4; q < 4; ++q) c4[q] = *reinterpret_cast<const f32x4*>(col + 4 * q);
@@ -403,18 +407,21 @@ __device__ void inv_diag(PrepSmem<EX>& sm) {
 
 // 16x16 block products on hi/lo bf16 operands (16x16x16 MFMA; lane l: A row
 // l % 16 with k 4 (l / 16) .. + 4; B and C column l % 16 with rows 4 (l / 16) .. + 4).
-// The A operand is the LDS block at (r0, c0) of an fp32 [64][LDF] matrix.
-__device__ __forceinline__ f32x4 mm_lds(const float* m, int r0, int c0, const f32x4& bv, f32x4 acc) {
-    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
-    const f32x4 av = *reinterpret_cast<const f32x4*>(m + (r0 + n) * LDF + c0 + 4 * g4);
-    bf16x4 ah, al, bh, bl;
-    split4(av, ah, al);
+__device__ __forceinline__ f32x4 mm_split(const bf16x4& ah, const bf16x4& al, const f32x4& bv, f32x4 acc) {
+    bf16x4 bh, bl;
     split4(bv, bh, bl);
     acc = mma16(ah, bh, acc);
     acc = mma16(ah, bl, acc);
     return mma16(al, bh, acc);
 }
-// The LDS block at (r0, c0) in the C (B operand) layout.
+// ... with the A operand the LDS block at (r0, c0) of an fp32 [64][LDF] matrix
+__device__ __forceinline__ f32x4 mm_lds(const float* m, int r0, int c0, const f32x4& bv, f32x4 acc) {
+    const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
+    bf16x4 ah, al;
+    split4(*reinterpret_cast<const f32x4*>(m + (r0 + n) * LDF + c0 + 4 * g4), ah, al);
+    return mm_split(ah, al, bv, acc);
+}
+// The LDS block at (r0, c0) in the C (B operand) layout, and back.
 __device__ __forceinline__ f32x4 blk_c(const float* m, int r0, int c0) {
     const int lane = lane_id(), n = lane & 15, g4 = lane >> 4;
     f32x4 v;
@@ -428,90 +435,46 @@ __device__ __forceinline__ void blk_store(float* m, int r0, int c0, const f32x4&
     for (int r = 0; r < 4; ++r) m[(r0 + 4 * g4 + r) * LDF + c0 + n] = v[r];
 }
 
-// Blocks below the diagonal, from T_iJ = -T_ii sum_{m=J}^{i-1} A_im T_mJ, four
-// waves with one block of the lower-left quadrant each (block row i = 2 + w / 2,
-// column j = w % 2):
-//   T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (the waves that need them
-//   compute them, and write them),
-//   X_aj = sum_{m=j}^{1} A_am T_mj (a = 2, 3),  T_ij = -sum_{a=2}^{i} T_ia X_aj.
-// T_32 enters as an A operand, so its waves write it to LDS and read it back
-// (after a wave-local fence; both write identical values).
-template <bool EX>
-__device__ void inv_off(PrepSmem<EX>& sm) {
-    const int w = wave_id(), bi = 2 + (w >> 1), bj = w & 1;
+// The six blocks below the diagonal by 2 x 2 block inversion of the 32-row
+// halves. With P, R the inverses of the upper-left and lower-right halves:
+//   T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,
+//   X = A_bl P (X_a0 = A_a0 T_00 + A_a1 T_10, X_a1 = A_a1 T_11, a = 2, 3),
+//   lower-left half = -R X (T_2j = -T_22 X_2j, T_3j = -(T_32 X_2j + T_33 X_3j)).
+// A's blocks come from registers (hi/lo, tiles 1, 3, 4, 6, 7, 8 of the gram);
+// T's blocks enter as A operands from LDS and as B operands in the C layout.
+__device__ void prep_inv_off(PrepSmem& sm, const bf16x4 ah[10], const bf16x4 al[10]) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 t10 = z;
-    if (bj == 0) {
-        t10 = -mm_lds(sm.t, 16, 16, mm_lds(sm.a, 16, 0, blk_c(sm.t, 0, 0), z), z);
-        if (w == 0) blk_store(sm.t, 16, 0, t10);
-    }
-    if (bi == 3) {
-        const f32x4 t32 = -mm_lds(sm.t, 48, 48, mm_lds(sm.a, 48, 32, blk_c(sm.t, 32, 32), z), z);
-        blk_store(sm.t, 48, 32, t32);
-    }
-    // X_2j and (for block row 3) X_3j
-    f32x4 x2, x3 = z;
-    if (bj == 0) {
-        const f32x4 t00 = blk_c(sm.t, 0, 0);
-        x2 = mm_lds(sm.a, 32, 16, t10, mm_lds(sm.a, 32, 0, t00, z));
-        if (bi == 3) x3 = mm_lds(sm.a, 48, 16, t10, mm_lds(sm.a, 48, 0, t00, z));
-    } else {
-        const f32x4 t11 = blk_c(sm.t, 16, 16);
-        x2 = mm_lds(sm.a, 32, 16, t11, z);
-        if (bi == 3) x3 = mm_lds(sm.a, 48, 16, t11, z);
-    }
+    const f32x4 t00 = blk_c(sm.t, 0, 0), t11 = blk_c(sm.t, 16, 16), t22 = blk_c(sm.t, 32, 32);
+    const f32x4 t10 = -mm_lds(sm.t, 16, 16, mm_split(ah[1], al[1], t00, z), z);
+    const f32x4 t32 = -mm_lds(sm.t, 48, 48, mm_split(ah[8], al[8], t22, z), z);
+    blk_store(sm.t, 16, 0, t10);
+    blk_store(sm.t, 48, 32, t32);
+    const f32x4 x20 = mm_split(ah[4], al[4], t10, mm_split(ah[3], al[3], t00, z));
+    const f32x4 x21 = mm_split(ah[4], al[4], t11, z);
+    const f32x4 x30 = mm_split(ah[7], al[7], t10, mm_split(ah[6], al[6], t00, z));
+    const f32x4 x31 = mm_split(ah[7], al[7], t11, z);
+    // T_32 is read back as an A operand: the wave's own stores above come first
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    f32x4 r;
-    if (bi == 2) r = -mm_lds(sm.t, 32, 32, x2, z);
-    else r = -mm_lds(sm.t, 48, 48, x3, mm_lds(sm.t, 48, 32, x2, z));
-    blk_store(sm.t, 16 * bi, 16 * bj, r);
-}
-
-// Inputs of one chunk for k_prep, prefetched into registers: K rows (bf16;
-// thread t: row (t + 256 j) / 16, columns 8 ((t + 256 j) % 16) .. + 8; fp32 K
-// is read from HBM by the gram itself) and g, beta of token lane.
-template <typename IO> struct PrepIn;
-template <> struct PrepIn<bf16> { u32x4 k[4]; float g, b; };
-template <> struct PrepIn<float> { float g, b; };
-
-// Loads are unconditional (rows past the end of the sequence read its last
-// row) and the values of those rows are replaced by zeros afterwards.
-template <typename IO>
-__device__ __forceinline__ void prep_fetch(PrepIn<IO>& r, const Params& p, size_t tok0, int nvalid, int h, int hq) {
-    const size_t ts = (size_t)p.h_qk * DK;
-    if constexpr (Io<IO>::kExact) {
-        const IO* kb = static_cast<const IO*>(p.k) + tok0 * ts + (size_t)hq * DK;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int pc = threadIdx.x + NTHR * j, row = pc >> 4, c8 = (pc & 15) * 8;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + (size_t)min(row, nvalid - 1) * ts + c8);
-            r.k[j] = row < nvalid ? kv : z;
-        }
-    }
-    const int lane = lane_id();
-    const size_t idx = (tok0 + min(lane, nvalid - 1)) * (size_t)p.h_v + h;
-    const float g = p.g[idx], b = p.beta[idx];
-    r.g = lane < nvalid ? g : 0.f;
-    r.b = lane < nvalid ? b : 0.f;
+    blk_store(sm.t, 32, 0, -mm_lds(sm.t, 32, 32, x20, z));
+    blk_store(sm.t, 32, 16, -mm_lds(sm.t, 32, 32, x21, z));
+    blk_store(sm.t, 48, 0, -mm_lds(sm.t, 48, 48, x30, mm_lds(sm.t, 48, 32, x20, z)));
+    blk_store(sm.t, 48, 16, -mm_lds(sm.t, 48, 48, x31, mm_lds(sm.t, 48, 32, x21, z)));
 }
 
 // Work items are (value head, chunk slot) pairs, item f = h n_chunks + slot;
-// workgroup b walks items [b prep_cpw, (b + 1) prep_cpw), fetching the next
-// item's inputs while it works on the current one (one round of about two
-// workgroups per CU, however the chunks and heads factor). Per (chunk slot, value head), block b = slot h_v + h:
+// workgroup (one wave) b walks items [b prep_cpw, (b + 1) prep_cpw), fetching
+// the next item's inputs while it works on the current one. Per (chunk slot,
+// value head), block b = slot h_v + h:
 //   prep_T + b t_stride: T diag(beta) split into bf16 hi and lo, [part][row][k]
 //     (2 x 64 x 64), the k (column) axis in the kp order of the chain
 //     kernels' LDS operands (zeros above the diagonal);
 //   prep_GB + b gb_stride: gamma (64 fp32), then beta (64 fp32).
 template <typename IO>
-__global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
-    constexpr bool EX = Io<IO>::kExact;
-    __shared__ PrepSmem<EX> sm;
-    const int wave = wave_id(), lane = lane_id();
+__global__ __launch_bounds__(64) void k_prep(Params p) {
+    __shared__ PrepSmem sm;
+    const int lane = lane_id();
     const long long n_items = (long long)p.n_chunks * p.h_v;
     const long long f0 = (long long)blockIdx.x * p.prep_cpw, f1 = min(f0 + (long long)p.prep_cpw, n_items);
-    const size_t ts = (size_t)p.h_qk * DK;
     if (f0 >= f1) return;
     // item f -> head, chunk slot and the slot's tokens
     int h, slot, nvalid;
@@ -526,89 +489,101 @@ __global__ __launch_bounds__(NTHR, 2) void k_prep(Params p) {
         nvalid = min(CH, len - c * CH);
     };
     locate(f0);
-    // the blocks of T above the diagonal stay zero (the chunk loop writes the
-    // diagonal and lower blocks only); the loop's first barrier orders this
-    for (int i = threadIdx.x; i < CH * LDF / 4; i += NTHR)
-        reinterpret_cast<f32x4*>(sm.t)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the blocks of T above the diagonal stay zero (the loop writes the
+    // diagonal and lower blocks only)
+    for (int i = lane; i < CH * LDF / 4; i += 64) reinterpret_cast<f32x4*>(sm.t)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     PrepIn<IO> nxt;
     prep_fetch<IO>(nxt, p, tok0, nvalid, h, h / p.group);
     if (p.sink) {   // (null for the low-level entry, which has no workspace)
         // the loop body's stores (gamma, beta; T) come after its loads; the same
-        // stores to the scratch line here make the loop's entry look alike, so
-        // that the wait at its head covers the loads only
+        // number of stores to the scratch line here make the loop's entry look
+        // alike, so that the wait at its head covers the loads only
         float* sk = p.sink + 32 * lane;
         sk[0] = 0.f;
         sk[1] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sk + 4 * i) = u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(sk + 4 * (i & 3)) = u32x4{0u, 0u, 0u, 0u};
     }
     for (long long f = f0; f < f1; ++f) {
         const size_t tok_cur = tok0;
-        const int nv_cur = nvalid, h_cur = h, slot_cur = slot;
-        const IO* krow0 = static_cast<const IO*>(p.k) + tok_cur * ts + (size_t)(h_cur / p.group) * DK;
-        if constexpr (EX) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int pc = threadIdx.x + NTHR * j, row = pc >> 4, c8 = (pc & 15) * 8;
-                *reinterpret_cast<u32x2*>(sm.k_rm + row * LDQ + pk(c8)) = u32x2{nxt.k[j][0], nxt.k[j][1]};
-                *reinterpret_cast<u32x2*>(sm.k_rm + row * LDQ + pk(c8 + 4)) = u32x2{nxt.k[j][2], nxt.k[j][3]};
-            }
-        }
-        {   // every wave scans and writes the same values (no branch in the loop)
-            const float gam = wave_scan(nxt.g);
+        const int h_cur = h, slot_cur = slot, hq_cur = h / p.group;
+        const PrepIn<IO> cur = nxt;
+        {
+            const bool ok = lane < cur.nv;
+            const float gam = wave_scan(ok ? cur.g : 0.f), bt = ok ? cur.b : 0.f;
             sm.gam[lane] = gam;
-            sm.beta[lane] = nxt.b;
+            sm.beta[lane] = bt;
             float* gb = p.prep_GB + ((size_t)slot_cur * p.h_v + h_cur) * (size_t)p.gb_stride;
             gb[lane] = gam;
-            gb[CH + lane] = nxt.b;
+            gb[CH + lane] = bt;
         }
-        __syncthreads();
-        // always a prefetch (the last slot fetches itself again), so that every
+        // always a prefetch (the last item fetches itself again), so that every
         // iteration has the same memory operations and the compiler's waits on
         // them stay exact across the loop
         locate(min(f + 1, f1 - 1));
         prep_fetch<IO>(nxt, p, tok0, nvalid, h, h / p.group);
-        // the ten tiles: three per wave, the last wave takes one
-        if (wave < 3) gram_a<IO, 3>(sm, krow0, ts, nv_cur, wave, 3);
-        else gram_a<IO, 1>(sm, krow0, ts, nv_cur, 9, 1);
-        __syncthreads();
-        // beta of the columns this thread scales T by below, read now: the next
-        // chunk's staging rewrites the gate arrays as soon as a wave has passed
-        // the barrier that ends this chunk's inversion
-        f32x4 bcol[4];
+        f32x4 acc[10];
+        prep_gram<IO>(cur, p, tok_cur, hq_cur, acc);
+        // A = beta_i exp(gamma_i - gamma_j) k_i . k_j below the diagonal: the
+        // off-diagonal tiles stay as hi/lo A operands, the diagonal ones go to
+        // ad transposed (position (i, j - 16 b) holds A[j][i], j > i)
+        bf16x4 ah[10], al[10];
         {
-            const int q = (threadIdx.x >> 1) & 1;
+            const int n = lane & 15, g4 = lane >> 4;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int l0 = 32 * q + 4 * (2 * (threadIdx.x & 1) + u);
-                bcol[2 * u] = *reinterpret_cast<const f32x4*>(sm.beta + l0);
-                bcol[2 * u + 1] = *reinterpret_cast<const f32x4*>(sm.beta + l0 + 16);
+            for (int t = 0; t < 10; ++t) {
+                int bi, bj;
+                lower_tile(t, bi, bj);
+                const int i = 16 * bi + n, j0 = 16 * bj + 4 * g4;
+                const float gi = sm.gam[i];
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(sm.gam + j0);
+                f32x4 v;
+                if (bi == bj) {
+                    const f32x4 bj4 = *reinterpret_cast<const f32x4*>(sm.beta + j0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = (j0 + r > i) ? bj4[r] * __expf(gj[r] - gi) * acc[t][r] : 0.f;
+                    *reinterpret_cast<f32x4*>(sm.ad + i * LDD + 4 * g4) = v;
+                } else {
+                    const float bt = sm.beta[i];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = bt * __expf(gi - gj[r]) * acc[t][r];
+                    split4(v, ah[t], al[t]);
+                }
             }
         }
-        inv_diag<EX>(sm);
-        // the diagonal blocks this wave reads next are the ones it just wrote
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        inv_off<EX>(sm);
-        __syncthreads();
-        // (the next chunk's LDS writes touch k_rm and the gate arrays, whose
-        // last reads come before the previous barrier; T is rewritten after two
-        // more).
-        // T diag(beta) with its column (token) axis in kp order: thread t takes
-        // row t / 4 and the physical 8-element pieces 32 q + 8 a, q = (t / 2) % 2,
-        // a = 2 (t % 2) + (0, 1); piece 32 q + 8 a holds logical columns
-        // 32 q + 4 a + (0..3) and 32 q + 16 + 4 a + (0..3).
+        prep_inv_diag(sm);
+        // the off-diagonal blocks read the diagonal ones just written
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        prep_inv_off(sm, ah, al);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        // T diag(beta) with its column (token) axis in kp order: lane l takes
+        // rows 16 u + l / 4 and the physical 8-element pieces 32 q + 8 a,
+        // q = (l / 2) % 2, a = 2 (l % 2) + (0, 1); piece 32 q + 8 a holds
+        // logical columns 32 q + 4 a + (0..3) and 32 q + 16 + 4 a + (0..3).
         bf16* Tg = reinterpret_cast<bf16*>(p.prep_T + ((size_t)slot_cur * p.h_v + h_cur) * (size_t)p.t_stride);
         {
-            const int row = threadIdx.x >> 2, q = (threadIdx.x >> 1) & 1;
+            const int q = (lane >> 1) & 1;
+            f32x4 bcol[4];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int a = 2 * (threadIdx.x & 1) + u, l0 = 32 * q + 4 * a, l1 = l0 + 16;
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l0) * bcol[2 * u];
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l1) * bcol[2 * u + 1];
-                bf16x8 hi, lo;
-                split8(x0, x1, hi, lo);
-                *reinterpret_cast<bf16x8*>(Tg + row * CH + 32 * q + 8 * a) = hi;
-                *reinterpret_cast<bf16x8*>(Tg + (CH + row) * CH + 32 * q + 8 * a) = lo;
+            for (int a2 = 0; a2 < 2; ++a2) {
+                const int l0 = 32 * q + 4 * (2 * (lane & 1) + a2);
+                bcol[2 * a2] = *reinterpret_cast<const f32x4*>(sm.beta + l0);
+                bcol[2 * a2 + 1] = *reinterpret_cast<const f32x4*>(sm.beta + l0 + 16);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int row = 16 * u + (lane >> 2);
+#pragma unroll
+                for (int a2 = 0; a2 < 2; ++a2) {
+                    const int a = 2 * (lane & 1) + a2, l0 = 32 * q + 4 * a, l1 = l0 + 16;
+                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l0) * bcol[2 * a2];
+                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l1) * bcol[2 * a2 + 1];
+                    bf16x8 hi, lo;
+                    split8(x0, x1, hi, lo);
+                    *reinterpret_cast<bf16x8*>(Tg + row * CH + 32 * q + 8 * a) = hi;
+                    *reinterpret_cast<bf16x8*>(Tg + (CH + row) * CH + 32 * q + 8 * a) = lo;
+                }
             }
         }
     }
@@ -2609,7 +2584,7 @@ static int launched() { return (int)hipGetLastError(); }
 int launch_prep(const Params& p, int io, void* stream) {
     if (p.n_chunks <= 0) return 0;
     const long long items = (long long)p.n_chunks * p.h_v;
-    const dim3 grid((unsigned)((items + p.prep_cpw - 1) / p.prep_cpw)), block(NTHR);
+    const dim3 grid((unsigned)((items + p.prep_cpw - 1) / p.prep_cpw)), block(64);
     if (io == kIoBf16) hipLaunchKernelGGL(k_prep<bf16>, grid, block, 0, (hipStream_t)stream, p);
     else hipLaunchKernelGGL(k_prep<float>, grid, block, 0, (hipStream_t)stream, p);
     return launched();
