@@ -39,7 +39,7 @@ struct Plan {
     int n_seqs = 0;
     std::vector<int> len;       // tokens per sequence
     int n_chunks_total = 0, n_chunks_max = 0;
-    int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0;
+    int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0, cp_order = 0;
     float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
     int comb_G = 0, comb_J = 0;   // grouped combine (0: one chain)
     size_t off_sink = 0, off_T = 0, off_GB = 0, off_state = 0, off_M = 0, off_H = 0, off_warm = 0;
@@ -199,6 +199,13 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
         // so the plan assumes the share the pages report (most heads forget fast:
         // 30 % exact, at least one). Grouped when that estimate beats the single
         // chain by more than the two extra launches (~4 steps).
+        // k_cp_prep puts the exact boundaries' workgroups (two each) first
+        // when, with the same 30 % estimate, they fit in about one round
+        // (2 E <= 5/4 CUs); with more, head-major order measured faster.
+        {
+            const long long pairs = (long long)(P.n_segments - P.n_seqs) * d->h_v, est = (3 * pairs + 9) / 10;
+            P.cp_order = 4 * (2 * est) <= 5LL * P.n_cu ? 1 : 0;
+        }
         const int nb = P.P_max - 1;
         const long long heads = std::max(1LL, ((long long)P.n_seqs * d->h_v * 3 + 9) / 10);
         double best = nb;
@@ -262,6 +269,7 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
     p.cp_mode = d->cp_mode;
     p.n_segments = P.n_segments;
     p.n_chunks = P.n_chunks_total;
+    p.cp_order = P.cp_order;
     p.log_eps = std::log(P.eps);
     p.t_stride = (int64_t)gdn::kChunk * gdn::kChunk;
     p.gb_stride = 2 * gdn::kChunk;

@@ -54,6 +54,7 @@ struct Params {
     int32_t cp_mode;          // gdn_cp_mode
     int32_t n_segments;
     int32_t n_chunks;
+    int32_t cp_order;         // k_cp_prep work order: 1 exact boundaries first, 0 head-major
     float log_eps;            // log(noise floor)
     float scale;
 };

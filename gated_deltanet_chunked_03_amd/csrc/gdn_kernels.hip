@@ -461,6 +461,57 @@ __device__ void prep_inv_off(PrepSmem& sm, const bf16x4 ah[10], const bf16x4 al[
     blk_store(sm.t, 48, 16, -mm_lds(sm.t, 48, 48, x31, mm_lds(sm.t, 48, 32, x21, z)));
 }
 
+// Gate-driven choice for the boundary at chunk a of a sequence (the start
+// of segment a / L): warm up iff the log-decay over the window of w chunks
+// before the boundary is at most log(noise floor) (or the window reaches the
+// sequence start, where the warm-up is exact). The warm-up then scans the
+// shortest run of chunks before the boundary (wq <= w) whose log-decay is
+// already at most log(noise floor); the state it misses is bounded by that
+// decay times the state at the run's start. Chunk log-decays are the gate
+// sums in the order of the gamma scan (the chunks before a boundary are
+// whole; tok_last is the first token of chunk a - 1). Written to the
+// boundary flags as class | wq << 8, class 0 (exact map), 1 (warm-up) or
+// 2 (warm-up from the sequence start, exact); k_cp_prep and the combine read
+// them.
+__device__ void classify_boundary(const Params& p, int seq, int N, int a, int h, size_t tok_last) {
+    const int lane = lane_id();
+    int cls = 0, wq = p.w;
+    if (p.cp_mode == kCpExact) {
+        cls = 0;
+    } else if (a - p.w <= 0) {
+        cls = 2;
+        wq = a;
+    } else {
+        float gl[8], sums[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)   // chunks a - 1 - j >= a - w >= 1 for j < w
+            gl[j] = j < p.w ? p.g[(tok_last - (size_t)j * CH + lane) * (size_t)p.h_v + h] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            sums[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan(gl[j])), 63));
+        float cum = 0.f;
+        int found = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            cum += sums[j];
+            if (!found && j < p.w && cum <= p.log_eps) found = j + 1;
+        }
+        if (found) {
+            cls = 1;
+            wq = found;
+        } else {
+            cls = (p.cp_mode == kCpWarmup) ? 1 : 0;
+        }
+    }
+    int seg_base = 0;
+    if (!p.cu) {
+        seg_base = seq * n_segs_of(N, p.L);
+    } else {
+        for (int n = 0; n < seq; ++n) seg_base += n_segs_of(n_chunks_of(p.cu[n + 1] - p.cu[n]), p.L);
+    }
+    if (lane == 0) p.warm[(size_t)(seg_base + a / p.L) * p.h_v + h] = cls == 0 ? 0 : (cls | (wq << 8));
+}
+
 // Work items are (value head, chunk slot) pairs, item f = h n_chunks + slot;
 // workgroup (one wave) b walks items [b prep_cpw, (b + 1) prep_cpw), fetching
 // the next item's inputs while it works on the current one. Per (chunk slot,
@@ -477,17 +528,26 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
     const long long f0 = (long long)blockIdx.x * p.prep_cpw, f1 = min(f0 + (long long)p.prep_cpw, n_items);
     if (f0 >= f1) return;
     // item f -> head, chunk slot and the slot's tokens
-    int h, slot, nvalid;
+    int h, slot, nvalid, seq, c, len;
     size_t tok0;
     auto locate = [&](long long f) {
         h = (int)(f / p.n_chunks);
         slot = (int)(f - (long long)h * p.n_chunks);
-        int seq, c, len;
         size_t tok_s;
         locate_chunk(p, slot, seq, c, len, tok_s);   // slot < n_chunks: always found
         tok0 = tok_s + (size_t)c * CH;
         nvalid = min(CH, len - c * CH);
     };
+    // the last chunk before a segment boundary classifies the boundary; done
+    // first, so that its loads overlap those of the first item, and outside
+    // the item loop, whose memory operations then stay branch-free
+    if (p.warm) {
+        for (long long f = f0; f < f1; ++f) {
+            locate(f);
+            const int N = n_chunks_of(len);
+            if ((c + 1) % p.L == 0 && c + 1 < N) classify_boundary(p, seq, N, c + 1, h, tok0);
+        }
+    }
     locate(f0);
     // the blocks of T above the diagonal stay zero (the loop writes the
     // diagonal and lower blocks only)
@@ -1183,55 +1243,62 @@ __device__ void store_m_operand(bf16* buf, const f32x4 S[8], bf16* dst) {
     }
 }
 
-// Warm-up or exact segment map for the boundary before segment s >= 1.
-// blockIdx.x = 2 * segment slot + part; part 0: warm-up state or H, part 1: M.
-template <typename IO>
-__global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
-    __shared__ ChainSmem<Io<IO>::kExact> sm;
-    const int slot = blockIdx.x >> 1, part = blockIdx.x & 1, h = blockIdx.y, hq = h / p.group;
-    const SegLoc loc = locate_segment(p, slot);
-    if (loc.seq < 0 || loc.s == 0) return;
-    const int a = loc.s * p.L;  // first chunk of segment s
+// Class of boundary pair q = slot h_v + head from the flags k_prep wrote:
+// -1 (no boundary: a sequence's first segment), 0 exact, 1 or 2 warm-up
+// (window length in bits 8 and up).
+__device__ __forceinline__ int pair_class(const Params& p, int q, int& wq) {
+    const SegLoc loc = locate_segment(p, q / p.h_v);
+    const int v = p.warm[q];
+    wq = v >> 8;
+    return (loc.seq < 0 || loc.s == 0) ? -1 : (v & 255);
+}
 
-    // Gate-driven choice: warm up iff the log-decay over the window of w chunks
-    // before the boundary is at most log(noise floor) (or the window reaches
-    // the sequence start, where the warm-up is exact). The warm-up then scans
-    // the shortest run of chunks before the boundary (wq <= w) whose log-decay
-    // is already at most log(noise floor); the state it misses is bounded by
-    // that decay times the state at the run's start.
-    // warm: 0 exact map, 1 warm-up (decayed below the floor, or forced), 2 warm-up
-    // from the sequence start (exact)
-    int warm, wq = p.w;
-    if (p.cp_mode == kCpExact) {
-        warm = 0;
-    } else if (a - p.w <= 0) {
-        warm = 2;
-        wq = a;
-    } else {
-        // chunk a - 1 - j (a full chunk: only a sequence's last chunk is short) -> red[j]
-        const int wave = wave_id(), lane = lane_id();
-        for (int j = wave; j < p.w; j += NW_CH) {
-            float s = p.g[(loc.tok0 + (size_t)(a - 1 - j) * CH + lane) * (size_t)p.h_v + h];
+// Block-wide exclusive prefix sum of one int per thread (512 threads).
+__device__ __forceinline__ int block_excl_scan(int x, int* red, int& total) {
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    int v = x;
 #pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
-            if (lane == 0) sm.red[j] = s;
-        }
-        __syncthreads();
-        float cum = 0.f;
-        int found = 0;
-        for (int j = 0; j < p.w && !found; ++j) {
-            cum += sm.red[j];
-            if (cum <= p.log_eps) found = j + 1;
-        }
-        if (found) {
-            warm = 1;
-            wq = found;
-        } else {
-            warm = (p.cp_mode == kCpWarmup) ? 1 : 0;
-        }
-        __syncthreads();
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(v, d, 64);
+        if (lane >= d) v += y;
     }
-    if (part == 0 && threadIdx.x == 0) p.warm[(size_t)(loc.seg_base + loc.s) * p.h_v + h] = warm;
+    if (lane == 63) red[w] = v;
+    __syncthreads();
+    int off = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < NW_CH; ++i) {
+        const int r = red[i];
+        if (i < w) off += r;
+        total += r;
+    }
+    return off + v - x;
+}
+
+// Warm-up or exact segment map for one boundary. The grid has a workgroup
+// for every (segment slot, part, head); part 0: the warm-up state or H,
+// part 1: M. Which boundaries need the long exact chains shows only on the
+// device (k_prep classifies them from the gates). The plan picks the order
+// in which the workgroups take the items:
+//   exact first (cp_order 1, when the exact chains should fit in about one
+//   round): every workgroup ranks the boundary flags (one load each), then
+//   workgroup i < 2 E takes part i % 2 of the (i / 2)-th exact boundary (E of
+//   them), the next ones the warm-up boundaries (part 0 only), and the rest
+//   exit; workgroups start in index order, so no exact chain waits behind
+//   warm-ups, whatever heads they belong to;
+//   head-major (cp_order 0): workgroup i takes head i / (2 n_segments), then
+//   slot and part, which spreads the short warm-ups among the rounds of exact
+//   chains.
+// Boundaries are enumerated as q = slot h_v + head.
+// One (segment slot, part, head) item of k_cp_prep.
+template <typename IO>
+__device__ void cp_prep_item(const Params& p, ChainSmem<Io<IO>::kExact>& sm, int slot, int part, int h) {
+    const int hq = h / p.group;
+    const SegLoc loc = locate_segment(p, slot);
+    int wq;
+    const int warm = pair_class(p, slot * p.h_v + h, wq);
+    if (warm < 0) return;
+    const int a = loc.s * p.L;  // first chunk of segment s
     if (warm && part == 1) return;
     // the map of segment 0 is only applied to a nonzero initial state
     if (!warm && part == 1 && loc.s == 1 && !p.s_init) return;
@@ -1252,6 +1319,51 @@ __global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
         store_m_operand(reinterpret_cast<bf16*>(&sm), S,
                         reinterpret_cast<bf16*>(p.seg_M + state_off(loc.seg_base + loc.s - 1, p.h_v, h)));
     }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
+    __shared__ ChainSmem<Io<IO>::kExact> sm;
+    __shared__ int rank_red[2 * NW_CH + 4];
+    const int i = (int)blockIdx.x;
+    if (!p.cp_order) {   // head-major order
+        cp_prep_item<IO>(p, sm, (i % (2 * p.n_segments)) >> 1, i & 1, i / (2 * p.n_segments));
+        return;
+    }
+    const int n_pairs = p.n_segments * p.h_v;
+    const int per = (n_pairs + NTHR_CH - 1) / NTHR_CH, q0 = threadIdx.x * per, q1 = min(q0 + per, n_pairs);
+    int n_ex = 0, n_wu = 0;
+    for (int q = q0; q < q1; ++q) {
+        int wq;
+        const int c = pair_class(p, q, wq);
+        n_ex += c == 0;
+        n_wu += c > 0;
+    }
+    int tot_ex, tot_wu;
+    const int pre_ex = block_excl_scan(n_ex, rank_red, tot_ex);
+    const int pre_wu = block_excl_scan(n_wu, rank_red + NW_CH, tot_wu);
+    const bool want_ex = i < 2 * tot_ex;
+    const int r = want_ex ? i >> 1 : i - 2 * tot_ex;
+    if (!want_ex && r >= tot_wu) return;   // (uniform: every thread has the totals)
+    // the thread whose range holds rank r of the wanted class names the boundary
+    const int pre = want_ex ? pre_ex : pre_wu, cnt = want_ex ? n_ex : n_wu;
+    if (r >= pre && r < pre + cnt) {
+        int k = pre;
+        for (int q = q0; q < q1; ++q) {
+            int wq;
+            const int c = pair_class(p, q, wq);
+            if (want_ex ? c == 0 : c > 0) {
+                if (k == r) {
+                    rank_red[2 * NW_CH] = q;
+                    break;
+                }
+                ++k;
+            }
+        }
+    }
+    __syncthreads();
+    const int q = rank_red[2 * NW_CH];
+    cp_prep_item<IO>(p, sm, q / p.h_v, want_ex ? (i & 1) : 0, q % p.h_v);
 }
 
 // Chains over the segment boundaries of one (sequence, head, 32-column
@@ -2451,7 +2563,7 @@ __global__ void k_debug_path(Params p, int32_t* path) {
     int nw = 0, ne = 0;
     for (int s = 1; s < P; ++s) {
         const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h];
-        nw += (f == 1);
+        nw += ((f & 255) == 1);
         ne += (f == 0);
     }
     path[idx] = (nw + ne == 0) ? 3 : (ne == 0 ? 1 : (nw == 0 ? 0 : 2));
@@ -2599,7 +2711,8 @@ int launch_wu(const Params& p, int io, void* stream) {
 }
 
 int launch_cp_prep(const Params& p, int io, void* stream) {
-    const dim3 grid(2 * p.n_segments, p.h_v), block(NTHR_CH);
+    // one workgroup per (segment slot, part, head); k_cp_prep hands them out
+    const dim3 grid((unsigned)(2LL * p.n_segments * p.h_v)), block(NTHR_CH);
     if (io == kIoBf16) hipLaunchKernelGGL(k_cp_prep<bf16>, grid, block, 0, (hipStream_t)stream, p);
     else hipLaunchKernelGGL(k_cp_prep<float>, grid, block, 0, (hipStream_t)stream, p);
     return launched();
