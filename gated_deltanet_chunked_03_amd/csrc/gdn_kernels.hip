@@ -74,7 +74,6 @@ constexpr int LDQ = 144;   // row stride (elements) of [64][128] bf16 tiles
 constexpr int LDKT = 80;   // row stride of [128][64] bf16 tiles
 constexpr int LDF = 72;    // row stride of [64][64] fp32 tiles
 constexpr int LDP = 80;    // row stride of [64][64] bf16 tiles
-constexpr int LDD = 20;    // row stride of the prep's transposed diagonal blocks (fp32)
 constexpr int kMaxFlags = kMaxSegsPerSeq;  // boundary flags the combine kernel keeps in LDS
 
 enum { kCpAuto = 0, kCpOff = 1, kCpExact = 2, kCpWarmup = 3 };
@@ -284,17 +283,24 @@ __device__ __forceinline__ float wave_scan(float s) {
 // own: its K rows come from HBM straight into MFMA operand registers, the
 // gram tiles below the diagonal stay in registers as the operands of the
 // block inversion, and only T (and A's diagonal blocks, for the substitution)
-// pass through the wave's own LDS. No barriers; six one-wave workgroups per
+// pass through the wave's own LDS. No barriers; eight one-wave workgroups per
 // CU. The chain kernels then read T instead of solving the triangular system
 // inside their sequential loops.
 
-// LDS of one prep wave.
+// LDS of one prep wave (about 18.5 KiB: eight waves per CU).
 struct __attribute__((aligned(16))) PrepSmem {
-    float t[CH * LDF];      // T = (I + A)^-1 (the blocks above the diagonal stay zero)
-    float ad[CH * LDD];     // A's diagonal 16x16 blocks, transposed: row 16 b + m holds column m of block b
+    float t[CH * LDF];      // T = (I + A)^-1 on and below the diagonal blocks; four of the
+                            // blocks above hold A's diagonal blocks (prep_ad)
     float gam[CH];
     float beta[CH];
 };
+
+// A's diagonal 16x16 block b, transposed (row m holds column m of the block,
+// row stride LDF), kept in an upper block of t, which T never uses: block b
+// goes to block (0, b + 1) for b < 3 and block 3 to (1, 3).
+__device__ __forceinline__ float* prep_ad(PrepSmem& sm, int b) {
+    return sm.t + (b == 3 ? 16 * LDF + 48 : 16 * (b + 1));
+}
 
 // Lower 16x16 tile number job (0..9) -> block row bi >= block column bj.
 __device__ __forceinline__ void lower_tile(int job, int& bi, int& bj) {
@@ -386,15 +392,16 @@ __device__ __forceinline__ void prep_gram(const PrepIn<IO>& r, const Params& p, 
 // Diagonal 16x16 blocks of T by forward substitution, column by column: lane
 // 16 b + j solves column j of block b in registers; step m fixes x_m and
 // removes its share from the rows below, reading column m of the block (one
-// LDS row of ad, a broadcast within the lane's block).
+// LDS row of the transposed block, a broadcast within the lane's block).
 __device__ void prep_inv_diag(PrepSmem& sm) {
     const int lane = lane_id(), b = 16 * (lane >> 4), j = lane & 15;
+    const float* ad = prep_ad(sm, lane >> 4);
     float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
     for (int m = 0; m < 15; ++m) {
-        const float* col = sm.ad + (b + m) * LDD;   // A[b + i][b + m] at col[i], i > m
+        const float* col = ad + m * LDF;   // A[b + i][b + m] at col[i], i > m
         f32x4 c4[4];
 #pragma unroll
         for (int q = (m + 1) / 4; q < 4; ++q) c4[q] = *reinterpret_cast<const f32x4*>(col + 4 * q);
@@ -549,9 +556,6 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
         }
     }
     locate(f0);
-    // the blocks of T above the diagonal stay zero (the loop writes the
-    // diagonal and lower blocks only)
-    for (int i = lane; i < CH * LDF / 4; i += 64) reinterpret_cast<f32x4*>(sm.t)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     PrepIn<IO> nxt;
     prep_fetch<IO>(nxt, p, tok0, nvalid, h, h / p.group);
     if (p.sink) {   // (null for the low-level entry, which has no workspace)
@@ -586,7 +590,7 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
         prep_gram<IO>(cur, p, tok_cur, hq_cur, acc);
         // A = beta_i exp(gamma_i - gamma_j) k_i . k_j below the diagonal: the
         // off-diagonal tiles stay as hi/lo A operands, the diagonal ones go to
-        // ad transposed (position (i, j - 16 b) holds A[j][i], j > i)
+        // LDS transposed (prep_ad(b): position (i - 16 b, j - 16 b) holds A[j][i], j > i)
         bf16x4 ah[10], al[10];
         {
             const int n = lane & 15, g4 = lane >> 4;
@@ -602,7 +606,7 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
                     const f32x4 bj4 = *reinterpret_cast<const f32x4*>(sm.beta + j0);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) v[r] = (j0 + r > i) ? bj4[r] * __expf(gj[r] - gi) * acc[t][r] : 0.f;
-                    *reinterpret_cast<f32x4*>(sm.ad + i * LDD + 4 * g4) = v;
+                    *reinterpret_cast<f32x4*>(prep_ad(sm, bi) + n * LDF + 4 * g4) = v;
                 } else {
                     const float bt = sm.beta[i];
 #pragma unroll
@@ -620,7 +624,9 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
         // T diag(beta) with its column (token) axis in kp order: lane l takes
         // rows 16 u + l / 4 and the physical 8-element pieces 32 q + 8 a,
         // q = (l / 2) % 2, a = 2 (l % 2) + (0, 1); piece 32 q + 8 a holds
-        // logical columns 32 q + 4 a + (0..3) and 32 q + 16 + 4 a + (0..3).
+        // logical columns 32 q + 4 a + (0..3) (block 2 q) and
+        // 32 q + 16 + 4 a + (0..3) (block 2 q + 1). Blocks above the diagonal
+        // (column block > row block u) are written as zeros, not read.
         bf16* Tg = reinterpret_cast<bf16*>(p.prep_T + ((size_t)slot_cur * p.h_v + h_cur) * (size_t)p.t_stride);
         {
             const int q = (lane >> 1) & 1;
@@ -637,8 +643,9 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
 #pragma unroll
                 for (int a2 = 0; a2 < 2; ++a2) {
                     const int a = 2 * (lane & 1) + a2, l0 = 32 * q + 4 * a, l1 = l0 + 16;
-                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l0) * bcol[2 * a2];
-                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l1) * bcol[2 * a2 + 1];
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 x0 = 2 * q <= u ? *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l0) * bcol[2 * a2] : z;
+                    const f32x4 x1 = 2 * q + 1 <= u ? *reinterpret_cast<const f32x4*>(sm.t + row * LDF + l1) * bcol[2 * a2 + 1] : z;
                     bf16x8 hi, lo;
                     split8(x0, x1, hi, lo);
                     *reinterpret_cast<bf16x8*>(Tg + row * CH + 32 * q + 8 * a) = hi;
