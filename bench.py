@@ -40,13 +40,13 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc", "gdn_kernels.hip")
 # HBM bytes per k_fwd launch on the tp8 workload (and per k_decode launch on the 256-row decode)
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
-# scaled by a 512 MiB copy's counts (FETCH x 1.99979, WRITE x 1.0). Valid only for the kernel
+# scaled by a 512 MiB copy's counts (FETCH x 1.99980, WRITE x 1.0). Valid only for the kernel
 # source with this hash; any other source reports null.
-MEASURED_TRAFFIC = {"tp8": {"sha256": "3ac544ea92d0de135111d85dea3939de7ffd26959461d7942f2e783eb14858a9",
-                            "read": 185296318, "write": 67649536},
+MEASURED_TRAFFIC = {"tp8": {"sha256": "b996bed6e3195926b9401f91041a727339b8e1a2b15b86f5aa74d6d5273a9a60",
+                            "read": 185289901, "write": 67649536},
                     # k_decode on the 256-row one-token decode, same passes and scale
-                    "decode256": {"sha256": "3ac544ea92d0de135111d85dea3939de7ffd26959461d7942f2e783eb14858a9",
-                                  "read": 135136448, "write": 134947136}}
+                    "decode256": {"sha256": "b996bed6e3195926b9401f91041a727339b8e1a2b15b86f5aa74d6d5273a9a60",
+                                  "read": 135138019, "write": 134952832}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
