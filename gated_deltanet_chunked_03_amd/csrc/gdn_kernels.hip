@@ -769,7 +769,7 @@ __device__ __forceinline__ void stage_chunk(ChainSmem<Io<IO>::kExact>& sm, const
                                             int b) {
     constexpr bool EX = Io<IO>::kExact;
     const int t = threadIdx.x, lane = lane_id(), m = t >> 5, c4 = (t & 31) * 4;
-    {   // every wave writes the same values (no branch in the chunk loop)
+    if (wave_id() == 0) {   // the gate factors: one wave (a scalar branch)
         const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.gl), 63));
         const float es = __expf(r.gl);
         sm.gam[lane] = r.gl;
@@ -1797,7 +1797,7 @@ __device__ void bwd_chain_fetch(const BwdParams& p, BwdChainIn& in, int f, size_
 
 __device__ void bwd_chain_stage(BwdChainSmem& sm, const BwdChainIn& in, float scale) {
     const int t = threadIdx.x, lane = lane_id(), m = t >> 5, c4 = (t & 31) * 4;
-    {   // every wave writes the same values
+    if (wave_id() == 0) {   // the gate factors: one wave (a scalar branch)
         const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, in.gl), 63));
         const float es = __expf(in.gl);
         sm.fr[lane] = __expf(gc - in.gl);
