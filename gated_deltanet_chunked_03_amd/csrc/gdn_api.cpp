@@ -95,6 +95,29 @@ gdn_status query_cu_count(int* n_cu) {
     return GDN_OK;
 }
 
+// Grouping of the segment combine over nb boundaries with `heads` chains
+// (see make_plan): the G with the least estimated steps, or G = 0 (one chain)
+// when none beats nb steps; J_max > 0 caps the group count (the workspace
+// holds that many group maps).
+void combine_grouping(int nb, long long heads, int n_cu, int J_max, int32_t* G_out, int32_t* J_out) {
+    *G_out = 0;
+    *J_out = 0;
+    double best = nb;
+    for (int G = 2; G < nb; ++G) {
+        const int J = (nb + G - 1) / G;
+        if (J < 2) break;
+        if (J_max > 0 && J > J_max) continue;
+        const long long wgs = 8LL * (J - 1) * heads, rounds = (wgs + n_cu - 1) / n_cu;
+        const double slow = 2 * wgs <= n_cu ? 1.0 : 2.5;
+        const double steps = slow * (G * rounds + G - 1) + std::max(J - 2, 0) + 4;
+        if (steps < best) {
+            best = steps;
+            *G_out = G;
+            *J_out = J;
+        }
+    }
+}
+
 // The AutoCP planner (section "Gate-Driven Automatic Intra-Card Context
 // Parallelism (AutoCP)": L = lambda sqrt(N) chunks per segment). Readings:
 // N is the chunk count of the longest sequence; lambda sqrt(N), rounded
@@ -206,21 +229,8 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
             const long long pairs = (long long)(P.n_segments - P.n_seqs) * d->h_v, est = (3 * pairs + 9) / 10;
             P.cp_order = 4 * (2 * est) <= 5LL * P.n_cu ? 1 : 0;
         }
-        const int nb = P.P_max - 1;
         const long long heads = std::max(1LL, ((long long)P.n_seqs * d->h_v * 3 + 9) / 10);
-        double best = nb;
-        for (int G = 2; G < nb; ++G) {
-            const int J = (nb + G - 1) / G;
-            if (J < 2) break;
-            const long long wgs = 8LL * (J - 1) * heads, rounds = (wgs + P.n_cu - 1) / P.n_cu;
-            const double slow = 2 * wgs <= P.n_cu ? 1.0 : 2.5;
-            const double steps = slow * (G * rounds + G - 1) + std::max(J - 2, 0) + 4;
-            if (steps < best) {
-                best = steps;
-                P.comb_G = G;
-                P.comb_J = J;
-            }
-        }
+        combine_grouping(P.P_max - 1, heads, P.n_cu, 0, &P.comb_G, &P.comb_J);
         if (P.comb_G) {
             const size_t grp = (size_t)P.n_seqs * P.comb_J * d->h_v * kStateElems * sizeof(float);
             P.off_GM = off; off = align_up(off + grp, 256);
@@ -481,6 +491,15 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
         b.seg_state = reinterpret_cast<float*>(w8 + P.off_state);
         b.seg_M = reinterpret_cast<float*>(w8 + P.off_M);
         b.seg_H = reinterpret_cast<float*>(w8 + P.off_H);
+        b.warm = reinterpret_cast<int32_t*>(w8 + P.off_warm);
+        // the backward links every head's segment ends (all exact); grouped only
+        // within the group maps the forward's workspace holds
+        if (P.comb_G)
+            combine_grouping(P.P_max - 1, (long long)P.n_seqs * desc->h_v, P.n_cu, P.comb_J, &b.comb_G, &b.comb_J);
+        if (b.comb_G) {
+            b.seg_GM = reinterpret_cast<float*>(w8 + P.off_GM);
+            b.seg_GH = reinterpret_cast<float*>(w8 + P.off_GH);
+        }
     }
     b.n_seqs = P.n_seqs;
     b.seq_len = desc->T;

@@ -24,7 +24,7 @@
 // Kernels: the forward (re-run with the state entering every chunk written
 // out), k_bwd_prep (T, P, gamma per chunk and head, and T^T / scale P^T as
 // bf16 hi/lo images), the reverse scan of dS over the chunks on the matrix
-// cores split by the forward's segments (k_bwd_chain_mma, k_bwd_link), every
+// cores split by the forward's segments (k_bwd_chain_mma, linked by k_cp_combine), every
 // other gradient of every chunk in parallel on the matrix cores
 // (k_bwd_chunk_mma) -- both in the forward's kernel file, whose operand
 // layouts they share -- and k_bwd_sum (query/key gradients summed over the

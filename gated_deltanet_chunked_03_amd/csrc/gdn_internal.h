@@ -98,6 +98,12 @@ struct BwdParams {
     float* seg_state;         // [n_segments][h_v] gradient of the state leaving segment s (s < P - 1)
     float* seg_M;             // [n_segments][h_v] map of segment s >= 1 (gradient at its end -> at its start)
     float* seg_H;             // [n_segments][h_v] the scan of segment s >= 1 from zero (last: from dS_final)
+                              // (seg_M, seg_H: segment s in slot P - 1 - s of its sequence, M in the
+                              // combine's operand layout; seg_state: gradient leaving s in slot P - 1 - s)
+    int32_t* warm;            // [n_segments][h_v] boundary flags for the combine (all exact)
+    float* seg_GM;            // the combine's group maps (comb_G > 0)
+    float* seg_GH;
+    int32_t comb_G, comb_J;   // the forward plan's combine grouping
     int32_t L, n_segments;    // chunks per segment, segments over all sequences
     int32_t n_seqs, seq_len, h_qk, h_v, group, n_chunks;
     float scale;

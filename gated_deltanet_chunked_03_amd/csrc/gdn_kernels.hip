@@ -24,25 +24,26 @@
 // S -> M S + H of the previous segment, k_cp_combine chains the exact maps,
 // and k_fwd runs every segment.
 //
-// Work layout of the chain kernels. A workgroup is 4 waves (256 lanes). Wave
-// w owns d_v columns [32w, 32w + 32): its 128 x 32 slice of S, its slice of
+// Work layout of the chain kernels. A workgroup is 8 waves (512 lanes). Wave
+// w owns d_v columns [16w, 16w + 16): its 128 x 16 slice of S, its slice of
 // Y / V' and of the output all stay in its registers, so the sequential state
-// chain never crosses waves. Operands that every wave needs (Q, K, K^T, V^T,
-// T, P = QK^T o D) are staged in LDS. Products use 32x32x16 bf16 MFMAs with
-// fp32 accumulation. Values that are not exact bf16 inputs (S, Y, V', T, P)
-// enter the MFMA as a hi + lo pair of bf16 (x = hi + lo to about 16 bits),
-// giving 2 or 3 MFMAs per product; diagonal gate factors are applied in fp32
-// on the accumulators instead of being rounded into operands.
+// chain never crosses waves; two waves share each SIMD. Operands that every
+// wave needs (Q, K, K^T, V^T, T, P = QK^T o D) are staged in LDS. Products use
+// 16x16x32 bf16 MFMAs with fp32 accumulation. Values that are not exact bf16
+// inputs (S, Y, V', T, P) enter the MFMA as a hi + lo pair of bf16 (x = hi +
+// lo to about 16 bits), giving 2 or 3 MFMAs per product; diagonal gate
+// factors are applied in fp32 on the accumulators instead of being rounded
+// into operands.
 //
-// Register layouts (verified on gfx950): 32x32x16 bf16 MFMA, lane l,
-//   A operand: row l % 32, 8 k values; B operand: column l % 32, 8 k values
-//   C/D: element i holds row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.
-// Element e of an operand is placed at k = kb + kperm(h, e), h = l / 32, with
-// kperm(h, e) = 4h + e (e < 4) or 8 + 4h + (e - 4); that is exactly where the
-// accumulator layout holds rows, so a 32-row accumulator tile serves directly
-// as the B operand of two consecutive k steps (elements 0..7 and 8..15), and,
-// as the A and B layouts mirror each other, as the A operand of the
-// transposed product.
+// Register layouts (gfx950), 16x16x32 bf16 MFMA, lane l = 16 g + c:
+//   A operand: row c, k values 8g .. 8g + 7; B operand: column c, the same k;
+//   C/D: rows 4g .. 4g + 3 of column c.
+// Two C tiles stacked (rows 0..15 and 16..31) hand lane group g the rows
+// 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3; with the contraction axis of every
+// LDS operand stored in the order kp (below), that is exactly a B (or,
+// mirrored, an A) operand, so accumulator tiles feed the next product without
+// shuffles. The segment combine and the 16x16 block products of the prep use
+// 32x32x16 and 16x16x16 MFMAs with their own layouts, described there.
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -2004,21 +2005,27 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
         bwd_chain_run<true, true>(p, sm, loc, 0, loc.N, h, D);
         if (p.dinit) store_state(p.dinit + state_off(loc.seq, p.h_v, h), D);
     } else if (MODE == kBwdMaps) {
+        // segment s goes to slot r = P - 1 - s: the segment ends are then linked
+        // by the forward's segment combine (boundary r + 1 applies M[r], H[r]),
+        // which runs the boundaries in increasing order
         const int part = blockIdx.x & 1;
         const SegLoc loc = locate_segment(p, blockIdx.x >> 1);
         if (loc.seq < 0 || loc.s == 0) return;
         const bool last = loc.s == loc.P - 1;
         if (part == 1 && last) return;
-        const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
+        const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N), r = loc.P - 1 - loc.s;
         if (part == 0) {
             if (last && p.dfinal) load_state(p.dfinal + state_off(loc.seq, p.h_v, h), D);
             else zero_state(D);
             bwd_chain_run<true, false>(p, sm, loc, c0, c1, h, D);
-            store_state(p.seg_H + state_off(loc.seg_base + loc.s, p.h_v, h), D);
+            store_state(p.seg_H + state_off(loc.seg_base + r, p.h_v, h), D);
+            if (threadIdx.x == 0) p.warm[(size_t)(loc.seg_base + r + 1) * p.h_v + h] = 0;   // exact
         } else {
             identity_state(D);
             bwd_chain_run<false, false>(p, sm, loc, c0, c1, h, D);
-            store_state(p.seg_M + state_off(loc.seg_base + loc.s, p.h_v, h), D);
+            // (the scan ended behind a barrier: its LDS is free for the staging)
+            store_m_operand(reinterpret_cast<bf16*>(&sm), D,
+                            reinterpret_cast<bf16*>(p.seg_M + state_off(loc.seg_base + r, p.h_v, h)));
         }
     } else {
         const SegLoc loc = locate_segment(p, blockIdx.x);
@@ -2027,73 +2034,11 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
             if (p.dfinal) load_state(p.dfinal + state_off(loc.seq, p.h_v, h), D);
             else zero_state(D);
         } else {
-            load_state(p.seg_state + state_off(loc.seg_base + loc.s, p.h_v, h), D);
+            load_state(p.seg_state + state_off(loc.seg_base + loc.P - 1 - loc.s, p.h_v, h), D);
         }
         const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
         bwd_chain_run<true, true>(p, sm, loc, c0, c1, h, D);
         if (loc.s == 0 && p.dinit) store_state(p.dinit + state_off(loc.seq, p.h_v, h), D);
-    }
-}
-
-// Links the segment ends of one sequence and head: with G(s) the gradient of
-// the state leaving segment s, G(P - 2) = seg_H[P - 1] and
-// G(s - 1) = seg_M[s] G(s) + seg_H[s] for s = P - 2 .. 1, into seg_state[s - 1].
-// Each map is staged in LDS split hi/lo with its columns in kp order (the
-// MFMA's A operand); the next map and H are loaded while a step computes.
-__global__ __launch_bounds__(NTHR_CH) void k_bwd_link(BwdParams p) {
-    __shared__ bf16 mh[DK * LDQ], ml[DK * LDQ];
-    const int seq = blockIdx.x, h = blockIdx.y, lane = lane_id(), c = lane & 15, g = lane >> 4, t = threadIdx.x;
-    int P, seg_base;
-    if (!p.cu) {
-        P = n_segs_of(n_chunks_of(p.seq_len), p.L);
-        seg_base = seq * P;
-    } else {
-        seg_base = 0;
-        for (int n = 0; n < seq; ++n) seg_base += n_segs_of(n_chunks_of(p.cu[n + 1] - p.cu[n]), p.L);
-        P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
-    }
-    if (P < 2) return;
-    f32x4 D[8], mreg[8], hreg[8];
-    auto fetch = [&](int s) {
-        const float* M = p.seg_M + state_off(seg_base + s, p.h_v, h);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mreg[j] = *reinterpret_cast<const f32x4*>(M + 4 * (t + NTHR_CH * j));
-        load_state(p.seg_H + state_off(seg_base + s, p.h_v, h), hreg);
-    };
-    load_state(p.seg_H + state_off(seg_base + P - 1, p.h_v, h), D);
-    store_state(p.seg_state + state_off(seg_base + P - 2, p.h_v, h), D);
-    if (P >= 3) fetch(P - 2);
-    for (int s = P - 2; s >= 1; --s) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {   // piece t + 512 j: row (t + 512 j) / 32, columns 4 ((t + 512 j) % 32) .. + 3
-            const int idx = t + NTHR_CH * j, row = idx >> 5, col = kp((idx & 31) * 4);
-            bf16x4 hi, lo;
-            split4(mreg[j], hi, lo);
-            *reinterpret_cast<bf16x4*>(mh + row * LDQ + col) = hi;
-            *reinterpret_cast<bf16x4*>(ml + row * LDQ + col) = lo;
-        }
-        f32x4 H[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) H[i] = hreg[i];
-        __syncthreads();
-        if (s > 1) fetch(s - 1);
-        SplitS ss;
-        split_state(D, ss);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int off = (16 * i + c) * LDQ + 32 * ks + 8 * g;
-                const bf16x8 ah = lds_op16(mh + off), al = lds_op16(ml + off);
-                H[i] = mma16k32(ah, ss.hi[ks], H[i]);
-                H[i] = mma16k32(ah, ss.lo[ks], H[i]);
-                H[i] = mma16k32(al, ss.hi[ks], H[i]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) D[i] = H[i];
-        store_state(p.seg_state + state_off(seg_base + s - 1, p.h_v, h), D);
-        __syncthreads();
     }
 }
 
@@ -2785,8 +2730,27 @@ int launch_bwd_chain_mma(const BwdParams& p, void* stream) {
     hipLaunchKernelGGL(k_bwd_chain_mma<kBwdMaps>, dim3(2 * p.n_segments, p.h_v), dim3(NTHR_CH), 0, s, p);
     int e = launched();
     if (e) return e;
-    hipLaunchKernelGGL(k_bwd_link, dim3(p.n_seqs, p.h_v), dim3(NTHR_CH), 0, s, p);
-    if ((e = launched())) return e;
+    // the segment ends: G(P - 2) = H_(P-1), G(s - 1) = M_s G(s) + H_s, in the
+    // reversed slots the maps pass wrote, by the forward's segment combine
+    // (no initial state: its first boundary takes H alone)
+    Params c{};
+    c.cu = p.cu;
+    c.n_seqs = p.n_seqs;
+    c.seq_len = p.seq_len;
+    c.h_qk = p.h_qk;
+    c.h_v = p.h_v;
+    c.group = p.group;
+    c.L = p.L;
+    c.n_segments = p.n_segments;
+    c.warm = p.warm;
+    c.seg_state = p.seg_state;
+    c.seg_M = p.seg_M;
+    c.seg_H = p.seg_H;
+    c.seg_GM = p.seg_GM;
+    c.seg_GH = p.seg_GH;
+    c.comb_G = p.comb_G;
+    c.comb_J = p.comb_J;
+    if ((e = launch_cp_combine(c, stream))) return e;
     hipLaunchKernelGGL(k_bwd_chain_mma<kBwdRerun>, dim3(p.n_segments, p.h_v), dim3(NTHR_CH), 0, s, p);
     return launched();
 }
