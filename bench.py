@@ -42,11 +42,11 @@ KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc", "gdn_ke
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
 # scaled by a 512 MiB copy's counts (FETCH x 1.99980, WRITE x 1.0). Valid only for the kernel
 # source with this hash; any other source reports null.
-MEASURED_TRAFFIC = {"tp8": {"sha256": "50b69a3ad79e61fe90667f47f500954442c58fa766f995c60088f70bcd3baeec",
-                            "read": 185299752, "write": 67649536},
+MEASURED_TRAFFIC = {"tp8": {"sha256": "e1baa3e911bd5581c47535f208469d1820c4dc7387b98dd3840656c15ccf7026",
+                            "read": 185275390, "write": 67649536},
                     # k_decode on the 256-row one-token decode, same passes and scale
-                    "decode256": {"sha256": "50b69a3ad79e61fe90667f47f500954442c58fa766f995c60088f70bcd3baeec",
-                                  "read": 135137923, "write": 134952448}}
+                    "decode256": {"sha256": "e1baa3e911bd5581c47535f208469d1820c4dc7387b98dd3840656c15ccf7026",
+                                  "read": 135125604, "write": 134952064}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
