@@ -220,16 +220,16 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
         // (measured), and a whole round more past the CUs. Only exact heads
         // compose; which heads are exact is decided on the device from the gates,
         // so the plan assumes the share the pages report (most heads forget fast:
-        // 30 % exact, at least one). Grouped when that estimate beats the single
-        // chain by more than the two extra launches (~4 steps).
+        // 30 % exact, to the nearest, at least one). Grouped when that estimate
+        // beats the single chain by more than the two extra launches (~4 steps).
         // k_cp_prep puts the exact boundaries' workgroups (two each) first
         // when, with the same 30 % estimate, they fit in about one round
         // (2 E <= 5/4 CUs); with more, head-major order measured faster.
         {
-            const long long pairs = (long long)(P.n_segments - P.n_seqs) * d->h_v, est = (3 * pairs + 9) / 10;
+            const long long pairs = (long long)(P.n_segments - P.n_seqs) * d->h_v, est = (3 * pairs + 5) / 10;
             P.cp_order = 4 * (2 * est) <= 5LL * P.n_cu ? 1 : 0;
         }
-        const long long heads = std::max(1LL, ((long long)P.n_seqs * d->h_v * 3 + 9) / 10);
+        const long long heads = std::max(1LL, ((long long)P.n_seqs * d->h_v * 3 + 5) / 10);
         combine_grouping(P.P_max - 1, heads, P.n_cu, 0, &P.comb_G, &P.comb_J);
         if (P.comb_G) {
             const size_t grp = (size_t)P.n_seqs * P.comb_J * d->h_v * kStateElems * sizeof(float);

@@ -111,10 +111,10 @@ def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
         # the grouped combine (the rule stated in gdn_api.cpp): G boundaries per group
         # when slow (G rounds + G - 1) + (J - 2) + 4 steps beat the single chain of
         # P - 1, J = ceil((P - 1) / G), assuming 30 % of the (sequence, head) pairs
-        # exact, 8 composing workgroups per group and exact head, slow = 2.5 past
-        # half the CUs
+        # exact (to the nearest, at least one), 8 composing workgroups per group and
+        # exact head, slow = 2.5 past half the CUs
         nb, best, G_exp = p["P_max"] - 1, float(p["P_max"] - 1), 0
-        heads = max(1, (B_ * h_v * 3 + 9) // 10)
+        heads = max(1, (B_ * h_v * 3 + 5) // 10)
         for G in range(2, nb):
             J = -(-nb // G)
             if J < 2:
