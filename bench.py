@@ -40,13 +40,13 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc", "gdn_kernels.hip")
 # HBM bytes per k_fwd launch on the tp8 workload (and per k_decode launch on the 256-row decode)
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
-# scaled by a 512 MiB copy's counts (FETCH x 1.99980, WRITE x 1.0). Valid only for the kernel
+# scaled by a 512 MiB copy's counts (FETCH x 1.99987, WRITE x 1.0). Valid only for the kernel
 # source with this hash; any other source reports null.
-MEASURED_TRAFFIC = {"tp8": {"sha256": "e1baa3e911bd5581c47535f208469d1820c4dc7387b98dd3840656c15ccf7026",
-                            "read": 185275390, "write": 67649536},
+MEASURED_TRAFFIC = {"tp8": {"sha256": "71742401b78dc2b0ff7ac00c9ec15f93cf4a945777605457df854c58bdafec56",
+                            "read": 185281751, "write": 67649536},
                     # k_decode on the 256-row one-token decode, same passes and scale
-                    "decode256": {"sha256": "e1baa3e911bd5581c47535f208469d1820c4dc7387b98dd3840656c15ccf7026",
-                                  "read": 135125604, "write": 134952064}}
+                    "decode256": {"sha256": "71742401b78dc2b0ff7ac00c9ec15f93cf4a945777605457df854c58bdafec56",
+                                  "read": 135130243, "write": 134955008}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak

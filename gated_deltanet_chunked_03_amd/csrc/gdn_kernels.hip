@@ -1347,6 +1347,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
         n_ex += c == 0;
         n_wu += c > 0;
     }
+    if (threadIdx.x == 0) rank_red[2 * NW_CH] = -1;   // (ordered before its use by the scans' barriers)
     int tot_ex, tot_wu;
     const int pre_ex = block_excl_scan(n_ex, rank_red, tot_ex);
     const int pre_wu = block_excl_scan(n_wu, rank_red + NW_CH, tot_wu);
@@ -1371,6 +1372,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
     }
     __syncthreads();
     const int q = rank_red[2 * NW_CH];
+    if (q < 0 || q >= n_pairs) return;   // (cannot happen: the ranks partition the boundaries)
     cp_prep_item<IO>(p, sm, q / p.h_v, want_ex ? (i & 1) : 0, q % p.h_v);
 }
 
