@@ -48,7 +48,7 @@ MEASURED_TRAFFIC = {"tp8": {"sha256": "71742401b78dc2b0ff7ac00c9ec15f93cf4a94577
                     "decode256": {"sha256": "71742401b78dc2b0ff7ac00c9ec15f93cf4a945777605457df854c58bdafec56",
                                   "read": 135130243, "write": 134955008}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
-PAGES_MS = {"tp8": 0.310, "tp2": 0.659, "tp1": 0.493}
+PAGES_MS = {"tp8": 0.310, "tp4": 0.486, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
@@ -209,7 +209,7 @@ def main():
     # of back-to-back work): fewer warm-up steps time the ramp, not the kernels
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="tp8",
-                    choices=["tiny", "tp8", "tp2", "tp1", "tp1_b4", "long"])
+                    choices=["tiny", "tp8", "tp4", "tp2", "tp1", "tp1_b4", "long"])
     ap.add_argument("--cp-mode", default="auto", choices=["auto", "off", "exact", "warmup"])
     ap.add_argument("--lam", type=float, default=0.0)
     ap.add_argument("--cpu-tokens", type=int, default=32768,

@@ -162,6 +162,7 @@ def make_inputs(B, T, h_qk, h_v, d_k=128, d_v=128, io_dtype="bf16", seed=0,
 CONFIGS = {
     "tiny":   dict(B=1, T=512, h_qk=1, h_v=1, io_dtype="f32", seed=1, gate="plain"),
     "tp8":    dict(B=1, T=32768, h_qk=2, h_v=8, seed=2, gate="mixed"),
+    "tp4":    dict(B=1, T=32768, h_qk=4, h_v=16, seed=6, gate="mixed"),
     "tp2":    dict(B=1, T=32768, h_qk=8, h_v=24, seed=3, gate="mixed"),
     "tp1":    dict(B=1, T=32768, h_qk=16, h_v=16, seed=4, gate="mixed"),
     "tp1_b4": dict(B=4, T=32768, h_qk=16, h_v=16, seed=40, gate="mixed"),

@@ -16,7 +16,7 @@ from gpu_util import assert_within_tolerance, oracle_run, to_device
 
 pytestmark = pytest.mark.gpu
 
-CASES = [("tiny", "auto"), ("tp8", "auto"), ("tp2", "auto"), ("tp1", "auto"),
+CASES = [("tiny", "auto"), ("tp8", "auto"), ("tp4", "auto"), ("tp2", "auto"), ("tp1", "auto"),
          ("tp1_b4", "auto"), ("tp1_b4", "off"), ("long", "auto")]
 
 
