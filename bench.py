@@ -39,11 +39,14 @@ METRIC = "GDN fwd ms & tokens/s at B=1,T=32768 per head config; % MFMA/HBM roofl
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc", "gdn_kernels.hip")
 # HBM bytes per k_fwd launch on the tp8 workload (and per k_decode launch on the 256-row decode)
-# from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
+# from rocprofv3 FETCH_SIZE / WRITE_SIZE passes (and k_fwd's executed bf16 MFMA work from an
+# MfmaFlopsBF16 pass),
 # scaled by a 512 MiB copy's counts (FETCH x 1.99987, WRITE x 1.0). Valid only for the kernel
 # source with this hash; any other source reports null.
 MEASURED_TRAFFIC = {"tp8": {"sha256": "71742401b78dc2b0ff7ac00c9ec15f93cf4a945777605457df854c58bdafec56",
-                            "read": 185281751, "write": 67649536},
+                            "read": 185281751, "write": 67649536,
+                            # MfmaFlopsBF16 per k_fwd launch (same kernel source)
+                            "mfma_flops": 73551314944},
                     # k_decode on the 256-row one-token decode, same passes and scale
                     "decode256": {"sha256": "71742401b78dc2b0ff7ac00c9ec15f93cf4a945777605457df854c58bdafec56",
                                   "read": 135130243, "write": 134955008}}
@@ -364,17 +367,24 @@ def main():
     achieved = nbytes / fwd_s / 1e9
     traffic = None
     mt = MEASURED_TRAFFIC.get(args.config)
+    executed_flops = None
     if mt and args.cp_mode == "auto" and args.lam == 0.0:
         sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
         if sha == mt["sha256"]:
             traffic = mt["read"] + mt["write"]
+            executed_flops = mt.get("mfma_flops")
     roofline = {"bound": "hbm", "kernel": "k_fwd", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": nbytes}
     mfma = {"algorithmic_tflops_fwd_kernel": round(flops / fwd_s / 1e12, 2),
             "peak_tflops_bf16": MFMA_BF16_PEAK_TFLOPS,
             "frac_algorithmic": round(flops / fwd_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "algorithmic_gflop": round(flops / 1e9, 2)}
+            "algorithmic_gflop": round(flops / 1e9, 2),
+            # bf16 matrix work k_fwd executes per launch (hi/lo splits included), from rocprofv3's
+            # MfmaFlopsBF16 counter for this kernel source, over the measured k_fwd time
+            "executed_gflop_measured": round(executed_flops / 1e9, 2) if executed_flops else None,
+            "frac_executed": (round(executed_flops / fwd_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+                              if executed_flops else None)}
 
     cpu = None
     parity = None
