@@ -294,7 +294,7 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
                    const float* beta, float scale, const float* s_init, const int32_t* cu, void* out,
                    float* s_final, void* ws, size_t ws_bytes, void* stream, float* seg_out,
                    int32_t* path_out, float* chunk_states = nullptr, float* bwd_y = nullptr,
-                   float* bwd_vp = nullptr, float* bwd_oi = nullptr) {
+                   float* bwd_vp = nullptr, float* bwd_oi = nullptr, const void* bwd_dout = nullptr) {
     Plan P;
     gdn_status st = make_plan(d, &P);
     if (st != GDN_OK) return st;
@@ -351,6 +351,7 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
     p.bwd_y = bwd_y;
     p.bwd_vp = bwd_vp;
     p.bwd_oi = bwd_oi;
+    p.bwd_dout = bwd_dout;
     if ((e = chunk_states ? gdn::launch_fwd_states(p, io, stream) : gdn::launch_fwd(p, io, stream)))
         return fail(GDN_ERR_HIP, "fwd launch: %s", hipGetErrorString((hipError_t)e));
     prof_mark(4, hs);
@@ -413,7 +414,8 @@ BwdLayout bwd_layout(const gdn_desc* d, const Plan& P) {
     const size_t blk = (size_t)P.n_chunks_total * d->h_v * gdn::kChunk * gdn::kDim * sizeof(float);
     L.off_y = off;   off = align_up(off + blk, 256);
     L.off_vp = off;  off = align_up(off + blk, 256);
-    L.off_oi = off;  off = align_up(off + blk, 256);
+    // the output's state term only as its per-token dot products with dO, eight partial sums
+    L.off_oi = off;  off = align_up(off + (size_t)P.n_chunks_total * d->h_v * 8 * gdn::kChunk * sizeof(float), 256);
     L.off_dvp = off; off = align_up(off + blk, 256);
     L.off_z = off;   off = align_up(off + blk, 256);
     L.off_dq = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
@@ -466,7 +468,7 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
         st = run_fwd(desc, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8 + L.off_o, nullptr, workspace,
                      P.ws_bytes, stream, nullptr, nullptr, reinterpret_cast<float*>(w8 + L.off_cs),
                      reinterpret_cast<float*>(w8 + L.off_y), reinterpret_cast<float*>(w8 + L.off_vp),
-                     reinterpret_cast<float*>(w8 + L.off_oi));
+                     reinterpret_cast<float*>(w8 + L.off_oi), d_out);
         if (st != GDN_OK) return st;
     }
     gdn::BwdParams b{};

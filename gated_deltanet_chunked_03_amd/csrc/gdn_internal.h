@@ -39,8 +39,9 @@ struct Params {
     float* sink;              // 8 KiB scratch line for stores of rows past a sequence's end
     float* chunk_states;      // [n_chunks][h_v][128][128] state entering each chunk (backward recompute)
     float* bwd_y;             // with chunk_states: per (chunk, head) [64][128] fp32 Y = V - diag(e^gamma) K S,
-    float* bwd_vp;            //   V', and scale diag(e^gamma) Q S
-    float* bwd_oi;
+    float* bwd_vp;            //   and V'; and per (chunk, head) [8 waves][64] partial sums over d_v of
+    float* bwd_oi;            //   (scale diag(e^gamma) Q S) o dO per token (the output's state term . dO)
+    const void* bwd_dout;     //   with chunk_states: the loss gradient of the output (bf16)
     // low-level chunk-prep outputs
     float* prep_gamma;        // [n_chunks][h_v][64]
     float* prep_W;            // [n_chunks][h_v][64][128]

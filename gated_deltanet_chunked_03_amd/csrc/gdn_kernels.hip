@@ -1681,8 +1681,8 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
             SplitS ss;
             split_state(S, ss);
             if constexpr (ST) {
-                // for the backward: Y, V' (token rows) and scale e^gamma Q S (the
-                // output's state part, O^T tiles) of this chunk, fp32
+                // for the backward: Y and V' of this chunk (token rows, fp32), and
+                // the output's state part scale e^gamma Q S as its dot with dO
                 f32x4 Y[4];
                 chain_vp<IO, true>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp, Y);
                 chain_qs<EX>(sm, ss, O);
@@ -1696,9 +1696,23 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
                         p.bwd_y[o] = Y[rt][e];
                         p.bwd_vp[o] = Vp[rt][e];
                     }
+                // the output's state term enters the gradients only through its dot
+                // product with dO per token (the dgamma sums): this wave's 16
+                // columns, summed over the lane groups, one partial per wave
+                const unsigned short* dob = static_cast<const unsigned short*>(p.bwd_dout) + tok0 * ts_v +
+                                            (size_t)h * DK + 16 * wave + 4 * g;
+                const int nv = min(CH, loc.len - c * CH);
+                float* part = p.bwd_oi + ((size_t)(loc.chunk_base + c) * p.h_v + h) * (NW_CH * CH) + wave * CH;
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-                    *reinterpret_cast<f32x4*>(p.bwd_oi + blk + (size_t)(16 * ct + cc) * DK + 16 * wave + 4 * g) = O[ct];
+                for (int ct = 0; ct < 4; ++ct) {
+                    // (rows past the end read the last row; the reader masks them)
+                    const u32x2 dw = *reinterpret_cast<const u32x2*>(dob + (size_t)min(16 * ct + cc, nv - 1) * ts_v);
+                    float sdot = O[ct][0] * __uint_as_float(dw[0] << 16) + O[ct][1] * __uint_as_float(dw[0] & 0xffff0000u) +
+                                 O[ct][2] * __uint_as_float(dw[1] << 16) + O[ct][3] * __uint_as_float(dw[1] & 0xffff0000u);
+                    sdot += __shfl_xor(sdot, 16, 64);
+                    sdot += __shfl_xor(sdot, 32, 64);
+                    if (g == 0) part[16 * ct + cc] = sdot;
+                }
             } else {
                 chain_vp<IO, true>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp);
                 chain_qs<EX>(sm, ss, O);
@@ -2134,7 +2148,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
     const float* dSn = p.ds + state_off(f, p.h_v, h);
     const float* Yb = p.y + blk;
     const float* Vpb = p.vp + blk;
-    const float* Oib = p.oi + blk;
+    const float* Oib = p.oi + ((size_t)f * p.h_v + h) * (NW_CH * CH);   // [8][64] partial sums
     const float* dVb = p.dvp + blk;
     const float* Zb = p.z + blk;
     const bf16* Kg = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK;
@@ -2182,25 +2196,23 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
     {
         const int r = t >> 3, c0 = (t & 7) * 16, rr = min(r, nv - 1);
         const bool ok = r < nv;
-        float zb = 0.f, vy = 0.f, qo = 0.f;
+        float zb = 0.f, vy = 0.f;
+        // the output's state term . dO over this thread's 16 columns (the forward
+        // re-run's partial sum of wave t % 8, whose columns these are)
+        float qo = Oib[(t & 7) * CH + r];
         const float br = sm.bet[r];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int col = c0 + 4 * q4;
             const f32x4 y = *reinterpret_cast<const f32x4*>(Yb + (size_t)r * DK + col);
             const f32x4 z = *reinterpret_cast<const f32x4*>(Zb + (size_t)r * DK + col);
-            const f32x4 oi = *reinterpret_cast<const f32x4*>(Oib + (size_t)r * DK + col);
             const u32x2 vw = *reinterpret_cast<const u32x2*>(Vg + (size_t)rr * ts_v + col);
-            const u32x2 dw = *reinterpret_cast<const u32x2*>(dOg + (size_t)rr * ts_v + col);
             const f32x4 v = {__uint_as_float(vw[0] << 16), __uint_as_float(vw[0] & 0xffff0000u),
                              __uint_as_float(vw[1] << 16), __uint_as_float(vw[1] & 0xffff0000u)};
-            const f32x4 d = {__uint_as_float(dw[0] << 16), __uint_as_float(dw[0] & 0xffff0000u),
-                             __uint_as_float(dw[1] << 16), __uint_as_float(dw[1] & 0xffff0000u)};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 zb += z[e] * y[e];
                 vy += (v[e] - y[e]) * (br * z[e]);
-                qo += oi[e] * d[e];
             }
         }
 #pragma unroll
