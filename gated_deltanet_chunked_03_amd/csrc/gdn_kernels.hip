@@ -1683,11 +1683,21 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
             if constexpr (ST) {
                 // for the backward: Y and V' of this chunk (token rows, fp32), and
                 // the output's state part scale e^gamma Q S as its dot with dO
+                const int l = lane_id(), cc = l & 15, g = l >> 4;
+                const int nv = min(CH, loc.len - c * CH);
+                // dO for the state term's dot products below, loaded first so that it
+                // arrives during the products (rows past the end read the last row;
+                // the reader masks them)
+                const unsigned short* dob = static_cast<const unsigned short*>(p.bwd_dout) + tok0 * ts_v +
+                                            (size_t)h * DK + 16 * wave + 4 * g;
+                u32x2 dw[4];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    dw[ct] = *reinterpret_cast<const u32x2*>(dob + (size_t)min(16 * ct + cc, nv - 1) * ts_v);
                 f32x4 Y[4];
-                chain_vp<IO, true>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp, Y);
+                chain_vp<IO, true>(sm, ss, vcol, ts_v, nv, Vp, Y);
                 chain_qs<EX>(sm, ss, O);
                 const size_t blk = ((size_t)(loc.chunk_base + c) * p.h_v + h) * CH * DK;
-                const int l = lane_id(), cc = l & 15, g = l >> 4;
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -1699,16 +1709,12 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
                 // the output's state term enters the gradients only through its dot
                 // product with dO per token (the dgamma sums): this wave's 16
                 // columns, summed over the lane groups, one partial per wave
-                const unsigned short* dob = static_cast<const unsigned short*>(p.bwd_dout) + tok0 * ts_v +
-                                            (size_t)h * DK + 16 * wave + 4 * g;
-                const int nv = min(CH, loc.len - c * CH);
                 float* part = p.bwd_oi + ((size_t)(loc.chunk_base + c) * p.h_v + h) * (NW_CH * CH) + wave * CH;
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    // (rows past the end read the last row; the reader masks them)
-                    const u32x2 dw = *reinterpret_cast<const u32x2*>(dob + (size_t)min(16 * ct + cc, nv - 1) * ts_v);
-                    float sdot = O[ct][0] * __uint_as_float(dw[0] << 16) + O[ct][1] * __uint_as_float(dw[0] & 0xffff0000u) +
-                                 O[ct][2] * __uint_as_float(dw[1] << 16) + O[ct][3] * __uint_as_float(dw[1] & 0xffff0000u);
+                    const u32x2 d = dw[ct];
+                    float sdot = O[ct][0] * __uint_as_float(d[0] << 16) + O[ct][1] * __uint_as_float(d[0] & 0xffff0000u) +
+                                 O[ct][2] * __uint_as_float(d[1] << 16) + O[ct][3] * __uint_as_float(d[1] & 0xffff0000u);
                     sdot += __shfl_xor(sdot, 16, 64);
                     sdot += __shfl_xor(sdot, 32, 64);
                     if (g == 0) part[16 * ct + cc] = sdot;
