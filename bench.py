@@ -41,15 +41,15 @@ KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc", "gdn_ke
 # HBM bytes per k_fwd launch on the tp8 workload (and per k_decode launch on the 256-row decode)
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE passes (and k_fwd's executed bf16 MFMA work from an
 # MfmaFlopsBF16 pass),
-# scaled by a 512 MiB copy's counts (FETCH x 1.99987, WRITE x 1.0). Valid only for the kernel
+# scaled by a 512 MiB copy's counts (FETCH x 1.99981, WRITE x 1.0). Valid only for the kernel
 # source with this hash; any other source reports null.
-MEASURED_TRAFFIC = {"tp8": {"sha256": "71742401b78dc2b0ff7ac00c9ec15f93cf4a945777605457df854c58bdafec56",
-                            "read": 185281751, "write": 67649536,
+MEASURED_TRAFFIC = {"tp8": {"sha256": "90dbec2e8e3c68c4de13a1c7bcfb7158da48e7899e038cc76a17ba8a0ccddfce",
+                            "read": 185276494, "write": 67649536,
                             # MfmaFlopsBF16 per k_fwd launch (same kernel source)
                             "mfma_flops": 73551314944},
                     # k_decode on the 256-row one-token decode, same passes and scale
-                    "decode256": {"sha256": "71742401b78dc2b0ff7ac00c9ec15f93cf4a945777605457df854c58bdafec56",
-                                  "read": 135130243, "write": 134955008}}
+                    "decode256": {"sha256": "90dbec2e8e3c68c4de13a1c7bcfb7158da48e7899e038cc76a17ba8a0ccddfce",
+                                  "read": 135138696, "write": 134929280}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp4": 0.486, "tp2": 0.659, "tp1": 0.493}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
