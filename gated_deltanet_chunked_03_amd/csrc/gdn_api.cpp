@@ -35,15 +35,22 @@ constexpr size_t kStateElems = (size_t)gdn::kDim * gdn::kDim;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Byte offsets of the workspace arrays of one forward pipeline.
+struct FwdLayout {
+    size_t off_sink = 0, off_T = 0, off_GB = 0, off_state = 0, off_M = 0, off_H = 0, off_warm = 0;
+    size_t off_GM = 0, off_GH = 0, bytes = 0;
+};
+
 struct Plan {
     int n_seqs = 0;
     std::vector<int> len;       // tokens per sequence
     int n_chunks_total = 0, n_chunks_max = 0;
     int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0, cp_order = 0;
     float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
-    int comb_G = 0, comb_J = 0;   // grouped combine (0: one chain)
-    size_t off_sink = 0, off_T = 0, off_GB = 0, off_state = 0, off_M = 0, off_H = 0, off_warm = 0;
-    size_t off_GM = 0, off_GH = 0, ws_bytes = 0;
+    int comb_G = 0, comb_J = 0;   // grouped combine of the backward's forward re-run (0: one chain)
+    FwdLayout fw;                 // the forward (fp16 chain kernels)
+    FwdLayout re;                 // the backward's forward re-run (split bf16 chain kernels)
+    size_t ws_bytes = 0;          // == fw.bytes
 };
 
 int n_chunks_of(int len) { return (len + gdn::kChunk - 1) / gdn::kChunk; }
@@ -200,44 +207,65 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
     if (ns > 0x7fffffffLL / 2) return fail(GDN_ERR_BAD_SHAPE, "too many segments");
     P.n_segments = (int)ns;
     P.cp_on = P.P_max > 1;
-    size_t off = 0;
-    const size_t blk = (size_t)gdn::kChunk * gdn::kChunk * sizeof(float);
-    if (P.n_chunks_total > 0) { P.off_sink = off; off += 8192; }
-    P.off_T = off;   off = align_up(off + (size_t)P.n_chunks_total * d->h_v * blk, 256);
-    P.off_GB = off;  off = align_up(off + (size_t)P.n_chunks_total * d->h_v * 2 * gdn::kChunk * sizeof(float), 256);
+    const size_t nch = (size_t)P.n_chunks_total * d->h_v, nsg = (size_t)P.n_segments * d->h_v;
+    const size_t st_bytes = nsg * kStateElems * sizeof(float);
+    // k_cp_prep puts the exact boundaries' workgroups (two each) first when,
+    // with the share of exact heads the pages report (most heads forget fast:
+    // 30 % exact, to the nearest), they fit in about one round (2 E <= 5/4 CUs);
+    // with more, head-major order measured faster.
     if (P.cp_on) {
-        const size_t st_bytes = (size_t)P.n_segments * d->h_v * kStateElems * sizeof(float);
-        P.off_state = off; off = align_up(off + st_bytes, 256);
-        P.off_M = off;     off = align_up(off + st_bytes, 256);
-        P.off_H = off;     off = align_up(off + st_bytes, 256);
-        P.off_warm = off;  off = align_up(off + (size_t)P.n_segments * d->h_v * sizeof(int32_t), 256);
-        // The combine chains the boundaries of a sequence, P - 1 steps in a row.
-        // Grouped (groups of G boundaries composed in parallel, then linked, then
-        // replayed in parallel) it takes about G + (J - 2) + (G - 1) steps, J =
-        // ceil((P - 1) / G), in three launches. Its composing steps read every
-        // map once per 32-column block (8 workgroups per group and exact head):
-        // with more of them than half the CUs those steps ran ~2.5x slower
-        // (measured), and a whole round more past the CUs. Only exact heads
-        // compose; which heads are exact is decided on the device from the gates,
-        // so the plan assumes the share the pages report (most heads forget fast:
-        // 30 % exact, to the nearest, at least one). Grouped when that estimate
-        // beats the single chain by more than the two extra launches (~4 steps).
-        // k_cp_prep puts the exact boundaries' workgroups (two each) first
-        // when, with the same 30 % estimate, they fit in about one round
-        // (2 E <= 5/4 CUs); with more, head-major order measured faster.
-        {
-            const long long pairs = (long long)(P.n_segments - P.n_seqs) * d->h_v, est = (3 * pairs + 5) / 10;
-            P.cp_order = 4 * (2 * est) <= 5LL * P.n_cu ? 1 : 0;
-        }
-        const long long heads = std::max(1LL, ((long long)P.n_seqs * d->h_v * 3 + 5) / 10);
-        combine_grouping(P.P_max - 1, heads, P.n_cu, 0, &P.comb_G, &P.comb_J);
-        if (P.comb_G) {
-            const size_t grp = (size_t)P.n_seqs * P.comb_J * d->h_v * kStateElems * sizeof(float);
-            P.off_GM = off; off = align_up(off + grp, 256);
-            P.off_GH = off; off = align_up(off + 2 * grp, 256);
-        }
+        const long long pairs = (long long)(P.n_segments - P.n_seqs) * d->h_v, est = (3 * pairs + 5) / 10;
+        P.cp_order = 4 * (2 * est) <= 5LL * P.n_cu ? 1 : 0;
     }
-    P.ws_bytes = off;
+    {
+        // The forward: an 8 KiB scratch line (stores of rows past a sequence's
+        // end land there), T diag(beta) as fp16 operand images (6 KiB per chunk
+        // and value head); with a split, the boundary states and H maps (fp32,
+        // 64 KiB, in the chain kernels' tile order), the M maps as the combine's
+        // fp16 A operands (32 KiB) and the boundary flags.
+        FwdLayout& F = P.fw;
+        size_t off = 0;
+        if (P.n_chunks_total > 0) { F.off_sink = off; off += 8192; }
+        F.off_T = off; off = align_up(off + nch * gdn::kTbHalfs * 2, 256);
+        if (P.cp_on) {
+            F.off_state = off; off = align_up(off + st_bytes, 256);
+            F.off_H = off;     off = align_up(off + st_bytes, 256);
+            F.off_M = off;     off = align_up(off + st_bytes / 2, 256);
+            F.off_warm = off;  off = align_up(off + nsg * sizeof(int32_t), 256);
+        }
+        F.bytes = off;
+    }
+    {
+        // The backward's re-run of the forward: T split hi/lo (16 KiB) and
+        // gamma, beta (512 bytes) per (chunk, value head); with a split, the
+        // segment states, maps M (split operands) and H, the boundary flags and
+        // the grouped combine's group maps. The combine chains the boundaries of
+        // a sequence, P - 1 steps in a row; grouped (groups of G boundaries
+        // composed in parallel, then linked, then replayed in parallel) it takes
+        // about G + (J - 2) + (G - 1) steps, J = ceil((P - 1) / G), in three
+        // launches; the re-run links every head (all exact).
+        FwdLayout& R = P.re;
+        size_t off = 0;
+        const size_t blk = (size_t)gdn::kChunk * gdn::kChunk * sizeof(float);
+        if (P.n_chunks_total > 0) { R.off_sink = off; off += 8192; }
+        R.off_T = off;  off = align_up(off + nch * blk, 256);
+        R.off_GB = off; off = align_up(off + nch * 2 * gdn::kChunk * sizeof(float), 256);
+        if (P.cp_on) {
+            R.off_state = off; off = align_up(off + st_bytes, 256);
+            R.off_M = off;     off = align_up(off + st_bytes, 256);
+            R.off_H = off;     off = align_up(off + st_bytes, 256);
+            R.off_warm = off;  off = align_up(off + nsg * sizeof(int32_t), 256);
+            const long long heads = std::max(1LL, ((long long)P.n_seqs * d->h_v * 3 + 5) / 10);
+            combine_grouping(P.P_max - 1, heads, P.n_cu, 0, &P.comb_G, &P.comb_J);
+            if (P.comb_G) {
+                const size_t grp = (size_t)P.n_seqs * P.comb_J * d->h_v * kStateElems * sizeof(float);
+                R.off_GM = off; off = align_up(off + grp, 256);
+                R.off_GH = off; off = align_up(off + 2 * grp, 256);
+            }
+        }
+        R.bytes = off;
+    }
+    P.ws_bytes = P.fw.bytes;
     *pl = std::move(P);
     return GDN_OK;
 }
@@ -273,8 +301,6 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
     p.h_v = d->h_v;
     p.group = d->h_v / d->h_qk;
     p.L = P.L;
-    p.comb_G = P.comb_G;
-    p.comb_J = P.comb_J;
     p.w = P.w;
     p.cp_mode = d->cp_mode;
     p.n_segments = P.n_segments;
@@ -290,48 +316,57 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
     return p;
 }
 
-gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* g,
-                   const float* beta, float scale, const float* s_init, const int32_t* cu, void* out,
-                   float* s_final, void* ws, size_t ws_bytes, void* stream, float* seg_out,
-                   int32_t* path_out, float* chunk_states = nullptr, float* bwd_y = nullptr,
-                   float* bwd_vp = nullptr, float* bwd_oi = nullptr, const void* bwd_dout = nullptr) {
-    Plan P;
-    gdn_status st = make_plan(d, &P);
-    if (st != GDN_OK) return st;
+// Validation shared by the forward entry points (pointers, sizes, workspace).
+gdn_status check_fwd_args(const gdn_desc* d, const Plan& P, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, float scale, const float* s_init, const int32_t* cu,
+                          const void* out, const float* s_final, const void* ws, size_t ws_bytes,
+                          size_t need_bytes) {
     const bool varlen = d->host_cu_seqlens != nullptr;
     if (varlen && !cu) return fail(GDN_ERR_NULL_ARG, "cu_seqlens is NULL but desc->host_cu_seqlens is set");
     if (!varlen && cu) return fail(GDN_ERR_NULL_ARG, "desc->host_cu_seqlens is required with cu_seqlens");
     const bool any = (long long)d->B * d->T > 0;
+    gdn_status st;
     if ((st = check_ptr(q, "q", any)) || (st = check_ptr(k, "k", any)) || (st = check_ptr(v, "v", any)) ||
         (st = check_ptr(g, "g", any)) || (st = check_ptr(beta, "beta", any)) ||
         (st = check_ptr(out, "out", any)) || (st = check_ptr(s_init, "initial_state", false)) ||
-        (st = check_ptr(s_final, "final_state", false)) || (st = check_ptr(cu, "cu_seqlens", false, 4)) ||
-        (st = check_ptr(seg_out, "seg_state_out", false)) || (st = check_ptr(path_out, "path_out", false, 4)))
+        (st = check_ptr(s_final, "final_state", false)) || (st = check_ptr(cu, "cu_seqlens", false, 4)))
         return st;
     if (!std::isfinite(scale)) return fail(GDN_ERR_BAD_SCALE, "scale is not finite");
-    if (ws_bytes < P.ws_bytes)
-        return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, P.ws_bytes);
-    if (P.ws_bytes > 0 && (st = check_ptr(ws, "workspace", true, 256))) return st;
+    if (ws_bytes < need_bytes)
+        return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, need_bytes);
+    if (need_bytes > 0 && (st = check_ptr(ws, "workspace", true, 256))) return st;
+    (void)P;
+    return GDN_OK;
+}
 
+void set_layout(gdn::Params& p, const FwdLayout& F, const Plan& P, char* w8) {
+    if (P.n_chunks_total > 0) p.sink = reinterpret_cast<float*>(w8 + F.off_sink);
+    if (P.cp_on) {
+        p.seg_state = reinterpret_cast<float*>(w8 + F.off_state);
+        p.seg_M = reinterpret_cast<float*>(w8 + F.off_M);
+        p.seg_H = reinterpret_cast<float*>(w8 + F.off_H);
+        p.warm = reinterpret_cast<int32_t*>(w8 + F.off_warm);
+    }
+}
+
+// The forward: k_prep (T diag(beta) images, boundary classes) | k_cp_prep16
+// (boundary states or maps) | k_combine16 (exact boundaries) | k_fwd16.
+gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, float scale, const float* s_init, const int32_t* cu, void* out,
+                   float* s_final, void* ws, size_t ws_bytes, void* stream, float* seg_out, int32_t* path_out) {
+    Plan P;
+    gdn_status st = make_plan(d, &P);
+    if (st != GDN_OK) return st;
+    if ((st = check_fwd_args(d, P, q, k, v, g, beta, scale, s_init, cu, out, s_final, ws, ws_bytes, P.fw.bytes)))
+        return st;
+    if ((st = check_ptr(seg_out, "seg_state_out", false)) || (st = check_ptr(path_out, "path_out", false, 4)))
+        return st;
     gdn::Params p = base_params(d, P);
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.s_init = s_init; p.cu = cu;
     p.out = out; p.s_final = s_final; p.scale = scale;
     char* w8 = static_cast<char*>(ws);
-    if (P.n_chunks_total > 0) {
-        p.sink = reinterpret_cast<float*>(w8 + P.off_sink);
-        p.prep_T = reinterpret_cast<float*>(w8 + P.off_T);
-        p.prep_GB = reinterpret_cast<float*>(w8 + P.off_GB);
-    }
-    if (P.cp_on) {
-        p.seg_state = reinterpret_cast<float*>(w8 + P.off_state);
-        p.seg_M = reinterpret_cast<float*>(w8 + P.off_M);
-        p.seg_H = reinterpret_cast<float*>(w8 + P.off_H);
-        p.warm = reinterpret_cast<int32_t*>(w8 + P.off_warm);
-        if (P.comb_G) {
-            p.seg_GM = reinterpret_cast<float*>(w8 + P.off_GM);
-            p.seg_GH = reinterpret_cast<float*>(w8 + P.off_GH);
-        }
-    }
+    set_layout(p, P.fw, P, w8);
+    if (P.n_chunks_total > 0) p.tb16 = w8 + P.fw.off_T;
     const int io = d->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
     const hipStream_t hs = (hipStream_t)stream;
     int e;
@@ -340,19 +375,14 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
         return fail(GDN_ERR_HIP, "prep launch: %s", hipGetErrorString((hipError_t)e));
     prof_mark(1, hs);
     if (P.cp_on) {
-        if ((e = gdn::launch_cp_prep(p, io, stream)))
+        if ((e = gdn::launch_cp_prep16(p, io, stream)))
             return fail(GDN_ERR_HIP, "cp_prep launch: %s", hipGetErrorString((hipError_t)e));
         prof_mark(2, hs);
-        if ((e = gdn::launch_cp_combine(p, stream)))
-            return fail(GDN_ERR_HIP, "cp_combine launch: %s", hipGetErrorString((hipError_t)e));
+        if ((e = gdn::launch_combine16(p, stream)))
+            return fail(GDN_ERR_HIP, "combine launch: %s", hipGetErrorString((hipError_t)e));
         prof_mark(3, hs);
     }
-    p.chunk_states = chunk_states;
-    p.bwd_y = bwd_y;
-    p.bwd_vp = bwd_vp;
-    p.bwd_oi = bwd_oi;
-    p.bwd_dout = bwd_dout;
-    if ((e = chunk_states ? gdn::launch_fwd_states(p, io, stream) : gdn::launch_fwd(p, io, stream)))
+    if ((e = gdn::launch_fwd16(p, io, stream)))
         return fail(GDN_ERR_HIP, "fwd launch: %s", hipGetErrorString((hipError_t)e));
     prof_mark(4, hs);
     if (g_prof.on) {
@@ -363,21 +393,21 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
     }
 
     if (seg_out || path_out) {
-        hipStream_t s = (hipStream_t)stream;
         const size_t per_seg = (size_t)d->h_v * kStateElems;
         hipError_t he = hipSuccess;
         if (seg_out) {
-            if (P.cp_on)
-                he = hipMemcpyAsync(seg_out, p.seg_state, P.n_segments * per_seg * sizeof(float),
-                                    hipMemcpyDeviceToDevice, s);
+            // boundary states (tile order in the workspace) -> row-major; each
+            // sequence's segment 0 takes its initial state
+            if (P.cp_on && (e = gdn::launch_tiles_to_rm(p.seg_state, seg_out, (long long)P.n_segments * d->h_v, stream)))
+                return fail(GDN_ERR_HIP, "debug copy: %s", hipGetErrorString((hipError_t)e));
             int base = 0;
             for (int n = 0; n < P.n_seqs && he == hipSuccess; ++n) {
                 float* dst = seg_out + (size_t)base * per_seg;
                 if (s_init)
                     he = hipMemcpyAsync(dst, s_init + (size_t)n * per_seg, per_seg * sizeof(float),
-                                        hipMemcpyDeviceToDevice, s);
+                                        hipMemcpyDeviceToDevice, hs);
                 else
-                    he = hipMemsetAsync(dst, 0, per_seg * sizeof(float), s);
+                    he = hipMemsetAsync(dst, 0, per_seg * sizeof(float), hs);
                 base += n_segs_of(n_chunks_of(P.len[n]), P.L);
             }
         }
@@ -386,6 +416,47 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
             return fail(GDN_ERR_HIP, "debug path launch: %s", hipGetErrorString((hipError_t)e));
     }
     g_last_error.clear();
+    return GDN_OK;
+}
+
+// The backward's re-run of the forward (split bf16 chain kernels, which also
+// write the state entering every chunk, Y, V' and the output's state term
+// dotted with dO), in the re-run layout of the workspace.
+gdn_status run_fwd_rerun(const gdn_desc* d, const Plan& P, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float scale, const float* s_init, const int32_t* cu,
+                         void* out, char* w8, void* stream, float* chunk_states, float* bwd_y, float* bwd_vp,
+                         float* bwd_oi, const void* bwd_dout) {
+    gdn::Params p = base_params(d, P);
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.s_init = s_init; p.cu = cu;
+    p.out = out; p.s_final = nullptr; p.scale = scale;
+    set_layout(p, P.re, P, w8);
+    if (P.n_chunks_total > 0) {
+        p.prep_T = reinterpret_cast<float*>(w8 + P.re.off_T);
+        p.prep_GB = reinterpret_cast<float*>(w8 + P.re.off_GB);
+    }
+    if (P.cp_on && P.comb_G) {
+        p.seg_GM = reinterpret_cast<float*>(w8 + P.re.off_GM);
+        p.seg_GH = reinterpret_cast<float*>(w8 + P.re.off_GH);
+    }
+    p.comb_G = P.comb_G;
+    p.comb_J = P.comb_J;
+    const int io = gdn::kIoBf16;
+    int e;
+    if ((e = gdn::launch_prep(p, io, stream)))
+        return fail(GDN_ERR_HIP, "prep launch: %s", hipGetErrorString((hipError_t)e));
+    if (P.cp_on) {
+        if ((e = gdn::launch_cp_prep(p, io, stream)))
+            return fail(GDN_ERR_HIP, "cp_prep launch: %s", hipGetErrorString((hipError_t)e));
+        if ((e = gdn::launch_cp_combine(p, stream)))
+            return fail(GDN_ERR_HIP, "cp_combine launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    p.chunk_states = chunk_states;
+    p.bwd_y = bwd_y;
+    p.bwd_vp = bwd_vp;
+    p.bwd_oi = bwd_oi;
+    p.bwd_dout = bwd_dout;
+    if ((e = gdn::launch_fwd_states(p, io, stream)))
+        return fail(GDN_ERR_HIP, "fwd launch: %s", hipGetErrorString((hipError_t)e));
     return GDN_OK;
 }
 
@@ -405,7 +476,7 @@ BwdLayout bwd_layout(const gdn_desc* d, const Plan& P) {
     BwdLayout L;
     for (int n = 0; n < P.n_seqs; ++n) L.tokens += (size_t)P.len[n];
     const size_t st = (size_t)P.n_chunks_total * d->h_v * kStateElems * sizeof(float);
-    size_t off = align_up(P.ws_bytes, 256);
+    size_t off = align_up(P.re.bytes, 256);
     L.off_o = off;   off = align_up(off + L.tokens * d->h_v * gdn::kDim * 2, 256);
     L.off_cs = off;  off = align_up(off + st, 256);
     L.off_ds = off;  off = align_up(off + st, 256);
@@ -465,10 +536,9 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     char* w8 = static_cast<char*>(workspace);
     // the forward again, keeping the state entering every chunk
     if (P.n_chunks_total > 0) {
-        st = run_fwd(desc, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8 + L.off_o, nullptr, workspace,
-                     P.ws_bytes, stream, nullptr, nullptr, reinterpret_cast<float*>(w8 + L.off_cs),
-                     reinterpret_cast<float*>(w8 + L.off_y), reinterpret_cast<float*>(w8 + L.off_vp),
-                     reinterpret_cast<float*>(w8 + L.off_oi), d_out);
+        st = run_fwd_rerun(desc, P, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8 + L.off_o, w8, stream,
+                           reinterpret_cast<float*>(w8 + L.off_cs), reinterpret_cast<float*>(w8 + L.off_y),
+                           reinterpret_cast<float*>(w8 + L.off_vp), reinterpret_cast<float*>(w8 + L.off_oi), d_out);
         if (st != GDN_OK) return st;
     }
     gdn::BwdParams b{};
@@ -490,17 +560,17 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     b.L = P.cp_on ? P.L : std::max(P.n_chunks_max, 1);
     b.n_segments = P.cp_on ? P.n_segments : P.n_seqs;
     if (P.cp_on) {
-        b.seg_state = reinterpret_cast<float*>(w8 + P.off_state);
-        b.seg_M = reinterpret_cast<float*>(w8 + P.off_M);
-        b.seg_H = reinterpret_cast<float*>(w8 + P.off_H);
-        b.warm = reinterpret_cast<int32_t*>(w8 + P.off_warm);
+        b.seg_state = reinterpret_cast<float*>(w8 + P.re.off_state);
+        b.seg_M = reinterpret_cast<float*>(w8 + P.re.off_M);
+        b.seg_H = reinterpret_cast<float*>(w8 + P.re.off_H);
+        b.warm = reinterpret_cast<int32_t*>(w8 + P.re.off_warm);
         // the backward links every head's segment ends (all exact); grouped only
         // within the group maps the forward's workspace holds
         if (P.comb_G)
             combine_grouping(P.P_max - 1, (long long)P.n_seqs * desc->h_v, P.n_cu, P.comb_J, &b.comb_G, &b.comb_J);
         if (b.comb_G) {
-            b.seg_GM = reinterpret_cast<float*>(w8 + P.off_GM);
-            b.seg_GH = reinterpret_cast<float*>(w8 + P.off_GH);
+            b.seg_GM = reinterpret_cast<float*>(w8 + P.re.off_GM);
+            b.seg_GH = reinterpret_cast<float*>(w8 + P.re.off_GH);
         }
     }
     b.n_seqs = P.n_seqs;

@@ -1,0 +1,700 @@
+// The forward's chain kernels on fp16 matrix-core operands (gfx950).
+//
+// What is computed: the chunked WY form of the gated delta rule (FlashQLA
+// pages, "FlashQLA: CP-/Bwd-friendly fused linear attention kernels for GDN",
+// section on optimising GDN chunked prefill), per chunk of 64 tokens with
+// incoming state S (d_k x d_v, fp32):
+//   Y  = V - diag(e^gamma) K S                  (prediction error)
+//   V' = T diag(beta) Y                         (= U - W S; T = (I + A)^-1 from k_prep)
+//   O  = scale (diag(e^gamma) Q S + (Q K^T o D) V'),  D[r][i] = e^(gamma_r - gamma_i), i <= r
+//   S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
+// and the intra-card context parallelism of the AutoCP section: segment
+// boundary states from a warm-up scan (gates decayed below the noise floor)
+// or from the exact segment maps S -> M S + H chained by k_combine16.
+//
+// Precision. Every product runs on 16x16x32 fp16 MFMAs with fp32
+// accumulation: the bf16 inputs q, k, v are exact in fp16 (within its
+// range), and the derived operands (S, Y, V', T diag(beta), P) are rounded
+// once to fp16 (11-bit significand, 8x finer than bf16); gate factors are
+// applied to fp32 accumulators. The state itself stays fp32.
+//
+// Work layout. A workgroup is 8 waves, two per SIMD; wave w owns the d_v
+// columns [16 w, 16 w + 16): its 128 x 16 slice of S (eight accumulator
+// tiles), of Y, V' and of the output stay in its registers, and the state
+// chain never crosses waves. Each wave issues a VALU instruction only every
+// ~7 cycles (measured), so two waves per SIMD are what keep its VALU and
+// matrix pipes busy; the LDS, which serves > 400 bytes per cycle per CU
+// (measured), absorbs every wave reading the whole chunk operands. A chunk's
+// K, K^T and Q (converted to fp16), its V rows (as they are) and T diag(beta)
+// (from k_prep, already in operand layout) are staged in LDS by all 512
+// threads; the next chunk's inputs are loaded into registers a chunk and a
+// half ahead. The causal matrix P = scale (Q K^T) o D is formed once per
+// chunk, each wave computing two of its 16 tiles, through LDS.
+//
+// Register layouts (16x16x32 MFMA, lane l = 16 g + c): A row c, B column c,
+// each with the k slots 8 g .. 8 g + 7; C/D rows 4 g .. 4 g + 3 of column c.
+// Two C tiles stacked along the contraction axis give lane group g the rows
+// 4 g + e and 16 + 4 g + e: the k slots of an operand once the contraction
+// axis of every LDS operand is stored in the order kp (gdn_device.h). V
+// reaches the accumulator layout through an identity product on the matrix
+// cores. The output is formed transposed (O^T = S^T Q^T + V'^T P^T, the same
+// registers in swapped operand roles), so that a lane holds four consecutive
+// d_v of one token and writes them with one 8-byte store.
+#include "gdn_device.h"
+
+namespace gdn {
+namespace {
+
+constexpr int NW8 = 8;           // waves per chain workgroup
+constexpr int NT8 = 64 * NW8;
+constexpr int LQ = 144;          // K, Q rows (fp16): 288 bytes, conflict-free operand reads
+constexpr int LT = 80;           // K^T rows: 160 bytes
+constexpr int LP = 80;           // P rows
+constexpr int LV = 136;          // V rows (elements of the input type): 272 / 544 bytes
+constexpr int LMI = 144;         // rows of the map image staged for the combine
+
+// The six nonzero T diag(beta) fragments (token tile m, k step j): 0 (0,0),
+// 1 (1,0), 2 (2,0), 3 (2,1), 4 (3,0), 5 (3,1) -- the same (m, j) pairs as
+// the causal P V' product.
+__device__ __forceinline__ int tb_frag(int m, int j) { return m < 2 ? m : 2 + 2 * (m - 2) + j; }
+
+// LDS of the chain kernels. OUT: the forward (Q and P as well). K, Q, V and
+// T diag(beta) are read in the first half of a chunk step only and restaged
+// after the step's first barrier; K^T is read in the second half, so it has
+// two buffers (the next chunk's is written while this one's is read).
+template <typename IO, bool OUT>
+struct __attribute__((aligned(16))) Smem16 {
+    f16 k[CH * LQ];                       // K token-major, d_k in kp order
+    f16 kt[2][DK * LT];                   // K^T: row d_k, tokens in kp order, 16-byte pieces XOR tswz(row)
+    f16 q[OUT ? CH * LQ : 8];             // Q token-major, d_k in kp order
+    IO v[CH * LV];                        // V rows as given
+    f16 tb[kTbHalfs];                     // T diag(beta) fragments (k_prep's image)
+    f16 p[OUT ? CH * LP : 8];             // P: row r, columns i in kp order
+    float gam[2][CH];                     // gamma
+    float eg[2][CH];                      // e^gamma
+    float egc[2][CH];                     // e^(gamma_C - gamma)
+    float ec[2][4];                       // e^gamma_C
+};
+
+// One chunk's inputs in registers between the loads and the LDS stores:
+// thread t holds tokens 4 (t / 32) + j (j < 4), columns 4 (t % 32) .. + 4 of
+// K, Q and V; piece t of the T diag(beta) image (t < 384); the gate of token
+// `lane`.
+template <typename IO> struct In16;
+template <> struct In16<bf16> { u32x2 k[4], q[4], v[4]; u32x4 tb; float g; };
+template <> struct In16<float> { f32x4 k[4], q[4], v[4]; u32x4 tb; float g; };
+
+// Rows past the end of the sequence read its last row again (those tokens
+// carry g = beta = 0: their columns of T diag(beta) are zero, so they reach
+// neither a valid output nor the state). Every chunk issues the same loads.
+template <typename IO, bool WANT_Q, bool WANT_V>
+__device__ __forceinline__ void fetch16(In16<IO>& r, const Params& p, size_t tok0, int nvalid, int h, int hq,
+                                        int slot) {
+    const int t = threadIdx.x, lane = lane_id(), rq = t >> 5, c4 = 4 * (t & 31);
+    const size_t ts = (size_t)p.h_qk * DK, tsv = (size_t)p.h_v * DK;
+    // the gate first (wave 0's scan waits for it), then K, Q, V, T diag(beta)
+    r.g = lane < nvalid ? p.g[(tok0 + lane) * (size_t)p.h_v + h] : 0.f;
+    const IO* kb = static_cast<const IO*>(p.k) + tok0 * ts + (size_t)hq * DK + c4;
+    const IO* qb = static_cast<const IO*>(p.q) + tok0 * ts + (size_t)hq * DK + c4;
+    const IO* vb = static_cast<const IO*>(p.v) + tok0 * tsv + (size_t)h * DK + c4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = min(4 * rq + j, nvalid - 1);
+        const unsigned o = (unsigned)(row * (int)ts), ov = (unsigned)(row * (int)tsv);
+        if constexpr (Io<IO>::kExact) {
+            r.k[j] = *reinterpret_cast<const u32x2*>(kb + o);
+            if (WANT_Q) r.q[j] = *reinterpret_cast<const u32x2*>(qb + o);
+            if (WANT_V) r.v[j] = *reinterpret_cast<const u32x2*>(vb + ov);
+        } else {
+            r.k[j] = *reinterpret_cast<const f32x4*>(kb + o);
+            if (WANT_Q) r.q[j] = *reinterpret_cast<const f32x4*>(qb + o);
+            if (WANT_V) r.v[j] = *reinterpret_cast<const f32x4*>(vb + ov);
+        }
+    }
+    // (threads past the 384 pieces load piece t - 384 again; only t < 384 store)
+    const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const f16*>(p.tb16) +
+                                                     ((size_t)slot * p.h_v + h) * (size_t)kTbHalfs);
+    r.tb = tb[t < kTbHalfs / 8 ? t : t - kTbHalfs / 8];
+}
+
+// four bf16 / fp32 values -> fp16
+__device__ __forceinline__ f16x4 to_h4(const u32x2& x) {
+    return __builtin_convertvector(f32x4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                                         __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)},
+                                   f16x4);
+}
+__device__ __forceinline__ f16x4 to_h4(const f32x4& x) { return __builtin_convertvector(x, f16x4); }
+
+// Writes a fetched chunk to LDS (K^T into buffer b): K token-major and
+// transposed, Q, V, T diag(beta), and (wave 0) the gate factors. Thread t's
+// columns 4 (t % 32) .. + 4 are the kp positions pk .. pk + 3; its four tokens
+// 4 (t / 32) .. + 4 the kp positions pt .. pt + 3.
+template <typename IO, bool OUT, bool WANT_V>
+__device__ __forceinline__ void stage16(Smem16<IO, OUT>& sm, const In16<IO>& r, int b) {
+    const int t = threadIdx.x, lane = lane_id(), cq = t & 31, rq = t >> 5;
+    if (wave_id() == 0) {
+        const float gam = wave_scan(r.g);
+        const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
+        sm.gam[b][lane] = gam;
+        sm.eg[b][lane] = __expf(gam);
+        sm.egc[b][lane] = __expf(gc - gam);
+        if (lane == 0) sm.ec[b][0] = __expf(gc);
+    }
+    const int pk = 32 * (cq >> 3) + 8 * (cq & 3) + 4 * ((cq >> 2) & 1);
+    const int pt = 32 * (rq >> 3) + 8 * (rq & 3) + 4 * ((rq >> 2) & 1);
+    f16x4 kr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        kr[j] = to_h4(r.k[j]);
+        *reinterpret_cast<f16x4*>(sm.k + (4 * rq + j) * LQ + pk) = kr[j];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int d = 4 * cq + e;
+        *reinterpret_cast<f16x4*>(sm.kt[b] + d * LT + (pt ^ tswz(d))) = f16x4{kr[0][e], kr[1][e], kr[2][e], kr[3][e]};
+    }
+    if constexpr (OUT) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<f16x4*>(sm.q + (4 * rq + j) * LQ + pk) = to_h4(r.q[j]);
+    }
+    if constexpr (WANT_V) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (Io<IO>::kExact) *reinterpret_cast<u32x2*>(sm.v + (4 * rq + j) * LV + 4 * cq) = r.v[j];
+            else *reinterpret_cast<f32x4*>(sm.v + (4 * rq + j) * LV + 4 * cq) = r.v[j];
+        }
+    }
+    if (t < kTbHalfs / 8) *reinterpret_cast<u32x4*>(sm.tb + 8 * t) = r.tb;
+}
+
+// ----------------------------------------------------------------------------
+// State tiles: wave w, tile i: rows 16 i + 4 g + e, column 16 w + c. In HBM the
+// segment states and H maps use the "tile order" of these registers: 128 x 128
+// fp32 as [i][u = 16-column tile][lane][4] (a 16-byte load or store per tile
+// and lane); the caller's initial and final states are row-major [128][128].
+
+__device__ __forceinline__ size_t tiles_off(int idx, int h_v, int h) {
+    return ((size_t)idx * h_v + h) * (size_t)DK * DK;
+}
+
+__device__ void load_rm(const float* Sg, f32x4 S[8]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[i][e] = Sg[(16 * i + 4 * g + e) * DK + 16 * w + c];
+}
+__device__ void store_rm(float* Sg, const f32x4 S[8]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sg[(16 * i + 4 * g + e) * DK + 16 * w + c] = S[i][e];
+}
+__device__ void load_tiles(const float* Sg, f32x4 S[8]) {
+    const int lane = lane_id(), w = wave_id();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S[i] = *reinterpret_cast<const f32x4*>(Sg + ((i * 8 + w) * 64 + lane) * 4);
+}
+__device__ void store_tiles(float* Sg, const f32x4 S[8]) {
+    const int lane = lane_id(), w = wave_id();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4*>(Sg + ((i * 8 + w) * 64 + lane) * 4) = S[i];
+}
+__device__ void set_state(f32x4 S[8], bool identity) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[i][e] = (identity && 16 * i + 4 * g + e == 16 * w + c) ? 1.f : 0.f;
+}
+
+// ----------------------------------------------------------------------------
+// One chunk step of the chain. OUT: the forward (output rows written to
+// orow + r * ts_v, rows past nvalid to the scratch line); else the scan
+// without output: the warm-up and H chains (WANT_V) or the M chain (V = 0).
+// The chunk is in LDS (K^T in buffer b); `nxt`, the next chunk's inputs, is
+// staged after the first barrier.
+template <typename IO, bool OUT, bool WANT_V>
+__device__ __forceinline__ void chain_step16(Smem16<IO, OUT>& sm, const In16<IO>& nxt, int b, f32x4 S[8],
+                                             float scale, IO* orow, size_t ts_v, int nvalid, float* sink) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
+    // the state as fp16 operands, one per k step j
+    f16x8 Sb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Sb[j] = pack8h(S[2 * j], S[2 * j + 1]);
+
+    // K S, Q S (transposed) and this wave's two tiles of P, k step by k step:
+    // tiles (r block w / 2, i blocks ib0, ib0 + 1), ib0 = 2 (w % 2)
+    const int rb = w >> 1, ib0 = 2 * (w & 1);
+    f32x4 Y[4], O[4], Pt[2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        Y[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    Pt[0] = Pt[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f16x8 kf[4], qf[4], qw, kw0, kw1;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            kf[m] = *reinterpret_cast<const f16x8*>(sm.k + (16 * m + c) * LQ + 32 * j + 8 * g);
+            if constexpr (OUT) qf[m] = *reinterpret_cast<const f16x8*>(sm.q + (16 * m + c) * LQ + 32 * j + 8 * g);
+        }
+        if constexpr (OUT) {
+            // (the P operands at wave-dependent rows, read again rather than picked by a branch)
+            qw = *reinterpret_cast<const f16x8*>(sm.q + (16 * rb + c) * LQ + 32 * j + 8 * g);
+            kw0 = *reinterpret_cast<const f16x8*>(sm.k + (16 * ib0 + c) * LQ + 32 * j + 8 * g);
+            kw1 = *reinterpret_cast<const f16x8*>(sm.k + (16 * ib0 + 16 + c) * LQ + 32 * j + 8 * g);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Y[m] = mmh(kf[m], Sb[j], Y[m]);
+        if constexpr (OUT) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) O[m] = mmh(Sb[j], qf[m], O[m]);
+            Pt[0] = mmh(kw0, qw, Pt[0]);
+            Pt[1] = mmh(kw1, qw, Pt[1]);
+        }
+    }
+    if constexpr (OUT) {
+        // P[r][i] = scale e^(gamma_r - gamma_i) (q_r . k_i), i <= r, else 0; the
+        // tiles hold P^T: lane (g, c) has r = 16 rb + c and i = 16 ib + 4 g + e
+        const int r = 16 * rb + c;
+        const float gr = sm.gam[b][r];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+            const int ib = ib0 + e2, i0 = 16 * ib + 4 * g;
+            const f32x4 gi = *reinterpret_cast<const f32x4*>(sm.gam[b] + i0);
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (i0 + e <= r) ? scale * __expf(gr - gi[e]) * Pt[e2][e] : 0.f;
+            *reinterpret_cast<f16x4*>(sm.p + r * LP + 32 * (ib >> 1) + 8 * g + 4 * (ib & 1)) =
+                __builtin_convertvector(v, f16x4);
+        }
+    }
+    // Y = V - e^gamma (K S) on rows 16 m + 4 g + e; V enters through the
+    // identity product V[:, 16 w + (0..15)] = V_rows E (32 columns of V as the
+    // A operand, E selecting this wave's 16)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Y[m] *= -*reinterpret_cast<const f32x4*>(sm.eg[b] + 16 * m + 4 * g);
+    if constexpr (WANT_V) {
+        const int vc = 32 * (w >> 1) + 8 * g;
+        if constexpr (Io<IO>::kExact) {
+            bf16x8 E;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) E[s] = (bf16)((8 * g + s == 16 * (w & 1) + c) ? 1.f : 0.f);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                Y[m] = mma16k32(*reinterpret_cast<const bf16x8*>(sm.v + (16 * m + c) * LV + vc), E, Y[m]);
+        } else {
+            f16x8 E;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) E[s] = (f16)((8 * g + s == 16 * (w & 1) + c) ? 1.f : 0.f);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                // fp32 rows as hi + lo fp16 (exact to about 2^-22)
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(sm.v + (16 * m + c) * LV + vc);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(sm.v + (16 * m + c) * LV + vc + 4);
+                const f16x8 hi = pack8h(a0, a1);
+                f32x4 l0, l1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    l0[e] = a0[e] - (float)hi[e];
+                    l1[e] = a1[e] - (float)hi[4 + e];
+                }
+                Y[m] = mmh(hi, E, Y[m]);
+                Y[m] = mmh(pack8h(l0, l1), E, Y[m]);
+            }
+        }
+    }
+    // V' = (T diag(beta)) Y; T diag(beta) is lower triangular
+    f32x4 Vp[4];
+    {
+        const f16x8 Yb0 = pack8h(Y[0], Y[1]), Yb1 = pack8h(Y[2], Y[3]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f16x8 t0 = *reinterpret_cast<const f16x8*>(sm.tb + (tb_frag(m, 0) * 64 + lane) * 8);
+            Vp[m] = mmh(t0, Yb0, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (m >= 2) {
+                const f16x8 t1 = *reinterpret_cast<const f16x8*>(sm.tb + (tb_frag(m, 1) * 64 + lane) * 8);
+                Vp[m] = mmh(t1, Yb1, Vp[m]);
+            }
+        }
+    }
+    if constexpr (OUT) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) O[m] *= scale * sm.eg[b][16 * m + c];
+    }
+    __syncthreads();   // P complete; K, Q, V, T diag(beta) and K^T[b ^ 1] free for the next chunk
+    f16x8 Vb[2];
+    Vb[0] = pack8h(Vp[0], Vp[1]);
+    Vb[1] = pack8h(Vp[2], Vp[3]);
+    if constexpr (OUT) {
+        // O^T += V'^T P^T (P causal: token tiles 0 and 1 need k step 0 only)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (j == 1 && m < 2) continue;
+                const f16x8 pf = *reinterpret_cast<const f16x8*>(sm.p + (16 * m + c) * LP + 32 * j + 8 * g);
+                O[m] = mmh(Vb[j], pf, O[m]);
+            }
+        // lane (g, c) of tile m: token 16 m + c, d_v 16 w + 4 g + (0..3)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * m + c;
+            IO* dst = (r < nvalid) ? orow + (size_t)r * ts_v + 16 * w + 4 * g : reinterpret_cast<IO*>(sink + 32 * lane);
+            if constexpr (Io<IO>::kExact)
+                *reinterpret_cast<u32x2*>(dst) = u32x2{pack_rne(O[m][0], O[m][1]), pack_rne(O[m][2], O[m][3])};
+            else
+                *reinterpret_cast<f32x4*>(dst) = O[m];
+        }
+    }
+    stage16<IO, OUT, WANT_V>(sm, nxt, b ^ 1);
+    // S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Vp[m] *= *reinterpret_cast<const f32x4*>(sm.egc[b] + 16 * m + 4 * g);
+    Vb[0] = pack8h(Vp[0], Vp[1]);
+    Vb[1] = pack8h(Vp[2], Vp[3]);
+    const float ec = sm.ec[b][0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S[i] *= ec;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        f16x8 ktf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ktf[i] = *reinterpret_cast<const f16x8*>(sm.kt[b] + (16 * i + c) * LT + ((32 * j + 8 * g) ^ tswz(16 * i)));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S[i] = mmh(ktf[i], Vb[j], S[i]);
+    }
+    __syncthreads();   // the next chunk staged
+}
+
+// Runs chunks [c_lo, c_hi) of sequence loc from the state S: the forward of a
+// segment (OUT) or a scan without output. Two register sets of chunk inputs
+// alternate (the loop is unrolled by two, with no branch in its body, so
+// every iteration issues the same memory operations and the compiler's waits
+// on them stay exact): step c stages the set holding chunk c + 1, and that
+// set is then refilled with chunk c + 3, a chunk and a half ahead of its use.
+template <typename IO, bool OUT, bool WANT_V>
+__device__ void run_chunks16(Smem16<IO, OUT>& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi,
+                             f32x4 S[8]) {
+    if (c_lo >= c_hi) return;
+    const int hq = h / p.group;
+    const size_t ts_v = (size_t)p.h_v * DK;
+    In16<IO> A, B;
+    auto fetch = [&](In16<IO>& r, int c) {
+        c = min(c, c_hi - 1);
+        fetch16<IO, OUT, WANT_V>(r, p, loc.tok0 + (size_t)c * CH, min(CH, loc.len - c * CH), h, hq,
+                                 loc.chunk_base + c);
+    };
+    auto step = [&](int c, const In16<IO>& nxt) {
+        const int b = (c - c_lo) & 1;
+        IO* orow = OUT ? static_cast<IO*>(p.out) + (loc.tok0 + (size_t)c * CH) * ts_v + (size_t)h * DK : nullptr;
+        chain_step16<IO, OUT, WANT_V>(sm, nxt, b, S, p.scale, orow, ts_v, min(CH, loc.len - c * CH), p.sink);
+    };
+    fetch(A, c_lo);
+    stage16<IO, OUT, WANT_V>(sm, A, 0);
+    fetch(B, c_lo + 1);
+    fetch(A, c_lo + 2);
+    __syncthreads();
+    int c = c_lo;
+    for (; c + 1 < c_hi; c += 2) {
+        step(c, B);
+        fetch(B, c + 3);
+        step(c + 1, A);
+        fetch(A, c + 4);
+    }
+    if (c < c_hi) step(c, B);
+}
+
+// ----------------------------------------------------------------------------
+// CP preprocessing: one 8-wave workgroup per (boundary, part). For an exact
+// boundary s (between segments s - 1 and s): part 0 runs segment s - 1 from
+// zero (H_{s-1}, tile order), part 1 from the identity with V = 0 (M_{s-1},
+// written as the combine's fp16 A-operand image); M_0 only matters with a
+// nonzero initial state. A warm-up boundary (part 0 only) scans its window
+// from zero (or from the initial state where the window starts at the
+// sequence start) and writes the boundary state. Work order as planned
+// (exact boundaries first, or head-major).
+
+// Class of boundary pair q = slot h_v + head: -1 (a sequence's first
+// segment), 0 exact, 1 or 2 warm-up (window length in bits 8 and up).
+__device__ __forceinline__ int pair_class16(const Params& p, int q, int& wq) {
+    const SegLoc loc = locate_segment(p, q / p.h_v);
+    const int v = p.warm[q];
+    wq = v >> 8;
+    return (loc.seq < 0 || loc.s == 0) ? -1 : (v & 255);
+}
+
+// Block-wide exclusive prefix sum (8 waves).
+__device__ __forceinline__ int block_excl_scan8(int x, int* red, int& total) {
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    int v = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(v, d, 64);
+        if (lane >= d) v += y;
+    }
+    if (lane == 63) red[w] = v;
+    __syncthreads();
+    int off = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < NW8; ++i) {
+        const int r = red[i];
+        if (i < w) off += r;
+        total += r;
+    }
+    return off + v - x;
+}
+
+// M (tile registers, columns 16 w + c) -> the combine's A-operand image:
+// fragment (row tile mt, k step j), lane (g', c') holds row 16 mt + c' at the
+// k slots 8 g' .. + 8, the columns of block j in kp order. Staged through LDS
+// (row i, columns in kp order), then copied out.
+template <typename IO>
+__device__ void store_map_image(Smem16<IO, false>& sm, const f32x4 M[8], f16* dst) {
+    f16* img = reinterpret_cast<f16*>(&sm);   // 128 rows of LMI fp16 (36 KiB) over the chunk buffers
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
+    __syncthreads();   // the chain's last LDS reads are done
+    // column k = 16 w + c -> kp position 32 (w / 2) + 8 (c / 4) + 4 (w % 2) + c % 4
+    const int col = 32 * (w >> 1) + 8 * (c >> 2) + 4 * (w & 1) + (c & 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) img[(16 * i + 4 * g + e) * LMI + col] = (f16)M[i][e];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // fragment F = 4 w + j: row tile w, k step j
+        *reinterpret_cast<f16x8*>(dst + ((size_t)(4 * w + j) * 64 + lane) * 8) =
+            *reinterpret_cast<const f16x8*>(img + (16 * w + c) * LMI + 32 * j + 8 * g);
+}
+
+template <typename IO>
+__device__ void cp_item16(const Params& p, Smem16<IO, false>& sm, int slot, int part, int h) {
+    const SegLoc loc = locate_segment(p, slot);
+    int wq;
+    const int cls = pair_class16(p, slot * p.h_v + h, wq);
+    if (cls < 0) return;
+    const int a = loc.s * p.L;   // first chunk of segment s
+    if (cls && part == 1) return;
+    if (!cls && part == 1 && loc.s == 1 && !p.s_init) return;
+    f32x4 S[8];
+    if (cls || part == 0) {
+        const int c_lo = cls ? a - wq : a - p.L;
+        if (cls && c_lo == 0 && p.s_init) load_rm(p.s_init + tiles_off(loc.seq, p.h_v, h), S);
+        else set_state(S, false);
+        run_chunks16<IO, false, true>(sm, p, loc, h, c_lo, a, S);
+        store_tiles(cls ? p.seg_state + tiles_off(loc.seg_base + loc.s, p.h_v, h)
+                        : p.seg_H + tiles_off(loc.seg_base + loc.s - 1, p.h_v, h), S);
+    } else {
+        set_state(S, true);
+        run_chunks16<IO, false, false>(sm, p, loc, h, a - p.L, a, S);
+        // (the image is 128 x 128 fp16: the same element count as a state block)
+        store_map_image<IO>(sm, S, reinterpret_cast<f16*>(p.seg_M) + tiles_off(loc.seg_base + loc.s - 1, p.h_v, h));
+    }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(NT8) void k_cp_prep16(Params p) {
+    __shared__ Smem16<IO, false> sm;
+    __shared__ int rank_red[2 * NW8 + 4];
+    const int i = (int)blockIdx.x;
+    if (!p.cp_order) {   // head-major order
+        cp_item16<IO>(p, sm, (i % (2 * p.n_segments)) >> 1, i & 1, i / (2 * p.n_segments));
+        return;
+    }
+    const int n_pairs = p.n_segments * p.h_v;
+    const int per = (n_pairs + NT8 - 1) / NT8, q0 = threadIdx.x * per, q1 = min(q0 + per, n_pairs);
+    int n_ex = 0, n_wu = 0;
+    for (int q = q0; q < q1; ++q) {
+        int wq;
+        const int c = pair_class16(p, q, wq);
+        n_ex += c == 0;
+        n_wu += c > 0;
+    }
+    if (threadIdx.x == 0) rank_red[2 * NW8] = -1;   // (ordered before its use by the scans' barriers)
+    int tot_ex, tot_wu;
+    const int pre_ex = block_excl_scan8(n_ex, rank_red, tot_ex);
+    const int pre_wu = block_excl_scan8(n_wu, rank_red + NW8, tot_wu);
+    const bool want_ex = i < 2 * tot_ex;
+    const int r = want_ex ? i >> 1 : i - 2 * tot_ex;
+    if (!want_ex && r >= tot_wu) return;   // (uniform: every thread has the totals)
+    const int pre = want_ex ? pre_ex : pre_wu, cnt = want_ex ? n_ex : n_wu;
+    if (r >= pre && r < pre + cnt) {
+        int k = pre;
+        for (int q = q0; q < q1; ++q) {
+            int wq;
+            const int c = pair_class16(p, q, wq);
+            if (want_ex ? c == 0 : c > 0) {
+                if (k == r) {
+                    rank_red[2 * NW8] = q;
+                    break;
+                }
+                ++k;
+            }
+        }
+    }
+    __syncthreads();
+    const int q = rank_red[2 * NW8];
+    if (q < 0 || q >= n_pairs) return;   // (cannot happen: the ranks partition the boundaries)
+    cp_item16<IO>(p, sm, q / p.h_v, want_ex ? (i & 1) : 0, q % p.h_v);
+}
+
+// ----------------------------------------------------------------------------
+// The segment combine: one wave per (sequence, value head, 16-column tile u).
+// Boundary s (1 <= s < P): exact, S0(s) = M_{s-1} S0(s-1) + H_{s-1} (the map
+// product on fp16 operands: the M image as A, the state's fp16 tiles as B;
+// M_0 only with an initial state); warm-up, S0(s) is the warm-up state
+// k_cp_prep16 wrote. The next step's map and H tile are loaded during the
+// current one (every step issues the same loads).
+__global__ __launch_bounds__(64) void k_combine16(Params p) {
+    const int u = blockIdx.x & 7, seq = blockIdx.x >> 3, h = blockIdx.y;
+    if (seq >= p.n_seqs) return;
+    int P, seg_base;
+    if (!p.cu) {
+        P = n_segs_of(n_chunks_of(p.seq_len), p.L);
+        seg_base = seq * P;
+    } else {
+        seg_base = 0;
+        for (int n = 0; n < seq; ++n) seg_base += n_segs_of(n_chunks_of(p.cu[n + 1] - p.cu[n]), p.L);
+        P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
+    }
+    if (P <= 1) return;
+    int any_exact = 0;
+    for (int s = 1 + lane_id(); s < P; s += 64) any_exact |= (p.warm[(size_t)(seg_base + s) * p.h_v + h] & 255) == 0;
+    if (!__any(any_exact)) return;   // every boundary warmed up: nothing to chain
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    f32x4 cur[8];
+    if (p.s_init) {
+        const float* S0 = p.s_init + tiles_off(seq, p.h_v, h);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cur[t][e] = S0[(16 * t + 4 * g + e) * DK + 16 * u + c];
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cur[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    struct Ops {
+        f32x4 add[8];
+        u32x4 m[32];
+    };
+    auto fetch = [&](Ops& o, int s) {
+        s = min(s, P - 1);
+        const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h] & 255;
+        const float* src = f ? p.seg_state + tiles_off(seg_base + s, p.h_v, h)
+                             : p.seg_H + tiles_off(seg_base + s - 1, p.h_v, h);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o.add[t] = *reinterpret_cast<const f32x4*>(src + ((t * 8 + u) * 64 + lane) * 4);
+        const u32x4* mi = reinterpret_cast<const u32x4*>(reinterpret_cast<const f16*>(p.seg_M) +
+                                                          tiles_off(seg_base + s - 1, p.h_v, h));
+#pragma unroll
+        for (int F = 0; F < 32; ++F) o.m[F] = mi[F * 64 + lane];
+    };
+    // a warm-up boundary keeps its state (written back unchanged); an exact
+    // one applies the map (M_0 only to an initial state). Both are evaluated
+    // and selected, so that every step issues the same memory operations.
+    auto step = [&](int s, const Ops& o) {
+        const int f = __builtin_amdgcn_readfirstlane(p.warm[(size_t)(seg_base + s) * p.h_v + h]) & 255;
+        const bool mm = !f && (s > 1 || p.s_init);
+        f16x8 Sb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Sb[j] = pack8h(cur[2 * j], cur[2 * j + 1]);
+        f32x4 acc[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[t] = mmh(__builtin_bit_cast(f16x8, o.m[4 * t + j]), Sb[j], acc[t]);
+        float* dst = p.seg_state + tiles_off(seg_base + s, p.h_v, h);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            cur[t] = mm ? o.add[t] + acc[t] : o.add[t];
+            *reinterpret_cast<f32x4*>(dst + ((t * 8 + u) * 64 + lane) * 4) = cur[t];
+        }
+    };
+    Ops A, B;
+    fetch(A, 1);
+    fetch(B, 2);
+    int s = 1;
+    for (; s + 1 < P; s += 2) {
+        step(s, A);
+        fetch(A, s + 2);
+        step(s + 1, B);
+        fetch(B, s + 3);
+    }
+    if (s < P) step(s, A);
+}
+
+// ----------------------------------------------------------------------------
+// The fused forward of one segment per (segment slot, value head): from its
+// initial state (the caller's for segment 0, else the boundary state), every
+// chunk's output and state update; the last segment writes the final state.
+template <typename IO>
+__global__ __launch_bounds__(NT8) void k_fwd16(Params p) {
+    __shared__ Smem16<IO, true> sm;
+    const int h = blockIdx.y;
+    const SegLoc loc = locate_segment(p, blockIdx.x);
+    if (loc.seq < 0) return;
+    f32x4 S[8];
+    if (loc.s == 0) {
+        if (p.s_init) load_rm(p.s_init + tiles_off(loc.seq, p.h_v, h), S);
+        else set_state(S, false);
+    } else {
+        load_tiles(p.seg_state + tiles_off(loc.seg_base + loc.s, p.h_v, h), S);
+    }
+    const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
+    run_chunks16<IO, true, true>(sm, p, loc, h, c0, c1, S);
+    if (loc.s == loc.P - 1 && p.s_final) store_rm(p.s_final + tiles_off(loc.seq, p.h_v, h), S);
+}
+
+// Boundary states in tile order -> row-major (debug copies).
+__global__ __launch_bounds__(64) void k_tiles_to_rm(const float* src, float* dst) {
+    const size_t blk = blockIdx.x;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const float* s = src + blk * DK * DK;
+    float* d = dst + blk * DK * DK;
+    for (int tu = 0; tu < 64; ++tu) {
+        const int t = tu >> 3, u = tu & 7;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(s + (tu * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[(16 * t + 4 * g + e) * DK + 16 * u + c] = v[e];
+    }
+}
+
+int launched16() { return (int)hipGetLastError(); }
+
+}  // namespace
+
+int launch_cp_prep16(const Params& p, int io, void* stream) {
+    const dim3 grid((unsigned)(2 * p.n_segments * p.h_v)), block(NT8);
+    if (io == kIoBf16) hipLaunchKernelGGL(k_cp_prep16<bf16>, grid, block, 0, (hipStream_t)stream, p);
+    else hipLaunchKernelGGL(k_cp_prep16<float>, grid, block, 0, (hipStream_t)stream, p);
+    return launched16();
+}
+
+int launch_combine16(const Params& p, void* stream) {
+    const dim3 grid((unsigned)(8 * p.n_seqs), (unsigned)p.h_v), block(64);
+    hipLaunchKernelGGL(k_combine16, grid, block, 0, (hipStream_t)stream, p);
+    return launched16();
+}
+
+int launch_fwd16(const Params& p, int io, void* stream) {
+    const dim3 grid((unsigned)p.n_segments, (unsigned)p.h_v), block(NT8);
+    if (io == kIoBf16) hipLaunchKernelGGL(k_fwd16<bf16>, grid, block, 0, (hipStream_t)stream, p);
+    else hipLaunchKernelGGL(k_fwd16<float>, grid, block, 0, (hipStream_t)stream, p);
+    return launched16();
+}
+
+int launch_tiles_to_rm(const float* src, float* dst, long long n_blocks, void* stream) {
+    if (n_blocks <= 0) return 0;
+    hipLaunchKernelGGL(k_tiles_to_rm, dim3((unsigned)n_blocks), dim3(64), 0, (hipStream_t)stream, src, dst);
+    return launched16();
+}
+
+}  // namespace gdn

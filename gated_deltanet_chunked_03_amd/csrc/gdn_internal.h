@@ -9,6 +9,7 @@ namespace gdn {
 constexpr int kChunk = 64;   // tokens per chunk
 constexpr int kDim = 128;    // d_k == d_v
 constexpr int kMaxSegsPerSeq = 2048;  // the combine kernel keeps one flag per segment in LDS
+constexpr int kTbHalfs = 6 * 64 * 8;  // fp16 per (chunk, value head) in the T diag(beta) image (6 KiB)
 
 struct Params {
     // inputs
@@ -37,6 +38,8 @@ struct Params {
     int64_t gb_stride;        // floats between consecutive gamma/beta blocks (>= 128)
     int32_t prep_cpw;         // (head, chunk) items per k_prep workgroup
     float* sink;              // 8 KiB scratch line for stores of rows past a sequence's end
+    void* tb16;               // [n_chunks][h_v] fp16 images of T diag(beta) (kTbHalfs each), or null:
+                              //   k_prep then writes the split T and gamma, beta (prep_T, prep_GB)
     float* chunk_states;      // [n_chunks][h_v][128][128] state entering each chunk (backward recompute)
     float* bwd_y;             // with chunk_states: per (chunk, head) [64][128] fp32 Y = V - diag(e^gamma) K S,
     float* bwd_vp;            //   and V'; and per (chunk, head) [8 waves][64] partial sums over d_v of
@@ -124,5 +127,12 @@ int launch_fwd(const Params& p, int io, void* stream);
 int launch_fwd_states(const Params& p, int io, void* stream);
 int launch_debug_path(const Params& p, int32_t* path_out, void* stream);
 int launch_decode(const Params& p, int io, void* stream);
+
+// The forward's fp16 chain kernels (gdn_fwd16.hip); k_prep writes their
+// T diag(beta) images when Params::tb16 is set.
+int launch_cp_prep16(const Params& p, int io, void* stream);
+int launch_combine16(const Params& p, void* stream);
+int launch_fwd16(const Params& p, int io, void* stream);
+int launch_tiles_to_rm(const float* src, float* dst, long long n_blocks, void* stream);
 
 }  // namespace gdn

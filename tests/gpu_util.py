@@ -5,6 +5,13 @@ Tolerance (stated for bf16 inputs; also applied to fp32 inputs):
     max |o - o_ref| <= 1e-2 * max |o_ref|
     sum |o - o_ref| / sum |o_ref| <= 2e-3      (mean relative error, as relative L1)
 o_ref is the fp64 sequential oracle on exactly the values the GPU sees.
+
+States (final states and segment boundary states) are checked at 1e-3
+relative, the bound the target states for the warm-up path's extra state
+error: the forward's chain runs on fp16 matrix-core operands (every derived
+operand rounded once to an 11-bit significand), which leaves states about
+5e-4 off (measured in a CPU model of that rounding), exact and warm-up
+boundaries alike.
 """
 from __future__ import annotations
 
@@ -14,6 +21,9 @@ from oracle import gdn_sequential
 
 MAX_TOL = 1e-2
 MEAN_TOL = 2e-3
+STATE_MAX_TOL = 2e-3    # max |S - S_ref| / max |S_ref|
+STATE_MEAN_TOL = 1e-3   # sum |S - S_ref| / sum |S_ref|
+BOUNDARY_TOL = 1e-3     # ||S0 - S0_ref||_F / ||S0_ref||_F per boundary, exact or warm-up
 
 
 def to_device(inp, device="cuda"):

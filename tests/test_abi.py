@@ -104,15 +104,17 @@ def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
     assert p["P_max"] == -(-N // L) and p["n_segments"] == B_ * p["P_max"]
     assert p["cp_on"] == int(p["P_max"] > 1)
     per_seg = h_v * 128 * 128 * 4
-    # T (64 x 64, split into two bf16 halves) and gamma, beta per (chunk, value head)
-    prep = p["n_chunks_total"] * h_v * (64 * 64 * 4 + 2 * 64 * 4) + 8192   # + the scratch line
+    # the scratch line, then T diag(beta) as fp16 operand images (6 KiB per chunk and value head)
+    prep = 8192 + p["n_chunks_total"] * h_v * 6 * 64 * 8 * 2
     if p["cp_on"]:
         flags = -(-(p["n_segments"] * h_v * 4) // 256) * 256
-        # the grouped combine (the rule stated in gdn_api.cpp): G boundaries per group
-        # when slow (G rounds + G - 1) + (J - 2) + 4 steps beat the single chain of
-        # P - 1, J = ceil((P - 1) / G), assuming 30 % of the (sequence, head) pairs
-        # exact (to the nearest, at least one), 8 composing workgroups per group and
-        # exact head, slow = 2.5 past half the CUs
+        # boundary states and H maps (fp32), M maps (fp16 images), boundary flags
+        assert p["workspace_bytes"] == prep + 2 * p["n_segments"] * per_seg + p["n_segments"] * per_seg // 2 + flags
+        # the grouped combine of the backward's re-run (the rule stated in gdn_api.cpp):
+        # G boundaries per group when slow (G rounds + G - 1) + (J - 2) + 4 steps beat
+        # the single chain of P - 1, J = ceil((P - 1) / G), assuming 30 % of the
+        # (sequence, head) pairs exact (to the nearest, at least one), 8 composing
+        # workgroups per group and exact head, slow = 2.5 past half the CUs
         nb, best, G_exp = p["P_max"] - 1, float(p["P_max"] - 1), 0
         heads = max(1, (B_ * h_v * 3 + 5) // 10)
         for G in range(2, nb):
@@ -128,8 +130,6 @@ def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
         assert p["combine_group"] == G_exp
         J_exp = -(-nb // G_exp) if G_exp else 0
         assert p["combine_groups"] == J_exp
-        grp = 3 * B_ * J_exp * per_seg   # CM, CH and a scratch block per (sequence, group, head)
-        assert p["workspace_bytes"] == prep + 3 * p["n_segments"] * per_seg + flags + grp
     else:
         assert p["workspace_bytes"] == prep and p["combine_group"] == 0
 

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from gated_deltanet_chunked_03_amd.synth import make_inputs
-from gpu_util import assert_within_tolerance, oracle_run, to_device
+from gpu_util import STATE_MAX_TOL, STATE_MEAN_TOL, assert_within_tolerance, oracle_run, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -73,9 +73,9 @@ def test_prefill_then_decode_continues_the_recurrence():
     o_ref, s_ref, _ = oracle_run(inp)
     o_dec = torch.cat(outs, dim=1).float().cpu().numpy()[0]
     assert_within_tolerance(o_dec, o_ref[T0:], "decoded outputs")
-    # the state went through the bf16-input chunked prefill first: its tolerance
-    # is the forward's final-state bound, not the fp32 decode's
-    assert_within_tolerance(state.cpu().numpy(), s_ref, "state after decode", 1e-3, 1e-4)
+    # the state went through the chunked prefill (fp16 matrix-core operands)
+    # first: its tolerance is the forward's final-state bound, not the fp32 decode's
+    assert_within_tolerance(state.cpu().numpy(), s_ref, "state after decode", STATE_MAX_TOL, STATE_MEAN_TOL)
 
 
 def test_decode_in_place_equals_out_of_place():
