@@ -52,6 +52,7 @@ constexpr int LT = 80;           // K^T rows: 160 bytes
 constexpr int LP = 80;           // P rows
 constexpr int LV = 136;          // V rows (elements of the input type): 272 / 544 bytes
 constexpr int LMI = 144;         // rows of the map image staged for the combine
+constexpr float kLog2e = 1.4426950408889634f;
 
 // The six nonzero T diag(beta) fragments (token tile m, k step j): 0 (0,0),
 // 1 (1,0), 2 (2,0), 3 (2,1), 4 (3,0), 5 (3,1) -- the same (m, j) pairs as
@@ -70,7 +71,7 @@ struct __attribute__((aligned(16))) Smem16 {
     IO v[CH * LV];                        // V rows as given
     f16 tb[kTbHalfs];                     // T diag(beta) fragments (k_prep's image)
     f16 p[OUT ? CH * LP : 8];             // P: row r, columns i in kp order
-    float gam[2][CH];                     // gamma
+    float gam[2][CH];                     // gamma log2(e)
     float eg[2][CH];                      // e^gamma
     float egc[2][CH];                     // e^(gamma_C - gamma)
     float ec[2][4];                       // e^gamma_C
@@ -84,31 +85,63 @@ template <typename IO> struct In16;
 template <> struct In16<bf16> { u32x2 k[4], q[4], v[4]; u32x4 tb; float g; };
 template <> struct In16<float> { f32x4 k[4], q[4], v[4]; u32x4 tb; float g; };
 
-// Rows past the end of the sequence read its last row again (those tokens
-// carry g = beta = 0: their columns of T diag(beta) are zero, so they reach
-// neither a valid output nor the state). Every chunk issues the same loads.
-template <typename IO, bool WANT_Q, bool WANT_V>
-__device__ __forceinline__ void fetch16(In16<IO>& r, const Params& p, size_t tok0, int nvalid, int h, int hq,
-                                        int slot) {
-    const int t = threadIdx.x, lane = lane_id(), rq = t >> 5, c4 = 4 * (t & 31);
-    const size_t ts = (size_t)p.h_qk * DK, tsv = (size_t)p.h_v * DK;
-    // the gate first (wave 0's scan waits for it), then K, Q, V, T diag(beta)
-    r.g = lane < nvalid ? p.g[(tok0 + lane) * (size_t)p.h_v + h] : 0.f;
-    const IO* kb = static_cast<const IO*>(p.k) + tok0 * ts + (size_t)hq * DK + c4;
-    const IO* qb = static_cast<const IO*>(p.q) + tok0 * ts + (size_t)hq * DK + c4;
-    const IO* vb = static_cast<const IO*>(p.v) + tok0 * tsv + (size_t)h * DK + c4;
+// Buffer descriptors (raw, 32-bit offsets; word 3 selects 32-bit data on
+// gfx9-family chips). Each chunk gets descriptors whose base is its first row
+// and whose range ends at its last valid row: loads past a sequence's end
+// then return zeros and stores there are dropped by the range check, so the
+// per-lane offsets never change across chunks and no row is clamped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Per-lane byte offsets of a chain workgroup's loads and stores, the same for
+// every chunk (thread t: tokens 4 (t / 32) + j, columns 4 (t % 32) .. + 4).
+struct Lanes {
+    unsigned kq[4];   // K, Q rows
+    unsigned v[4];    // V rows
+    unsigned g;       // gate of token `lane`
+    unsigned o[4];    // output: token 16 m + c, d_v 16 w + 4 g
+};
+
+template <typename IO>
+__device__ Lanes make_lanes(const Params& p) {
+    Lanes L;
+    const int t = threadIdx.x, lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
+    const unsigned es = sizeof(IO), ts = (unsigned)p.h_qk * DK, tsv = (unsigned)p.h_v * DK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int row = min(4 * rq + j, nvalid - 1);
-        const unsigned o = (unsigned)(row * (int)ts), ov = (unsigned)(row * (int)tsv);
+        const unsigned row = 4 * (t >> 5) + j;
+        L.kq[j] = (row * ts + 4 * (t & 31)) * es;
+        L.v[j] = (row * tsv + 4 * (t & 31)) * es;
+        L.o[j] = ((16 * j + c) * tsv + 16 * w + 4 * g) * es;
+    }
+    L.g = (unsigned)lane * p.h_v * 4;
+    return L;
+}
+
+// Loads one chunk's inputs: the gate first (wave 0's scan waits for it),
+// then K, Q, V, T diag(beta).
+template <typename IO, bool WANT_Q, bool WANT_V>
+__device__ __forceinline__ void fetch16(In16<IO>& r, const Params& p, const Lanes& L, size_t tok0, int nvalid,
+                                        int h, int hq, int slot) {
+    const int t = threadIdx.x;
+    const unsigned es = sizeof(IO), nv = (unsigned)nvalid;
+    const size_t ts = (size_t)p.h_qk * DK, tsv = (size_t)p.h_v * DK;
+    r.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        rsrc(p.g + tok0 * p.h_v + h, nv * p.h_v * 4), (int)L.g, 0, 0));
+    const auto rk = rsrc(static_cast<const IO*>(p.k) + tok0 * ts + (size_t)hq * DK, nv * (unsigned)ts * es);
+    const auto rq = rsrc(static_cast<const IO*>(p.q) + tok0 * ts + (size_t)hq * DK, nv * (unsigned)ts * es);
+    const auto rv = rsrc(static_cast<const IO*>(p.v) + tok0 * tsv + (size_t)h * DK, nv * (unsigned)tsv * es);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
         if constexpr (Io<IO>::kExact) {
-            r.k[j] = *reinterpret_cast<const u32x2*>(kb + o);
-            if (WANT_Q) r.q[j] = *reinterpret_cast<const u32x2*>(qb + o);
-            if (WANT_V) r.v[j] = *reinterpret_cast<const u32x2*>(vb + ov);
+            r.k[j] = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)L.kq[j], 0, 0);
+            if (WANT_Q) r.q[j] = __builtin_amdgcn_raw_buffer_load_b64(rq, (int)L.kq[j], 0, 0);
+            if (WANT_V) r.v[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)L.v[j], 0, 0);
         } else {
-            r.k[j] = *reinterpret_cast<const f32x4*>(kb + o);
-            if (WANT_Q) r.q[j] = *reinterpret_cast<const f32x4*>(qb + o);
-            if (WANT_V) r.v[j] = *reinterpret_cast<const f32x4*>(vb + ov);
+            r.k[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)L.kq[j], 0, 0));
+            if (WANT_Q) r.q[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)L.kq[j], 0, 0));
+            if (WANT_V) r.v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)L.v[j], 0, 0));
         }
     }
     // (threads past the 384 pieces load piece t - 384 again; only t < 384 store)
@@ -135,7 +168,7 @@ __device__ __forceinline__ void stage16(Smem16<IO, OUT>& sm, const In16<IO>& r, 
     if (wave_id() == 0) {
         const float gam = wave_scan(r.g);
         const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
-        sm.gam[b][lane] = gam;
+        sm.gam[b][lane] = gam * kLog2e;   // (P's decay factors are formed as powers of two)
         sm.eg[b][lane] = __expf(gam);
         sm.egc[b][lane] = __expf(gc - gam);
         if (lane == 0) sm.ec[b][0] = __expf(gc);
@@ -215,9 +248,9 @@ __device__ void set_state(f32x4 S[8], bool identity) {
 // without output: the warm-up and H chains (WANT_V) or the M chain (V = 0).
 // The chunk is in LDS (K^T in buffer b); `nxt`, the next chunk's inputs, is
 // staged after the first barrier.
-template <typename IO, bool OUT, bool WANT_V>
-__device__ __forceinline__ void chain_step16(Smem16<IO, OUT>& sm, const In16<IO>& nxt, int b, f32x4 S[8],
-                                             float scale, IO* orow, size_t ts_v, int nvalid, float* sink) {
+template <typename IO, bool OUT, bool WANT_V, int b>
+__device__ __forceinline__ void chain_step16(Smem16<IO, OUT>& sm, const In16<IO>& nxt, f32x4 S[8], float scale,
+                                             float log2_scale, const Lanes& L, __amdgpu_buffer_rsrc_t ro) {
     const int lane = lane_id(), c = lane & 15, g = lane >> 4, w = wave_id();
     // the state as fp16 operands, one per k step j
     f16x8 Sb[4];
@@ -260,15 +293,16 @@ __device__ __forceinline__ void chain_step16(Smem16<IO, OUT>& sm, const In16<IO>
     if constexpr (OUT) {
         // P[r][i] = scale e^(gamma_r - gamma_i) (q_r . k_i), i <= r, else 0; the
         // tiles hold P^T: lane (g, c) has r = 16 rb + c and i = 16 ib + 4 g + e
+        // (gamma is kept times log2(e): the factor is 2^(gr - gi), the scale folded in)
         const int r = 16 * rb + c;
-        const float gr = sm.gam[b][r];
+        const float gr = sm.gam[b][r] + log2_scale;
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
             const int ib = ib0 + e2, i0 = 16 * ib + 4 * g;
             const f32x4 gi = *reinterpret_cast<const f32x4*>(sm.gam[b] + i0);
             f32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (i0 + e <= r) ? scale * __expf(gr - gi[e]) * Pt[e2][e] : 0.f;
+            for (int e = 0; e < 4; ++e) v[e] = (i0 + e <= r) ? __builtin_amdgcn_exp2f(gr - gi[e]) * Pt[e2][e] : 0.f;
             *reinterpret_cast<f16x4*>(sm.p + r * LP + 32 * (ib >> 1) + 8 * g + 4 * (ib & 1)) =
                 __builtin_convertvector(v, f16x4);
         }
@@ -340,15 +374,15 @@ __device__ __forceinline__ void chain_step16(Smem16<IO, OUT>& sm, const In16<IO>
                 const f16x8 pf = *reinterpret_cast<const f16x8*>(sm.p + (16 * m + c) * LP + 32 * j + 8 * g);
                 O[m] = mmh(Vb[j], pf, O[m]);
             }
-        // lane (g, c) of tile m: token 16 m + c, d_v 16 w + 4 g + (0..3)
+        // lane (g, c) of tile m: token 16 m + c, d_v 16 w + 4 g + (0..3) (rows
+        // past the sequence's end fall outside the descriptor's range: dropped)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int r = 16 * m + c;
-            IO* dst = (r < nvalid) ? orow + (size_t)r * ts_v + 16 * w + 4 * g : reinterpret_cast<IO*>(sink + 32 * lane);
             if constexpr (Io<IO>::kExact)
-                *reinterpret_cast<u32x2*>(dst) = u32x2{pack_rne(O[m][0], O[m][1]), pack_rne(O[m][2], O[m][3])};
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_rne(O[m][0], O[m][1]), pack_rne(O[m][2], O[m][3])}, ro,
+                                                      (int)L.o[m], 0, 0);
             else
-                *reinterpret_cast<f32x4*>(dst) = O[m];
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, O[m]), ro, (int)L.o[m], 0, 0);
         }
     }
     stage16<IO, OUT, WANT_V>(sm, nxt, b ^ 1);
@@ -384,16 +418,17 @@ __device__ void run_chunks16(Smem16<IO, OUT>& sm, const Params& p, const SegLoc&
     if (c_lo >= c_hi) return;
     const int hq = h / p.group;
     const size_t ts_v = (size_t)p.h_v * DK;
+    const Lanes L = make_lanes<IO>(p);
+    const float log2_scale = __log2f(p.scale);
     In16<IO> A, B;
     auto fetch = [&](In16<IO>& r, int c) {
         c = min(c, c_hi - 1);
-        fetch16<IO, OUT, WANT_V>(r, p, loc.tok0 + (size_t)c * CH, min(CH, loc.len - c * CH), h, hq,
+        fetch16<IO, OUT, WANT_V>(r, p, L, loc.tok0 + (size_t)c * CH, min(CH, loc.len - c * CH), h, hq,
                                  loc.chunk_base + c);
     };
-    auto step = [&](int c, const In16<IO>& nxt) {
-        const int b = (c - c_lo) & 1;
-        IO* orow = OUT ? static_cast<IO*>(p.out) + (loc.tok0 + (size_t)c * CH) * ts_v + (size_t)h * DK : nullptr;
-        chain_step16<IO, OUT, WANT_V>(sm, nxt, b, S, p.scale, orow, ts_v, min(CH, loc.len - c * CH), p.sink);
+    auto orsrc = [&](int c) {
+        return rsrc(OUT ? static_cast<IO*>(p.out) + (loc.tok0 + (size_t)c * CH) * ts_v + (size_t)h * DK : nullptr,
+                    OUT ? (unsigned)min(CH, loc.len - c * CH) * (unsigned)(ts_v * sizeof(IO)) : 0u);
     };
     fetch(A, c_lo);
     stage16<IO, OUT, WANT_V>(sm, A, 0);
@@ -402,12 +437,12 @@ __device__ void run_chunks16(Smem16<IO, OUT>& sm, const Params& p, const SegLoc&
     __syncthreads();
     int c = c_lo;
     for (; c + 1 < c_hi; c += 2) {
-        step(c, B);
+        chain_step16<IO, OUT, WANT_V, 0>(sm, B, S, p.scale, log2_scale, L, orsrc(c));
         fetch(B, c + 3);
-        step(c + 1, A);
+        chain_step16<IO, OUT, WANT_V, 1>(sm, A, S, p.scale, log2_scale, L, orsrc(c + 1));
         fetch(A, c + 4);
     }
-    if (c < c_hi) step(c, B);
+    if (c < c_hi) chain_step16<IO, OUT, WANT_V, 0>(sm, B, S, p.scale, log2_scale, L, orsrc(c));
 }
 
 // ----------------------------------------------------------------------------
@@ -545,13 +580,20 @@ __global__ __launch_bounds__(NT8) void k_cp_prep16(Params p) {
 }
 
 // ----------------------------------------------------------------------------
-// The segment combine: one wave per (sequence, value head, 16-column tile u).
-// Boundary s (1 <= s < P): exact, S0(s) = M_{s-1} S0(s-1) + H_{s-1} (the map
-// product on fp16 operands: the M image as A, the state's fp16 tiles as B;
-// M_0 only with an initial state); warm-up, S0(s) is the warm-up state
-// k_cp_prep16 wrote. The next step's map and H tile are loaded during the
-// current one (every step issues the same loads).
-__global__ __launch_bounds__(64) void k_combine16(Params p) {
+// The segment combine: one 4-wave workgroup per (sequence, value head,
+// 16-column tile u). Boundary s (1 <= s < P): exact, S0(s) = M_{s-1} S0(s-1)
+// + H_{s-1} (the map product on fp16 operands: the M image as A, the state
+// column tile as B; M_0 only with an initial state); warm-up, S0(s) is the
+// warm-up state k_cp_prep16 wrote. Wave r owns rows [32 r, 32 r + 32) of the
+// column tile -- exactly the k step r of the next product's B operand -- and
+// hands its fp16 rows to the others through LDS once per step, so a step is
+// eight MFMAs per wave plus one exchange. The boundary flags are read into LDS
+// first; each step's operands (eight M fragments, two H tiles per lane) are
+// loaded two steps ahead, and every step issues the same memory operations.
+constexpr int NTC = 256;
+__global__ __launch_bounds__(NTC) void k_combine16(Params p) {
+    __shared__ int flags[kMaxSegsPerSeq];
+    __shared__ __attribute__((aligned(16))) f16 xb[2][4 * 64 * 8];   // the state tile as B operands, per k step
     const int u = blockIdx.x & 7, seq = blockIdx.x >> 3, h = blockIdx.y;
     if (seq >= p.n_seqs) return;
     int P, seg_base;
@@ -563,72 +605,84 @@ __global__ __launch_bounds__(64) void k_combine16(Params p) {
         for (int n = 0; n < seq; ++n) seg_base += n_segs_of(n_chunks_of(p.cu[n + 1] - p.cu[n]), p.L);
         P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
     }
-    if (P <= 1) return;
+    if (P <= 1 || P > kMaxSegsPerSeq) return;
     int any_exact = 0;
-    for (int s = 1 + lane_id(); s < P; s += 64) any_exact |= (p.warm[(size_t)(seg_base + s) * p.h_v + h] & 255) == 0;
-    if (!__any(any_exact)) return;   // every boundary warmed up: nothing to chain
-    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
-    f32x4 cur[8];
-    if (p.s_init) {
-        const float* S0 = p.s_init + tiles_off(seq, p.h_v, h);
+    for (int s = 1 + (int)threadIdx.x; s < P; s += NTC) {
+        const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h] & 255;
+        flags[s] = f;
+        any_exact |= f == 0;
+    }
+    if (!__syncthreads_or(any_exact)) return;   // every boundary warmed up: nothing to chain
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, r = wave_id();
+    // S0(0) (row tiles 2 r, 2 r + 1 of column tile u) -> this wave's k step of the B operand
+    {
+        f32x4 cur[2];
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * r + tt;
+            if (p.s_init) {
+                const float* S0 = p.s_init + tiles_off(seq, p.h_v, h);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) cur[t][e] = S0[(16 * t + 4 * g + e) * DK + 16 * u + c];
-    } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) cur[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int e = 0; e < 4; ++e) cur[tt][e] = S0[(16 * t + 4 * g + e) * DK + 16 * u + c];
+            } else {
+                cur[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        *reinterpret_cast<f16x8*>(xb[0] + (r * 64 + lane) * 8) = pack8h(cur[0], cur[1]);
     }
     struct Ops {
-        f32x4 add[8];
-        u32x4 m[32];
+        f32x4 add[2];   // H_{s-1} or the warm-up state, row tiles 2 r, 2 r + 1
+        u32x4 m[8];     // M_{s-1} fragments (row tile 2 r + f / 4, k step f % 4)
     };
     auto fetch = [&](Ops& o, int s) {
         s = min(s, P - 1);
-        const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h] & 255;
+        const int f = flags[s];
         const float* src = f ? p.seg_state + tiles_off(seg_base + s, p.h_v, h)
                              : p.seg_H + tiles_off(seg_base + s - 1, p.h_v, h);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o.add[t] = *reinterpret_cast<const f32x4*>(src + ((t * 8 + u) * 64 + lane) * 4);
+        for (int tt = 0; tt < 2; ++tt)
+            o.add[tt] = *reinterpret_cast<const f32x4*>(src + (((2 * r + tt) * 8 + u) * 64 + lane) * 4);
         const u32x4* mi = reinterpret_cast<const u32x4*>(reinterpret_cast<const f16*>(p.seg_M) +
                                                           tiles_off(seg_base + s - 1, p.h_v, h));
 #pragma unroll
-        for (int F = 0; F < 32; ++F) o.m[F] = mi[F * 64 + lane];
+        for (int f8 = 0; f8 < 8; ++f8) o.m[f8] = mi[(8 * r + f8) * 64 + lane];
     };
     // a warm-up boundary keeps its state (written back unchanged); an exact
     // one applies the map (M_0 only to an initial state). Both are evaluated
     // and selected, so that every step issues the same memory operations.
-    auto step = [&](int s, const Ops& o) {
-        const int f = __builtin_amdgcn_readfirstlane(p.warm[(size_t)(seg_base + s) * p.h_v + h]) & 255;
-        const bool mm = !f && (s > 1 || p.s_init);
+    auto step = [&](int s, const Ops& o, int buf) {
+        __syncthreads();   // the previous state's B operand is in xb[buf]
+        const bool mm = flags[s] == 0 && (s > 1 || p.s_init);
         f16x8 Sb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Sb[j] = pack8h(cur[2 * j], cur[2 * j + 1]);
-        f32x4 acc[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j) Sb[j] = *reinterpret_cast<const f16x8*>(xb[buf] + (j * 64 + lane) * 8);
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) acc[t] = mmh(__builtin_bit_cast(f16x8, o.m[4 * t + j]), Sb[j], acc[t]);
+            for (int tt = 0; tt < 2; ++tt) acc[tt] = mmh(__builtin_bit_cast(f16x8, o.m[4 * tt + j]), Sb[j], acc[tt]);
         float* dst = p.seg_state + tiles_off(seg_base + s, p.h_v, h);
+        f32x4 cur[2];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            cur[t] = mm ? o.add[t] + acc[t] : o.add[t];
-            *reinterpret_cast<f32x4*>(dst + ((t * 8 + u) * 64 + lane) * 4) = cur[t];
+        for (int tt = 0; tt < 2; ++tt) {
+            // (a select, not a product with 0: the maps of warm-up boundaries and
+            // M_0 without an initial state are never written and may hold NaNs)
+            cur[tt] = mm ? o.add[tt] + acc[tt] : o.add[tt];
+            *reinterpret_cast<f32x4*>(dst + (((2 * r + tt) * 8 + u) * 64 + lane) * 4) = cur[tt];
         }
+        *reinterpret_cast<f16x8*>(xb[buf ^ 1] + (r * 64 + lane) * 8) = pack8h(cur[0], cur[1]);
     };
     Ops A, B;
     fetch(A, 1);
     fetch(B, 2);
     int s = 1;
     for (; s + 1 < P; s += 2) {
-        step(s, A);
+        step(s, A, 0);
         fetch(A, s + 2);
-        step(s + 1, B);
+        step(s + 1, B, 1);
         fetch(B, s + 3);
     }
-    if (s < P) step(s, A);
+    if (s < P) step(s, A, 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -651,6 +705,389 @@ __global__ __launch_bounds__(NT8) void k_fwd16(Params p) {
     const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
     run_chunks16<IO, true, true>(sm, p, loc, h, c0, c1, S);
     if (loc.s == loc.P - 1 && p.s_final) store_rm(p.s_final + tiles_off(loc.seq, p.h_v, h), S);
+}
+
+// ----------------------------------------------------------------------------
+// The fused forward with specialised waves (bf16 inputs). The chunk step's
+// dependent chain is S -> K S -> Y -> V' -> S; the output (Q S, P, P V'),
+// the stores and the staging of the next chunk hang off it. Waves 0-3
+// (chain) own the d_v columns [32 w, 32 w + 32) of S in registers and run
+// only the chain; waves 4-7 (output) each sit beside one chain wave on its
+// SIMD and do the rest for the same 32 columns, reading the state and V' as
+// fp16 operands that the chain wave leaves in LDS. Per chunk:
+//   chain:  Y = K S, Y = V - e^gamma Y (V through the identity product,
+//           its rows loaded a chunk and a half ahead), V' = T diag(beta) Y,
+//           V' -> LDS
+//   output: O^T = S^T Q^T (S from LDS), its row block of P, scale
+//   -- barrier --
+//   chain:  S = e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V', S -> LDS
+//   output: O^T += V'^T P^T, stores, stage the next chunk (K, Q, T diag(beta)
+//           single-buffered: their readers are past the first barrier; K^T and
+//           the gate factors double-buffered)
+//   -- barrier --
+// so the matrix-core work of the output half overlaps the chain's VALU work
+// and the other way round.
+struct __attribute__((aligned(16))) SmemWS {
+    f16 k[CH * LQ];                       // K token-major, d_k in kp order
+    f16 q[CH * LQ];                       // Q token-major, d_k in kp order
+    f16 kt[2][DK * LT];                   // K^T: row d_k, tokens in kp order, 16-byte pieces XOR tswz(row)
+    f16 tb[kTbHalfs];                     // T diag(beta) fragments (k_prep's image)
+    f16 p[CH * LP];                       // P: row r, columns i in kp order
+    f16 sx[4][8 * 64 * 8];                // per column block: the state's fp16 operands [k step][tile][lane]
+    f16 vx[4][4 * 64 * 8];                // per column block: V' as fp16 operands [k step][tile][lane]
+    float gam[2][CH];                     // gamma log2(e)
+    float eg[2][CH];                      // e^gamma
+    float egc[2][CH];                     // e^(gamma_C - gamma)
+    float ec[2][4];                       // e^gamma_C
+};
+
+// The output waves' staging loads: thread t (0..255) holds tokens
+// 4 (t / 16) + j, d_k 8 (t % 16) .. + 8 of K and Q, pieces t and t + 256
+// (< 384) of the T diag(beta) image, and the gate of token `lane`.
+struct InWS {
+    u32x4 k[4], q[4], tb[2];
+    float g;
+};
+
+__device__ __forceinline__ f16x8 to_h8(const u32x4& x) {
+    return __builtin_convertvector(
+        f32x8{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u), __uint_as_float(x[1] << 16),
+              __uint_as_float(x[1] & 0xffff0000u), __uint_as_float(x[2] << 16), __uint_as_float(x[2] & 0xffff0000u),
+              __uint_as_float(x[3] << 16), __uint_as_float(x[3] & 0xffff0000u)},
+        f16x8);
+}
+
+// Chunk c's loads of the output waves (ot = thread index among them).
+__device__ __forceinline__ void ws_fetch(InWS& r, const Params& p, size_t tok0, int nvalid, int h, int hq, int slot,
+                                         int ot) {
+    const unsigned nv = (unsigned)nvalid;
+    const size_t ts = (size_t)p.h_qk * DK;
+    r.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        rsrc(p.g + tok0 * p.h_v + h, nv * p.h_v * 4), (int)((ot & 63) * p.h_v * 4), 0, 0));
+    const auto rk = rsrc(static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK, nv * (unsigned)ts * 2);
+    const auto rq = rsrc(static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK, nv * (unsigned)ts * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int o = (int)(((4 * (ot >> 4) + j) * ts + 8 * (ot & 15)) * 2);
+        r.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
+        r.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
+    }
+    const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const f16*>(p.tb16) +
+                                                     ((size_t)slot * p.h_v + h) * (size_t)kTbHalfs);
+    r.tb[0] = tb[ot];
+    r.tb[1] = tb[ot < 128 ? 256 + ot : ot];   // (pieces 256..383; the rest load piece ot again)
+}
+
+// Stages a fetched chunk (K^T and gate factors into buffer b).
+__device__ __forceinline__ void ws_stage(SmemWS& sm, const InWS& r, int b, int ot) {
+    const int lane = ot & 63, cq = ot & 15, rq = ot >> 4;
+    if (ot < 64) {   // the first output wave: the gate factors
+        const float gam = wave_scan(r.g);
+        const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
+        sm.gam[b][lane] = gam * kLog2e;
+        sm.eg[b][lane] = __expf(gam);
+        sm.egc[b][lane] = __expf(gc - gam);
+        if (lane == 0) sm.ec[b][0] = __expf(gc);
+    }
+    // d_k 8 cq .. + 8 -> kp positions p0 .. p0 + 3 and p0 + 8 .. p0 + 11; tokens
+    // 4 rq .. + 3 -> kp positions pt .. pt + 3
+    const int p0 = 32 * (cq >> 2) + 16 * (cq & 1) + 4 * ((cq >> 1) & 1);
+    const int pt = 32 * (rq >> 3) + 8 * (rq & 3) + 4 * ((rq >> 2) & 1);
+    f16x8 kr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        kr[j] = to_h8(r.k[j]);
+        f16* dk = sm.k + (4 * rq + j) * LQ;
+        *reinterpret_cast<f16x4*>(dk + p0) = f16x4{kr[j][0], kr[j][1], kr[j][2], kr[j][3]};
+        *reinterpret_cast<f16x4*>(dk + p0 + 8) = f16x4{kr[j][4], kr[j][5], kr[j][6], kr[j][7]};
+        const f16x8 qr = to_h8(r.q[j]);
+        f16* dq = sm.q + (4 * rq + j) * LQ;
+        *reinterpret_cast<f16x4*>(dq + p0) = f16x4{qr[0], qr[1], qr[2], qr[3]};
+        *reinterpret_cast<f16x4*>(dq + p0 + 8) = f16x4{qr[4], qr[5], qr[6], qr[7]};
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int d = 8 * cq + e;
+        *reinterpret_cast<f16x4*>(sm.kt[b] + d * LT + (pt ^ tswz(d))) = f16x4{kr[0][e], kr[1][e], kr[2][e], kr[3][e]};
+    }
+    *reinterpret_cast<u32x4*>(sm.tb + 8 * ot) = r.tb[0];
+    if (ot < 128) *reinterpret_cast<u32x4*>(sm.tb + 8 * (256 + ot)) = r.tb[1];
+}
+
+// The state (tiles [i][n], rows 16 i + 4 g + e, column 32 cw + 16 n + c) as the
+// fp16 operands of k step j, written for the output wave of the same columns.
+__device__ __forceinline__ void ws_put_state(SmemWS& sm, int cw, const f16x8 Sb[4][2]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) *reinterpret_cast<f16x8*>(sm.sx[cw] + ((2 * j + n) * 64 + lane) * 8) = Sb[j][n];
+}
+
+// Chain wave cw over chunks [c_lo, c_hi): S[8][2] in registers.
+__device__ void ws_chain(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw,
+                         f32x4 S[8][2]) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    const size_t tsv = (size_t)p.h_v * DK;
+    // this wave's V rows, as the A operands of the identity product: token
+    // 16 m + c, d_v 32 cw + 8 g .. + 8 (rows past the end read as zeros)
+    auto vfetch = [&](u32x4 V[4], int cc) {
+        cc = min(cc, c_hi - 1);
+        const auto rv = rsrc(static_cast<const bf16*>(p.v) + (loc.tok0 + (size_t)cc * CH) * tsv + (size_t)h * DK,
+                             (unsigned)min(CH, loc.len - cc * CH) * (unsigned)tsv * 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            V[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(((16 * m + c) * tsv + 32 * cw + 8 * g) * 2), 0, 0);
+    };
+    bf16x8 E[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) E[n][s] = (bf16)((8 * g + s == 16 * n + c) ? 1.f : 0.f);
+    f16x8 Sb[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) Sb[j][n] = pack8h(S[2 * j][n], S[2 * j + 1][n]);
+    ws_put_state(sm, cw, Sb);
+    u32x4 VA[4], VB[4];
+    vfetch(VA, c_lo);
+    vfetch(VB, c_lo + 1);
+    __syncthreads();   // (1) the first chunk staged, the state written
+    auto step = [&](int b, const u32x4 (&V)[4]) {
+        // Y = K S
+        f32x4 Y[4][2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) Y[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f16x8 kf[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) kf[m] = *reinterpret_cast<const f16x8*>(sm.k + (16 * m + c) * LQ + 32 * j + 8 * g);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) Y[m][n] = mmh(kf[m], Sb[j][n], Y[m][n]);
+        }
+        // Y = V - e^gamma (K S)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(sm.eg[b] + 16 * m + 4 * g);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) Y[m][n] = mma16k32(__builtin_bit_cast(bf16x8, V[m]), E[n], Y[m][n] * -eg);
+        }
+        // V' = (T diag(beta)) Y
+        f32x4 Vp[4][2];
+        {
+            f16x8 Yb[2][2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) Yb[j][n] = pack8h(Y[2 * j][n], Y[2 * j + 1][n]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f16x8 t0 = *reinterpret_cast<const f16x8*>(sm.tb + (tb_frag(m, 0) * 64 + lane) * 8);
+#pragma unroll
+                for (int n = 0; n < 2; ++n) Vp[m][n] = mmh(t0, Yb[0][n], f32x4{0.f, 0.f, 0.f, 0.f});
+                if (m >= 2) {
+                    const f16x8 t1 = *reinterpret_cast<const f16x8*>(sm.tb + (tb_frag(m, 1) * 64 + lane) * 8);
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) Vp[m][n] = mmh(t1, Yb[1][n], Vp[m][n]);
+                }
+            }
+        }
+        // V' for the output wave
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                *reinterpret_cast<f16x8*>(sm.vx[cw] + ((2 * j + n) * 64 + lane) * 8) = pack8h(Vp[2 * j][n], Vp[2 * j + 1][n]);
+        __syncthreads();   // (2) P and V' complete; the readers of K, Q, T diag(beta) are past
+        // S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
+        f16x8 Vb[2][2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 f = *reinterpret_cast<const f32x4*>(sm.egc[b] + 16 * m + 4 * g);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) Vp[m][n] *= f;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) Vb[j][n] = pack8h(Vp[2 * j][n], Vp[2 * j + 1][n]);
+        const float ec = sm.ec[b][0];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) S[i][n] *= ec;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f16x8 ktf[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ktf[i] = *reinterpret_cast<const f16x8*>(sm.kt[b] + (16 * i + c) * LT + ((32 * j + 8 * g) ^ tswz(16 * i)));
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) S[i][n] = mmh(ktf[i], Vb[j][n], S[i][n]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) Sb[j][n] = pack8h(S[2 * j][n], S[2 * j + 1][n]);
+        ws_put_state(sm, cw, Sb);
+        __syncthreads();   // (3) the next chunk staged, the new state written
+    };
+    int cc = c_lo;
+    for (; cc + 1 < c_hi; cc += 2) {
+        step(0, VA);
+        vfetch(VA, cc + 2);
+        step(1, VB);
+        vfetch(VB, cc + 3);
+    }
+    if (cc < c_hi) step(0, VA);
+}
+
+// Output wave for column block cw over chunks [c_lo, c_hi); ot = 64 cw + lane.
+__device__ void ws_output(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, ot = 64 * cw + lane;
+    const int hq = h / p.group;
+    const size_t tsv = (size_t)p.h_v * DK;
+    const float log2_scale = __log2f(p.scale);
+    InWS in;
+    auto fetch = [&](int cc) {
+        cc = min(cc, c_hi - 1);
+        ws_fetch(in, p, loc.tok0 + (size_t)cc * CH, min(CH, loc.len - cc * CH), h, hq, loc.chunk_base + cc, ot);
+    };
+    fetch(c_lo);
+    ws_stage(sm, in, 0, ot);
+    fetch(c_lo + 1);
+    __syncthreads();   // (1)
+    auto step = [&](int b, int cc) {
+        // O^T = S^T Q^T (this block's 32 columns; S from the chain wave) and P's
+        // row block [16 cw, 16 cw + 16): P^T tiles k_i . q_r, i block ib
+        f32x4 O[2][4], Pt[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            O[0][m] = O[1][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Pt[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f16x8 qf[4], kf[4], sb[2];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                qf[m] = *reinterpret_cast<const f16x8*>(sm.q + (16 * m + c) * LQ + 32 * j + 8 * g);
+                kf[m] = *reinterpret_cast<const f16x8*>(sm.k + (16 * m + c) * LQ + 32 * j + 8 * g);
+            }
+            const f16x8 qw = *reinterpret_cast<const f16x8*>(sm.q + (16 * cw + c) * LQ + 32 * j + 8 * g);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) sb[n] = *reinterpret_cast<const f16x8*>(sm.sx[cw] + ((2 * j + n) * 64 + lane) * 8);
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) O[n][m] = mmh(sb[n], qf[m], O[n][m]);
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) Pt[ib] = mmh(kf[ib], qw, Pt[ib]);
+        }
+        {
+            const int r = 16 * cw + c;
+            const float gr = sm.gam[b][r] + log2_scale;
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                const int i0 = 16 * ib + 4 * g;
+                const f32x4 gi = *reinterpret_cast<const f32x4*>(sm.gam[b] + i0);
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (i0 + e <= r) ? __builtin_amdgcn_exp2f(gr - gi[e]) * Pt[ib][e] : 0.f;
+                *reinterpret_cast<f16x4*>(sm.p + r * LP + 32 * (ib >> 1) + 8 * g + 4 * (ib & 1)) =
+                    __builtin_convertvector(v, f16x4);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float es = p.scale * sm.eg[b][16 * m + c];
+            O[0][m] *= es;
+            O[1][m] *= es;
+        }
+        __syncthreads();   // (2)
+        // O^T += V'^T P^T (P causal: token tiles 0 and 1 need k step 0 only)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f16x8 vb[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n) vb[n] = *reinterpret_cast<const f16x8*>(sm.vx[cw] + ((2 * j + n) * 64 + lane) * 8);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (j == 1 && m < 2) continue;
+                const f16x8 pf = *reinterpret_cast<const f16x8*>(sm.p + (16 * m + c) * LP + 32 * j + 8 * g);
+#pragma unroll
+                for (int n = 0; n < 2; ++n) O[n][m] = mmh(vb[n], pf, O[n][m]);
+            }
+        }
+        // lane (g, c) of tile (n, m): token 16 m + c, d_v 32 cw + 16 n + 4 g + (0..3)
+        // (rows past the sequence's end fall outside the descriptor: dropped)
+        const auto ro = rsrc(static_cast<bf16*>(p.out) + (loc.tok0 + (size_t)cc * CH) * tsv + (size_t)h * DK,
+                             (unsigned)min(CH, loc.len - cc * CH) * (unsigned)tsv * 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_rne(O[n][m][0], O[n][m][1]), pack_rne(O[n][m][2], O[n][m][3])},
+                                                      ro, (int)(((16 * m + c) * tsv + 32 * cw + 16 * n + 4 * g) * 2), 0, 0);
+        ws_stage(sm, in, b ^ 1, ot);
+        fetch(cc + 2);
+        __syncthreads();   // (3)
+    };
+    int cc = c_lo;
+    for (; cc + 1 < c_hi; cc += 2) {
+        step(0, cc);
+        step(1, cc + 1);
+    }
+    if (cc < c_hi) step(0, cc);
+}
+
+__global__ __launch_bounds__(NT8) void k_fwd_ws(Params p) {
+    __shared__ SmemWS sm;
+    const int h = blockIdx.y, w = wave_id();
+    const SegLoc loc = locate_segment(p, blockIdx.x);
+    if (loc.seq < 0) return;
+    const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
+    if (w < 4) {
+        const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+        f32x4 S[8][2];
+        const float* src = loc.s == 0 ? p.s_init : p.seg_state;
+        if (loc.s == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[i][n][e] = src ? src[tiles_off(loc.seq, p.h_v, h) + (16 * i + 4 * g + e) * DK + 32 * w + 16 * n + c] : 0.f;
+        } else {
+            const float* sg = src + tiles_off(loc.seg_base + loc.s, p.h_v, h);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    S[i][n] = *reinterpret_cast<const f32x4*>(sg + ((i * 8 + 2 * w + n) * 64 + lane) * 4);
+        }
+        if (c0 < c1) ws_chain(sm, p, loc, h, c0, c1, w, S);
+        if (loc.s == loc.P - 1 && p.s_final) {
+            float* dst = p.s_final + tiles_off(loc.seq, p.h_v, h);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[(16 * i + 4 * g + e) * DK + 32 * w + 16 * n + c] = S[i][n][e];
+        }
+    } else if (c0 < c1) {
+        ws_output(sm, p, loc, h, c0, c1, w - 4);
+    }
 }
 
 // Boundary states in tile order -> row-major (debug copies).
@@ -679,14 +1116,14 @@ int launch_cp_prep16(const Params& p, int io, void* stream) {
 }
 
 int launch_combine16(const Params& p, void* stream) {
-    const dim3 grid((unsigned)(8 * p.n_seqs), (unsigned)p.h_v), block(64);
+    const dim3 grid((unsigned)(8 * p.n_seqs), (unsigned)p.h_v), block(NTC);
     hipLaunchKernelGGL(k_combine16, grid, block, 0, (hipStream_t)stream, p);
     return launched16();
 }
 
 int launch_fwd16(const Params& p, int io, void* stream) {
     const dim3 grid((unsigned)p.n_segments, (unsigned)p.h_v), block(NT8);
-    if (io == kIoBf16) hipLaunchKernelGGL(k_fwd16<bf16>, grid, block, 0, (hipStream_t)stream, p);
+    if (io == kIoBf16) hipLaunchKernelGGL(k_fwd_ws, grid, block, 0, (hipStream_t)stream, p);
     else hipLaunchKernelGGL(k_fwd16<float>, grid, block, 0, (hipStream_t)stream, p);
     return launched16();
 }
