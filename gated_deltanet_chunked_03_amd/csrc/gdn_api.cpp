@@ -220,13 +220,14 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
     {
         // The forward: an 8 KiB scratch line (stores of rows past a sequence's
         // end land there), T diag(beta) as fp16 operand images (6 KiB per chunk
-        // and value head); with a split, the boundary states and H maps (fp32,
+        // and value head) and the chunk's gate factors (1 KiB); with a split, the boundary states and H maps (fp32,
         // 64 KiB, in the chain kernels' tile order), the M maps as the combine's
         // fp16 A operands (32 KiB) and the boundary flags.
         FwdLayout& F = P.fw;
         size_t off = 0;
         if (P.n_chunks_total > 0) { F.off_sink = off; off += 8192; }
-        F.off_T = off; off = align_up(off + nch * gdn::kTbHalfs * 2, 256);
+        F.off_T = off;  off = align_up(off + nch * gdn::kTbHalfs * 2, 256);
+        F.off_GB = off; off = align_up(off + nch * gdn::kGfFloats * sizeof(float), 256);
         if (P.cp_on) {
             F.off_state = off; off = align_up(off + st_bytes, 256);
             F.off_H = off;     off = align_up(off + st_bytes, 256);
@@ -366,7 +367,10 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
     p.out = out; p.s_final = s_final; p.scale = scale;
     char* w8 = static_cast<char*>(ws);
     set_layout(p, P.fw, P, w8);
-    if (P.n_chunks_total > 0) p.tb16 = w8 + P.fw.off_T;
+    if (P.n_chunks_total > 0) {
+        p.tb16 = w8 + P.fw.off_T;
+        p.gf16 = reinterpret_cast<float*>(w8 + P.fw.off_GB);
+    }
     const int io = d->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
     const hipStream_t hs = (hipStream_t)stream;
     int e;

@@ -708,45 +708,47 @@ __global__ __launch_bounds__(NT8) void k_fwd16(Params p) {
 }
 
 // ----------------------------------------------------------------------------
-// The fused forward with specialised waves (bf16 inputs). The chunk step's
-// dependent chain is S -> K S -> Y -> V' -> S; the output (Q S, P, P V'),
-// the stores and the staging of the next chunk hang off it. Waves 0-3
-// (chain) own the d_v columns [32 w, 32 w + 32) of S in registers and run
-// only the chain; waves 4-7 (output) each sit beside one chain wave on its
-// SIMD and do the rest for the same 32 columns, reading the state and V' as
-// fp16 operands that the chain wave leaves in LDS. Per chunk:
-//   chain:  Y = K S, Y = V - e^gamma Y (V through the identity product,
-//           its rows loaded a chunk and a half ahead), V' = T diag(beta) Y,
-//           V' -> LDS
-//   output: O^T = S^T Q^T (S from LDS), its row block of P, scale
+// The fused forward with specialised waves (bf16 inputs). Waves 0-3 (state
+// waves) own the d_v columns [32 w, 32 w + 32) of S in registers and produce
+// the same columns of the output; waves 4-7 (staging waves) compute P and
+// stage every operand, one per SIMD beside a state wave. Per chunk n:
+//   state:   O^T = S^T Q^T and Y = K S from the state's fp16 copy,
+//            S <- e^gamma_C S, Y = V - e^gamma Y (V through the identity
+//            product, its rows loaded a chunk and a half ahead),
+//            V' = T diag(beta) Y, O^T scaled by scale e^gamma
+//   staging: the next chunk's gate factors; its row block of P
 //   -- barrier --
-//   chain:  S = e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V', S -> LDS
-//   output: O^T += V'^T P^T, stores, stage the next chunk (K, Q, T diag(beta)
-//           single-buffered: their readers are past the first barrier; K^T and
-//           the gate factors double-buffered)
+//   state:   O^T += V'^T P^T, stores; S += K~^T V' with
+//            K~ = diag(e^(gamma_C - gamma)) K (staged scaled)
+//   staging: the next chunk's K, K~^T, Q and T diag(beta); loads for the
+//            one after
 //   -- barrier --
-// so the matrix-core work of the output half overlaps the chain's VALU work
-// and the other way round.
-struct __attribute__((aligned(16))) SmemWS {
-    f16 k[CH * LQ];                       // K token-major, d_k in kp order
-    f16 q[CH * LQ];                       // Q token-major, d_k in kp order
-    f16 kt[2][DK * LT];                   // K^T: row d_k, tokens in kp order, 16-byte pieces XOR tswz(row)
-    f16 tb[kTbHalfs];                     // T diag(beta) fragments (k_prep's image)
-    f16 p[CH * LP];                       // P: row r, columns i in kp order
-    f16 sx[4][8 * 64 * 8];                // per column block: the state's fp16 operands [k step][tile][lane]
-    f16 vx[4][4 * 64 * 8];                // per column block: V' as fp16 operands [k step][tile][lane]
-    float gam[2][CH];                     // gamma log2(e)
-    float eg[2][CH];                      // e^gamma
-    float egc[2][CH];                     // e^(gamma_C - gamma)
-    float ec[2][4];                       // e^gamma_C
-};
+// The state and V' stay in the state waves' registers: LDS carries only
+// the staged inputs and P. K~^T and the gate factors are double-buffered;
+// K, Q and T diag(beta) single (their readers are past the first barrier
+// when they are restaged). The gate factors come from k_prep, per chunk and
+// head.
+//
+// LDS layouts (row strides chosen by measurement: each operand read and
+// staging write runs at the LDS's full rate):
+//   K, Q   [64 tokens][128 d_k in kp order, + 16]
+//   K~^T   [128 d_k][64 tokens in kp order, + 16], 16-byte pieces of row d
+//          at piece ^ tswz(d)
+//   P      [64 rows][64 columns in kp order, + 8]
+constexpr int kWsRow = 144;                                   // halfs per K / Q row
+constexpr int kWsRowT = 80;                                   // halfs per K~^T row
+constexpr int kWsRowP = 72;                                   // halfs per P row
+__device__ __forceinline__ int kq_at(int r, int piece) { return r * kWsRow + 8 * piece; }
+__device__ __forceinline__ int kt_at(int d, int piece) { return d * kWsRowT + ((8 * piece) ^ tswz(d)); }
+__device__ __forceinline__ int p_at(int r, int piece) { return r * kWsRowP + 8 * piece; }
 
-// The output waves' staging loads: thread t (0..255) holds tokens
-// 4 (t / 16) + j, d_k 8 (t % 16) .. + 8 of K and Q, pieces t and t + 256
-// (< 384) of the T diag(beta) image, and the gate of token `lane`.
-struct InWS {
-    u32x4 k[4], q[4], tb[2];
-    float g;
+struct __attribute__((aligned(16))) SmemWS {
+    f16 k[CH * kWsRow];                   // K
+    f16 q[CH * kWsRow];                   // Q
+    f16 kt[2][DK * kWsRowT];              // K~^T
+    f16 tb[kTbHalfs];                     // T diag(beta) fragments (k_prep's image)
+    f16 p[CH * kWsRowP];                  // P
+    float gf[2][kGfFloats];               // gamma log2(e), e^gamma, e^(gamma_C - gamma), e^gamma_C
 };
 
 __device__ __forceinline__ f16x8 to_h8(const u32x4& x) {
@@ -757,75 +759,37 @@ __device__ __forceinline__ f16x8 to_h8(const u32x4& x) {
         f16x8);
 }
 
-// Chunk c's loads of the output waves (ot = thread index among them).
-__device__ __forceinline__ void ws_fetch(InWS& r, const Params& p, size_t tok0, int nvalid, int h, int hq, int slot,
-                                         int ot) {
-    const unsigned nv = (unsigned)nvalid;
-    const size_t ts = (size_t)p.h_qk * DK;
-    r.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                        rsrc(p.g + tok0 * p.h_v + h, nv * p.h_v * 4), (int)((ot & 63) * p.h_v * 4), 0, 0));
-    const auto rk = rsrc(static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK, nv * (unsigned)ts * 2);
-    const auto rq = rsrc(static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK, nv * (unsigned)ts * 2);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int o = (int)(((4 * (ot >> 4) + j) * ts + 8 * (ot & 15)) * 2);
-        r.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
-        r.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
-    }
-    const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const f16*>(p.tb16) +
-                                                     ((size_t)slot * p.h_v + h) * (size_t)kTbHalfs);
-    r.tb[0] = tb[ot];
-    r.tb[1] = tb[ot < 128 ? 256 + ot : ot];   // (pieces 256..383; the rest load piece ot again)
+// Staging map of thread t < 256 of the staging waves: tokens 4 (t / 16) + j
+// (j < 4), d_k 8 (t % 16) .. + 8; in kp order the d_k are the positions
+// ws_p0(t) .. + 4 and ws_p0(t) + 8 .. + 12, the tokens ws_pt(t) .. + 4.
+__device__ __forceinline__ int ws_p0(int t) { return 32 * ((t & 15) >> 2) + 16 * (t & 1) + 4 * ((t >> 1) & 1); }
+__device__ __forceinline__ int ws_pt(int t) {
+    const int rq = (t >> 4) & 15;
+    return 32 * (rq >> 3) + 8 * (rq & 3) + 4 * ((rq >> 2) & 1);
 }
-
-// Stages a fetched chunk (K^T and gate factors into buffer b).
-__device__ __forceinline__ void ws_stage(SmemWS& sm, const InWS& r, int b, int ot) {
-    const int lane = ot & 63, cq = ot & 15, rq = ot >> 4;
-    if (ot < 64) {   // the first output wave: the gate factors
-        const float gam = wave_scan(r.g);
-        const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
-        sm.gam[b][lane] = gam * kLog2e;
-        sm.eg[b][lane] = __expf(gam);
-        sm.egc[b][lane] = __expf(gc - gam);
-        if (lane == 0) sm.ec[b][0] = __expf(gc);
-    }
-    // d_k 8 cq .. + 8 -> kp positions p0 .. p0 + 3 and p0 + 8 .. p0 + 11; tokens
-    // 4 rq .. + 3 -> kp positions pt .. pt + 3
-    const int p0 = 32 * (cq >> 2) + 16 * (cq & 1) + 4 * ((cq >> 1) & 1);
-    const int pt = 32 * (rq >> 3) + 8 * (rq & 3) + 4 * ((rq >> 2) & 1);
-    f16x8 kr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        kr[j] = to_h8(r.k[j]);
-        f16* dk = sm.k + (4 * rq + j) * LQ;
-        *reinterpret_cast<f16x4*>(dk + p0) = f16x4{kr[j][0], kr[j][1], kr[j][2], kr[j][3]};
-        *reinterpret_cast<f16x4*>(dk + p0 + 8) = f16x4{kr[j][4], kr[j][5], kr[j][6], kr[j][7]};
-        const f16x8 qr = to_h8(r.q[j]);
-        f16* dq = sm.q + (4 * rq + j) * LQ;
-        *reinterpret_cast<f16x4*>(dq + p0) = f16x4{qr[0], qr[1], qr[2], qr[3]};
-        *reinterpret_cast<f16x4*>(dq + p0 + 8) = f16x4{qr[4], qr[5], qr[6], qr[7]};
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int d = 8 * cq + e;
-        *reinterpret_cast<f16x4*>(sm.kt[b] + d * LT + (pt ^ tswz(d))) = f16x4{kr[0][e], kr[1][e], kr[2][e], kr[3][e]};
-    }
-    *reinterpret_cast<u32x4*>(sm.tb + 8 * ot) = r.tb[0];
-    if (ot < 128) *reinterpret_cast<u32x4*>(sm.tb + 8 * (256 + ot)) = r.tb[1];
-}
-
-// The state (tiles [i][n], rows 16 i + 4 g + e, column 32 cw + 16 n + c) as the
-// fp16 operands of k step j, written for the output wave of the same columns.
-__device__ __forceinline__ void ws_put_state(SmemWS& sm, int cw, const f16x8 Sb[4][2]) {
-    const int lane = lane_id();
+// rows of one chunk's [tokens][heads][128] bf16 input in the staging map
+// (rows past the sequence's end read as zeros)
+__device__ __forceinline__ void ws_load_rows(u32x4 (&x)[4], const void* base, size_t tok0, size_t ts, int hd,
+                                             int nvalid, int t) {
+    const auto r = rsrc(static_cast<const bf16*>(base) + tok0 * ts + (size_t)hd * DK, (unsigned)nvalid * (unsigned)ts * 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
+        x[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(((4 * ((t >> 4) & 15) + j) * ts + 8 * (t & 15)) * 2), 0, 0);
+}
+__device__ __forceinline__ void ws_put_rows(f16* dst, const u32x4 (&x)[4], int t) {
+    const int p0 = ws_p0(t), r0 = 4 * ((t >> 4) & 15);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) *reinterpret_cast<f16x8*>(sm.sx[cw] + ((2 * j + n) * 64 + lane) * 8) = Sb[j][n];
+    for (int j = 0; j < 4; ++j) {
+        const f16x8 h = to_h8(x[j]);
+        f16* d = dst + (r0 + j) * kWsRow;
+        *reinterpret_cast<f16x4*>(d + p0) = f16x4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<f16x4*>(d + p0 + 8) = f16x4{h[4], h[5], h[6], h[7]};
+    }
 }
 
-// Chain wave cw over chunks [c_lo, c_hi): S[8][2] in registers.
-__device__ void ws_chain(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw,
+// State wave cw over chunks [c_lo, c_hi): S[8][2] (tiles [i][n], rows
+// 16 i + 4 g + e, column 32 cw + 16 n + c) in registers.
+__device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw,
                          f32x4 S[8][2]) {
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
     const size_t tsv = (size_t)p.h_v * DK;
@@ -843,189 +807,101 @@ __device__ void ws_chain(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) E[n][s] = (bf16)((8 * g + s == 16 * n + c) ? 1.f : 0.f);
-    f16x8 Sb[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) Sb[j][n] = pack8h(S[2 * j][n], S[2 * j + 1][n]);
-    ws_put_state(sm, cw, Sb);
+        for (int s2 = 0; s2 < 8; ++s2) E[n][s2] = (bf16)((8 * g + s2 == 16 * n + c) ? 1.f : 0.f);
     u32x4 VA[4], VB[4];
     vfetch(VA, c_lo);
     vfetch(VB, c_lo + 1);
-    __syncthreads();   // (1) the first chunk staged, the state written
-    auto step = [&](int b, const u32x4 (&V)[4]) {
-        // Y = K S
-        f32x4 Y[4][2];
+    __syncthreads();   // (0) the first chunk's gate factors staged
+    __syncthreads();   // (1) the first chunk staged
+    auto step = [&](int b, const u32x4 (&V)[4], int cc) {
+        const float* gf = sm.gf[b];
+        // O^T = S^T Q^T and Y = K S from the state's fp16 copy
+        f32x4 O[2][4], Y[4][2];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int n = 0; n < 2; ++n) Y[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < 2; ++n) O[n][m] = Y[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            f16x8 kf[4];
+            f16x8 sb[2], kf[4], qf[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) kf[m] = *reinterpret_cast<const f16x8*>(sm.k + (16 * m + c) * LQ + 32 * j + 8 * g);
+            for (int n = 0; n < 2; ++n) sb[n] = pack8h(S[2 * j][n], S[2 * j + 1][n]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                kf[m] = *reinterpret_cast<const f16x8*>(sm.k + kq_at(16 * m + c, 4 * j + g));
+                qf[m] = *reinterpret_cast<const f16x8*>(sm.q + kq_at(16 * m + c, 4 * j + g));
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int n = 0; n < 2; ++n) Y[m][n] = mmh(kf[m], Sb[j][n], Y[m][n]);
-        }
-        // Y = V - e^gamma (K S)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f32x4 eg = *reinterpret_cast<const f32x4*>(sm.eg[b] + 16 * m + 4 * g);
-#pragma unroll
-            for (int n = 0; n < 2; ++n) Y[m][n] = mma16k32(__builtin_bit_cast(bf16x8, V[m]), E[n], Y[m][n] * -eg);
-        }
-        // V' = (T diag(beta)) Y
-        f32x4 Vp[4][2];
-        {
-            f16x8 Yb[2][2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int n = 0; n < 2; ++n) Yb[j][n] = pack8h(Y[2 * j][n], Y[2 * j + 1][n]);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const f16x8 t0 = *reinterpret_cast<const f16x8*>(sm.tb + (tb_frag(m, 0) * 64 + lane) * 8);
-#pragma unroll
-                for (int n = 0; n < 2; ++n) Vp[m][n] = mmh(t0, Yb[0][n], f32x4{0.f, 0.f, 0.f, 0.f});
-                if (m >= 2) {
-                    const f16x8 t1 = *reinterpret_cast<const f16x8*>(sm.tb + (tb_frag(m, 1) * 64 + lane) * 8);
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) Vp[m][n] = mmh(t1, Yb[1][n], Vp[m][n]);
+                for (int n = 0; n < 2; ++n) {
+                    Y[m][n] = mmh(kf[m], sb[n], Y[m][n]);
+                    O[n][m] = mmh(sb[n], qf[m], O[n][m]);
                 }
-            }
+            __builtin_amdgcn_sched_barrier(0);   // (bounds the operand reads in flight)
         }
-        // V' for the output wave
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                *reinterpret_cast<f16x8*>(sm.vx[cw] + ((2 * j + n) * 64 + lane) * 8) = pack8h(Vp[2 * j][n], Vp[2 * j + 1][n]);
-        __syncthreads();   // (2) P and V' complete; the readers of K, Q, T diag(beta) are past
-        // S <- e^gamma_C S + K^T diag(e^(gamma_C - gamma)) V'
-        f16x8 Vb[2][2];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f32x4 f = *reinterpret_cast<const f32x4*>(sm.egc[b] + 16 * m + 4 * g);
-#pragma unroll
-            for (int n = 0; n < 2; ++n) Vp[m][n] *= f;
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) Vb[j][n] = pack8h(Vp[2 * j][n], Vp[2 * j + 1][n]);
-        const float ec = sm.ec[b][0];
+        // the decay of this chunk's state update, ahead of it
+        const float ec = gf[3 * CH];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int n = 0; n < 2; ++n) S[i][n] *= ec;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f16x8 ktf[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                ktf[i] = *reinterpret_cast<const f16x8*>(sm.kt[b] + (16 * i + c) * LT + ((32 * j + 8 * g) ^ tswz(16 * i)));
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int n = 0; n < 2; ++n) S[i][n] = mmh(ktf[i], Vb[j][n], S[i][n]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) Sb[j][n] = pack8h(S[2 * j][n], S[2 * j + 1][n]);
-        ws_put_state(sm, cw, Sb);
-        __syncthreads();   // (3) the next chunk staged, the new state written
-    };
-    int cc = c_lo;
-    for (; cc + 1 < c_hi; cc += 2) {
-        step(0, VA);
-        vfetch(VA, cc + 2);
-        step(1, VB);
-        vfetch(VB, cc + 3);
-    }
-    if (cc < c_hi) step(0, VA);
-}
-
-// Output wave for column block cw over chunks [c_lo, c_hi); ot = 64 cw + lane.
-__device__ void ws_output(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw) {
-    const int lane = lane_id(), c = lane & 15, g = lane >> 4, ot = 64 * cw + lane;
-    const int hq = h / p.group;
-    const size_t tsv = (size_t)p.h_v * DK;
-    const float log2_scale = __log2f(p.scale);
-    InWS in;
-    auto fetch = [&](int cc) {
-        cc = min(cc, c_hi - 1);
-        ws_fetch(in, p, loc.tok0 + (size_t)cc * CH, min(CH, loc.len - cc * CH), h, hq, loc.chunk_base + cc, ot);
-    };
-    fetch(c_lo);
-    ws_stage(sm, in, 0, ot);
-    fetch(c_lo + 1);
-    __syncthreads();   // (1)
-    auto step = [&](int b, int cc) {
-        // O^T = S^T Q^T (this block's 32 columns; S from the chain wave) and P's
-        // row block [16 cw, 16 cw + 16): P^T tiles k_i . q_r, i block ib
-        f32x4 O[2][4], Pt[4];
+        // Y = V - e^gamma (K S)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            O[0][m] = O[1][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Pt[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(gf + CH + 16 * m + 4 * g);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) Y[m][n] = mma16k32(__builtin_bit_cast(bf16x8, V[m]), E[n], Y[m][n] * -eg);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f16x8 qf[4], kf[4], sb[2];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                qf[m] = *reinterpret_cast<const f16x8*>(sm.q + (16 * m + c) * LQ + 32 * j + 8 * g);
-                kf[m] = *reinterpret_cast<const f16x8*>(sm.k + (16 * m + c) * LQ + 32 * j + 8 * g);
-            }
-            const f16x8 qw = *reinterpret_cast<const f16x8*>(sm.q + (16 * cw + c) * LQ + 32 * j + 8 * g);
-#pragma unroll
-            for (int n = 0; n < 2; ++n) sb[n] = *reinterpret_cast<const f16x8*>(sm.sx[cw] + ((2 * j + n) * 64 + lane) * 8);
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) O[n][m] = mmh(sb[n], qf[m], O[n][m]);
-#pragma unroll
-            for (int ib = 0; ib < 4; ++ib) Pt[ib] = mmh(kf[ib], qw, Pt[ib]);
-        }
+        // V' = (T diag(beta)) Y
+        f16x8 Vb[2][2];
         {
-            const int r = 16 * cw + c;
-            const float gr = sm.gam[b][r] + log2_scale;
+            f16x8 Yb[2][2], tf[6];
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                const int i0 = 16 * ib + 4 * g;
-                const f32x4 gi = *reinterpret_cast<const f32x4*>(sm.gam[b] + i0);
-                f32x4 v;
+            for (int f = 0; f < 6; ++f) tf[f] = *reinterpret_cast<const f16x8*>(sm.tb + (f * 64 + lane) * 8);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (i0 + e <= r) ? __builtin_amdgcn_exp2f(gr - gi[e]) * Pt[ib][e] : 0.f;
-                *reinterpret_cast<f16x4*>(sm.p + r * LP + 32 * (ib >> 1) + 8 * g + 4 * (ib & 1)) =
-                    __builtin_convertvector(v, f16x4);
-            }
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) Yb[j][n] = pack8h(Y[2 * j][n], Y[2 * j + 1][n]);
+            f32x4 Vp[4][2];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    Vp[m][n] = mmh(tf[tb_frag(m, 0)], Yb[0][n], f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (m >= 2) Vp[m][n] = mmh(tf[tb_frag(m, 1)], Yb[1][n], Vp[m][n]);
+                }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) Vb[j][n] = pack8h(Vp[2 * j][n], Vp[2 * j + 1][n]);
         }
+        // O^T scaled per token by scale e^gamma
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const float es = p.scale * sm.eg[b][16 * m + c];
+            const float es = p.scale * gf[CH + 16 * m + c];
             O[0][m] *= es;
             O[1][m] *= es;
         }
-        __syncthreads();   // (2)
+        __syncthreads();   // (2) P complete; the readers of K, Q and T diag(beta) are past
         // O^T += V'^T P^T (P causal: token tiles 0 and 1 need k step 0 only)
+        {
+            f16x8 pf[6];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f16x8 vb[2];
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int n = 0; n < 2; ++n) vb[n] = *reinterpret_cast<const f16x8*>(sm.vx[cw] + ((2 * j + n) * 64 + lane) * 8);
+                for (int j = 0; j < 2; ++j) {
+                    if (j == 1 && m < 2) continue;
+                    pf[tb_frag(m, j)] = *reinterpret_cast<const f16x8*>(sm.p + p_at(16 * m + c, 4 * j + g));
+                }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (j == 1 && m < 2) continue;
-                const f16x8 pf = *reinterpret_cast<const f16x8*>(sm.p + (16 * m + c) * LP + 32 * j + 8 * g);
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int n = 0; n < 2; ++n) O[n][m] = mmh(vb[n], pf, O[n][m]);
-            }
+                for (int j = 0; j < 2; ++j) {
+                    if (j == 1 && m < 2) continue;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) O[n][m] = mmh(Vb[j][n], pf[tb_frag(m, j)], O[n][m]);
+                }
         }
         // lane (g, c) of tile (n, m): token 16 m + c, d_v 32 cw + 16 n + 4 g + (0..3)
         // (rows past the sequence's end fall outside the descriptor: dropped)
@@ -1037,8 +913,123 @@ __device__ void ws_output(SmemWS& sm, const Params& p, const SegLoc& loc, int h,
             for (int n = 0; n < 2; ++n)
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_rne(O[n][m][0], O[n][m][1]), pack_rne(O[n][m][2], O[n][m][3])},
                                                       ro, (int)(((16 * m + c) * tsv + 32 * cw + 16 * n + 4 * g) * 2), 0, 0);
-        ws_stage(sm, in, b ^ 1, ot);
+        // S += K~^T V'
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f16x8 ktf[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ktf[i] = *reinterpret_cast<const f16x8*>(sm.kt[b] + kt_at(16 * i + c, 4 * j + g));
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) S[i][n] = mmh(ktf[i], Vb[j][n], S[i][n]);
+        }
+        __syncthreads();   // (3) the next chunk staged
+    };
+    int cc = c_lo;
+    for (; cc + 1 < c_hi; cc += 2) {
+        step(0, VA, cc);
+        vfetch(VA, cc + 2);
+        step(1, VB, cc + 1);
+        vfetch(VB, cc + 3);
+    }
+    if (cc < c_hi) step(0, VA, cc);
+}
+
+// Staging wave cw over chunks [c_lo, c_hi) (threads t = 64 cw + lane): P's
+// row block [16 cw, 16 cw + 16) and the staging of every operand.
+__device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw) {
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4, t = 64 * cw + lane;
+    const int hq = h / p.group;
+    const size_t ts = (size_t)p.h_qk * DK;
+    const float log2_scale = __log2f(p.scale);
+    u32x4 kr[4], qr[4], tbr[2];
+    auto fetch = [&](int cc) {
+        cc = min(cc, c_hi - 1);
+        const size_t tok0 = loc.tok0 + (size_t)cc * CH;
+        const int nv = min(CH, loc.len - cc * CH);
+        ws_load_rows(kr, p.k, tok0, ts, hq, nv, t);
+        ws_load_rows(qr, p.q, tok0, ts, hq, nv, t);
+        const size_t blk = (size_t)(loc.chunk_base + cc) * p.h_v + h;
+        const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const f16*>(p.tb16) + blk * (size_t)kTbHalfs);
+        tbr[0] = tb[t];
+        tbr[1] = tb[t < 128 ? 256 + t : t];   // (pieces 256..383; the rest load piece t again)
+    };
+    // gate factors, loaded two chunks ahead of their staging
+    auto gfetch = [&](int cc) {
+        cc = min(cc, c_hi - 1);
+        return p.gf16[((size_t)(loc.chunk_base + cc) * p.h_v + h) * kGfFloats + t];
+    };
+    // K, K~^T (into kt[b], from the gate factors in gf[b]), Q and T diag(beta)
+    auto stage = [&](int b) {
+        // (the factors are read ahead of the writes: an LDS read waits for
+        // every LDS access issued before it)
+        const f32x4 kfac = *reinterpret_cast<const f32x4*>(sm.gf[b] + 2 * CH + 4 * ((t >> 4) & 15));
+        __builtin_amdgcn_sched_barrier(0);
+        ws_put_rows(sm.k, kr, t);
+        ws_put_rows(sm.q, qr, t);
+        *reinterpret_cast<u32x4*>(sm.tb + 8 * t) = tbr[0];
+        if (t < 128) *reinterpret_cast<u32x4*>(sm.tb + 8 * (256 + t)) = tbr[1];
+        const int pt = ws_pt(t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = 8 * (t & 15) + e;
+            f32x4 col;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned wv = kr[j][e >> 1];
+                col[j] = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16)) * kfac[j];
+            }
+            *reinterpret_cast<f16x4*>(sm.kt[b] + d * kWsRowT + (pt ^ tswz(d))) = __builtin_convertvector(col, f16x4);
+        }
+    };
+    // (loads issue in the loop's order: operands, then gate factors)
+    float gfr[2];
+    sm.gf[0][t] = gfetch(c_lo);
+    gfr[1] = gfetch(c_lo + 1);
+    fetch(c_lo);
+    __syncthreads();   // (0)
+    stage(0);
+    fetch(c_lo + 1);
+    gfr[0] = gfetch(c_lo + 2);
+    __syncthreads();   // (1)
+    auto step = [&](int b, int cc) {
+        const float* gf = sm.gf[b];
+        // the next chunk's gate factors (their buffer's last readers passed
+        // the previous step's end)
+        sm.gf[b ^ 1][t] = gfr[b ^ 1];
+        // P's row block: P^T tiles k_i . q_r, i block ib
+        f32x4 Pt[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Pt[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f16x8 kf[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) kf[m] = *reinterpret_cast<const f16x8*>(sm.k + kq_at(16 * m + c, 4 * j + g));
+            const f16x8 qw = *reinterpret_cast<const f16x8*>(sm.q + kq_at(16 * cw + c, 4 * j + g));
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) Pt[ib] = mmh(kf[ib], qw, Pt[ib]);
+        }
+        {
+            // P[r][i] = scale 2^(gamma_r - gamma_i) (q_r . k_i), i <= r (gamma times log2 e)
+            const int r = 16 * cw + c;
+            const float gr = gf[r] + log2_scale;
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                const int i0 = 16 * ib + 4 * g;
+                const f32x4 gi = *reinterpret_cast<const f32x4*>(gf + i0);
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (i0 + e <= r) ? __builtin_amdgcn_exp2f(gr - gi[e]) * Pt[ib][e] : 0.f;
+                *reinterpret_cast<f16x4*>(sm.p + p_at(r, 4 * (ib >> 1) + g) + 4 * (ib & 1)) =
+                    __builtin_convertvector(v, f16x4);
+            }
+        }
+        __syncthreads();   // (2)
+        stage(b ^ 1);
         fetch(cc + 2);
+        gfr[b ^ 1] = gfetch(cc + 3);
         __syncthreads();   // (3)
     };
     int cc = c_lo;
@@ -1075,7 +1066,7 @@ __global__ __launch_bounds__(NT8) void k_fwd_ws(Params p) {
                 for (int n = 0; n < 2; ++n)
                     S[i][n] = *reinterpret_cast<const f32x4*>(sg + ((i * 8 + 2 * w + n) * 64 + lane) * 4);
         }
-        if (c0 < c1) ws_chain(sm, p, loc, h, c0, c1, w, S);
+        if (c0 < c1) ws_state(sm, p, loc, h, c0, c1, w, S);
         if (loc.s == loc.P - 1 && p.s_final) {
             float* dst = p.s_final + tiles_off(loc.seq, p.h_v, h);
 #pragma unroll
@@ -1086,7 +1077,7 @@ __global__ __launch_bounds__(NT8) void k_fwd_ws(Params p) {
                     for (int e = 0; e < 4; ++e) dst[(16 * i + 4 * g + e) * DK + 32 * w + 16 * n + c] = S[i][n][e];
         }
     } else if (c0 < c1) {
-        ws_output(sm, p, loc, h, c0, c1, w - 4);
+        ws_stage(sm, p, loc, h, c0, c1, w - 4);
     }
 }
 

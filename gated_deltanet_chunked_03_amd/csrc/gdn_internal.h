@@ -10,6 +10,7 @@ constexpr int kChunk = 64;   // tokens per chunk
 constexpr int kDim = 128;    // d_k == d_v
 constexpr int kMaxSegsPerSeq = 2048;  // the combine kernel keeps one flag per segment in LDS
 constexpr int kTbHalfs = 6 * 64 * 8;  // fp16 per (chunk, value head) in the T diag(beta) image (6 KiB)
+constexpr int kGfFloats = 4 * 64;     // fp32 per (chunk, value head): gate factors of the chain kernels
 
 struct Params {
     // inputs
@@ -40,6 +41,8 @@ struct Params {
     float* sink;              // 8 KiB scratch line for stores of rows past a sequence's end
     void* tb16;               // [n_chunks][h_v] fp16 images of T diag(beta) (kTbHalfs each), or null:
                               //   k_prep then writes the split T and gamma, beta (prep_T, prep_GB)
+    float* gf16;              // with tb16: [n_chunks][h_v][4][64] gamma log2(e), e^gamma,
+                              //   e^(gamma_C - gamma), e^gamma_C (all 64 the same)
     float* chunk_states;      // [n_chunks][h_v][128][128] state entering each chunk (backward recompute)
     float* bwd_y;             // with chunk_states: per (chunk, head) [64][128] fp32 Y = V - diag(e^gamma) K S,
     float* bwd_vp;            //   and V'; and per (chunk, head) [8 waves][64] partial sums over d_v of

@@ -362,6 +362,15 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
                 float* gb = p.prep_GB + ((size_t)slot_cur * p.h_v + h_cur) * (size_t)p.gb_stride;
                 gb[lane] = gam;
                 gb[CH + lane] = bt;
+            } else {
+                // the chain kernels' gate factors: gamma log2(e), e^gamma,
+                // e^(gamma_C - gamma), e^gamma_C (padding tokens carry g = 0)
+                const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam), 63));
+                float* gf = p.gf16 + ((size_t)slot_cur * p.h_v + h_cur) * (size_t)kGfFloats;
+                gf[lane] = gam * 1.4426950408889634f;
+                gf[CH + lane] = __expf(gam);
+                gf[2 * CH + lane] = __expf(gc - gam);
+                gf[3 * CH + lane] = __expf(gc);
             }
         }
         // always a prefetch (the last item fetches itself again), so that every

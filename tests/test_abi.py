@@ -104,8 +104,9 @@ def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
     assert p["P_max"] == -(-N // L) and p["n_segments"] == B_ * p["P_max"]
     assert p["cp_on"] == int(p["P_max"] > 1)
     per_seg = h_v * 128 * 128 * 4
-    # the scratch line, then T diag(beta) as fp16 operand images (6 KiB per chunk and value head)
-    prep = 8192 + p["n_chunks_total"] * h_v * 6 * 64 * 8 * 2
+    # the scratch line, then T diag(beta) as fp16 operand images (6 KiB per chunk and value
+    # head) and the chunk's gate factors (4 x 64 fp32)
+    prep = 8192 + p["n_chunks_total"] * h_v * (6 * 64 * 8 * 2 + 4 * 64 * 4)
     if p["cp_on"]:
         flags = -(-(p["n_segments"] * h_v * 4) // 256) * 256
         # boundary states and H maps (fp32), M maps (fp16 images), boundary flags
