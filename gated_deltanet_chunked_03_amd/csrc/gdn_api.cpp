@@ -310,8 +310,8 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
     p.log_eps = std::log(P.eps);
     p.t_stride = (int64_t)gdn::kChunk * gdn::kChunk;
     p.gb_stride = 2 * gdn::kChunk;
-    // (head, chunk) items per k_prep workgroup (one wave): one round of eight
-    // workgroups per CU (at most 32 items each; larger inputs take more rounds)
+    // (head, chunk) items per k_prep wave: one round of eight waves (one
+    // workgroup) per CU (at most 32 items each; larger inputs take more rounds)
     const long long items = (long long)P.n_chunks_total * d->h_v, slots = 8LL * std::max(P.n_cu, 1);
     p.prep_cpw = (int)std::min<long long>(std::max<long long>((items + slots - 1) / slots, 1), 32);
     return p;

@@ -37,7 +37,7 @@ struct Params {
     int64_t t_stride;         // floats between consecutive T blocks (>= 64 * 64)
     float* prep_GB;           // [n_chunks][h_v] blocks of gb_stride floats: gamma (64), beta (64)
     int64_t gb_stride;        // floats between consecutive gamma/beta blocks (>= 128)
-    int32_t prep_cpw;         // (head, chunk) items per k_prep workgroup
+    int32_t prep_cpw;         // (head, chunk) items per k_prep wave
     float* sink;              // 8 KiB scratch line for stores of rows past a sequence's end
     void* tb16;               // [n_chunks][h_v] fp16 images of T diag(beta) (kTbHalfs each), or null:
                               //   k_prep then writes the split T and gamma, beta (prep_T, prep_GB)

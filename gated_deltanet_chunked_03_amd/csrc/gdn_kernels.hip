@@ -62,6 +62,7 @@ namespace {
 // inside their sequential loops.
 
 // LDS of one prep wave (about 18.5 KiB: eight waves per CU).
+constexpr int kPrepWaves = 8;
 struct __attribute__((aligned(16))) PrepSmem {
     float t[CH * LDF];      // T = (I + A)^-1 on and below the diagonal blocks; four of the
                             // blocks above hold A's diagonal blocks (prep_ad)
@@ -293,9 +294,13 @@ __device__ void classify_boundary(const Params& p, int seq, int N, int a, int h,
     if (lane == 0) p.warm[(size_t)(seg_base + a / p.L) * p.h_v + h] = cls == 0 ? 0 : (cls | (wq << 8));
 }
 
-// Work items are (value head, chunk slot) pairs, item f = h n_chunks + slot;
-// workgroup (one wave) b walks items [b prep_cpw, (b + 1) prep_cpw), fetching
-// the next item's inputs while it works on the current one. Per (chunk slot,
+// Work items are (value head, chunk slot) pairs, item f = slot h_v + h (the
+// value heads that share a key head are neighbours: their K rows come from
+// the same cache lines);
+// wave b (wave b % 8 of workgroup b / 8; the waves share nothing) walks items
+// [b prep_cpw, (b + 1) prep_cpw), fetching the next item's inputs while it
+// works on the current one. (Eight waves per workgroup: one-wave workgroups
+// are dispatched too slowly to fill the chip at once.) Per (chunk slot,
 // value head), block b = slot h_v + h:
 //   prep_T + b t_stride: T diag(beta) split into bf16 hi and lo, [part][row][k]
 //     (2 x 64 x 64), the k (column) axis in the kp order of the chain
@@ -309,18 +314,20 @@ __device__ void classify_boundary(const Params& p, int seq, int N, int a, int h,
 // 32 j + 16 (s / 4) + 4 g + s % 4 (s < 8) of the kp order, and nothing of
 // gamma or beta (the chain kernels scan the gates themselves).
 template <typename IO, bool F16>
-__global__ __launch_bounds__(64) void k_prep(Params p) {
-    __shared__ PrepSmem sm;
+__global__ __launch_bounds__(64 * kPrepWaves) void k_prep(Params p) {
+    __shared__ PrepSmem sm_all[kPrepWaves];
+    PrepSmem& sm = sm_all[wave_id()];
     const int lane = lane_id();
     const long long n_items = (long long)p.n_chunks * p.h_v;
-    const long long f0 = (long long)blockIdx.x * p.prep_cpw, f1 = min(f0 + (long long)p.prep_cpw, n_items);
+    const long long wv = (long long)blockIdx.x * kPrepWaves + wave_id();
+    const long long f0 = wv * p.prep_cpw, f1 = min(f0 + (long long)p.prep_cpw, n_items);
     if (f0 >= f1) return;
     // item f -> head, chunk slot and the slot's tokens
     int h, slot, nvalid, seq, c, len;
     size_t tok0;
     auto locate = [&](long long f) {
-        h = (int)(f / p.n_chunks);
-        slot = (int)(f - (long long)h * p.n_chunks);
+        slot = (int)(f / p.h_v);
+        h = (int)(f - (long long)slot * p.h_v);
         size_t tok_s;
         locate_chunk(p, slot, seq, c, len, tok_s);   // slot < n_chunks: always found
         tok0 = tok_s + (size_t)c * CH;
@@ -336,9 +343,17 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
             if ((c + 1) % p.L == 0 && c + 1 < N) classify_boundary(p, seq, N, c + 1, h, tok0);
         }
     }
-    locate(f0);
-    PrepIn<IO> nxt;
-    prep_fetch<IO>(nxt, p, tok0, nvalid, h, h / p.group);
+    // Items come in groups of the value heads (in this wave's range) that
+    // share a chunk and a key head: the gram of the group's K rows is formed
+    // once (its tiles stay in registers through the group, so the next
+    // group's K rows load after it). Each item's gates load one item ahead.
+    float g_nx, b_nx;
+    {
+        locate(f0);
+        const size_t idx = (tok0 + min(lane, nvalid - 1)) * (size_t)p.h_v + h;
+        g_nx = p.g[idx];
+        b_nx = p.beta[idx];
+    }
     if (p.sink) {   // (null for the low-level entry, which has no workspace)
         // the loop body's stores (gamma, beta; T) come after its loads; the same
         // number of stores to the scratch line here make the loop's entry look
@@ -349,13 +364,30 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(sk + 4 * (i & 3)) = u32x4{0u, 0u, 0u, 0u};
     }
-    for (long long f = f0; f < f1; ++f) {
+    for (long long fg = f0; fg < f1;) {
+        locate(fg);
+        const int hq_cur = h / p.group, slot_cur = slot, nv_cur = nvalid;
         const size_t tok_cur = tok0;
-        const int h_cur = h, slot_cur = slot, hq_cur = h / p.group;
-        const PrepIn<IO> cur = nxt;
+        const long long g_end = min(f1, (long long)slot_cur * p.h_v + (long long)(hq_cur + 1) * p.group);
+        PrepIn<IO> kin;
+        prep_fetch<IO>(kin, p, tok_cur, nv_cur, h, hq_cur);
+        f32x4 acc[10];
+        kin.nv = nv_cur;
+        prep_gram<IO>(kin, p, tok_cur, hq_cur, acc);
+    for (long long f = fg; f < g_end; ++f) {
+        const int h_cur = (int)(f - (long long)slot_cur * p.h_v);
+        const float g_cur = g_nx, b_cur = b_nx;
         {
-            const bool ok = lane < cur.nv;
-            const float gam = wave_scan(ok ? cur.g : 0.f), bt = ok ? cur.b : 0.f;
+            // the next item's gates (the last item loads its own again)
+            const long long fn = min(f + 1, f1 - 1);
+            locate(fn);
+            const size_t idx = (tok0 + min(lane, nvalid - 1)) * (size_t)p.h_v + h;
+            g_nx = p.g[idx];
+            b_nx = p.beta[idx];
+        }
+        {
+            const bool ok = lane < nv_cur;
+            const float gam = wave_scan(ok ? g_cur : 0.f), bt = ok ? b_cur : 0.f;
             sm.gam[lane] = gam;
             sm.beta[lane] = bt;
             if constexpr (!F16) {
@@ -373,13 +405,6 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
                 gf[3 * CH + lane] = __expf(gc);
             }
         }
-        // always a prefetch (the last item fetches itself again), so that every
-        // iteration has the same memory operations and the compiler's waits on
-        // them stay exact across the loop
-        locate(min(f + 1, f1 - 1));
-        prep_fetch<IO>(nxt, p, tok0, nvalid, h, h / p.group);
-        f32x4 acc[10];
-        prep_gram<IO>(cur, p, tok_cur, hq_cur, acc);
         // A = beta_i exp(gamma_i - gamma_j) k_i . k_j below the diagonal: the
         // off-diagonal tiles stay as hi/lo A operands, the diagonal ones go to
         // LDS transposed (prep_ad(b): position (i - 16 b, j - 16 b) holds A[j][i], j > i)
@@ -466,6 +491,8 @@ __global__ __launch_bounds__(64) void k_prep(Params p) {
                 }
             }
         }
+    }
+        fg = g_end;
     }
 }
 
@@ -2479,8 +2506,8 @@ static int launched() { return (int)hipGetLastError(); }
 
 int launch_prep(const Params& p, int io, void* stream) {
     if (p.n_chunks <= 0) return 0;
-    const long long items = (long long)p.n_chunks * p.h_v;
-    const dim3 grid((unsigned)((items + p.prep_cpw - 1) / p.prep_cpw)), block(64);
+    const long long items = (long long)p.n_chunks * p.h_v, waves = (items + p.prep_cpw - 1) / p.prep_cpw;
+    const dim3 grid((unsigned)((waves + kPrepWaves - 1) / kPrepWaves)), block(64 * kPrepWaves);
     if (p.tb16) {
         if (io == kIoBf16) hipLaunchKernelGGL((k_prep<bf16, true>), grid, block, 0, (hipStream_t)stream, p);
         else hipLaunchKernelGGL((k_prep<float, true>), grid, block, 0, (hipStream_t)stream, p);
