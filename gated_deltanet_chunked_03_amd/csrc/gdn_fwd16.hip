@@ -636,7 +636,7 @@ __global__ __launch_bounds__(NTC) void k_combine16(Params p) {
     };
     auto fetch = [&](Ops& o, int s) {
         s = min(s, P - 1);
-        const int f = flags[s];
+        const int f = __builtin_amdgcn_readfirstlane(flags[s]);   // (uniform: a branch-free select)
         const float* src = f ? p.seg_state + tiles_off(seg_base + s, p.h_v, h)
                              : p.seg_H + tiles_off(seg_base + s - 1, p.h_v, h);
 #pragma unroll
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(NTC) void k_combine16(Params p) {
     // and selected, so that every step issues the same memory operations.
     auto step = [&](int s, const Ops& o, int buf) {
         __syncthreads();   // the previous state's B operand is in xb[buf]
-        const bool mm = flags[s] == 0 && (s > 1 || p.s_init);
+        const bool mm = __builtin_amdgcn_readfirstlane(flags[s]) == 0 && (s > 1 || p.s_init);
         f16x8 Sb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) Sb[j] = *reinterpret_cast<const f16x8*>(xb[buf] + (j * 64 + lane) * 8);
