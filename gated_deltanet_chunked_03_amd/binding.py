@@ -22,7 +22,7 @@ STATUS_NAMES = ["GDN_OK", "GDN_ERR_NULL_ARG", "GDN_ERR_BAD_SHAPE", "GDN_ERR_UNSU
 CP_MODES = {"auto": 0, "off": 1, "exact": 2, "warmup": 3}
 GDN_BF16, GDN_F32 = 0, 1
 
-EXPORTED = ["gdn_plan", "gdn_fwd_workspace_bytes", "gdn_fwd", "gdn_fwd_debug", "gdn_chunk_prep",
+EXPORTED = ["gdn_plan", "gdn_fwd_workspace_bytes", "gdn_fwd", "gdn_fwd_noalloc", "gdn_fwd_debug", "gdn_chunk_prep",
             "gdn_decode", "gdn_bwd_workspace_bytes", "gdn_bwd", "gdn_calibrate_lambda", "gdn_profile_enable", "gdn_profile_read", "gdn_status_string", "gdn_last_error"]
 
 
@@ -82,6 +82,8 @@ def load_library(path: Optional[str] = None):
                     ctypes.c_size_t, P]
         lib.gdn_fwd.argtypes = fwd_args
         lib.gdn_fwd.restype = S
+        lib.gdn_fwd_noalloc.argtypes = fwd_args[:11] + [P]
+        lib.gdn_fwd_noalloc.restype = S
         lib.gdn_fwd_debug.argtypes = fwd_args + [P, P]
         lib.gdn_fwd_debug.restype = S
         lib.gdn_chunk_prep.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, P, P, P, P]
@@ -252,6 +254,45 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=Tru
     _check(lib, lib.gdn_fwd_debug(*args, _ptr(seg), _ptr(path)))
     del keep
     return out, fs, {"plan": info, "seg_state": seg, "path": path}
+
+
+def fwd_noalloc(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+                cu_seqlens=None, cp_mode="auto", lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0,
+                out=None, final_state=None):
+    """``fwd`` through gdn_fwd_noalloc: the library's per-device scratch array
+    serves as the workspace (descriptors needing more than
+    NOALLOC_SCRATCH_BYTES raise). Calls that overlap on one device race."""
+    torch = _torch()
+    B, T, h_qk, h_v, d_k, d_v, io, cu_dev, cu_host = _prepare(q, k, v, g, beta, cu_seqlens)
+    dev = q.device
+    n_seqs = B if cu_host is None else len(cu_host) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32, dev, (n_seqs, h_v, d_k, d_v))
+    desc, keep = make_desc(B, T, h_qk, h_v, d_k, d_v, io, cu_host, cp_mode, lam, warmup_chunks,
+                           noise_floor, n_cu)
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _req(out, "out", v.dtype, dev, tuple(v.shape))
+    fs = None
+    if output_final_state:
+        if final_state is None:
+            fs = torch.empty((n_seqs, h_v, d_k, d_v), dtype=torch.float32, device=dev)
+        else:
+            _req(final_state, "final_state", torch.float32, dev, (n_seqs, h_v, d_k, d_v))
+            fs = final_state
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    _check(lib, lib.gdn_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    float(scale), _ptr(initial_state), _ptr(cu_dev), _ptr(out), _ptr(fs),
+                                    stream))
+    del keep
+    return out, fs
+
+
+NOALLOC_SCRATCH_BYTES = 80 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 
 
 def profile_enable(on=True):

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libgdn.so")
 SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_fwd16.hip"),
-           os.path.join(CSRC, "gdn_bwd.hip"), os.path.join(CSRC, "gdn_api.cpp")]
+           os.path.join(CSRC, "gdn_bwd.hip"), os.path.join(CSRC, "gdn_noalloc.hip"),
+           os.path.join(CSRC, "gdn_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

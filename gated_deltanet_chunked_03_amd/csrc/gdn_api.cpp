@@ -27,6 +27,20 @@ gdn_status fail(gdn_status s, const char* fmt, ...) {
     return s;
 }
 
+}  // namespace
+
+int gdn::record_error(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+namespace {
+
 constexpr float kDefaultLambda = 1.0f;
 constexpr int kDefaultWarmup = 6;
 constexpr int kMaxWarmup = 8;

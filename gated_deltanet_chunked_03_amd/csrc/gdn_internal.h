@@ -68,6 +68,10 @@ struct Params {
 
 enum IoType { kIoBf16 = 0, kIoF32 = 1 };
 
+// Records a failed call's message for gdn_last_error (printf format) and
+// returns status (a gdn_status value).
+int record_error(int status, const char* fmt, ...);
+
 // Backward pass (gdn_bwd.hip). Chunks are numbered sequence by sequence as in
 // the forward; states are [128][128] fp32 blocks in the API layout.
 constexpr int kBwdTpg = 2 * kChunk * kChunk + kChunk;   // floats per (chunk, head): T, P, gamma

@@ -135,6 +135,26 @@ gdn_status gdn_fwd(const gdn_desc* desc,
                    void* out, float* final_state,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. gdn_fwd with the same arguments except the workspace, which
+ * lives in a scratch array the library holds on every device it runs on
+ * (GDN_NOALLOC_SCRATCH_BYTES per device, kept until the process ends). A
+ * descriptor whose gdn_fwd_workspace_bytes exceed it fails with
+ * GDN_ERR_WORKSPACE_TOO_SMALL before any launch. The call allocates nothing
+ * (the array's device address is looked up on the first call on each device).
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (gdn_fwd reads no workspace byte it has not written, so
+ * nothing needs clearing): calls that can overlap on one device -- on
+ * different streams, or from host threads without ordering -- race and must
+ * be serialised by the caller. Same ownership and error behaviour as gdn_fwd. */
+#define GDN_NOALLOC_SCRATCH_BYTES (80u << 20)
+gdn_status gdn_fwd_noalloc(const gdn_desc* desc,
+                           const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, float scale,
+                           const float* initial_state, const int32_t* cu_seqlens,
+                           void* out, float* final_state, void* stream);
+
 /* gdn_fwd, then copies of what the context-parallel step decided (section
  * "Gate-Driven Automatic Intra-Card Context Parallelism (AutoCP)"):
  *   seg_state_out  device fp32 [n_segments, h_v, d_k, d_v]: the initial state of
