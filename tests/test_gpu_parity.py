@@ -68,17 +68,19 @@ def test_fwd_single_segment(io, T, h_qk, h_v):
     print(f"[fwd off {io} T={T} {h_qk}/{h_v}] o {mx:.2e}/{mean:.2e} S {smx:.2e}/{smean:.2e}")
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
 @pytest.mark.parametrize("mode", ["exact", "warmup", "auto"])
-def test_fwd_context_parallel(mode):
+def test_fwd_context_parallel(mode, io):
     """Segments of L chunks with exact or warm-up boundary states: outputs
     within tolerance and the segment initial states close to the true states
-    (exact: to fp32 accuracy; warm-up on fast heads: <= 1e-3 relative)."""
+    (exact: to fp32 accuracy; warm-up on fast heads: <= 1e-3 relative), for
+    bf16 and fp32 inputs."""
     import torch
     T, L = 64 * 40 + 5, 4
-    inp = make_inputs(1, T, 2, 8, seed=30, gate="mixed", init_std=0.05)
+    inp = make_inputs(1, T, 2, 8, seed=30, gate="mixed", init_std=0.05, io_dtype=io)
     o, S, info = _run(inp, cp_mode=mode, n_cu=32, lam=0.6, debug=True)
     plan = info["plan"]
-    print(f"[cp {mode}] plan L={plan['L']} P={plan['P_max']} segs={plan['n_segments']}")
+    print(f"[cp {mode} {io}] plan L={plan['L']} P={plan['P_max']} segs={plan['n_segments']}")
     assert plan["cp_on"] == 1 and plan["L"] == L
     o_ref, S_ref, snaps = oracle_run(inp, snap_stride=64 * L, n_snap=plan["P_max"])
     seg = info["seg_state"].cpu().numpy()
@@ -165,18 +167,18 @@ def test_empty_inputs_pass_the_state_through():
             assert o.numel() == 0 and torch.equal(S, S0) and torch.count_nonzero(S2) == 0
 
 
-@pytest.mark.parametrize("mode", ["exact", "auto"])
-def test_grouped_combine(mode):
-    """Enough segments that the planner composes the boundary maps in groups
-    (three launches: group maps, links between groups, replay inside groups):
-    two packed sequences of different lengths (so different group counts), an
-    initial state, a ragged tail, exact and warm-up boundaries. Every boundary
-    state against the oracle's state there; outputs at the stated tolerance."""
+@pytest.mark.parametrize("mode,io", [("exact", "bf16"), ("auto", "bf16"), ("auto", "f32")])
+def test_grouped_combine(mode, io):
+    """Many segments per sequence (long boundary chains in the combine; the
+    planner also groups them, which the backward's forward re-run uses): two
+    packed sequences of different lengths, an initial state, a ragged tail,
+    exact and warm-up boundaries. Every boundary state against the oracle's
+    state there; outputs at the stated tolerance."""
     cu = [0, 64 * 129 + 37, 64 * 129 + 37 + 64 * 70 + 5]
-    inp = make_inputs(1, cu[-1], 2, 4, seed=61, gate="mixed", cu_seqlens=cu, init_std=0.05)
+    inp = make_inputs(1, cu[-1], 2, 4, seed=61, gate="mixed", cu_seqlens=cu, init_std=0.05, io_dtype=io)
     o, S, info = _run(inp, cp_mode=mode, n_cu=256, debug=True)
     plan = info["plan"]
-    print(f"\n[grouped {mode}] plan L={plan['L']} P={plan['P_max']} G={plan['combine_group']} "
+    print(f"\n[grouped {mode} {io}] plan L={plan['L']} P={plan['P_max']} G={plan['combine_group']} "
           f"J={plan['combine_groups']}", flush=True)
     assert plan["cp_on"] == 1 and plan["combine_group"] > 0 and plan["combine_groups"] >= 3
     L = plan["L"]
