@@ -130,6 +130,41 @@ def choose_path(g_seq, N, L, w, eps):
     return "warmup"
 
 
+def boundary_rule(g_seq, a, w, eps):
+    """Decision for the segment boundary at chunk a under the per-boundary
+    reading of the AutoCP section (gates decide per boundary, not per head):
+      ('start', a)   the w-chunk window reaches the sequence start: warm up over
+                     [0, a) from the initial state, which is exact;
+      ('warmup', j)  j <= w is the shortest run of whole chunks before a whose
+                     total log-decay sum(g) is at most ln(eps): warm up over
+                     [a - j, a) from zero -- the state the scan misses has been
+                     damped below the noise floor;
+      ('exact', 0)   no run of up to w chunks decays that far: the boundary
+                     state comes from the previous segment's exact map."""
+    if a - w <= 0:
+        return "start", a
+    cum = 0.0
+    for j in range(1, w + 1):
+        cum += float(np.sum(g_seq[(a - j) * CHUNK:(a - j + 1) * CHUNK]))
+        if cum <= math.log(eps):
+            return "warmup", j
+    return "exact", 0
+
+
+def boundary_summary(kinds):
+    """Path code of one (sequence, head) over its boundaries' decisions, the
+    boundaries whose window reaches the sequence start left out: 1 all warmed
+    up, 0 all exact, 2 mixed, 3 no such boundary."""
+    ks = [k for k, _ in kinds if k != "start"]
+    if not ks:
+        return 3
+    if all(k == "warmup" for k in ks):
+        return 1
+    if all(k == "exact" for k in ks):
+        return 0
+    return 2
+
+
 def _head_inputs(q, k, v, g, beta, t0, t1, h, hq):
     return q[t0:t1, hq], k[t0:t1, hq], v[t0:t1, h], g[t0:t1, h], beta[t0:t1, h]
 
@@ -142,9 +177,13 @@ def chunked_forward(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None
     mode: 'off' (one segment per sequence), 'exact' (segment initial states by
     composing the chunk maps: S0(s+1) = M_s S0(s) + H_s), 'warmup' (each
     boundary state by scanning the w chunks before it from zero), 'auto'
-    (per (sequence, head) via ``choose_path``).
+    (per (sequence, head) via ``choose_path``), 'boundary' (per boundary via
+    ``boundary_rule``: a warm-up or start boundary takes its scanned state, an
+    exact one the previous segment's map applied to the previous boundary's
+    state, whichever way that one was obtained).
     Returns (o, final_state, info) with info['S0'][n][h] = list of segment
-    initial states and info['path'][n][h].
+    initial states and info['path'][n][h] (for 'boundary' the code of
+    ``boundary_summary``, and info['boundary'][n][h] the decisions).
     """
     q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
     T, h_qk, d_k = q.shape
@@ -154,7 +193,8 @@ def chunked_forward(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None
     o = np.zeros((T, h_v, d_v))
     fin = np.zeros((n_seqs, h_v, d_k, d_v))
     info = {"S0": [[None] * h_v for _ in range(n_seqs)],
-            "path": [[None] * h_v for _ in range(n_seqs)]}
+            "path": [[None] * h_v for _ in range(n_seqs)],
+            "boundary": [[None] * h_v for _ in range(n_seqs)]}
     for n in range(n_seqs):
         t0, t1 = cu[n], cu[n + 1]
         N = n_chunks(t1 - t0)
@@ -180,7 +220,30 @@ def chunked_forward(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None
 
             # segment initial states
             S0 = [S_init]
-            if path == "exact":
+            if path == "boundary":
+                kinds = []
+                for s_ in range(1, len(segs)):
+                    a = segs[s_][0]
+                    kind, j = boundary_rule(gs, a, w, eps)
+                    kinds.append((kind, j))
+                    if kind == "exact":
+                        M = np.eye(d_k)
+                        Hm = np.zeros((d_k, d_v))
+                        for c in range(segs[s_ - 1][0], segs[s_ - 1][1]):
+                            sl, gam, _, _, W, U = prep[c]
+                            Mc, Hc = chunk_affine(ks[sl], gam, W, U)
+                            M, Hm = Mc @ M, Mc @ Hm + Hc
+                        S0.append(M @ S0[-1] + Hm)
+                    else:
+                        lo = 0 if kind == "start" else a - j
+                        S = S_init.copy() if kind == "start" else np.zeros((d_k, d_v))
+                        for c in range(lo, a):
+                            sl, gam, _, _, W, U = prep[c]
+                            _, S, _ = chunk_forward(S, qs[sl], ks[sl], gam, W, U, scale)
+                        S0.append(S)
+                info["boundary"][n][h] = kinds
+                info["path"][n][h] = boundary_summary(kinds)
+            elif path == "exact":
                 for (a, b_) in segs[:-1]:
                     M = np.eye(d_k)
                     Hm = np.zeros((d_k, d_v))

@@ -189,3 +189,75 @@ def test_prep_all_layout_and_padding():
     np.testing.assert_allclose(G[1, 1, 6:], gam[-1])
     np.testing.assert_allclose(W[1, 1, :6], W1)
     assert np.all(W[1, 1, 6:] == 0) and np.all(U[1, 1, 6:] == 0)
+
+
+def _switch_gates(N, switch_chunk, slow=-2e-4, fast=-0.4, fast_first=False):
+    """One head whose gates switch regime at a chunk: slow decay before it
+    (no run of <= 6 chunks decays below 1e-4), fast after it (one chunk does);
+    or the reverse with fast_first."""
+    a, b = (fast, slow) if fast_first else (slow, fast)
+    g = np.full(64 * N, a)
+    g[64 * switch_chunk:] = b
+    return g
+
+
+def test_boundary_rule_regime_switch_and_windows():
+    """The per-boundary rule, pinned by gates whose chunk sums are known in
+    closed form: a head that switches from slow to fast decay mid-sequence is
+    exact before the switch and warms up (one chunk) after it (summary: mixed);
+    constant decays of ln(eps) / (j - 1/2) per chunk give windows of exactly j
+    chunks for j = 2..5; boundaries within w chunks of the start are 'start'."""
+    eps, w, L, N = 1e-4, 6, 4, 40
+    g = _switch_gates(N, 20)
+    kinds = [cm.boundary_rule(g, a, w, eps) for a in range(L, N, L)]
+    # a = 4: window reaches the start; 8..20: the chunks before a are all slow
+    # (6 chunks sum to -0.077 > ln 1e-4); 24..36: chunk a - 1 is fast (-25.6)
+    expect = [("start", 4)] + [("exact", 0)] * 4 + [("warmup", 1)] * 4
+    assert kinds == expect
+    assert cm.boundary_summary(kinds) == 2
+    assert cm.boundary_summary([("start", 4), ("warmup", 1)]) == 1
+    assert cm.boundary_summary([("start", 4), ("exact", 0)]) == 0
+    assert cm.boundary_summary([("start", 4)]) == 3
+    for j in range(2, 6):
+        per_chunk = math.log(eps) / (j - 0.5)
+        gj = np.full(64 * 20, per_chunk / 64)
+        assert cm.boundary_rule(gj, 12, w, eps) == ("warmup", j), j
+    # a run that never decays far enough stays exact even at the window's end
+    assert cm.boundary_rule(np.full(64 * 20, math.log(eps) / (6.5 * 64)), 12, w, eps) == ("exact", 0)
+
+
+@pytest.mark.parametrize("switch,fast_first", [(20, False), (9, False), (14, True)])
+def test_boundary_mode_states(switch, fast_first):
+    """'boundary' mode against the sequential oracle's states: exact boundaries
+    (the previous segment's map applied to the previous boundary's state, even
+    when that one was warmed up) to fp64 accuracy on top of the inherited
+    warm-up error; warm-up boundaries within the contraction bound
+    exp(sum g over the window) |S at the window start|; 'start' boundaries
+    exact."""
+    T, L, w, eps = 64 * 32, 4, 6, 1e-4
+    inp, q, k, v, g, b = _case(T, h_qk=1, h_v=1, seed=17, gate="plain", init_std=0.5)
+    g[:, 0] = _switch_gates(32, switch, fast_first=fast_first).astype(np.float32)
+    _, _, snaps = gdn_sequential(q, k, v, g, b, inp.scale, inp.initial_state, snap_stride=64, n_snap=33)
+    o, fin, info = cm.chunked_forward(q, k, v, g, b, inp.scale, inp.initial_state, L=L, mode="boundary",
+                                      w=w, eps=eps)
+    S0s, kinds = info["S0"][0][0], info["boundary"][0][0]
+    assert info["path"][0][0] == 2
+    prev_err = 0.0
+    for s in range(1, len(S0s)):
+        a = s * L
+        kind, j = kinds[s - 1]
+        err = np.linalg.norm(S0s[s] - snaps[0, 0, a])
+        if kind == "start":
+            assert err < 1e-10 * np.linalg.norm(snaps[0, 0, a])
+        elif kind == "warmup":
+            bound = math.exp(float(np.sum(g[(a - j) * 64:a * 64, 0], dtype=np.float64))) * \
+                np.linalg.norm(snaps[0, 0, a - j])
+            assert 0.0 < err <= bound * (1 + 1e-9) + 1e-12
+        else:
+            # the map is exact; an error inherited from the previous boundary
+            # only contracts through the segment (|M|_2 <= 1 here)
+            assert err <= prev_err * (1 + 1e-9) + 1e-10 * np.linalg.norm(snaps[0, 0, a])
+        prev_err = err
+    # the reversed switch has exact boundaries after warmed-up ones
+    if fast_first:
+        assert ("exact", 0) in kinds and kinds.index(("exact", 0)) > kinds.index(("warmup", 1))

@@ -220,3 +220,48 @@ def test_calibrate_lambda_picks_a_candidate():
     torch.cuda.synchronize()
     o_ref, _, _ = oracle_run(inp)
     assert_within_tolerance(o.float().cpu().numpy().reshape(o_ref.shape), o_ref, "o")
+
+
+def test_per_boundary_rule_switch_heads_and_windows():
+    """AUTO decides per boundary: a head whose gates switch from slow to fast
+    decay mid-sequence (exact, then warm-up: mixed), one switching the other
+    way (exact boundaries chained onto warmed-up ones), and constant decays
+    that need warm-up windows of exactly 2, 3, 4 and 5 chunks. With a noise
+    floor of 0.05 a window one chunk too short or too long moves the boundary
+    state by percents, so every boundary state is compared with the fp64
+    chunk model's per-boundary reading of the same inputs (same windows, same
+    chaining), and the per-head path codes with the model's."""
+    import math
+    eps, w, N = 0.05, 6, 49
+    T = 64 * (N - 1) + 7
+    inp = make_inputs(1, T, 1, 6, seed=71, gate="plain", init_std=0.1)
+    g = inp.g
+    g[0, :, 0] = -2e-4
+    g[0, 64 * 24:, 0] = -0.4                  # slow -> fast at chunk 24
+    g[0, :, 1] = -0.4
+    g[0, 64 * 20:, 1] = -2e-4                 # fast -> slow at chunk 20
+    for h, j in zip(range(2, 6), range(2, 6)):
+        g[0, :, h] = math.log(eps) / (64 * (j - 0.5))
+    o, S, info = _run(inp, cp_mode="auto", n_cu=32, lam=0.6, warmup_chunks=w, noise_floor=eps, debug=True)
+    plan = info["plan"]
+    L = plan["L"]
+    print(f"\n[per-boundary] plan L={L} P={plan['P_max']}", flush=True)
+    assert plan["cp_on"] == 1 and L == 4
+    q, k, v, gg, b = inp.flat()
+    o_m, S_m, minfo = chunk_model.chunked_forward(q, k, v, gg, b, inp.scale, inp.initial_state, L=L,
+                                                  mode="boundary", w=w, eps=eps)
+    seg = info["seg_state"].cpu().numpy()
+    path = info["path"].cpu().numpy()
+    for h in range(inp.h_v):
+        kinds = minfo["boundary"][0][h]
+        rel = [np.linalg.norm(seg[s, h] - minfo["S0"][0][h][s]) / np.linalg.norm(minfo["S0"][0][h][s])
+               for s in range(1, plan["P_max"])]
+        print(f"  head {h}: path {path[0, h]} (model {minfo['path'][0][h]}) "
+              f"windows {sorted(set(j for kk, j in kinds if kk == 'warmup'))} max rel {max(rel):.2e}")
+        assert path[0, h] == minfo["path"][0][h], h
+        assert max(rel) < BOUNDARY_TOL, h
+    assert [minfo["path"][0][h] for h in range(6)] == [2, 2, 1, 1, 1, 1]
+    for h, j in zip(range(2, 6), range(2, 6)):
+        assert {jj for kk, jj in minfo["boundary"][0][h] if kk == "warmup"} == {j}
+    assert_within_tolerance(_o_np(o, inp), o_m)
+    assert_within_tolerance(S.cpu().numpy(), S_m, "final_state", STATE_MAX_TOL, STATE_MEAN_TOL)
