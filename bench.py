@@ -1,21 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark: Gated DeltaNet chunked-prefill forward on one MI355X.
 
-One step = one call of the library's forward (k_prep, k_cp_prep, k_cp_combine
-and the fused forward kernel) over one batch of seeded synthetic input already
-resident in HBM. Before every step a 1 GiB fill evicts the L2 caches and the
-256 MB Infinity Cache (outside the measured interval); each step's GPU time
-comes from HIP events on the stream around the step's four eager launches.
-A second pass with events between the kernels gives the per-kernel split;
-with --graph the step is also replayed from a HIP graph of the same launches
-(each replay first checked bit for bit against the eager result) and timed.
-The default workload is the TP8-shaped prompt (B=1, T=32768, h_qk=2, h_v=8,
-d=128, chunk 64, bf16 inputs).
+One step = one call of the library's forward (k_prep, k_cp_prep16, k_combine16
+and the fused forward kernel k_fwd_ws) over one batch of seeded synthetic input
+already resident in HBM. Before every step a 1 GiB fill evicts the L2 caches
+and the 256 MB Infinity Cache (outside the measured interval); each step's GPU
+time comes from HIP events on the stream around the step's four eager
+launches. A second pass with events between the kernels gives the per-kernel
+split; with --graph the step is also replayed from a HIP graph of the same
+launches (each replay first checked bit for bit against the eager result) and
+timed. The default workload is the TP8-shaped prompt (B=1, T=32768, h_qk=2,
+h_v=8, d=128, chunk 64, bf16 inputs).
 
 Prints one JSON line. Besides the contract fields it carries:
-  roofline      the forward kernel's algorithmic HBM bytes / its measured time
+  roofline      the whole step's algorithmic HBM bytes / ms_per_step (headline),
+                with the dominant kernel's own figure under "kernel" and the
+                summed counter traffic of the step's kernels
+  mfma          the step's algorithmic matrix work / ms_per_step against the
+                dense fp16/bf16 peak
+  step_ms_stats median, p10 and p90 of the timed steps
+  gpu_clock_mhz the shader clock sampled from sysfs while the timed steps ran
   cpu_baseline  the fp64 CPU oracle timed on the host cores on a token prefix
+                (threads used, host core count and CPU model stated)
   parity        GPU output vs that oracle on the same prefix
+  boundary_state_error  per value head: the largest relative error of the
+                segment initial states the forward used (warm-up or exact)
+                against the oracle's states at those boundaries
   backward      the backward pass (gdn_bwd) on the same workload: time per call, bytes,
                 matrix work of its chunk-gradient kernel, parity on a token prefix vs the fp64
                 backward oracle
@@ -37,22 +47,33 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GDN fwd ms & tokens/s at B=1,T=32768 per head config; % MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc", "gdn_kernels.hip")
-# HBM bytes per k_fwd launch on the tp8 workload (and per k_decode launch on the 256-row decode)
-# from rocprofv3 FETCH_SIZE / WRITE_SIZE passes (and k_fwd's executed bf16 MFMA work from an
-# MfmaFlopsBF16 pass),
-# scaled by a 512 MiB copy's counts (FETCH x 1.99981, WRITE x 1.0). Valid only for the kernel
-# source with this hash; any other source reports null.
-MEASURED_TRAFFIC = {"tp8": {"sha256": "90dbec2e8e3c68c4de13a1c7bcfb7158da48e7899e038cc76a17ba8a0ccddfce",
-                            "read": 185276494, "write": 67649536,
-                            # MfmaFlopsBF16 per k_fwd launch (same kernel source)
-                            "mfma_flops": 73551314944},
-                    # k_decode on the 256-row one-token decode, same passes and scale
-                    "decode256": {"sha256": "90dbec2e8e3c68c4de13a1c7bcfb7158da48e7899e038cc76a17ba8a0ccddfce",
-                                  "read": 135138696, "write": 134929280}}
+CSRC = os.path.join(ROOT, "gated_deltanet_chunked_03_amd", "csrc")
+# the sources the forward and decode kernels are built from; measured counter
+# figures below are valid only for sources with this combined hash
+KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("gdn_device.h", "gdn_internal.h", "gdn_kernels.hip",
+                                               "gdn_fwd16.hip")]
+# HBM bytes per launch of each forward kernel on the tp8 workload (AutoCP, default lambda) and
+# of k_decode on the 256-row decode, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by a
+# 512 MiB copy's counts (profiles/forward_kernels_tp8.md, decode_k_decode_256rows.md); None
+# until taken for the current sources.
+MEASURED_TRAFFIC = {"sha256": "8fda686b798646a92facf4cb7ad1bfc5d785236fb1ef605e4818f3f1e5c2b9bd",
+                    # bytes read, written per launch (keys as the per-kernel timings)
+                    "tp8": {"per_kernel": {"prep": [19971227, 29393888], "cp_prep": [72068361, 18219008], "cp_combine": [20429435, 4063232], "fwd": [146873813, 67895296]},
+                            "dominant": "fwd",
+                            # MfmaFlopsF16 + MfmaFlopsBF16 of the step's kernels per step
+                            "mfma_flops": 53140000000},
+                    "decode256": {"read": 135124865, "write": 134976256}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp4": 0.486, "tp2": 0.659, "tp1": 0.493}
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 matrix peak
+DOMINANT_KERNEL = "fwd"      # the fused forward kernel: the step's longest launch
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def algorithmic_bytes(B, T, h_qk, h_v, d=128, e_io=2, initial=False, final=True, n_seqs=None):
@@ -144,7 +165,7 @@ def measure_backward(args, gdn, torch, np, dev, flush, inp, q, k, v, g, beta, s0
     return {"ms_per_call": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
             "algorithmic_bytes": nbytes, "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
             "gflop_per_kernel": {kname: round(f / 1e9, 2) for kname, f in flops.items()},
-            "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_peak_tflops": MFMA_PEAK_TFLOPS,
             "precision": "bf16 MFMA with hi/lo splits of fp32 operands, fp32 accumulation; "
                          "forward re-run as in gdn_fwd",
             "parity_prefix": {"tokens": n_tok, "max_rel_and_mean_rel_l1": par,
@@ -185,7 +206,7 @@ def measure_decode(args, gdn, torch, np, dev, flush, timed):
     print(f"[bench] decode {rows} rows: {us:.2f} us/call, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
     traffic = None
     mt = MEASURED_TRAFFIC.get(f"decode{rows}")
-    if mt and hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest() == mt["sha256"]:
+    if mt and MEASURED_TRAFFIC["sha256"] == sources_sha256():
         traffic = mt["read"] + mt["write"]
     return {"workload": f"one-token decode: {rows} rows, h_qk={h_qk} h_v={h_v} d_k=d_v=128, bf16 "
                         f"inputs, fp32 states N(0, 0.1), state read and written once per call",
@@ -195,6 +216,70 @@ def measure_decode(args, gdn, torch, np, dev, flush, timed):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "algorithmic_bytes": nbytes},
             "parity": {"o_max_rel": omx, "o_mean_rel_l1": omean, "state_max_rel": smx,
                        "state_mean_rel_l1": smean}}
+
+
+class ClockSampler:
+    """Samples the GPU shader clock from sysfs (pp_dpm_sclk: the line marked
+    '*' holds the current clock) from a host thread, from warm-up to the end
+    of the timed steps; summary() reports the samples inside a window."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period_s, self.samples, self._stop = period_s, [], threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for path in self.paths:
+            try:
+                for line in open(path):
+                    if "*" in line:
+                        return float(line.split(":")[1].strip().lower().split("mhz")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            mhz = self._read()
+            if mhz is not None:
+                self.samples.append((time.time(), mhz))
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self.paths:
+            self._thread.join()
+
+    def summary(self, t0, t1):
+        if not self.paths:
+            return {"source": "sysfs pp_dpm_sclk", "samples": 0, "note": "no readable clock file on this host"}
+        x = sorted(m for t, m in self.samples if t0 <= t <= t1)
+        out = {"source": "sysfs pp_dpm_sclk (current shader clock) read every 2 ms by a host thread",
+               "window": "the timed steps (host enqueue start to the final synchronize)", "samples": len(x)}
+        if x:
+            pick = lambda f: x[min(len(x) - 1, int(f * (len(x) - 1) + 0.5))]  # noqa: E731
+            out.update({"min": x[0], "median": pick(0.5), "max": x[-1]})
+        return out
+
+
+def host_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"host_cores_online": os.cpu_count(), "host_cores_available": cores_available(),
+            "cpu_model": model}
 
 
 def cores_available():
@@ -272,6 +357,7 @@ def main():
         gdn.fwd(q, k, v, g, beta, scale=inp.scale, initial_state=s0, cp_mode=args.cp_mode,
                 lam=args.lam, workspace=ws, out=out, final_state=fs)
 
+    clock = ClockSampler().start()
     for _ in range(args.warmup):
         if not args.no_flush:
             flush.zero_()
@@ -301,6 +387,7 @@ def main():
     t0 = time.time()
     eager_ms = timed(step, args.steps)
     wall = time.time() - t0
+    clock_timed = clock.summary(t0, t0 + wall)
 
     # the same four launches replayed from a HIP graph (no host launch gaps);
     # every replay is checked against the eager result before it is timed
@@ -331,6 +418,7 @@ def main():
               file=sys.stderr, flush=True)
 
     # per-kernel times (events between the kernels; eager, cold caches)
+    t_pk = time.time()
     gdn.profile_enable(True)
     per = {"prep": [], "cp_prep": [], "cp_combine": [], "fwd": [], "total": []}
     for _ in range(args.steps):
@@ -345,6 +433,11 @@ def main():
         step()
         warm.append(gdn.profile_read()["total"])
     gdn.profile_enable(False)
+    clock.stop()
+    clock_pk = clock.summary(t_pk, time.time())
+    clock_pk["window"] = "the per-kernel pass (one synchronisation per step)"
+    clock_timed["note"] = ("the power controller's averaged clock: it includes the gaps between "
+                           "steps and the cache flushes, not only the kernels")
     print(f"[bench] timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
 
     backward = None
@@ -363,57 +456,93 @@ def main():
     nbytes = algorithmic_bytes(B, T, h_qk, h_v, e_io=2 if inp.io_dtype == "bf16" else 4,
                                initial=s0 is not None, final=True, n_seqs=n_seqs)
     flops = algorithmic_flops(B, T, h_qk, h_v)
-    fwd_s = mean["fwd"] * 1e-3
-    achieved = nbytes / fwd_s / 1e9
-    traffic = None
-    mt = MEASURED_TRAFFIC.get(args.config)
-    executed_flops = None
-    if mt and args.cp_mode == "auto" and args.lam == 0.0:
-        sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if sha == mt["sha256"]:
-            traffic = mt["read"] + mt["write"]
-            executed_flops = mt.get("mfma_flops")
-    roofline = {"bound": "hbm", "kernel": "k_fwd", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes": nbytes}
-    mfma = {"algorithmic_tflops_fwd_kernel": round(flops / fwd_s / 1e12, 2),
-            "peak_tflops_bf16": MFMA_BF16_PEAK_TFLOPS,
-            "frac_algorithmic": round(flops / fwd_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "algorithmic_gflop": round(flops / 1e9, 2),
-            # bf16 matrix work k_fwd executes per launch (hi/lo splits included), from rocprofv3's
-            # MfmaFlopsBF16 counter for this kernel source, over the measured k_fwd time
-            "executed_gflop_measured": round(executed_flops / 1e9, 2) if executed_flops else None,
-            "frac_executed": (round(executed_flops / fwd_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
-                              if executed_flops else None)}
+    step_gbs = nbytes / (ms * 1e-3) / 1e9
+    k_s = mean[DOMINANT_KERNEL] * 1e-3
+    k_gbs = nbytes / k_s / 1e9
+    # counter traffic (valid for the sources it was taken on, the default plan only)
+    mt = MEASURED_TRAFFIC.get(args.config) if MEASURED_TRAFFIC["sha256"] == sources_sha256() else None
+    if args.cp_mode != "auto" or args.lam != 0.0:
+        mt = None
+    step_traffic = round(sum(r + w for r, w in mt["per_kernel"].values())) if mt else None
+    kernel_traffic = round(sum(mt["per_kernel"][mt["dominant"]])) if mt else None
+    roofline = {"bound": "hbm", "scope": "whole forward step (ms_per_step)",
+                "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(step_gbs / HBM_PEAK_GBS, 4), "traffic": step_traffic,
+                "algorithmic_bytes": nbytes,
+                "kernel": {"name": "k_fwd_ws" if inp.io_dtype == "bf16" else "k_fwd16<float>",
+                           "ms": round(mean[DOMINANT_KERNEL], 4),
+                           "achieved": round(k_gbs, 1), "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                           "traffic": kernel_traffic,
+                           "note": "the step's algorithmic bytes over this kernel's event-timed "
+                                   "duration alone"},
+                "traffic_per_kernel_mb": ({kname: [round(r / 1e6, 1), round(w / 1e6, 1)]
+                                           for kname, (r, w) in mt["per_kernel"].items()} if mt else None)}
+    mfma = {"algorithmic_gflop": round(flops / 1e9, 2),
+            "achieved_tflops_step": round(flops / (ms * 1e-3) / 1e12, 2),
+            "peak_tflops": MFMA_PEAK_TFLOPS,
+            "frac_step": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "frac_dominant_kernel": round(flops / k_s / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            # matrix work the step's kernels execute (rocprofv3 MfmaFlopsF16 + MfmaFlopsBF16)
+            "executed_gflop_step_measured": round(mt["mfma_flops"] / 1e9, 2) if mt else None,
+            "frac_executed_step": (round(mt["mfma_flops"] / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
+                                   if mt else None)}
 
     cpu = None
     parity = None
+    boundary = None
     if args.cpu_tokens > 0:
         from oracle import gdn_sequential
         n_tok = min(args.cpu_tokens, T if inp.cu_seqlens is None else int(inp.cu_seqlens[1]))
         threads = max(1, min(cores_available(), 16, h_v))
         qf, kf, vf, gf, bf = (a[:n_tok] for a in inp.flat())
         s0_np = None if inp.initial_state is None else inp.initial_state[:1]
+        # the oracle also keeps its states at the segment boundaries inside the prefix
+        stride = 64 * pl["L"] if pl["cp_on"] else 0
+        n_snap = (n_tok // stride + 1) if stride else 0
         runs, t1 = 0, time.time()
         while runs == 0 or time.time() - t1 < 3.0:   # repeat to a few seconds of wall time
-            o_ref, _, _ = gdn_sequential(qf, kf, vf, gf, bf, inp.scale, s0_np, None,
-                                         n_threads=threads)
+            o_ref, _, snaps = gdn_sequential(qf, kf, vf, gf, bf, inp.scale, s0_np, None,
+                                             snap_stride=stride, n_snap=n_snap, n_threads=threads)
             runs += 1
         cpu_s = (time.time() - t1) / runs
         cpu = {"value": round(n_tok / cpu_s, 1), "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
                "sample": f"first {n_tok} tokens of sequence 0, all {h_v} value heads, fp64 "
                          f"token-by-token recurrence, one thread per head; mean of {runs} runs, "
-                         f"{cpu_s:.2f}s each"}
+                         f"{cpu_s:.2f}s each",
+               **host_info()}
         o_gpu = out[0, :n_tok].float().cpu().numpy().astype(np.float64)
         d = np.abs(o_gpu - o_ref)
         parity = {"tokens": n_tok, "max_rel": float(d.max() / np.abs(o_ref).max()),
                   "mean_rel_l1": float(d.sum() / np.abs(o_ref).sum()),
                   "tol_max_rel": 1e-2, "tol_mean_rel": 2e-3}
+        if stride and n_snap > 1:
+            # the segment initial states the forward used (one debug call, same plan)
+            _, _, dbg = gdn.fwd(q, k, v, g, beta, scale=inp.scale, initial_state=s0, cp_mode=args.cp_mode,
+                                lam=args.lam, workspace=ws, debug=True)
+            seg = dbg["seg_state"].cpu().numpy()
+            path = dbg["path"].cpu().numpy()[0]
+            P0 = min(pl["P_max"], n_snap)
+            per_head = []
+            for h in range(h_v):
+                rel = [float(np.linalg.norm(seg[s, h] - snaps[0, h, s]) / np.linalg.norm(snaps[0, h, s]))
+                       for s in range(1, P0) if 64 * pl["L"] * s < n_tok]
+                per_head.append(round(max(rel), 7) if rel else None)
+            codes = {0: "exact", 1: "warm-up", 2: "mixed", 3: "start only", -1: "not split"}
+            boundary = {"metric": "max over boundaries of |S0 - S_ref|_F / |S_ref|_F",
+                        "tol": 1e-3, "boundaries": P0 - 1,
+                        "per_head": per_head,
+                        "path_per_head": [codes.get(int(c), str(int(c))) for c in path],
+                        "head_class": list(inp.head_class),
+                        "max_warmup_heads": max([e for e, c in zip(per_head, path) if c == 1 and e is not None],
+                                                default=None),
+                        "max_exact_heads": max([e for e, c in zip(per_head, path) if c != 1 and e is not None],
+                                               default=None)}
 
     cfg = CONFIGS[args.config]
     workload = (f"{args.config}: B={B} T={T} h_qk={h_qk} h_v={h_v} d_k=d_v=128 chunk=64 "
                 f"{inp.io_dtype} inputs, fp32 state, heads {','.join(inp.head_class)}")
+    qs = lambda f: float(np.percentile(eager_ms, f))  # noqa: E731
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -421,21 +550,28 @@ def main():
         "vs_baseline": (round(value / (T / (PAGES_MS[args.config] * 1e-3)), 3)
                         if args.config in PAGES_MS and B == 1 else None),
         "baseline": ({"value": round(T / (PAGES_MS[args.config] * 1e-3), 1), "unit": "tokens/s",
-                      "source": "the pages' FlashQLA forward time for this shape on an H200",
+                      "source": "the pages' FlashQLA forward time for this shape on an H200 (context)",
                       "ms": PAGES_MS[args.config]} if args.config in PAGES_MS else None),
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": inp.io_dtype, "data": "synthetic",
         "config": {"workload": workload, "B": B, "T": T, "h_qk": h_qk, "h_v": h_v, "d": 128,
                    "chunk": 64, "cp_mode": args.cp_mode, "seed": cfg["seed"]},
         "roofline": roofline, "cpu_baseline": cpu,
+        "step_ms_stats": {"median": round(qs(50), 4), "p10": round(qs(10), 4), "p90": round(qs(90), 4),
+                          "min": round(min(eager_ms), 4), "max": round(max(eager_ms), 4)},
+        "gpu_clock_mhz": clock_timed, "gpu_clock_mhz_per_kernel_pass": clock_pk,
         "launch": "eager",
         "eager_ms_per_step": round(eager, 4),
         "graph_ms_per_step": round(float(np.mean(graph_ms)), 4) if graph_ok else None,
         "kernels_ms": {key: round(val, 4) for key, val in mean.items()},
         "warm_cache_ms_per_step": round(float(np.mean(warm)), 4),
-        "mfma": mfma, "parity": parity, "backward": backward, "decode": decode,
+        "mfma": mfma, "parity": parity, "boundary_state_error": boundary,
+        "backward": backward, "decode": decode,
         "plan": {key: pl[key] for key in ("L", "n_segments", "P_max", "cp_on", "warmup_chunks",
                                           "n_cu", "lambda")},
-        "precision": "bf16 MFMA operands, fp32 accumulation; non-input operands split hi+lo",
+        "precision": ("fp16 matrix-core operands for the chunk chain (state, V', K, Q, "
+                      "T diag(beta), P), V through an exact bf16 identity product, fp32 "
+                      "accumulation and fp32 state" if inp.io_dtype == "bf16" else
+                      "fp16 matrix-core operands from fp32 inputs, fp32 accumulation and state"),
         "wall_s": round(wall, 3),
     }
     print(json.dumps(line), flush=True)
