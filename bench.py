@@ -300,6 +300,8 @@ def main():
                     choices=["tiny", "tp8", "tp4", "tp2", "tp1", "tp1_b4", "long"])
     ap.add_argument("--cp-mode", default="auto", choices=["auto", "off", "exact", "warmup"])
     ap.add_argument("--lam", type=float, default=0.0)
+    ap.add_argument("--dv-split", type=int, default=0, choices=[0, 1, 2, 4],
+                    help="column blocks of d_v in the forward (0 = the planner decides)")
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of sequence 0 the CPU oracle runs (0 = skip)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
@@ -341,7 +343,7 @@ def main():
     out = torch.empty_like(v)
     fs = torch.empty((n_seqs, h_v, 128, 128), dtype=torch.float32, device=dev)
     pl = gdn.plan(B, T, h_qk, h_v, io_dtype=0 if inp.io_dtype == "bf16" else 1,
-                  cp_mode=args.cp_mode, lam=args.lam)
+                  cp_mode=args.cp_mode, lam=args.lam, dv_split=args.dv_split)
     ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
@@ -355,7 +357,7 @@ def main():
 
     def step():
         gdn.fwd(q, k, v, g, beta, scale=inp.scale, initial_state=s0, cp_mode=args.cp_mode,
-                lam=args.lam, workspace=ws, out=out, final_state=fs)
+                lam=args.lam, workspace=ws, out=out, final_state=fs, dv_split=args.dv_split)
 
     clock = ClockSampler().start()
     for _ in range(args.warmup):
@@ -519,7 +521,7 @@ def main():
         if stride and n_snap > 1:
             # the segment initial states the forward used (one debug call, same plan)
             _, _, dbg = gdn.fwd(q, k, v, g, beta, scale=inp.scale, initial_state=s0, cp_mode=args.cp_mode,
-                                lam=args.lam, workspace=ws, debug=True)
+                                lam=args.lam, workspace=ws, debug=True, dv_split=args.dv_split)
             seg = dbg["seg_state"].cpu().numpy()
             path = dbg["path"].cpu().numpy()[0]
             P0 = min(pl["P_max"], n_snap)
@@ -554,7 +556,7 @@ def main():
                       "ms": PAGES_MS[args.config]} if args.config in PAGES_MS else None),
         "dtype": inp.io_dtype, "data": "synthetic",
         "config": {"workload": workload, "B": B, "T": T, "h_qk": h_qk, "h_v": h_v, "d": 128,
-                   "chunk": 64, "cp_mode": args.cp_mode, "seed": cfg["seed"]},
+                   "chunk": 64, "cp_mode": args.cp_mode, "dv_split": pl["dv_split"], "seed": cfg["seed"]},
         "roofline": roofline, "cpu_baseline": cpu,
         "step_ms_stats": {"median": round(qs(50), 4), "p10": round(qs(10), 4), "p90": round(qs(90), 4),
                           "min": round(min(eager_ms), 4), "max": round(max(eager_ms), 4)},
@@ -566,7 +568,7 @@ def main():
         "warm_cache_ms_per_step": round(float(np.mean(warm)), 4),
         "mfma": mfma, "parity": parity, "boundary_state_error": boundary,
         "backward": backward, "decode": decode,
-        "plan": {key: pl[key] for key in ("L", "n_segments", "P_max", "cp_on", "warmup_chunks",
+        "plan": {key: pl[key] for key in ("L", "n_segments", "P_max", "cp_on", "dv_split", "warmup_chunks",
                                           "n_cu", "lambda")},
         "precision": ("fp16 matrix-core operands for the chunk chain (state, V', K, Q, "
                       "T diag(beta), P), V through an exact bf16 identity product, fp32 "

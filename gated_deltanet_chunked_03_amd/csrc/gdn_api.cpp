@@ -8,6 +8,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -46,6 +48,12 @@ constexpr int kDefaultWarmup = 6;
 constexpr int kMaxWarmup = 8;
 constexpr float kDefaultNoiseFloor = 1e-4f;
 constexpr size_t kStateElems = (size_t)gdn::kDim * gdn::kDim;
+// Relative time of one chunk step of a forward workgroup over 128 / s_dv
+// columns (index s_dv) against the full 128 columns, all CUs busy: 0.50 for
+// four blocks (measured at the TP1 B=4 shape: 2.1 against 4.2 us; the operand
+// staging, P and the dependent chain do not shrink with the columns), 0.65
+// for two (estimated between).
+constexpr double kColStep[5] = {0.0, 1.0, 0.65, 0.0, 0.50};
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -60,6 +68,7 @@ struct Plan {
     std::vector<int> len;       // tokens per sequence
     int n_chunks_total = 0, n_chunks_max = 0;
     int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0, cp_order = 0;
+    int s_dv = 1;                 // column blocks of d_v in the fused forward
     float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
     int comb_G = 0, comb_J = 0;   // grouped combine of the backward's forward re-run (0: one chain)
     FwdLayout fw;                 // the forward (fp16 chain kernels)
@@ -91,6 +100,12 @@ gdn_status validate_desc(const gdn_desc* d) {
     if (!(d->noise_floor >= 0.f && d->noise_floor < 1.f))
         return fail(GDN_ERR_BAD_OPTION, "noise_floor must be in [0, 1)");
     if (d->n_cu < 0) return fail(GDN_ERR_BAD_OPTION, "n_cu must be >= 0");
+    if (d->dv_split != 0 && d->dv_split != 1 && d->dv_split != 2 && d->dv_split != 4)
+        return fail(GDN_ERR_BAD_OPTION, "dv_split must be 0 (planner), 1, 2 or 4 (got %d)", d->dv_split);
+    if (d->dv_split > 1 && d->io_dtype != GDN_BF16)
+        return fail(GDN_ERR_BAD_OPTION, "dv_split > 1 needs bf16 inputs");
+    if (d->dv_split > 1 && d->cp_mode != GDN_CP_AUTO && d->cp_mode != GDN_CP_OFF)
+        return fail(GDN_ERR_BAD_OPTION, "dv_split > 1 runs without a context-parallel split (cp_mode AUTO or OFF)");
     if ((long long)d->B * d->T > 0x7fffffffLL)
         return fail(GDN_ERR_BAD_SHAPE, "B * T exceeds 2^31 - 1 tokens");
     if (d->host_cu_seqlens) {
@@ -153,7 +168,7 @@ void combine_grouping(int nb, long long heads, int n_cu, int J_max, int32_t* G_o
 // there), T (split hi/lo, 16 KiB) and gamma, beta (512 bytes) per (chunk,
 // value head); with a split, the segment states, the maps M and H, and the
 // boundary flags.
-gdn_status make_plan(const gdn_desc* d, Plan* pl) {
+gdn_status make_plan(const gdn_desc* d, Plan* pl, bool column_split = true) {
     gdn_status st = validate_desc(d);
     if (st != GDN_OK) return st;
     Plan P;
@@ -185,6 +200,14 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
     if (split && d->cp_mode == GDN_CP_AUTO &&
         ((long long)P.n_seqs * d->h_v >= P.n_cu || Nm < 2 * (P.w + 1)))
         split = false;
+    if (column_split && d->dv_split > 1) {   // forced column split: no segments
+        P.s_dv = d->dv_split;
+        split = false;
+    }
+    // AUTO may split d_v instead of the sequences (bf16 inputs): chosen below
+    // when it fills the CUs and its estimated time is lower
+    const bool try_columns = column_split && d->dv_split == 0 && split && d->cp_mode == GDN_CP_AUTO &&
+                             d->io_dtype == GDN_BF16;
     if (!split) {
         P.L = std::max(Nm, 1);
     } else {
@@ -211,6 +234,24 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl) {
         int L = best_L;
         while (n_segs_of(Nm, L) > gdn::kMaxSegsPerSeq) ++L;
         P.L = L;
+        if (try_columns) {
+            // Column blocks instead: the whole sequence per workgroup, d_v in
+            // the fewest blocks (2 or 4) that fill the CUs, each chunk step
+            // costing kColStep[s_dv] of a full one; taken when cheaper than
+            // the split's estimate.
+            const long long seq_heads = (long long)P.n_seqs * d->h_v;
+            for (int s_dv : {2, 4}) {
+                const long long wg = seq_heads * s_dv;
+                if (wg < P.n_cu) continue;
+                const long long rounds = (wg + P.n_cu - 1) / P.n_cu;
+                const double cost = kColStep[s_dv] * (double)rounds * Nm;
+                if (cost < best) {
+                    P.s_dv = s_dv;
+                    P.L = std::max(Nm, 1);
+                }
+                break;
+            }
+        }
     }
     long long ns = 0;
     for (int n = 0; n < P.n_seqs; ++n) {
@@ -316,6 +357,7 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
     p.h_v = d->h_v;
     p.group = d->h_v / d->h_qk;
     p.L = P.L;
+    p.dv_split = P.s_dv;
     p.w = P.w;
     p.cp_mode = d->cp_mode;
     p.n_segments = P.n_segments;
@@ -366,12 +408,32 @@ void set_layout(gdn::Params& p, const FwdLayout& F, const Plan& P, char* w8) {
 
 // The forward: k_prep (T diag(beta) images, boundary classes) | k_cp_prep16
 // (boundary states or maps) | k_combine16 (exact boundaries) | k_fwd16.
+// GDN_LOG=1 in the environment: one line per forward call on stderr with the
+// plan it runs (read once per process).
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("GDN_LOG");
+        return e && *e && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+void log_plan(const gdn_desc* d, const Plan& P) {
+    std::fprintf(stderr,
+                 "[gdn] fwd B=%d T=%d h_qk=%d h_v=%d io=%s cp_mode=%d: chunks=%d (max %d) cp_on=%d L=%d "
+                 "segments=%d (max %d per sequence) dv_split=%d w=%d eps=%g lambda=%g n_cu=%d workspace=%zu\n",
+                 d->B, d->T, d->h_qk, d->h_v, d->io_dtype == GDN_BF16 ? "bf16" : "f32", d->cp_mode,
+                 P.n_chunks_total, P.n_chunks_max, P.cp_on, P.L, P.n_segments, P.P_max, P.s_dv, P.w,
+                 (double)P.eps, (double)P.lambda, P.n_cu, P.ws_bytes);
+}
+
 gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, float scale, const float* s_init, const int32_t* cu, void* out,
                    float* s_final, void* ws, size_t ws_bytes, void* stream, float* seg_out, int32_t* path_out) {
     Plan P;
     gdn_status st = make_plan(d, &P);
     if (st != GDN_OK) return st;
+    if (log_enabled()) log_plan(d, P);
     if ((st = check_fwd_args(d, P, q, k, v, g, beta, scale, s_init, cu, out, s_final, ws, ws_bytes, P.fw.bytes)))
         return st;
     if ((st = check_ptr(seg_out, "seg_state_out", false)) || (st = check_ptr(path_out, "path_out", false, 4)))
@@ -519,7 +581,7 @@ extern "C" {
 
 size_t gdn_bwd_workspace_bytes(const gdn_desc* desc) {
     Plan P;
-    if (make_plan(desc, &P) != GDN_OK) return 0;
+    if (make_plan(desc, &P, false) != GDN_OK) return 0;
     return bwd_layout(desc, P).bytes;
 }
 
@@ -529,7 +591,7 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
                    float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
                    void* stream) {
     Plan P;
-    gdn_status st = make_plan(desc, &P);
+    gdn_status st = make_plan(desc, &P, false);   // (the re-run keeps all columns together)
     if (st != GDN_OK) return st;
     if (desc->io_dtype != GDN_BF16)
         return fail(GDN_ERR_BAD_DTYPE, "the backward takes bf16 q, k, v (io_dtype GDN_BF16)");
@@ -624,6 +686,7 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->workspace_bytes = P.ws_bytes;
     out->combine_group = P.comb_G;
     out->combine_groups = P.comb_J;
+    out->dv_split = P.s_dv;
     g_last_error.clear();
     return GDN_OK;
 }

@@ -787,27 +787,31 @@ __device__ __forceinline__ void ws_put_rows(f16* dst, const u32x4 (&x)[4], int t
     }
 }
 
-// State wave cw over chunks [c_lo, c_hi): S[8][2] (tiles [i][n], rows
-// 16 i + 4 g + e, column 32 cw + 16 n + c) in registers.
-__device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw,
-                         f32x4 S[8][2]) {
+// State wave over chunks [c_lo, c_hi) owning the NC 16-column tiles from
+// column col (a multiple of 16 NC): S[8][NC] (tiles [i][n], rows 16 i + 4 g + e,
+// column col + 16 n + c) in registers.
+template <int NC>
+__device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int col,
+                         f32x4 S[8][NC]) {
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
     const size_t tsv = (size_t)p.h_v * DK;
-    // this wave's V rows, as the A operands of the identity product: token
-    // 16 m + c, d_v 32 cw + 8 g .. + 8 (rows past the end read as zeros)
+    // V rows of the 32 columns around this wave's, as the A operands of the
+    // identity product: token 16 m + c, d_v v32 + 8 g .. + 8 (rows past the end
+    // read as zeros); E[n] picks column tile e0 + n of the 32
+    const int v32 = col & ~31, e0 = (col >> 4) & 1;
     auto vfetch = [&](u32x4 V[4], int cc) {
         cc = min(cc, c_hi - 1);
         const auto rv = rsrc(static_cast<const bf16*>(p.v) + (loc.tok0 + (size_t)cc * CH) * tsv + (size_t)h * DK,
                              (unsigned)min(CH, loc.len - cc * CH) * (unsigned)tsv * 2);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-            V[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(((16 * m + c) * tsv + 32 * cw + 8 * g) * 2), 0, 0);
+            V[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(((16 * m + c) * tsv + v32 + 8 * g) * 2), 0, 0);
     };
-    bf16x8 E[2];
+    bf16x8 E[NC];
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
+    for (int n = 0; n < NC; ++n)
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) E[n][s2] = (bf16)((8 * g + s2 == 16 * n + c) ? 1.f : 0.f);
+        for (int s2 = 0; s2 < 8; ++s2) E[n][s2] = (bf16)((8 * g + s2 == 16 * (e0 + n) + c) ? 1.f : 0.f);
     u32x4 VA[4], VB[4];
     vfetch(VA, c_lo);
     vfetch(VB, c_lo + 1);
@@ -816,16 +820,16 @@ __device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
     auto step = [&](int b, const u32x4 (&V)[4], int cc) {
         const float* gf = sm.gf[b];
         // O^T = S^T Q^T and Y = K S from the state's fp16 copy
-        f32x4 O[2][4], Y[4][2];
+        f32x4 O[NC][4], Y[4][NC];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int n = 0; n < 2; ++n) O[n][m] = Y[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < NC; ++n) O[n][m] = Y[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            f16x8 sb[2], kf[4], qf[4];
+            f16x8 sb[NC], kf[4], qf[4];
 #pragma unroll
-            for (int n = 0; n < 2; ++n) sb[n] = pack8h(S[2 * j][n], S[2 * j + 1][n]);
+            for (int n = 0; n < NC; ++n) sb[n] = pack8h(S[2 * j][n], S[2 * j + 1][n]);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 kf[m] = *reinterpret_cast<const f16x8*>(sm.k + kq_at(16 * m + c, 4 * j + g));
@@ -834,7 +838,7 @@ __device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int n = 0; n < 2; ++n) {
+                for (int n = 0; n < NC; ++n) {
                     Y[m][n] = mmh(kf[m], sb[n], Y[m][n]);
                     O[n][m] = mmh(sb[n], qf[m], O[n][m]);
                 }
@@ -845,43 +849,43 @@ __device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int n = 0; n < 2; ++n) S[i][n] *= ec;
+            for (int n = 0; n < NC; ++n) S[i][n] *= ec;
         // Y = V - e^gamma (K S)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const f32x4 eg = *reinterpret_cast<const f32x4*>(gf + CH + 16 * m + 4 * g);
 #pragma unroll
-            for (int n = 0; n < 2; ++n) Y[m][n] = mma16k32(__builtin_bit_cast(bf16x8, V[m]), E[n], Y[m][n] * -eg);
+            for (int n = 0; n < NC; ++n) Y[m][n] = mma16k32(__builtin_bit_cast(bf16x8, V[m]), E[n], Y[m][n] * -eg);
         }
         // V' = (T diag(beta)) Y
-        f16x8 Vb[2][2];
+        f16x8 Vb[2][NC];
         {
-            f16x8 Yb[2][2], tf[6];
+            f16x8 Yb[2][NC], tf[6];
 #pragma unroll
             for (int f = 0; f < 6; ++f) tf[f] = *reinterpret_cast<const f16x8*>(sm.tb + (f * 64 + lane) * 8);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int n = 0; n < 2; ++n) Yb[j][n] = pack8h(Y[2 * j][n], Y[2 * j + 1][n]);
-            f32x4 Vp[4][2];
+                for (int n = 0; n < NC; ++n) Yb[j][n] = pack8h(Y[2 * j][n], Y[2 * j + 1][n]);
+            f32x4 Vp[4][NC];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int n = 0; n < 2; ++n) {
+                for (int n = 0; n < NC; ++n) {
                     Vp[m][n] = mmh(tf[tb_frag(m, 0)], Yb[0][n], f32x4{0.f, 0.f, 0.f, 0.f});
                     if (m >= 2) Vp[m][n] = mmh(tf[tb_frag(m, 1)], Yb[1][n], Vp[m][n]);
                 }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int n = 0; n < 2; ++n) Vb[j][n] = pack8h(Vp[2 * j][n], Vp[2 * j + 1][n]);
+                for (int n = 0; n < NC; ++n) Vb[j][n] = pack8h(Vp[2 * j][n], Vp[2 * j + 1][n]);
         }
         // O^T scaled per token by scale e^gamma
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const float es = p.scale * gf[CH + 16 * m + c];
-            O[0][m] *= es;
-            O[1][m] *= es;
+#pragma unroll
+            for (int n = 0; n < NC; ++n) O[n][m] *= es;
         }
         __syncthreads();   // (2) P complete; the readers of K, Q and T diag(beta) are past
         // O^T += V'^T P^T (P causal: token tiles 0 and 1 need k step 0 only)
@@ -900,19 +904,19 @@ __device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
                 for (int j = 0; j < 2; ++j) {
                     if (j == 1 && m < 2) continue;
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) O[n][m] = mmh(Vb[j][n], pf[tb_frag(m, j)], O[n][m]);
+                    for (int n = 0; n < NC; ++n) O[n][m] = mmh(Vb[j][n], pf[tb_frag(m, j)], O[n][m]);
                 }
         }
-        // lane (g, c) of tile (n, m): token 16 m + c, d_v 32 cw + 16 n + 4 g + (0..3)
+        // lane (g, c) of tile (n, m): token 16 m + c, d_v col + 16 n + 4 g + (0..3)
         // (rows past the sequence's end fall outside the descriptor: dropped)
         const auto ro = rsrc(static_cast<bf16*>(p.out) + (loc.tok0 + (size_t)cc * CH) * tsv + (size_t)h * DK,
                              (unsigned)min(CH, loc.len - cc * CH) * (unsigned)tsv * 2);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int n = 0; n < 2; ++n)
+            for (int n = 0; n < NC; ++n)
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_rne(O[n][m][0], O[n][m][1]), pack_rne(O[n][m][2], O[n][m][3])},
-                                                      ro, (int)(((16 * m + c) * tsv + 32 * cw + 16 * n + 4 * g) * 2), 0, 0);
+                                                      ro, (int)(((16 * m + c) * tsv + col + 16 * n + 4 * g) * 2), 0, 0);
         // S += K~^T V'
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -922,7 +926,7 @@ __device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int n = 0; n < 2; ++n) S[i][n] = mmh(ktf[i], Vb[j][n], S[i][n]);
+                for (int n = 0; n < NC; ++n) S[i][n] = mmh(ktf[i], Vb[j][n], S[i][n]);
         }
         __syncthreads();   // (3) the next chunk staged
     };
@@ -1040,44 +1044,50 @@ __device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
     if (cc < c_hi) step(0, cc);
 }
 
-__global__ __launch_bounds__(NT8) void k_fwd_ws(Params p) {
+// The fused forward, grid (segment slot, value head, column block): column
+// block cb of p.dv_split covers the d_v columns [cb 128 / dv_split, ...); NSW
+// state waves own NC 16-column tiles each (NSW 16 NC = 128 / dv_split), the
+// four staging waves follow them.
+template <int NSW, int NC>
+__global__ __launch_bounds__(64 * (NSW + 4)) void k_fwd_ws(Params p) {
     __shared__ SmemWS sm;
     const int h = blockIdx.y, w = wave_id();
     const SegLoc loc = locate_segment(p, blockIdx.x);
     if (loc.seq < 0) return;
     const int c0 = loc.s * p.L, c1 = min(c0 + p.L, loc.N);
-    if (w < 4) {
+    if (w < NSW) {
         const int lane = lane_id(), c = lane & 15, g = lane >> 4;
-        f32x4 S[8][2];
+        const int col = (int)blockIdx.z * (16 * NC * NSW) + 16 * NC * w;
+        f32x4 S[8][NC];
         const float* src = loc.s == 0 ? p.s_init : p.seg_state;
         if (loc.s == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+                for (int n = 0; n < NC; ++n)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        S[i][n][e] = src ? src[tiles_off(loc.seq, p.h_v, h) + (16 * i + 4 * g + e) * DK + 32 * w + 16 * n + c] : 0.f;
+                        S[i][n][e] = src ? src[tiles_off(loc.seq, p.h_v, h) + (16 * i + 4 * g + e) * DK + col + 16 * n + c] : 0.f;
         } else {
             const float* sg = src + tiles_off(loc.seg_base + loc.s, p.h_v, h);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
-                    S[i][n] = *reinterpret_cast<const f32x4*>(sg + ((i * 8 + 2 * w + n) * 64 + lane) * 4);
+                for (int n = 0; n < NC; ++n)
+                    S[i][n] = *reinterpret_cast<const f32x4*>(sg + ((i * 8 + (col >> 4) + n) * 64 + lane) * 4);
         }
-        if (c0 < c1) ws_state(sm, p, loc, h, c0, c1, w, S);
+        if (c0 < c1) ws_state<NC>(sm, p, loc, h, c0, c1, col, S);
         if (loc.s == loc.P - 1 && p.s_final) {
             float* dst = p.s_final + tiles_off(loc.seq, p.h_v, h);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+                for (int n = 0; n < NC; ++n)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[(16 * i + 4 * g + e) * DK + 32 * w + 16 * n + c] = S[i][n][e];
+                    for (int e = 0; e < 4; ++e) dst[(16 * i + 4 * g + e) * DK + col + 16 * n + c] = S[i][n][e];
         }
     } else if (c0 < c1) {
-        ws_stage(sm, p, loc, h, c0, c1, w - 4);
+        ws_stage(sm, p, loc, h, c0, c1, w - NSW);
     }
 }
 
@@ -1113,9 +1123,14 @@ int launch_combine16(const Params& p, void* stream) {
 }
 
 int launch_fwd16(const Params& p, int io, void* stream) {
-    const dim3 grid((unsigned)p.n_segments, (unsigned)p.h_v), block(NT8);
-    if (io == kIoBf16) hipLaunchKernelGGL(k_fwd_ws, grid, block, 0, (hipStream_t)stream, p);
-    else hipLaunchKernelGGL(k_fwd16<float>, grid, block, 0, (hipStream_t)stream, p);
+    const unsigned s_dv = io == kIoBf16 ? (unsigned)p.dv_split : 1u;
+    const dim3 grid((unsigned)p.n_segments, (unsigned)p.h_v, s_dv);
+    hipStream_t hs = (hipStream_t)stream;
+    if (io != kIoBf16) hipLaunchKernelGGL(k_fwd16<float>, grid, dim3(NT8), 0, hs, p);
+    else if (s_dv == 1) hipLaunchKernelGGL((k_fwd_ws<4, 2>), grid, dim3(64 * 8), 0, hs, p);
+    else if (s_dv == 2) hipLaunchKernelGGL((k_fwd_ws<4, 1>), grid, dim3(64 * 8), 0, hs, p);
+    else if (s_dv == 4) hipLaunchKernelGGL((k_fwd_ws<2, 1>), grid, dim3(64 * 6), 0, hs, p);
+    else return (int)hipErrorInvalidValue;
     return launched16();
 }
 

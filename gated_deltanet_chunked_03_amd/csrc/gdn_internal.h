@@ -57,6 +57,7 @@ struct Params {
     int32_t seq_len;          // tokens per sequence when cu == null (decode: tokens per row)
     int32_t h_qk, h_v, group; // group = h_v / h_qk
     int32_t L;                // chunks per segment
+    int32_t dv_split;         // column blocks of d_v in the fused forward (1, 2 or 4; bf16 inputs)
     int32_t w;                // warm-up chunks
     int32_t cp_mode;          // gdn_cp_mode
     int32_t n_segments;

@@ -80,6 +80,9 @@ typedef struct {
     int32_t warmup_chunks;             /* warm-up window in chunks, 1..8; 0 = default (6) */
     float noise_floor;                 /* warm-up accepted if window decay <= this; 0 = default 1e-4 */
     int32_t n_cu;                      /* compute units to plan for; 0 = query the current device */
+    int32_t dv_split;                  /* column blocks of d_v the forward runs in parallel: 1, 2 or 4
+                                          (bf16 inputs, without a context-parallel split: cp_mode
+                                          AUTO or OFF); 0 = the planner decides (see gdn_plan) */
 } gdn_desc;
 
 /* Result of planning (host-only arithmetic on the descriptor). */
@@ -98,14 +101,25 @@ typedef struct {
     size_t workspace_bytes;  /* what gdn_fwd needs for this descriptor */
     int32_t combine_group;   /* boundaries per group of the grouped combine (0: one chain) */
     int32_t combine_groups;  /* groups of the longest sequence (0: one chain) */
+    int32_t dv_split;        /* column blocks of d_v in the forward (1: none) */
 } gdn_plan_info;
 
-/* Plan a forward: chunk counts, segment length L and workspace size.
- * Host arithmetic only, except that n_cu == 0 queries the current device's
- * compute-unit count. */
+/* Plan a forward (section "Gate-Driven Automatic Intra-Card Context
+ * Parallelism (AutoCP)" for the split; the section on optimising GDN chunked
+ * prefill for why one (sequence, head) per workgroup leaves CUs idle): chunk
+ * counts, the segment length L <= lambda sqrt(N) (N = chunks of the longest
+ * sequence) and the workspace size. When sequences x value heads alone leave
+ * CUs idle, AUTO either splits the sequences into segments (L chosen so that
+ * the segments fill the CUs in whole rounds) or, for bf16 inputs, splits d_v
+ * into 2 or 4 column blocks (the columns of the state evolve independently)
+ * when that fills the CUs and its estimated time is lower. Host arithmetic
+ * only, except that n_cu == 0 queries the current device's compute-unit count. */
 gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out);
 
-/* Workspace bytes gdn_fwd needs for desc (0 and a message on an invalid desc). */
+/* Workspace bytes gdn_fwd needs for desc (0 and a message on an invalid desc):
+ * the plan's per-chunk T diag(beta) images and gate factors, and with an
+ * AutoCP split (section "Gate-Driven Automatic Intra-Card Context Parallelism
+ * (AutoCP)") the boundary states, maps and flags. */
 size_t gdn_fwd_workspace_bytes(const gdn_desc* desc);
 
 /* The forward pass (the chunked-prefill forward of the FlashQLA pages, section on

@@ -190,6 +190,9 @@ def call_fwd(d, q=0x1000, k=0x1000, v=0x1000, g=0x1000, beta=0x1000, scale=0.1, 
     (dict(B=2, cu_seqlens=[0, 10, 20], T=20), "GDN_ERR_BAD_SHAPE"),
     (dict(T=20, cu_seqlens=[0, 15, 10, 20]), "GDN_ERR_BAD_SHAPE"),
     (dict(T=20, cu_seqlens=[0, 10, 19]), "GDN_ERR_BAD_SHAPE"),
+    (dict(dv_split=3), "GDN_ERR_BAD_OPTION"),
+    (dict(dv_split=2, io_dtype=1), "GDN_ERR_BAD_OPTION"),
+    (dict(dv_split=4, cp_mode="exact"), "GDN_ERR_BAD_OPTION"),
 ])
 def test_bad_descriptor(kw, status):
     d, keep = desc(**kw)
@@ -339,3 +342,24 @@ def test_python_binding_rejects_host_tensors():
     g = torch.zeros(1, 64, 1)
     with pytest.raises(ValueError):
         B.fwd(x, x, x, g, g)
+
+
+def test_plan_column_split():
+    """d_v column blocks: forced (1, 2, 4) runs without segments; AUTO takes
+    them only where they fill the CUs and the estimate beats the segment split
+    (short sequences, sequences x heads = half the CUs), never for fp32 inputs,
+    and keeps the split at the TP shapes (measured faster there)."""
+    for s_dv in (1, 2, 4):
+        p = B.plan(1, 32768, 2, 8, n_cu=256, dv_split=s_dv)
+        assert p["dv_split"] == s_dv and (p["cp_on"] == 0 or s_dv == 1)
+    p = B.plan(16, 896, 8, 8, n_cu=256)
+    assert (p["cp_on"], p["dv_split"], p["L"]) == (0, 2, 14)
+    p = B.plan(16, 896, 8, 8, n_cu=256, io_dtype=B.GDN_F32)
+    assert p["cp_on"] == 1 and p["dv_split"] == 1
+    for args in [(1, 32768, 2, 8), (4, 32768, 16, 16), (1, 32768, 16, 16)]:
+        p = B.plan(*args, n_cu=256)
+        assert p["dv_split"] == 1 and p["cp_on"] == 1, args
+    # forced column split with cp_mode OFF; workspace without the split's arrays
+    p0 = B.plan(1, 32768, 2, 8, n_cu=256, cp_mode="off")
+    p4 = B.plan(1, 32768, 2, 8, n_cu=256, dv_split=4)
+    assert p4["workspace_bytes"] == p0["workspace_bytes"]

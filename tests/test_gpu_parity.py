@@ -265,3 +265,20 @@ def test_per_boundary_rule_switch_heads_and_windows():
         assert {jj for kk, jj in minfo["boundary"][0][h] if kk == "warmup"} == {j}
     assert_within_tolerance(_o_np(o, inp), o_m)
     assert_within_tolerance(S.cpu().numpy(), S_m, "final_state", STATE_MAX_TOL, STATE_MEAN_TOL)
+
+
+@pytest.mark.parametrize("dv_split", [1, 2, 4])
+def test_fwd_column_split(dv_split):
+    """The forward with d_v in 1, 2 or 4 column blocks (one workgroup per
+    (sequence, head, block), no segments): outputs and final states against
+    the oracle; two sequences, a ragged tail, grouped heads, an initial state."""
+    cu = [0, 64 * 9 + 17, 64 * 9 + 17 + 64 * 4]
+    inp = make_inputs(1, cu[-1], 2, 4, seed=81, gate="mixed", cu_seqlens=cu, init_std=0.1)
+    o, S, info = _run(inp, cp_mode="auto", n_cu=16, dv_split=dv_split, debug=True)
+    plan = info["plan"]
+    print(f"\n[dv_split {dv_split}] plan cp_on={plan['cp_on']} dv_split={plan['dv_split']}", flush=True)
+    assert plan["cp_on"] == 0 and plan["dv_split"] == dv_split
+    o_ref, S_ref, _ = oracle_run(inp)
+    mx, mean = assert_within_tolerance(_o_np(o, inp), o_ref)
+    smx, smean = assert_within_tolerance(S.cpu().numpy(), S_ref, "final_state", STATE_MAX_TOL, STATE_MEAN_TOL)
+    print(f"  o {mx:.2e}/{mean:.2e} S {smx:.2e}/{smean:.2e}")
