@@ -2,7 +2,7 @@
 // planner and kernel launches. Host code only; see include/gdn.h.
 #include "gdn.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cmath>
