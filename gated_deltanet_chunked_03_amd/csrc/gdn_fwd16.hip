@@ -18,13 +18,17 @@
 // once to fp16 (11-bit significand, 8x finer than bf16); gate factors are
 // applied to fp32 accumulators. The state itself stays fp32.
 //
-// Work layout. A workgroup is 8 waves, two per SIMD; wave w owns the d_v
+// Work layouts. The bf16 forward runs the warp-specialised kernel k_fwd_ws
+// (state waves beside staging waves; described at its definition). The CP
+// preprocessing (k_cp_prep16) and the fp32 forward (k_fwd16<float>) use the
+// symmetric layout: a workgroup is 8 waves, two per SIMD; wave w owns the d_v
 // columns [16 w, 16 w + 16): its 128 x 16 slice of S (eight accumulator
 // tiles), of Y, V' and of the output stay in its registers, and the state
 // chain never crosses waves. Each wave issues a VALU instruction only every
 // ~7 cycles (measured), so two waves per SIMD are what keep its VALU and
-// matrix pipes busy; the LDS, which serves > 400 bytes per cycle per CU
-// (measured), absorbs every wave reading the whole chunk operands. A chunk's
+// matrix pipes busy; the LDS, which serves > 300 bytes per cycle per CU to
+// 16-byte reads (measured; writes about 75), absorbs every wave reading the
+// whole chunk operands. A chunk's
 // K, K^T and Q (converted to fp16), its V rows (as they are) and T diag(beta)
 // (from k_prep, already in operand layout) are staged in LDS by all 512
 // threads; the next chunk's inputs are loaded into registers a chunk and a
