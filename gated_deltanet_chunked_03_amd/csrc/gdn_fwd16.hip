@@ -468,8 +468,9 @@ __device__ __forceinline__ int pair_class16(const Params& p, int q, int& wq) {
     return (loc.seq < 0 || loc.s == 0) ? -1 : (v & 255);
 }
 
-// Block-wide exclusive prefix sum (8 waves).
-__device__ __forceinline__ int block_excl_scan8(int x, int* red, int& total) {
+// Block-wide exclusive prefix sum (NW waves).
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int x, int* red, int& total) {
     const int lane = lane_id(), w = threadIdx.x >> 6;
     int v = x;
 #pragma unroll
@@ -482,12 +483,62 @@ __device__ __forceinline__ int block_excl_scan8(int x, int* red, int& total) {
     int off = 0;
     total = 0;
 #pragma unroll
-    for (int i = 0; i < NW8; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const int r = red[i];
         if (i < w) off += r;
         total += r;
     }
     return off + v - x;
+}
+
+// The boundary pair (slot h_v + head) that workgroup i of the CP
+// preprocessing takes, and its part; -1: none (uniform over the workgroup).
+// An exact boundary takes PX workgroups (parts 0 .. PX - 1), a warm-up one
+// part 0 of one. Order as planned: exact boundaries first, then the warm-up
+// ones, each in pair order; or head-major (PX workgroups per pair).
+// red: 2 NW + 4 ints of LDS.
+template <int NW, int PX>
+__device__ int cp_pick(const Params& p, int i, int* red, int& part) {
+    constexpr int NT = 64 * NW;
+    if (!p.cp_order) {
+        part = i % PX;
+        return ((i % (PX * p.n_segments)) / PX) * p.h_v + i / (PX * p.n_segments);
+    }
+    const int n_pairs = p.n_segments * p.h_v;
+    const int per = (n_pairs + NT - 1) / NT, q0 = threadIdx.x * per, q1 = min(q0 + per, n_pairs);
+    int n_ex = 0, n_wu = 0;
+    for (int q = q0; q < q1; ++q) {
+        int wq;
+        const int c = pair_class16(p, q, wq);
+        n_ex += c == 0;
+        n_wu += c > 0;
+    }
+    if (threadIdx.x == 0) red[2 * NW] = -1;   // (ordered before its use by the scans' barriers)
+    int tot_ex, tot_wu;
+    const int pre_ex = block_excl_scan<NW>(n_ex, red, tot_ex);
+    const int pre_wu = block_excl_scan<NW>(n_wu, red + NW, tot_wu);
+    const bool want_ex = i < PX * tot_ex;
+    const int r = want_ex ? i / PX : i - PX * tot_ex;
+    part = want_ex ? i % PX : 0;
+    if (!want_ex && r >= tot_wu) return -1;   // (uniform: every thread has the totals)
+    const int pre = want_ex ? pre_ex : pre_wu, cnt = want_ex ? n_ex : n_wu;
+    if (r >= pre && r < pre + cnt) {
+        int k = pre;
+        for (int q = q0; q < q1; ++q) {
+            int wq;
+            const int c = pair_class16(p, q, wq);
+            if (want_ex ? c == 0 : c > 0) {
+                if (k == r) {
+                    red[2 * NW] = q;
+                    break;
+                }
+                ++k;
+            }
+        }
+    }
+    __syncthreads();
+    const int q = red[2 * NW];
+    return (q < 0 || q >= n_pairs) ? -1 : q;   // (q < 0 cannot happen: the ranks partition the boundaries)
 }
 
 // M (tile registers, columns 16 w + c) -> the combine's A-operand image:
@@ -541,46 +592,10 @@ template <typename IO>
 __global__ __launch_bounds__(NT8) void k_cp_prep16(Params p) {
     __shared__ Smem16<IO, false> sm;
     __shared__ int rank_red[2 * NW8 + 4];
-    const int i = (int)blockIdx.x;
-    if (!p.cp_order) {   // head-major order
-        cp_item16<IO>(p, sm, (i % (2 * p.n_segments)) >> 1, i & 1, i / (2 * p.n_segments));
-        return;
-    }
-    const int n_pairs = p.n_segments * p.h_v;
-    const int per = (n_pairs + NT8 - 1) / NT8, q0 = threadIdx.x * per, q1 = min(q0 + per, n_pairs);
-    int n_ex = 0, n_wu = 0;
-    for (int q = q0; q < q1; ++q) {
-        int wq;
-        const int c = pair_class16(p, q, wq);
-        n_ex += c == 0;
-        n_wu += c > 0;
-    }
-    if (threadIdx.x == 0) rank_red[2 * NW8] = -1;   // (ordered before its use by the scans' barriers)
-    int tot_ex, tot_wu;
-    const int pre_ex = block_excl_scan8(n_ex, rank_red, tot_ex);
-    const int pre_wu = block_excl_scan8(n_wu, rank_red + NW8, tot_wu);
-    const bool want_ex = i < 2 * tot_ex;
-    const int r = want_ex ? i >> 1 : i - 2 * tot_ex;
-    if (!want_ex && r >= tot_wu) return;   // (uniform: every thread has the totals)
-    const int pre = want_ex ? pre_ex : pre_wu, cnt = want_ex ? n_ex : n_wu;
-    if (r >= pre && r < pre + cnt) {
-        int k = pre;
-        for (int q = q0; q < q1; ++q) {
-            int wq;
-            const int c = pair_class16(p, q, wq);
-            if (want_ex ? c == 0 : c > 0) {
-                if (k == r) {
-                    rank_red[2 * NW8] = q;
-                    break;
-                }
-                ++k;
-            }
-        }
-    }
-    __syncthreads();
-    const int q = rank_red[2 * NW8];
-    if (q < 0 || q >= n_pairs) return;   // (cannot happen: the ranks partition the boundaries)
-    cp_item16<IO>(p, sm, q / p.h_v, want_ex ? (i & 1) : 0, q % p.h_v);
+    int part;
+    const int q = cp_pick<NW8, 2>(p, (int)blockIdx.x, rank_red, part);
+    if (q < 0) return;
+    cp_item16<IO>(p, sm, q / p.h_v, part, q % p.h_v);
 }
 
 // ----------------------------------------------------------------------------
@@ -1095,6 +1110,275 @@ __global__ __launch_bounds__(64 * (NSW + 4)) void k_fwd_ws(Params p) {
     }
 }
 
+// ----------------------------------------------------------------------------
+// CP preprocessing with specialised waves (bf16 inputs): one 12-wave
+// workgroup per boundary pair. Waves 0-3 run the state (each owning 32 d_v
+// columns): from zero over the previous segment (H of an exact boundary) or
+// over the warm-up window (from zero, or from the initial state where the
+// window starts at the sequence start). Waves 4-7 run the map of an exact
+// boundary's previous segment from the identity with V = 0 (M, 32 columns
+// each), on the same staged chunks. Waves 8-11 stage K, K~^T, V,
+// T diag(beta) and the gate factors of every chunk; all of them are
+// double-buffered in LDS, so a chunk step needs one barrier and the state
+// and map waves issue no global loads. The chunk step of a state or map
+// wave is the forward's without the output: Y = K S, S <- e^gamma_C S,
+// Y = V - e^gamma Y (V = 0 for M), V' = T diag(beta) Y, S += K~^T V'.
+struct __attribute__((aligned(16))) SmemCP {
+    // (the small buffers first: more of the operand reads reach their
+    // addresses through the LDS instructions' 16-bit offsets)
+    float gf[2][kGfFloats];               // gate factors (as in the fused forward)
+    f16 tb[2][kTbHalfs];                  // T diag(beta) fragments
+    f16 k[2][CH * kWsRow];                // K (the map image overlays both at the end)
+    f16 kt[2][DK * kWsRowT];              // K~^T
+    bf16 v[2][CH * kWsRow];               // V rows, d_v in natural order
+};
+static_assert(sizeof(f16) * 2 * CH * kWsRow >= sizeof(f16) * DK * LMI, "map image fits over K");
+constexpr int kCpWaves = 12;
+
+// State (WANT_V) or map wave over chunks [c_lo, c_hi), 32 columns from col:
+// S[i][n] is the tile of rows 16 i + 4 g + e, column col + 16 n + c.
+template <bool WANT_V>
+__device__ void cp_state(SmemCP& sm, int c_lo, int c_hi, int col, f32x4 S[8][2]) {
+    constexpr int NC = 2;
+    const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+    // K~^T operand offsets: kt_at(16 i + c, 4 j + g) splits into this lane's
+    // part for i % 4 and a constant (the swizzle XORs bits 3-5 of the piece
+    // offset with 8 i)
+    int ktl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ktl[r] = c * kWsRowT + ((8 * g) ^ (8 * r));
+    bf16x8 E[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n)
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) E[n][s2] = (bf16)((8 * g + s2 == 16 * n + c) ? 1.f : 0.f);
+    __syncthreads();   // the first chunk staged
+    auto step = [&](int b) {
+        const float* gf = sm.gf[b];
+        // Y = K S from the state's fp16 copy
+        f32x4 Y[4][NC];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = 0; n < NC; ++n) Y[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f16x8 sb[NC], kf[4];
+#pragma unroll
+            for (int n = 0; n < NC; ++n) sb[n] = pack8h(S[2 * j][n], S[2 * j + 1][n]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) kf[m] = *reinterpret_cast<const f16x8*>(sm.k[b] + kq_at(16 * m + c, 4 * j + g));
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) Y[m][n] = mmh(kf[m], sb[n], Y[m][n]);
+            __builtin_amdgcn_sched_barrier(0);   // (bounds the operand reads in flight)
+        }
+        const float ec = gf[3 * CH];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int n = 0; n < NC; ++n) S[i][n] *= ec;
+        // Y = V - e^gamma (K S); V through the identity product (A: token
+        // 16 m + c, d_v col + 8 g .. + 8)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(gf + CH + 16 * m + 4 * g);
+            if constexpr (WANT_V) {
+                const bf16x8 vr = *reinterpret_cast<const bf16x8*>(sm.v[b] + (16 * m + c) * kWsRow + col + 8 * g);
+#pragma unroll
+                for (int n = 0; n < NC; ++n) Y[m][n] = mma16k32(vr, E[n], Y[m][n] * -eg);
+            } else {
+#pragma unroll
+                for (int n = 0; n < NC; ++n) Y[m][n] *= -eg;
+            }
+        }
+        // V' = (T diag(beta)) Y
+        f16x8 Vb[2][NC];
+        {
+            f16x8 Yb[2][NC], tf[6];
+#pragma unroll
+            for (int f = 0; f < 6; ++f) tf[f] = *reinterpret_cast<const f16x8*>(sm.tb[b] + (f * 64 + lane) * 8);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) Yb[j][n] = pack8h(Y[2 * j][n], Y[2 * j + 1][n]);
+            f32x4 Vp[4][NC];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) {
+                    Vp[m][n] = mmh(tf[tb_frag(m, 0)], Yb[0][n], f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (m >= 2) Vp[m][n] = mmh(tf[tb_frag(m, 1)], Yb[1][n], Vp[m][n]);
+                }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) Vb[j][n] = pack8h(Vp[2 * j][n], Vp[2 * j + 1][n]);
+        }
+        // S += K~^T V'
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f16x8 ktf[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ktf[i] = *reinterpret_cast<const f16x8*>(sm.kt[b] + ktl[i & 3] + 16 * i * kWsRowT + ((32 * j) ^ (32 * (i >> 2))));
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int n = 0; n < NC; ++n) S[i][n] = mmh(ktf[i], Vb[j][n], S[i][n]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();   // the next chunk staged; this one's buffers free
+    };
+    int cc = c_lo;
+    for (; cc + 1 < c_hi; cc += 2) {
+        step(0);
+        step(1);
+    }
+    if (cc < c_hi) step(0);
+}
+
+// Staging wave cw of the CP preprocessing (threads t = 64 cw + lane): during
+// the step of chunk n it stages chunk n + 1 into the other buffers and loads
+// chunk n + 2 (past the last chunk, the last one again: staged, never read).
+__device__ void cp_stage(SmemCP& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw) {
+    const int t = 64 * cw + lane_id();
+    const int hq = h / p.group;
+    const size_t ts = (size_t)p.h_qk * DK, tsv = (size_t)p.h_v * DK;
+    u32x4 kr[4], vr[4], tbr[2];
+    float gfr;
+    f32x4 kfac;   // e^(gamma_C - gamma) of this thread's four tokens
+    auto fetch = [&](int cc) {
+        cc = min(cc, c_hi - 1);
+        const size_t tok0 = loc.tok0 + (size_t)cc * CH;
+        const int nv = min(CH, loc.len - cc * CH);
+        ws_load_rows(kr, p.k, tok0, ts, hq, nv, t);
+        ws_load_rows(vr, p.v, tok0, tsv, h, nv, t);
+        const size_t blk = (size_t)(loc.chunk_base + cc) * p.h_v + h;
+        const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const f16*>(p.tb16) + blk * (size_t)kTbHalfs);
+        tbr[0] = tb[t];
+        tbr[1] = tb[t < 128 ? 256 + t : t];   // (pieces 256..383; the rest load piece t again)
+        const float* gfb = p.gf16 + blk * (size_t)kGfFloats;
+        gfr = gfb[t];
+        kfac = *reinterpret_cast<const f32x4*>(gfb + 2 * CH + 4 * ((t >> 4) & 15));
+    };
+    auto stage = [&](int b) {
+        ws_put_rows(sm.k[b], kr, t);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<u32x4*>(sm.v[b] + (4 * ((t >> 4) & 15) + j) * kWsRow + 8 * (t & 15)) = vr[j];
+        *reinterpret_cast<u32x4*>(sm.tb[b] + 8 * t) = tbr[0];
+        if (t < 128) *reinterpret_cast<u32x4*>(sm.tb[b] + 8 * (256 + t)) = tbr[1];
+        sm.gf[b][t] = gfr;
+        const int pt = ws_pt(t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = 8 * (t & 15) + e;
+            f32x4 col;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned wv = kr[j][e >> 1];
+                col[j] = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16)) * kfac[j];
+            }
+            *reinterpret_cast<f16x4*>(sm.kt[b] + d * kWsRowT + (pt ^ tswz(d))) = __builtin_convertvector(col, f16x4);
+        }
+    };
+    fetch(c_lo);
+    stage(0);
+    fetch(c_lo + 1);
+    __syncthreads();   // the first chunk staged
+    int cc = c_lo;
+    for (; cc + 1 < c_hi; cc += 2) {
+        stage(1);
+        fetch(cc + 2);
+        __syncthreads();
+        stage(0);
+        fetch(cc + 3);
+        __syncthreads();
+    }
+    if (cc < c_hi) {
+        stage(1);
+        __syncthreads();
+    }
+}
+
+// One workgroup per boundary pair (order as planned, see cp_pick). Output:
+// exact boundary s (between segments s - 1 and s): H_{s-1} (tile order) and,
+// where it matters (s > 1 or an initial state), M_{s-1} as the combine's fp16
+// A-operand image; warm-up boundary: its state (tile order).
+__global__ __launch_bounds__(64 * kCpWaves) void k_cp_ws(Params p) {
+    __shared__ SmemCP sm;
+    __shared__ int rank_red[2 * kCpWaves + 4];
+    int part;
+    const int q = cp_pick<kCpWaves, 1>(p, (int)blockIdx.x, rank_red, part);
+    if (q < 0) return;
+    const int slot = q / p.h_v, h = q % p.h_v;
+    const SegLoc loc = locate_segment(p, slot);
+    int wq;
+    const int cls = pair_class16(p, q, wq);
+    if (cls < 0) return;
+    const int a = loc.s * p.L;   // first chunk of segment s
+    const int c_lo = cls ? a - wq : a - p.L, c_hi = a;
+    const bool want_m = cls == 0 && (loc.s > 1 || p.s_init);
+    const int w = wave_id(), lane = lane_id(), c = lane & 15, g = lane >> 4;
+    if (w < 4) {
+        const int col = 32 * w;
+        f32x4 S[8][2];
+        const bool from_init = cls && c_lo == 0 && p.s_init;
+        const float* s0 = from_init ? p.s_init + tiles_off(loc.seq, p.h_v, h) : nullptr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[i][n][e] = s0 ? s0[(16 * i + 4 * g + e) * DK + col + 16 * n + c] : 0.f;
+        cp_state<true>(sm, c_lo, c_hi, col, S);
+        float* dst = cls ? p.seg_state + tiles_off(loc.seg_base + loc.s, p.h_v, h)
+                         : p.seg_H + tiles_off(loc.seg_base + loc.s - 1, p.h_v, h);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                *reinterpret_cast<f32x4*>(dst + ((i * 8 + (col >> 4) + n) * 64 + lane) * 4) = S[i][n];
+    } else if (w < 8) {
+        if (!want_m) {
+            for (int k = c_lo; k <= c_hi; ++k) __syncthreads();   // (the chain's barriers)
+            return;
+        }
+        const int wm = w - 4, col = 32 * wm;
+        f32x4 S[8][2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[i][n][e] = (16 * i + 4 * g + e == col + 16 * n + c) ? 1.f : 0.f;
+        cp_state<false>(sm, c_lo, c_hi, col, S);
+        // M -> the combine's A-operand image: fragment F = 4 rt + j holds, in
+        // lane (g, c), row 16 rt + c at the kp positions 32 j + 8 g .. + 8 --
+        // columns of block j, which are this wave's when j = wm. Staged through
+        // LDS (row i, columns in kp order) over the K buffers, whose last
+        // readers passed the chain's last barrier; each wave reads back only
+        // what it wrote.
+        f16* img = &sm.k[0][0];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    img[(16 * i + 4 * g + e) * LMI + col + 8 * (c >> 2) + 4 * n + (c & 3)] = (f16)S[i][n][e];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        f16* dst = reinterpret_cast<f16*>(p.seg_M) + tiles_off(loc.seg_base + loc.s - 1, p.h_v, h);
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+            *reinterpret_cast<f16x8*>(dst + ((size_t)(4 * rt + wm) * 64 + lane) * 8) =
+                *reinterpret_cast<const f16x8*>(img + (16 * rt + c) * LMI + col + 8 * g);
+    } else {
+        cp_stage(sm, p, loc, h, c_lo, c_hi, w - 8);
+    }
+}
+
 // Boundary states in tile order -> row-major (debug copies).
 __global__ __launch_bounds__(64) void k_tiles_to_rm(const float* src, float* dst) {
     const size_t blk = blockIdx.x;
@@ -1114,9 +1398,13 @@ int launched16() { return (int)hipGetLastError(); }
 }  // namespace
 
 int launch_cp_prep16(const Params& p, int io, void* stream) {
-    const dim3 grid((unsigned)(2 * p.n_segments * p.h_v)), block(NT8);
-    if (io == kIoBf16) hipLaunchKernelGGL(k_cp_prep16<bf16>, grid, block, 0, (hipStream_t)stream, p);
-    else hipLaunchKernelGGL(k_cp_prep16<float>, grid, block, 0, (hipStream_t)stream, p);
+    if (io == kIoBf16) {
+        hipLaunchKernelGGL(k_cp_ws, dim3((unsigned)(p.n_segments * p.h_v)), dim3(64 * kCpWaves), 0,
+                           (hipStream_t)stream, p);
+    } else {
+        hipLaunchKernelGGL(k_cp_prep16<float>, dim3((unsigned)(2 * p.n_segments * p.h_v)), dim3(NT8), 0,
+                           (hipStream_t)stream, p);
+    }
     return launched16();
 }
 
