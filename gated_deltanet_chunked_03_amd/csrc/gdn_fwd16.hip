@@ -814,6 +814,12 @@ __device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
                          f32x4 S[8][NC]) {
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
     const size_t tsv = (size_t)p.h_v * DK;
+    // K~^T operand offsets: kt_at(16 i + c, 4 j + g) splits into this lane's
+    // part for i % 4 and a constant (the swizzle XORs bits 3-5 of the piece
+    // offset with 8 i)
+    int ktl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ktl[r] = c * kWsRowT + ((8 * g) ^ (8 * r));
     // V rows of the 32 columns around this wave's, as the A operands of the
     // identity product: token 16 m + c, d_v v32 + 8 g .. + 8 (rows past the end
     // read as zeros); E[n] picks column tile e0 + n of the 32
@@ -941,7 +947,8 @@ __device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
         for (int j = 0; j < 2; ++j) {
             f16x8 ktf[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ktf[i] = *reinterpret_cast<const f16x8*>(sm.kt[b] + kt_at(16 * i + c, 4 * j + g));
+            for (int i = 0; i < 8; ++i)
+                ktf[i] = *reinterpret_cast<const f16x8*>(sm.kt[b] + ktl[i & 3] + 16 * i * kWsRowT + ((32 * j) ^ (32 * (i >> 2))));
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -960,23 +967,44 @@ __device__ void ws_state(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
 }
 
 // Staging wave cw over chunks [c_lo, c_hi) (threads t = 64 cw + lane): P's
-// row block [16 cw, 16 cw + 16) and the staging of every operand.
+// row block [16 cw, 16 cw + 16) and the staging of every operand. Chunk c's
+// inputs are held in register set c % 2 (of the loop's parity b) between their
+// loads and their staging: during the step of chunk n the set of chunk n + 2
+// (free since chunk n was staged) is filled half in the first part of the
+// step (K rows, T diag(beta)) and half after the first barrier (Q rows), so
+// the memory pipe's time for the loads is spread over both halves, beside
+// the P product and beside the staging of chunk n + 1.
+struct WsIn {
+    u32x4 kr[4], qr[4], tbr[2];
+};
 __device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw) {
     const int lane = lane_id(), c = lane & 15, g = lane >> 4, t = 64 * cw + lane;
     const int hq = h / p.group;
     const size_t ts = (size_t)p.h_qk * DK;
     const float log2_scale = __log2f(p.scale);
-    u32x4 kr[4], qr[4], tbr[2];
-    auto fetch = [&](int cc) {
+    WsIn R[2];
+    auto rows_of = [&](int& cc, size_t& tok0, int& nv) {
         cc = min(cc, c_hi - 1);
-        const size_t tok0 = loc.tok0 + (size_t)cc * CH;
-        const int nv = min(CH, loc.len - cc * CH);
-        ws_load_rows(kr, p.k, tok0, ts, hq, nv, t);
-        ws_load_rows(qr, p.q, tok0, ts, hq, nv, t);
+        tok0 = loc.tok0 + (size_t)cc * CH;
+        nv = min(CH, loc.len - cc * CH);
+    };
+    // K rows and T diag(beta) of chunk cc
+    auto fetch_a = [&](WsIn& r, int cc) {
+        size_t tok0;
+        int nv;
+        rows_of(cc, tok0, nv);
+        ws_load_rows(r.kr, p.k, tok0, ts, hq, nv, t);
         const size_t blk = (size_t)(loc.chunk_base + cc) * p.h_v + h;
         const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const f16*>(p.tb16) + blk * (size_t)kTbHalfs);
-        tbr[0] = tb[t];
-        tbr[1] = tb[t < 128 ? 256 + t : t];   // (pieces 256..383; the rest load piece t again)
+        r.tbr[0] = tb[t];
+        r.tbr[1] = tb[t < 128 ? 256 + t : t];   // (pieces 256..383; the rest load piece t again)
+    };
+    // Q rows of chunk cc
+    auto fetch_b = [&](WsIn& r, int cc) {
+        size_t tok0;
+        int nv;
+        rows_of(cc, tok0, nv);
+        ws_load_rows(r.qr, p.q, tok0, ts, hq, nv, t);
     };
     // gate factors, loaded two chunks ahead of their staging
     auto gfetch = [&](int cc) {
@@ -984,15 +1012,15 @@ __device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
         return p.gf16[((size_t)(loc.chunk_base + cc) * p.h_v + h) * kGfFloats + t];
     };
     // K, K~^T (into kt[b], from the gate factors in gf[b]), Q and T diag(beta)
-    auto stage = [&](int b) {
+    auto stage = [&](int b, const WsIn& r) {
         // (the factors are read ahead of the writes: an LDS read waits for
         // every LDS access issued before it)
         const f32x4 kfac = *reinterpret_cast<const f32x4*>(sm.gf[b] + 2 * CH + 4 * ((t >> 4) & 15));
         __builtin_amdgcn_sched_barrier(0);
-        ws_put_rows(sm.k, kr, t);
-        ws_put_rows(sm.q, qr, t);
-        *reinterpret_cast<u32x4*>(sm.tb + 8 * t) = tbr[0];
-        if (t < 128) *reinterpret_cast<u32x4*>(sm.tb + 8 * (256 + t)) = tbr[1];
+        ws_put_rows(sm.k, r.kr, t);
+        ws_put_rows(sm.q, r.qr, t);
+        *reinterpret_cast<u32x4*>(sm.tb + 8 * t) = r.tbr[0];
+        if (t < 128) *reinterpret_cast<u32x4*>(sm.tb + 8 * (256 + t)) = r.tbr[1];
         const int pt = ws_pt(t);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -1000,7 +1028,7 @@ __device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
             f32x4 col;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const unsigned wv = kr[j][e >> 1];
+                const unsigned wv = r.kr[j][e >> 1];
                 col[j] = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16)) * kfac[j];
             }
             *reinterpret_cast<f16x4*>(sm.kt[b] + d * kWsRowT + (pt ^ tswz(d))) = __builtin_convertvector(col, f16x4);
@@ -1010,10 +1038,12 @@ __device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
     float gfr[2];
     sm.gf[0][t] = gfetch(c_lo);
     gfr[1] = gfetch(c_lo + 1);
-    fetch(c_lo);
+    fetch_a(R[0], c_lo);
+    fetch_b(R[0], c_lo);
     __syncthreads();   // (0)
-    stage(0);
-    fetch(c_lo + 1);
+    stage(0, R[0]);
+    fetch_a(R[1], c_lo + 1);
+    fetch_b(R[1], c_lo + 1);
     gfr[0] = gfetch(c_lo + 2);
     __syncthreads();   // (1)
     auto step = [&](int b, int cc) {
@@ -1034,6 +1064,8 @@ __device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) Pt[ib] = mmh(kf[ib], qw, Pt[ib]);
         }
+        // chunk cc + 2 into the set chunk cc left (staged in the previous step)
+        fetch_a(R[b], cc + 2);
         {
             // P[r][i] = scale 2^(gamma_r - gamma_i) (q_r . k_i), i <= r (gamma times log2 e)
             const int r = 16 * cw + c;
@@ -1050,8 +1082,8 @@ __device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
             }
         }
         __syncthreads();   // (2)
-        stage(b ^ 1);
-        fetch(cc + 2);
+        stage(b ^ 1, R[b ^ 1]);
+        fetch_b(R[b], cc + 2);
         gfr[b ^ 1] = gfetch(cc + 3);
         __syncthreads();   // (3)
     };
