@@ -32,7 +32,8 @@ class GdnDesc(ctypes.Structure):
                 ("n_seqs", ctypes.c_int32), ("host_cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
                 ("io_dtype", ctypes.c_int32), ("cp_mode", ctypes.c_int32),
                 ("lambda_", ctypes.c_float), ("warmup_chunks", ctypes.c_int32),
-                ("noise_floor", ctypes.c_float), ("n_cu", ctypes.c_int32), ("dv_split", ctypes.c_int32)]
+                ("noise_floor", ctypes.c_float), ("n_cu", ctypes.c_int32), ("dv_split", ctypes.c_int32),
+                ("cp_layout", ctypes.c_int32)]
 
 
 class GdnPlanInfo(ctypes.Structure):
@@ -42,7 +43,8 @@ class GdnPlanInfo(ctypes.Structure):
                 ("warmup_chunks", ctypes.c_int32), ("n_cu", ctypes.c_int32),
                 ("lambda_", ctypes.c_float), ("noise_floor", ctypes.c_float),
                 ("workspace_bytes", ctypes.c_size_t), ("combine_group", ctypes.c_int32),
-                ("combine_groups", ctypes.c_int32), ("dv_split", ctypes.c_int32)]
+                ("combine_groups", ctypes.c_int32), ("dv_split", ctypes.c_int32),
+                ("cp_layout", ctypes.c_int32)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}
@@ -117,7 +119,7 @@ def _check(lib, status):
 
 
 def make_desc(B, T, h_qk, h_v, d_k=128, d_v=128, io_dtype=GDN_BF16, cu_seqlens=None,
-              cp_mode="auto", lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0, dv_split=0):
+              cp_mode="auto", lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0, dv_split=0, cp_layout=0):
     """Descriptor plus the host cu_seqlens buffer it points to (keep both alive)."""
     d = GdnDesc()
     d.B, d.T, d.h_qk, d.h_v, d.d_k, d.d_v = B, T, h_qk, h_v, d_k, d_v
@@ -133,6 +135,7 @@ def make_desc(B, T, h_qk, h_v, d_k=128, d_v=128, io_dtype=GDN_BF16, cu_seqlens=N
     d.cp_mode = CP_MODES[cp_mode] if isinstance(cp_mode, str) else int(cp_mode)
     d.lambda_, d.warmup_chunks, d.noise_floor, d.n_cu = lam, warmup_chunks, noise_floor, n_cu
     d.dv_split = dv_split
+    d.cp_layout = cp_layout
     return d, host_cu
 
 
@@ -144,10 +147,10 @@ def plan_desc(desc):
 
 
 def plan(B, T, h_qk, h_v, d_k=128, d_v=128, io_dtype=GDN_BF16, cu_seqlens=None, cp_mode="auto",
-         lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0, dv_split=0):
+         lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0, dv_split=0, cp_layout=0):
     """Host-only planning (n_cu=0 queries the current device)."""
     d, keep = make_desc(B, T, h_qk, h_v, d_k, d_v, io_dtype, cu_seqlens, cp_mode, lam, warmup_chunks,
-                        noise_floor, n_cu, dv_split)
+                        noise_floor, n_cu, dv_split, cp_layout)
     out = plan_desc(d)
     del keep
     return out
@@ -207,7 +210,7 @@ def _prepare(q, k, v, g, beta, cu_seqlens):
 
 def fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
         cu_seqlens=None, cp_mode="auto", lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0,
-        workspace=None, out=None, final_state=None, debug=False, dv_split=0):
+        workspace=None, out=None, final_state=None, debug=False, dv_split=0, cp_layout=0):
     """Gated DeltaNet chunked-prefill forward on the GPU.
 
     q, k: [B, T, h_qk, 128]; v: [B, T, h_v, 128] (bf16 or fp32, same dtype);
@@ -225,7 +228,7 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=Tru
     if initial_state is not None:
         _req(initial_state, "initial_state", torch.float32, dev, (n_seqs, h_v, d_k, d_v))
     desc, keep = make_desc(B, T, h_qk, h_v, d_k, d_v, io, cu_host, cp_mode, lam, warmup_chunks,
-                           noise_floor, n_cu, dv_split)
+                           noise_floor, n_cu, dv_split, cp_layout)
     lib = load_library()
     info = plan_desc(desc)
     if out is None:
@@ -259,7 +262,7 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=Tru
 
 def fwd_noalloc(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
                 cu_seqlens=None, cp_mode="auto", lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0,
-                out=None, final_state=None, dv_split=0):
+                out=None, final_state=None, dv_split=0, cp_layout=0):
     """``fwd`` through gdn_fwd_noalloc: the library's per-device scratch array
     serves as the workspace (descriptors needing more than
     NOALLOC_SCRATCH_BYTES raise). Calls that overlap on one device race."""
@@ -272,7 +275,7 @@ def fwd_noalloc(q, k, v, g, beta, scale=None, initial_state=None, output_final_s
     if initial_state is not None:
         _req(initial_state, "initial_state", torch.float32, dev, (n_seqs, h_v, d_k, d_v))
     desc, keep = make_desc(B, T, h_qk, h_v, d_k, d_v, io, cu_host, cp_mode, lam, warmup_chunks,
-                           noise_floor, n_cu, dv_split)
+                           noise_floor, n_cu, dv_split, cp_layout)
     lib = load_library()
     if out is None:
         out = torch.empty_like(v)

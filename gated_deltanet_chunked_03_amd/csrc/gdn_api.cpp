@@ -67,7 +67,7 @@ struct Plan {
     int n_seqs = 0;
     std::vector<int> len;       // tokens per sequence
     int n_chunks_total = 0, n_chunks_max = 0;
-    int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0, cp_order = 0;
+    int L = 1, n_segments = 0, P_max = 0, cp_on = 0, w = kDefaultWarmup, n_cu = 0, cp_order = 0, cp_split = 0;
     int s_dv = 1;                 // column blocks of d_v in the fused forward
     float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
     int comb_G = 0, comb_J = 0;   // grouped combine of the backward's forward re-run (0: one chain)
@@ -102,6 +102,8 @@ gdn_status validate_desc(const gdn_desc* d) {
     if (d->n_cu < 0) return fail(GDN_ERR_BAD_OPTION, "n_cu must be >= 0");
     if (d->dv_split != 0 && d->dv_split != 1 && d->dv_split != 2 && d->dv_split != 4)
         return fail(GDN_ERR_BAD_OPTION, "dv_split must be 0 (planner), 1, 2 or 4 (got %d)", d->dv_split);
+    if (d->cp_layout < 0 || d->cp_layout > 2)
+        return fail(GDN_ERR_BAD_OPTION, "cp_layout must be 0 (planner), 1 or 2 (got %d)", d->cp_layout);
     if (d->dv_split > 1 && d->io_dtype != GDN_BF16)
         return fail(GDN_ERR_BAD_OPTION, "dv_split > 1 needs bf16 inputs");
     if (d->dv_split > 1 && d->cp_mode != GDN_CP_AUTO && d->cp_mode != GDN_CP_OFF)
@@ -268,9 +270,17 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl, bool column_split = true) {
     // with the share of exact heads the pages report (most heads forget fast:
     // 30 % exact, to the nearest), they fit in about one round (2 E <= 5/4 CUs);
     // with more, head-major order measured faster.
+    // With bf16 inputs (cp_layout 0) an exact boundary's H and M run in two
+    // 8-wave workgroups when there are no more boundary pairs than CUs (each chain
+    // wave then has a SIMD's matrix pipe to itself: TP8 CP preprocessing
+    // 40 -> 32 us), else in one 12-wave workgroup sharing the staged chunks
+    // (fewer workgroups: TP2 95 -> 69 us, TP1 66 -> 46 us, measured).
     if (P.cp_on) {
         const long long pairs = (long long)(P.n_segments - P.n_seqs) * d->h_v, est = (3 * pairs + 5) / 10;
         P.cp_order = 4 * (2 * est) <= 5LL * P.n_cu ? 1 : 0;
+        // (cp_mode EXACT: every pair takes two workgroups)
+        const long long wgs = (long long)P.n_segments * d->h_v * (d->cp_mode == GDN_CP_EXACT ? 2 : 1);
+        P.cp_split = d->cp_layout == 2 || (d->cp_layout == 0 && wgs <= P.n_cu) ? 1 : 0;
     }
     {
         // The forward: an 8 KiB scratch line (stores of rows past a sequence's
@@ -363,6 +373,7 @@ gdn::Params base_params(const gdn_desc* d, const Plan& P) {
     p.n_segments = P.n_segments;
     p.n_chunks = P.n_chunks_total;
     p.cp_order = P.cp_order;
+    p.cp_split = P.cp_split;
     p.log_eps = std::log(P.eps);
     p.t_stride = (int64_t)gdn::kChunk * gdn::kChunk;
     p.gb_stride = 2 * gdn::kChunk;
@@ -421,10 +432,11 @@ bool log_enabled() {
 void log_plan(const gdn_desc* d, const Plan& P) {
     std::fprintf(stderr,
                  "[gdn] fwd B=%d T=%d h_qk=%d h_v=%d io=%s cp_mode=%d: chunks=%d (max %d) cp_on=%d L=%d "
-                 "segments=%d (max %d per sequence) dv_split=%d w=%d eps=%g lambda=%g n_cu=%d workspace=%zu\n",
+                 "segments=%d (max %d per sequence) dv_split=%d w=%d eps=%g lambda=%g n_cu=%d cp_order=%d "
+                 "cp_split=%d workspace=%zu\n",
                  d->B, d->T, d->h_qk, d->h_v, d->io_dtype == GDN_BF16 ? "bf16" : "f32", d->cp_mode,
                  P.n_chunks_total, P.n_chunks_max, P.cp_on, P.L, P.n_segments, P.P_max, P.s_dv, P.w,
-                 (double)P.eps, (double)P.lambda, P.n_cu, P.ws_bytes);
+                 (double)P.eps, (double)P.lambda, P.n_cu, P.cp_order, P.cp_split, P.ws_bytes);
 }
 
 gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* g,
@@ -687,6 +699,7 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->combine_group = P.comb_G;
     out->combine_groups = P.comb_J;
     out->dv_split = P.s_dv;
+    out->cp_layout = P.cp_on && desc->io_dtype == GDN_BF16 ? (P.cp_split ? 2 : 1) : 0;
     g_last_error.clear();
     return GDN_OK;
 }

@@ -1143,18 +1143,20 @@ __global__ __launch_bounds__(64 * (NSW + 4)) void k_fwd_ws(Params p) {
 }
 
 // ----------------------------------------------------------------------------
-// CP preprocessing with specialised waves (bf16 inputs): one 12-wave
-// workgroup per boundary pair. Waves 0-3 run the state (each owning 32 d_v
-// columns): from zero over the previous segment (H of an exact boundary) or
-// over the warm-up window (from zero, or from the initial state where the
-// window starts at the sequence start). Waves 4-7 run the map of an exact
-// boundary's previous segment from the identity with V = 0 (M, 32 columns
-// each), on the same staged chunks. Waves 8-11 stage K, K~^T, V,
-// T diag(beta) and the gate factors of every chunk; all of them are
-// double-buffered in LDS, so a chunk step needs one barrier and the state
-// and map waves issue no global loads. The chunk step of a state or map
-// wave is the forward's without the output: Y = K S, S <- e^gamma_C S,
-// Y = V - e^gamma Y (V = 0 for M), V' = T diag(beta) Y, S += K~^T V'.
+// CP preprocessing with specialised waves (bf16 inputs). Four state waves
+// (each owning 32 d_v columns) run the state: from zero over the previous
+// segment (H of an exact boundary) or over the warm-up window (from zero, or
+// from the initial state where the window starts at the sequence start).
+// Four map waves run the map of an exact boundary's previous segment from
+// the identity with V = 0 (M, 32 columns each). Four staging waves stage K,
+// K~^T, V, T diag(beta) and the gate factors of every chunk, all
+// double-buffered in LDS, so a chunk step needs one barrier and the chain
+// waves issue no global loads. Two layouts: the state and map waves of an
+// exact boundary in one 12-wave workgroup on the same staged chunks, or
+// (SPLIT) in two 8-wave workgroups, one chain wave per SIMD with the whole
+// register file's share. The chunk step of a state or map wave is the
+// forward's without the output: Y = K S, S <- e^gamma_C S, Y = V - e^gamma Y
+// (V = 0 for M), V' = T diag(beta) Y, S += K~^T V'.
 struct __attribute__((aligned(16))) SmemCP {
     // (the small buffers first: more of the operand reads reach their
     // addresses through the LDS instructions' 16-bit offsets)
@@ -1168,8 +1170,9 @@ static_assert(sizeof(f16) * 2 * CH * kWsRow >= sizeof(f16) * DK * LMI, "map imag
 constexpr int kCpWaves = 12;
 
 // State (WANT_V) or map wave over chunks [c_lo, c_hi), 32 columns from col:
-// S[i][n] is the tile of rows 16 i + 4 g + e, column col + 16 n + c.
-template <bool WANT_V>
+// S[i][n] is the tile of rows 16 i + 4 g + e, column col + 16 n + c. WIDE:
+// the register budget of an 8-wave workgroup (operand reads run ahead).
+template <bool WANT_V, bool WIDE>
 __device__ void cp_state(SmemCP& sm, int c_lo, int c_hi, int col, f32x4 S[8][2]) {
     constexpr int NC = 2;
     const int lane = lane_id(), c = lane & 15, g = lane >> 4;
@@ -1204,7 +1207,7 @@ __device__ void cp_state(SmemCP& sm, int c_lo, int c_hi, int col, f32x4 S[8][2])
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int n = 0; n < NC; ++n) Y[m][n] = mmh(kf[m], sb[n], Y[m][n]);
-            __builtin_amdgcn_sched_barrier(0);   // (bounds the operand reads in flight)
+            if constexpr (!WIDE) __builtin_amdgcn_sched_barrier(0);   // (bounds the operand reads in flight)
         }
         const float ec = gf[3 * CH];
 #pragma unroll
@@ -1258,7 +1261,7 @@ __device__ void cp_state(SmemCP& sm, int c_lo, int c_hi, int col, f32x4 S[8][2])
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int n = 0; n < NC; ++n) S[i][n] = mmh(ktf[i], Vb[j][n], S[i][n]);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!WIDE) __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();   // the next chunk staged; this one's buffers free
     };
@@ -1272,36 +1275,44 @@ __device__ void cp_state(SmemCP& sm, int c_lo, int c_hi, int col, f32x4 S[8][2])
 
 // Staging wave cw of the CP preprocessing (threads t = 64 cw + lane): during
 // the step of chunk n it stages chunk n + 1 into the other buffers and loads
-// chunk n + 2 (past the last chunk, the last one again: staged, never read).
-__device__ void cp_stage(SmemCP& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw) {
-    const int t = 64 * cw + lane_id();
-    const int hq = h / p.group;
-    const size_t ts = (size_t)p.h_qk * DK, tsv = (size_t)p.h_v * DK;
+// chunk n + 3 into the register set chunk n + 1 left (two sets: the loads have
+// two steps to land; past the last chunk, the last one again: staged, never
+// read). want_v: stage V (no map-only workgroup reads it).
+struct CpIn {
     u32x4 kr[4], vr[4], tbr[2];
     float gfr;
     f32x4 kfac;   // e^(gamma_C - gamma) of this thread's four tokens
-    auto fetch = [&](int cc) {
+};
+__device__ void cp_stage(SmemCP& sm, const Params& p, const SegLoc& loc, int h, int c_lo, int c_hi, int cw,
+                         bool want_v) {
+    const int t = 64 * cw + lane_id();
+    const int hq = h / p.group;
+    const size_t ts = (size_t)p.h_qk * DK, tsv = (size_t)p.h_v * DK;
+    CpIn R[2];
+    auto fetch = [&](CpIn& r, int cc) {
         cc = min(cc, c_hi - 1);
         const size_t tok0 = loc.tok0 + (size_t)cc * CH;
         const int nv = min(CH, loc.len - cc * CH);
-        ws_load_rows(kr, p.k, tok0, ts, hq, nv, t);
-        ws_load_rows(vr, p.v, tok0, tsv, h, nv, t);
+        ws_load_rows(r.kr, p.k, tok0, ts, hq, nv, t);
+        if (want_v) ws_load_rows(r.vr, p.v, tok0, tsv, h, nv, t);
         const size_t blk = (size_t)(loc.chunk_base + cc) * p.h_v + h;
         const u32x4* tb = reinterpret_cast<const u32x4*>(static_cast<const f16*>(p.tb16) + blk * (size_t)kTbHalfs);
-        tbr[0] = tb[t];
-        tbr[1] = tb[t < 128 ? 256 + t : t];   // (pieces 256..383; the rest load piece t again)
+        r.tbr[0] = tb[t];
+        r.tbr[1] = tb[t < 128 ? 256 + t : t];   // (pieces 256..383; the rest load piece t again)
         const float* gfb = p.gf16 + blk * (size_t)kGfFloats;
-        gfr = gfb[t];
-        kfac = *reinterpret_cast<const f32x4*>(gfb + 2 * CH + 4 * ((t >> 4) & 15));
+        r.gfr = gfb[t];
+        r.kfac = *reinterpret_cast<const f32x4*>(gfb + 2 * CH + 4 * ((t >> 4) & 15));
     };
-    auto stage = [&](int b) {
-        ws_put_rows(sm.k[b], kr, t);
+    auto stage = [&](int b, const CpIn& r) {
+        ws_put_rows(sm.k[b], r.kr, t);
+        if (want_v) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4*>(sm.v[b] + (4 * ((t >> 4) & 15) + j) * kWsRow + 8 * (t & 15)) = vr[j];
-        *reinterpret_cast<u32x4*>(sm.tb[b] + 8 * t) = tbr[0];
-        if (t < 128) *reinterpret_cast<u32x4*>(sm.tb[b] + 8 * (256 + t)) = tbr[1];
-        sm.gf[b][t] = gfr;
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x4*>(sm.v[b] + (4 * ((t >> 4) & 15) + j) * kWsRow + 8 * (t & 15)) = r.vr[j];
+        }
+        *reinterpret_cast<u32x4*>(sm.tb[b] + 8 * t) = r.tbr[0];
+        if (t < 128) *reinterpret_cast<u32x4*>(sm.tb[b] + 8 * (256 + t)) = r.tbr[1];
+        sm.gf[b][t] = r.gfr;
         const int pt = ws_pt(t);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -1309,40 +1320,46 @@ __device__ void cp_stage(SmemCP& sm, const Params& p, const SegLoc& loc, int h, 
             f32x4 col;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const unsigned wv = kr[j][e >> 1];
-                col[j] = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16)) * kfac[j];
+                const unsigned wv = r.kr[j][e >> 1];
+                col[j] = __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16)) * r.kfac[j];
             }
             *reinterpret_cast<f16x4*>(sm.kt[b] + d * kWsRowT + (pt ^ tswz(d))) = __builtin_convertvector(col, f16x4);
         }
     };
-    fetch(c_lo);
-    stage(0);
-    fetch(c_lo + 1);
+    fetch(R[0], c_lo);
+    fetch(R[1], c_lo + 1);
+    stage(0, R[0]);
+    fetch(R[0], c_lo + 2);
     __syncthreads();   // the first chunk staged
     int cc = c_lo;
     for (; cc + 1 < c_hi; cc += 2) {
-        stage(1);
-        fetch(cc + 2);
+        stage(1, R[1]);
+        fetch(R[1], cc + 3);
         __syncthreads();
-        stage(0);
-        fetch(cc + 3);
+        stage(0, R[0]);
+        fetch(R[0], cc + 4);
         __syncthreads();
     }
     if (cc < c_hi) {
-        stage(1);
+        stage(1, R[1]);
         __syncthreads();
     }
 }
 
-// One workgroup per boundary pair (order as planned, see cp_pick). Output:
-// exact boundary s (between segments s - 1 and s): H_{s-1} (tile order) and,
-// where it matters (s > 1 or an initial state), M_{s-1} as the combine's fp16
-// A-operand image; warm-up boundary: its state (tile order).
-__global__ __launch_bounds__(64 * kCpWaves) void k_cp_ws(Params p) {
+// One workgroup per boundary pair (order as planned, see cp_pick), or with
+// SPLIT one per part: an exact boundary's H and M then run in two 8-wave
+// workgroups (four state or map waves, four staging waves), each with a
+// SIMD's matrix pipe to one chain wave. Output: exact boundary s (between
+// segments s - 1 and s): H_{s-1} (tile order) and, where it matters (s > 1
+// or an initial state), M_{s-1} as the combine's fp16 A-operand image;
+// warm-up boundary: its state (tile order).
+template <bool SPLIT>
+__global__ __launch_bounds__(64 * (SPLIT ? 8 : kCpWaves)) void k_cp_ws(Params p) {
+    constexpr int NW = SPLIT ? 8 : kCpWaves;
     __shared__ SmemCP sm;
-    __shared__ int rank_red[2 * kCpWaves + 4];
+    __shared__ int rank_red[2 * NW + 4];
     int part;
-    const int q = cp_pick<kCpWaves, 1>(p, (int)blockIdx.x, rank_red, part);
+    const int q = cp_pick<NW, SPLIT ? 2 : 1>(p, (int)blockIdx.x, rank_red, part);
     if (q < 0) return;
     const int slot = q / p.h_v, h = q % p.h_v;
     const SegLoc loc = locate_segment(p, slot);
@@ -1352,9 +1369,14 @@ __global__ __launch_bounds__(64 * kCpWaves) void k_cp_ws(Params p) {
     const int a = loc.s * p.L;   // first chunk of segment s
     const int c_lo = cls ? a - wq : a - p.L, c_hi = a;
     const bool want_m = cls == 0 && (loc.s > 1 || p.s_init);
+    if (SPLIT && part == 1 && !want_m) return;
+    // waves: [0, 4) state (or, with SPLIT and part 1, map); without SPLIT
+    // [4, 8) map; the last four staging
+    const bool run_h = !SPLIT || part == 0, run_m = SPLIT ? part == 1 : want_m;
     const int w = wave_id(), lane = lane_id(), c = lane & 15, g = lane >> 4;
-    if (w < 4) {
-        const int col = 32 * w;
+    const int role = w >= NW - 4 ? 2 : (SPLIT ? (run_h ? 0 : 1) : (w < 4 ? 0 : 1));
+    if (role == 0) {
+        const int col = 32 * (w & 3);
         f32x4 S[8][2];
         const bool from_init = cls && c_lo == 0 && p.s_init;
         const float* s0 = from_init ? p.s_init + tiles_off(loc.seq, p.h_v, h) : nullptr;
@@ -1364,7 +1386,7 @@ __global__ __launch_bounds__(64 * kCpWaves) void k_cp_ws(Params p) {
             for (int n = 0; n < 2; ++n)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[i][n][e] = s0 ? s0[(16 * i + 4 * g + e) * DK + col + 16 * n + c] : 0.f;
-        cp_state<true>(sm, c_lo, c_hi, col, S);
+        cp_state<true, SPLIT>(sm, c_lo, c_hi, col, S);
         float* dst = cls ? p.seg_state + tiles_off(loc.seg_base + loc.s, p.h_v, h)
                          : p.seg_H + tiles_off(loc.seg_base + loc.s - 1, p.h_v, h);
 #pragma unroll
@@ -1372,12 +1394,12 @@ __global__ __launch_bounds__(64 * kCpWaves) void k_cp_ws(Params p) {
 #pragma unroll
             for (int n = 0; n < 2; ++n)
                 *reinterpret_cast<f32x4*>(dst + ((i * 8 + (col >> 4) + n) * 64 + lane) * 4) = S[i][n];
-    } else if (w < 8) {
-        if (!want_m) {
+    } else if (role == 1) {
+        if (!run_m) {
             for (int k = c_lo; k <= c_hi; ++k) __syncthreads();   // (the chain's barriers)
             return;
         }
-        const int wm = w - 4, col = 32 * wm;
+        const int wm = w & 3, col = 32 * wm;
         f32x4 S[8][2];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -1385,7 +1407,7 @@ __global__ __launch_bounds__(64 * kCpWaves) void k_cp_ws(Params p) {
             for (int n = 0; n < 2; ++n)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[i][n][e] = (16 * i + 4 * g + e == col + 16 * n + c) ? 1.f : 0.f;
-        cp_state<false>(sm, c_lo, c_hi, col, S);
+        cp_state<false, SPLIT>(sm, c_lo, c_hi, col, S);
         // M -> the combine's A-operand image: fragment F = 4 rt + j holds, in
         // lane (g, c), row 16 rt + c at the kp positions 32 j + 8 g .. + 8 --
         // columns of block j, which are this wave's when j = wm. Staged through
@@ -1407,7 +1429,7 @@ __global__ __launch_bounds__(64 * kCpWaves) void k_cp_ws(Params p) {
             *reinterpret_cast<f16x8*>(dst + ((size_t)(4 * rt + wm) * 64 + lane) * 8) =
                 *reinterpret_cast<const f16x8*>(img + (16 * rt + c) * LMI + col + 8 * g);
     } else {
-        cp_stage(sm, p, loc, h, c_lo, c_hi, w - 8);
+        cp_stage(sm, p, loc, h, c_lo, c_hi, w - (NW - 4), run_h);
     }
 }
 
@@ -1431,8 +1453,12 @@ int launched16() { return (int)hipGetLastError(); }
 
 int launch_cp_prep16(const Params& p, int io, void* stream) {
     if (io == kIoBf16) {
-        hipLaunchKernelGGL(k_cp_ws, dim3((unsigned)(p.n_segments * p.h_v)), dim3(64 * kCpWaves), 0,
-                           (hipStream_t)stream, p);
+        if (p.cp_split)
+            hipLaunchKernelGGL(k_cp_ws<true>, dim3((unsigned)(2 * p.n_segments * p.h_v)), dim3(64 * 8), 0,
+                               (hipStream_t)stream, p);
+        else
+            hipLaunchKernelGGL(k_cp_ws<false>, dim3((unsigned)(p.n_segments * p.h_v)), dim3(64 * kCpWaves), 0,
+                               (hipStream_t)stream, p);
     } else {
         hipLaunchKernelGGL(k_cp_prep16<float>, dim3((unsigned)(2 * p.n_segments * p.h_v)), dim3(NT8), 0,
                            (hipStream_t)stream, p);

@@ -63,6 +63,7 @@ struct Params {
     int32_t n_segments;
     int32_t n_chunks;
     int32_t cp_order;         // k_cp_prep work order: 1 exact boundaries first, 0 head-major
+    int32_t cp_split;         // bf16 CP preprocessing: 1 H and M of an exact boundary in two workgroups
     float log_eps;            // log(noise floor)
     float scale;
 };

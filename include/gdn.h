@@ -83,6 +83,12 @@ typedef struct {
     int32_t dv_split;                  /* column blocks of d_v the forward runs in parallel: 1, 2 or 4
                                           (bf16 inputs, without a context-parallel split: cp_mode
                                           AUTO or OFF); 0 = the planner decides (see gdn_plan) */
+    int32_t cp_layout;                 /* workgroups of the boundary preprocessing (bf16 inputs; fp32
+                                          inputs have one layout and ignore it): 1 = one per boundary,
+                                          an exact boundary's H and M chains sharing its staged chunks;
+                                          2 = H and M of an exact boundary in two workgroups; 0 = the
+                                          planner decides (2 when every boundary of the plan fits on
+                                          the CUs at once, else 1) */
 } gdn_desc;
 
 /* Result of planning (host-only arithmetic on the descriptor). */
@@ -102,6 +108,8 @@ typedef struct {
     int32_t combine_group;   /* boundaries per group of the grouped combine (0: one chain) */
     int32_t combine_groups;  /* groups of the longest sequence (0: one chain) */
     int32_t dv_split;        /* column blocks of d_v in the forward (1: none) */
+    int32_t cp_layout;       /* boundary preprocessing layout run (1 or 2, as in gdn_desc); 0 without
+                                a context-parallel split or with fp32 inputs */
 } gdn_plan_info;
 
 /* Plan a forward (section "Gate-Driven Automatic Intra-Card Context

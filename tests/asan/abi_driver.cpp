@@ -71,6 +71,8 @@ int main() {
         CHECK(gdn_plan(&d, &info) == GDN_ERR_BAD_OPTION);
         d = make(1, 64, 2, 8); d.dv_split = 3;
         CHECK(gdn_plan(&d, &info) == GDN_ERR_BAD_OPTION);
+        d = make(1, 64, 2, 8); d.cp_layout = 3;
+        CHECK(gdn_plan(&d, &info) == GDN_ERR_BAD_OPTION);
         CHECK(gdn_plan(nullptr, &info) == GDN_ERR_NULL_ARG);
         CHECK(gdn_fwd_workspace_bytes(nullptr) == 0);
     }

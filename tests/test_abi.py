@@ -193,6 +193,8 @@ def call_fwd(d, q=0x1000, k=0x1000, v=0x1000, g=0x1000, beta=0x1000, scale=0.1, 
     (dict(dv_split=3), "GDN_ERR_BAD_OPTION"),
     (dict(dv_split=2, io_dtype=1), "GDN_ERR_BAD_OPTION"),
     (dict(dv_split=4, cp_mode="exact"), "GDN_ERR_BAD_OPTION"),
+    (dict(cp_layout=3), "GDN_ERR_BAD_OPTION"),
+    (dict(cp_layout=-1), "GDN_ERR_BAD_OPTION"),
 ])
 def test_bad_descriptor(kw, status):
     d, keep = desc(**kw)
@@ -342,6 +344,23 @@ def test_python_binding_rejects_host_tensors():
     g = torch.zeros(1, 64, 1)
     with pytest.raises(ValueError):
         B.fwd(x, x, x, g, g)
+
+
+def test_plan_cp_layout():
+    """Boundary preprocessing layout: the planner takes two workgroups per
+    exact boundary (2) when every boundary pair fits on the CUs at once (TP8:
+    32 x 8 on 256 CUs; with cp_mode EXACT every pair counts twice), else one
+    (1: TP2, TP1, long); a forced layout is kept; 0 without a split or with
+    fp32 inputs."""
+    assert B.plan(1, 32768, 2, 8, n_cu=256)["cp_layout"] == 2
+    for args in [(1, 32768, 8, 24), (1, 32768, 16, 16), (1, 262144, 2, 8)]:
+        assert B.plan(*args, n_cu=256)["cp_layout"] == 1, args
+    for lay in (1, 2):
+        assert B.plan(1, 32768, 2, 8, n_cu=256, cp_layout=lay)["cp_layout"] == lay
+        assert B.plan(1, 32768, 16, 16, n_cu=256, cp_layout=lay)["cp_layout"] == lay
+    assert B.plan(1, 32768, 2, 8, n_cu=256, cp_mode="exact")["cp_layout"] == 1   # 2 x 256 workgroups
+    assert B.plan(1, 32768, 2, 8, n_cu=256, cp_mode="off")["cp_layout"] == 0
+    assert B.plan(1, 32768, 2, 8, n_cu=256, io_dtype=B.GDN_F32)["cp_layout"] == 0
 
 
 def test_plan_column_split():

@@ -68,20 +68,21 @@ def test_fwd_single_segment(io, T, h_qk, h_v):
     print(f"[fwd off {io} T={T} {h_qk}/{h_v}] o {mx:.2e}/{mean:.2e} S {smx:.2e}/{smean:.2e}")
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("io,layout", [("bf16", 1), ("bf16", 2), ("f32", 0)])
 @pytest.mark.parametrize("mode", ["exact", "warmup", "auto"])
-def test_fwd_context_parallel(mode, io):
+def test_fwd_context_parallel(mode, io, layout):
     """Segments of L chunks with exact or warm-up boundary states: outputs
     within tolerance and the segment initial states close to the true states
     (exact: to fp32 accuracy; warm-up on fast heads: <= 1e-3 relative), for
-    bf16 and fp32 inputs."""
+    bf16 inputs in both boundary preprocessing layouts (H and M of an exact
+    boundary in one workgroup or in two) and for fp32 inputs."""
     import torch
     T, L = 64 * 40 + 5, 4
     inp = make_inputs(1, T, 2, 8, seed=30, gate="mixed", init_std=0.05, io_dtype=io)
-    o, S, info = _run(inp, cp_mode=mode, n_cu=32, lam=0.6, debug=True)
+    o, S, info = _run(inp, cp_mode=mode, n_cu=32, lam=0.6, debug=True, cp_layout=layout)
     plan = info["plan"]
-    print(f"[cp {mode} {io}] plan L={plan['L']} P={plan['P_max']} segs={plan['n_segments']}")
-    assert plan["cp_on"] == 1 and plan["L"] == L
+    print(f"[cp {mode} {io} layout {layout}] plan L={plan['L']} P={plan['P_max']} segs={plan['n_segments']}")
+    assert plan["cp_on"] == 1 and plan["L"] == L and plan["cp_layout"] == layout
     o_ref, S_ref, snaps = oracle_run(inp, snap_stride=64 * L, n_snap=plan["P_max"])
     seg = info["seg_state"].cpu().numpy()
     path = info["path"].cpu().numpy()
@@ -104,19 +105,21 @@ def test_fwd_context_parallel(mode, io):
         assert_within_tolerance(_o_np(o, inp)[:, fast], o_ref[:, fast])
 
 
-def test_varlen_with_initial_state():
+@pytest.mark.parametrize("layout", [1, 2])
+def test_varlen_with_initial_state(layout):
     """Packed sequences (including an empty one and a one-token one) with
-    per-sequence initial states equal separate oracle runs."""
+    per-sequence initial states equal separate oracle runs (both boundary
+    preprocessing layouts)."""
     cu = [0, 700, 700, 701, 64 * 20 + 3, 64 * 20 + 3 + 130]
     T = cu[-1]
     inp = make_inputs(1, T, 1, 4, seed=40, gate="mixed", cu_seqlens=cu, init_std=0.1)
     for mode in ("off", "auto", "exact"):
-        o, S = _run(inp, cp_mode=mode, n_cu=64, lam=0.5, warmup_chunks=2)
+        o, S = _run(inp, cp_mode=mode, n_cu=64, lam=0.5, warmup_chunks=2, cp_layout=layout)
         o_ref, S_ref, _ = oracle_run(inp)
         mx, mean = assert_within_tolerance(_o_np(o, inp), o_ref)
         assert_within_tolerance(S.cpu().numpy(), S_ref, "final_state", STATE_MAX_TOL, STATE_MEAN_TOL)
         np.testing.assert_allclose(S.cpu().numpy()[1], inp.initial_state[1], rtol=0, atol=0)
-        print(f"[varlen {mode}] o {mx:.2e}/{mean:.2e}")
+        print(f"[varlen {mode} layout {layout}] o {mx:.2e}/{mean:.2e}")
 
 
 def test_deterministic_rerun():
