@@ -90,12 +90,14 @@ def test_bwd_varlen_auto_cp():
     np.testing.assert_array_equal(got["d_initial"][1], d_fin[1])
 
 
-@pytest.mark.parametrize("config", ["tp8"])
+@pytest.mark.parametrize("config", ["tp8", "tp2", "tp1", "long"])
 def test_bwd_full_size(config):
-    """The benchmark's workload at full size (B = 1, T = 32768; AutoCP splits it
-    into 32 segments per head, so the segment maps, the linking pass and the
-    re-run all take part): every gradient element against the fp64 backward
-    oracle (about 7 s on 8 host threads)."""
+    """The workloads at full size (T = 32768 at the TP8, TP2 and TP1 head
+    counts; T = 262144 with an initial state; AutoCP splits every one into
+    segments, so the segment maps, the linking pass and the re-run all take
+    part): every gradient element against the fp64 backward oracle (about 7 s
+    per 2.6e5 head-tokens on 8 host threads: TP8 7 s, TP2 21 s, TP1 14 s,
+    long 56 s)."""
     from gated_deltanet_chunked_03_amd.synth import config_inputs
     inp = config_inputs(config)
     print(f"\n[bwd/full/{config}] T={inp.T} h_qk={inp.h_qk} h_v={inp.h_v}", flush=True)
