@@ -1,4 +1,7 @@
-"""Build the HIP library ``_build/libgdn.so`` in-tree with hipcc for gfx950.
+"""Build the HIP library ``_build/libgdn.so`` in-tree with hipcc for gfx950,
+and beside it ``_build/libgdn_poison.so``: the same sources with LDS poisoning
+(every kernel first fills its shared memory with NaN words; a debug build that
+the GPU tests compare with the normal one).
 
     python -m gated_deltanet_chunked_03_amd.build
 """
@@ -13,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(BUILD, "libgdn.so")
+LIB_POISON = os.path.join(BUILD, "libgdn_poison.so")
 SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_fwd16.hip"),
            os.path.join(CSRC, "gdn_bwd.hip"), os.path.join(CSRC, "gdn_noalloc.hip"),
            os.path.join(CSRC, "gdn_api.cpp")]
@@ -29,11 +33,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into the in-tree shared library (always recompiles)."""
-    os.makedirs(BUILD, exist_ok=True)
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def _compile(target: str, extra: list, verbose: bool) -> None:
+    tmp = target + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
@@ -41,7 +43,18 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{out}")
     if verbose and out.strip():
         print(out, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, target)
+
+
+def build(verbose: bool = False, poison: bool = True) -> str:
+    """Compile every source into the in-tree shared library (always recompiles),
+    and the LDS-poisoning debug build beside it (poison=True)."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(LIB, [])] + ([(LIB_POISON, ["-DGDN_LDS_POISON"])] if poison else [])
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        for f in [ex.submit(_compile, t, e, verbose) for t, e in jobs]:
+            f.result()
     return LIB
 
 

@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
+#include "gdn_poison.h"
 
 namespace gdn {
 namespace {
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
     __shared__ bf16 kb[CH][LKB], qb[CH][LKB];
     __shared__ float am[CH][LM], tm[CH][LM];
     __shared__ float gam[CH], bet[CH];
+    GDN_LDS_POISON_ALL(kb, qb, am, tm, gam, bet);
     // P takes Q's tile once Q K^T is formed (same size: 64 x 136 bf16 = 64 x 68 fp32)
     float (*pmat)[LM] = reinterpret_cast<float (*)[LM]>(&qb[0][0]);
     static_assert(sizeof(qb) == CH * LM * sizeof(float), "P reuses the Q tile");

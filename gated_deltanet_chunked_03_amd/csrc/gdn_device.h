@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
+#include "gdn_poison.h"
 
 namespace gdn {
 namespace {

@@ -592,6 +592,7 @@ template <typename IO>
 __global__ __launch_bounds__(NT8) void k_cp_prep16(Params p) {
     __shared__ Smem16<IO, false> sm;
     __shared__ int rank_red[2 * NW8 + 4];
+    GDN_LDS_POISON_ALL(sm, rank_red);
     int part;
     const int q = cp_pick<NW8, 2>(p, (int)blockIdx.x, rank_red, part);
     if (q < 0) return;
@@ -613,6 +614,7 @@ constexpr int NTC = 256;
 __global__ __launch_bounds__(NTC) void k_combine16(Params p) {
     __shared__ int flags[kMaxSegsPerSeq];
     __shared__ __attribute__((aligned(16))) f16 xb[2][4 * 64 * 8];   // the state tile as B operands, per k step
+    GDN_LDS_POISON_ALL(flags, xb);
     const int u = blockIdx.x & 7, seq = blockIdx.x >> 3, h = blockIdx.y;
     if (seq >= p.n_seqs) return;
     int P, seg_base;
@@ -711,6 +713,7 @@ __global__ __launch_bounds__(NTC) void k_combine16(Params p) {
 template <typename IO>
 __global__ __launch_bounds__(NT8) void k_fwd16(Params p) {
     __shared__ Smem16<IO, true> sm;
+    GDN_LDS_POISON_ALL(sm);
     const int h = blockIdx.y;
     const SegLoc loc = locate_segment(p, blockIdx.x);
     if (loc.seq < 0) return;
@@ -1102,6 +1105,7 @@ __device__ void ws_stage(SmemWS& sm, const Params& p, const SegLoc& loc, int h, 
 template <int NSW, int NC>
 __global__ __launch_bounds__(64 * (NSW + 4)) void k_fwd_ws(Params p) {
     __shared__ SmemWS sm;
+    GDN_LDS_POISON_ALL(sm);
     const int h = blockIdx.y, w = wave_id();
     const SegLoc loc = locate_segment(p, blockIdx.x);
     if (loc.seq < 0) return;
@@ -1358,6 +1362,7 @@ __global__ __launch_bounds__(64 * (SPLIT ? 8 : kCpWaves)) void k_cp_ws(Params p)
     constexpr int NW = SPLIT ? 8 : kCpWaves;
     __shared__ SmemCP sm;
     __shared__ int rank_red[2 * NW + 4];
+    GDN_LDS_POISON_ALL(sm, rank_red);
     int part;
     const int q = cp_pick<NW, SPLIT ? 2 : 1>(p, (int)blockIdx.x, rank_red, part);
     if (q < 0) return;

@@ -316,6 +316,7 @@ __device__ void classify_boundary(const Params& p, int seq, int N, int a, int h,
 template <typename IO, bool F16>
 __global__ __launch_bounds__(64 * kPrepWaves) void k_prep(Params p) {
     __shared__ PrepSmem sm_all[kPrepWaves];
+    GDN_LDS_POISON_ALL(sm_all);
     PrepSmem& sm = sm_all[wave_id()];
     const int lane = lane_id();
     const long long n_items = (long long)p.n_chunks * p.h_v;
@@ -982,6 +983,7 @@ template <typename IO>
 __global__ __launch_bounds__(NTHR_CH) void k_wu(Params p) {
     constexpr bool EX = Io<IO>::kExact;
     __shared__ ChainSmem<EX> sm;
+    GDN_LDS_POISON_ALL(sm);
     const int h = blockIdx.y, hq = h / p.group;
     int seq, c, len;
     size_t tok_s;
@@ -1172,6 +1174,7 @@ template <typename IO>
 __global__ __launch_bounds__(NTHR_CH) void k_cp_prep(Params p) {
     __shared__ ChainSmem<Io<IO>::kExact> sm;
     __shared__ int rank_red[2 * NW_CH + 4];
+    GDN_LDS_POISON_ALL(sm, rank_red);
     const int i = (int)blockIdx.x;
     if (!p.cp_order) {   // head-major order
         cp_prep_item<IO>(p, sm, (i % (2 * p.n_segments)) >> 1, i & 1, i / (2 * p.n_segments));
@@ -1263,6 +1266,7 @@ template <int MODE>
 __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
     __shared__ __attribute__((aligned(16))) bf16 sB[2][8 * 2 * 64 * 8];  // the state block as split B operands
     __shared__ int wflag[kMaxFlags];
+    GDN_LDS_POISON_ALL(sB, wflag);
     const int h = blockIdx.y;
     int seq, j = 0, cb;   // cb: 32-column block (0..7 when composing: 0..3 the M part, 4..7 the H part)
     if (MODE == kCombAll || MODE == kCombGroups) {
@@ -1478,6 +1482,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
     constexpr bool EX = Io<IO>::kExact;
     constexpr bool DB = ChainSmem<EX>::NB == 2;
     __shared__ ChainSmem<EX> sm;
+    GDN_LDS_POISON_ALL(sm);
     const int h = blockIdx.y, hq = h / p.group, wave = wave_id();
     const SegLoc loc = locate_segment(p, blockIdx.x);
     if (loc.seq < 0) return;
@@ -1856,6 +1861,7 @@ enum { kBwdWhole = 0, kBwdMaps = 1, kBwdRerun = 2 };
 template <int MODE>
 __global__ __launch_bounds__(NTHR_CH) void k_bwd_chain_mma(BwdParams p) {
     __shared__ BwdChainSmem sm;
+    GDN_LDS_POISON_ALL(sm);
     const int h = blockIdx.y;
     f32x4 D[8];
     if (MODE == kBwdWhole) {
@@ -1980,6 +1986,7 @@ __device__ __forceinline__ float tile_colsum(const f32x4& x) {
 
 __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
     __shared__ BwdChunkSmem sm;
+    GDN_LDS_POISON_ALL(sm);
     const int f = blockIdx.x, h = blockIdx.y, hq = h / p.group, t = threadIdx.x;
     const int w = wave_id(), lane = lane_id(), c = lane & 15, g = lane >> 4;
     int seq, cidx, len;

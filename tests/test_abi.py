@@ -41,6 +41,17 @@ def test_exports_every_declared_function():
         assert hasattr(l, n), n
 
 
+def test_poison_build_exports_the_same():
+    """The LDS-poisoning debug build (built beside libgdn.so) loads and exports
+    every declared function; its GPU test compares its results with the
+    normal build's."""
+    import os
+    path = os.path.join(os.path.dirname(B.LIB_PATH), "libgdn_poison.so")
+    l = B.load_library(path)
+    for n in header_functions():
+        assert hasattr(l, n), n
+
+
 def test_status_strings():
     l = lib()
     for code, name in enumerate(B.STATUS_NAMES):
