@@ -601,7 +601,7 @@ __global__ __launch_bounds__(NT8) void k_cp_prep16(Params p) {
 
 // ----------------------------------------------------------------------------
 // The segment combine: one 4-wave workgroup per (sequence, value head,
-// 16-column tile u). Boundary s (1 <= s < P): exact, S0(s) = M_{s-1} S0(s-1)
+// 16-column tile u), the eight tiles of a (sequence, head) on one XCD. Boundary s (1 <= s < P): exact, S0(s) = M_{s-1} S0(s-1)
 // + H_{s-1} (the map product on fp16 operands: the M image as A, the state
 // column tile as B; M_0 only with an initial state); warm-up, S0(s) is the
 // warm-up state k_cp_prep16 wrote. Wave r owns rows [32 r, 32 r + 32) of the
@@ -615,8 +615,13 @@ __global__ __launch_bounds__(NTC) void k_combine16(Params p) {
     __shared__ int flags[kMaxSegsPerSeq];
     __shared__ __attribute__((aligned(16))) f16 xb[2][4 * 64 * 8];   // the state tile as B operands, per k step
     GDN_LDS_POISON_ALL(flags, xb);
-    const int u = blockIdx.x & 7, seq = blockIdx.x >> 3, h = blockIdx.y;
-    if (seq >= p.n_seqs) return;
+    // workgroup id = XCD slot (q % 8) + 8 (column tile + 8 (q / 8)), q = seq h_v + head:
+    // the eight column tiles of a (sequence, head) run on one XCD (workgroups
+    // are dealt to the XCDs round-robin), so each M image is fetched into one
+    // L2 instead of eight
+    const int id = (int)blockIdx.x, u = (id >> 3) & 7, q = 8 * (id >> 6) + (id & 7);
+    if (q >= p.n_seqs * p.h_v) return;
+    const int seq = q / p.h_v, h = q % p.h_v;
     int P, seg_base;
     if (!p.cu) {
         P = n_segs_of(n_chunks_of(p.seq_len), p.L);
@@ -1472,7 +1477,7 @@ int launch_cp_prep16(const Params& p, int io, void* stream) {
 }
 
 int launch_combine16(const Params& p, void* stream) {
-    const dim3 grid((unsigned)(8 * p.n_seqs), (unsigned)p.h_v), block(NTC);
+    const dim3 grid((unsigned)(64 * ((p.n_seqs * p.h_v + 7) / 8))), block(NTC);
     hipLaunchKernelGGL(k_combine16, grid, block, 0, (hipStream_t)stream, p);
     return launched16();
 }
