@@ -495,16 +495,27 @@ __device__ __forceinline__ int block_excl_scan(int x, int* red, int& total) {
 // preprocessing takes, and its part; -1: none (uniform over the workgroup).
 // An exact boundary takes PX workgroups (parts 0 .. PX - 1), a warm-up one
 // part 0 of one. Order as planned: exact boundaries first, then the warm-up
-// ones, each in pair order; or head-major (PX workgroups per pair).
-// red: 2 NW + 4 ints of LDS.
+// ones, each in pair order; or head-major (PX workgroups per pair). With
+// PX = 2 the two parts of a pair are workgroups 8 apart (pair index
+// (i % 8) + 8 (i / 16), part (i / 8) % 2): the XCDs are dealt workgroups
+// round-robin, so both run on one XCD and share its L2 for the chunks they
+// both stage; the exact region is padded to whole groups of 16, and the grid
+// has 16 ceil(pairs / 8) + 16 workgroups. red: 2 NW + 4 ints of LDS.
 template <int NW, int PX>
 __device__ int cp_pick(const Params& p, int i, int* red, int& part) {
     constexpr int NT = 64 * NW;
-    if (!p.cp_order) {
-        part = i % PX;
-        return ((i % (PX * p.n_segments)) / PX) * p.h_v + i / (PX * p.n_segments);
-    }
+    static_assert(PX == 1 || PX == 2, "one or two workgroups per pair");
     const int n_pairs = p.n_segments * p.h_v;
+    if (!p.cp_order) {
+        int pi = i;
+        part = 0;
+        if (PX == 2) {
+            pi = (i & 7) + 8 * (i >> 4);
+            part = (i >> 3) & 1;
+        }
+        if (pi >= n_pairs) return -1;
+        return (pi % p.n_segments) * p.h_v + pi / p.n_segments;
+    }
     const int per = (n_pairs + NT - 1) / NT, q0 = threadIdx.x * per, q1 = min(q0 + per, n_pairs);
     int n_ex = 0, n_wu = 0;
     for (int q = q0; q < q1; ++q) {
@@ -517,10 +528,11 @@ __device__ int cp_pick(const Params& p, int i, int* red, int& part) {
     int tot_ex, tot_wu;
     const int pre_ex = block_excl_scan<NW>(n_ex, red, tot_ex);
     const int pre_wu = block_excl_scan<NW>(n_wu, red + NW, tot_wu);
-    const bool want_ex = i < PX * tot_ex;
-    const int r = want_ex ? i / PX : i - PX * tot_ex;
-    part = want_ex ? i % PX : 0;
-    if (!want_ex && r >= tot_wu) return -1;   // (uniform: every thread has the totals)
+    const int ex_wgs = PX == 2 ? 16 * ((tot_ex + 7) / 8) : tot_ex;   // the exact region (padded with PX = 2)
+    const bool want_ex = i < ex_wgs;
+    const int r = want_ex ? (PX == 2 ? (i & 7) + 8 * (i >> 4) : i) : i - ex_wgs;
+    part = want_ex && PX == 2 ? (i >> 3) & 1 : 0;
+    if (r >= (want_ex ? tot_ex : tot_wu)) return -1;   // (uniform: every thread has the totals)
     const int pre = want_ex ? pre_ex : pre_wu, cnt = want_ex ? n_ex : n_wu;
     if (r >= pre && r < pre + cnt) {
         int k = pre;
@@ -1464,13 +1476,13 @@ int launched16() { return (int)hipGetLastError(); }
 int launch_cp_prep16(const Params& p, int io, void* stream) {
     if (io == kIoBf16) {
         if (p.cp_split)
-            hipLaunchKernelGGL(k_cp_ws<true>, dim3((unsigned)(2 * p.n_segments * p.h_v)), dim3(64 * 8), 0,
-                               (hipStream_t)stream, p);
+            hipLaunchKernelGGL(k_cp_ws<true>, dim3((unsigned)(16 * ((p.n_segments * p.h_v + 7) / 8) + 16)),
+                               dim3(64 * 8), 0, (hipStream_t)stream, p);
         else
             hipLaunchKernelGGL(k_cp_ws<false>, dim3((unsigned)(p.n_segments * p.h_v)), dim3(64 * kCpWaves), 0,
                                (hipStream_t)stream, p);
     } else {
-        hipLaunchKernelGGL(k_cp_prep16<float>, dim3((unsigned)(2 * p.n_segments * p.h_v)), dim3(NT8), 0,
+        hipLaunchKernelGGL(k_cp_prep16<float>, dim3((unsigned)(16 * ((p.n_segments * p.h_v + 7) / 8) + 16)), dim3(NT8), 0,
                            (hipStream_t)stream, p);
     }
     return launched16();
