@@ -56,13 +56,13 @@ KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("gdn_device.h", "gdn_internal.h",
 # of k_decode on the 256-row decode, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by a
 # 512 MiB copy's counts (profiles/forward_kernels_tp8.md, decode_k_decode_256rows.md); None
 # until taken for the current sources.
-MEASURED_TRAFFIC = {"sha256": "8fda686b798646a92facf4cb7ad1bfc5d785236fb1ef605e4818f3f1e5c2b9bd",
+MEASURED_TRAFFIC = {"sha256": "cc65d7a73b6a180bbeb8c3a0dc7d4d4c4965cb7e13dab336aecd4cd4f32cfc34",
                     # bytes read, written per launch (keys as the per-kernel timings)
-                    "tp8": {"per_kernel": {"prep": [19971227, 29393888], "cp_prep": [72068361, 18219008], "cp_combine": [20429435, 4063232], "fwd": [146873813, 67895296]},
+                    "tp8": {"per_kernel": {"prep": [19919821, 29393888], "cp_prep": [47344643, 18219008], "cp_combine": [6163063, 4063232], "fwd": [146594600, 67633152]},
                             "dominant": "fwd",
                             # MfmaFlopsF16 + MfmaFlopsBF16 of the step's kernels per step
-                            "mfma_flops": 53140000000},
-                    "decode256": {"read": 135124865, "write": 134976256}}
+                            "mfma_flops": 53130000000},
+                    "decode256": {"read": 135136351, "write": 134942336}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp4": 0.486, "tp2": 0.659, "tp1": 0.493}
 MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 matrix peak
