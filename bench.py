@@ -313,6 +313,9 @@ def main():
     ap.add_argument("--decode-rows", type=int, default=256,
                     help="rows (sequences) of the one-token decode measurement at the TP8 head "
                          "counts (0 = skip)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed forwards (each after the cache flush, as a step) for this long before "
+                         "the warm-up steps, so that the shader clock has left its idle level")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (a kernel of known "
                          "traffic that scales the HBM byte counters of a profiled run)")
@@ -360,6 +363,20 @@ def main():
                 lam=args.lam, workspace=ws, out=out, final_state=fs, dv_split=args.dv_split)
 
     clock = ClockSampler().start()
+    # The power controller raises the shader clock over tens of milliseconds of
+    # load after the idle input setup; the forwards below (each after the flush,
+    # exactly as a step) let it settle, so that the warm-up and timed steps
+    # measure the kernels rather than the ramp. Reported as "settle".
+    settle_steps, t_settle = 0, time.time()
+    while (time.time() - t_settle) * 1e3 < args.settle_ms:
+        if not args.no_flush:
+            flush.zero_()
+        step()
+        settle_steps += 1
+        if settle_steps % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    settle = {"ms": round((time.time() - t_settle) * 1e3, 1), "forwards": settle_steps}
     for _ in range(args.warmup):
         if not args.no_flush:
             flush.zero_()
@@ -547,7 +564,7 @@ def main():
     qs = lambda f: float(np.percentile(eager_ms, f))  # noqa: E731
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle": settle, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": (round(value / (T / (PAGES_MS[args.config] * 1e-3)), 3)
                         if args.config in PAGES_MS and B == 1 else None),
@@ -568,8 +585,8 @@ def main():
         "warm_cache_ms_per_step": round(float(np.mean(warm)), 4),
         "mfma": mfma, "parity": parity, "boundary_state_error": boundary,
         "backward": backward, "decode": decode,
-        "plan": {key: pl[key] for key in ("L", "n_segments", "P_max", "cp_on", "dv_split", "warmup_chunks",
-                                          "n_cu", "lambda")},
+        "plan": {key: pl[key] for key in ("L", "n_segments", "P_max", "cp_on", "dv_split", "cp_layout",
+                                          "warmup_chunks", "n_cu", "lambda")},
         "precision": ("fp16 matrix-core operands for the chunk chain (state, V', K, Q, "
                       "T diag(beta), P), V through an exact bf16 identity product, fp32 "
                       "accumulation and fp32 state" if inp.io_dtype == "bf16" else
