@@ -2112,11 +2112,18 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
         for (int rt = 0; rt < 4; ++rt) aq[rt] = a1[rt] = a2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const float* Srow = S + (size_t)(16 * w + c) * DK;
         const float* Drow = dSn + (size_t)(16 * w + c) * DK;
+        // this wave's S row (every k step) in flight during the staging and the barrier
+        f32x4 srow[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            srow[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
+            srow[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
+        }
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             bf16x8 sh, sl;
-            kp_op_f32(Srow, ks, g, 1.f, sh, sl);
+            split8(srow[ks][0], srow[ks][1], sh, sl);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int o = (16 * rt + c) * LDQ + 32 * ks + 8 * g;
@@ -2129,13 +2136,20 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 a2[rt] = mma16k32(yl, sh, a2[rt]);
             }
         }
+        // this wave's dSn row, in flight during the V' staging
+        f32x4 drow[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            drow[ks][0] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 4 * g);
+            drow[ks][1] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 16 + 4 * g);
+        }
         __syncthreads();
         stage_f32(st_x, Vpb, false);
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             bf16x8 dh, dl;
-            kp_op_f32(Drow, ks, g, 1.f, dh, dl);
+            split8(drow[ks][0], drow[ks][1], dh, dl);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int o = (16 * rt + c) * LDQ + 32 * ks + 8 * g;
@@ -2156,7 +2170,9 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = r0 + e;
-                const float kv = (float)Kg[(size_t)min(r, nv - 1) * ts + 16 * w + c];
+                // K[r][16 w + c] from the staged K^T (rows past the end hold the last row, as in Kg)
+                const int dkc = 16 * w + c;
+                const float kv = (float)sm.kt[dkc * LDKT + ((kp(r & ~3) ^ tswz(dkc)) | (r & 3))];
                 const float kap = tile_rowsum(fr[e] * kv * a1[rt][e]);
                 if (c == 0 && r < nv) {
                     atomicAdd(&sm.dgam[r], -kap);
@@ -2175,12 +2191,39 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
         const int ra = 16 * prt + c;
         const bf16* st_do = sm.sa;                       // staged in step 2 (dO, then V' hi / lo rows)
         const bf16* st_v = sm.sa + CH * LDQ;
+        // the operands read from memory (K rows ra and rb, dV' row ra, Y rows rb), one k step ahead
+        struct Ops3 {
+            u32x2 ka[2], kb[2][2];
+            f32x4 dv[2], y[2][2];
+        };
+        const float brb[2] = {sm.bet[16 * pct0 + c], sm.bet[16 * (pct0 + 1) + c]};
+        auto load3 = [&](Ops3& o, int ks) {
+            const bf16* kra = Kg + (size_t)min(ra, nv - 1) * ts + 32 * ks + 4 * g;
+            o.ka[0] = *reinterpret_cast<const u32x2*>(kra);
+            o.ka[1] = *reinterpret_cast<const u32x2*>(kra + 16);
+            const float* dvr = dVb + (size_t)ra * DK + 32 * ks + 4 * g;
+            o.dv[0] = *reinterpret_cast<const f32x4*>(dvr);
+            o.dv[1] = *reinterpret_cast<const f32x4*>(dvr + 16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int rb = 16 * (pct0 + j) + c;
+                const float* yr = Yb + (size_t)rb * DK + 32 * ks + 4 * g;
+                o.y[j][0] = *reinterpret_cast<const f32x4*>(yr);
+                o.y[j][1] = *reinterpret_cast<const f32x4*>(yr + 16);
+                const bf16* krb = Kg + (size_t)min(rb, nv - 1) * ts + 32 * ks + 4 * g;
+                o.kb[j][0] = *reinterpret_cast<const u32x2*>(krb);
+                o.kb[j][1] = *reinterpret_cast<const u32x2*>(krb + 16);
+            }
+        };
+        Ops3 cur, nxt;
+        load3(cur, 0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            if (ks < 3) load3(nxt, ks + 1);
             const bf16x8 ao = lds_op16(st_do + ra * LDQ + 32 * ks + 8 * g);
-            const bf16x8 ak = kp_op_bf16(Kg + (size_t)min(ra, nv - 1) * ts, ks, g, true);
+            const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{cur.ka[0][0], cur.ka[0][1], cur.ka[1][0], cur.ka[1][1]});
             bf16x8 adh, adl;
-            kp_op_f32(dVb + (size_t)ra * DK, ks, g, 1.f, adh, adl);
+            split8(cur.dv[0], cur.dv[1], adh, adl);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int rb = 16 * (pct0 + j) + c;
@@ -2189,13 +2232,15 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 const bf16x8 vl = lds_op16(st_v + (CH + rb) * LDQ + 32 * ks + 8 * g);
                 dp[j] = mma16k32(ao, vh, dp[j]);
                 dp[j] = mma16k32(ao, vl, dp[j]);
-                kp_op_f32(Yb + (size_t)rb * DK, ks, g, sm.bet[rb], yh, yl);
+                split8(cur.y[j][0] * brb[j], cur.y[j][1] * brb[j], yh, yl);
                 dt[j] = mma16k32(adh, yh, dt[j]);
                 dt[j] = mma16k32(adh, yl, dt[j]);
                 dt[j] = mma16k32(adl, yh, dt[j]);
-                const bf16x8 bk = kp_op_bf16(Kg + (size_t)min(rb, nv - 1) * ts, ks, g, true);
+                const bf16x8 bk =
+                    __builtin_bit_cast(bf16x8, u32x4{cur.kb[j][0][0], cur.kb[j][0][1], cur.kb[j][1][0], cur.kb[j][1][1]});
                 kkt[j] = mma16k32(ak, bk, kkt[j]);
             }
+            if (ks < 3) cur = nxt;
         }
         __syncthreads();   // the staging area becomes the image slots again
 #pragma unroll
