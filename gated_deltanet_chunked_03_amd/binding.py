@@ -324,16 +324,15 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
 def bwd(q, k, v, g, beta, d_out, scale=None, initial_state=None, d_final_state=None, cu_seqlens=None,
         cp_mode="auto", lam=0.0, warmup_chunks=0, noise_floor=0.0, n_cu=0, workspace=None,
         want_d_initial=True):
-    """Gradients of ``fwd`` (bf16 q, k, v): given d_out (like v) and optionally
-    d_final_state ([n_seqs, h_v, 128, 128] fp32), returns a dict with dq, dk
-    (like q), dv (like v), dg, dbeta (like g) and d_initial ([n_seqs, h_v, 128, 128]
-    fp32, or None when want_d_initial is False). The forward runs again inside,
-    with the same plan options as ``fwd``."""
+    """Gradients of ``fwd``: given d_out (like v) and optionally d_final_state
+    ([n_seqs, h_v, 128, 128] fp32), returns a dict with dq, dk (like q), dv
+    (like v), dg, dbeta (like g) and d_initial ([n_seqs, h_v, 128, 128] fp32, or
+    None when want_d_initial is False). The forward runs again inside, with the
+    same plan options as ``fwd``. fp32 q, k, v and d_out are rounded once to
+    bf16 inside; their gradients come back in fp32."""
     torch = _torch()
     B, T, h_qk, h_v, d_k, d_v, io, cu_dev, cu_host = _prepare(q, k, v, g, beta, cu_seqlens)
     dev = q.device
-    if io != GDN_BF16:
-        raise ValueError("the backward takes bfloat16 q, k, v")
     n_seqs = B if cu_host is None else len(cu_host) - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d_k)

@@ -561,6 +561,7 @@ gdn_status run_fwd_rerun(const gdn_desc* d, const Plan& P, const void* q, const 
 struct BwdLayout {
     size_t off_o = 0, off_cs = 0, off_ds = 0, off_tpg = 0, off_tpt = 0, off_dq = 0, off_dk = 0, bytes = 0;
     size_t off_y = 0, off_vp = 0, off_oi = 0, off_dvp = 0, off_z = 0;
+    size_t off_q = 0, off_k = 0, off_v = 0, off_do = 0;   // bf16 copies of fp32 inputs
     size_t tokens = 0;
 };
 
@@ -583,6 +584,12 @@ BwdLayout bwd_layout(const gdn_desc* d, const Plan& P) {
     L.off_z = off;   off = align_up(off + blk, 256);
     L.off_dq = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
     L.off_dk = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * sizeof(float), 256);
+    if (d->io_dtype == GDN_F32) {
+        L.off_q = off;  off = align_up(off + L.tokens * d->h_qk * gdn::kDim * 2, 256);
+        L.off_k = off;  off = align_up(off + L.tokens * d->h_qk * gdn::kDim * 2, 256);
+        L.off_v = off;  off = align_up(off + L.tokens * d->h_v * gdn::kDim * 2, 256);
+        L.off_do = off; off = align_up(off + L.tokens * d->h_v * gdn::kDim * 2, 256);
+    }
     L.bytes = off;
     return L;
 }
@@ -594,6 +601,11 @@ extern "C" {
 size_t gdn_bwd_workspace_bytes(const gdn_desc* desc) {
     Plan P;
     if (make_plan(desc, &P, false) != GDN_OK) return 0;
+    if (desc->io_dtype == GDN_F32) {   // planned as the bf16 run it becomes
+        gdn_desc d16 = *desc;
+        d16.io_dtype = GDN_BF16;
+        if (make_plan(&d16, &P, false) != GDN_OK) return 0;
+    }
     return bwd_layout(desc, P).bytes;
 }
 
@@ -605,8 +617,13 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     Plan P;
     gdn_status st = make_plan(desc, &P, false);   // (the re-run keeps all columns together)
     if (st != GDN_OK) return st;
-    if (desc->io_dtype != GDN_BF16)
-        return fail(GDN_ERR_BAD_DTYPE, "the backward takes bf16 q, k, v (io_dtype GDN_BF16)");
+    // fp32 inputs: q, k, v and d_out are rounded once to bf16 in the workspace,
+    // everything after runs as for bf16 inputs (so it is planned as that run),
+    // and dq, dk, dv are written in fp32
+    const bool f32 = desc->io_dtype == GDN_F32;
+    gdn_desc d16 = *desc;
+    d16.io_dtype = GDN_BF16;
+    if (f32 && (st = make_plan(&d16, &P, false)) != GDN_OK) return st;
     const bool varlen = desc->host_cu_seqlens != nullptr;
     if (varlen && !cu_seqlens) return fail(GDN_ERR_NULL_ARG, "cu_seqlens is NULL but desc->host_cu_seqlens is set");
     if (!varlen && cu_seqlens) return fail(GDN_ERR_NULL_ARG, "desc->host_cu_seqlens is required with cu_seqlens");
@@ -626,9 +643,21 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
         return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", workspace_bytes, L.bytes);
     if (L.bytes > 0 && (st = check_ptr(workspace, "workspace", true, 256))) return st;
     char* w8 = static_cast<char*>(workspace);
+    if (f32 && L.tokens > 0) {
+        const long long nq = (long long)L.tokens * desc->h_qk * gdn::kDim, nv = (long long)L.tokens * desc->h_v * gdn::kDim;
+        int e = gdn::launch_round_bf16(static_cast<const float*>(q), w8 + L.off_q, nq, stream);
+        if (!e) e = gdn::launch_round_bf16(static_cast<const float*>(k), w8 + L.off_k, nq, stream);
+        if (!e) e = gdn::launch_round_bf16(static_cast<const float*>(v), w8 + L.off_v, nv, stream);
+        if (!e) e = gdn::launch_round_bf16(static_cast<const float*>(d_out), w8 + L.off_do, nv, stream);
+        if (e) return fail(GDN_ERR_HIP, "bf16 rounding launch: %s", hipGetErrorString((hipError_t)e));
+        q = w8 + L.off_q;
+        k = w8 + L.off_k;
+        v = w8 + L.off_v;
+        d_out = w8 + L.off_do;
+    }
     // the forward again, keeping the state entering every chunk
     if (P.n_chunks_total > 0) {
-        st = run_fwd_rerun(desc, P, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8 + L.off_o, w8, stream,
+        st = run_fwd_rerun(&d16, P, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8 + L.off_o, w8, stream,
                            reinterpret_cast<float*>(w8 + L.off_cs), reinterpret_cast<float*>(w8 + L.off_y),
                            reinterpret_cast<float*>(w8 + L.off_vp), reinterpret_cast<float*>(w8 + L.off_oi), d_out);
         if (st != GDN_OK) return st;
@@ -671,6 +700,7 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     b.h_v = desc->h_v;
     b.group = desc->h_v / desc->h_qk;
     b.n_chunks = P.n_chunks_total;
+    b.out_f32 = f32;
     b.scale = scale;
     int e = gdn::launch_bwd(b, stream);
     if (!e) e = gdn::launch_bwd_sum(b, (long long)L.tokens, stream);

@@ -28,7 +28,8 @@
 // other gradient of every chunk in parallel on the matrix cores
 // (k_bwd_chunk_mma) -- both in the forward's kernel file, whose operand
 // layouts they share -- and k_bwd_sum (query/key gradients summed over the
-// value heads of a group). bf16 inputs only.
+// value heads of a group). The kernels read bf16 q, k, v, dO; fp32 inputs are
+// rounded once to bf16 by k_round_bf16 and their gradients written in fp32.
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -280,8 +281,41 @@ __global__ __launch_bounds__(NT) void k_bwd_sum(BwdParams p, long long n_tokens)
         b += *reinterpret_cast<const f32x4*>(p.dk_part + o);
     }
     const size_t oo = ((size_t)tok * p.h_qk + hq) * DK + col;
+    if (p.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.dq) + oo) = a;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.dk) + oo) = b;
+        return;
+    }
     *reinterpret_cast<u32x2*>(static_cast<bf16*>(p.dq) + oo) = u32x2{pack_rne(a[0], a[1]), pack_rne(a[2], a[3])};
     *reinterpret_cast<u32x2*>(static_cast<bf16*>(p.dk) + oo) = u32x2{pack_rne(b[0], b[1]), pack_rne(b[2], b[3])};
+}
+
+// dv = diag(beta) Z in fp32 (for fp32 inputs; the bf16 dv is written by the
+// state-gradient scan as it forms Z). One workgroup per (chunk, value head).
+__global__ __launch_bounds__(NT) void k_bwd_dv32(BwdParams p) {
+    const int f = blockIdx.x, h = blockIdx.y;
+    int seq, c, len;
+    size_t tok_s;
+    if (!bwd_locate(p, f, seq, c, len, tok_s)) return;
+    const size_t tok0 = tok_s + (size_t)c * CH;
+    const int nv = min(CH, len - c * CH);
+    const float* z = p.z + ((size_t)f * p.h_v + h) * CH * DK;
+    float* dv = static_cast<float*>(p.dv) + tok0 * p.h_v * DK + (size_t)h * DK;
+    for (int idx = threadIdx.x; idx < CH * DK / 4; idx += NT) {
+        const int r = idx / (DK / 4), col = (idx % (DK / 4)) * 4;
+        if (r >= nv) break;
+        const float b = p.beta[(tok0 + r) * p.h_v + h];
+        *reinterpret_cast<f32x4*>(dv + (size_t)r * p.h_v * DK + col) =
+            b * *reinterpret_cast<const f32x4*>(z + r * DK + col);
+    }
+}
+
+// fp32 -> bf16 with round-to-nearest-even, four elements per thread.
+__global__ __launch_bounds__(NT) void k_round_bf16(const float* x, bf16* y, long long n4) {
+    const long long i = (long long)blockIdx.x * NT + threadIdx.x;
+    if (i >= n4) return;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(x + 4 * i);
+    *reinterpret_cast<u32x2*>(y + 4 * i) = u32x2{pack_rne(a[0], a[1]), pack_rne(a[2], a[3])};
 }
 
 }  // namespace
@@ -296,10 +330,22 @@ int launch_bwd(const BwdParams& p, void* stream) {
         if ((e = launched())) return e;
     }
     if ((e = launch_bwd_chain_mma(p, stream))) return e;
+    if (p.n_chunks > 0 && p.out_f32) {
+        hipLaunchKernelGGL(k_bwd_dv32, dim3(p.n_chunks, p.h_v), dim3(NT), 0, s, p);
+        if ((e = launched())) return e;
+    }
     if (p.n_chunks > 0) {
         if ((e = launch_bwd_chunk_mma(p, stream))) return e;
     }
     return 0;
+}
+
+int launch_round_bf16(const float* x, void* y, long long n, void* stream) {
+    if (n <= 0) return 0;
+    const long long n4 = n / 4;
+    hipLaunchKernelGGL(k_round_bf16, dim3((unsigned)((n4 + NT - 1) / NT)), dim3(NT), 0, (hipStream_t)stream, x,
+                       static_cast<bf16*>(y), n4);
+    return launched();
 }
 
 int launch_bwd_sum(const BwdParams& p, long long n_tokens, void* stream) {

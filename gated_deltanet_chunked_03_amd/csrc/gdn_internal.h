@@ -80,7 +80,7 @@ constexpr int kBwdTpg = 2 * kChunk * kChunk + kChunk;   // floats per (chunk, he
 constexpr int kBwdTpt = 6 * kChunk * kChunk;            // bf16 per (chunk, head) in the T^T / P^T / T images
 
 struct BwdParams {
-    const void* q;            // [tokens][h_qk][128] bf16
+    const void* q;            // [tokens][h_qk][128] bf16 (fp32 inputs: their bf16 rounding)
     const void* k;
     const void* v;            // [tokens][h_v][128] bf16
     const float* g;           // [tokens][h_v]
@@ -88,9 +88,9 @@ struct BwdParams {
     const void* dout;         // [tokens][h_v][128] bf16: loss gradient of the output
     const float* dfinal;      // [n_seqs][h_v][128][128] loss gradient of the final state, or null
     const int32_t* cu;        // [n_seqs + 1] or null (uniform sequences of seq_len)
-    void* dq;                 // [tokens][h_qk][128] bf16
+    void* dq;                 // [tokens][h_qk][128] bf16, fp32 if out_f32
     void* dk;
-    void* dv;                 // [tokens][h_v][128] bf16
+    void* dv;                 // [tokens][h_v][128] bf16, fp32 if out_f32
     float* dg;                // [tokens][h_v]
     float* dbeta;
     float* dinit;             // [n_seqs][h_v][128][128] or null
@@ -119,6 +119,7 @@ struct BwdParams {
     int32_t comb_G, comb_J;   // the forward plan's combine grouping
     int32_t L, n_segments;    // chunks per segment, segments over all sequences
     int32_t n_seqs, seq_len, h_qk, h_v, group, n_chunks;
+    int32_t out_f32;          // dq, dk, dv written as fp32 (the caller's inputs were fp32)
     float scale;
 };
 
@@ -126,6 +127,7 @@ int launch_bwd(const BwdParams& p, void* stream);                       // prep,
 int launch_bwd_sum(const BwdParams& p, long long n_tokens, void* stream);  // dq, dk group sums
 int launch_bwd_chain_mma(const BwdParams& p, void* stream);                // dS scan on matrix cores
 int launch_bwd_chunk_mma(const BwdParams& p, void* stream);                // chunk gradients on matrix cores
+int launch_round_bf16(const float* x, void* y, long long n, void* stream);  // fp32 -> bf16 (RNE), n % 4 == 0
 
 // Kernel launchers (gdn_kernels.hip). Return 0 or a hipError_t value.
 int launch_prep(const Params& p, int io, void* stream);

@@ -1795,13 +1795,14 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
             float* zb = p.z + ((size_t)(loc.chunk_base + cc) * p.h_v + h) * CH * DK + 16 * wave_id() + c + 4 * g * DK;
             const unsigned ts_v = (unsigned)(p.h_v * DK);
             bf16* dv = static_cast<bf16*>(p.dv) + (loc.tok0 + (size_t)cc * CH) * ts_v + (size_t)h * DK + 16 * wave_id() + c;
+            const int dv_rows = p.out_f32 ? 0 : in_nv;   // fp32 dv: formed from Z afterwards
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rt + 4 * g + e;
                     zb[(16 * rt + e) * DK] = Z[rt][e];
-                    if (r < in_nv) dv[r * ts_v] = (bf16)(sm.bet[r] * Z[rt][e]);
+                    if (r < dv_rows) dv[r * ts_v] = (bf16)(sm.bet[r] * Z[rt][e]);
                 }
         }
 #pragma unroll

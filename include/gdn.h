@@ -242,20 +242,23 @@ gdn_status gdn_calibrate_lambda(const gdn_desc* desc,
  * gdn_fwd), writing the state that enters every chunk; the state gradient is
  * then scanned backwards over the chunks and every chunk's gradients are
  * formed in parallel.
- *   desc, q, k, v, g, beta, scale, initial_state, cu_seqlens   as for gdn_fwd;
- *                      io_dtype must be GDN_BF16
- *   d_out              device [B, T, h_v, d_v] bf16, loss gradient of the output
+ *   desc, q, k, v, g, beta, scale, initial_state, cu_seqlens   as for gdn_fwd
+ *                      (GDN_F32: q, k, v and d_out are rounded once to bf16 in the
+ *                      workspace and the bf16 computation runs on them; the
+ *                      gradients are then written in fp32)
+ *   d_out              device [B, T, h_v, d_v] io_dtype, loss gradient of the output
  *   d_final_state      device [n_seqs, h_v, d_k, d_v] fp32, or NULL for zero
- *   dq, dk             device [B, T, h_qk, d_k] bf16 (summed over the value heads
- *                      that share a query/key head)
- *   dv                 device [B, T, h_v, d_v] bf16
+ *   dq, dk             device [B, T, h_qk, d_k] io_dtype (summed over the value
+ *                      heads that share a query/key head)
+ *   dv                 device [B, T, h_v, d_v] io_dtype
  *   dg, dbeta          device [B, T, h_v] fp32
  *   d_initial_state    device [n_seqs, h_v, d_k, d_v] fp32, or NULL to skip
  *   workspace          device scratch of at least gdn_bwd_workspace_bytes(desc)
  *                      bytes, 256-byte aligned (the forward's workspace, then per
  *                      (chunk, value head) two 64 KiB states, 32.25 KiB of T, P
  *                      and gamma, 48 KiB of their bf16 images and five 32 KiB
- *                      intermediates, and per token and value head 1.25 KiB)
+ *                      intermediates, and per token and value head 1.25 KiB;
+ *                      GDN_F32 adds the bf16 copies of q, k, v and d_out)
  * Same ownership and error behaviour as gdn_fwd. */
 size_t gdn_bwd_workspace_bytes(const gdn_desc* desc);
 gdn_status gdn_bwd(const gdn_desc* desc,

@@ -97,6 +97,27 @@ int main() {
               GDN_OK);
         CHECK(gdn::g_launches > before);
     }
+    // backward: bf16 and fp32 inputs (the fp32 workspace adds bf16 copies of q, k, v, d_out)
+    for (int io : {GDN_BF16, GDN_F32}) {
+        gdn_desc d = make(1, 4096, 2, 8);
+        d.io_dtype = io;
+        const size_t need = gdn_bwd_workspace_bytes(&d);
+        CHECK(need > 0);
+        if (io == GDN_F32) {
+            gdn_desc d16 = make(1, 4096, 2, 8);
+            CHECK(need >= gdn_bwd_workspace_bytes(&d16) + (size_t)4096 * (2 + 8) * 128 * 2 * 2);
+        }
+        std::vector<unsigned char> host(4096);
+        void* p = (void*)(((uintptr_t)host.data() + 255) & ~(uintptr_t)255);
+        float* f = (float*)p;
+        const int before = gdn::g_launches;
+        CHECK(gdn_bwd(&d, p, p, p, f, f, 0.1f, nullptr, nullptr, p, nullptr, p, p, p, f, f, nullptr, p, need - 1,
+                      nullptr) == GDN_ERR_WORKSPACE_TOO_SMALL);
+        CHECK(gdn::g_launches == before);
+        CHECK(gdn_bwd(&d, p, p, p, f, f, 0.1f, nullptr, nullptr, p, nullptr, p, p, p, f, f, nullptr, p, need,
+                      nullptr) == GDN_OK);
+        CHECK(gdn::g_launches > before);
+    }
     // status strings
     for (int s = 0; s <= 9; ++s) CHECK(std::strlen(gdn_status_string((gdn_status)s)) > 0);
     CHECK(gdn_status_string((gdn_status)99) != nullptr);

@@ -13,6 +13,7 @@ int launch_bwd(const BwdParams&, void*) { return reached(); }
 int launch_bwd_sum(const BwdParams&, long long, void*) { return reached(); }
 int launch_bwd_chain_mma(const BwdParams&, void*) { return reached(); }
 int launch_bwd_chunk_mma(const BwdParams&, void*) { return reached(); }
+int launch_round_bf16(const float*, void*, long long, void*) { return reached(); }
 int launch_prep(const Params&, int, void*) { return reached(); }
 int launch_wu(const Params&, int, void*) { return reached(); }
 int launch_cp_prep(const Params&, int, void*) { return reached(); }

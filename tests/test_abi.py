@@ -296,11 +296,19 @@ def call_bwd(d, q=0x1000, k=0x1000, v=0x1000, g=0x1000, beta=0x1000, scale=0.1, 
 
 
 def test_bwd_validation():
-    """gdn_bwd rejects bad arguments before any launch (only bf16 inputs; every
-    gradient output and d_out required; workspace size and alignment)."""
-    d, keep = desc(io_dtype=B.GDN_F32)
-    st, msg = call_bwd(d)
-    assert B.STATUS_NAMES[st] == "GDN_ERR_BAD_DTYPE" and "bf16" in msg
+    """gdn_bwd rejects bad arguments before any launch (dtype; every gradient
+    output and d_out required; workspace size and alignment)."""
+    d, keep = desc(io_dtype=7)
+    assert B.STATUS_NAMES[call_bwd(d)[0]] == "GDN_ERR_BAD_DTYPE"
+    # fp32 inputs: the workspace also holds their bf16 copies (q, k: 2 x 256 B per
+    # token and query/key head; v, d_out: 2 x 256 B per token and value head)
+    d16, keep16 = desc()
+    d32, keep32 = desc(io_dtype=B.GDN_F32)
+    n16 = lib().gdn_bwd_workspace_bytes(ctypes.byref(d16))
+    n32 = lib().gdn_bwd_workspace_bytes(ctypes.byref(d32))
+    assert n32 >= n16 + 2 * 256 * d32.B * d32.T * (d32.h_qk + d32.h_v)
+    st, msg = call_bwd(d32, ws_bytes=n32 - 1)
+    assert B.STATUS_NAMES[st] == "GDN_ERR_WORKSPACE_TOO_SMALL" and str(n32) in msg
     d, keep = desc(d_k=64, d_v=64)
     assert B.STATUS_NAMES[call_bwd(d)[0]] == "GDN_ERR_UNSUPPORTED_DIM"
     d, keep = desc()
