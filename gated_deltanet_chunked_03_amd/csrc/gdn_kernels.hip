@@ -2011,6 +2011,19 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
     const float* tp = p.tpg + ((size_t)f * p.h_v + h) * kBwdTpg;
     const float scale = p.scale;
 
+    // step 1's operands (row t / 8, columns 16 (t % 8) .. + 15 of Y, Z, V and the
+    // output term's partial sum), in flight during the staging
+    const int r1 = t >> 3, c01 = (t & 7) * 16;
+    f32x4 y1[4], z1[4];
+    u32x2 v1[4];
+    const float qo1 = Oib[(t & 7) * CH + r1];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const int col = c01 + 4 * q4;
+        y1[q4] = *reinterpret_cast<const f32x4*>(Yb + (size_t)r1 * DK + col);
+        z1[q4] = *reinterpret_cast<const f32x4*>(Zb + (size_t)r1 * DK + col);
+        v1[q4] = *reinterpret_cast<const u32x2*>(Vg + (size_t)min(r1, nv - 1) * ts_v + col);
+    }
     // ---- staging: K^T, Q^T (rows past the end repeat the last; harmless, see the products), images, gates
     {
         const int m = t >> 5, c4 = (t & 31) * 4, tk = kp(4 * m) ^ tswz(c4);
@@ -2047,19 +2060,17 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
     if (t < CH) sm.fr[t] = __expf(sm.gam[CH - 1] - sm.gam[t]);
     // ---- 1. row sums over d_v: thread t takes row t / 8, columns 16 (t % 8) .. + 15
     {
-        const int r = t >> 3, c0 = (t & 7) * 16, rr = min(r, nv - 1);
+        const int r = r1;
         const bool ok = r < nv;
         float zb = 0.f, vy = 0.f;
         // the output's state term . dO over this thread's 16 columns (the forward
         // re-run's partial sum of wave t % 8, whose columns these are)
-        float qo = Oib[(t & 7) * CH + r];
+        float qo = qo1;
         const float br = sm.bet[r];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int col = c0 + 4 * q4;
-            const f32x4 y = *reinterpret_cast<const f32x4*>(Yb + (size_t)r * DK + col);
-            const f32x4 z = *reinterpret_cast<const f32x4*>(Zb + (size_t)r * DK + col);
-            const u32x2 vw = *reinterpret_cast<const u32x2*>(Vg + (size_t)rr * ts_v + col);
+            const f32x4 y = y1[q4], z = z1[q4];
+            const u32x2 vw = v1[q4];
             const f32x4 v = {__uint_as_float(vw[0] << 16), __uint_as_float(vw[0] & 0xffff0000u),
                              __uint_as_float(vw[1] << 16), __uint_as_float(vw[1] & 0xffff0000u)};
 #pragma unroll
@@ -2137,16 +2148,27 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 a2[rt] = mma16k32(yl, sh, a2[rt]);
             }
         }
-        // this wave's dSn row, in flight during the V' staging
-        f32x4 drow[4][2];
+        // this wave's dSn row (and its S row again, for <S, dSn>), in flight during the V' staging
+        f32x4 drow[4][2], srw[4][2];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             drow[ks][0] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 4 * g);
             drow[ks][1] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 16 + 4 * g);
+            srw[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
+            srw[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
         }
         __syncthreads();
         stage_f32(st_x, Vpb, false);
         __syncthreads();
+        {   // dgamma_C from the decay of the state, e^gamma_C <S, dSn>: this wave's
+            // 16 rows of both are in its registers
+            float part = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) part += dot4v(srw[ks][0], drow[ks][0]) + dot4v(srw[ks][1], drow[ks][1]);
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
+            if (lane == 0) atomicAdd(&sm.dgc, __expf(sm.gam[CH - 1]) * part);
+        }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             bf16x8 dh, dl;
@@ -2216,11 +2238,22 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 o.kb[j][1] = *reinterpret_cast<const u32x2*>(krb + 16);
             }
         };
+        // the fp32 P entries of this wave's dP tiles (for dP o P after the loop),
+        // loaded in the last k step in place of that step's operands
+        float pP[2][4];
         Ops3 cur, nxt;
         load3(cur, 0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            if (ks < 3) load3(nxt, ks + 1);
+            if (ks < 3) {
+                load3(nxt, ks + 1);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pP[j][e] = tp[CH * CH + (16 * prt + 4 * g + e) * CH + 16 * (pct0 + j) + c];
+            }
             const bf16x8 ao = lds_op16(st_do + ra * LDQ + 32 * ks + 8 * g);
             const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{cur.ka[0][0], cur.ka[0][1], cur.ka[1][0], cur.ka[1][1]});
             bf16x8 adh, adl;
@@ -2254,7 +2287,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 const float d = scale * dp[j][e];
                 const bool low = m <= r;
                 psi[e] = low ? d * __expf(sm.gam[r] - sm.gam[m]) : 0.f;
-                E[e] = low ? d * tp[CH * CH + r * CH + m] : 0.f;   // dP o P (P is the fp32 copy)
+                E[e] = low ? d * pP[j][e] : 0.f;   // dP o P (P is the fp32 copy)
             }
             put_img(sm.sa, prt, ct, c, g, psi);
             put_img_t(sm.sb, prt, ct, c, g, psi);
@@ -2352,17 +2385,6 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
             const float cs = tile_colsum(gA);
             if (g == 0) atomicAdd(&sm.dgam[i], -cs);
         }
-    }
-    {   // dgamma_C from the decay of the state: e^gamma_C <S, dSn>
-        float part = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int idx = t + NTHR_CH * j;
-            part += dot4v(*reinterpret_cast<const f32x4*>(S + 4 * idx), *reinterpret_cast<const f32x4*>(dSn + 4 * idx));
-        }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
-        if (lane == 0) atomicAdd(&sm.dgc, __expf(sm.gam[CH - 1]) * part);
     }
     __syncthreads();
     // ---- 6. dk += (G + G^T) K
