@@ -1985,443 +1985,489 @@ __device__ __forceinline__ float tile_colsum(const f32x4& x) {
     return s;
 }
 
-__global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
-    __shared__ BwdChunkSmem sm;
-    GDN_LDS_POISON_ALL(sm);
-    const int f = blockIdx.x, h = blockIdx.y, hq = h / p.group, t = threadIdx.x;
-    const int w = wave_id(), lane = lane_id(), c = lane & 15, g = lane >> 4;
+// One item's operands that the staging and step 1 read from memory. They are
+// fetched an item ahead, during the previous item's last steps (few memory
+// operations there), so that their latency hides behind that work.
+struct BwdItemIn {
+    u32x2 kk[4], qq[4];   // K, Q rows 4 (t / 32) + j, columns 4 (t % 32) ..
+    u32x4 img[4];         // pieces t, t + 512 of the T^T and T image parts
+    float gm, b, qo1;     // gamma, beta of token t (t < 64); the output term's partial sum
+    f32x4 y1[4], z1[4];   // Y, Z: row t / 8, columns 16 (t % 8) ..
+    u32x2 v1[4];          // V: the same
+};
+
+// Items: (chunk slot f, value head h) = (item / h_v, item % h_v), so that the
+// value heads of a chunk (which share K and Q rows) run at the same time.
+__device__ __forceinline__ void bwd_item_fetch(const BwdParams& p, long long item, BwdItemIn& in) {
+    const int f = (int)(item / p.h_v), h = (int)(item - (long long)f * p.h_v), hq = h / p.group, t = threadIdx.x;
     int seq, cidx, len;
     size_t tok_s;
-    if (!locate_chunk(p, f, seq, cidx, len, tok_s)) return;
+    locate_chunk(p, f, seq, cidx, len, tok_s);   // item < n_chunks h_v: always found
     const size_t tok0 = tok_s + (size_t)cidx * CH;
     const int nv = min(CH, len - cidx * CH);
     const size_t ts = (size_t)p.h_qk * DK, ts_v = (size_t)p.h_v * DK;
     const size_t blk = ((size_t)f * p.h_v + h) * CH * DK;
-    const float* S = p.cs + state_off(f, p.h_v, h);
-    const float* dSn = p.ds + state_off(f, p.h_v, h);
-    const float* Yb = p.y + blk;
-    const float* Vpb = p.vp + blk;
-    const float* Oib = p.oi + ((size_t)f * p.h_v + h) * (NW_CH * CH);   // [8][64] partial sums
-    const float* dVb = p.dvp + blk;
-    const float* Zb = p.z + blk;
     const bf16* Kg = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK;
     const bf16* Qg = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK;
-    const bf16* Vg = static_cast<const bf16*>(p.v) + tok0 * ts_v + (size_t)h * DK;
-    const bf16* dOg = static_cast<const bf16*>(p.dout) + tok0 * ts_v + (size_t)h * DK;
-    const float* tp = p.tpg + ((size_t)f * p.h_v + h) * kBwdTpg;
-    const float scale = p.scale;
-
-    // step 1's operands (row t / 8, columns 16 (t % 8) .. + 15 of Y, Z, V and the
-    // output term's partial sum), in flight during the staging
+    const int m = t >> 5, c4 = (t & 31) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = min(4 * m + j, nv - 1);
+        in.kk[j] = *reinterpret_cast<const u32x2*>(Kg + (size_t)row * ts + c4);
+        in.qq[j] = *reinterpret_cast<const u32x2*>(Qg + (size_t)row * ts + c4);
+    }
+    const u32x4* img = reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        in.img[2 * j] = img[t + NTHR_CH * j];
+        in.img[2 * j + 1] = img[t + NTHR_CH * j + 2048];
+    }
+    const int tt = min(t, CH - 1);
+    in.gm = p.tpg[((size_t)f * p.h_v + h) * kBwdTpg + 2 * CH * CH + tt];
+    in.b = p.beta[(tok0 + min(tt, nv - 1)) * p.h_v + h];
     const int r1 = t >> 3, c01 = (t & 7) * 16;
-    f32x4 y1[4], z1[4];
-    u32x2 v1[4];
-    const float qo1 = Oib[(t & 7) * CH + r1];
+    in.qo1 = p.oi[((size_t)f * p.h_v + h) * (NW_CH * CH) + (t & 7) * CH + r1];
+    const bf16* Vg = static_cast<const bf16*>(p.v) + tok0 * ts_v + (size_t)h * DK;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
         const int col = c01 + 4 * q4;
-        y1[q4] = *reinterpret_cast<const f32x4*>(Yb + (size_t)r1 * DK + col);
-        z1[q4] = *reinterpret_cast<const f32x4*>(Zb + (size_t)r1 * DK + col);
-        v1[q4] = *reinterpret_cast<const u32x2*>(Vg + (size_t)min(r1, nv - 1) * ts_v + col);
+        in.y1[q4] = *reinterpret_cast<const f32x4*>(p.y + blk + (size_t)r1 * DK + col);
+        in.z1[q4] = *reinterpret_cast<const f32x4*>(p.z + blk + (size_t)r1 * DK + col);
+        in.v1[q4] = *reinterpret_cast<const u32x2*>(Vg + (size_t)min(r1, nv - 1) * ts_v + col);
     }
-    // ---- staging: K^T, Q^T (rows past the end repeat the last; harmless, see the products), images, gates
-    {
-        const int m = t >> 5, c4 = (t & 31) * 4, tk = kp(4 * m) ^ tswz(c4);
-        u32x2 kk[4], qq[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = min(4 * m + j, nv - 1);
-            kk[j] = *reinterpret_cast<const u32x2*>(Kg + (size_t)row * ts + c4);
-            qq[j] = *reinterpret_cast<const u32x2*>(Qg + (size_t)row * ts + c4);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            *reinterpret_cast<u32x2*>(sm.kt + (c4 + e) * LDKT + tk) = pack_col4(kk, e);
-            *reinterpret_cast<u32x2*>(sm.qt + (c4 + e) * LDKT + tk) = pack_col4(qq, e);
-        }
-        const u32x4* img = reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt);
-        // pieces of the [T^T hi, T^T lo, P^T hi, P^T lo, T hi, T lo] image: parts 0, 1 and 4, 5
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int idx = t + NTHR_CH * j, part = idx >> 9, row = (idx >> 3) & 63, k8 = (idx & 7) * 8;
-            *reinterpret_cast<u32x4*>(sm.ttim + (part * CH + row) * LDP + k8) = img[idx];
-            *reinterpret_cast<u32x4*>(sm.tim + (part * CH + row) * LDP + k8) = img[idx + 2048];
-        }
-        if (t < CH) {
-            const float gm = tp[2 * CH * CH + t];
-            sm.gam[t] = gm;
-            sm.eg[t] = __expf(gm);
-            const float b = p.beta[(tok0 + min(t, nv - 1)) * p.h_v + h];
-            sm.bet[t] = t < nv ? b : 0.f;
-        }
-        if (t == 0) sm.dgc = 0.f;
-    }
-    __syncthreads();
-    if (t < CH) sm.fr[t] = __expf(sm.gam[CH - 1] - sm.gam[t]);
-    // ---- 1. row sums over d_v: thread t takes row t / 8, columns 16 (t % 8) .. + 15
-    {
-        const int r = r1;
-        const bool ok = r < nv;
-        float zb = 0.f, vy = 0.f;
-        // the output's state term . dO over this thread's 16 columns (the forward
-        // re-run's partial sum of wave t % 8, whose columns these are)
-        float qo = qo1;
-        const float br = sm.bet[r];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 y = y1[q4], z = z1[q4];
-            const u32x2 vw = v1[q4];
-            const f32x4 v = {__uint_as_float(vw[0] << 16), __uint_as_float(vw[0] & 0xffff0000u),
-                             __uint_as_float(vw[1] << 16), __uint_as_float(vw[1] & 0xffff0000u)};
+}
+
+// One workgroup per CU (its LDS allows no second), walking the items
+// blockIdx.x, blockIdx.x + gridDim.x, ...
+__global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
+    __shared__ BwdChunkSmem sm;
+    GDN_LDS_POISON_ALL(sm);
+    const long long n_items = (long long)p.n_chunks * p.h_v;
+    long long item = blockIdx.x;
+    if (item >= n_items) return;
+    BwdItemIn in;
+    bwd_item_fetch(p, item, in);
+    for (; item < n_items; item += gridDim.x) {
+        // the thread index through an opaque move: the many LDS offsets derived
+        // from it are then formed in each item where they are used, instead of
+        // being hoisted out of the loop and held in registers throughout
+        int t;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+        const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, c = lane & 15, g = lane >> 4;
+        const int f = (int)(item / p.h_v), h = (int)(item - (long long)f * p.h_v), hq = h / p.group;
+        int seq, cidx, len;
+        size_t tok_s;
+        locate_chunk(p, f, seq, cidx, len, tok_s);
+        const size_t tok0 = tok_s + (size_t)cidx * CH;
+        const int nv = min(CH, len - cidx * CH);
+        const size_t ts = (size_t)p.h_qk * DK, ts_v = (size_t)p.h_v * DK;
+        const size_t blk = ((size_t)f * p.h_v + h) * CH * DK;
+        const float* S = p.cs + state_off(f, p.h_v, h);
+        const float* dSn = p.ds + state_off(f, p.h_v, h);
+        const float* Yb = p.y + blk;
+        const float* Vpb = p.vp + blk;
+        const float* dVb = p.dvp + blk;
+        const float* Zb = p.z + blk;
+        const bf16* Kg = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK;
+        const bf16* Qg = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK;
+        const bf16* dOg = static_cast<const bf16*>(p.dout) + tok0 * ts_v + (size_t)h * DK;
+        const float* tp = p.tpg + ((size_t)f * p.h_v + h) * kBwdTpg;
+        const float scale = p.scale;
+        const int r1 = t >> 3;
+        __syncthreads();   // the previous item's last LDS reads are done
+        // ---- staging: K^T, Q^T (rows past the end repeat the last; harmless, see the products), images, gates
+        {
+            const int m = t >> 5, c4 = (t & 31) * 4, tk = kp(4 * m) ^ tswz(c4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                zb += z[e] * y[e];
-                vy += (v[e] - y[e]) * (br * z[e]);
+                *reinterpret_cast<u32x2*>(sm.kt + (c4 + e) * LDKT + tk) = pack_col4(in.kk, e);
+                *reinterpret_cast<u32x2*>(sm.qt + (c4 + e) * LDKT + tk) = pack_col4(in.qq, e);
+            }
+            // pieces of the [T^T hi, T^T lo, P^T hi, P^T lo, T hi, T lo] image: parts 0, 1 and 4, 5
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int idx = t + NTHR_CH * j, part = idx >> 9, row = (idx >> 3) & 63, k8 = (idx & 7) * 8;
+                *reinterpret_cast<u32x4*>(sm.ttim + (part * CH + row) * LDP + k8) = in.img[2 * j];
+                *reinterpret_cast<u32x4*>(sm.tim + (part * CH + row) * LDP + k8) = in.img[2 * j + 1];
+            }
+            if (t < CH) {
+                sm.gam[t] = in.gm;
+                sm.eg[t] = __expf(in.gm);
+                sm.bet[t] = t < nv ? in.b : 0.f;
+            }
+            if (t == 0) sm.dgc = 0.f;
+        }
+        __syncthreads();
+        if (t < CH) sm.fr[t] = __expf(sm.gam[CH - 1] - sm.gam[t]);
+        // ---- 1. row sums over d_v: thread t takes row t / 8, columns 16 (t % 8) .. + 15
+        {
+            const int r = r1;
+            const bool ok = r < nv;
+            float zb = 0.f, vy = 0.f;
+            // the output's state term . dO over this thread's 16 columns (the forward
+            // re-run's partial sum of wave t % 8, whose columns these are)
+            float qo = in.qo1;
+            const float br = sm.bet[r];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 y = in.y1[q4], z = in.z1[q4];
+                const u32x2 vw = in.v1[q4];
+                const f32x4 v = {__uint_as_float(vw[0] << 16), __uint_as_float(vw[0] & 0xffff0000u),
+                                 __uint_as_float(vw[1] << 16), __uint_as_float(vw[1] & 0xffff0000u)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    zb += z[e] * y[e];
+                    vy += (v[e] - y[e]) * (br * z[e]);
+                }
+            }
+#pragma unroll
+            for (int m = 1; m < 8; m <<= 1) {
+                zb += __shfl_xor(zb, m, 64);
+                vy += __shfl_xor(vy, m, 64);
+                qo += __shfl_xor(qo, m, 64);
+            }
+            if ((t & 7) == 0) {
+                sm.dbe[r] = ok ? zb : 0.f;       // dbeta: Z . Y (through V' = T diag(beta) Y)
+                sm.dgam[r] = ok ? qo - vy : 0.f; // dgamma: the output's e^gamma Q S term, the e^gamma K S term of Y
             }
         }
+        __syncthreads();
+        // ---- 2. d_k-column products: dq = diag(scale e^gamma) dO S^T, dk = diag(f) V' dSn^T - diag(e^gamma) dY S^T.
+        // The token-row operands (dO, dY = diag(beta) Z, V'), which every wave needs, are staged once in LDS
+        // (rows with d_v in kp order; the image slots sa .. sc are free until step 3): first dO and dY, then V'.
+        f32x4 dq[4], dk[4];
+        {
+            bf16* st = sm.sa;                          // 60 KiB: sa, sb, sc
+            bf16* st_do = st;                          // [64][LDQ] dO (kept through step 3's dP)
+            bf16* st_x = st + CH * LDQ;                // [128][LDQ] dY, then V': hi rows, then lo rows
+            static_assert(sizeof(sm.sa) + sizeof(sm.sb) + sizeof(sm.sc) >= 3 * CH * LDQ * sizeof(bf16), "staging fits");
+            auto stage_f32 = [&](bf16* dst, const float* src, bool by_beta) {
 #pragma unroll
-        for (int m = 1; m < 8; m <<= 1) {
-            zb += __shfl_xor(zb, m, 64);
-            vy += __shfl_xor(vy, m, 64);
-            qo += __shfl_xor(qo, m, 64);
-        }
-        if ((t & 7) == 0) {
-            sm.dbe[r] = ok ? zb : 0.f;       // dbeta: Z . Y (through V' = T diag(beta) Y)
-            sm.dgam[r] = ok ? qo - vy : 0.f; // dgamma: the output's e^gamma Q S term, the e^gamma K S term of Y
-        }
-    }
-    __syncthreads();
-    // ---- 2. d_k-column products: dq = diag(scale e^gamma) dO S^T, dk = diag(f) V' dSn^T - diag(e^gamma) dY S^T.
-    // The token-row operands (dO, dY = diag(beta) Z, V'), which every wave needs, are staged once in LDS
-    // (rows with d_v in kp order; the image slots sa .. sc are free until step 3): first dO and dY, then V'.
-    f32x4 dq[4], dk[4];
-    {
-        bf16* st = sm.sa;                          // 60 KiB: sa, sb, sc
-        bf16* st_do = st;                          // [64][LDQ] dO (kept through step 3's dP)
-        bf16* st_x = st + CH * LDQ;                // [128][LDQ] dY, then V': hi rows, then lo rows
-        static_assert(sizeof(sm.sa) + sizeof(sm.sb) + sizeof(sm.sc) >= 3 * CH * LDQ * sizeof(bf16), "staging fits");
-        auto stage_f32 = [&](bf16* dst, const float* src, bool by_beta) {
+                for (int j = 0; j < 4; ++j) {   // piece t + 512 j: row / 32, four d_v at 4 (piece % 32)
+                    const int idx = t + NTHR_CH * j, r = idx >> 5, c4 = (idx & 31) * 4;
+                    f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)r * DK + c4);
+                    if (by_beta) x *= sm.bet[r];
+                    bf16x4 hi, lo;
+                    split4(x, hi, lo);
+                    *reinterpret_cast<bf16x4*>(dst + r * LDQ + kp(c4)) = hi;
+                    *reinterpret_cast<bf16x4*>(dst + (CH + r) * LDQ + kp(c4)) = lo;
+                }
+            };
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {   // piece t + 512 j: row / 32, four d_v at 4 (piece % 32)
+            for (int j = 0; j < 4; ++j) {   // dO, rows past the end zero (loads issued for every row)
                 const int idx = t + NTHR_CH * j, r = idx >> 5, c4 = (idx & 31) * 4;
-                f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)r * DK + c4);
-                if (by_beta) x *= sm.bet[r];
-                bf16x4 hi, lo;
-                split4(x, hi, lo);
-                *reinterpret_cast<bf16x4*>(dst + r * LDQ + kp(c4)) = hi;
-                *reinterpret_cast<bf16x4*>(dst + (CH + r) * LDQ + kp(c4)) = lo;
+                const u32x2 x = *reinterpret_cast<const u32x2*>(dOg + (size_t)min(r, nv - 1) * ts_v + c4);
+                *reinterpret_cast<u32x2*>(st_do + r * LDQ + kp(c4)) = r < nv ? x : u32x2{0u, 0u};
             }
-        };
+            stage_f32(st_x, Zb, true);
+            f32x4 aq[4], a1[4], a2[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {   // dO, rows past the end zero (loads issued for every row)
-            const int idx = t + NTHR_CH * j, r = idx >> 5, c4 = (idx & 31) * 4;
-            const u32x2 x = *reinterpret_cast<const u32x2*>(dOg + (size_t)min(r, nv - 1) * ts_v + c4);
-            *reinterpret_cast<u32x2*>(st_do + r * LDQ + kp(c4)) = r < nv ? x : u32x2{0u, 0u};
-        }
-        stage_f32(st_x, Zb, true);
-        f32x4 aq[4], a1[4], a2[4];
+            for (int rt = 0; rt < 4; ++rt) aq[rt] = a1[rt] = a2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const float* Srow = S + (size_t)(16 * w + c) * DK;
+            const float* Drow = dSn + (size_t)(16 * w + c) * DK;
+            // this wave's S row (every k step) in flight during the staging and the barrier
+            f32x4 srow[4][2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) aq[rt] = a1[rt] = a2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const float* Srow = S + (size_t)(16 * w + c) * DK;
-        const float* Drow = dSn + (size_t)(16 * w + c) * DK;
-        // this wave's S row (every k step) in flight during the staging and the barrier
-        f32x4 srow[4][2];
+            for (int ks = 0; ks < 4; ++ks) {
+                srow[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
+                srow[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
+            }
+            __syncthreads();
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            srow[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
-            srow[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
-        }
-        __syncthreads();
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8 sh, sl;
+                split8(srow[ks][0], srow[ks][1], sh, sl);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 sh, sl;
-            split8(srow[ks][0], srow[ks][1], sh, sl);
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int o = (16 * rt + c) * LDQ + 32 * ks + 8 * g;
+                    const bf16x8 ao = lds_op16(st_do + o);
+                    aq[rt] = mma16k32(ao, sh, aq[rt]);
+                    aq[rt] = mma16k32(ao, sl, aq[rt]);
+                    const bf16x8 yh = lds_op16(st_x + o), yl = lds_op16(st_x + CH * LDQ + o);
+                    a2[rt] = mma16k32(yh, sh, a2[rt]);
+                    a2[rt] = mma16k32(yh, sl, a2[rt]);
+                    a2[rt] = mma16k32(yl, sh, a2[rt]);
+                }
+            }
+            // this wave's dSn row (and its S row again, for <S, dSn>), in flight during the V' staging
+            f32x4 drow[4][2], srw[4][2];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                drow[ks][0] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 4 * g);
+                drow[ks][1] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 16 + 4 * g);
+                srw[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
+                srw[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
+            }
+            __syncthreads();
+            stage_f32(st_x, Vpb, false);
+            __syncthreads();
+            {   // dgamma_C from the decay of the state, e^gamma_C <S, dSn>: this wave's
+                // 16 rows of both are in its registers
+                float part = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) part += dot4v(srw[ks][0], drow[ks][0]) + dot4v(srw[ks][1], drow[ks][1]);
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
+                if (lane == 0) atomicAdd(&sm.dgc, __expf(sm.gam[CH - 1]) * part);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8 dh, dl;
+                split8(drow[ks][0], drow[ks][1], dh, dl);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int o = (16 * rt + c) * LDQ + 32 * ks + 8 * g;
+                    const bf16x8 vh = lds_op16(st_x + o), vl = lds_op16(st_x + CH * LDQ + o);
+                    a1[rt] = mma16k32(vh, dh, a1[rt]);
+                    a1[rt] = mma16k32(vh, dl, a1[rt]);
+                    a1[rt] = mma16k32(vl, dh, a1[rt]);
+                }
+            }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                const int o = (16 * rt + c) * LDQ + 32 * ks + 8 * g;
-                const bf16x8 ao = lds_op16(st_do + o);
-                aq[rt] = mma16k32(ao, sh, aq[rt]);
-                aq[rt] = mma16k32(ao, sl, aq[rt]);
-                const bf16x8 yh = lds_op16(st_x + o), yl = lds_op16(st_x + CH * LDQ + o);
-                a2[rt] = mma16k32(yh, sh, a2[rt]);
-                a2[rt] = mma16k32(yh, sl, a2[rt]);
-                a2[rt] = mma16k32(yl, sh, a2[rt]);
-            }
-        }
-        // this wave's dSn row (and its S row again, for <S, dSn>), in flight during the V' staging
-        f32x4 drow[4][2], srw[4][2];
+                const int r0 = 16 * rt + 4 * g;
+                const f32x4 eg = *reinterpret_cast<const f32x4*>(sm.eg + r0);
+                const f32x4 fr = *reinterpret_cast<const f32x4*>(sm.fr + r0);
+                dq[rt] = (scale * eg) * aq[rt];
+                dk[rt] = fr * a1[rt] - eg * a2[rt];
+                // kappa_r = f_r K_r . dK~_r: through the decay factors of K~
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            drow[ks][0] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 4 * g);
-            drow[ks][1] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 16 + 4 * g);
-            srw[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
-            srw[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
-        }
-        __syncthreads();
-        stage_f32(st_x, Vpb, false);
-        __syncthreads();
-        {   // dgamma_C from the decay of the state, e^gamma_C <S, dSn>: this wave's
-            // 16 rows of both are in its registers
-            float part = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) part += dot4v(srw[ks][0], drow[ks][0]) + dot4v(srw[ks][1], drow[ks][1]);
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
-            if (lane == 0) atomicAdd(&sm.dgc, __expf(sm.gam[CH - 1]) * part);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 dh, dl;
-            split8(drow[ks][0], drow[ks][1], dh, dl);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const int o = (16 * rt + c) * LDQ + 32 * ks + 8 * g;
-                const bf16x8 vh = lds_op16(st_x + o), vl = lds_op16(st_x + CH * LDQ + o);
-                a1[rt] = mma16k32(vh, dh, a1[rt]);
-                a1[rt] = mma16k32(vh, dl, a1[rt]);
-                a1[rt] = mma16k32(vl, dh, a1[rt]);
-            }
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int r0 = 16 * rt + 4 * g;
-            const f32x4 eg = *reinterpret_cast<const f32x4*>(sm.eg + r0);
-            const f32x4 fr = *reinterpret_cast<const f32x4*>(sm.fr + r0);
-            dq[rt] = (scale * eg) * aq[rt];
-            dk[rt] = fr * a1[rt] - eg * a2[rt];
-            // kappa_r = f_r K_r . dK~_r: through the decay factors of K~
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = r0 + e;
-                // K[r][16 w + c] from the staged K^T (rows past the end hold the last row, as in Kg)
-                const int dkc = 16 * w + c;
-                const float kv = (float)sm.kt[dkc * LDKT + ((kp(r & ~3) ^ tswz(dkc)) | (r & 3))];
-                const float kap = tile_rowsum(fr[e] * kv * a1[rt][e]);
-                if (c == 0 && r < nv) {
-                    atomicAdd(&sm.dgam[r], -kap);
-                    atomicAdd(&sm.dgc, kap);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = r0 + e;
+                    // K[r][16 w + c] from the staged K^T (rows past the end hold the last row, as in Kg)
+                    const int dkc = 16 * w + c;
+                    const float kv = (float)sm.kt[dkc * LDKT + ((kp(r & ~3) ^ tswz(dkc)) | (r & 3))];
+                    const float kap = tile_rowsum(fr[e] * kv * a1[rt][e]);
+                    if (c == 0 && r < nv) {
+                        atomicAdd(&sm.dgam[r], -kap);
+                        atomicAdd(&sm.dgc, kap);
+                    }
                 }
             }
         }
-    }
-    // ---- 3. 64 x 64 tiles: dP -> Psi (images), dT (image), K K^T (kept)
-    const int prt = w >> 1, pct0 = 2 * (w & 1);
-    f32x4 kkt[2];
-    {
-        f32x4 dp[2], dt[2];
+        // ---- 3. 64 x 64 tiles: dP -> Psi (images), dT (image), K K^T (kept)
+        const int prt = w >> 1, pct0 = 2 * (w & 1);
+        f32x4 kkt[2];
+        {
+            f32x4 dp[2], dt[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dp[j] = dt[j] = kkt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int ra = 16 * prt + c;
-        const bf16* st_do = sm.sa;                       // staged in step 2 (dO, then V' hi / lo rows)
-        const bf16* st_v = sm.sa + CH * LDQ;
-        // the operands read from memory (K rows ra and rb, dV' row ra, Y rows rb), one k step ahead
-        struct Ops3 {
-            u32x2 ka[2], kb[2][2];
-            f32x4 dv[2], y[2][2];
-        };
-        const float brb[2] = {sm.bet[16 * pct0 + c], sm.bet[16 * (pct0 + 1) + c]};
-        auto load3 = [&](Ops3& o, int ks) {
-            const bf16* kra = Kg + (size_t)min(ra, nv - 1) * ts + 32 * ks + 4 * g;
-            o.ka[0] = *reinterpret_cast<const u32x2*>(kra);
-            o.ka[1] = *reinterpret_cast<const u32x2*>(kra + 16);
-            const float* dvr = dVb + (size_t)ra * DK + 32 * ks + 4 * g;
-            o.dv[0] = *reinterpret_cast<const f32x4*>(dvr);
-            o.dv[1] = *reinterpret_cast<const f32x4*>(dvr + 16);
+            for (int j = 0; j < 2; ++j) dp[j] = dt[j] = kkt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int ra = 16 * prt + c;
+            const bf16* st_do = sm.sa;                       // staged in step 2 (dO, then V' hi / lo rows)
+            const bf16* st_v = sm.sa + CH * LDQ;
+            // the operands read from memory (K rows ra and rb, dV' row ra, Y rows rb), one k step ahead
+            struct Ops3 {
+                u32x2 ka[2], kb[2][2];
+                f32x4 dv[2], y[2][2];
+            };
+            const float brb[2] = {sm.bet[16 * pct0 + c], sm.bet[16 * (pct0 + 1) + c]};
+            auto load3 = [&](Ops3& o, int ks) {
+                const bf16* kra = Kg + (size_t)min(ra, nv - 1) * ts + 32 * ks + 4 * g;
+                o.ka[0] = *reinterpret_cast<const u32x2*>(kra);
+                o.ka[1] = *reinterpret_cast<const u32x2*>(kra + 16);
+                const float* dvr = dVb + (size_t)ra * DK + 32 * ks + 4 * g;
+                o.dv[0] = *reinterpret_cast<const f32x4*>(dvr);
+                o.dv[1] = *reinterpret_cast<const f32x4*>(dvr + 16);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int rb = 16 * (pct0 + j) + c;
+                    const float* yr = Yb + (size_t)rb * DK + 32 * ks + 4 * g;
+                    o.y[j][0] = *reinterpret_cast<const f32x4*>(yr);
+                    o.y[j][1] = *reinterpret_cast<const f32x4*>(yr + 16);
+                    const bf16* krb = Kg + (size_t)min(rb, nv - 1) * ts + 32 * ks + 4 * g;
+                    o.kb[j][0] = *reinterpret_cast<const u32x2*>(krb);
+                    o.kb[j][1] = *reinterpret_cast<const u32x2*>(krb + 16);
+                }
+            };
+            // the fp32 P entries of this wave's dP tiles (for dP o P after the loop),
+            // loaded in the last k step in place of that step's operands
+            float pP[2][4];
+            Ops3 cur, nxt;
+            load3(cur, 0);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks < 3) {
+                    load3(nxt, ks + 1);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pP[j][e] = tp[CH * CH + (16 * prt + 4 * g + e) * CH + 16 * (pct0 + j) + c];
+                }
+                const bf16x8 ao = lds_op16(st_do + ra * LDQ + 32 * ks + 8 * g);
+                const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{cur.ka[0][0], cur.ka[0][1], cur.ka[1][0], cur.ka[1][1]});
+                bf16x8 adh, adl;
+                split8(cur.dv[0], cur.dv[1], adh, adl);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int rb = 16 * (pct0 + j) + c;
+                    bf16x8 yh, yl;
+                    const bf16x8 vh = lds_op16(st_v + rb * LDQ + 32 * ks + 8 * g);
+                    const bf16x8 vl = lds_op16(st_v + (CH + rb) * LDQ + 32 * ks + 8 * g);
+                    dp[j] = mma16k32(ao, vh, dp[j]);
+                    dp[j] = mma16k32(ao, vl, dp[j]);
+                    split8(cur.y[j][0] * brb[j], cur.y[j][1] * brb[j], yh, yl);
+                    dt[j] = mma16k32(adh, yh, dt[j]);
+                    dt[j] = mma16k32(adh, yl, dt[j]);
+                    dt[j] = mma16k32(adl, yh, dt[j]);
+                    const bf16x8 bk =
+                        __builtin_bit_cast(bf16x8, u32x4{cur.kb[j][0][0], cur.kb[j][0][1], cur.kb[j][1][0], cur.kb[j][1][1]});
+                    kkt[j] = mma16k32(ak, bk, kkt[j]);
+                }
+                if (ks < 3) cur = nxt;
+            }
+            __syncthreads();   // the staging area becomes the image slots again
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int rb = 16 * (pct0 + j) + c;
-                const float* yr = Yb + (size_t)rb * DK + 32 * ks + 4 * g;
-                o.y[j][0] = *reinterpret_cast<const f32x4*>(yr);
-                o.y[j][1] = *reinterpret_cast<const f32x4*>(yr + 16);
-                const bf16* krb = Kg + (size_t)min(rb, nv - 1) * ts + 32 * ks + 4 * g;
-                o.kb[j][0] = *reinterpret_cast<const u32x2*>(krb);
-                o.kb[j][1] = *reinterpret_cast<const u32x2*>(krb + 16);
+                const int ct = pct0 + j, m = 16 * ct + c;
+                f32x4 psi, E;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * prt + 4 * g + e;
+                    const float d = scale * dp[j][e];
+                    const bool low = m <= r;
+                    psi[e] = low ? d * __expf(sm.gam[r] - sm.gam[m]) : 0.f;
+                    E[e] = low ? d * pP[j][e] : 0.f;   // dP o P (P is the fp32 copy)
+                }
+                put_img(sm.sa, prt, ct, c, g, psi);
+                put_img_t(sm.sb, prt, ct, c, g, psi);
+                put_img(sm.sc, prt, ct, c, g, dt[j]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float rs = tile_rowsum(E[e]);
+                    if (c == 0) atomicAdd(&sm.dgam[16 * prt + 4 * g + e], rs);
+                }
+                const float cs = tile_colsum(E);
+                if (g == 0) atomicAdd(&sm.dgam[m], -cs);
             }
-        };
-        // the fp32 P entries of this wave's dP tiles (for dP o P after the loop),
-        // loaded in the last k step in place of that step's operands
-        float pP[2][4];
-        Ops3 cur, nxt;
-        load3(cur, 0);
+        }
+        __syncthreads();
+        // ---- 4. W1 = dT T^T (tiles); dq += Psi K; dk += Psi^T Q
+        f32x4 w1[2];
+        {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (ks < 3) {
-                load3(nxt, ks + 1);
-            } else {
+            for (int j = 0; j < 2; ++j) w1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+            for (int ks = 0; ks < 2; ++ks) {
+                const int oa = (16 * prt + c) * LDP + 32 * ks + 8 * g;
+                const bf16x8 ah = lds_op16(sm.sc + oa), al = lds_op16(sm.sc + CH * LDP + oa);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        pP[j][e] = tp[CH * CH + (16 * prt + 4 * g + e) * CH + 16 * (pct0 + j) + c];
+                for (int j = 0; j < 2; ++j) {
+                    const int ob = (16 * (pct0 + j) + c) * LDP + 32 * ks + 8 * g;
+                    const bf16x8 bh = lds_op16(sm.tim + ob), bl = lds_op16(sm.tim + CH * LDP + ob);
+                    w1[j] = mma16k32(ah, bh, w1[j]);
+                    w1[j] = mma16k32(ah, bl, w1[j]);
+                    w1[j] = mma16k32(al, bh, w1[j]);
+                }
             }
-            const bf16x8 ao = lds_op16(st_do + ra * LDQ + 32 * ks + 8 * g);
-            const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{cur.ka[0][0], cur.ka[0][1], cur.ka[1][0], cur.ka[1][1]});
-            bf16x8 adh, adl;
-            split8(cur.dv[0], cur.dv[1], adh, adl);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int ob = (16 * w + c) * LDKT + ((32 * ks + 8 * g) ^ (8 * w));
+                const bf16x8 kb = lds_op16(sm.kt + ob), qb = lds_op16(sm.qt + ob);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int oa = (16 * rt + c) * LDP + 32 * ks + 8 * g;
+                    dq[rt] = mma16k32(lds_op16(sm.sa + oa), kb, dq[rt]);
+                    dq[rt] = mma16k32(lds_op16(sm.sa + CH * LDP + oa), kb, dq[rt]);
+                    dk[rt] = mma16k32(lds_op16(sm.sb + oa), qb, dk[rt]);
+                    dk[rt] = mma16k32(lds_op16(sm.sb + CH * LDP + oa), qb, dk[rt]);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) put_img_t(sm.sc, prt, pct0 + j, c, g, w1[j]);   // W1^T
+        __syncthreads();
+            // the next item's staging and step-1 operands, in flight through steps 5 and 6
+        // (after the last item, this one's again: every path issues the loads, so
+        // that the operands are dead through steps 2 to 4)
+        bwd_item_fetch(p, item + gridDim.x < n_items ? item + gridDim.x : item, in);
+        // ---- 5. dA = -T^T W1 (strictly lower) -> dbeta, dgamma, G, G^T (images)
+        {
+            f32x4 da[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) da[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int oa = (16 * prt + c) * LDP + 32 * ks + 8 * g;
+                const bf16x8 ah = lds_op16(sm.ttim + oa), al = lds_op16(sm.ttim + CH * LDP + oa);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int ob = (16 * (pct0 + j) + c) * LDP + 32 * ks + 8 * g;
+                    const bf16x8 bh = lds_op16(sm.sc + ob), bl = lds_op16(sm.sc + CH * LDP + ob);
+                    da[j] = mma16k32(ah, bh, da[j]);
+                    da[j] = mma16k32(ah, bl, da[j]);
+                    da[j] = mma16k32(al, bh, da[j]);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int rb = 16 * (pct0 + j) + c;
-                bf16x8 yh, yl;
-                const bf16x8 vh = lds_op16(st_v + rb * LDQ + 32 * ks + 8 * g);
-                const bf16x8 vl = lds_op16(st_v + (CH + rb) * LDQ + 32 * ks + 8 * g);
-                dp[j] = mma16k32(ao, vh, dp[j]);
-                dp[j] = mma16k32(ao, vl, dp[j]);
-                split8(cur.y[j][0] * brb[j], cur.y[j][1] * brb[j], yh, yl);
-                dt[j] = mma16k32(adh, yh, dt[j]);
-                dt[j] = mma16k32(adh, yl, dt[j]);
-                dt[j] = mma16k32(adl, yh, dt[j]);
-                const bf16x8 bk =
-                    __builtin_bit_cast(bf16x8, u32x4{cur.kb[j][0][0], cur.kb[j][0][1], cur.kb[j][1][0], cur.kb[j][1][1]});
-                kkt[j] = mma16k32(ak, bk, kkt[j]);
+                const int ct = pct0 + j, i = 16 * ct + c;
+                f32x4 G, gA;
+                float dbr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * prt + 4 * g + e;
+                    const bool low = i < r;
+                    const float ex = low ? __expf(sm.gam[r] - sm.gam[i]) : 0.f;
+                    const float dA = low ? -da[j][e] : 0.f;
+                    const float wv = dA * ex * kkt[j][e];   // dA_ri times dA_ri / dbeta_r
+                    dbr[e] = wv;
+                    gA[e] = wv * sm.bet[r];                 // dA_ri A_ri
+                    G[e] = dA * sm.bet[r] * ex;
+                }
+                put_img(sm.sa, prt, ct, c, g, G);
+                put_img_t(sm.sb, prt, ct, c, g, G);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float rb = tile_rowsum(dbr[e]), rg = tile_rowsum(gA[e]);
+                    if (c == 0) {
+                        atomicAdd(&sm.dbe[16 * prt + 4 * g + e], rb);
+                        atomicAdd(&sm.dgam[16 * prt + 4 * g + e], rg);
+                    }
+                }
+                const float cs = tile_colsum(gA);
+                if (g == 0) atomicAdd(&sm.dgam[i], -cs);
             }
-            if (ks < 3) cur = nxt;
         }
-        __syncthreads();   // the staging area becomes the image slots again
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int ct = pct0 + j, m = 16 * ct + c;
-            f32x4 psi, E;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * prt + 4 * g + e;
-                const float d = scale * dp[j][e];
-                const bool low = m <= r;
-                psi[e] = low ? d * __expf(sm.gam[r] - sm.gam[m]) : 0.f;
-                E[e] = low ? d * pP[j][e] : 0.f;   // dP o P (P is the fp32 copy)
-            }
-            put_img(sm.sa, prt, ct, c, g, psi);
-            put_img_t(sm.sb, prt, ct, c, g, psi);
-            put_img(sm.sc, prt, ct, c, g, dt[j]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float rs = tile_rowsum(E[e]);
-                if (c == 0) atomicAdd(&sm.dgam[16 * prt + 4 * g + e], rs);
-            }
-            const float cs = tile_colsum(E);
-            if (g == 0) atomicAdd(&sm.dgam[m], -cs);
-        }
-    }
-    __syncthreads();
-    // ---- 4. W1 = dT T^T (tiles); dq += Psi K; dk += Psi^T Q
-    f32x4 w1[2];
-    {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) w1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        // ---- 6. dk += (G + G^T) K
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int oa = (16 * prt + c) * LDP + 32 * ks + 8 * g;
-            const bf16x8 ah = lds_op16(sm.sc + oa), al = lds_op16(sm.sc + CH * LDP + oa);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int ob = (16 * (pct0 + j) + c) * LDP + 32 * ks + 8 * g;
-                const bf16x8 bh = lds_op16(sm.tim + ob), bl = lds_op16(sm.tim + CH * LDP + ob);
-                w1[j] = mma16k32(ah, bh, w1[j]);
-                w1[j] = mma16k32(ah, bl, w1[j]);
-                w1[j] = mma16k32(al, bh, w1[j]);
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ob = (16 * w + c) * LDKT + ((32 * ks + 8 * g) ^ (8 * w));
-            const bf16x8 kb = lds_op16(sm.kt + ob), qb = lds_op16(sm.qt + ob);
+            const bf16x8 kb = lds_op16(sm.kt + (16 * w + c) * LDKT + ((32 * ks + 8 * g) ^ (8 * w)));
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int oa = (16 * rt + c) * LDP + 32 * ks + 8 * g;
-                dq[rt] = mma16k32(lds_op16(sm.sa + oa), kb, dq[rt]);
-                dq[rt] = mma16k32(lds_op16(sm.sa + CH * LDP + oa), kb, dq[rt]);
-                dk[rt] = mma16k32(lds_op16(sm.sb + oa), qb, dk[rt]);
-                dk[rt] = mma16k32(lds_op16(sm.sb + CH * LDP + oa), qb, dk[rt]);
+                dk[rt] = mma16k32(lds_op16(sm.sa + oa), kb, dk[rt]);
+                dk[rt] = mma16k32(lds_op16(sm.sa + CH * LDP + oa), kb, dk[rt]);
+                dk[rt] = mma16k32(lds_op16(sm.sb + oa), kb, dk[rt]);
+                dk[rt] = mma16k32(lds_op16(sm.sb + CH * LDP + oa), kb, dk[rt]);
             }
         }
-    }
-    __syncthreads();
+        // ---- outputs: per-value-head dq, dk parts; dg (reverse cumulative sum of dgamma), dbeta
 #pragma unroll
-    for (int j = 0; j < 2; ++j) put_img_t(sm.sc, prt, pct0 + j, c, g, w1[j]);   // W1^T
-    __syncthreads();
-    // ---- 5. dA = -T^T W1 (strictly lower) -> dbeta, dgamma, G, G^T (images)
-    {
-        f32x4 da[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) da[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int oa = (16 * prt + c) * LDP + 32 * ks + 8 * g;
-            const bf16x8 ah = lds_op16(sm.ttim + oa), al = lds_op16(sm.ttim + CH * LDP + oa);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int ob = (16 * (pct0 + j) + c) * LDP + 32 * ks + 8 * g;
-                const bf16x8 bh = lds_op16(sm.sc + ob), bl = lds_op16(sm.sc + CH * LDP + ob);
-                da[j] = mma16k32(ah, bh, da[j]);
-                da[j] = mma16k32(ah, bl, da[j]);
-                da[j] = mma16k32(al, bh, da[j]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int ct = pct0 + j, i = 16 * ct + c;
-            f32x4 G, gA;
-            float dbr[4];
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * prt + 4 * g + e;
-                const bool low = i < r;
-                const float ex = low ? __expf(sm.gam[r] - sm.gam[i]) : 0.f;
-                const float dA = low ? -da[j][e] : 0.f;
-                const float wv = dA * ex * kkt[j][e];   // dA_ri times dA_ri / dbeta_r
-                dbr[e] = wv;
-                gA[e] = wv * sm.bet[r];                 // dA_ri A_ri
-                G[e] = dA * sm.bet[r] * ex;
-            }
-            put_img(sm.sa, prt, ct, c, g, G);
-            put_img_t(sm.sb, prt, ct, c, g, G);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float rb = tile_rowsum(dbr[e]), rg = tile_rowsum(gA[e]);
-                if (c == 0) {
-                    atomicAdd(&sm.dbe[16 * prt + 4 * g + e], rb);
-                    atomicAdd(&sm.dgam[16 * prt + 4 * g + e], rg);
+                const int r = 16 * rt + 4 * g + e;
+                if (r < nv) {
+                    const size_t o = ((tok0 + r) * p.h_v + h) * DK + 16 * w + c;
+                    p.dq_part[o] = dq[rt][e];
+                    p.dk_part[o] = dk[rt][e];
                 }
             }
-            const float cs = tile_colsum(gA);
-            if (g == 0) atomicAdd(&sm.dgam[i], -cs);
-        }
-    }
-    __syncthreads();
-    // ---- 6. dk += (G + G^T) K
+        if (t < CH) {
+            float x = sm.dgam[t] + (t == CH - 1 ? sm.dgc : 0.f);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 kb = lds_op16(sm.kt + (16 * w + c) * LDKT + ((32 * ks + 8 * g) ^ (8 * w)));
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int oa = (16 * rt + c) * LDP + 32 * ks + 8 * g;
-            dk[rt] = mma16k32(lds_op16(sm.sa + oa), kb, dk[rt]);
-            dk[rt] = mma16k32(lds_op16(sm.sa + CH * LDP + oa), kb, dk[rt]);
-            dk[rt] = mma16k32(lds_op16(sm.sb + oa), kb, dk[rt]);
-            dk[rt] = mma16k32(lds_op16(sm.sb + CH * LDP + oa), kb, dk[rt]);
-        }
-    }
-    // ---- outputs: per-value-head dq, dk parts; dg (reverse cumulative sum of dgamma), dbeta
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rt + 4 * g + e;
-            if (r < nv) {
-                const size_t o = ((tok0 + r) * p.h_v + h) * DK + 16 * w + c;
-                p.dq_part[o] = dq[rt][e];
-                p.dk_part[o] = dk[rt][e];
+            for (int d = 1; d < 64; d <<= 1) {
+                const float y = __shfl_down(x, d, 64);
+                if (t + d < 64) x += y;
             }
-        }
-    if (t < CH) {
-        float x = sm.dgam[t] + (t == CH - 1 ? sm.dgc : 0.f);
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float y = __shfl_down(x, d, 64);
-            if (t + d < 64) x += y;
-        }
-        if (t < nv) {
-            p.dg[(tok0 + t) * p.h_v + h] = x;
-            p.dbeta[(tok0 + t) * p.h_v + h] = sm.dbe[t];
+            if (t < nv) {
+                p.dg[(tok0 + t) * p.h_v + h] = x;
+                p.dbeta[(tok0 + t) * p.h_v + h] = sm.dbe[t];
+            }
         }
     }
 }
@@ -2696,7 +2742,14 @@ int launch_bwd_chain_mma(const BwdParams& p, void* stream) {
 
 int launch_bwd_chunk_mma(const BwdParams& p, void* stream) {
     if (p.n_chunks <= 0) return 0;
-    hipLaunchKernelGGL(k_bwd_chunk_mma, dim3(p.n_chunks, p.h_v), dim3(NTHR_CH), 0, (hipStream_t)stream, p);
+    // one workgroup per CU (persistent over the items)
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return (int)e;
+    const long long items = (long long)p.n_chunks * p.h_v;
+    const unsigned grid = (unsigned)std::min<long long>(items, std::max(n_cu, 1));
+    hipLaunchKernelGGL(k_bwd_chunk_mma, dim3(grid), dim3(NTHR_CH), 0, (hipStream_t)stream, p);
     return launched();
 }
 
