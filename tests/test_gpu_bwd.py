@@ -96,6 +96,17 @@ def test_bwd_varlen_auto_cp():
     np.testing.assert_array_equal(got["d_initial"][1], d_fin[1])
 
 
+def test_bwd_items_past_one_round():
+    """More (chunk, head) items than the chunk-gradient kernel has workgroups
+    (one per CU) and not a multiple of them: 71 chunks x 4 heads = 284 items,
+    so some workgroups take a second item (and fetch it during the first)."""
+    inp = make_inputs(name="bwdR", B=1, T=64 * 70 + 9, h_qk=1, h_v=4, seed=36, gate="mixed", init_std=0.1)
+    print(f"\n[bwd/items] T={inp.T}", flush=True)
+    d_out, d_fin = _grads(136, inp.v.shape, 1, inp.h_v)
+    got = _run(inp, d_out, d_fin, cp_mode="auto", n_cu=64, lam=0.5)
+    _check(inp, d_out, d_fin, got, "items past one round")
+
+
 # fp32 inputs are rounded once to bf16 inside the backward, which then runs as
 # for bf16 inputs and writes every gradient in fp32. Two checks: against the
 # oracle's gradient at the rounded inputs, every output (dq, dk, dv now fp32
