@@ -71,6 +71,7 @@ struct Plan {
     int s_dv = 1;                 // column blocks of d_v in the fused forward
     float lambda = kDefaultLambda, eps = kDefaultNoiseFloor;
     int comb_G = 0, comb_J = 0;   // grouped combine of the backward's forward re-run (0: one chain)
+    int g16_G = 0, g16_J = 0;     // grouped combine of the forward (0: one chain)
     FwdLayout fw;                 // the forward (fp16 chain kernels)
     FwdLayout re;                 // the backward's forward re-run (split bf16 chain kernels)
     size_t ws_bytes = 0;          // == fw.bytes
@@ -148,6 +149,28 @@ void combine_grouping(int nb, long long heads, int n_cu, int J_max, int32_t* G_o
         const long long wgs = 8LL * (J - 1) * heads, rounds = (wgs + n_cu - 1) / n_cu;
         const double slow = 2 * wgs <= n_cu ? 1.0 : 2.5;
         const double steps = slow * (G * rounds + G - 1) + std::max(J - 2, 0) + 4;
+        if (steps < best) {
+            best = steps;
+            *G_out = G;
+            *J_out = J;
+        }
+    }
+}
+
+// The forward's (fp16) combine grouping: G boundaries per group when its two
+// launches' 2 G + J - 2 steps, plus about eight steps for the extra launch
+// (measured: a launch costs about as much as eight boundary steps), beat the
+// single chain's nb steps; the composing launch's workgroups (16 per group and
+// exact (sequence, head)) beyond two per CU stretch its steps.
+void combine16_grouping(int nb, long long exact_heads, int n_cu, int32_t* G_out, int32_t* J_out) {
+    *G_out = 0;
+    *J_out = 0;
+    double best = nb;
+    for (int G = 2; G < nb; ++G) {
+        const int J = (nb + G - 1) / G;
+        if (J < 2) break;
+        const double load = std::max(1.0, (double)(16LL * (J - 1) * exact_heads) / (2.0 * std::max(n_cu, 1)));
+        const double steps = G * load + (J - 2) + G + 8;
         if (steps < best) {
             best = steps;
             *G_out = G;
@@ -298,6 +321,15 @@ gdn_status make_plan(const gdn_desc* d, Plan* pl, bool column_split = true) {
             F.off_H = off;     off = align_up(off + st_bytes, 256);
             F.off_M = off;     off = align_up(off + st_bytes / 2, 256);
             F.off_warm = off;  off = align_up(off + nsg * sizeof(int32_t), 256);
+            // the grouped combine: per (sequence, group, head) the composed map CM
+            // (fp16 image, 32 KiB) and CH (fp32, 64 KiB)
+            const long long heads = std::max(1LL, ((long long)P.n_seqs * d->h_v * 3 + 5) / 10);
+            combine16_grouping(P.P_max - 1, heads, P.n_cu, &P.g16_G, &P.g16_J);
+            if (P.g16_G) {
+                const size_t grp = (size_t)P.n_seqs * P.g16_J * d->h_v * kStateElems;
+                F.off_GM = off; off = align_up(off + grp * 2, 256);
+                F.off_GH = off; off = align_up(off + grp * sizeof(float), 256);
+            }
         }
         F.bytes = off;
     }
@@ -433,10 +465,10 @@ void log_plan(const gdn_desc* d, const Plan& P) {
     std::fprintf(stderr,
                  "[gdn] fwd B=%d T=%d h_qk=%d h_v=%d io=%s cp_mode=%d: chunks=%d (max %d) cp_on=%d L=%d "
                  "segments=%d (max %d per sequence) dv_split=%d w=%d eps=%g lambda=%g n_cu=%d cp_order=%d "
-                 "cp_split=%d workspace=%zu\n",
+                 "cp_split=%d combine_G=%d combine_J=%d workspace=%zu\n",
                  d->B, d->T, d->h_qk, d->h_v, d->io_dtype == GDN_BF16 ? "bf16" : "f32", d->cp_mode,
                  P.n_chunks_total, P.n_chunks_max, P.cp_on, P.L, P.n_segments, P.P_max, P.s_dv, P.w,
-                 (double)P.eps, (double)P.lambda, P.n_cu, P.cp_order, P.cp_split, P.ws_bytes);
+                 (double)P.eps, (double)P.lambda, P.n_cu, P.cp_order, P.cp_split, P.g16_G, P.g16_J, P.ws_bytes);
 }
 
 gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* v, const float* g,
@@ -458,6 +490,12 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
     if (P.n_chunks_total > 0) {
         p.tb16 = w8 + P.fw.off_T;
         p.gf16 = reinterpret_cast<float*>(w8 + P.fw.off_GB);
+    }
+    p.comb_G = P.g16_G;
+    p.comb_J = P.g16_J;
+    if (P.cp_on && P.g16_G) {
+        p.seg_GM = reinterpret_cast<float*>(w8 + P.fw.off_GM);
+        p.seg_GH = reinterpret_cast<float*>(w8 + P.fw.off_GH);
     }
     const int io = d->io_dtype == GDN_BF16 ? gdn::kIoBf16 : gdn::kIoF32;
     const hipStream_t hs = (hipStream_t)stream;
@@ -726,8 +764,8 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->lambda = P.lambda;
     out->noise_floor = P.eps;
     out->workspace_bytes = P.ws_bytes;
-    out->combine_group = P.comb_G;
-    out->combine_groups = P.comb_J;
+    out->combine_group = P.g16_G;
+    out->combine_groups = P.g16_J;
     out->dv_split = P.s_dv;
     out->cp_layout = P.cp_on && desc->io_dtype == GDN_BF16 ? (P.cp_split ? 2 : 1) : 0;
     g_last_error.clear();

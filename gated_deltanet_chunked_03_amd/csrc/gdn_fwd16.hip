@@ -612,17 +612,132 @@ __global__ __launch_bounds__(NT8) void k_cp_prep16(Params p) {
 }
 
 // ----------------------------------------------------------------------------
-// The segment combine: one 4-wave workgroup per (sequence, value head,
-// 16-column tile u), the eight tiles of a (sequence, head) on one XCD. Boundary s (1 <= s < P): exact, S0(s) = M_{s-1} S0(s-1)
-// + H_{s-1} (the map product on fp16 operands: the M image as A, the state
-// column tile as B; M_0 only with an initial state); warm-up, S0(s) is the
-// warm-up state k_cp_prep16 wrote. Wave r owns rows [32 r, 32 r + 32) of the
-// column tile -- exactly the k step r of the next product's B operand -- and
-// hands its fp16 rows to the others through LDS once per step, so a step is
-// eight MFMAs per wave plus one exchange. The boundary flags are read into LDS
-// first; each step's operands (eight M fragments, two H tiles per lane) are
-// loaded two steps ahead, and every step issues the same memory operations.
+// The segment combine: the boundary states S0(s) of the exact boundaries from
+// the segment maps, in 4-wave workgroups, each over one 16-column tile of the
+// state (the columns evolve independently).
 constexpr int NTC = 256;
+// Boundary count, first segment slot and boundary flags (LDS, 0 exact) of a
+// (sequence, head); false if no boundary is exact (nothing to chain).
+__device__ bool comb_setup(const Params& p, int seq, int h, int* flags, int& P, int& seg_base) {
+    if (!p.cu) {
+        P = n_segs_of(n_chunks_of(p.seq_len), p.L);
+        seg_base = seq * P;
+    } else {
+        seg_base = 0;
+        for (int n = 0; n < seq; ++n) seg_base += n_segs_of(n_chunks_of(p.cu[n + 1] - p.cu[n]), p.L);
+        P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
+    }
+    if (P <= 1 || P > kMaxSegsPerSeq) return false;
+    int any_exact = 0;
+    for (int s = 1 + (int)threadIdx.x; s < P; s += NTC) {
+        const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h] & 255;
+        flags[s] = f;
+        any_exact |= f == 0;
+    }
+    return __syncthreads_or(any_exact);
+}
+
+// Column tile u of a row-major 128 x 128 state (row tiles 2 r, 2 r + 1 of wave r).
+__device__ __forceinline__ void comb_load_rm_tile(const float* S0, int u, f32x4 cur[2]) {
+    const int r = wave_id(), lane = lane_id(), c = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cur[tt][e] = S0[(16 * (2 * r + tt) + 4 * g + e) * DK + 16 * u + c];
+}
+// The state tile X (row tiles 2 r, 2 r + 1 of column tile u, in registers) as
+// this wave's k step of the next product's B operand.
+__device__ __forceinline__ void comb_put(f16* xb, const f32x4 cur[2]) {
+    *reinterpret_cast<f16x8*>(xb + (wave_id() * 64 + lane_id()) * 8) = pack8h(cur[0], cur[1]);
+}
+// ... from a block in tile order
+__device__ __forceinline__ void comb_load_tile(const float* src, int u, f32x4 cur[2]) {
+    const int r = wave_id(), lane = lane_id();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) cur[tt] = *reinterpret_cast<const f32x4*>(src + (((2 * r + tt) * 8 + u) * 64 + lane) * 4);
+}
+
+struct CombOps {
+    f32x4 add[2];   // H_{b-1} or the warm-up state, row tiles 2 r, 2 r + 1
+    u32x4 m[8];     // M_{b-1} fragments (row tile 2 r + f / 4, k step f % 4)
+};
+
+// The chain over boundaries [b_lo, b_hi) of one (sequence, head) for column
+// tile u, from X(b_lo - 1), which the caller has put in xb[0]; on return cur
+// holds X(b_hi - 1). An exact boundary maps X(b) = M_{b-1} X(b-1) + add (M_0
+// only to an initial state), a warm-up one sets X(b) = add. KIND 0: add = H_{b-1}
+// or the warm-up state, every X(b) stored as the boundary state; KIND 1 (a
+// group's composed map CM): add = 0; KIND 2 (its CH): as KIND 0, nothing stored.
+// Wave r owns rows [32 r, 32 r + 32) of the tile -- exactly the k step r of the
+// next product's B operand -- and hands its fp16 rows to the others through
+// LDS once per step, so a step is eight MFMAs per wave plus one exchange. Each
+// step's operands are loaded two steps ahead, and every step issues the same
+// memory operations (both cases evaluated and selected).
+template <int KIND>
+__device__ void comb_chain(const Params& p, const int* flags, f16 (*xb)[4 * 64 * 8], int seg_base, int h, int u,
+                           int b_lo, int b_hi, f32x4 cur[2]) {
+    const int lane = lane_id(), r = wave_id();
+    auto fetch = [&](CombOps& o, int b) {
+        b = min(b, b_hi - 1);
+        const int f = __builtin_amdgcn_readfirstlane(flags[b]);   // (uniform: a branch-free select)
+        const float* src = f ? p.seg_state + tiles_off(seg_base + b, p.h_v, h)
+                             : p.seg_H + tiles_off(seg_base + b - 1, p.h_v, h);
+        if (KIND != 1) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                o.add[tt] = *reinterpret_cast<const f32x4*>(src + (((2 * r + tt) * 8 + u) * 64 + lane) * 4);
+        }
+        const u32x4* mi = reinterpret_cast<const u32x4*>(reinterpret_cast<const f16*>(p.seg_M) +
+                                                          tiles_off(seg_base + b - 1, p.h_v, h));
+#pragma unroll
+        for (int f8 = 0; f8 < 8; ++f8) o.m[f8] = mi[(8 * r + f8) * 64 + lane];
+    };
+    auto step = [&](int b, const CombOps& o, int buf) {
+        __syncthreads();   // the previous X's B operand is in xb[buf]
+        const bool exact = __builtin_amdgcn_readfirstlane(flags[b]) == 0;
+        const bool mm = exact && (b > 1 || p.s_init);
+        f16x8 Sb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Sb[j] = *reinterpret_cast<const f16x8*>(xb[buf] + (j * 64 + lane) * 8);
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) acc[tt] = mmh(__builtin_bit_cast(f16x8, o.m[4 * tt + j]), Sb[j], acc[tt]);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            // (a select, not a product with 0: the maps of warm-up boundaries and
+            // M_0 without an initial state are never written and may hold NaNs)
+            const f32x4 add = KIND == 1 ? f32x4{0.f, 0.f, 0.f, 0.f} : o.add[tt];
+            cur[tt] = mm ? add + acc[tt] : add;
+        }
+        if (KIND == 0) {
+            float* dst = p.seg_state + tiles_off(seg_base + b, p.h_v, h);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                *reinterpret_cast<f32x4*>(dst + (((2 * r + tt) * 8 + u) * 64 + lane) * 4) = cur[tt];
+        }
+        comb_put(xb[buf ^ 1], cur);
+    };
+    CombOps A, B;
+    fetch(A, b_lo);
+    fetch(B, b_lo + 1);
+    int b = b_lo;
+    for (; b + 1 < b_hi; b += 2) {
+        step(b, A, 0);
+        fetch(A, b + 2);
+        step(b + 1, B, 1);
+        fetch(B, b + 3);
+    }
+    if (b < b_hi) step(b, A, 0);
+}
+
+// The segment combine as one chain: one 4-wave workgroup per (sequence, value
+// head, 16-column tile u), the eight tiles of a (sequence, head) on one XCD.
+// Boundary s (1 <= s < P): exact, S0(s) = M_{s-1} S0(s-1) + H_{s-1} (the map
+// product on fp16 operands: the M image as A, the state column tile as B; M_0
+// only with an initial state); warm-up, S0(s) is the warm-up state the CP
+// preprocessing wrote.
 __global__ __launch_bounds__(NTC) void k_combine16(Params p) {
     __shared__ int flags[kMaxSegsPerSeq];
     __shared__ __attribute__((aligned(16))) f16 xb[2][4 * 64 * 8];   // the state tile as B operands, per k step
@@ -635,92 +750,136 @@ __global__ __launch_bounds__(NTC) void k_combine16(Params p) {
     if (q >= p.n_seqs * p.h_v) return;
     const int seq = q / p.h_v, h = q % p.h_v;
     int P, seg_base;
-    if (!p.cu) {
-        P = n_segs_of(n_chunks_of(p.seq_len), p.L);
-        seg_base = seq * P;
-    } else {
-        seg_base = 0;
-        for (int n = 0; n < seq; ++n) seg_base += n_segs_of(n_chunks_of(p.cu[n + 1] - p.cu[n]), p.L);
-        P = n_segs_of(n_chunks_of(p.cu[seq + 1] - p.cu[seq]), p.L);
+    if (!comb_setup(p, seq, h, flags, P, seg_base)) return;
+    f32x4 cur[2];
+    if (p.s_init) comb_load_rm_tile(p.s_init + tiles_off(seq, p.h_v, h), u, cur);
+    else cur[0] = cur[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    comb_put(xb[0], cur);
+    comb_chain<0>(p, flags, xb, seg_base, h, u, 1, P, cur);
+}
+
+// The combine in two launches over groups of G = comb_G consecutive
+// boundaries (group j: boundaries [1 + j G, min(1 + (j + 1) G, P)); its last,
+// e_j): 2 G + J - 2 steps in sequence instead of P - 1.
+//   k_comb16_groups  group 0 as a chain from S0(0); every later group, in 16
+//                    column tiles of X = [CM | CH] from [I | 0], composes its
+//                    boundaries' affine maps into one, S -> CM S + CH (CM as an
+//                    fp16 A-operand image, CH in tile order);
+//   k_comb16_apply   every group j >= 1: S0(e_{j-1}) from S0(e_0) through
+//                    CM_i, CH_i (i = 1 .. j - 1), then its boundaries in turn.
+// The (sequence, head, group) bundles' workgroups share an XCD.
+__device__ __forceinline__ int comb_group_end(int j, int G, int P) { return min((j + 1) * G, P - 1); }
+
+__global__ __launch_bounds__(NTC) void k_comb16_groups(Params p) {
+    __shared__ int flags[kMaxSegsPerSeq];
+    __shared__ __attribute__((aligned(16))) f16 xb[2][4 * 64 * 8];
+    GDN_LDS_POISON_ALL(flags, xb);
+    const int id = (int)blockIdx.x, k = (id >> 3) & 15, x = 8 * (id >> 7) + (id & 7);
+    const int J = p.comb_J, G = p.comb_G;
+    if (x >= p.n_seqs * p.h_v * J) return;
+    const int j = x % J, q = x / J, seq = q / p.h_v, h = q % p.h_v;
+    if (j == 0 && k >= 8) return;
+    int P, seg_base;
+    if (!comb_setup(p, seq, h, flags, P, seg_base)) return;
+    const int b_lo = 1 + j * G, b_hi = min(b_lo + G, P);
+    if (b_lo >= P) return;
+    const int u = k & 7, r = wave_id(), lane = lane_id(), c = lane & 15, g = lane >> 4;
+    f32x4 cur[2];
+    if (j == 0) {
+        if (p.s_init) comb_load_rm_tile(p.s_init + tiles_off(seq, p.h_v, h), u, cur);
+        else cur[0] = cur[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        comb_put(xb[0], cur);
+        comb_chain<0>(p, flags, xb, seg_base, h, u, b_lo, b_hi, cur);
+        return;
     }
-    if (P <= 1 || P > kMaxSegsPerSeq) return;
-    int any_exact = 0;
-    for (int s = 1 + (int)threadIdx.x; s < P; s += NTC) {
-        const int f = p.warm[(size_t)(seg_base + s) * p.h_v + h] & 255;
-        flags[s] = f;
-        any_exact |= f == 0;
-    }
-    if (!__syncthreads_or(any_exact)) return;   // every boundary warmed up: nothing to chain
-    const int lane = lane_id(), c = lane & 15, g = lane >> 4, r = wave_id();
-    // S0(0) (row tiles 2 r, 2 r + 1 of column tile u) -> this wave's k step of the B operand
-    {
-        f32x4 cur[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * r + tt;
-            if (p.s_init) {
-                const float* S0 = p.s_init + tiles_off(seq, p.h_v, h);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) cur[tt][e] = S0[(16 * t + 4 * g + e) * DK + 16 * u + c];
-            } else {
-                cur[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        *reinterpret_cast<f16x8*>(xb[0] + (r * 64 + lane) * 8) = pack8h(cur[0], cur[1]);
-    }
-    struct Ops {
-        f32x4 add[2];   // H_{s-1} or the warm-up state, row tiles 2 r, 2 r + 1
-        u32x4 m[8];     // M_{s-1} fragments (row tile 2 r + f / 4, k step f % 4)
-    };
-    auto fetch = [&](Ops& o, int s) {
-        s = min(s, P - 1);
-        const int f = __builtin_amdgcn_readfirstlane(flags[s]);   // (uniform: a branch-free select)
-        const float* src = f ? p.seg_state + tiles_off(seg_base + s, p.h_v, h)
-                             : p.seg_H + tiles_off(seg_base + s - 1, p.h_v, h);
+    const size_t grp = (size_t)(seq * J + j) * p.h_v + h;
+    if (k < 8) {   // CM from I
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
-            o.add[tt] = *reinterpret_cast<const f32x4*>(src + (((2 * r + tt) * 8 + u) * 64 + lane) * 4);
-        const u32x4* mi = reinterpret_cast<const u32x4*>(reinterpret_cast<const f16*>(p.seg_M) +
-                                                          tiles_off(seg_base + s - 1, p.h_v, h));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cur[tt][e] = (32 * r + 16 * tt + 4 * g + e == 16 * u + c) ? 1.f : 0.f;
+        comb_put(xb[0], cur);
+        comb_chain<1>(p, flags, xb, seg_base, h, u, b_lo, b_hi, cur);
+        // X[row][16 u + c] -> the A-operand image (fragment 4 (row / 16) + u / 2; lane
+        // 16 (c / 4) + row % 16; slot 4 (u % 2) + c % 4: the kp order of the chain)
+        f16* img = reinterpret_cast<f16*>(p.seg_GM) + grp * (size_t)DK * DK;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 32 * r + 16 * tt + 4 * g + e;
+                img[((4 * (row >> 4) + (u >> 1)) * 64 + 16 * (c >> 2) + (row & 15)) * 8 + 4 * (u & 1) + (c & 3)] =
+                    (f16)cur[tt][e];
+            }
+    } else {       // CH from 0
+        cur[0] = cur[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        comb_put(xb[0], cur);
+        comb_chain<2>(p, flags, xb, seg_base, h, u, b_lo, b_hi, cur);
+        float* dst = p.seg_GH + grp * (size_t)DK * DK;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+            *reinterpret_cast<f32x4*>(dst + (((2 * r + tt) * 8 + u) * 64 + lane) * 4) = cur[tt];
+    }
+}
+
+__global__ __launch_bounds__(NTC) void k_comb16_apply(Params p) {
+    __shared__ int flags[kMaxSegsPerSeq];
+    __shared__ __attribute__((aligned(16))) f16 xb[2][4 * 64 * 8];
+    GDN_LDS_POISON_ALL(flags, xb);
+    const int id = (int)blockIdx.x, u = (id >> 3) & 7, x = 8 * (id >> 6) + (id & 7);
+    const int J = p.comb_J, G = p.comb_G;
+    if (x >= p.n_seqs * p.h_v * J) return;
+    const int j = x % J, q = x / J, seq = q / p.h_v, h = q % p.h_v;
+    if (j == 0) return;
+    int P, seg_base;
+    if (!comb_setup(p, seq, h, flags, P, seg_base)) return;
+    const int b_lo = 1 + j * G, b_hi = min(b_lo + G, P);
+    if (b_lo >= P) return;
+    const int r = wave_id(), lane = lane_id();
+    // S0(e_{j-1}): from S0(e_0) through the composed maps of groups 1 .. j - 1
+    f32x4 cur[2];
+    comb_load_tile(p.seg_state + tiles_off(seg_base + comb_group_end(0, G, P), p.h_v, h), u, cur);
+    comb_put(xb[0], cur);
+    struct LinkOps { f32x4 add[2]; u32x4 m[8]; };
+    auto fetch = [&](LinkOps& o, int jj) {
+        jj = min(jj, j - 1);
+        const size_t grp = (size_t)(seq * J + jj) * p.h_v + h;
+        comb_load_tile(p.seg_GH + grp * (size_t)DK * DK, u, o.add);
+        const u32x4* mi = reinterpret_cast<const u32x4*>(reinterpret_cast<const f16*>(p.seg_GM) + grp * (size_t)DK * DK);
 #pragma unroll
         for (int f8 = 0; f8 < 8; ++f8) o.m[f8] = mi[(8 * r + f8) * 64 + lane];
     };
-    // a warm-up boundary keeps its state (written back unchanged); an exact
-    // one applies the map (M_0 only to an initial state). Both are evaluated
-    // and selected, so that every step issues the same memory operations.
-    auto step = [&](int s, const Ops& o, int buf) {
-        __syncthreads();   // the previous state's B operand is in xb[buf]
-        const bool mm = __builtin_amdgcn_readfirstlane(flags[s]) == 0 && (s > 1 || p.s_init);
+    auto step = [&](const LinkOps& o, int buf) {
+        __syncthreads();
         f16x8 Sb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Sb[j] = *reinterpret_cast<const f16x8*>(xb[buf] + (j * 64 + lane) * 8);
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int kk = 0; kk < 4; ++kk) Sb[kk] = *reinterpret_cast<const f16x8*>(xb[buf] + (kk * 64 + lane) * 8);
+        f32x4 acc[2] = {o.add[0], o.add[1]};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) acc[tt] = mmh(__builtin_bit_cast(f16x8, o.m[4 * tt + j]), Sb[j], acc[tt]);
-        float* dst = p.seg_state + tiles_off(seg_base + s, p.h_v, h);
-        f32x4 cur[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            // (a select, not a product with 0: the maps of warm-up boundaries and
-            // M_0 without an initial state are never written and may hold NaNs)
-            cur[tt] = mm ? o.add[tt] + acc[tt] : o.add[tt];
-            *reinterpret_cast<f32x4*>(dst + (((2 * r + tt) * 8 + u) * 64 + lane) * 4) = cur[tt];
-        }
-        *reinterpret_cast<f16x8*>(xb[buf ^ 1] + (r * 64 + lane) * 8) = pack8h(cur[0], cur[1]);
+            for (int tt = 0; tt < 2; ++tt) acc[tt] = mmh(__builtin_bit_cast(f16x8, o.m[4 * tt + kk]), Sb[kk], acc[tt]);
+        cur[0] = acc[0];
+        cur[1] = acc[1];
+        comb_put(xb[buf ^ 1], cur);
     };
-    Ops A, B;
-    fetch(A, 1);
-    fetch(B, 2);
-    int s = 1;
-    for (; s + 1 < P; s += 2) {
-        step(s, A, 0);
-        fetch(A, s + 2);
-        step(s + 1, B, 1);
-        fetch(B, s + 3);
+    if (j > 1) {
+        LinkOps A, B;
+        fetch(A, 1);
+        fetch(B, 2);
+        int jj = 1;
+        for (; jj + 1 < j; jj += 2) {
+            step(A, 0);
+            fetch(A, jj + 2);
+            step(B, 1);
+            fetch(B, jj + 3);
+        }
+        if (jj < j) step(A, 0);
+        __syncthreads();   // every wave's last step is done: the state goes to xb[0]
+        comb_put(xb[0], cur);
     }
-    if (s < P) step(s, A, 0);
+    // then the group's boundaries, every state stored
+    comb_chain<0>(p, flags, xb, seg_base, h, u, b_lo, b_hi, cur);
 }
 
 // ----------------------------------------------------------------------------
@@ -1489,8 +1648,18 @@ int launch_cp_prep16(const Params& p, int io, void* stream) {
 }
 
 int launch_combine16(const Params& p, void* stream) {
-    const dim3 grid((unsigned)(64 * ((p.n_seqs * p.h_v + 7) / 8))), block(NTC);
-    hipLaunchKernelGGL(k_combine16, grid, block, 0, (hipStream_t)stream, p);
+    const hipStream_t s = (hipStream_t)stream;
+    const dim3 block(NTC);
+    const unsigned heads = (unsigned)((p.n_seqs * p.h_v + 7) / 8);
+    if (p.comb_G <= 0) {
+        hipLaunchKernelGGL(k_combine16, dim3(64 * heads), block, 0, s, p);
+        return launched16();
+    }
+    const unsigned bundles = (unsigned)(((long long)p.n_seqs * p.h_v * p.comb_J + 7) / 8);
+    hipLaunchKernelGGL(k_comb16_groups, dim3(128 * bundles), block, 0, s, p);
+    const int e = launched16();
+    if (e) return e;
+    hipLaunchKernelGGL(k_comb16_apply, dim3(64 * bundles), block, 0, s, p);
     return launched16();
 }
 

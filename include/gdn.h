@@ -105,8 +105,8 @@ typedef struct {
     float lambda;
     float noise_floor;
     size_t workspace_bytes;  /* what gdn_fwd needs for this descriptor */
-    int32_t combine_group;   /* boundaries per group of the grouped combine (0: one chain) */
-    int32_t combine_groups;  /* groups of the longest sequence (0: one chain) */
+    int32_t combine_group;   /* boundaries per group of the forward's grouped combine (0: one chain) */
+    int32_t combine_groups;  /* its groups in the longest sequence (0: one chain) */
     int32_t dv_split;        /* column blocks of d_v in the forward (1: none) */
     int32_t cp_layout;       /* boundary preprocessing layout run (1 or 2, as in gdn_desc); 0 without
                                 a context-parallel split or with fp32 inputs */

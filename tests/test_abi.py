@@ -121,27 +121,30 @@ def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
     if p["cp_on"]:
         flags = -(-(p["n_segments"] * h_v * 4) // 256) * 256
         # boundary states and H maps (fp32), M maps (fp16 images), boundary flags
-        assert p["workspace_bytes"] == prep + 2 * p["n_segments"] * per_seg + p["n_segments"] * per_seg // 2 + flags
-        # the grouped combine of the backward's re-run (the rule stated in gdn_api.cpp):
-        # G boundaries per group when slow (G rounds + G - 1) + (J - 2) + 4 steps beat
-        # the single chain of P - 1, J = ceil((P - 1) / G), assuming 30 % of the
-        # (sequence, head) pairs exact (to the nearest, at least one), 8 composing
-        # workgroups per group and exact head, slow = 2.5 past half the CUs
+        ws_expect = prep + 2 * p["n_segments"] * per_seg + p["n_segments"] * per_seg // 2 + flags
+        # the forward's grouped combine (the rule stated in gdn_api.cpp): G boundaries per
+        # group when G load + (J - 2) + G + 8 steps beat the single chain of P - 1,
+        # J = ceil((P - 1) / G), assuming 30 % of the (sequence, head) pairs exact (to the
+        # nearest, at least one), 16 composing workgroups per group and exact head, load =
+        # max(1, their count / (2 CUs))
         nb, best, G_exp = p["P_max"] - 1, float(p["P_max"] - 1), 0
         heads = max(1, (B_ * h_v * 3 + 5) // 10)
         for G in range(2, nb):
             J = -(-nb // G)
             if J < 2:
                 break
-            wgs = 8 * (J - 1) * heads
-            rounds = -(-wgs // 256)
-            slow = 1.0 if 2 * wgs <= 256 else 2.5
-            steps = slow * (G * rounds + G - 1) + max(J - 2, 0) + 4
+            load = max(1.0, 16 * (J - 1) * heads / (2.0 * 256))
+            steps = G * load + (J - 2) + G + 8
             if steps < best:
                 best, G_exp = steps, G
         assert p["combine_group"] == G_exp
         J_exp = -(-nb // G_exp) if G_exp else 0
         assert p["combine_groups"] == J_exp
+        # its composed maps: per (sequence, group, head) CM (fp16) and CH (fp32)
+        if G_exp:
+            grp = B_ * J_exp * h_v * 128 * 128
+            ws_expect += -(-(grp * 2) // 256) * 256 + -(-(grp * 4) // 256) * 256
+        assert p["workspace_bytes"] == ws_expect
     else:
         assert p["workspace_bytes"] == prep and p["combine_group"] == 0
 
