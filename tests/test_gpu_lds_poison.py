@@ -10,7 +10,7 @@ backward's chunk kernel sums some row terms with LDS atomics in wave order,
 so its outputs are compared to 1e-5 relative. Every output is also checked
 to be finite. The cases cover each kernel: T diag(beta) preparation (both
 image kinds), the CP preprocessing in both layouts and for fp32 inputs, the
-boundary-state chains, the fused forward in every column split, the debug
+boundary-state chains (single and grouped), the fused forward in every column split, the debug
 copies, the backward's kernels and the decode.
 """
 from __future__ import annotations
@@ -117,6 +117,18 @@ def test_forward_same_under_poison(case):
     inp = make_inputs(1, case["T"], *case["h"], seed=90, gate="mixed", init_std=0.05, io_dtype=case["io"])
     a, b = _both(_fwd_case(inp, **case["kw"]))
     _same(a, b, f"fwd {case['io']} {case['kw']}")
+
+
+def test_grouped_combine_same_under_poison():
+    """Long boundary chains, so that the planner groups the combine (composed
+    group maps, then the replay)."""
+    from gated_deltanet_chunked_03_amd import plan
+    cu = [0, 64 * 129 + 37, 64 * 129 + 37 + 64 * 70 + 5]
+    inp = make_inputs(1, cu[-1], 2, 4, seed=95, gate="mixed", cu_seqlens=cu, init_std=0.05)
+    for mode in ("exact", "auto"):
+        assert plan(1, cu[-1], 2, 4, cu_seqlens=cu, cp_mode=mode, n_cu=256)["combine_group"] > 0
+        a, b = _both(_fwd_case(inp, cp_mode=mode, n_cu=256))
+        _same(a, b, f"grouped combine {mode}")
 
 
 def test_varlen_same_under_poison():
