@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
         }
         gam[t] = x;
         bet[t] = t < nv ? p.beta[(tok0 + t) * p.h_v + h] : 0.f;
-        out[2 * CH * CH + t] = x;
+        out[CH * CH + t] = x;
     }
     __syncthreads();
     {   // K K^T and Q K^T on the ten lower 16x16 tiles (16x16x32 MFMA; lane 16 g + c:
@@ -230,12 +230,11 @@ __global__ __launch_bounds__(NT) void k_bwd_prep(BwdParams p) {
             __syncthreads();
         }
     }
-    // fp32 T and P (zero above the diagonal blocks / the diagonal)
+    // fp32 P (zero above the diagonal; T goes out only as the images below)
     auto tv = [&](int r, int col) { return (col >> 4) > (r >> 4) ? 0.f : tm[r][col]; };
     auto pv = [&](int r, int col) { return col > r ? 0.f : pmat[r][col]; };
     for (int idx = t; idx < CH * CH; idx += NT) {
-        out[idx] = tv(idx >> 6, idx & 63);
-        out[CH * CH + idx] = pv(idx >> 6, idx & 63);
+        out[idx] = pv(idx >> 6, idx & 63);
     }
     // T^T, scale P^T and T as hi/lo bf16 rows with the contraction token in kp order
     // (four consecutive tokens stay consecutive in kp order: one 8-byte store each)

@@ -76,7 +76,7 @@ int record_error(int status, const char* fmt, ...);
 
 // Backward pass (gdn_bwd.hip). Chunks are numbered sequence by sequence as in
 // the forward; states are [128][128] fp32 blocks in the API layout.
-constexpr int kBwdTpg = 2 * kChunk * kChunk + kChunk;   // floats per (chunk, head): T, P, gamma
+constexpr int kBwdTpg = kChunk * kChunk + kChunk;       // floats per (chunk, head): P, gamma
 constexpr int kBwdTpt = 6 * kChunk * kChunk;            // bf16 per (chunk, head) in the T^T / P^T / T images
 
 struct BwdParams {
@@ -97,7 +97,7 @@ struct BwdParams {
     // workspace
     const float* cs;          // [n_chunks][h_v] state entering each chunk (from the forward)
     float* ds;                // [n_chunks][h_v] loss gradient of the state leaving each chunk
-    float* tpg;               // [n_chunks][h_v] blocks of kBwdTpg floats: T, P (row-major 64 x 64), gamma
+    float* tpg;               // [n_chunks][h_v] blocks of kBwdTpg floats: P (row-major 64 x 64), gamma
     void* tpt;                // [n_chunks][h_v] bf16 images for the matrix cores: [T^T hi, T^T lo,
                               // scale P^T hi, lo, T hi, lo], rows of 64, contraction token in kp order
     const float* y;           // [n_chunks][h_v][64][128] fp32 from the forward re-run: Y, V', scale e^gamma Q S

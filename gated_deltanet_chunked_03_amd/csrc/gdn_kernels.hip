@@ -1657,7 +1657,7 @@ __device__ void bwd_chain_fetch(const BwdParams& p, BwdChainIn& in, int f, size_
     const u32x4* img = reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt);
 #pragma unroll
     for (int j = 0; j < 4; ++j) in.img[j] = img[t + NTHR_CH * j];
-    in.gl = p.tpg[((size_t)f * p.h_v + h) * kBwdTpg + 2 * CH * CH + lane];
+    in.gl = p.tpg[((size_t)f * p.h_v + h) * kBwdTpg + CH * CH + lane];
     in.bl = p.beta[(tok0 + min(lane, nv - 1)) * p.h_v + h];
     in.nv = nv;   // (the masking waits for the loads: it happens when the chunk is staged)
 }
@@ -2023,7 +2023,7 @@ __device__ __forceinline__ void bwd_item_fetch(const BwdParams& p, long long ite
         in.img[2 * j + 1] = img[t + NTHR_CH * j + 2048];
     }
     const int tt = min(t, CH - 1);
-    in.gm = p.tpg[((size_t)f * p.h_v + h) * kBwdTpg + 2 * CH * CH + tt];
+    in.gm = p.tpg[((size_t)f * p.h_v + h) * kBwdTpg + CH * CH + tt];
     in.b = p.beta[(tok0 + min(tt, nv - 1)) * p.h_v + h];
     const int r1 = t >> 3, c01 = (t & 7) * 16;
     in.qo1 = p.oi[((size_t)f * p.h_v + h) * (NW_CH * CH) + (t & 7) * CH + r1];
@@ -2293,7 +2293,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                     for (int j = 0; j < 2; ++j)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            pP[j][e] = tp[CH * CH + (16 * prt + 4 * g + e) * CH + 16 * (pct0 + j) + c];
+                            pP[j][e] = tp[(16 * prt + 4 * g + e) * CH + 16 * (pct0 + j) + c];
                 }
                 const bf16x8 ao = lds_op16(st_do + ra * LDQ + 32 * ks + 8 * g);
                 const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{cur.ka[0][0], cur.ka[0][1], cur.ka[1][0], cur.ka[1][1]});
