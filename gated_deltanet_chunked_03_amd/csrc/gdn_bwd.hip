@@ -53,15 +53,6 @@ constexpr int LKB = 136;   // bf16 row stride of the [64][128] K, Q tiles
 constexpr int LM = 68;     // fp32 row stride of [64][64] tiles
 
 __device__ __forceinline__ int n_chunks_of(int len) { return (len + CH - 1) / CH; }
-__device__ __forceinline__ size_t state_off(int idx, int h_v, int h) {
-    return ((size_t)idx * h_v + h) * (size_t)DK * DK;
-}
-__device__ __forceinline__ f32x4 bf4(const bf16* x) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(x);
-    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
-                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
-}
-__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 __device__ __forceinline__ unsigned pack_rne(float a, float b) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }

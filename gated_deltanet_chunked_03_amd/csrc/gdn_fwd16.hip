@@ -154,12 +154,6 @@ __device__ __forceinline__ void fetch16(In16<IO>& r, const Params& p, const Lane
     r.tb = tb[t < kTbHalfs / 8 ? t : t - kTbHalfs / 8];
 }
 
-// four bf16 / fp32 values -> fp16
-__device__ __forceinline__ f16x4 to_h4(const u32x2& x) {
-    return __builtin_convertvector(f32x4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
-                                         __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)},
-                                   f16x4);
-}
 __device__ __forceinline__ f16x4 to_h4(const f32x4& x) { return __builtin_convertvector(x, f16x4); }
 
 // Writes a fetched chunk to LDS (K^T into buffer b): K token-major and
@@ -937,7 +931,6 @@ constexpr int kWsRow = 144;                                   // halfs per K / Q
 constexpr int kWsRowT = 80;                                   // halfs per K~^T row
 constexpr int kWsRowP = 72;                                   // halfs per P row
 __device__ __forceinline__ int kq_at(int r, int piece) { return r * kWsRow + 8 * piece; }
-__device__ __forceinline__ int kt_at(int d, int piece) { return d * kWsRowT + ((8 * piece) ^ tswz(d)); }
 __device__ __forceinline__ int p_at(int r, int piece) { return r * kWsRowP + 8 * piece; }
 
 struct __attribute__((aligned(16))) SmemWS {

@@ -1644,8 +1644,8 @@ struct BwdChainIn {
 };
 
 __device__ void bwd_chain_fetch(const BwdParams& p, BwdChainIn& in, int f, size_t tok0, int nv, int h, int hq) {
-    const int t = threadIdx.x, m = t >> 5, c4 = (t & 31) * 4, lane = lane_id(), c = lane & 15, g = lane >> 4;
-    const size_t ts = (size_t)p.h_qk * DK, ts_v = (size_t)p.h_v * DK;
+    const int t = threadIdx.x, m = t >> 5, c4 = (t & 31) * 4, lane = lane_id();
+    const size_t ts = (size_t)p.h_qk * DK;
     const bf16* kb = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK + c4;
     const bf16* qb = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK + c4;
 #pragma unroll
@@ -1938,19 +1938,6 @@ struct BwdChunkSmem {
 };
 
 __device__ __forceinline__ float dot4v(f32x4 a, f32x4 b) { return (a[0] * b[0] + a[1] * b[1]) + (a[2] * b[2] + a[3] * b[3]); }
-// Eight consecutive kp positions 32 ks + 8 g .. of an fp32 row (two 16-byte
-// loads), times s, split hi/lo; and of a bf16 row (two 8-byte loads).
-__device__ __forceinline__ void kp_op_f32(const float* row, int ks, int g, float s, bf16x8& hi, bf16x8& lo) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(row + 32 * ks + 4 * g);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(row + 32 * ks + 16 + 4 * g);
-    split8(a * s, b * s, hi, lo);
-}
-__device__ __forceinline__ bf16x8 kp_op_bf16(const bf16* row, int ks, int g, bool keep) {
-    const u32x2 a = *reinterpret_cast<const u32x2*>(row + 32 * ks + 4 * g);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(row + 32 * ks + 16 + 4 * g);
-    const u32x4 v = keep ? u32x4{a[0], a[1], b[0], b[1]} : u32x4{0u, 0u, 0u, 0u};
-    return __builtin_bit_cast(bf16x8, v);
-}
 // Accumulator element (row 16 rt + 4 g + e, column 16 ct + c) of a 64 x 64 tile
 // into an image: at [row][kp(col)] (scalar) or transposed at [col][kp(row)]
 // (the four rows of a lane are consecutive in kp order: one 8-byte store).
@@ -2069,7 +2056,6 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
         const float* dVb = p.dvp + blk;
         const float* Zb = p.z + blk;
         const bf16* Kg = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK;
-        const bf16* Qg = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK;
         const bf16* dOg = static_cast<const bf16*>(p.dout) + tok0 * ts_v + (size_t)h * DK;
         const float* tp = p.tpg + ((size_t)f * p.h_v + h) * kBwdTpg;
         const float scale = p.scale;
