@@ -158,19 +158,24 @@ void combine_grouping(int nb, long long heads, int n_cu, int J_max, int32_t* G_o
 }
 
 // The forward's (fp16) combine grouping: G boundaries per group when its two
-// launches' 2 G + J - 2 steps, plus about eight steps for the extra launch
-// (measured: a launch costs about as much as eight boundary steps), beat the
-// single chain's nb steps; the composing launch's workgroups (16 per group and
-// exact (sequence, head)) beyond two per CU stretch its steps.
+// launches' steps -- G composing steps, then J - 2 + G linking and replaying
+// steps, each stretched by the workgroups beyond one per CU (16 per group and
+// exact (sequence, head) composing, 8 replaying: a combine step is bound by its
+// operand loads, which workgroups sharing a CU share) -- plus about eight steps
+// for the extra launch, come to less than 0.8 of the single chain's nb steps
+// (measured: a launch costs about as much as eight boundary steps; with more
+// composing workgroups than CUs the grouped combine lost to the chain).
 void combine16_grouping(int nb, long long exact_heads, int n_cu, int32_t* G_out, int32_t* J_out) {
     *G_out = 0;
     *J_out = 0;
-    double best = nb;
+    double best = 0.8 * nb;
+    const double cus = std::max(n_cu, 1);
     for (int G = 2; G < nb; ++G) {
         const int J = (nb + G - 1) / G;
         if (J < 2) break;
-        const double load = std::max(1.0, (double)(16LL * (J - 1) * exact_heads) / (2.0 * std::max(n_cu, 1)));
-        const double steps = G * load + (J - 2) + G + 8;
+        const double load1 = std::max(1.0, 16.0 * (J - 1) * exact_heads / cus);
+        const double load2 = std::max(1.0, 8.0 * (J - 1) * exact_heads / cus);
+        const double steps = G * load1 + (J - 2 + G) * load2 + 8;
         if (steps < best) {
             best = steps;
             *G_out = G;

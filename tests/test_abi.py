@@ -123,18 +123,20 @@ def test_plan_for_the_workloads(name, B_, T, h_qk, h_v, L):
         # boundary states and H maps (fp32), M maps (fp16 images), boundary flags
         ws_expect = prep + 2 * p["n_segments"] * per_seg + p["n_segments"] * per_seg // 2 + flags
         # the forward's grouped combine (the rule stated in gdn_api.cpp): G boundaries per
-        # group when G load + (J - 2) + G + 8 steps beat the single chain of P - 1,
-        # J = ceil((P - 1) / G), assuming 30 % of the (sequence, head) pairs exact (to the
-        # nearest, at least one), 16 composing workgroups per group and exact head, load =
-        # max(1, their count / (2 CUs))
-        nb, best, G_exp = p["P_max"] - 1, float(p["P_max"] - 1), 0
+        # group when G load1 + (J - 2 + G) load2 + 8 steps come to less than 0.8 of the
+        # single chain's P - 1, J = ceil((P - 1) / G), assuming 30 % of the (sequence,
+        # head) pairs exact (to the nearest, at least one); load1 = max(1, 16 (J - 1)
+        # heads / CUs), load2 = max(1, 8 (J - 1) heads / CUs)
+        nb, G_exp = p["P_max"] - 1, 0
+        best = 0.8 * nb
         heads = max(1, (B_ * h_v * 3 + 5) // 10)
         for G in range(2, nb):
             J = -(-nb // G)
             if J < 2:
                 break
-            load = max(1.0, 16 * (J - 1) * heads / (2.0 * 256))
-            steps = G * load + (J - 2) + G + 8
+            load1 = max(1.0, 16 * (J - 1) * heads / 256)
+            load2 = max(1.0, 8 * (J - 1) * heads / 256)
+            steps = G * load1 + (J - 2 + G) * load2 + 8
             if steps < best:
                 best, G_exp = steps, G
         assert p["combine_group"] == G_exp
