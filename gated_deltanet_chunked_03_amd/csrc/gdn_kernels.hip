@@ -1629,6 +1629,7 @@ struct BwdChainSmem {
     bf16 qt[DK * LDKT];                   // Q^T, same layout
     bf16 tt[2 * CH * LDP];                // T^T: hi rows, then lo rows; tokens in kp order
     bf16 pt[2 * CH * LDP];                // scale P^T, same
+    bf16 dot[DK * LDKT];                  // dO^T: row d_v, tokens in kp order (chunks swizzled), rows past the end zero
     float fr[CH];                         // exp(gamma_C - gamma)
     float egb[CH];                        // -exp(gamma) beta
     float egs[CH];                        // scale exp(gamma)
@@ -1638,21 +1639,25 @@ struct BwdChainSmem {
 
 struct BwdChainIn {
     u32x2 k[4], q[4];                     // tokens 4 (t / 32) + j, d_k 4 (t % 32) .. + 3
+    u32x2 d[4];                           // dO: tokens 4 (t / 32) + j, d_v 4 (t % 32) .. + 3
     u32x4 img[4];                         // pieces t + 512 j of the T^T / P^T images
     float gl, bl;                         // gamma, beta of token lane
     int nv;                               // valid tokens of the chunk
 };
 
+template <bool WANT_DO>
 __device__ void bwd_chain_fetch(const BwdParams& p, BwdChainIn& in, int f, size_t tok0, int nv, int h, int hq) {
     const int t = threadIdx.x, m = t >> 5, c4 = (t & 31) * 4, lane = lane_id();
-    const size_t ts = (size_t)p.h_qk * DK;
+    const size_t ts = (size_t)p.h_qk * DK, ts_v = (size_t)p.h_v * DK;
     const bf16* kb = static_cast<const bf16*>(p.k) + tok0 * ts + (size_t)hq * DK + c4;
     const bf16* qb = static_cast<const bf16*>(p.q) + tok0 * ts + (size_t)hq * DK + c4;
+    const bf16* db = static_cast<const bf16*>(p.dout) + tok0 * ts_v + (size_t)h * DK + c4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {   // rows past the end read the last row (their values never matter)
-        const int row = min(4 * m + j, nv - 1);
+    for (int j = 0; j < 4; ++j) {   // rows past the end read the last row (K, Q: their values never
+        const int row = min(4 * m + j, nv - 1);   // matter; dO: zeroed when staged)
         in.k[j] = *reinterpret_cast<const u32x2*>(kb + (size_t)row * ts);
         in.q[j] = *reinterpret_cast<const u32x2*>(qb + (size_t)row * ts);
+        if (WANT_DO) in.d[j] = *reinterpret_cast<const u32x2*>(db + (size_t)row * ts_v);
     }
     const u32x4* img = reinterpret_cast<const u32x4*>(static_cast<const bf16*>(p.tpt) + ((size_t)f * p.h_v + h) * kBwdTpt);
 #pragma unroll
@@ -1662,6 +1667,7 @@ __device__ void bwd_chain_fetch(const BwdParams& p, BwdChainIn& in, int f, size_
     in.nv = nv;   // (the masking waits for the loads: it happens when the chunk is staged)
 }
 
+template <bool WANT_DO>
 __device__ void bwd_chain_stage(BwdChainSmem& sm, const BwdChainIn& in, float scale) {
     const int t = threadIdx.x, lane = lane_id(), m = t >> 5, c4 = (t & 31) * 4;
     if (wave_id() == 0) {   // the gate factors: one wave (a scalar branch)
@@ -1680,6 +1686,13 @@ __device__ void bwd_chain_stage(BwdChainSmem& sm, const BwdChainIn& in, float sc
     for (int e = 0; e < 4; ++e) {
         *reinterpret_cast<u32x2*>(sm.kt + (c4 + e) * LDKT + tk) = pack_col4(in.k, e);
         *reinterpret_cast<u32x2*>(sm.qt + (c4 + e) * LDKT + tk) = pack_col4(in.q, e);
+    }
+    if (WANT_DO) {
+        u32x2 d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = 4 * m + j < in.nv ? in.d[j] : u32x2{0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x2*>(sm.dot + (c4 + e) * LDKT + tk) = pack_col4(d, e);
     }
     // images: piece idx -> part idx / 512 (T hi, T lo, P hi, P lo), row (idx / 8) % 64, 8 elements at 8 (idx % 8)
 #pragma unroll
@@ -1700,29 +1713,17 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
     const int hq = h / p.group, lane = lane_id(), c = lane & 15, g = lane >> 4;
     BwdChainIn in;
     auto fetch = [&](int cc) {
-        bwd_chain_fetch(p, in, loc.chunk_base + cc, loc.tok0 + (size_t)cc * CH, min(CH, loc.len - cc * CH), h, hq);
+        bwd_chain_fetch<WANT_DO>(p, in, loc.chunk_base + cc, loc.tok0 + (size_t)cc * CH, min(CH, loc.len - cc * CH),
+                                 h, hq);
     };
     if (c_lo < c_hi) fetch(c_hi - 1);
     for (int cc = c_hi - 1; cc >= c_lo; --cc) {
         // stage first: its wait then covers the prefetched loads only, not the
         // stores below (loads and stores share one counter)
-        bwd_chain_stage(sm, in, p.scale);
+        bwd_chain_stage<WANT_DO>(sm, in, p.scale);
         const int in_nv = in.nv;
         if (WRITE_DS) store_state(p.ds + state_off(loc.chunk_base + cc, p.h_v, h), D);
         __syncthreads();
-        // this chunk's dO (tokens 16 rt + 4 g + e, column 16 w + c) is loaded here, to
-        // arrive during K dS; every load is issued (rows past the end read the last
-        // row) and masked after the wait: a conditional load would make the
-        // compiler drain every outstanding load at its branch
-        unsigned draw[16];
-        if (WANT_DO) {
-            const unsigned short* dob = reinterpret_cast<const unsigned short*>(p.dout) +
-                                        (loc.tok0 + (size_t)cc * CH) * (size_t)(p.h_v * DK) + (size_t)h * DK +
-                                        16 * wave_id() + c;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                draw[i] = dob[(size_t)min(16 * (i >> 2) + 4 * g + (i & 3), in_nv - 1) * (size_t)(p.h_v * DK)];
-        }
         if (cc > c_lo) fetch(cc - 1);
         // X = diag(f) K dS + scale P^T dO
         f32x4 X[4];
@@ -1744,13 +1745,20 @@ __device__ void bwd_chain_run(const BwdParams& p, BwdChainSmem& sm, const SegLoc
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) X[rt] *= *reinterpret_cast<const f32x4*>(sm.fr + 16 * rt + 4 * g);
-        unsigned dO[8];   // this lane's dO tokens as bf16 pairs, rows past the end zero
+        // this lane's dO as B operands (column 16 w + c, the tokens of k step s in kp
+        // order: 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3), bf16 pairs
+        unsigned dO[8];
+        if (WANT_DO) {
+            const int col = 16 * wave_id() + c;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r0 = 16 * (i >> 1) + 4 * g + 2 * (i & 1);
-            const unsigned lo = (WANT_DO && r0 < in_nv) ? draw[2 * i] : 0u;
-            const unsigned hi = (WANT_DO && r0 + 1 < in_nv) ? draw[2 * i + 1] : 0u;
-            dO[i] = lo | (hi << 16);
+            for (int s = 0; s < 2; ++s) {
+                const u32x4 v = __builtin_bit_cast(u32x4, lds_op16(sm.dot + col * LDKT + ((32 * s + 8 * g) ^ tswz(col))));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dO[4 * s + i] = v[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dO[i] = 0u;
         }
         if (WANT_DO) {
 #pragma unroll
