@@ -225,7 +225,9 @@ def test_calibrate_lambda_picks_a_candidate():
     assert_within_tolerance(o.float().cpu().numpy().reshape(o_ref.shape), o_ref, "o")
 
 
-def test_per_boundary_rule_switch_heads_and_windows():
+@pytest.mark.parametrize("N,n_cu,lam,grouped", [(49, 32, 0.6, False), (193, 256, 1.0, True)],
+                         ids=["chain", "grouped-combine"])
+def test_per_boundary_rule_switch_heads_and_windows(N, n_cu, lam, grouped):
     """AUTO decides per boundary: a head whose gates switch from slow to fast
     decay mid-sequence (exact, then warm-up: mixed), one switching the other
     way (exact boundaries chained onto warmed-up ones), and constant decays
@@ -233,23 +235,27 @@ def test_per_boundary_rule_switch_heads_and_windows():
     floor of 0.05 a window one chunk too short or too long moves the boundary
     state by percents, so every boundary state is compared with the fp64
     chunk model's per-boundary reading of the same inputs (same windows, same
-    chaining), and the per-head path codes with the model's."""
+    chaining), and the per-head path codes with the model's. The longer case
+    has enough boundaries for the grouped combine, whose composed group maps
+    then hold warm-up boundaries between exact ones."""
     import math
-    eps, w, N = 0.05, 6, 49
+    eps, w = 0.05, 6
     T = 64 * (N - 1) + 7
     inp = make_inputs(1, T, 1, 6, seed=71, gate="plain", init_std=0.1)
     g = inp.g
     g[0, :, 0] = -2e-4
-    g[0, 64 * 24:, 0] = -0.4                  # slow -> fast at chunk 24
+    g[0, 64 * (N // 2):, 0] = -0.4            # slow -> fast mid-sequence
     g[0, :, 1] = -0.4
-    g[0, 64 * 20:, 1] = -2e-4                 # fast -> slow at chunk 20
+    g[0, 64 * (N * 2 // 5):, 1] = -2e-4       # fast -> slow
     for h, j in zip(range(2, 6), range(2, 6)):
         g[0, :, h] = math.log(eps) / (64 * (j - 0.5))
-    o, S, info = _run(inp, cp_mode="auto", n_cu=32, lam=0.6, warmup_chunks=w, noise_floor=eps, debug=True)
+    o, S, info = _run(inp, cp_mode="auto", n_cu=n_cu, lam=lam, warmup_chunks=w, noise_floor=eps, debug=True)
     plan = info["plan"]
     L = plan["L"]
-    print(f"\n[per-boundary] plan L={L} P={plan['P_max']}", flush=True)
-    assert plan["cp_on"] == 1 and L == 4
+    print(f"\n[per-boundary] plan L={L} P={plan['P_max']} combine G={plan['combine_group']}", flush=True)
+    assert plan["cp_on"] == 1 and (plan["combine_group"] > 0) == grouped
+    if not grouped:
+        assert L == 4
     q, k, v, gg, b = inp.flat()
     o_m, S_m, minfo = chunk_model.chunked_forward(q, k, v, gg, b, inp.scale, inp.initial_state, L=L,
                                                   mode="boundary", w=w, eps=eps)
