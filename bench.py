@@ -328,7 +328,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU (the library has no multi-GPU path); use --gpus 1"}))
         sys.exit(2)
 
     import numpy as np

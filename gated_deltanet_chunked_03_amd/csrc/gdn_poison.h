@@ -5,7 +5,7 @@
 // fp16 and bf16; -1 as an int) and waits for the whole workgroup. A result
 // computed from LDS that no thread of the workgroup wrote then comes out NaN
 // or wrong, and the poisoned build's outputs differ from the normal build's
-// (the GPU test of this build compares the two). Without GDN_LDS_POISON the
+// (a GPU test compares the two libraries' results). Without GDN_LDS_POISON the
 // macro expands to nothing.
 #pragma once
 
