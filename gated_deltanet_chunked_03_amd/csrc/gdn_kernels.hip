@@ -2091,6 +2091,23 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
             }
             if (t == 0) sm.dgc = 0.f;
         }
+        // step 2's dO and Z pieces and this wave's S row (every k step), in flight through
+        // step 1 (dO rows past the end repeat the last)
+        const float* Srow = S + (size_t)(16 * w + c) * DK;
+        const float* Drow = dSn + (size_t)(16 * w + c) * DK;
+        u32x2 dox[4];
+        f32x4 zx[4], srow[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            srow[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
+            srow[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = t + NTHR_CH * j, r = idx >> 5, c4 = (idx & 31) * 4;
+            dox[j] = *reinterpret_cast<const u32x2*>(dOg + (size_t)min(r, nv - 1) * ts_v + c4);
+            zx[j] = *reinterpret_cast<const f32x4*>(Zb + (size_t)r * DK + c4);
+        }
         __syncthreads();
         if (t < CH) sm.fr[t] = __expf(sm.gam[CH - 1] - sm.gam[t]);
         // ---- 1. row sums over d_v: thread t takes row t / 8, columns 16 (t % 8) .. + 15
@@ -2126,6 +2143,33 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
             }
         }
         __syncthreads();
+        // step 3's tiles: this wave's row tile and pair of column tiles
+        const int prt = w >> 1, pct0 = 2 * (w & 1), ra = 16 * prt + c;
+        // the operands read from memory (K rows ra and rb, dV' row ra, Y rows rb), one k step ahead
+        struct Ops3 {
+            u32x2 ka[2], kb[2][2];
+            f32x4 dv[2], y[2][2];
+        };
+        const float brb[2] = {sm.bet[16 * pct0 + c], sm.bet[16 * (pct0 + 1) + c]};
+        auto load3 = [&](Ops3& o, int ks) {
+            const bf16* kra = Kg + (size_t)min(ra, nv - 1) * ts + 32 * ks + 4 * g;
+            o.ka[0] = *reinterpret_cast<const u32x2*>(kra);
+            o.ka[1] = *reinterpret_cast<const u32x2*>(kra + 16);
+            const float* dvr = dVb + (size_t)ra * DK + 32 * ks + 4 * g;
+            o.dv[0] = *reinterpret_cast<const f32x4*>(dvr);
+            o.dv[1] = *reinterpret_cast<const f32x4*>(dvr + 16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int rb = 16 * (pct0 + j) + c;
+                const float* yr = Yb + (size_t)rb * DK + 32 * ks + 4 * g;
+                o.y[j][0] = *reinterpret_cast<const f32x4*>(yr);
+                o.y[j][1] = *reinterpret_cast<const f32x4*>(yr + 16);
+                const bf16* krb = Kg + (size_t)min(rb, nv - 1) * ts + 32 * ks + 4 * g;
+                o.kb[j][0] = *reinterpret_cast<const u32x2*>(krb);
+                o.kb[j][1] = *reinterpret_cast<const u32x2*>(krb + 16);
+            }
+        };
+        Ops3 cur;   // its first k step's operands, issued at the end of step 2
         // ---- 2. d_k-column products: dq = diag(scale e^gamma) dO S^T, dk = diag(f) V' dSn^T - diag(e^gamma) dY S^T.
         // The token-row operands (dO, dY = diag(beta) Z, V'), which every wave needs, are staged once in LDS
         // (rows with d_v in kp order; the image slots sa .. sc are free until step 3): first dO and dY, then V'.
@@ -2135,36 +2179,32 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
             bf16* st_do = st;                          // [64][LDQ] dO (kept through step 3's dP)
             bf16* st_x = st + CH * LDQ;                // [128][LDQ] dY, then V': hi rows, then lo rows
             static_assert(sizeof(sm.sa) + sizeof(sm.sb) + sizeof(sm.sc) >= 3 * CH * LDQ * sizeof(bf16), "staging fits");
-            auto stage_f32 = [&](bf16* dst, const float* src, bool by_beta) {
+            // hi and lo bf16 rows of fp32 pieces held in registers
+            auto put_f32 = [&](bf16* dst, const f32x4 (&x)[4]) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {   // piece t + 512 j: row / 32, four d_v at 4 (piece % 32)
                     const int idx = t + NTHR_CH * j, r = idx >> 5, c4 = (idx & 31) * 4;
-                    f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)r * DK + c4);
-                    if (by_beta) x *= sm.bet[r];
                     bf16x4 hi, lo;
-                    split4(x, hi, lo);
+                    split4(x[j], hi, lo);
                     *reinterpret_cast<bf16x4*>(dst + r * LDQ + kp(c4)) = hi;
                     *reinterpret_cast<bf16x4*>(dst + (CH + r) * LDQ + kp(c4)) = lo;
                 }
             };
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {   // dO, rows past the end zero (loads issued for every row)
+            for (int j = 0; j < 4; ++j) {   // dO, rows past the end zero; dY = diag(beta) Z
                 const int idx = t + NTHR_CH * j, r = idx >> 5, c4 = (idx & 31) * 4;
-                const u32x2 x = *reinterpret_cast<const u32x2*>(dOg + (size_t)min(r, nv - 1) * ts_v + c4);
-                *reinterpret_cast<u32x2*>(st_do + r * LDQ + kp(c4)) = r < nv ? x : u32x2{0u, 0u};
+                *reinterpret_cast<u32x2*>(st_do + r * LDQ + kp(c4)) = r < nv ? dox[j] : u32x2{0u, 0u};
+                zx[j] *= sm.bet[r];
             }
-            stage_f32(st_x, Zb, true);
+            put_f32(st_x, zx);
             f32x4 aq[4], a1[4], a2[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) aq[rt] = a1[rt] = a2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const float* Srow = S + (size_t)(16 * w + c) * DK;
-            const float* Drow = dSn + (size_t)(16 * w + c) * DK;
-            // this wave's S row (every k step) in flight during the staging and the barrier
-            f32x4 srow[4][2];
+            f32x4 vpx[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                srow[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
-                srow[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
+            for (int j = 0; j < 4; ++j) {
+                const int idx = t + NTHR_CH * j;
+                vpx[j] = *reinterpret_cast<const f32x4*>(Vpb + (size_t)(idx >> 5) * DK + (idx & 31) * 4);
             }
             __syncthreads();
 #pragma unroll
@@ -2183,7 +2223,8 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                     a2[rt] = mma16k32(yl, sh, a2[rt]);
                 }
             }
-            // this wave's dSn row (and its S row again, for <S, dSn>), in flight during the V' staging
+            // this wave's dSn row (and its S row again, for <S, dSn>) and this thread's
+            // V' pieces, in flight across the barrier
             f32x4 drow[4][2], srw[4][2];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -2193,7 +2234,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 srw[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
             }
             __syncthreads();
-            stage_f32(st_x, Vpb, false);
+            put_f32(st_x, vpx);
             __syncthreads();
             {   // dgamma_C from the decay of the state, e^gamma_C <S, dSn>: this wave's
                 // 16 rows of both are in its registers
@@ -2217,6 +2258,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                     a1[rt] = mma16k32(vl, dh, a1[rt]);
                 }
             }
+            load3(cur, 0);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int r0 = 16 * rt + 4 * g;
@@ -2240,44 +2282,17 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
             }
         }
         // ---- 3. 64 x 64 tiles: dP -> Psi (images), dT (image), K K^T (kept)
-        const int prt = w >> 1, pct0 = 2 * (w & 1);
         f32x4 kkt[2];
         {
             f32x4 dp[2], dt[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) dp[j] = dt[j] = kkt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int ra = 16 * prt + c;
             const bf16* st_do = sm.sa;                       // staged in step 2 (dO, then V' hi / lo rows)
             const bf16* st_v = sm.sa + CH * LDQ;
-            // the operands read from memory (K rows ra and rb, dV' row ra, Y rows rb), one k step ahead
-            struct Ops3 {
-                u32x2 ka[2], kb[2][2];
-                f32x4 dv[2], y[2][2];
-            };
-            const float brb[2] = {sm.bet[16 * pct0 + c], sm.bet[16 * (pct0 + 1) + c]};
-            auto load3 = [&](Ops3& o, int ks) {
-                const bf16* kra = Kg + (size_t)min(ra, nv - 1) * ts + 32 * ks + 4 * g;
-                o.ka[0] = *reinterpret_cast<const u32x2*>(kra);
-                o.ka[1] = *reinterpret_cast<const u32x2*>(kra + 16);
-                const float* dvr = dVb + (size_t)ra * DK + 32 * ks + 4 * g;
-                o.dv[0] = *reinterpret_cast<const f32x4*>(dvr);
-                o.dv[1] = *reinterpret_cast<const f32x4*>(dvr + 16);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int rb = 16 * (pct0 + j) + c;
-                    const float* yr = Yb + (size_t)rb * DK + 32 * ks + 4 * g;
-                    o.y[j][0] = *reinterpret_cast<const f32x4*>(yr);
-                    o.y[j][1] = *reinterpret_cast<const f32x4*>(yr + 16);
-                    const bf16* krb = Kg + (size_t)min(rb, nv - 1) * ts + 32 * ks + 4 * g;
-                    o.kb[j][0] = *reinterpret_cast<const u32x2*>(krb);
-                    o.kb[j][1] = *reinterpret_cast<const u32x2*>(krb + 16);
-                }
-            };
             // the fp32 P entries of this wave's dP tiles (for dP o P after the loop),
             // loaded in the last k step in place of that step's operands
             float pP[2][4];
-            Ops3 cur, nxt;
-            load3(cur, 0);
+            Ops3 nxt;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 if (ks < 3) {
