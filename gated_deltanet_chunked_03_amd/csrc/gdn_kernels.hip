@@ -2200,11 +2200,17 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
             f32x4 aq[4], a1[4], a2[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) aq[rt] = a1[rt] = a2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 vpx[4];
+            // this thread's V' pieces and this wave's dSn row, in flight through the dO and dY products
+            f32x4 vpx[4], drow[4][2];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int idx = t + NTHR_CH * j;
                 vpx[j] = *reinterpret_cast<const f32x4*>(Vpb + (size_t)(idx >> 5) * DK + (idx & 31) * 4);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                drow[ks][0] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 4 * g);
+                drow[ks][1] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 16 + 4 * g);
             }
             __syncthreads();
 #pragma unroll
@@ -2223,28 +2229,18 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                     a2[rt] = mma16k32(yl, sh, a2[rt]);
                 }
             }
-            // this wave's dSn row (and its S row again, for <S, dSn>) and this thread's
-            // V' pieces, in flight across the barrier
-            f32x4 drow[4][2], srw[4][2];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                drow[ks][0] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 4 * g);
-                drow[ks][1] = *reinterpret_cast<const f32x4*>(Drow + 32 * ks + 16 + 4 * g);
-                srw[ks][0] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 4 * g);
-                srw[ks][1] = *reinterpret_cast<const f32x4*>(Srow + 32 * ks + 16 + 4 * g);
-            }
-            __syncthreads();
-            put_f32(st_x, vpx);
-            __syncthreads();
             {   // dgamma_C from the decay of the state, e^gamma_C <S, dSn>: this wave's
                 // 16 rows of both are in its registers
                 float part = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) part += dot4v(srw[ks][0], drow[ks][0]) + dot4v(srw[ks][1], drow[ks][1]);
+                for (int ks = 0; ks < 4; ++ks) part += dot4v(srow[ks][0], drow[ks][0]) + dot4v(srow[ks][1], drow[ks][1]);
 #pragma unroll
                 for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
                 if (lane == 0) atomicAdd(&sm.dgc, __expf(sm.gam[CH - 1]) * part);
             }
+            __syncthreads();   // dY read by every wave: V' takes its place
+            put_f32(st_x, vpx);
+            __syncthreads();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 bf16x8 dh, dl;
