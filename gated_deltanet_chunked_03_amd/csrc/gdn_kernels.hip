@@ -1966,18 +1966,41 @@ __device__ __forceinline__ void put_img_t(bf16* img, int rt, int ct, int c, int 
     *reinterpret_cast<bf16x4*>(img + o) = hi;
     *reinterpret_cast<bf16x4*>(img + CH * LDP + o) = lo;
 }
-// row sums of a 16x16 tile over its 16 columns (lanes c) and column sums over
-// its 16 rows (e, then lane groups g)
-__device__ __forceinline__ float tile_rowsum(float x) {
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
-    return x;
-}
+// column sums of a 16x16 tile over its 16 rows (e, then lane groups g)
 __device__ __forceinline__ float tile_colsum(const f32x4& x) {
     float s = (x[0] + x[1]) + (x[2] + x[3]);
     s += __shfl_xor(s, 16, 64);
     s += __shfl_xor(s, 32, 64);
     return s;
+}
+// Row sums of N values at once (N = 4, 8 or 16), each over the 16 lanes c of a
+// lane group, as a reduce-scatter: at each exchange a lane keeps one half of its
+// values, adds its partner's copy of that half and sends the other half, so N
+// sums take N - 1 exchanges in four dependent rounds. Lane c returns the sum of
+// value (c * N) / 16 (for N < 16 the lanes c that share it hold the same sum).
+template <int N, int M>
+__device__ __forceinline__ void rowsum_round(float* a, int c) {
+    if constexpr (M >= 1) {
+        if constexpr (N > 1) {
+            const bool up = (c & M) != 0;
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) {
+                const float send = up ? a[i] : a[i + N / 2];
+                const float keep = up ? a[i + N / 2] : a[i];
+                a[i] = keep + __shfl_xor(send, M, 64);
+            }
+            rowsum_round<N / 2, M / 2>(a, c);
+        } else {
+            a[0] += __shfl_xor(a[0], M, 64);
+            rowsum_round<1, M / 2>(a, c);
+        }
+    }
+}
+template <int N>
+__device__ __forceinline__ float tile_rowsums(float (&a)[N], int c) {
+    static_assert(N == 4 || N == 8 || N == 16, "four, eight or sixteen values");
+    rowsum_round<N, 8>(a, c);
+    return a[0];
 }
 
 // One item's operands that the staging and step 1 read from memory. They are
@@ -2229,15 +2252,11 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                     a2[rt] = mma16k32(yl, sh, a2[rt]);
                 }
             }
-            {   // dgamma_C from the decay of the state, e^gamma_C <S, dSn>: this wave's
-                // 16 rows of both are in its registers
-                float part = 0.f;
+            // dgamma_C from the decay of the state, e^gamma_C <S, dSn>: this wave's 16 rows
+            // of both are in its registers (this lane's part; summed with the kappas below)
+            float sdp = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) part += dot4v(srow[ks][0], drow[ks][0]) + dot4v(srow[ks][1], drow[ks][1]);
-#pragma unroll
-                for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
-                if (lane == 0) atomicAdd(&sm.dgc, __expf(sm.gam[CH - 1]) * part);
-            }
+            for (int ks = 0; ks < 4; ++ks) sdp += dot4v(srow[ks][0], drow[ks][0]) + dot4v(srow[ks][1], drow[ks][1]);
             __syncthreads();   // dY read by every wave: V' takes its place
             put_f32(st_x, vpx);
             __syncthreads();
@@ -2255,6 +2274,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 }
             }
             load3(cur, 0);
+            float kps[16];   // this wave's 16 columns' parts of kappa for row 16 rt + 4 g + e, at 4 rt + e
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int r0 = 16 * rt + 4 * g;
@@ -2269,12 +2289,17 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                     // K[r][16 w + c] from the staged K^T (rows past the end hold the last row, as in Kg)
                     const int dkc = 16 * w + c;
                     const float kv = (float)sm.kt[dkc * LDKT + ((kp(r & ~3) ^ tswz(dkc)) | (r & 3))];
-                    const float kap = tile_rowsum(fr[e] * kv * a1[rt][e]);
-                    if (c == 0 && r < nv) {
-                        atomicAdd(&sm.dgam[r], -kap);
-                        atomicAdd(&sm.dgc, kap);
-                    }
+                    kps[4 * rt + e] = fr[e] * kv * a1[rt][e];
                 }
+            }
+            {   // lane c holds kappa of row 16 (c / 4) + 4 g + c % 4; dgamma_C takes every kappa
+                const float kap = tile_rowsums(kps, c);
+                const int r = 16 * (c >> 2) + 4 * g + (c & 3);
+                if (r < nv) atomicAdd(&sm.dgam[r], -kap);
+                float part = __expf(sm.gam[CH - 1]) * sdp + (r < nv ? kap : 0.f);
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m, 64);
+                if (lane == 0) atomicAdd(&sm.dgc, part);
             }
         }
         // ---- 3. 64 x 64 tiles: dP -> Psi (images), dT (image), K K^T (kept)
@@ -2323,6 +2348,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 if (ks < 3) cur = nxt;
             }
             __syncthreads();   // the staging area becomes the image slots again
+            float es[4] = {0.f, 0.f, 0.f, 0.f};   // row 16 prt + 4 g + e's part of dP o P, both tiles
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int ct = pct0 + j, m = 16 * ct + c;
@@ -2339,13 +2365,12 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 put_img_t(sm.sb, prt, ct, c, g, psi);
                 put_img(sm.sc, prt, ct, c, g, dt[j]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float rs = tile_rowsum(E[e]);
-                    if (c == 0) atomicAdd(&sm.dgam[16 * prt + 4 * g + e], rs);
-                }
+                for (int e = 0; e < 4; ++e) es[e] += E[e];
                 const float cs = tile_colsum(E);
                 if (g == 0) atomicAdd(&sm.dgam[m], -cs);
             }
+            const float rs = tile_rowsums(es, c);   // row 16 prt + 4 g + c / 4
+            if ((c & 3) == 0) atomicAdd(&sm.dgam[16 * prt + 4 * g + (c >> 2)], rs);
         }
         __syncthreads();
         // ---- 4. W1 = dT T^T (tiles); dq += Psi K; dk += Psi^T Q
@@ -2391,6 +2416,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
         // ---- 5. dA = -T^T W1 (strictly lower) -> dbeta, dgamma, G, G^T (images)
         {
             f32x4 da[2];
+            float rsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // row 16 prt + 4 g + e: dbeta at e, dgamma at 4 + e
 #pragma unroll
             for (int j = 0; j < 2; ++j) da[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -2426,15 +2452,15 @@ __global__ __launch_bounds__(NTHR_CH) void k_bwd_chunk_mma(BwdParams p) {
                 put_img_t(sm.sb, prt, ct, c, g, G);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float rb = tile_rowsum(dbr[e]), rg = tile_rowsum(gA[e]);
-                    if (c == 0) {
-                        atomicAdd(&sm.dbe[16 * prt + 4 * g + e], rb);
-                        atomicAdd(&sm.dgam[16 * prt + 4 * g + e], rg);
-                    }
+                    rsum[e] += dbr[e];
+                    rsum[4 + e] += gA[e];
                 }
                 const float cs = tile_colsum(gA);
                 if (g == 0) atomicAdd(&sm.dgam[i], -cs);
             }
+            // lane c: the sum of value c / 2 (dbeta parts, then dgamma parts) of row 16 prt + 4 g + (c / 2) % 4
+            const float rs = tile_rowsums(rsum, c);
+            if ((c & 1) == 0) atomicAdd((c < 8 ? sm.dbe : sm.dgam) + 16 * prt + 4 * g + ((c >> 1) & 3), rs);
         }
         __syncthreads();
         // ---- 6. dk += (G + G^T) K
