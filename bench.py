@@ -56,7 +56,7 @@ KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("gdn_device.h", "gdn_internal.h",
 # of k_decode on the 256-row decode, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by a
 # 512 MiB copy's counts (profiles/forward_kernels_tp8.md, decode_k_decode_256rows.md); None
 # until taken for the current sources.
-MEASURED_TRAFFIC = {"sha256": "738771b4106b92a31772ff2cbc74157158978b220b6e6c25838146b013394d01",
+MEASURED_TRAFFIC = {"sha256": "e2066181ed2b82c8ad382d8a5bb3a89de4945a58584e10af065074a2ea780f2b",
                     # bytes read, written per launch (keys as the per-kernel timings; cp_combine
                     # is the grouped combine's two launches)
                     "tp8": {"per_kernel": {"prep": [19959942, 29393888], "cp_prep": [47357667, 18219008], "cp_combine": [16713831, 5439488], "fwd": [146598206, 67633152]},
