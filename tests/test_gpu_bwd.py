@@ -151,6 +151,22 @@ def test_bwd_fp32_varlen():
     _check_fp32_inputs(inp, d_out, d_fin, got, "fp32/varlen")
 
 
+def test_bwd_varlen_many_items():
+    """Variable-length sequences with more (chunk, head) items than the
+    persistent prep (two workgroups per CU) and chunk-gradient kernel (one per
+    CU) have workgroups: three sequences, 533 chunks x 8 value heads = 4264
+    items, so each workgroup takes several items, of different sequences
+    (located through cu_seqlens), each fetched during the one before (about
+    8 s of oracle)."""
+    cu = [0, 9000, 29001, 34004]
+    inp = make_inputs(name="bwdVL", B=1, T=cu[-1], h_qk=2, h_v=8, seed=37, gate="mixed", init_std=0.1,
+                      cu_seqlens=cu)
+    print(f"\n[bwd/varlen/items] cu={cu}", flush=True)
+    d_out, d_fin = _grads(137, inp.v.shape, len(cu) - 1, inp.h_v)
+    got = _run(inp, d_out, d_fin)
+    _check(inp, d_out, d_fin, got, "varlen/many items")
+
+
 @pytest.mark.parametrize("config", ["tp8", "tp2", "tp1", "long"])
 def test_bwd_full_size(config):
     """The workloads at full size (T = 32768 at the TP8, TP2 and TP1 head
