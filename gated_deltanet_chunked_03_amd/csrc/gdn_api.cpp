@@ -559,11 +559,12 @@ gdn_status run_fwd(const gdn_desc* d, const void* q, const void* k, const void* 
 // dotted with dO), in the re-run layout of the workspace.
 gdn_status run_fwd_rerun(const gdn_desc* d, const Plan& P, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, float scale, const float* s_init, const int32_t* cu,
-                         void* out, char* w8, void* stream, float* chunk_states, float* bwd_y, float* bwd_vp,
+                         char* w8, void* stream, float* chunk_states, float* bwd_y, float* bwd_vp,
                          float* bwd_oi, const void* bwd_dout) {
     gdn::Params p = base_params(d, P);
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.s_init = s_init; p.cu = cu;
-    p.out = out; p.s_final = nullptr; p.scale = scale;
+    p.out = nullptr;   // (the backward needs no output, only the per-chunk blocks below)
+    p.s_final = nullptr; p.scale = scale;
     set_layout(p, P.re, P, w8);
     if (P.n_chunks_total > 0) {
         p.prep_T = reinterpret_cast<float*>(w8 + P.re.off_T);
@@ -595,14 +596,14 @@ gdn_status run_fwd_rerun(const gdn_desc* d, const Plan& P, const void* q, const 
     return GDN_OK;
 }
 
-// Workspace of the backward: the forward's (for its re-run), then the re-run's
-// output, the state entering every chunk, the gradient of the state leaving
+// Workspace of the backward: the forward's (for its re-run, which writes no
+// output), then the state entering every chunk, the gradient of the state leaving
 // every chunk, T / P / gamma per chunk and head (fp32, and T^T / scale P^T / T
 // as bf16 hi/lo images), per chunk and head Y, V', scale e^gamma Q S (from the
 // re-run) and dV', T^T dV' (from the state-gradient scan), and the
 // per-value-head parts of dq and dk.
 struct BwdLayout {
-    size_t off_o = 0, off_cs = 0, off_ds = 0, off_tpg = 0, off_tpt = 0, off_dq = 0, off_dk = 0, bytes = 0;
+    size_t off_cs = 0, off_ds = 0, off_tpg = 0, off_tpt = 0, off_dq = 0, off_dk = 0, bytes = 0;
     size_t off_y = 0, off_vp = 0, off_oi = 0, off_dvp = 0, off_z = 0;
     size_t off_q = 0, off_k = 0, off_v = 0, off_do = 0;   // bf16 copies of fp32 inputs
     size_t tokens = 0;
@@ -613,7 +614,6 @@ BwdLayout bwd_layout(const gdn_desc* d, const Plan& P) {
     for (int n = 0; n < P.n_seqs; ++n) L.tokens += (size_t)P.len[n];
     const size_t st = (size_t)P.n_chunks_total * d->h_v * kStateElems * sizeof(float);
     size_t off = align_up(P.re.bytes, 256);
-    L.off_o = off;   off = align_up(off + L.tokens * d->h_v * gdn::kDim * 2, 256);
     L.off_cs = off;  off = align_up(off + st, 256);
     L.off_ds = off;  off = align_up(off + st, 256);
     L.off_tpg = off; off = align_up(off + (size_t)P.n_chunks_total * d->h_v * gdn::kBwdTpg * sizeof(float), 256);
@@ -700,7 +700,7 @@ gdn_status gdn_bwd(const gdn_desc* desc, const void* q, const void* k, const voi
     }
     // the forward again, keeping the state entering every chunk
     if (P.n_chunks_total > 0) {
-        st = run_fwd_rerun(&d16, P, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8 + L.off_o, w8, stream,
+        st = run_fwd_rerun(&d16, P, q, k, v, g, beta, scale, initial_state, cu_seqlens, w8, stream,
                            reinterpret_cast<float*>(w8 + L.off_cs), reinterpret_cast<float*>(w8 + L.off_y),
                            reinterpret_cast<float*>(w8 + L.off_vp), reinterpret_cast<float*>(w8 + L.off_oi), d_out);
         if (st != GDN_OK) return st;

@@ -1475,8 +1475,10 @@ __global__ __launch_bounds__(NTHR) void k_cp_combine(Params p) {
 // steps in the same order: the two waves of a SIMD then tend to reach their
 // VALU and their MFMA runs together, which issues faster than interleaving
 // (a 16x16x32 MFMA leaves little room for VALU work beside it).
-// With ST the kernel also writes the state entering every chunk (the
-// backward pass recomputes its chunk gradients from these).
+// With ST (the backward's re-run) the kernel instead writes, per chunk, the
+// entering state, Y and V' and the output's state part as its dot with dO (the
+// backward recomputes its chunk gradients from these), and neither forms the
+// P tiles nor the output.
 template <typename IO, bool ST>
 __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
     constexpr bool EX = Io<IO>::kExact;
@@ -1511,6 +1513,7 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
         // same stores (to the scratch line) after the loads before the loop
         // make its entry look alike, so that the waits stay exact
         auto sink_stores = [&]() {
+            if constexpr (ST) return;   // (no output stores in the loop)
             IO* dst = reinterpret_cast<IO*>(p.sink + 32 * lane_id());
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1567,9 +1570,12 @@ __global__ __launch_bounds__(NTHR_CH) void k_fwd(Params p) {
                 chain_vp<IO, true>(sm, ss, vcol, ts_v, min(CH, loc.len - c * CH), Vp);
                 chain_qs<EX>(sm, ss, O);
             }
-            gram_p<EX>(sm, p.scale);
+            if constexpr (!ST) gram_p<EX>(sm, p.scale);
         };
+        // the output: O += P V' and the rows stored (not in the re-run for the
+        // backward, which needs only the state part's dot with dO)
         auto out_part = [&](int c, const f32x4 Vp[4], f32x4 O[4]) {
+            if constexpr (ST) return;
             const size_t tok0 = loc.tok0 + (size_t)c * CH;
             chain_pv_out<IO>(sm, Vp, O, static_cast<IO*>(p.out) + tok0 * ts_v + (size_t)h * DK, ts_v,
                              min(CH, loc.len - c * CH), p.sink);

@@ -258,7 +258,7 @@ gdn_status gdn_calibrate_lambda(const gdn_desc* desc,
  *                      (chunk, value head) two 64 KiB states, 16.25 KiB of P and
  *                      gamma, 48 KiB of bf16 images of T^T, P^T and T, four 32 KiB
  *                      intermediates and 2 KiB of output-term sums, and per token
- *                      and value head 1.25 KiB;
+ *                      and value head 1 KiB;
  *                      GDN_F32 adds the bf16 copies of q, k, v and d_out)
  * Same ownership and error behaviour as gdn_fwd. */
 size_t gdn_bwd_workspace_bytes(const gdn_desc* desc);
