@@ -56,14 +56,14 @@ KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("gdn_device.h", "gdn_internal.h",
 # of k_decode on the 256-row decode, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by a
 # 512 MiB copy's counts (profiles/forward_kernels_tp8.md, decode_k_decode_256rows.md); None
 # until taken for the current sources.
-MEASURED_TRAFFIC = {"sha256": "e2066181ed2b82c8ad382d8a5bb3a89de4945a58584e10af065074a2ea780f2b",
+MEASURED_TRAFFIC = {"sha256": "664e70c7552fd5037bd5794484bc80a6623fbd8103e8fc403eff8a24b3149450",
                     # bytes read, written per launch (keys as the per-kernel timings; cp_combine
                     # is the grouped combine's two launches)
-                    "tp8": {"per_kernel": {"prep": [19959942, 29393888], "cp_prep": [47357667, 18219008], "cp_combine": [16713831, 5439488], "fwd": [146598206, 67633152]},
+                    "tp8": {"per_kernel": {"prep": [19861124, 29393888], "cp_prep": [47348275, 18219008], "cp_combine": [16714197, 5439488], "fwd": [146601421, 67633152]},
                             "dominant": "fwd",
                             # MfmaFlopsF16 + MfmaFlopsBF16 of the step's kernels per step
                             "mfma_flops": 53763000000},
-                    "decode256": {"read": 135135900, "write": 134941632}}
+                    "decode256": {"read": 135138864, "write": 134953632}}
 # The pages' own per-forward times for 1 x 32768 tokens on an H200 (other hardware; context).
 PAGES_MS = {"tp8": 0.310, "tp4": 0.486, "tp2": 0.659, "tp1": 0.493}
 MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 matrix peak
