@@ -317,8 +317,8 @@ __global__ __launch_bounds__(NT) void k_bwd_sum(BwdParams p, long long n_tokens)
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
     for (int e = 0; e < p.group; ++e) {
         const size_t o = ((size_t)tok * p.h_v + hq * p.group + e) * DK + col;
-        a += *reinterpret_cast<const f32x4*>(p.dq_part + o);
-        b += *reinterpret_cast<const f32x4*>(p.dk_part + o);
+        a += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.dq_part + o));   // (read once)
+        b += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.dk_part + o));
     }
     const size_t oo = ((size_t)tok * p.h_qk + hq) * DK + col;
     if (p.out_f32) {
